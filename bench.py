@@ -1,0 +1,222 @@
+"""Benchmark: MoE expert layer forward + backward on one MI355X.
+
+One step = the whole hot path on one batch: route, dispatch, grouped SwiGLU
+FFN forward, combine, then combine backward, grouped FFN backward (dgrad and
+wgrad), router backward and dispatch backward. Inputs are seeded synthetic
+tensors already resident in HBM. The default workload is the bf16 layer with
+8 experts (T=8192, d_model=2048, top-4, d_ff=1024).
+
+Prints one JSON line: tokens/s for the step, plus the grouped-GEMM TFLOP/s,
+dispatch/combine GB/s, a roofline object for the dominant library call
+(timed with HIP events on the stream it runs on) and the fp64 oracle timed
+on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA / packed vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "routing_grouped_gemm_softmax_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, n), "rb") as fh:
+            h.update(n.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(wl):
+    """FLOPs and HBM bytes the method must move, per library call, per step."""
+    T, d, E, k, f = wl.T, wl.d, wl.E, wl.k, wl.f
+    S = T * k
+    b = 4 if wl.dtype == "f32" else 2
+    work = {
+        "moe_grouped_ffn_fwd": {"flops": 6 * S * d * f},
+        "moe_grouped_ffn_bwd": {"flops": 12 * S * d * f},
+        # token-major copies: read the token row once, write/read k routed rows
+        "moe_dispatch": {"bytes": (1 + k) * T * d * b},
+        "moe_combine": {"bytes": (1 + k) * T * d * b},
+        "moe_combine_bwd": {"bytes": (1 + 2 * k) * T * d * b},
+        "moe_dispatch_bwd": {"bytes": (1 + k) * T * d * b},
+    }
+    if wl.routing == "learned":
+        work["moe_route"] = {"flops": 2 * T * d * E}
+        work["moe_route_bwd"] = {"flops": 2 * T * d * E}
+    return work
+
+
+def cpu_baseline(wl, inp):
+    """The fp64 oracle (as it stands) on the same workload, on the host cores."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    t0 = time.perf_counter()
+    fwd = O.layer_forward(inp, wl.k)
+    O.layer_backward(inp, fwd)
+    dt = time.perf_counter() - t0
+    return {"value": wl.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full fp64 forward+backward of the {wl.name} workload (T={wl.T}) "
+                      f"on the host CPU, {dt:.1f} s"}
+
+
+def load_traffic(workload: str, call: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("calls", {}).get(call, {}).get("hbm_bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_e8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import routing_grouped_gemm_softmax_amd as M
+    from moe_inputs import WORKLOADS, make_inputs
+
+    M.load()  # fails loudly if libmoe.so is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload]
+    if wl.dtype == "mxfp8":
+        print("the MXFP8 grouped GEMM is not built yet", file=sys.stderr)
+        sys.exit(1)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    inp = make_inputs(wl, 0)
+
+    def dev(a, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype)
+
+    t = {n: dev(inp[n]) for n in ("x", "dy", "w_gate", "w_up", "w_down")}
+    learned = wl.routing == "learned"
+    if learned:
+        t["w_router"] = dev(inp["w_router"])
+    else:
+        t["topk_idx"] = dev(inp["topk_idx"], torch.int32)
+        t["topk_gate"] = dev(inp["topk_gate"], torch.float32)
+    layer = M.MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, wl.dtype, learned_routing=learned)
+    stream = torch.cuda.current_stream()
+
+    def step(mark=None):
+        if learned:
+            layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_router=t["w_router"], mark=mark)
+        else:
+            layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=t["topk_idx"],
+                          topk_gate=t["topk_gate"], mark=mark)
+        layer.backward(t["dy"], mark=mark)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Events on the stream the library launches on, one after each call.
+    marks = []  # per step: list of (name, event)
+
+    def recorder(lst):
+        def mark(name):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            lst.append((name, ev))
+        return mark
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        lst = []
+        start = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        lst.append(("start", start))
+        step(recorder(lst))
+        marks.append(lst)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_call = {}
+    for lst in marks:
+        for (_, a), (name, b) in zip(lst[:-1], lst[1:]):
+            per_call.setdefault(name, []).append(a.elapsed_time(b))
+    avg_ms = {n: sum(v) / len(v) for n, v in per_call.items()}
+
+    work = algorithmic_work(wl)
+    gemm_ms = avg_ms["moe_grouped_ffn_fwd"] + avg_ms["moe_grouped_ffn_bwd"]
+    gemm_flops = work["moe_grouped_ffn_fwd"]["flops"] + work["moe_grouped_ffn_bwd"]["flops"]
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+    calls = {}
+    for n, ms in avg_ms.items():
+        rec = {"ms": round(ms, 4)}
+        if "flops" in work.get(n, {}):
+            rec["tflops"] = round(work[n]["flops"] / (ms * 1e-3) / 1e12, 2)
+        if "bytes" in work.get(n, {}):
+            rec["gbs"] = round(work[n]["bytes"] / (ms * 1e-3) / 1e9, 1)
+            rec["hbm_frac"] = round(rec["gbs"] / PEAK_HBM_GBS, 3)
+        calls[n] = rec
+    dc_names = [n for n in ("moe_dispatch", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd") if n in avg_ms]
+    dc_bytes = sum(work[n]["bytes"] for n in dc_names)
+    dc_ms = sum(avg_ms[n] for n in dc_names)
+
+    dom = max(("moe_grouped_ffn_fwd", "moe_grouped_ffn_bwd"), key=lambda n: avg_ms[n])
+    achieved = work[dom]["flops"] / (avg_ms[dom] * 1e-3) / 1e12
+    ms_per_step = elapsed / args.steps * 1e3
+    out = {
+        "metric": "MoE layer fwd+bwd tokens/s and grouped-GEMM TFLOP/s (% MFMA peak), 1 GPU",
+        "value": round(wl.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype != "f32" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": dict(wl.describe(), parallelism="none (1 GPU)"),
+        "grouped_gemm": {"tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / peak, 4),
+                         "peak_tflops": peak, "ms": round(gemm_ms, 4)},
+        "dispatch_combine": {"gbs": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
+                             "frac_of_hbm": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "ms": round(dc_ms, 4)},
+        "calls": calls,
+        "roofline": {"kernel": f"{dom} (its grouped GEMM kernels, back to back)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": load_traffic(wl.name, dom)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) MoE expert-layer library, libmoe.so.
+ *
+ * The layer, on one GPU's share of T tokens (forward, then backward):
+ *   route     logits = x W_r; softmax; top-k experts per token; gates
+ *             renormalised over the chosen k            [moe_route]
+ *   dispatch  per-expert histogram and prefix scan on the device, then a
+ *             stable placement of every routed token row into one contiguous
+ *             per-expert input buffer xp                 [moe_dispatch]
+ *   experts   grouped SwiGLU FFN over the per-expert row ranges, scheduled on
+ *             the device from the offsets array          [moe_grouped_ffn_fwd]
+ *   combine   y[t] = sum_j gate[t,j] * o[row_of_slot[t,j]] [moe_combine]
+ *   backward  moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd,
+ *             moe_dispatch_bwd; MXFP8 operands via mxfp8_quantize.
+ *
+ * Sources. The pages that describe the method say, in words only:
+ *  - each token activates 4 of the E experts — "Olmo-core 3 é lançado com
+ *    infraestrutura para treinar modelos MoE" (noticiarioia.com), section
+ *    "Mudança de arquitetura e ganhos de desempenho"; "Ai2 rilascia
+ *    Olmo-Core 3, stack di addestramento aperto per MoE da trilioni di
+ *    parametri" (unite.ai), introduction;
+ *  - routed data is written straight into the experts' input buffers, the
+ *    routing metadata stays on the GPU so the CPU enqueues work without
+ *    waiting for copies back, and the expert matmuls run as a grouped GEMM
+ *    scheduled on the device — "Olmo-core 3 escala el entrenamiento de
+ *    mixture-of-experts a billones de parámetros" (bytechap.com), section
+ *    "Cómo funciona"; unite.ai page, section "Parallelismo, precisione e
+ *    tecniche di memoria";
+ *  - MXFP8 is supported — noticiarioia.com page, section "Otimizações e testes
+ *    em escala de trilhões"; unite.ai page, section "Parallelismo, precisione
+ *    e tecniche di memoria".
+ * The layer specification fixes what the pages leave open: softmax routing,
+ * top-k gates renormalised to sum to 1 (ties in the logits go to the lower
+ * expert index), SwiGLU experts silu(x W_gate) * (x W_up) then W_down, no
+ * biases, no capacity limit, no dropped tokens, gates applied after the FFN.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer argument is DEVICE memory owned by the caller unless
+ *    stated otherwise; the library never allocates, frees or keeps it.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only
+ *    enqueue work: no host synchronisation, no device-to-host copy. Counts,
+ *    offsets and the permutation never leave the device.
+ *  - Tensors are dense row-major. Sizes are int64_t. Floating tensors are in
+ *    the layer dtype `shape->dtype` (MOE_F32 or MOE_BF16; MXFP8 layers keep
+ *    bf16 master tensors) unless the argument says fp32. Weights:
+ *    w_router [d][E]; w_gate, w_up [E][d][f]; w_down [E][f][d].
+ *  - Row counts: S = T*k routed rows. Index tensors are int32.
+ *  - Validation is host-side only and never reads device memory. Errors:
+ *    MOE_ERR_INVALID_ARG (null pointer, bad sizes, k > E), MOE_ERR_UNSUPPORTED
+ *    (d or f not a multiple of 64, E > 256, k > 8, dtype not available for
+ *    the call), MOE_ERR_MISALIGNED (a tensor pointer not 16-byte aligned),
+ *    MOE_ERR_WORKSPACE (workspace/save buffer smaller than the query says),
+ *    MOE_ERR_HIP (a launch failed; the message names the HIP error).
+ *    On error nothing is enqueued. moe_last_error_message() gives a
+ *    thread-local description of the last failure.
+ *  - Results are deterministic: no floating-point atomics; reruns on the same
+ *    inputs are bit-identical.
+ *  - Calls that share a workspace or save buffer must be ordered on one
+ *    stream (or otherwise serialised) by the caller.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,
+  MOE_ERR_UNSUPPORTED = -2,
+  MOE_ERR_MISALIGNED = -3,
+  MOE_ERR_WORKSPACE = -4,
+  MOE_ERR_HIP = -5
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 };
+
+/* Operation ids for moe_workspace_size. */
+enum moe_op {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_DISPATCH = 1,
+  MOE_OP_FFN_FWD = 2,
+  MOE_OP_FFN_BWD = 3,
+  MOE_OP_ROUTE_BWD = 4,
+  MOE_OP_DISPATCH_BWD = 5
+};
+
+/* Device-side status bits, read back with moe_read_device_status. */
+enum moe_device_status { MOE_DEV_OK = 0, MOE_DEV_BAD_EXPERT = 1 };
+
+typedef struct moe_shape {
+  int64_t T;     /* tokens on this GPU (>= 1) */
+  int64_t d;     /* model width (multiple of 64) */
+  int64_t E;     /* experts (1..256) */
+  int64_t k;     /* experts per token (1..min(E, 8)) */
+  int64_t f;     /* expert FFN width d_ff (multiple of 64) */
+  int32_t dtype; /* enum moe_dtype */
+  int32_t reserved; /* must be 0 */
+} moe_shape;
+
+int moe_abi_version(void);
+const char* moe_status_string(int status);
+const char* moe_last_error_message(void);
+
+/* Bytes of scratch workspace `op` needs for `shape` (0 if none). Never fails;
+ * returns (size_t)-1 for an invalid shape. Workspaces carry no state between
+ * calls except the device status word written by moe_dispatch. */
+size_t moe_workspace_size(int op, const moe_shape* shape);
+
+/* Bytes of the buffer that moe_grouped_ffn_fwd fills with the activations the
+ * backward needs (G, U, H: three [S][f] tensors in the layer dtype). */
+size_t moe_save_size(const moe_shape* shape);
+
+/* Router: logits[T][E] (fp32) = x[T][d] · w_router[d][E] with fp32
+ * accumulation; then per token the k largest logits in decreasing order,
+ * equal values to the lower expert index, written to topk_idx[T][k];
+ * topk_gate[T][k] (fp32) = softmax over the k chosen logits, which equals the
+ * full softmax renormalised over the chosen set.
+ * Passage: noticiarioia.com page, "Mudança de arquitetura e ganhos de
+ * desempenho" (4 of E experts per token); bytechap.com page, "Cómo funciona"
+ * (routing kept on the GPU). */
+int moe_route(const void* x, const void* w_router, const moe_shape* shape,
+              float* logits_out, int32_t* topk_idx_out, float* topk_gate_out,
+              void* stream);
+
+/* Dispatch: counts[E] = rows per expert, offsets[E+1] = exclusive prefix sum
+ * (offsets[E] = S), all computed on the device. Expert e's rows are
+ * offsets[e]..offsets[e+1]-1 and hold its tokens in increasing token order;
+ * row_of_slot[T][k] gives the row of every (token, slot); token_of_row[S] the
+ * inverse; xp[S][d] (layer dtype) is x gathered into that order.
+ * An expert id outside [0, E) is not routed (its row_of_slot is -1), and the
+ * device status word in `ws` is set to MOE_DEV_BAD_EXPERT.
+ * ws: at least moe_workspace_size(MOE_OP_DISPATCH) bytes, 256-byte aligned.
+ * Passage: bytechap.com page, "Cómo funciona"; unite.ai page, "Parallelismo,
+ * precisione e tecniche di memoria" (rows written straight into the experts'
+ * input buffers; routing metadata stays on the GPU). */
+int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* shape,
+                 int32_t* counts_out, int32_t* offsets_out, int32_t* row_of_slot_out,
+                 int32_t* token_of_row_out, void* xp_out, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Reads the device status word that the last moe_dispatch on `ws` wrote.
+ * Synchronises `stream`. For debugging and tests; returns MOE_DEV_* bits, or a
+ * negative moe_status on failure. */
+int moe_read_device_status(const void* ws, void* stream);
+
+/* Grouped SwiGLU FFN forward over the per-expert row ranges in `offsets`
+ * (device array, E+1 entries; never read by the host). For expert e and each
+ * of its rows r: G = xp[r] · w_gate[e], U = xp[r] · w_up[e],
+ * H = silu(G) * U with silu(z) = z / (1 + exp(-z)), o[r] = H · w_down[e];
+ * fp32 accumulation, one rounding to the layer dtype per stored value.
+ * save (>= moe_save_size bytes) receives G, U, H for the backward.
+ * ws: moe_workspace_size(MOE_OP_FFN_FWD) bytes (may be 0 -> NULL allowed).
+ * Passage: bytechap.com page, "Cómo funciona" (grouped GEMM combining many
+ * small expert computations); unite.ai page, "Parallelismo, precisione e
+ * tecniche di memoria" (matmuls scheduled on the device). */
+int moe_grouped_ffn_fwd(const void* xp, const void* w_gate, const void* w_up,
+                        const void* w_down, const int32_t* offsets, const moe_shape* shape,
+                        void* save, size_t save_bytes, void* o_out, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Combine: y[t] = sum_j topk_gate[t,j] * o[row_of_slot[t,j]], summed in fp32
+ * in slot order, one rounding. Slots with row -1 contribute nothing.
+ * Passage: the gate-weighted combine of the layer specification. */
+int moe_combine(const void* o, const float* topk_gate, const int32_t* row_of_slot,
+                const moe_shape* shape, void* y_out, void* stream);
+
+/* Combine backward: d_o[row_of_slot[t,j]] = topk_gate[t,j] * dy[t] (layer
+ * dtype) and dgate[t,j] (fp32) = <dy[t], o[row_of_slot[t,j]]>. */
+int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
+                    const int32_t* row_of_slot, const moe_shape* shape, void* d_o_out,
+                    float* dgate_out, void* stream);
+
+/* Grouped FFN backward, per expert e on its rows:
+ *   dH = d_o · w_down[e]^T;  dU = dH * silu(G);
+ *   dG = dH * U * sig(G) * (1 + G (1 - sig(G)))   (from the saved G, U, H)
+ *   dxp = dG · w_gate[e]^T + dU · w_up[e]^T
+ *   dw_down[e] = H^T · d_o;  dw_gate[e] = xp^T · dG;  dw_up[e] = xp^T · dU
+ * Weight gradients of experts with no rows are written as zeros. All outputs
+ * in the layer dtype. ws: moe_workspace_size(MOE_OP_FFN_BWD) bytes. */
+int moe_grouped_ffn_bwd(const void* d_o, const void* xp, const void* w_gate, const void* w_up,
+                        const void* w_down, const int32_t* offsets, const moe_shape* shape,
+                        const void* save, void* dxp_out, void* dw_gate_out, void* dw_up_out,
+                        void* dw_down_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Router backward through the renormalised top-k softmax:
+ *   dlogits[t,i] = g_ti (dgate_ti - sum_j g_tj dgate_tj) for i in the chosen
+ *   set of token t, 0 elsewhere (fp32 [T][E]);
+ *   dw_router[d][E] (layer dtype) = x^T · dlogits, reduced over T in a fixed
+ *   order (deterministic split over token blocks).
+ * ws: moe_workspace_size(MOE_OP_ROUTE_BWD) bytes. */
+int moe_route_bwd(const void* x, const void* w_router, const int32_t* topk_idx,
+                  const float* topk_gate, const float* dgate, const moe_shape* shape,
+                  float* dlogits_out, void* dw_router_out, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Dispatch backward: dx[t] = sum_j dxp[row_of_slot[t,j]]
+ * (+ sum_e dlogits[t,e] * w_router[:,e] when dlogits and w_router are both
+ * non-NULL), accumulated in fp32, one rounding to the layer dtype.
+ * ws: moe_workspace_size(MOE_OP_DISPATCH_BWD) bytes (needed only with the
+ * router term). */
+int moe_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* dlogits,
+                     const void* w_router, const moe_shape* shape, void* dx_out, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* MXFP8 quantisation of a bf16 matrix in_bf16[rows][cols]:
+ * axis 0: blocks of 32 consecutive elements along a row (cols % 32 == 0);
+ *         scale_out is [rows][cols/32].
+ * axis 1: blocks of 32 consecutive rows within a column (rows % 32 == 0);
+ *         scale_out is [rows/32][cols].
+ * Per block: amax = max |v|; E8M0 scale code c = clamp(floor(log2 amax) - 8
+ * + 127, 0, 254) (0 for an all-zero block); q_out = E4M3 ("FN": bias 7, max
+ * 448) code of v / 2^(c-127), rounded to nearest even, saturated to +-448,
+ * sign kept. q_out has the shape of the input. This is the OCP Microscaling
+ * (MX) v1.0 conversion; the pages only say that MXFP8 is used —
+ * noticiarioia.com page, "Otimizações e testes em escala de trilhões";
+ * unite.ai page, "Parallelismo, precisione e tecniche di memoria".
+ * Inputs must be finite. */
+int mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, int axis, uint8_t* q_out,
+                   uint8_t* scale_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

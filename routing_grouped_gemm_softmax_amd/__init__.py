@@ -1,0 +1,12 @@
+"""MI355X (gfx950) MoE expert layer: route, dispatch, grouped SwiGLU FFN,
+combine, and their backward passes, as hand-written HIP kernels behind the
+C ABI of libmoe.so (include/moe.h). This package is the Python binding:
+argument marshalling and buffer allocation with torch, nothing else.
+"""
+from . import _lib  # noqa: F401
+from ._lib import (  # noqa: F401
+    MoeShape, MoeError, load, moe_route, moe_dispatch, moe_read_device_status, moe_grouped_ffn_fwd,
+    moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd, moe_dispatch_bwd, mxfp8_quantize,
+    workspace_size, save_size,
+)
+from .layer import MoELayer  # noqa: F401

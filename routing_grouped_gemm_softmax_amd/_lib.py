@@ -1,0 +1,204 @@
+"""ctypes binding of libmoe.so: the C entry points under the same names.
+
+Argument marshalling only: torch tensors (device memory) become pointers, the
+current torch stream becomes the hipStream_t. Every step of the layer runs in
+the HIP kernels of libmoe.so. Loading fails loudly if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4, -5
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+(MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
+ MOE_OP_ROUTE_BWD, MOE_OP_DISPATCH_BWD) = range(6)
+MOE_DEV_BAD_EXPERT = 1
+
+DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.bfloat16}
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("f", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    @classmethod
+    def make(cls, T, d, E, k, f, dtype) -> "MoeShape":
+        code = DTYPE_CODE[dtype] if isinstance(dtype, str) else int(dtype)
+        return cls(int(T), int(d), int(E), int(k), int(f), code, 0)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {code} ({msg})")
+        self.code = code
+
+
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_SHAPE = ctypes.POINTER(MoeShape)
+
+# name -> (restype, argtypes); mirrors include/moe.h
+SIGNATURES = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error_message": (ctypes.c_char_p, []),
+    "moe_workspace_size": (_SZ, [ctypes.c_int, _SHAPE]),
+    "moe_save_size": (_SZ, [_SHAPE]),
+    "moe_route": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P]),
+    "moe_dispatch": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_read_device_status": (ctypes.c_int, [_P, _P]),
+    "moe_grouped_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _SHAPE, _P, _SZ, _P, _P, _SZ, _P]),
+    "moe_combine": (ctypes.c_int, [_P, _P, _P, _SHAPE, _P, _P]),
+    "moe_combine_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _P]),
+    "moe_grouped_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _SZ, _P]),
+    "moe_dispatch_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _SZ, _P]),
+    "mxfp8_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by routing_grouped_gemm_softmax_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libmoe.so not built: {LIB_PATH} is missing "
+                              "(run routing_grouped_gemm_softmax_amd.build.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load().moe_last_error_message().decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(fn, rc, last_error())
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a tensor (None stays NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmoe must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _expect(t, dtype, numel, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+
+
+def workspace_size(op: int, shape: MoeShape) -> int:
+    n = load().moe_workspace_size(op, ctypes.byref(shape))
+    if n == ctypes.c_size_t(-1).value:
+        raise MoeError("moe_workspace_size", MOE_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def save_size(shape: MoeShape) -> int:
+    n = load().moe_save_size(ctypes.byref(shape))
+    if n == ctypes.c_size_t(-1).value:
+        raise MoeError("moe_save_size", MOE_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def moe_route(x, w_router, shape, logits, topk_idx, topk_gate, stream=None):
+    T, E, k = shape.T, shape.E, shape.k
+    _expect(logits, torch.float32, T * E, "logits")
+    _expect(topk_idx, torch.int32, T * k, "topk_idx")
+    _expect(topk_gate, torch.float32, T * k, "topk_gate")
+    _check("moe_route", load().moe_route(_ptr(x), _ptr(w_router), ctypes.byref(shape), _ptr(logits),
+                                         _ptr(topk_idx), _ptr(topk_gate), _stream(stream)))
+
+
+def moe_dispatch(x, topk_idx, shape, counts, offsets, row_of_slot, token_of_row, xp, ws, stream=None):
+    _expect(topk_idx, torch.int32, shape.T * shape.k, "topk_idx")
+    _expect(counts, torch.int32, shape.E, "counts")
+    _expect(offsets, torch.int32, shape.E + 1, "offsets")
+    _check("moe_dispatch", load().moe_dispatch(
+        _ptr(x), _ptr(topk_idx), ctypes.byref(shape), _ptr(counts), _ptr(offsets), _ptr(row_of_slot),
+        _ptr(token_of_row), _ptr(xp), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_read_device_status(ws, stream=None) -> int:
+    rc = load().moe_read_device_status(_ptr(ws), _stream(stream))
+    if rc < 0:
+        raise MoeError("moe_read_device_status", rc, last_error())
+    return rc
+
+
+def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, shape, save, o, ws=None, stream=None):
+    _check("moe_grouped_ffn_fwd", load().moe_grouped_ffn_fwd(
+        _ptr(xp), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(offsets), ctypes.byref(shape), _ptr(save),
+        save.numel() * save.element_size(), _ptr(o), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def moe_combine(o, topk_gate, row_of_slot, shape, y, stream=None):
+    _check("moe_combine", load().moe_combine(_ptr(o), _ptr(topk_gate), _ptr(row_of_slot), ctypes.byref(shape),
+                                             _ptr(y), _stream(stream)))
+
+
+def moe_combine_bwd(dy, o, topk_gate, row_of_slot, shape, d_o, dgate, stream=None):
+    _expect(dgate, torch.float32, shape.T * shape.k, "dgate")
+    _check("moe_combine_bwd", load().moe_combine_bwd(_ptr(dy), _ptr(o), _ptr(topk_gate), _ptr(row_of_slot),
+                                                     ctypes.byref(shape), _ptr(d_o), _ptr(dgate), _stream(stream)))
+
+
+def moe_grouped_ffn_bwd(d_o, xp, w_gate, w_up, w_down, offsets, shape, save, dxp, dw_gate, dw_up, dw_down, ws,
+                        stream=None):
+    _check("moe_grouped_ffn_bwd", load().moe_grouped_ffn_bwd(
+        _ptr(d_o), _ptr(xp), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(offsets), ctypes.byref(shape),
+        _ptr(save), _ptr(dxp), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_route_bwd(x, w_router, topk_idx, topk_gate, dgate, shape, dlogits, dw_router, ws, stream=None):
+    _expect(dlogits, torch.float32, shape.T * shape.E, "dlogits")
+    _check("moe_route_bwd", load().moe_route_bwd(
+        _ptr(x), _ptr(w_router), _ptr(topk_idx), _ptr(topk_gate), _ptr(dgate), ctypes.byref(shape), _ptr(dlogits),
+        _ptr(dw_router), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_dispatch_bwd(dxp, row_of_slot, dlogits, w_router, shape, dx, ws=None, stream=None):
+    _check("moe_dispatch_bwd", load().moe_dispatch_bwd(
+        _ptr(dxp), _ptr(row_of_slot), _ptr(dlogits), _ptr(w_router), ctypes.byref(shape), _ptr(dx), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mxfp8_quantize(x, axis, q, scale, stream=None):
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("mxfp8_quantize takes a 2-D bf16 tensor")
+    rows, cols = x.shape
+    _expect(q, torch.uint8, rows * cols, "q")
+    _expect(scale, torch.uint8, rows * cols // 32, "scale")
+    _check("mxfp8_quantize", load().mxfp8_quantize(_ptr(x), rows, cols, int(axis), _ptr(q), _ptr(scale),
+                                                   _stream(stream)))

@@ -1,0 +1,255 @@
+// C ABI of libmoe.so: host-side validation, workspace sizing and kernel launch.
+// Validation never touches device memory; on any error nothing is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+// Shape checks shared by every layer entry point.
+int check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "shape.reserved must be 0");
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
+  if (s->T < 1 || s->d < 1 || s->E < 1 || s->k < 1 || s->f < 1)
+    return fail(MOE_ERR_INVALID_ARG, "T, d, E, k, f must be >= 1 (got %lld %lld %lld %lld %lld)",
+                (long long)s->T, (long long)s->d, (long long)s->E, (long long)s->k, (long long)s->f);
+  if (s->k > s->E) return fail(MOE_ERR_INVALID_ARG, "k (%lld) > E (%lld)", (long long)s->k, (long long)s->E);
+  if (s->E > 256) return fail(MOE_ERR_UNSUPPORTED, "E > 256 is not supported");
+  if (s->k > 8) return fail(MOE_ERR_UNSUPPORTED, "k > 8 is not supported");
+  if (s->d % 64 || s->f % 64) return fail(MOE_ERR_UNSUPPORTED, "d and f must be multiples of 64");
+  // Index arithmetic is 32-bit for row ids and 64-bit for element offsets.
+  if (s->T * s->k > (int64_t)1 << 30 || s->d > 65536 || s->f > 65536 || s->T > (int64_t)1 << 28)
+    return fail(MOE_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  return MOE_OK;
+}
+
+// The bf16 path serves MXFP8 layers' master tensors until the scaled GEMM exists.
+int check_dense_dtype(const moe_shape* s, const char* who) {
+  if (s->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "%s: MOE_MXFP8 grouped GEMM is not available", who);
+  return MOE_OK;
+}
+
+#define CHECK(expr)              \
+  do {                           \
+    int _rc = (expr);            \
+    if (_rc != MOE_OK) return _rc; \
+  } while (0)
+
+#define NEED(ptr)                                                                   \
+  do {                                                                              \
+    if (!(ptr)) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #ptr); \
+    if (!aligned16(ptr)) return fail(MOE_ERR_MISALIGNED, "%s: %s is not 16-byte aligned", __func__, #ptr); \
+  } while (0)
+
+#define LAUNCH(call)                                          \
+  do {                                                        \
+    hipError_t _e = (call);                                   \
+    if (_e != hipSuccess) return hip_fail(_e, __func__);      \
+  } while (0)
+
+size_t save_bytes_for(const moe_shape* s) {
+  return (size_t)3 * s->T * s->k * s->f * elem_bytes(s->dtype);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error_message(void) { return g_msg; }
+
+size_t moe_workspace_size(int op, const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return (size_t)-1;
+  const int T = (int)s->T, d = (int)s->d, E = (int)s->E, f = (int)s->f, k = (int)s->k;
+  switch (op) {
+    case MOE_OP_ROUTE: return 0;
+    case MOE_OP_DISPATCH: return moe::dispatch_workspace(T, E);
+    case MOE_OP_FFN_FWD: return 0;
+    case MOE_OP_FFN_BWD: return (size_t)T * k * 2 * f * elem_bytes(s->dtype);  // dG|dU rows
+    case MOE_OP_ROUTE_BWD: return moe::route_bwd_workspace(T, d, E);
+    case MOE_OP_DISPATCH_BWD: return moe::dispatch_bwd_workspace(d, E, s->dtype == MOE_F32);
+    default: fail(MOE_ERR_INVALID_ARG, "unknown op %d", op); return (size_t)-1;
+  }
+}
+
+size_t moe_save_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return (size_t)-1;
+  return save_bytes_for(s);
+}
+
+int moe_route(const void* x, const void* w_router, const moe_shape* s, float* logits_out, int32_t* topk_idx_out,
+              float* topk_gate_out, void* stream) {
+  CHECK(check_shape(s));
+  NEED(x); NEED(w_router); NEED(logits_out); NEED(topk_idx_out); NEED(topk_gate_out);
+  LAUNCH(moe::launch_route(x, w_router, s->dtype == MOE_F32, (int)s->T, (int)s->d, (int)s->E, (int)s->k, logits_out,
+                           topk_idx_out, topk_gate_out, as_stream(stream)));
+  return MOE_OK;
+}
+
+int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* s, int32_t* counts_out,
+                 int32_t* offsets_out, int32_t* row_of_slot_out, int32_t* token_of_row_out, void* xp_out, void* ws,
+                 size_t ws_bytes, void* stream) {
+  CHECK(check_shape(s));
+  NEED(x); NEED(topk_idx); NEED(counts_out); NEED(offsets_out); NEED(row_of_slot_out); NEED(token_of_row_out);
+  NEED(xp_out); NEED(ws);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MOE_ERR_MISALIGNED, "moe_dispatch: ws must be 256-byte aligned");
+  const size_t need = moe::dispatch_workspace((int)s->T, (int)s->E);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_dispatch: workspace %zu < %zu bytes", ws_bytes, need);
+  LAUNCH(moe::launch_dispatch(x, topk_idx, elem_bytes(s->dtype), (int)s->T, (int)s->d, (int)s->E, (int)s->k,
+                              counts_out, offsets_out, row_of_slot_out, token_of_row_out, xp_out, ws,
+                              as_stream(stream)));
+  return MOE_OK;
+}
+
+int moe_read_device_status(const void* ws, void* stream) {
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "moe_read_device_status: ws is NULL");
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_read_device_status");
+  return v;
+}
+
+int moe_grouped_ffn_fwd(const void* xp, const void* w_gate, const void* w_up, const void* w_down,
+                        const int32_t* offsets, const moe_shape* s, void* save, size_t save_bytes, void* o_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  CHECK(check_shape(s));
+  CHECK(check_dense_dtype(s, "moe_grouped_ffn_fwd"));
+  NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(save); NEED(o_out);
+  if (save_bytes < save_bytes_for(s))
+    return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_fwd: save buffer %zu < %zu bytes", save_bytes, save_bytes_for(s));
+  moe::FfnArgs a{};
+  a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
+  a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
+  const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
+  a.G = save; a.U = static_cast<char*>(save) + plane; a.H = static_cast<char*>(save) + 2 * plane;
+  a.o = o_out;
+  LAUNCH(moe::launch_ffn_fwd(a, s->dtype == MOE_F32, as_stream(stream)));
+  return MOE_OK;
+}
+
+int moe_combine(const void* o, const float* topk_gate, const int32_t* row_of_slot, const moe_shape* s, void* y_out,
+                void* stream) {
+  CHECK(check_shape(s));
+  NEED(o); NEED(topk_gate); NEED(row_of_slot); NEED(y_out);
+  LAUNCH(moe::launch_combine(o, topk_gate, row_of_slot, s->dtype == MOE_F32, (int)s->T, (int)s->d, (int)s->k, y_out,
+                             as_stream(stream)));
+  return MOE_OK;
+}
+
+int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate, const int32_t* row_of_slot,
+                    const moe_shape* s, void* d_o_out, float* dgate_out, void* stream) {
+  CHECK(check_shape(s));
+  NEED(dy); NEED(o); NEED(topk_gate); NEED(row_of_slot); NEED(d_o_out); NEED(dgate_out);
+  LAUNCH(moe::launch_combine_bwd(dy, o, topk_gate, row_of_slot, s->dtype == MOE_F32, (int)s->T, (int)s->d, (int)s->k,
+                                 d_o_out, dgate_out, as_stream(stream)));
+  return MOE_OK;
+}
+
+int moe_grouped_ffn_bwd(const void* d_o, const void* xp, const void* w_gate, const void* w_up, const void* w_down,
+                        const int32_t* offsets, const moe_shape* s, const void* save, void* dxp_out,
+                        void* dw_gate_out, void* dw_up_out, void* dw_down_out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  CHECK(check_shape(s));
+  CHECK(check_dense_dtype(s, "moe_grouped_ffn_bwd"));
+  NEED(d_o); NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(save); NEED(dxp_out);
+  NEED(dw_gate_out); NEED(dw_up_out); NEED(dw_down_out); NEED(ws);
+  const size_t need = moe_workspace_size(MOE_OP_FFN_BWD, s);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_bwd: workspace %zu < %zu bytes", ws_bytes, need);
+  moe::FfnArgs a{};
+  a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
+  a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
+  const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
+  char* sv = const_cast<char*>(static_cast<const char*>(save));
+  a.G = sv; a.U = sv + plane; a.H = sv + 2 * plane;
+  a.d_o = d_o; a.dgu = ws; a.dxp = dxp_out; a.dw_gate = dw_gate_out; a.dw_up = dw_up_out; a.dw_down = dw_down_out;
+  LAUNCH(moe::launch_ffn_bwd(a, s->dtype == MOE_F32, as_stream(stream)));
+  return MOE_OK;
+}
+
+int moe_route_bwd(const void* x, const void* w_router, const int32_t* topk_idx, const float* topk_gate,
+                  const float* dgate, const moe_shape* s, float* dlogits_out, void* dw_router_out, void* ws,
+                  size_t ws_bytes, void* stream) {
+  (void)w_router;
+  CHECK(check_shape(s));
+  NEED(x); NEED(topk_idx); NEED(topk_gate); NEED(dgate); NEED(dlogits_out); NEED(dw_router_out); NEED(ws);
+  const size_t need = moe::route_bwd_workspace((int)s->T, (int)s->d, (int)s->E);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route_bwd: workspace %zu < %zu bytes", ws_bytes, need);
+  LAUNCH(moe::launch_route_bwd(x, topk_idx, topk_gate, dgate, s->dtype == MOE_F32, (int)s->T, (int)s->d, (int)s->E,
+                               (int)s->k, dlogits_out, dw_router_out, ws, as_stream(stream)));
+  return MOE_OK;
+}
+
+int moe_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* dlogits, const void* w_router,
+                     const moe_shape* s, void* dx_out, void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_shape(s));
+  NEED(dxp); NEED(row_of_slot); NEED(dx_out);
+  const bool router = dlogits != nullptr && w_router != nullptr;
+  if ((dlogits == nullptr) != (w_router == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_bwd: dlogits and w_router must be both set or both NULL");
+  if (router) {
+    NEED(dlogits); NEED(w_router); NEED(ws);
+    const size_t need = moe::dispatch_bwd_workspace((int)s->d, (int)s->E, s->dtype == MOE_F32);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_dispatch_bwd: workspace %zu < %zu bytes", ws_bytes, need);
+  }
+  LAUNCH(moe::launch_dispatch_bwd(dxp, row_of_slot, dlogits, w_router, s->dtype == MOE_F32, (int)s->T, (int)s->d,
+                                  (int)s->E, (int)s->k, dx_out, ws, as_stream(stream)));
+  return MOE_OK;
+}
+
+int mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, int axis, uint8_t* q_out, uint8_t* scale_out,
+                   void* stream) {
+  if (!in_bf16 || !q_out || !scale_out) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize: NULL pointer");
+  if (rows < 1 || cols < 1) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize: rows and cols must be >= 1");
+  if (axis != 0 && axis != 1) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize: axis must be 0 or 1");
+  if ((axis == 0 && cols % 32) || (axis == 1 && rows % 32))
+    return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize: the blocked axis must be a multiple of 32");
+  if (axis == 0 && (!aligned16(in_bf16) || !aligned16(q_out)))
+    return fail(MOE_ERR_MISALIGNED, "mxfp8_quantize: in and q must be 16-byte aligned");
+  if (rows * cols > ((int64_t)1 << 40)) return fail(MOE_ERR_UNSUPPORTED, "mxfp8_quantize: too large");
+  LAUNCH(moe::launch_mxfp8_quantize(in_bf16, rows, cols, axis, q_out, scale_out, as_stream(stream)));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Device-side helpers shared by the MoE layer kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef uint16_t bf16_t;  // raw bf16 bit pattern in memory
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- scalar conversions -----------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Element-type traits: storage type <-> fp32 math.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
+  __device__ __forceinline__ static float from_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  __device__ __forceinline__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// A 16-byte vector of elements, unpacked to fp32 (8 for bf16, 4 for fp32).
+template <typename T> struct Vec16 {
+  static constexpr int N = 16 / Elem<T>::kBytes;
+};
+
+__device__ __forceinline__ void unpack16(const uint4& v, float (&o)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const uint4& v, float (&o)[4]) {
+  o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+  o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ uint4 pack16(const float (&o)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_bf16(o[2 * i])) |
+           (static_cast<uint32_t>(f32_to_bf16(o[2 * i + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ uint4 pack16(const float (&o)[4]) {
+  return make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]),
+                    __float_as_uint(o[2]), __float_as_uint(o[3]));
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, const uint4& v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+// ---- wave primitives ----------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return (l == 0) ? 0ull : (~0ull >> (64 - l));
+}
+
+// Sum over the 64 lanes of a wave with a fixed butterfly order (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Exclusive prefix sum of an int over the lanes of a wave.
+__device__ __forceinline__ int wave_exclusive_scan(int v) {
+  const int l = lane_id();
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(inc, o, kWave);
+    if (l >= o) inc += t;
+  }
+  return inc - v;
+}
+
+// Mask of the active lanes whose `key` equals this lane's key (key < 2^bits).
+__device__ __forceinline__ uint64_t match_any(int key, bool valid, int bits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const uint64_t on = __ballot(valid && ((key >> b) & 1));
+    m &= ((key >> b) & 1) ? on : ~on;
+  }
+  return valid ? m : 0ull;
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace moe

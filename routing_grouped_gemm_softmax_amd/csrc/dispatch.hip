@@ -1,0 +1,447 @@
+// Dispatch (histogram, prefix scan, stable placement, row gather), combine,
+// and their backward passes.
+//
+// The pages place routed rows straight into contiguous per-expert input
+// buffers and keep the routing metadata on the GPU so the host enqueues work
+// without waiting ("Olmo-core 3 escala el entrenamiento de mixture-of-experts
+// a billones de parámetros", section "Cómo funciona"; "Ai2 rilascia Olmo-Core
+// 3...", section "Parallelismo, precisione e tecniche di memoria"). On one GPU
+// that placement is a local permute: a stable counting sort of the (token,
+// slot) pairs by expert, followed by a token-major row copy that reads each
+// token row once and writes it to its k destinations.
+//
+// Placement order inside an expert is increasing token index, which makes
+// the permutation unique; it is computed without atomics on the slot order:
+//   1. count:  per chunk of kChunkTok tokens, an LDS histogram of expert ids;
+//   2. scan:   one workgroup turns the [chunk][expert] counts into counts,
+//              offsets and the first row of every (chunk, expert) pair;
+//   3. place:  per chunk, waves walk the slots in order; a ballot-based
+//              match gives each slot its rank among equal experts of the
+//              wave, and per-wave totals in LDS give the ranks across waves.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kChunkTok = 512;  // tokens per histogram chunk
+
+struct DispatchWs {
+  int32_t* status;       // 1 int (padded to 256 B)
+  int32_t* chunk_counts; // [nch][E]
+  int32_t* chunk_base;   // [nch][E]
+  int32_t* chunk_bad;    // [nch]
+};
+
+static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+static DispatchWs carve(void* ws, int nch, int E) {
+  char* p = static_cast<char*>(ws);
+  DispatchWs w;
+  w.status = reinterpret_cast<int32_t*>(p); p += 256;
+  w.chunk_counts = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * nch * E);
+  w.chunk_base = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * nch * E);
+  w.chunk_bad = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+size_t dispatch_workspace(int T, int E) {
+  const int nch = (T + kChunkTok - 1) / kChunkTok;
+  return 256 + 2 * align256(sizeof(int32_t) * nch * E) + align256(sizeof(int32_t) * nch);
+}
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                             DispatchWs w) {
+  __shared__ int hist[256];
+  __shared__ int bad;
+  const int c = blockIdx.x, tid = threadIdx.x;
+  hist[tid] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  const int64_t s0 = static_cast<int64_t>(c) * kChunkTok * k;
+  const int64_t s1 = min(static_cast<int64_t>(T), static_cast<int64_t>(c + 1) * kChunkTok) * k;
+  int my_bad = 0;
+  for (int64_t s = s0 + tid; s < s1; s += 256) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);  // integer counts: order-independent
+    else my_bad = 1;
+  }
+  if (my_bad) bad = 1;
+  __syncthreads();
+  if (tid < E) w.chunk_counts[static_cast<int64_t>(c) * E + tid] = hist[tid];
+  if (tid == 0) w.chunk_bad[c] = bad;
+}
+
+// Single workgroup: counts, offsets, and chunk_base[c][e] = offsets[e] + rows
+// of expert e in chunks before c. Also writes the device status word.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int nch, int E, DispatchWs w, int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets) {
+  __shared__ int segsum[1024];
+  __shared__ int tot[256];
+  __shared__ int off[257];
+  const int tid = threadIdx.x;
+  const int nseg = max(1, min(nch, 1024 / E));
+  const int cps = (nch + nseg - 1) / nseg;
+  const int seg = tid / E, e = tid % E;
+  const bool mine = seg < nseg;
+  if (mine) {
+    int sum = 0;
+    const int c1 = min(nch, (seg + 1) * cps);
+    for (int c = seg * cps; c < c1; ++c) sum += w.chunk_counts[static_cast<int64_t>(c) * E + e];
+    segsum[seg * E + e] = sum;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int run = 0;
+    for (int s = 0; s < nseg; ++s) {
+      const int v = segsum[s * E + tid];
+      segsum[s * E + tid] = run;
+      run += v;
+    }
+    tot[tid] = run;
+  }
+  __syncthreads();
+  if (tid < 64) {  // exclusive scan over experts: 4 experts per lane
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ee = tid * 4 + q;
+      v[q] = ee < E ? tot[ee] : 0;
+      sum += v[q];
+    }
+    int run = wave_exclusive_scan(sum);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ee = tid * 4 + q;
+      if (ee < E) off[ee] = run;
+      run += v[q];
+    }
+    if (tid == 63) off[E] = run;
+  }
+  __syncthreads();
+  if (tid < E) counts[tid] = tot[tid];
+  if (tid <= E) offsets[tid] = off[tid];
+  if (mine) {
+    int base = off[e] + segsum[seg * E + e];
+    const int c1 = min(nch, (seg + 1) * cps);
+    for (int c = seg * cps; c < c1; ++c) {
+      w.chunk_base[static_cast<int64_t>(c) * E + e] = base;
+      base += w.chunk_counts[static_cast<int64_t>(c) * E + e];
+    }
+  }
+  if (tid == 0) {
+    int bad = 0;
+    for (int c = 0; c < nch; ++c) bad |= w.chunk_bad[c];
+    w.status[0] = bad ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                             int bits, DispatchWs w, int32_t* __restrict__ row_of_slot,
+                                                             int32_t* __restrict__ token_of_row) {
+  __shared__ int base[256];
+  __shared__ int wcnt[4][256];
+  const int c = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  if (tid < E) {
+    base[tid] = w.chunk_base[static_cast<int64_t>(c) * E + tid];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+  }
+  __syncthreads();
+  const int64_t s0 = static_cast<int64_t>(c) * kChunkTok * k;
+  const int64_t s1 = min(static_cast<int64_t>(T), static_cast<int64_t>(c + 1) * kChunkTok) * k;
+  for (int64_t sb = s0; sb < s1; sb += 256) {
+    const int64_t s = sb + tid;
+    const bool in = s < s1;
+    const int e = in ? idx[s] : -1;
+    const bool ok = in && e >= 0 && e < E;
+    const uint64_t m = match_any(ok ? e : 0, ok, bits);
+    const int rank = __popcll(m & lanemask_lt());
+    if (ok && rank == 0) wcnt[wave][e] = __popcll(m);
+    __syncthreads();
+    if (ok) {
+      int row = base[e] + rank;
+      for (int q = 0; q < wave; ++q) row += wcnt[q][e];
+      row_of_slot[s] = row;
+      token_of_row[row] = static_cast<int32_t>(s / k);
+    } else if (in) {
+      row_of_slot[s] = -1;
+    }
+    __syncthreads();
+    if (tid < E) {
+      base[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// Lanes per token for row kernels: enough 16-byte vectors to cover one row.
+static int lanes_per_token(int nvec) {
+  int l = 1;
+  while (l < nvec && l < 256) l <<= 1;
+  return l;
+}
+
+// xp[row_of_slot[t][j]] = x[t]: read the token row once, write it k times.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ x, const int32_t* __restrict__ row_of_slot,
+                                                          int T, int k, int nvec, int lpt, char* __restrict__ xp) {
+  const int tpw = 256 / lpt;
+  const int t = blockIdx.x * tpw + threadIdx.x / lpt;
+  const int sub = threadIdx.x % lpt;
+  if (t >= T) return;
+  const int64_t rb = static_cast<int64_t>(nvec) * 16;
+  int rows[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rows[j] = j < k ? row_of_slot[static_cast<int64_t>(t) * k + j] : -1;
+  for (int v = sub; v < nvec; v += lpt) {
+    const uint4 val = ld16(x + t * rb + v * 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (rows[j] >= 0) st16(xp + rows[j] * rb + v * 16, val);
+  }
+}
+
+hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E, int k,
+                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
+                           void* xp, void* ws, hipStream_t s) {
+  const int nch = (T + kChunkTok - 1) / kChunkTok;
+  DispatchWs w = carve(ws, nch, E);
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(256), 0, s, topk_idx, T, E, k, w);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, nch, E, w, counts, offsets);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_place_kernel, dim3(nch), dim3(256), 0, s, topk_idx, T, E, k, bits, w, row_of_slot,
+                     token_of_row);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int nvec = d * elem_bytes / 16;
+  const int lpt = lanes_per_token(nvec);
+  const int tpw = 256 / lpt;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((T + tpw - 1) / tpw), dim3(256), 0, s,
+                     static_cast<const char*>(x), row_of_slot, T, k, nvec, lpt, static_cast<char*>(xp));
+  return hipGetLastError();
+}
+
+// y[t] = sum_j gate[t][j] * o[row_of_slot[t][j]]  (fp32, slot order, one rounding).
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, const float* __restrict__ gate,
+                                                      const int32_t* __restrict__ row_of_slot, int Tn, int k,
+                                                      int nvec, int lpt, T* __restrict__ y) {
+  constexpr int VE = Vec16<T>::N;
+  const int tpw = 256 / lpt;
+  const int t = blockIdx.x * tpw + threadIdx.x / lpt;
+  const int sub = threadIdx.x % lpt;
+  if (t >= Tn) return;
+  const int64_t re = static_cast<int64_t>(nvec) * VE;  // elements per row
+  int rows[8];
+  float g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    rows[j] = j < k ? row_of_slot[static_cast<int64_t>(t) * k + j] : -1;
+    g[j] = j < k ? gate[static_cast<int64_t>(t) * k + j] : 0.0f;
+  }
+  for (int v = sub; v < nvec; v += lpt) {
+    float acc[VE];
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (rows[j] < 0) continue;
+      float ov[VE];
+      unpack16(ld16(o + rows[j] * re + v * VE), ov);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) acc[i] = fmaf(g[j], ov[i], acc[i]);
+    }
+    st16(y + t * re + v * VE, pack16(acc));
+  }
+}
+
+// d_o[row(t,j)] = gate[t][j] * dy[t];  dgate[t][j] = <dy[t], o[row(t,j)]> (fp32,
+// fixed reduction tree: per-thread partials, lane butterfly, then waves in order).
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ o,
+                                                          const float* __restrict__ gate,
+                                                          const int32_t* __restrict__ row_of_slot, int Tn, int k,
+                                                          int nvec, int lpt, T* __restrict__ d_o,
+                                                          float* __restrict__ dgate) {
+  constexpr int VE = Vec16<T>::N;
+  __shared__ float red[4][8];
+  const int tpw = 256 / lpt;
+  const int t = blockIdx.x * tpw + threadIdx.x / lpt;
+  const int sub = threadIdx.x % lpt;
+  const bool live = t < Tn;
+  const int64_t re = static_cast<int64_t>(nvec) * VE;
+  int rows[8];
+  float g[8], part[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    rows[j] = (live && j < k) ? row_of_slot[static_cast<int64_t>(t) * k + j] : -1;
+    g[j] = (live && j < k) ? gate[static_cast<int64_t>(t) * k + j] : 0.0f;
+    part[j] = 0.0f;
+  }
+  if (live) {
+    for (int v = sub; v < nvec; v += lpt) {
+      float dv[VE];
+      unpack16(ld16(dy + t * re + v * VE), dv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (rows[j] < 0) continue;
+        float ov[VE], sv[VE];
+        unpack16(ld16(o + rows[j] * re + v * VE), ov);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) {
+          part[j] = fmaf(dv[i], ov[i], part[j]);
+          sv[i] = g[j] * dv[i];
+        }
+        st16(d_o + rows[j] * re + v * VE, pack16(sv));
+      }
+    }
+  }
+  // Reduce part[j] over the lpt lanes of the token.
+  const int width = lpt < 64 ? lpt : 64;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    for (int off = width >> 1; off > 0; off >>= 1) part[j] += __shfl_xor(part[j], off, kWave);
+  if (lpt <= 64) {
+    if (live && sub == 0)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < k) dgate[static_cast<int64_t>(t) * k + j] = rows[j] >= 0 ? part[j] : 0.0f;
+  } else {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[wave][j] = part[j];
+    __syncthreads();
+    if (live && sub == 0) {
+      const int w0 = (threadIdx.x / lpt) * (lpt / 64);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= k) break;
+        float s = 0.0f;
+        for (int q = 0; q < lpt / 64; ++q) s += red[w0 + q][j];
+        dgate[static_cast<int64_t>(t) * k + j] = rows[j] >= 0 ? s : 0.0f;
+      }
+    }
+  }
+}
+
+hipError_t launch_combine(const void* o, const float* gate, const int32_t* row_of_slot, bool is_f32, int T, int d,
+                          int k, void* y, hipStream_t s) {
+  const int nvec = d * (is_f32 ? 4 : 2) / 16;
+  const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
+  const dim3 grid((T + tpw - 1) / tpw);
+  if (is_f32)
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(o), gate, row_of_slot,
+                       T, k, nvec, lpt, static_cast<float*>(y));
+  else
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(o), gate,
+                       row_of_slot, T, k, nvec, lpt, static_cast<bf16_t*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate, const int32_t* row_of_slot,
+                              bool is_f32, int T, int d, int k, void* d_o, float* dgate, hipStream_t s) {
+  const int nvec = d * (is_f32 ? 4 : 2) / 16;
+  const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
+  const dim3 grid((T + tpw - 1) / tpw);
+  if (is_f32)
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(dy),
+                       static_cast<const float*>(o), gate, row_of_slot, T, k, nvec, lpt, static_cast<float*>(d_o),
+                       dgate);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(dy),
+                       static_cast<const bf16_t*>(o), gate, row_of_slot, T, k, nvec, lpt,
+                       static_cast<bf16_t*>(d_o), dgate);
+  return hipGetLastError();
+}
+
+// W_r [d][E] -> W_rT [E][d] (same dtype), so the router term of dx reads rows.
+template <typename T>
+__global__ void transpose_router_kernel(const T* __restrict__ w, int d, int E, T* __restrict__ wt) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(d) * E) return;
+  const int r = static_cast<int>(i / E), e = static_cast<int>(i % E);
+  wt[static_cast<int64_t>(e) * d + r] = w[i];
+}
+
+// dx[t] = sum_j dxp[row(t,j)] (+ sum_{e: dl[t][e] != 0} dl[t][e] * W_rT[e]).
+// dl is zero off the chosen set, so only those k columns are read.
+template <typename T>
+__global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__ dxp, const int32_t* __restrict__ row_of_slot,
+                                                           const float* __restrict__ dl, const T* __restrict__ wt,
+                                                           int Tn, int E, int k, int nvec, int lpt, T* __restrict__ dx) {
+  constexpr int VE = Vec16<T>::N;
+  const int tpw = 256 / lpt;
+  const int t = blockIdx.x * tpw + threadIdx.x / lpt;
+  const int sub = threadIdx.x % lpt;
+  if (t >= Tn) return;
+  const int64_t re = static_cast<int64_t>(nvec) * VE;
+  int rows[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rows[j] = j < k ? row_of_slot[static_cast<int64_t>(t) * k + j] : -1;
+  for (int v = sub; v < nvec; v += lpt) {
+    float acc[VE];
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (rows[j] < 0) continue;
+      float gv[VE];
+      unpack16(ld16(dxp + rows[j] * re + v * VE), gv);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) acc[i] += gv[i];
+    }
+    if (dl != nullptr) {
+      const float* dlt = dl + static_cast<int64_t>(t) * E;
+      for (int e = 0; e < E; ++e) {
+        const float c = dlt[e];
+        if (c == 0.0f) continue;
+        float wv[VE];
+        unpack16(ld16(wt + e * re + v * VE), wv);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) acc[i] = fmaf(c, wv[i], acc[i]);
+      }
+    }
+    st16(dx + t * re + v * VE, pack16(acc));
+  }
+}
+
+size_t dispatch_bwd_workspace(int d, int E, bool is_f32) {
+  return static_cast<size_t>(d) * E * (is_f32 ? 4 : 2);
+}
+
+hipError_t launch_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* dlogits,
+                               const void* w_router, bool is_f32, int T, int d, int E, int k, void* dx, void* ws,
+                               hipStream_t s) {
+  const bool router = dlogits != nullptr && w_router != nullptr;
+  hipError_t err;
+  if (router) {
+    const int64_t n = static_cast<int64_t>(d) * E;
+    const dim3 g(static_cast<unsigned>((n + 255) / 256));
+    if (is_f32)
+      hipLaunchKernelGGL(transpose_router_kernel<float>, g, dim3(256), 0, s, static_cast<const float*>(w_router), d,
+                         E, static_cast<float*>(ws));
+    else
+      hipLaunchKernelGGL(transpose_router_kernel<bf16_t>, g, dim3(256), 0, s, static_cast<const bf16_t*>(w_router),
+                         d, E, static_cast<bf16_t*>(ws));
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  const int nvec = d * (is_f32 ? 4 : 2) / 16;
+  const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
+  const dim3 grid((T + tpw - 1) / tpw);
+  const float* dl = router ? dlogits : nullptr;
+  if (is_f32)
+    hipLaunchKernelGGL(dispatch_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(dxp), row_of_slot,
+                       dl, static_cast<const float*>(ws), T, E, k, nvec, lpt, static_cast<float*>(dx));
+  else
+    hipLaunchKernelGGL(dispatch_bwd_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(dxp),
+                       row_of_slot, dl, static_cast<const bf16_t*>(ws), T, E, k, nvec, lpt,
+                       static_cast<bf16_t*>(dx));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,60 @@
+// Internal launcher declarations shared by the kernel files and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct FfnArgs {
+  int S, d, f, E;
+  const int32_t* offsets;
+  const void* xp;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  // forward outputs / saved activations
+  void* G;
+  void* U;
+  void* H;
+  void* o;
+  // backward
+  const void* d_o;
+  void* dgu;      // [S][2f] workspace
+  void* dxp;
+  void* dw_gate;
+  void* dw_up;
+  void* dw_down;
+};
+
+hipError_t launch_ffn_fwd(const FfnArgs& a, bool is_f32, hipStream_t s);
+hipError_t launch_ffn_bwd(const FfnArgs& a, bool is_f32, hipStream_t s);
+
+// Router (route.hip)
+hipError_t launch_route(const void* x, const void* w_router, bool is_f32, int T, int d, int E, int k,
+                        float* logits, int32_t* topk_idx, float* topk_gate, hipStream_t s);
+size_t route_bwd_workspace(int T, int d, int E);
+hipError_t launch_route_bwd(const void* x, const int32_t* topk_idx, const float* topk_gate,
+                            const float* dgate, bool is_f32, int T, int d, int E, int k,
+                            float* dlogits, void* dw_router, void* ws, hipStream_t s);
+
+// Dispatch / combine (dispatch.hip)
+size_t dispatch_workspace(int T, int E);
+hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d,
+                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                           int32_t* token_of_row, void* xp, void* ws, hipStream_t s);
+hipError_t launch_combine(const void* o, const float* gate, const int32_t* row_of_slot, bool is_f32,
+                          int T, int d, int k, void* y, hipStream_t s);
+hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate,
+                              const int32_t* row_of_slot, bool is_f32, int T, int d, int k,
+                              void* d_o, float* dgate, hipStream_t s);
+size_t dispatch_bwd_workspace(int d, int E, bool is_f32);
+hipError_t launch_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* dlogits,
+                               const void* w_router, bool is_f32, int T, int d, int E, int k,
+                               void* dx, void* ws, hipStream_t s);
+
+// MXFP8 (mxfp8.hip)
+hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,
+                                 uint8_t* scale, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,106 @@
+"""One MoE expert layer (forward + backward) driven through libmoe's C entry points.
+
+All device buffers are allocated once, up front, with torch; forward() and
+backward() only enqueue the library's kernels on the current stream, in the
+order route -> dispatch -> grouped FFN -> combine and back. Nothing is
+copied to the host.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class MoELayer:
+    def __init__(self, T: int, d: int, E: int, k: int, f: int, dtype: str = "bf16",
+                 learned_routing: bool = True, device: str = "cuda"):
+        self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
+        self.shape = L.MoeShape.make(T, d, E, k, f, dtype)
+        self.dtype = L.TORCH_DTYPE[self.shape.dtype]
+        self.learned = learned_routing
+        S = T * k
+        dev = torch.device(device)
+        f32, i32, dt = torch.float32, torch.int32, self.dtype
+
+        def buf(*shape, dtype=dt):
+            return torch.empty(*shape, dtype=dtype, device=dev)
+
+        def ws(op):
+            n = L.workspace_size(op, self.shape)
+            return torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+
+        # forward
+        self.logits = buf(T, E, dtype=f32) if learned_routing else None
+        self.topk_idx = buf(T, k, dtype=i32)
+        self.topk_gate = buf(T, k, dtype=f32)
+        self.counts = buf(E, dtype=i32)
+        self.offsets = buf(E + 1, dtype=i32)
+        self.row_of_slot = buf(T, k, dtype=i32)
+        self.token_of_row = buf(S, dtype=i32)
+        self.xp = buf(S, d)
+        self.save = torch.empty(L.save_size(self.shape), dtype=torch.uint8, device=dev)
+        self.o = buf(S, d)
+        self.y = buf(T, d)
+        self.ws_dispatch = ws(L.MOE_OP_DISPATCH)
+        # backward
+        self.d_o = buf(S, d)
+        self.dgate = buf(T, k, dtype=f32)
+        self.dxp = buf(S, d)
+        self.dw_gate = buf(E, d, f)
+        self.dw_up = buf(E, d, f)
+        self.dw_down = buf(E, f, d)
+        self.dx = buf(T, d)
+        self.ws_ffn_bwd = ws(L.MOE_OP_FFN_BWD)
+        if learned_routing:
+            self.dlogits = buf(T, E, dtype=f32)
+            self.dw_router = buf(d, E)
+            self.ws_route_bwd = ws(L.MOE_OP_ROUTE_BWD)
+            self.ws_dispatch_bwd = ws(L.MOE_OP_DISPATCH_BWD)
+
+    def saved(self):
+        """(G, U, H) views of the save buffer, each [S][f]."""
+        S, f = self.T * self.k, self.f
+        flat = self.save.view(self.dtype)
+        return tuple(flat[i * S * f:(i + 1) * S * f].view(S, f) for i in range(3))
+
+    def forward(self, x, w_gate, w_up, w_down, w_router=None, topk_idx=None, topk_gate=None, stream=None,
+                mark=None):
+        """Enqueue the forward pass. ``mark(name)``, if given, is called after
+        each library call is enqueued (the benchmark records events there)."""
+        s = self.shape
+        mark = mark or (lambda name: None)
+        self.x, self.w_gate, self.w_up, self.w_down, self.w_router = x, w_gate, w_up, w_down, w_router
+        if self.learned:
+            L.moe_route(x, w_router, s, self.logits, self.topk_idx, self.topk_gate, stream)
+            mark("moe_route")
+        else:
+            self.topk_idx.copy_(topk_idx)
+            self.topk_gate.copy_(topk_gate)
+        L.moe_dispatch(x, self.topk_idx, s, self.counts, self.offsets, self.row_of_slot, self.token_of_row,
+                       self.xp, self.ws_dispatch, stream)
+        mark("moe_dispatch")
+        L.moe_grouped_ffn_fwd(self.xp, w_gate, w_up, w_down, self.offsets, s, self.save, self.o, None, stream)
+        mark("moe_grouped_ffn_fwd")
+        L.moe_combine(self.o, self.topk_gate, self.row_of_slot, s, self.y, stream)
+        mark("moe_combine")
+        return self.y
+
+    def backward(self, dy, stream=None, mark=None):
+        s = self.shape
+        mark = mark or (lambda name: None)
+        L.moe_combine_bwd(dy, self.o, self.topk_gate, self.row_of_slot, s, self.d_o, self.dgate, stream)
+        mark("moe_combine_bwd")
+        L.moe_grouped_ffn_bwd(self.d_o, self.xp, self.w_gate, self.w_up, self.w_down, self.offsets, s, self.save,
+                              self.dxp, self.dw_gate, self.dw_up, self.dw_down, self.ws_ffn_bwd, stream)
+        mark("moe_grouped_ffn_bwd")
+        if self.learned:
+            L.moe_route_bwd(self.x, self.w_router, self.topk_idx, self.topk_gate, self.dgate, s, self.dlogits,
+                            self.dw_router, self.ws_route_bwd, stream)
+            mark("moe_route_bwd")
+            L.moe_dispatch_bwd(self.dxp, self.row_of_slot, self.dlogits, self.w_router, s, self.dx,
+                               self.ws_dispatch_bwd, stream)
+        else:
+            L.moe_dispatch_bwd(self.dxp, self.row_of_slot, None, None, s, self.dx, None, stream)
+        mark("moe_dispatch_bwd")
+        return self.dx
