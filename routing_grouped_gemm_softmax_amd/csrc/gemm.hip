@@ -19,32 +19,12 @@
 // operands of the weight gradients) are transposed in registers on their way
 // into LDS, so every MFMA fragment is one 16-byte LDS read per lane.
 #include "common.h"
+#include "grouped_gemm.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moe {
-
-enum GemmMode { FWD_GU = 0, FWD_DOWN = 1, BWD_DOWN = 2, BWD_GU = 3, WGRAD = 4 };
-
-struct GemmParams {
-  const void* a;      // A operand
-  int64_t lda;
-  const void* b0;     // B operand (first source)
-  const void* b1;     // second source (w_up for FWD_GU / BWD_GU)
-  int64_t ldb;
-  int64_t bstride;    // elements between experts in b0/b1 (0 for WGRAD)
-  void* c0;           // outputs
-  void* c1;
-  void* c2;
-  int64_t ldc;
-  const void* e0;     // epilogue inputs (BWD_DOWN: saved G, U)
-  const void* e1;
-  const int32_t* offsets;
-  int E, S;
-  int M;              // WGRAD: rows of each weight gradient
-  int N, K;           // logical N (FWD_GU: 2f) and K (ragged modes)
-  int f;              // split point: FWD_GU/BWD_GU/WGRAD(gate|up)
-  int cstride;        // WGRAD: elements between experts in c0/c1
-};
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -476,6 +456,28 @@ static hipError_t launch_wgrad(const GemmParams& p, hipStream_t s) {
   return launch_mode<T, WGRAD, 64, 64>(p, grid, s);
 }
 
+// fp32 layers use the kernel above; bf16 layers the kernel of gemm_bf16.hip.
+template <typename T>
+static hipError_t ragged(int mode, const GemmParams& p, hipStream_t s) {
+  if constexpr (std::is_same<T, float>::value) {
+    switch (mode) {
+      case FWD_GU: return launch_ragged<T, FWD_GU>(p, s);
+      case FWD_DOWN: return launch_ragged<T, FWD_DOWN>(p, s);
+      case BWD_DOWN: return launch_ragged<T, BWD_DOWN>(p, s);
+      case BWD_GU: return launch_ragged<T, BWD_GU>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return launch_bf16_ragged(mode, p, s);
+  }
+}
+
+template <typename T>
+static hipError_t wgrad(const GemmParams& p, hipStream_t s) {
+  if constexpr (std::is_same<T, float>::value) return launch_wgrad<T>(p, s);
+  else return launch_bf16_wgrad(p, s);
+}
+
 template <typename T>
 static hipError_t ffn_fwd_t(const FfnArgs& a, hipStream_t s) {
   const int S = a.S, d = a.d, f = a.f;
@@ -485,14 +487,14 @@ static hipError_t ffn_fwd_t(const FfnArgs& a, hipStream_t s) {
   p.a = a.xp; p.lda = d; p.b0 = a.w_gate; p.b1 = a.w_up; p.ldb = f;
   p.bstride = static_cast<int64_t>(d) * f;
   p.c0 = a.G; p.c1 = a.U; p.c2 = a.H; p.ldc = f; p.N = 2 * f; p.K = d;
-  hipError_t err = launch_ragged<T, FWD_GU>(p, s);
+  hipError_t err = ragged<T>(FWD_GU, p, s);
   if (err != hipSuccess) return err;
   // O = H W_down
   GemmParams q{};
   q.offsets = a.offsets; q.E = a.E; q.S = S; q.f = f;
   q.a = a.H; q.lda = f; q.b0 = a.w_down; q.ldb = d; q.bstride = static_cast<int64_t>(f) * d;
   q.c0 = a.o; q.ldc = d; q.N = d; q.K = f;
-  return launch_ragged<T, FWD_DOWN>(q, s);
+  return ragged<T>(FWD_DOWN, q, s);
 }
 
 template <typename T>
@@ -504,7 +506,7 @@ static hipError_t ffn_bwd_t(const FfnArgs& a, hipStream_t s) {
     p.offsets = a.offsets; p.E = a.E; p.S = S; p.f = f;
     p.a = a.d_o; p.lda = d; p.b0 = a.w_down; p.ldb = d; p.bstride = static_cast<int64_t>(f) * d;
     p.c0 = a.dgu; p.ldc = 2 * f; p.e0 = a.G; p.e1 = a.U; p.N = f; p.K = d;
-    if ((err = launch_ragged<T, BWD_DOWN>(p, s)) != hipSuccess) return err;
+    if ((err = ragged<T>(BWD_DOWN, p, s)) != hipSuccess) return err;
   }
   {  // dXp = dG W_gate^T + dU W_up^T   (K = 2f)
     GemmParams p{};
@@ -512,21 +514,21 @@ static hipError_t ffn_bwd_t(const FfnArgs& a, hipStream_t s) {
     p.a = a.dgu; p.lda = 2 * f; p.b0 = a.w_gate; p.b1 = a.w_up; p.ldb = f;
     p.bstride = static_cast<int64_t>(d) * f;
     p.c0 = a.dxp; p.ldc = d; p.N = d; p.K = 2 * f;
-    if ((err = launch_ragged<T, BWD_GU>(p, s)) != hipSuccess) return err;
+    if ((err = ragged<T>(BWD_GU, p, s)) != hipSuccess) return err;
   }
   {  // dW_down[e] = H_e^T dO_e   ([f][d], K = n_e)
     GemmParams p{};
     p.offsets = a.offsets; p.E = a.E; p.S = S;
     p.a = a.H; p.lda = f; p.b0 = a.d_o; p.ldb = d;
     p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = f * d; p.M = f; p.N = d; p.f = d;
-    if ((err = launch_wgrad<T>(p, s)) != hipSuccess) return err;
+    if ((err = wgrad<T>(p, s)) != hipSuccess) return err;
   }
   {  // [dW_gate | dW_up][e] = Xp_e^T [dG | dU]_e   ([d][2f] split at column f)
     GemmParams p{};
     p.offsets = a.offsets; p.E = a.E; p.S = S;
     p.a = a.xp; p.lda = d; p.b0 = a.dgu; p.ldb = 2 * f;
     p.c0 = a.dw_gate; p.c1 = a.dw_up; p.ldc = f; p.cstride = d * f; p.M = d; p.N = 2 * f; p.f = f;
-    if ((err = launch_wgrad<T>(p, s)) != hipSuccess) return err;
+    if ((err = wgrad<T>(p, s)) != hipSuccess) return err;
   }
   return hipSuccess;
 }

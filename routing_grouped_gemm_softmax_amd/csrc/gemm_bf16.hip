@@ -1,0 +1,641 @@
+// bf16 grouped GEMMs of the expert SwiGLU FFN for gfx950 (forward, dgrad,
+// wgrad), scheduled on the device from the per-expert row offsets.
+//
+// The pages run the experts' matmuls as one grouped GEMM whose schedule lives
+// on the device, so the host never waits for routing metadata ("Olmo-core 3
+// escala el entrenamiento de mixture-of-experts a billones de parámetros",
+// section "Cómo funciona"; "Ai2 rilascia Olmo-Core 3...", section
+// "Parallelismo, precisione e tecniche di memoria"). Every workgroup reads the
+// E+1 offsets, derives the per-expert tile counts with a wave scan and maps
+// its id to (expert, row tile, column tile); the grid is sized on the host
+// from the count-free bound ceil(S/BM) + E row tiles.
+//
+// Tile: 256 threads = 4 waves in 2 x 2; a BM x BN output tile, each wave a
+// (BM/2) x (BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16) with
+// the accumulators in AGPRs. K advances in slabs of 64 elements.
+//
+// Operands move HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
+// VGPR staging), double-buffered: the loads of slab kt+1 fly while slab kt is
+// multiplied. The buffer range check zero-fills rows past an expert's end,
+// which both masks ragged row tiles and gives the weight gradients their
+// ragged K for free. LDS layouts:
+//  - K-contiguous operand: [row][64 k] rows of 128 B, 16-byte chunks
+//    XOR-swizzled by the row; fragments are one ds_read_b128 per lane.
+//  - row-contiguous operand ([k][rows] in HBM: the weights in the forward and
+//    both operands of the weight gradients): [64 k][rows] as stored, chunks
+//    XOR-swizzled by k; fragments are two ds_read_b64_tr_b16 per lane, which
+//    transpose 16 x 4 blocks on the way out of LDS.
+// The N-side fragment is the MFMA's first operand, so every lane ends up with
+// four consecutive output columns of one row: the epilogue stores 8 bytes per
+// lane and reads the saved G, U the same way.
+#include "common.h"
+#include "grouped_gemm.h"
+#include "kernels.h"
+
+#include <type_traits>
+
+namespace moe {
+namespace {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4s lds_v4s_t;
+
+constexpr int kBK = 32;     // K elements per slab (64 bytes of bf16)
+constexpr int kStages = 4;  // LDS ring depth: slabs kt+1..kt+3 fly while kt is multiplied
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), 0x00020000);
+}
+
+// One 16-byte load per lane into LDS: lane i writes lds_wave + 16 i (lds_wave
+// is wave-uniform and goes to M0). Issued as inline assembly so the compiler,
+// which cannot tell the ring slots apart, does not add a full vmcnt(0) wait in
+// front of every LDS read; the kernel waits for these loads itself
+// (wait_vmcnt before the barrier that publishes a slab).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_wave) {
+  asm volatile("buffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "{m0}"(lds_wave), "s"(r) : "memory");
+}
+
+// K-contiguous tiles: rows of 64 bytes (4 chunks of 16); a 16-lane quarter of
+// a ds_read_b128 reads one chunk column of 16 consecutive rows, so XOR-ing the
+// chunk with (row / 4) % 4 spreads those rows over all 64 banks.
+__device__ __forceinline__ int swz_row(int row) { return (row >> 2) & 3; }
+// Row-contiguous tiles: a transposing read touches 4 consecutive k-rows x 32
+// bytes per 16-lane group; XOR-ing the chunk index with 4 (k % 4) puts the 16
+// (row, chunk) pairs of a half-wave on distinct banks (64 banks of 4 bytes).
+// Rows of only 8 chunks (R = 64) use 2 (k % 4).
+template <int R>
+__device__ __forceinline__ int swz_k(int k) { return R >= 128 ? (k & 3) << 2 : (k & 3) << 1; }
+
+// K-contiguous tile of R rows x 32 k: stage rows [0, R) of a descriptor whose
+// base is the tile's first row at the slab's first k; ld in elements. One
+// wave-wide load fills 16 rows.
+template <int R>
+__device__ __forceinline__ void stage_kmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane) {
+#pragma unroll
+  for (int q = 0; q < R / 64; ++q) {
+    const int rbase = (q * 4 + wave) * 16;
+    const int row = rbase + (lane >> 2);
+    const int g = (lane & 3) ^ swz_row(row);
+    load_lds16(r, static_cast<uint32_t>(row * ld * 2 + g * 16), dst + rbase * 64);
+  }
+}
+
+// Row-contiguous tile: 32 k-rows of R elements; descriptor base at (slab's
+// first k, tile's first column).
+template <int R>
+__device__ __forceinline__ void stage_mnmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane) {
+  constexpr int RB = R * 2;
+#pragma unroll
+  for (int q = 0; q < R / 64; ++q) {
+    const int byte0 = (q * 4 + wave) * 1024;
+    const int byte = byte0 + lane * 16;
+    const int k = byte / RB;
+    const int g = ((byte % RB) >> 4) ^ swz_k<R>(k);
+    load_lds16(r, static_cast<uint32_t>(k * ld * 2 + g * 16), dst + byte0);
+  }
+}
+
+// Fragment (32 rows x 16 k) of a K-contiguous tile: lane -> row rb + lane%32,
+// k = 16 kk + 8 (lane/32) .. +7.
+__device__ __forceinline__ bf16x8 frag_kmajor(const char* t, int rb, int kk, int lane) {
+  const int row = rb + (lane & 31);
+  const int chunk = (kk * 2 + (lane >> 5)) ^ swz_row(row);
+  return *reinterpret_cast<const bf16x8*>(t + row * 64 + chunk * 16);
+}
+
+// Same fragment from a row-contiguous tile of R columns, via two transposing
+// reads: within each 16-lane group, source lane s points at (k0 + s/4, c0 +
+// 4 (s%4)) and result lane i receives k0..k0+3 of column c0 + i.
+template <int R>
+__device__ __forceinline__ bf16x8 frag_mnmajor(const char* t, int cb, int kk, int lane) {
+  constexpr int RB = R * 2;
+  const int g = lane >> 4, s = lane & 15;
+  const int c = cb + 16 * (g & 1) + 4 * (s & 3);
+  const int kb = kk * 16 + 8 * (g >> 1) + (s >> 2);
+  v4s h[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int k = kb + 4 * half;
+    const int byte = c * 2;
+    const int off = k * RB + ((((byte >> 4) ^ swz_k<R>(k))) << 4) + (byte & 15);
+    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(const_cast<char*>(t) + off));
+  }
+  bf16x8 v;
+  __builtin_memcpy(&v, h, 16);
+  return v;
+}
+
+// Four fp32 -> four bf16 (round to nearest even) with gfx950's packed convert.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const bf16x2_t r = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2(pack2(a, b), pack2(c, d));
+}
+__device__ __forceinline__ void unpack4(uint2 v, float (&o)[4]) {
+  o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, fully unrolled, so
+// accumulator indices stay compile-time constants (a runtime index would put
+// the accumulators in scratch memory).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
+
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+template <int MODE, int BM, int BN>
+__global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr bool M_MN = (MODE == WGRAD);                                      // A stored [k][m]
+  constexpr bool N_MN = (MODE == FWD_GU || MODE == FWD_DOWN || MODE == WGRAD);  // B stored [k][n]
+  constexpr int TILE_M = BM * kBK * 2, TILE_N = BN * kBK * 2;
+  constexpr int STAGE = TILE_M + TILE_N;  // bytes of one ring slot
+  static_assert(MODE != FWD_GU || NB % 2 == 0, "SwiGLU pairing needs gate and up blocks in every wave");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_info[8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int bid = blockIdx.x;
+  const int NT = p.N / BN;
+
+  // ---- device-side tile schedule ------------------------------------------------
+  if (wave == 0) {
+    int e_sel = -1, row0 = 0, row_end = 0, nt = 0, m0 = 0;
+    if constexpr (MODE == WGRAD) {
+      const int MT = p.M / BM;
+      const int R = p.E * MT * NT;
+      if (bid < R) {
+        const int q = R / 8, rmd = R % 8, x = bid % 8, i = bid / 8;
+        const int logical = x * q + min(x, rmd) + i;
+        e_sel = logical / (MT * NT);
+        const int rest = logical % (MT * NT);
+        m0 = (rest / NT) * BM;
+        nt = rest % NT;
+        row0 = p.offsets[e_sel];
+        row_end = p.offsets[e_sel + 1];
+      }
+    } else {
+      int tq[4], tsum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane * 4 + q;
+        const int n = (e < p.E) ? (p.offsets[e + 1] - p.offsets[e]) : 0;
+        tq[q] = (n + BM - 1) / BM;
+        tsum += tq[q];
+      }
+      const int excl = wave_exclusive_scan(tsum);
+      const int RM = __shfl(excl + tsum, 63, kWave);
+      const int R = RM * NT;
+      if (bid < R) {
+        // Each XCD (bid % 8) takes a contiguous range of tiles; inside it,
+        // groups of GM row tiles sweep the column tiles so concurrently
+        // running tiles share operands in that XCD's L2.
+        const int q = R / 8, rmd = R % 8, x = bid % 8, i = bid / 8;
+        const int logical = x * q + min(x, rmd) + i;
+        constexpr int GM = 8;
+        const int g = logical / (GM * NT);
+        const int gm = min(GM, RM - g * GM);
+        const int local = logical - g * GM * NT;
+        const int mt = g * GM + local % gm;
+        nt = local / gm;
+        int run = excl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = lane * 4 + q;
+          if (mt >= run && mt < run + tq[q]) {
+            e_sel = e;
+            row0 = p.offsets[e] + (mt - run) * BM;
+            row_end = p.offsets[e + 1];
+          }
+          run += tq[q];
+        }
+        const uint64_t who = __ballot(e_sel >= 0);
+        const int src = who ? __ffsll(static_cast<long long>(who)) - 1 : 0;
+        e_sel = __shfl(e_sel, src, kWave);
+        row0 = __shfl(row0, src, kWave);
+        row_end = __shfl(row_end, src, kWave);
+        if (!who) e_sel = -1;
+      }
+    }
+    if (lane == 0) {
+      s_info[0] = e_sel; s_info[1] = row0; s_info[2] = row_end; s_info[3] = nt; s_info[4] = m0;
+    }
+  }
+  __syncthreads();
+  // The tile coordinates are workgroup-uniform: keep them (and every address
+  // and buffer descriptor derived from them) in scalar registers.
+  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
+  if (e < 0) return;
+  const int row0 = __builtin_amdgcn_readfirstlane(s_info[1]);
+  const int row_end = __builtin_amdgcn_readfirstlane(s_info[2]);
+  const int nt = __builtin_amdgcn_readfirstlane(s_info[3]);
+  const int m0 = __builtin_amdgcn_readfirstlane(s_info[4]);
+  const int n0 = nt * BN;
+  const int nk = (MODE == WGRAD) ? (row_end - row0 + kBK - 1) / kBK : p.K / kBK;
+
+  const char* const A = static_cast<const char*>(p.a);
+  const int64_t bexp = static_cast<int64_t>(e) * p.bstride;
+
+  // ---- HBM -> LDS for slab kt ---------------------------------------------------------
+  // A slab at or past the end (kt == nk) gets empty descriptors: its loads
+  // read nothing and only zero-fill the LDS stage nobody reads again.
+  auto stage_m = [&](int kt, uint32_t dst) {
+    const bool live = kt < nk;
+    if constexpr (!M_MN) {
+      const char* base = A + (static_cast<int64_t>(row0) * p.lda + kt * kBK) * 2;
+      const int valid = live ? min(BM, row_end - row0) : 0;
+      stage_kmajor<BM>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, dst, wave, lane);
+    } else {
+      const int k0 = row0 + kt * kBK;
+      const char* base = A + (static_cast<int64_t>(k0) * p.lda + m0) * 2;
+      const int valid = live ? min(kBK, row_end - k0) : 0;
+      stage_mnmajor<BM>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, dst, wave, lane);
+    }
+  };
+  auto stage_n = [&](int kt, uint32_t dst) {
+    const bool live = kt < nk;
+    if constexpr (MODE == FWD_GU) {
+      // Two sub-tiles [64 k][BN/2]: gate columns then the same up columns.
+      const int fb = nt * (BN / 2);
+      const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + fb) * 2;
+      const int64_t bytes = live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0;
+      stage_mnmajor<BN / 2>(make_rsrc(static_cast<const char*>(p.b0) + off, bytes), p.ldb, dst, wave, lane);
+      stage_mnmajor<BN / 2>(make_rsrc(static_cast<const char*>(p.b1) + off, bytes), p.ldb, dst + TILE_N / 2, wave,
+                            lane);
+    } else if constexpr (MODE == FWD_DOWN) {
+      const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + n0) * 2;
+      const int64_t bytes = live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0;
+      stage_mnmajor<BN>(make_rsrc(static_cast<const char*>(p.b0) + off, bytes), p.ldb, dst, wave, lane);
+    } else if constexpr (MODE == WGRAD) {
+      const int k0 = row0 + kt * kBK;
+      const int valid = live ? min(kBK, row_end - k0) : 0;
+      stage_mnmajor<BN>(make_rsrc(static_cast<const char*>(p.b0) + (static_cast<int64_t>(k0) * p.ldb + n0) * 2,
+                                  static_cast<int64_t>(valid) * p.ldb * 2),
+                        p.ldb, dst, wave, lane);
+    } else {  // BWD_DOWN, BWD_GU: B stored [n][k]
+      const char* src = static_cast<const char*>(p.b0);
+      int kcol = kt * kBK;
+      if constexpr (MODE == BWD_GU) {
+        if (kcol >= p.f) { src = static_cast<const char*>(p.b1); kcol -= p.f; }
+      }
+      const char* base = src + (bexp + static_cast<int64_t>(n0) * p.ldb + kcol) * 2;
+      const int64_t bytes = live ? static_cast<int64_t>(BN) * p.ldb * 2 : 0;
+      stage_kmajor<BN>(make_rsrc(base, bytes), p.ldb, dst, wave, lane);
+    }
+  };
+
+  floatx16 acc[NB][MB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+  // Fragments of one 16-deep k step: MB from the M side, NB from the N side.
+  struct Frags {
+    bf16x8 m[MB], n[NB];
+  };
+  auto read_frags = [&](const char* tm, const char* tn, int kk, Frags& F) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      if constexpr (M_MN) F.m[i] = frag_mnmajor<BM>(tm, wm * WM + i * 32, kk, lane);
+      else F.m[i] = frag_kmajor(tm, wm * WM + i * 32, kk, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (MODE == FWD_GU) {
+        // Blocks [0, NB/2) are gate columns, [NB/2, NB) the same up columns.
+        const int half = j / (NB / 2), jj = j % (NB / 2);
+        F.n[j] = frag_mnmajor<BN / 2>(tn + half * (TILE_N / 2), wn * (WN / 2) + jj * 32, kk, lane);
+      } else if constexpr (N_MN) {
+        F.n[j] = frag_mnmajor<BN>(tn, wn * WN + j * 32, kk, lane);
+      } else {
+        F.n[j] = frag_kmajor(tn, wn * WN + j * 32, kk, lane);
+      }
+    }
+  };
+  auto mfma_all = [&](const Frags& F) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.n[j], F.m[i], acc[j][i], 0, 0, 0);
+  };
+  // LDS reads per k step and buffer loads per slab, for the schedule hints.
+  constexpr int kReads = MB * (M_MN ? 2 : 1) + NB * (N_MN ? 2 : 1);
+  constexpr int kMfma = MB * NB;
+  constexpr int kLoads = (BM + BN) / 64;  // per thread per slab
+
+  // ---- main loop -------------------------------------------------------------------------
+  // Ring of kStages = 4 slots, one slab (32 k) each; each slab is two 16-deep
+  // k steps. Iteration kt:
+  //   MFMAs of step 0 of slab kt, interleaved with the LDS reads of step 1;
+  //   wait until slab kt+1 has landed (slabs kt+2, kt+3 may still fly) and
+  //   barrier: everyone is done reading slot kt, and slab kt+1 is visible;
+  //   issue the loads of slab kt+4 into slot kt (empty past the end);
+  //   MFMAs of step 1 of slab kt, interleaved with the reads of step 0 of
+  //   slab kt+1.
+  // So the load of a slab has three slabs of MFMAs to land in, and no LDS
+  // read latency is exposed at slab boundaries.
+  static_assert(kStages == 4 && kBK == 32, "schedule written for a 4-slot ring of 2-step slabs");
+  auto interleave = [&]() {
+    constexpr int inter = kReads < kMfma ? kReads : kMfma;
+#pragma unroll
+    for (int r = 0; r < inter; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+    if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+  };
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+#pragma unroll
+  for (int s0 = 0; s0 < kStages; ++s0) {
+    stage_m(s0, ring + s0 * STAGE);
+    stage_n(s0, ring + s0 * STAGE + TILE_M);
+  }
+  Frags F[2];
+  wait_vmcnt<kLoads * (kStages - 1)>();
+  __syncthreads();
+  read_frags(smem, smem + TILE_M, 0, F[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* cur = smem + (kt % kStages) * STAGE;
+    const char* nxt = smem + ((kt + 1) % kStages) * STAGE;
+    read_frags(cur, cur + TILE_M, 1, F[1]);
+    mfma_all(F[0]);
+    interleave();
+    wait_vmcnt<kLoads * (kStages - 2)>();
+    __syncthreads();
+    const uint32_t slot = ring + (kt % kStages) * STAGE;
+    stage_m(kt + kStages, slot);
+    stage_n(kt + kStages, slot + TILE_M);
+    read_frags(nxt, nxt + TILE_M, 0, F[0]);
+    mfma_all(F[1]);
+    interleave();
+  }
+  // Drain the (empty) loads still in flight before the LDS is reused or the
+  // wave ends.
+  wait_vmcnt<0>();
+
+  // ---- epilogue ---------------------------------------------------------------------------
+  // acc[j][i] element r of lane l: n = wn*WN + 32 j + 8 (r/4) + 4 (l/32) + r%4,
+  // m = wm*WM + 32 i + l%32; four consecutive r are four consecutive columns.
+  // Outputs go through a per-wave LDS area in column groups of up to 64: the
+  // lanes put their 8-byte pieces into a [WM rows][64 cols] bf16 staging
+  // tile, then every store writes 128 contiguous bytes of a row. Saved inputs
+  // of the epilogue (G, U for BWD_DOWN) come in the same way by LDS DMA.
+  __syncthreads();  // every wave is done with the ring
+  const int hl = lane >> 5, l32 = lane & 31;
+  constexpr int kSlot = WM * 128;  // one staging tile: WM rows x 64 columns of bf16
+  char* const wa = smem + wave * 2 * kSlot;
+  // Chunk c (16 bytes) of staging row r lives at chunk c ^ ((r / 2) % 8).
+  auto st_off = [](int r, int col) {
+    return r * 128 + ((((col >> 3) ^ (r >> 1)) & 7) << 4) + ((col & 4) << 1);
+  };
+  auto put4 = [&](int slot, int r, int col, uint2 v) {
+    *reinterpret_cast<uint2*>(wa + slot * kSlot + st_off(r, col)) = v;
+  };
+  auto get4 = [&](int slot, int r, int col) -> uint2 {
+    return *reinterpret_cast<const uint2*>(wa + slot * kSlot + st_off(r, col));
+  };
+  auto wave_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+  };
+  // Rows [0, rows) and columns [0, cols) of staging tile `slot` -> global
+  // rows g + r*ld (bytes), 16 bytes per lane, 8 lanes per 128-byte row.
+  auto flush = [&](int slot, char* g, int64_t ld, int rows, int cols) {
+    wave_sync();
+    const int c = lane & 7;
+#pragma unroll 4
+    for (int t = 0; t < WM / 8; ++t) {
+      const int r = t * 8 + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4*>(wa + slot * kSlot + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
+      if (r < rows && c * 8 < cols) *reinterpret_cast<uint4*>(g + r * ld + c * 16) = v;
+    }
+    wave_sync();
+  };
+  const int mrow = (MODE == WGRAD ? m0 : row0) + wm * WM;   // first row of this wave's block
+  const int rows = (MODE == WGRAD) ? WM : max(0, min(WM, row_end - mrow));
+  auto acc4 = [&](int j, int i, int q) {
+    return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
+  };
+
+  if constexpr (MODE == FWD_GU) {
+    // Gate blocks [0, NB/2) and up blocks [NB/2, NB) cover the same NB*16 f-columns.
+    constexpr int GC = NB * 16;
+    const int col0 = nt * (BN / 2) + wn * (WN / 2);
+    const int64_t ld = p.ldc * 2;
+    char* G = static_cast<char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
+    char* U = static_cast<char*>(p.c1) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
+    char* H = static_cast<char*>(p.c2) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
+    // Pass 1: G and H (= silu(G) U) from the gate and up accumulators; pass 2: U.
+    static_for<MB>([&](auto I) {
+      static_for<NB / 2>([&](auto JJ) {
+        static_for<4>([&](auto Q) {
+          const int r = I * 32 + l32, col = JJ * 32 + 8 * Q + 4 * hl;
+          float h[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float g = acc[JJ][I][4 * Q + c], u = acc[JJ + NB / 2][I][4 * Q + c];
+            h[c] = g * sigmoid_f(g) * u;
+          }
+          put4(0, r, col, acc4(JJ, I, Q));
+          put4(1, r, col, pack4(h[0], h[1], h[2], h[3]));
+        });
+      });
+    });
+    flush(0, G, ld, rows, GC);
+    flush(1, H, ld, rows, GC);
+    static_for<MB>([&](auto I) {
+      static_for<NB / 2>([&](auto JJ) {
+        static_for<4>([&](auto Q) { put4(0, I * 32 + l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JJ + NB / 2, I, Q)); });
+      });
+    });
+    flush(0, U, ld, rows, GC);
+  } else if constexpr (MODE == BWD_DOWN) {
+    // dH -> dG = dH U sig(G) (1 + G (1 - sig(G))), dU = dH G sig(G); a row of
+    // dGU is [dG (f) | dU (f)]. Column groups of 64 (NB = 1: 32).
+    constexpr int GC = NB >= 2 ? 64 : 32;
+    constexpr int JG = NB >= 2 ? 2 : 1;  // 32-column blocks per group
+    const int64_t ld = p.ldc * 2, lds_ = static_cast<int64_t>(p.f) * 2;
+    static_for<NB / JG>([&](auto JP) {
+      const int col0 = n0 + wn * WN + JP * 64;
+      // Saved G, U of this group -> staging tiles 0, 1 (rows past the end read 0).
+      const int64_t sbase = (static_cast<int64_t>(mrow) * p.f + col0) * 2;
+      const int64_t sbytes = static_cast<int64_t>(rows) * p.f * 2;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const auto rs = make_rsrc(static_cast<const char*>(sl ? p.e1 : p.e0) + sbase, sbytes);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wa + sl * kSlot));
+#pragma unroll
+        for (int t = 0; t < WM / 8; ++t) {
+          const int r = t * 8 + (lane >> 3);
+          const int c = (lane & 7) ^ ((r >> 1) & 7);   // logical chunk held by this lane's slot
+          const uint32_t voff = (c * 8 < GC) ? static_cast<uint32_t>(r * lds_ + c * 16) : 0x80000000u;
+          load_lds16(rs, voff, dst + t * 1024);
+        }
+      }
+      wait_vmcnt<0>();
+      wave_sync();
+      static_for<MB>([&](auto I) {
+        static_for<JG>([&](auto JJ) {
+          static_for<4>([&](auto Q) {
+            constexpr int j = JP * JG + JJ;
+            const int r = I * 32 + l32, col = JJ * 32 + 8 * Q + 4 * hl;
+            float g[4], u[4], dg[4], du[4];
+            unpack4(get4(0, r, col), g);
+            unpack4(get4(1, r, col), u);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float dh = acc[j][I][4 * Q + c];
+              const float sg = sigmoid_f(g[c]);
+              du[c] = dh * g[c] * sg;
+              dg[c] = dh * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
+            }
+            put4(0, r, col, pack4(dg[0], dg[1], dg[2], dg[3]));
+            put4(1, r, col, pack4(du[0], du[1], du[2], du[3]));
+          });
+        });
+      });
+      char* C = static_cast<char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
+      flush(0, C, ld, rows, GC);
+      flush(1, C + static_cast<int64_t>(p.f) * 2, ld, rows, GC);
+    });
+  } else {
+    // FWD_DOWN, BWD_GU: C[row][n]; WGRAD: C[e][m][n], columns >= f of the
+    // gate|up weight gradient go to the second output (dw_up).
+    char* out = static_cast<char*>(p.c0);
+    int cn0 = n0;
+    if constexpr (MODE == WGRAD) {
+      if (p.c1 != nullptr && n0 >= p.f) { out = static_cast<char*>(p.c1); cn0 = n0 - p.f; }
+      out += static_cast<int64_t>(e) * p.cstride * 2;
+    }
+    constexpr int GC = NB >= 2 ? 64 : 32;
+    constexpr int JG = NB >= 2 ? 2 : 1;
+    const int64_t ld = p.ldc * 2;
+    static_for<NB / JG>([&](auto JP) {
+      static_for<MB>([&](auto I) {
+        static_for<JG>([&](auto JJ) {
+          static_for<4>([&](auto Q) {
+            put4(JP & 1, I * 32 + l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JP * JG + JJ, I, Q));
+          });
+        });
+      });
+      const int col0 = cn0 + wn * WN + JP * 64;
+      flush(JP & 1, out + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2, ld, rows, GC);
+    });
+  }
+}
+
+template <int MODE, int BM, int BN>
+hipError_t launch_tile(const GemmParams& p, int grid, hipStream_t s) {
+  // The ring, reused by the epilogue's per-wave staging (4 waves x 2 tiles of
+  // (BM/2) x 64 bf16).
+  constexpr int ring = kStages * (BM + BN) * kBK * 2, stage = 4 * 2 * (BM / 2) * 128;
+  constexpr int lds = ring > stage ? ring : stage;
+  auto kern = gg_bf16_kernel<MODE, BM, BN>;
+  static bool attr_set = false;  // benign race: idempotent attribute write
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
+
+// Grid bound for row-ragged modes: sum_e ceil(n_e/BM) <= ceil(S/BM) + E.
+int ragged_grid(int S, int E, int BM, int NT) {
+  return round8((static_cast<int64_t>((S + BM - 1) / BM) + E) * NT);
+}
+
+template <int MODE, int BM>
+hipError_t ragged_bn(const GemmParams& p, hipStream_t s) {
+  if (p.N % 256 == 0) return launch_tile<MODE, BM, 256>(p, ragged_grid(p.S, p.E, BM, p.N / 256), s);
+  if (p.N % 128 == 0) return launch_tile<MODE, BM, 128>(p, ragged_grid(p.S, p.E, BM, p.N / 128), s);
+  // N only a multiple of 64: narrow tiles (small shapes). FWD_GU has N = 2f,
+  // always a multiple of 128.
+  if constexpr (MODE != FWD_GU) return launch_tile<MODE, 128, 64>(p, ragged_grid(p.S, p.E, 128, p.N / 64), s);
+  return hipErrorInvalidValue;
+}
+
+template <int MODE>
+hipError_t ragged_mode(const GemmParams& p, hipStream_t s) {
+  // Experts with few rows each waste less of a 128-row tile.
+  if (static_cast<int64_t>(p.S) >= 1024LL * p.E) return ragged_bn<MODE, 256>(p, s);
+  return ragged_bn<MODE, 128>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_bf16_ragged(int mode, const GemmParams& p, hipStream_t s) {
+  switch (mode) {
+    case FWD_GU: {
+      // A 256-wide tile holds 128 gate + 128 up columns: needs f % 128 == 0.
+      if (p.f % 128 == 0) return ragged_mode<FWD_GU>(p, s);
+      if (static_cast<int64_t>(p.S) >= 1024LL * p.E)
+        return launch_tile<FWD_GU, 256, 128>(p, ragged_grid(p.S, p.E, 256, p.N / 128), s);
+      return launch_tile<FWD_GU, 128, 128>(p, ragged_grid(p.S, p.E, 128, p.N / 128), s);
+    }
+    case FWD_DOWN: return ragged_mode<FWD_DOWN>(p, s);
+    case BWD_DOWN: return ragged_mode<BWD_DOWN>(p, s);
+    case BWD_GU: return ragged_mode<BWD_GU>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bf16_wgrad(const GemmParams& p, hipStream_t s) {
+  // A column tile must not straddle the gate|up split at column f.
+  const int nsplit = p.c1 ? p.f : p.N;
+  const bool m256 = p.M % 256 == 0, n256 = p.N % 256 == 0 && nsplit % 256 == 0;
+  const bool m128 = p.M % 128 == 0, n128 = p.N % 128 == 0 && nsplit % 128 == 0;
+  auto grid = [&](int bm, int bn) { return round8(static_cast<int64_t>(p.E) * (p.M / bm) * (p.N / bn)); };
+  if (m256 && n256) return launch_tile<WGRAD, 256, 256>(p, grid(256, 256), s);
+  if (m256 && n128) return launch_tile<WGRAD, 256, 128>(p, grid(256, 128), s);
+  if (m128 && n256) return launch_tile<WGRAD, 128, 256>(p, grid(128, 256), s);
+  if (m128 && n128) return launch_tile<WGRAD, 128, 128>(p, grid(128, 128), s);
+  // Dimensions only multiples of 64: narrow tiles (small shapes).
+  if (m128) return launch_tile<WGRAD, 128, 64>(p, grid(128, 64), s);
+  if (n128) return launch_tile<WGRAD, 64, 128>(p, grid(64, 128), s);
+  return launch_tile<WGRAD, 64, 64>(p, grid(64, 64), s);
+}
+
+}  // namespace moe

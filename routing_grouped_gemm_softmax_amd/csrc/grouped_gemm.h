@@ -1,0 +1,42 @@
+// Parameters of the device-scheduled grouped GEMMs of the expert SwiGLU FFN,
+// shared by the fp32 kernel (gemm.hip) and the bf16 kernel (gemm_bf16.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// FWD_GU   [G|U|H] = SwiGLU(xp W_gate, xp W_up)       rows ragged by expert
+// FWD_DOWN o = H W_down                                rows ragged
+// BWD_DOWN dGU = SwiGLU'(dO W_down^T; saved G, U)      rows ragged
+// BWD_GU   dxp = [dG|dU] [W_gate|W_up]^T  (K = 2f)     rows ragged
+// WGRAD    dW[e] = X_e^T Y_e                           K = rows of expert e
+enum GemmMode { FWD_GU = 0, FWD_DOWN = 1, BWD_DOWN = 2, BWD_GU = 3, WGRAD = 4 };
+
+struct GemmParams {
+  const void* a;      // A operand
+  int64_t lda;
+  const void* b0;     // B operand (first source)
+  const void* b1;     // second source (w_up for FWD_GU / BWD_GU)
+  int64_t ldb;
+  int64_t bstride;    // elements between experts in b0/b1 (0 for WGRAD)
+  void* c0;           // outputs
+  void* c1;
+  void* c2;
+  int64_t ldc;
+  const void* e0;     // epilogue inputs (BWD_DOWN: saved G, U)
+  const void* e1;
+  const int32_t* offsets;
+  int E, S;
+  int M;              // WGRAD: rows of each weight gradient
+  int N, K;           // logical N (FWD_GU: 2f) and K (ragged modes)
+  int f;              // split point: FWD_GU/BWD_GU/WGRAD(gate|up)
+  int cstride;        // WGRAD: elements between experts in c0/c1
+};
+
+// bf16 grouped GEMMs (gemm_bf16.hip).
+hipError_t launch_bf16_ragged(int mode, const GemmParams& p, hipStream_t s);
+hipError_t launch_bf16_wgrad(const GemmParams& p, hipStream_t s);
+
+}  // namespace moe
