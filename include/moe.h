@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum moe_status {
   MOE_OK = 0,
@@ -122,12 +122,14 @@ size_t moe_save_size(const moe_shape* shape);
  * equal values to the lower expert index, written to topk_idx[T][k];
  * topk_gate[T][k] (fp32) = softmax over the k chosen logits, which equals the
  * full softmax renormalised over the chosen set.
+ * ws: moe_workspace_size(MOE_OP_ROUTE) bytes (bf16 layers: a transposed copy
+ * of w_router; 0 for fp32 layers, where ws may be NULL).
  * Passage: noticiarioia.com page, "Mudança de arquitetura e ganhos de
  * desempenho" (4 of E experts per token); bytechap.com page, "Cómo funciona"
  * (routing kept on the GPU). */
 int moe_route(const void* x, const void* w_router, const moe_shape* shape,
               float* logits_out, int32_t* topk_idx_out, float* topk_gate_out,
-              void* stream);
+              void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch: counts[E] = rows per expert, offsets[E+1] = exclusive prefix sum
  * (offsets[E] = S), all computed on the device. Expert e's rows are

@@ -52,7 +52,7 @@ SIGNATURES = {
     "moe_last_error_message": (ctypes.c_char_p, []),
     "moe_workspace_size": (_SZ, [ctypes.c_int, _SHAPE]),
     "moe_save_size": (_SZ, [_SHAPE]),
-    "moe_route": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P]),
+    "moe_route": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _SZ, _P]),
     "moe_dispatch": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_read_device_status": (ctypes.c_int, [_P, _P]),
     "moe_grouped_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _SHAPE, _P, _SZ, _P, _P, _SZ, _P]),
@@ -103,6 +103,11 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+def _nbytes(t) -> int:
+    """Size in bytes of an optional workspace tensor (0 for None)."""
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -130,13 +135,13 @@ def save_size(shape: MoeShape) -> int:
     return n
 
 
-def moe_route(x, w_router, shape, logits, topk_idx, topk_gate, stream=None):
+def moe_route(x, w_router, shape, logits, topk_idx, topk_gate, ws=None, stream=None):
     T, E, k = shape.T, shape.E, shape.k
     _expect(logits, torch.float32, T * E, "logits")
     _expect(topk_idx, torch.int32, T * k, "topk_idx")
     _expect(topk_gate, torch.float32, T * k, "topk_gate")
     _check("moe_route", load().moe_route(_ptr(x), _ptr(w_router), ctypes.byref(shape), _ptr(logits),
-                                         _ptr(topk_idx), _ptr(topk_gate), _stream(stream)))
+                                         _ptr(topk_idx), _ptr(topk_gate), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_dispatch(x, topk_idx, shape, counts, offsets, row_of_slot, token_of_row, xp, ws, stream=None):

@@ -102,11 +102,12 @@ size_t moe_workspace_size(int op, const moe_shape* s) {
   if (check_shape(s) != MOE_OK) return (size_t)-1;
   const int T = (int)s->T, d = (int)s->d, E = (int)s->E, f = (int)s->f, k = (int)s->k;
   switch (op) {
-    case MOE_OP_ROUTE: return 0;
+    case MOE_OP_ROUTE: return s->dtype == MOE_F32 ? 0 : moe::route_bf16_workspace(d, E);
     case MOE_OP_DISPATCH: return moe::dispatch_workspace(T, E);
     case MOE_OP_FFN_FWD: return 0;
     case MOE_OP_FFN_BWD: return (size_t)T * k * 2 * f * elem_bytes(s->dtype);  // dG|dU rows
-    case MOE_OP_ROUTE_BWD: return moe::route_bwd_workspace(T, d, E);
+    case MOE_OP_ROUTE_BWD:
+      return s->dtype == MOE_F32 ? moe::route_bwd_workspace(T, d, E) : moe::route_bwd_bf16_workspace(T, d, E);
     case MOE_OP_DISPATCH_BWD: return moe::dispatch_bwd_workspace(d, E, s->dtype == MOE_F32);
     default: fail(MOE_ERR_INVALID_ARG, "unknown op %d", op); return (size_t)-1;
   }
@@ -118,11 +119,20 @@ size_t moe_save_size(const moe_shape* s) {
 }
 
 int moe_route(const void* x, const void* w_router, const moe_shape* s, float* logits_out, int32_t* topk_idx_out,
-              float* topk_gate_out, void* stream) {
+              float* topk_gate_out, void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_shape(s));
   NEED(x); NEED(w_router); NEED(logits_out); NEED(topk_idx_out); NEED(topk_gate_out);
-  LAUNCH(moe::launch_route(x, w_router, s->dtype == MOE_F32, (int)s->T, (int)s->d, (int)s->E, (int)s->k, logits_out,
-                           topk_idx_out, topk_gate_out, as_stream(stream)));
+  const size_t need = moe_workspace_size(MOE_OP_ROUTE, s);
+  if (need) {
+    NEED(ws);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu bytes", ws_bytes, need);
+  }
+  if (s->dtype == MOE_F32)
+    LAUNCH(moe::launch_route(x, w_router, true, (int)s->T, (int)s->d, (int)s->E, (int)s->k, logits_out,
+                             topk_idx_out, topk_gate_out, as_stream(stream)));
+  else
+    LAUNCH(moe::launch_route_bf16(x, w_router, (int)s->T, (int)s->d, (int)s->E, (int)s->k, logits_out, topk_idx_out,
+                                  topk_gate_out, ws, as_stream(stream)));
   return MOE_OK;
 }
 
@@ -214,10 +224,14 @@ int moe_route_bwd(const void* x, const void* w_router, const int32_t* topk_idx, 
   (void)w_router;
   CHECK(check_shape(s));
   NEED(x); NEED(topk_idx); NEED(topk_gate); NEED(dgate); NEED(dlogits_out); NEED(dw_router_out); NEED(ws);
-  const size_t need = moe::route_bwd_workspace((int)s->T, (int)s->d, (int)s->E);
+  const size_t need = moe_workspace_size(MOE_OP_ROUTE_BWD, s);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route_bwd: workspace %zu < %zu bytes", ws_bytes, need);
-  LAUNCH(moe::launch_route_bwd(x, topk_idx, topk_gate, dgate, s->dtype == MOE_F32, (int)s->T, (int)s->d, (int)s->E,
-                               (int)s->k, dlogits_out, dw_router_out, ws, as_stream(stream)));
+  if (s->dtype == MOE_F32)
+    LAUNCH(moe::launch_route_bwd(x, topk_idx, topk_gate, dgate, true, (int)s->T, (int)s->d, (int)s->E, (int)s->k,
+                                 dlogits_out, dw_router_out, ws, as_stream(stream)));
+  else
+    LAUNCH(moe::launch_route_bwd_bf16(x, topk_idx, topk_gate, dgate, (int)s->T, (int)s->d, (int)s->E, (int)s->k,
+                                      dlogits_out, dw_router_out, ws, as_stream(stream)));
   return MOE_OK;
 }
 

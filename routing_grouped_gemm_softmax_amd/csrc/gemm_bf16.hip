@@ -44,9 +44,15 @@ typedef __attribute__((address_space(3))) v4s lds_v4s_t;
 constexpr int kBK = 32;     // K elements per slab (64 bytes of bf16)
 constexpr int kStages = 4;  // LDS ring depth: slabs kt+1..kt+3 fly while kt is multiplied
 
+// Buffer descriptor over [base, base + bytes) (out-of-range loads read 0),
+// built from wave-uniform values so it lives in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), 0x00020000);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, n,
+                                           0x00020000);
 }
 
 // One 16-byte load per lane into LDS: lane i writes lds_wave + 16 i (lds_wave

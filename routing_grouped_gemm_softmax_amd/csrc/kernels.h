@@ -38,6 +38,15 @@ hipError_t launch_route_bwd(const void* x, const int32_t* topk_idx, const float*
                             const float* dgate, bool is_f32, int T, int d, int E, int k,
                             float* dlogits, void* dw_router, void* ws, hipStream_t s);
 
+// bf16 router on the matrix cores (route_bf16.hip)
+size_t route_bf16_workspace(int d, int E);
+hipError_t launch_route_bf16(const void* x, const void* w_router, int T, int d, int E, int k, float* logits,
+                             int32_t* topk_idx, float* topk_gate, void* ws, hipStream_t s);
+size_t route_bwd_bf16_workspace(int T, int d, int E);
+hipError_t launch_route_bwd_bf16(const void* x, const int32_t* topk_idx, const float* topk_gate, const float* dgate,
+                                 int T, int d, int E, int k, float* dlogits, void* dw_router, void* ws,
+                                 hipStream_t s);
+
 // Dispatch / combine (dispatch.hip)
 size_t dispatch_workspace(int T, int E);
 hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d,

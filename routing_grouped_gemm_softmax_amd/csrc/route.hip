@@ -16,6 +16,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -122,9 +123,7 @@ __global__ __launch_bounds__(256) void narrow_gemm_kernel(const TA* __restrict__
   }
 }
 
-// One wave per token: k rounds of a wave-wide arg-max over the logits (larger
-// value wins, equal values go to the lower index), then the gates
-// g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), l_0 being the largest logit.
+// One wave per token: top-k and gates of the logits (topk.h).
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
   const int lane = threadIdx.x & 63;
@@ -138,39 +137,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     live[q] = e < E;
     v[q] = live[q] ? logits[static_cast<int64_t>(t) * E + e] : 0.0f;
   }
-  float sel_v[8];
+  float sel_v[8], g[8];
   int sel_i[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {  // fully unrolled so sel_v/sel_i stay in registers
-    if (j >= k) break;
-    float bv = 0.0f;
-    int bi = -1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)  // ascending index inside the lane; strict > keeps the lower index
-      if (live[q] && (bi < 0 || v[q] > bv)) { bv = v[q]; bi = q * 64 + lane; }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const bool take = (oi >= 0) && (bi < 0 || ov > bv || (ov == bv && oi < bi));
-      if (take) { bv = ov; bi = oi; }
-    }
-    sel_v[j] = bv;
-    sel_i[j] = bi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q == (bi >> 6) && (bi & 63) == lane) live[q] = false;
-  }
-  if (lane == 0) {
-    float ex[8], sum = 0.0f;
+  wave_topk(v, live, k, lane, sel_v, sel_i);
+  topk_gates(sel_v, k, g);
+  if (lane < k) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < k) { ex[j] = expf(sel_v[j] - sel_v[0]); sum += ex[j]; }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) {
+      if (j == lane) {
         topk_idx[static_cast<int64_t>(t) * k + j] = sel_i[j];
-        topk_gate[static_cast<int64_t>(t) * k + j] = ex[j] / sum;
+        topk_gate[static_cast<int64_t>(t) * k + j] = g[j];
       }
   }
 }

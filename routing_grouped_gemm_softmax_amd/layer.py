@@ -32,6 +32,7 @@ class MoELayer:
 
         # forward
         self.logits = buf(T, E, dtype=f32) if learned_routing else None
+        self.ws_route = ws(L.MOE_OP_ROUTE) if learned_routing else None
         self.topk_idx = buf(T, k, dtype=i32)
         self.topk_gate = buf(T, k, dtype=f32)
         self.counts = buf(E, dtype=i32)
@@ -72,7 +73,7 @@ class MoELayer:
         mark = mark or (lambda name: None)
         self.x, self.w_gate, self.w_up, self.w_down, self.w_router = x, w_gate, w_up, w_down, w_router
         if self.learned:
-            L.moe_route(x, w_router, s, self.logits, self.topk_idx, self.topk_gate, stream)
+            L.moe_route(x, w_router, s, self.logits, self.topk_idx, self.topk_gate, self.ws_route, stream)
             mark("moe_route")
         else:
             self.topk_idx.copy_(topk_idx)

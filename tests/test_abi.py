@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
                        (-3, b"MOE_ERR_MISALIGNED"), (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == name
@@ -70,7 +70,7 @@ def test_workspace_queries():
 def test_shape_validation(bad, code):
     s = shape(**bad)
     fake = ctypes.c_void_p(0x100000)
-    rc = L.load().moe_route(fake, fake, ctypes.byref(s), fake, fake, fake, None)
+    rc = L.load().moe_route(fake, fake, ctypes.byref(s), fake, fake, fake, fake, 1 << 30, None)
     assert rc == code, L.last_error()
     assert L.last_error()
 
@@ -79,9 +79,9 @@ def test_null_and_misaligned_pointers():
     lib = L.load()
     s = shape()
     ok = ctypes.c_void_p(0x100000)
-    assert lib.moe_route(None, ok, ctypes.byref(s), ok, ok, ok, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, ok, ctypes.byref(s), ok, ok, ok, ok, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
     assert "x is NULL" in L.last_error()
-    assert lib.moe_route(ctypes.c_void_p(0x100008), ok, ctypes.byref(s), ok, ok, ok, None) == L.MOE_ERR_MISALIGNED
+    assert lib.moe_route(ctypes.c_void_p(0x100008), ok, ctypes.byref(s), ok, ok, ok, ok, 1 << 30, None) == L.MOE_ERR_MISALIGNED
     assert lib.moe_combine(ok, ok, None, ctypes.byref(s), ok, None) == L.MOE_ERR_INVALID_ARG
     rc = lib.moe_dispatch_bwd(ok, ok, ok, None, ctypes.byref(s), ok, None, 0, None)
     assert rc == L.MOE_ERR_INVALID_ARG  # dlogits without w_router
@@ -103,6 +103,10 @@ def test_workspace_too_small():
     assert rc == L.MOE_ERR_WORKSPACE
     rc = lib.moe_route_bwd(p, p, p, p, p, ctypes.byref(s), p, p, p, 0, None)
     assert rc == L.MOE_ERR_WORKSPACE
+    sb = shape(dtype="bf16")
+    rc = lib.moe_route(p, p, ctypes.byref(sb), p, p, p, p, 16, None)  # bf16 router needs W_r^T space
+    assert rc == L.MOE_ERR_WORKSPACE
+    assert L.workspace_size(L.MOE_OP_ROUTE, s) == 0 and L.workspace_size(L.MOE_OP_ROUTE, sb) == 16 * 64 * 2
 
 
 def test_mxfp8_layer_gemm_reported_unsupported():
