@@ -246,8 +246,9 @@ def dispatch_backward(dxp, row_of_slot, dx_router=None) -> np.ndarray:
 # Whole layer.
 # --------------------------------------------------------------------------
 
-def layer_forward(inp: dict, k: int, logits=None) -> dict:
+def layer_forward(inp: dict, k: int, logits=None, mx: bool = False) -> dict:
     """Forward pass on an input dict (keys as produced by moe_inputs).
+    mx=True uses the MXFP8 expert FFN (ffn_forward_mx).
 
     Learned routing uses x W_r, unless ``logits`` is given: then the top-k
     sets and gates are computed from those values (widened exactly), which is
@@ -264,19 +265,22 @@ def layer_forward(inp: dict, k: int, logits=None) -> dict:
         idx, gates = np.asarray(inp["topk_idx"], dtype=np.int32), _f64(inp["topk_gate"])
     counts, offsets, row_of_slot, token_of_row = dispatch_plan(idx, E)
     xp = gather_rows(x, token_of_row)
-    G, U, H, O = ffn_forward(xp, inp["w_gate"], inp["w_up"], inp["w_down"], offsets)
+    ffn = ffn_forward_mx if mx else ffn_forward
+    G, U, H, O = ffn(xp, inp["w_gate"], inp["w_up"], inp["w_down"], offsets)
     out.update(topk_idx=idx, gates=gates, counts=counts, offsets=offsets,
                row_of_slot=row_of_slot, token_of_row=token_of_row,
                xp=xp, G=G, U=U, H=H, O=O, y=combine(O, gates, row_of_slot))
     return out
 
 
-def layer_backward(inp: dict, fwd: dict, dy=None) -> dict:
-    """Backward pass given the forward's saved values; dy defaults to inp['dy']."""
+def layer_backward(inp: dict, fwd: dict, dy=None, mx: bool = False) -> dict:
+    """Backward pass given the forward's saved values; dy defaults to inp['dy'].
+    mx=True uses the MXFP8 expert FFN backward (ffn_backward_mx)."""
     dy = _f64(inp["dy"] if dy is None else dy)
     d_o, dgate = combine_backward(dy, fwd["O"], fwd["gates"], fwd["row_of_slot"])
-    dxp, dwg, dwu, dwd, dG, dU = ffn_backward(d_o, fwd["xp"], inp["w_gate"], inp["w_up"],
-                                              inp["w_down"], fwd["offsets"], fwd["G"], fwd["U"], fwd["H"])
+    ffn = ffn_backward_mx if mx else ffn_backward
+    dxp, dwg, dwu, dwd, dG, dU = ffn(d_o, fwd["xp"], inp["w_gate"], inp["w_up"],
+                                     inp["w_down"], fwd["offsets"], fwd["G"], fwd["U"], fwd["H"])
     out = dict(dO=d_o, dgate=dgate, dXp=dxp, dG=dG, dU=dU,
                dw_gate=dwg, dw_up=dwu, dw_down=dwd)
     dx_router = None
@@ -383,3 +387,105 @@ def mx_dequantize(codes, scales, along: str = "cols") -> np.ndarray:
     R, C = v.shape
     return (v.reshape(R, C // MX_BLOCK, MX_BLOCK)
             * e8m0_decode(scales)[:, :, None]).reshape(R, C)
+
+
+# --------------------------------------------------------------------------
+# MXFP8 expert FFN: every grouped-GEMM operand quantised along that GEMM's K.
+# The pages only say that MXFP8 is used for the expert computation and the
+# data moved between experts ([P1] "Otimizações e testes em escala de
+# trilhões"; [P3] "Parallelismo, precisione e tecniche di memoria"). Reading
+# taken: every operand of every grouped GEMM of the forward and the backward
+# is quantised in blocks of 32 along that GEMM's reduction axis; products are
+# then exact on the dequantised values (accumulation in fp64 here). For the
+# weight gradients the reduction runs over one expert's tokens, so those
+# operands are blocked along the rows inside each expert's range, the range
+# zero-padded to a multiple of 32. Elementwise steps (SwiGLU and its
+# derivative) use the unquantised GEMM results.
+# --------------------------------------------------------------------------
+
+def mx_roundtrip(a, along: str) -> np.ndarray:
+    """Exact fp64 value of a after MXFP8 quantisation in blocks of 32 along
+    `along` ("cols": inside a row; "rows": down a column)."""
+    q, s = mx_quantize(a, along)
+    return mx_dequantize(q, s, along)
+
+
+def mx_rows_grouped(a, offsets) -> np.ndarray:
+    """mx_roundtrip along rows, blocked separately inside every row range
+    [offsets[e], offsets[e+1]), each range zero-padded to a multiple of 32."""
+    a = _f64(a)
+    out = np.zeros_like(a)
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if lo == hi:
+            continue
+        n = hi - lo
+        pad = np.zeros(((n + MX_BLOCK - 1) // MX_BLOCK * MX_BLOCK, a.shape[1]))
+        pad[:n] = a[lo:hi]
+        out[lo:hi] = mx_roundtrip(pad, "rows")[:n]
+    return out
+
+
+def ffn_forward_mx(xp, w_gate, w_up, w_down, offsets, h_in=None):
+    """ffn_forward with MXFP8 GEMM operands: Xp and H along the row (K = d,
+    f), W_gate, W_up along d and W_down along f (down their columns).
+    h_in, if given, is the H that the down GEMM quantises (a device stores H
+    in bf16 before quantising it; comparing stage by stage feeds that H).
+    Returns (G, U, H, O)."""
+    E = len(offsets) - 1
+    xq = mx_roundtrip(xp, "cols")
+    S, f = xq.shape[0], np.shape(w_gate)[2]
+    G = np.zeros((S, f)); U = np.zeros((S, f)); H = np.zeros((S, f))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        G[a:b] = xq[a:b] @ mx_roundtrip(w_gate[e], "rows")
+        U[a:b] = xq[a:b] @ mx_roundtrip(w_up[e], "rows")
+        H[a:b] = G[a:b] * sigmoid(G[a:b]) * U[a:b]
+    hq = mx_roundtrip(H if h_in is None else h_in, "cols")
+    O = np.zeros((S, np.shape(w_down)[2]))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a < b:
+            O[a:b] = hq[a:b] @ mx_roundtrip(w_down[e], "rows")
+    return G, U, H, O
+
+
+def ffn_backward_mx(d_o, xp, w_gate, w_up, w_down, offsets, G, U, H, dgdu_in=None):
+    """ffn_backward with MXFP8 GEMM operands, each along its GEMM's K:
+    dH = q(dO) q(W_down)^T (both along d); dXp = q(dG) q(W_gate)^T +
+    q(dU) q(W_up)^T (along f); dW_down = q(H)^T q(dO), dW_gate = q(Xp)^T
+    q(dG), dW_up = q(Xp)^T q(dU), each along the expert's tokens.
+    dgdu_in, if given, is the (dG, dU) pair that the later GEMMs quantise
+    (for a stage-by-stage comparison with a device that stores them in bf16).
+    Returns (dXp, dW_gate, dW_up, dW_down, dG, dU)."""
+    E = len(offsets) - 1
+    S, d = np.shape(xp)
+    f = np.shape(w_gate)[2]
+    doq = mx_roundtrip(d_o, "cols")
+    dG = np.zeros((S, f)); dU = np.zeros((S, f))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        g, u = _f64(G[a:b]), _f64(U[a:b])
+        s = sigmoid(g)
+        dh = doq[a:b] @ mx_roundtrip(w_down[e], "cols").T
+        dU[a:b] = dh * g * s
+        dG[a:b] = dh * u * s * (1.0 + g * (1.0 - s))
+    dg_in, du_in = (dG, dU) if dgdu_in is None else dgdu_in
+    dgq, duq = mx_roundtrip(dg_in, "cols"), mx_roundtrip(du_in, "cols")
+    hg, dog = mx_rows_grouped(H, offsets), mx_rows_grouped(d_o, offsets)
+    xg, dgg, dug = mx_rows_grouped(xp, offsets), mx_rows_grouped(dg_in, offsets), mx_rows_grouped(du_in, offsets)
+    dxp = np.zeros((S, d))
+    dwg = np.zeros((E, d, f)); dwu = np.zeros((E, d, f)); dwd = np.zeros((E, f, np.shape(w_down)[2]))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        dxp[a:b] = dgq[a:b] @ mx_roundtrip(w_gate[e], "cols").T + duq[a:b] @ mx_roundtrip(w_up[e], "cols").T
+        dwd[e] = hg[a:b].T @ dog[a:b]
+        dwg[e] = xg[a:b].T @ dgg[a:b]
+        dwu[e] = xg[a:b].T @ dug[a:b]
+    return dxp, dwg, dwu, dwd, dG, dU
