@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["route.hip", "route_bf16.hip", "dispatch.hip", "gemm.hip", "gemm_bf16.hip", "mxfp8.hip", "abi.cpp"]
+SOURCES = ["route.hip", "route_bf16.hip", "dispatch.hip", "gemm.hip", "gemm_bf16.hip", "gemm_mx.hip",
+           "ffn_mx.hip", "mxfp8.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

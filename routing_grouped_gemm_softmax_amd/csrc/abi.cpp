@@ -50,9 +50,12 @@ int check_shape(const moe_shape* s) {
   return MOE_OK;
 }
 
-// The bf16 path serves MXFP8 layers' master tensors until the scaled GEMM exists.
-int check_dense_dtype(const moe_shape* s, const char* who) {
-  if (s->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "%s: MOE_MXFP8 grouped GEMM is not available", who);
+// MXFP8 layers run the grouped GEMMs on E4M3 operands whose slabs are 128
+// bytes of K per 32-row block pair; the quantised layouts need d and f to be
+// multiples of 128.
+int check_ffn_dtype(const moe_shape* s, const char* who) {
+  if (s->dtype == MOE_MXFP8 && (s->d % 128 || s->f % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: MXFP8 layers need d and f to be multiples of 128", who);
   return MOE_OK;
 }
 
@@ -104,8 +107,12 @@ size_t moe_workspace_size(int op, const moe_shape* s) {
   switch (op) {
     case MOE_OP_ROUTE: return s->dtype == MOE_F32 ? 0 : moe::route_bf16_workspace(d, E);
     case MOE_OP_DISPATCH: return moe::dispatch_workspace(T, E);
-    case MOE_OP_FFN_FWD: return 0;
-    case MOE_OP_FFN_BWD: return (size_t)T * k * 2 * f * elem_bytes(s->dtype);  // dG|dU rows
+    case MOE_OP_FFN_FWD:
+      return s->dtype == MOE_MXFP8 ? moe::ffn_mx_fwd_workspace(T * k, d, f, E) : 0;
+    case MOE_OP_FFN_BWD: {
+      const size_t dgu = ((size_t)T * k * 2 * f * elem_bytes(s->dtype) + 255) & ~(size_t)255;  // dG|dU rows
+      return dgu + (s->dtype == MOE_MXFP8 ? moe::ffn_mx_bwd_workspace(T * k, d, f, E) : 0);
+    }
     case MOE_OP_ROUTE_BWD:
       return s->dtype == MOE_F32 ? moe::route_bwd_workspace(T, d, E) : moe::route_bwd_bf16_workspace(T, d, E);
     case MOE_OP_DISPATCH_BWD: return moe::dispatch_bwd_workspace(d, E, s->dtype == MOE_F32);
@@ -163,10 +170,14 @@ int moe_read_device_status(const void* ws, void* stream) {
 int moe_grouped_ffn_fwd(const void* xp, const void* w_gate, const void* w_up, const void* w_down,
                         const int32_t* offsets, const moe_shape* s, void* save, size_t save_bytes, void* o_out,
                         void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   CHECK(check_shape(s));
-  CHECK(check_dense_dtype(s, "moe_grouped_ffn_fwd"));
+  CHECK(check_ffn_dtype(s, "moe_grouped_ffn_fwd"));
   NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(save); NEED(o_out);
+  const size_t need = moe_workspace_size(MOE_OP_FFN_FWD, s);
+  if (need) {
+    NEED(ws);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
+  }
   if (save_bytes < save_bytes_for(s))
     return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_fwd: save buffer %zu < %zu bytes", save_bytes, save_bytes_for(s));
   moe::FfnArgs a{};
@@ -175,7 +186,10 @@ int moe_grouped_ffn_fwd(const void* xp, const void* w_gate, const void* w_up, co
   const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
   a.G = save; a.U = static_cast<char*>(save) + plane; a.H = static_cast<char*>(save) + 2 * plane;
   a.o = o_out;
-  LAUNCH(moe::launch_ffn_fwd(a, s->dtype == MOE_F32, as_stream(stream)));
+  if (s->dtype == MOE_MXFP8)
+    LAUNCH(moe::launch_ffn_mx_fwd(a, ws, as_stream(stream)));
+  else
+    LAUNCH(moe::launch_ffn_fwd(a, s->dtype == MOE_F32, as_stream(stream)));
   return MOE_OK;
 }
 
@@ -202,7 +216,7 @@ int moe_grouped_ffn_bwd(const void* d_o, const void* xp, const void* w_gate, con
                         void* dw_gate_out, void* dw_up_out, void* dw_down_out, void* ws, size_t ws_bytes,
                         void* stream) {
   CHECK(check_shape(s));
-  CHECK(check_dense_dtype(s, "moe_grouped_ffn_bwd"));
+  CHECK(check_ffn_dtype(s, "moe_grouped_ffn_bwd"));
   NEED(d_o); NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(save); NEED(dxp_out);
   NEED(dw_gate_out); NEED(dw_up_out); NEED(dw_down_out); NEED(ws);
   const size_t need = moe_workspace_size(MOE_OP_FFN_BWD, s);
@@ -214,7 +228,12 @@ int moe_grouped_ffn_bwd(const void* d_o, const void* xp, const void* w_gate, con
   char* sv = const_cast<char*>(static_cast<const char*>(save));
   a.G = sv; a.U = sv + plane; a.H = sv + 2 * plane;
   a.d_o = d_o; a.dgu = ws; a.dxp = dxp_out; a.dw_gate = dw_gate_out; a.dw_up = dw_up_out; a.dw_down = dw_down_out;
-  LAUNCH(moe::launch_ffn_bwd(a, s->dtype == MOE_F32, as_stream(stream)));
+  if (s->dtype == MOE_MXFP8) {
+    const size_t dgu = ((size_t)a.S * 2 * a.f * 2 + 255) & ~(size_t)255;
+    LAUNCH(moe::launch_ffn_mx_bwd(a, static_cast<char*>(ws) + dgu, as_stream(stream)));
+  } else {
+    LAUNCH(moe::launch_ffn_bwd(a, s->dtype == MOE_F32, as_stream(stream)));
+  }
   return MOE_OK;
 }
 

@@ -1,0 +1,183 @@
+// MXFP8 expert FFN, forward and backward: quantise every grouped-GEMM operand
+// along that GEMM's K into the MX GEMM's layout, then run the grouped GEMMs.
+//
+// The pages use MXFP8 for the expert computation ("Olmo-core 3 é lançado com
+// infraestrutura para treinar modelos MoE", section "Otimizações e testes em
+// escala de trilhões"; "Ai2 rilascia Olmo-Core 3...", section "Parallelismo,
+// precisione e tecniche di memoria"). The layer's bf16 tensors stay the
+// masters (G, U, H, O, dGU, dXp and the weight gradients are bf16); each GEMM
+// consumes E4M3 copies with one E8M0 scale per 32 elements along its K:
+//   forward   G,U = q(Xp) q(W_gate), q(W_up)   K = d  (weights transposed)
+//             O   = q(H) q(W_down)              K = f  (weight transposed)
+//   dgrad     dGU = SwiGLU'(q(dO) q(W_down)^T)  K = d
+//             dXp = q(dGU) q([W_gate|W_up])^T   K = 2f
+//   wgrad     dW_down = q(H)^T q(dO), [dW_gate|dW_up] = q(Xp)^T q(dGU), K =
+//             an expert's tokens, each expert's range padded to 64 rows.
+#include "common.h"
+#include "grouped_gemm.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+size_t a256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+// Bump allocator over the caller's workspace: 256-byte aligned pieces, each
+// with 16 bytes of slack (a scale tile of a ragged row range is read up to the
+// next whole dword).
+struct Carve {
+  char* p;
+  size_t used = 0;
+  uint8_t* take(size_t n) {
+    uint8_t* r = reinterpret_cast<uint8_t*>(p + used);
+    used += a256(n + 16);
+    return r;
+  }
+};
+
+int64_t padded_rows(int S, int E) { return (static_cast<int64_t>(S) + 63LL * E + 63) / 64 * 64; }
+
+struct FwdWs {
+  uint8_t *xq, *xs, *wgq, *wgs, *wuq, *wus, *hq, *hs, *wdq, *wds;
+};
+FwdWs carve_fwd(char* base, int S, int d, int f, int E, size_t* total) {
+  Carve c{base};
+  const size_t sd = static_cast<size_t>(S) * d, sf = static_cast<size_t>(S) * f;
+  const size_t w = static_cast<size_t>(E) * d * f;
+  FwdWs o;
+  o.xq = c.take(sd); o.xs = c.take(sd / 32);
+  o.wgq = c.take(w); o.wgs = c.take(w / 32);
+  o.wuq = c.take(w); o.wus = c.take(w / 32);
+  o.hq = c.take(sf); o.hs = c.take(sf / 32);
+  o.wdq = c.take(w); o.wds = c.take(w / 32);
+  if (total) *total = c.used;
+  return o;
+}
+
+struct BwdWs {
+  uint8_t *doq, *dos, *wdq, *wds, *dguq, *dgus, *wgq, *wgs, *wuq, *wus;
+  int32_t* poff;
+  uint8_t *ht, *hts, *dot, *dots, *xt, *xts, *dgut, *dguts;
+};
+BwdWs carve_bwd(char* base, int S, int d, int f, int E, size_t* total) {
+  Carve c{base};
+  const size_t sd = static_cast<size_t>(S) * d, s2f = static_cast<size_t>(S) * 2 * f;
+  const size_t w = static_cast<size_t>(E) * d * f;
+  const size_t P = static_cast<size_t>(padded_rows(S, E));
+  BwdWs o;
+  o.doq = c.take(sd); o.dos = c.take(sd / 32);
+  o.wdq = c.take(w); o.wds = c.take(w / 32);
+  o.dguq = c.take(s2f); o.dgus = c.take(s2f / 32);
+  o.wgq = c.take(w); o.wgs = c.take(w / 32);
+  o.wuq = c.take(w); o.wus = c.take(w / 32);
+  o.poff = reinterpret_cast<int32_t*>(c.take(static_cast<size_t>(E + 1) * 4));
+  o.ht = c.take(P * f); o.hts = c.take(P * f / 32);
+  o.dot = c.take(P * d); o.dots = c.take(P * d / 32);
+  o.xt = c.take(P * d); o.xts = c.take(P * d / 32);
+  o.dgut = c.take(P * 2 * f); o.dguts = c.take(P * 2 * f / 32);
+  if (total) *total = c.used;
+  return o;
+}
+
+#define TRY(x)                                \
+  do {                                        \
+    hipError_t _e = (x);                      \
+    if (_e != hipSuccess) return _e;          \
+  } while (0)
+
+}  // namespace
+
+size_t ffn_mx_fwd_workspace(int S, int d, int f, int E) {
+  size_t n = 0;
+  carve_fwd(nullptr, S, d, f, E, &n);
+  return n;
+}
+
+size_t ffn_mx_bwd_workspace(int S, int d, int f, int E) {
+  size_t n = 0;
+  carve_bwd(nullptr, S, d, f, E, &n);
+  return n;
+}
+
+hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
+  const int S = a.S, d = a.d, f = a.f, E = a.E;
+  const FwdWs w = carve_fwd(static_cast<char*>(ws), S, d, f, E, nullptr);
+  const int64_t wsz = static_cast<int64_t>(d) * f;
+  // Operands: Xp along d; W_gate, W_up along d, transposed to [f][d].
+  TRY(launch_mx_kmajor(a.xp, S, d, 1, 0, w.xq, 0, w.xs, 0, s));
+  TRY(launch_mx_tgroup(a.w_gate, d, f, nullptr, nullptr, 1, E, wsz, w.wgq, d, wsz, w.wgs, wsz / 32, s));
+  TRY(launch_mx_tgroup(a.w_up, d, f, nullptr, nullptr, 1, E, wsz, w.wuq, d, wsz, w.wus, wsz / 32, s));
+  {
+    GemmParams p{};
+    p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
+    p.a = w.xq; p.lda = d; p.as = w.xs; p.as_slab = 2LL * S;
+    p.b0 = w.wgq; p.b1 = w.wuq; p.ldb = d; p.bstride = wsz;
+    p.bs0 = w.wgs; p.bs1 = w.wus; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
+    p.c0 = a.G; p.c1 = a.U; p.c2 = a.H; p.ldc = f; p.N = 2 * f; p.K = d;
+    TRY(launch_mx_ragged(FWD_GU, p, s));
+  }
+  // Operands: H along f; W_down along f, transposed to [d][f].
+  TRY(launch_mx_kmajor(a.H, S, f, 1, 0, w.hq, 0, w.hs, 0, s));
+  TRY(launch_mx_tgroup(a.w_down, f, d, nullptr, nullptr, 1, E, wsz, w.wdq, f, wsz, w.wds, wsz / 32, s));
+  GemmParams q{};
+  q.offsets = a.offsets; q.E = E; q.S = S; q.f = f;
+  q.a = w.hq; q.lda = f; q.as = w.hs; q.as_slab = 2LL * S;
+  q.b0 = w.wdq; q.ldb = f; q.bstride = wsz; q.bs0 = w.wds; q.bs_slab = 2LL * d; q.bs_estride = wsz / 32;
+  q.c0 = a.o; q.ldc = d; q.N = d; q.K = f;
+  return launch_mx_ragged(FWD_DOWN, q, s);
+}
+
+hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
+  const int S = a.S, d = a.d, f = a.f, E = a.E;
+  const BwdWs w = carve_bwd(static_cast<char*>(ws), S, d, f, E, nullptr);
+  const int64_t wsz = static_cast<int64_t>(d) * f;
+  const int64_t P = padded_rows(S, E);
+  {  // dGU = SwiGLU'(q(dO) q(W_down)^T): dO and W_down [f][d] along d.
+    TRY(launch_mx_kmajor(a.d_o, S, d, 1, 0, w.doq, 0, w.dos, 0, s));
+    TRY(launch_mx_kmajor(a.w_down, f, d, E, wsz, w.wdq, wsz, w.wds, wsz / 32, s));
+    GemmParams p{};
+    p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
+    p.a = w.doq; p.lda = d; p.as = w.dos; p.as_slab = 2LL * S;
+    p.b0 = w.wdq; p.ldb = d; p.bstride = wsz; p.bs0 = w.wds; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
+    p.c0 = a.dgu; p.ldc = 2 * f; p.e0 = a.G; p.e1 = a.U; p.N = f; p.K = d;
+    TRY(launch_mx_ragged(BWD_DOWN, p, s));
+  }
+  {  // dXp = q(dGU) q([W_gate | W_up])^T: dGU and the weights [d][f] along f.
+    TRY(launch_mx_kmajor(a.dgu, S, 2 * f, 1, 0, w.dguq, 0, w.dgus, 0, s));
+    TRY(launch_mx_kmajor(a.w_gate, d, f, E, wsz, w.wgq, wsz, w.wgs, wsz / 32, s));
+    TRY(launch_mx_kmajor(a.w_up, d, f, E, wsz, w.wuq, wsz, w.wus, wsz / 32, s));
+    GemmParams p{};
+    p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
+    p.a = w.dguq; p.lda = 2 * f; p.as = w.dgus; p.as_slab = 2LL * S;
+    p.b0 = w.wgq; p.b1 = w.wuq; p.ldb = f; p.bstride = wsz;
+    p.bs0 = w.wgs; p.bs1 = w.wus; p.bs_slab = 2LL * d; p.bs_estride = wsz / 32;
+    p.c0 = a.dxp; p.ldc = d; p.N = d; p.K = 2 * f;
+    TRY(launch_mx_ragged(BWD_GU, p, s));
+  }
+  // Weight gradients: every operand along the expert's tokens, transposed.
+  TRY(launch_mx_poff(a.offsets, E, w.poff, s));
+  {  // dW_down[e] = q(H_e)^T q(dO_e)
+    TRY(launch_mx_tgroup(a.H, S, f, a.offsets, w.poff, E, 1, 0, w.ht, P, 0, w.hts, 0, s));
+    TRY(launch_mx_tgroup(a.d_o, S, d, a.offsets, w.poff, E, 1, 0, w.dot, P, 0, w.dots, 0, s));
+    GemmParams p{};
+    p.offsets = w.poff; p.E = E; p.S = S;
+    p.a = w.ht; p.lda = P; p.as = w.hts; p.as_slab = 2LL * f;
+    p.b0 = w.dot; p.ldb = P; p.bs0 = w.dots; p.bs_slab = 2LL * d;
+    p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = f * d; p.M = f; p.N = d; p.f = d;
+    TRY(launch_mx_wgrad(p, s));
+  }
+  {  // [dW_gate | dW_up][e] = q(Xp_e)^T q(dGU_e)
+    TRY(launch_mx_tgroup(a.xp, S, d, a.offsets, w.poff, E, 1, 0, w.xt, P, 0, w.xts, 0, s));
+    TRY(launch_mx_tgroup(a.dgu, S, 2 * f, a.offsets, w.poff, E, 1, 0, w.dgut, P, 0, w.dguts, 0, s));
+    GemmParams p{};
+    p.offsets = w.poff; p.E = E; p.S = S;
+    p.a = w.xt; p.lda = P; p.as = w.xts; p.as_slab = 2LL * d;
+    p.b0 = w.dgut; p.ldb = P; p.bs0 = w.dguts; p.bs_slab = 4LL * f;
+    p.c0 = a.dw_gate; p.c1 = a.dw_up; p.ldc = f; p.cstride = d * f; p.M = d; p.N = 2 * f; p.f = f;
+    TRY(launch_mx_wgrad(p, s));
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -30,152 +30,16 @@
 // lane and reads the saved G, U the same way.
 #include "common.h"
 #include "grouped_gemm.h"
+#include "gemm_device.h"
 #include "kernels.h"
-
-#include <type_traits>
 
 namespace moe {
 namespace {
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) v4s lds_v4s_t;
+using namespace gemm;
 
 constexpr int kBK = 32;     // K elements per slab (64 bytes of bf16)
 constexpr int kStages = 4;  // LDS ring depth: slabs kt+1..kt+3 fly while kt is multiplied
-
-// Buffer descriptor over [base, base + bytes) (out-of-range loads read 0),
-// built from wave-uniform values so it lives in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
-  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes)));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, n,
-                                           0x00020000);
-}
-
-// One 16-byte load per lane into LDS: lane i writes lds_wave + 16 i (lds_wave
-// is wave-uniform and goes to M0). Issued as inline assembly so the compiler,
-// which cannot tell the ring slots apart, does not add a full vmcnt(0) wait in
-// front of every LDS read; the kernel waits for these loads itself
-// (wait_vmcnt before the barrier that publishes a slab).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_wave) {
-  asm volatile("buffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "{m0}"(lds_wave), "s"(r) : "memory");
-}
-
-// K-contiguous tiles: rows of 64 bytes (4 chunks of 16); a 16-lane quarter of
-// a ds_read_b128 reads one chunk column of 16 consecutive rows, so XOR-ing the
-// chunk with (row / 4) % 4 spreads those rows over all 64 banks.
-__device__ __forceinline__ int swz_row(int row) { return (row >> 2) & 3; }
-// Row-contiguous tiles: a transposing read touches 4 consecutive k-rows x 32
-// bytes per 16-lane group; XOR-ing the chunk index with 4 (k % 4) puts the 16
-// (row, chunk) pairs of a half-wave on distinct banks (64 banks of 4 bytes).
-// Rows of only 8 chunks (R = 64) use 2 (k % 4).
-template <int R>
-__device__ __forceinline__ int swz_k(int k) { return R >= 128 ? (k & 3) << 2 : (k & 3) << 1; }
-
-// K-contiguous tile of R rows x 32 k: stage rows [0, R) of a descriptor whose
-// base is the tile's first row at the slab's first k; ld in elements. One
-// wave-wide load fills 16 rows.
-template <int R>
-__device__ __forceinline__ void stage_kmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane) {
-#pragma unroll
-  for (int q = 0; q < R / 64; ++q) {
-    const int rbase = (q * 4 + wave) * 16;
-    const int row = rbase + (lane >> 2);
-    const int g = (lane & 3) ^ swz_row(row);
-    load_lds16(r, static_cast<uint32_t>(row * ld * 2 + g * 16), dst + rbase * 64);
-  }
-}
-
-// Row-contiguous tile: 32 k-rows of R elements; descriptor base at (slab's
-// first k, tile's first column).
-template <int R>
-__device__ __forceinline__ void stage_mnmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane) {
-  constexpr int RB = R * 2;
-#pragma unroll
-  for (int q = 0; q < R / 64; ++q) {
-    const int byte0 = (q * 4 + wave) * 1024;
-    const int byte = byte0 + lane * 16;
-    const int k = byte / RB;
-    const int g = ((byte % RB) >> 4) ^ swz_k<R>(k);
-    load_lds16(r, static_cast<uint32_t>(k * ld * 2 + g * 16), dst + byte0);
-  }
-}
-
-// Fragment (32 rows x 16 k) of a K-contiguous tile: lane -> row rb + lane%32,
-// k = 16 kk + 8 (lane/32) .. +7.
-__device__ __forceinline__ bf16x8 frag_kmajor(const char* t, int rb, int kk, int lane) {
-  const int row = rb + (lane & 31);
-  const int chunk = (kk * 2 + (lane >> 5)) ^ swz_row(row);
-  return *reinterpret_cast<const bf16x8*>(t + row * 64 + chunk * 16);
-}
-
-// Same fragment from a row-contiguous tile of R columns, via two transposing
-// reads: within each 16-lane group, source lane s points at (k0 + s/4, c0 +
-// 4 (s%4)) and result lane i receives k0..k0+3 of column c0 + i.
-template <int R>
-__device__ __forceinline__ bf16x8 frag_mnmajor(const char* t, int cb, int kk, int lane) {
-  constexpr int RB = R * 2;
-  const int g = lane >> 4, s = lane & 15;
-  const int c = cb + 16 * (g & 1) + 4 * (s & 3);
-  const int kb = kk * 16 + 8 * (g >> 1) + (s >> 2);
-  v4s h[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int k = kb + 4 * half;
-    const int byte = c * 2;
-    const int off = k * RB + ((((byte >> 4) ^ swz_k<R>(k))) << 4) + (byte & 15);
-    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(const_cast<char*>(t) + off));
-  }
-  bf16x8 v;
-  __builtin_memcpy(&v, h, 16);
-  return v;
-}
-
-// Four fp32 -> four bf16 (round to nearest even) with gfx950's packed convert.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  const bf16x2_t r = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
-  uint32_t u;
-  __builtin_memcpy(&u, &r, 4);
-  return u;
-}
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  return make_uint2(pack2(a, b), pack2(c, d));
-}
-__device__ __forceinline__ void unpack4(uint2 v, float (&o)[4]) {
-  o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
-  o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
-}
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
-// vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, fully unrolled, so
-// accumulator indices stay compile-time constants (a runtime index would put
-// the accumulators in scratch memory).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for_impl(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for_impl<I + 1, N>(f);
-  }
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
-
-__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 template <int MODE, int BM, int BN>
 __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
@@ -193,81 +57,10 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int bid = blockIdx.x;
-  const int NT = p.N / BN;
 
-  // ---- device-side tile schedule ------------------------------------------------
-  if (wave == 0) {
-    int e_sel = -1, row0 = 0, row_end = 0, nt = 0, m0 = 0;
-    if constexpr (MODE == WGRAD) {
-      const int MT = p.M / BM;
-      const int R = p.E * MT * NT;
-      if (bid < R) {
-        const int q = R / 8, rmd = R % 8, x = bid % 8, i = bid / 8;
-        const int logical = x * q + min(x, rmd) + i;
-        e_sel = logical / (MT * NT);
-        const int rest = logical % (MT * NT);
-        m0 = (rest / NT) * BM;
-        nt = rest % NT;
-        row0 = p.offsets[e_sel];
-        row_end = p.offsets[e_sel + 1];
-      }
-    } else {
-      int tq[4], tsum = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane * 4 + q;
-        const int n = (e < p.E) ? (p.offsets[e + 1] - p.offsets[e]) : 0;
-        tq[q] = (n + BM - 1) / BM;
-        tsum += tq[q];
-      }
-      const int excl = wave_exclusive_scan(tsum);
-      const int RM = __shfl(excl + tsum, 63, kWave);
-      const int R = RM * NT;
-      if (bid < R) {
-        // Each XCD (bid % 8) takes a contiguous range of tiles; inside it,
-        // groups of GM row tiles sweep the column tiles so concurrently
-        // running tiles share operands in that XCD's L2.
-        const int q = R / 8, rmd = R % 8, x = bid % 8, i = bid / 8;
-        const int logical = x * q + min(x, rmd) + i;
-        constexpr int GM = 8;
-        const int g = logical / (GM * NT);
-        const int gm = min(GM, RM - g * GM);
-        const int local = logical - g * GM * NT;
-        const int mt = g * GM + local % gm;
-        nt = local / gm;
-        int run = excl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = lane * 4 + q;
-          if (mt >= run && mt < run + tq[q]) {
-            e_sel = e;
-            row0 = p.offsets[e] + (mt - run) * BM;
-            row_end = p.offsets[e + 1];
-          }
-          run += tq[q];
-        }
-        const uint64_t who = __ballot(e_sel >= 0);
-        const int src = who ? __ffsll(static_cast<long long>(who)) - 1 : 0;
-        e_sel = __shfl(e_sel, src, kWave);
-        row0 = __shfl(row0, src, kWave);
-        row_end = __shfl(row_end, src, kWave);
-        if (!who) e_sel = -1;
-      }
-    }
-    if (lane == 0) {
-      s_info[0] = e_sel; s_info[1] = row0; s_info[2] = row_end; s_info[3] = nt; s_info[4] = m0;
-    }
-  }
-  __syncthreads();
-  // The tile coordinates are workgroup-uniform: keep them (and every address
-  // and buffer descriptor derived from them) in scalar registers.
-  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
-  if (e < 0) return;
-  const int row0 = __builtin_amdgcn_readfirstlane(s_info[1]);
-  const int row_end = __builtin_amdgcn_readfirstlane(s_info[2]);
-  const int nt = __builtin_amdgcn_readfirstlane(s_info[3]);
-  const int m0 = __builtin_amdgcn_readfirstlane(s_info[4]);
+  const TileCoord tc = tile_schedule<MODE, BM, BN>(p, s_info, wave, lane);
+  if (tc.e < 0) return;
+  const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, nt = tc.nt, m0 = tc.m0;
   const int n0 = nt * BN;
   const int nk = (MODE == WGRAD) ? (row_end - row0 + kBK - 1) / kBK : p.K / kBK;
 
@@ -416,155 +209,8 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
   // wave ends.
   wait_vmcnt<0>();
 
-  // ---- epilogue ---------------------------------------------------------------------------
-  // acc[j][i] element r of lane l: n = wn*WN + 32 j + 8 (r/4) + 4 (l/32) + r%4,
-  // m = wm*WM + 32 i + l%32; four consecutive r are four consecutive columns.
-  // Outputs go through a per-wave LDS area in column groups of up to 64: the
-  // lanes put their 8-byte pieces into a [WM rows][64 cols] bf16 staging
-  // tile, then every store writes 128 contiguous bytes of a row. Saved inputs
-  // of the epilogue (G, U for BWD_DOWN) come in the same way by LDS DMA.
   __syncthreads();  // every wave is done with the ring
-  const int hl = lane >> 5, l32 = lane & 31;
-  constexpr int kSlot = WM * 128;  // one staging tile: WM rows x 64 columns of bf16
-  char* const wa = smem + wave * 2 * kSlot;
-  // Chunk c (16 bytes) of staging row r lives at chunk c ^ ((r / 2) % 8).
-  auto st_off = [](int r, int col) {
-    return r * 128 + ((((col >> 3) ^ (r >> 1)) & 7) << 4) + ((col & 4) << 1);
-  };
-  auto put4 = [&](int slot, int r, int col, uint2 v) {
-    *reinterpret_cast<uint2*>(wa + slot * kSlot + st_off(r, col)) = v;
-  };
-  auto get4 = [&](int slot, int r, int col) -> uint2 {
-    return *reinterpret_cast<const uint2*>(wa + slot * kSlot + st_off(r, col));
-  };
-  auto wave_sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-  };
-  // Rows [0, rows) and columns [0, cols) of staging tile `slot` -> global
-  // rows g + r*ld (bytes), 16 bytes per lane, 8 lanes per 128-byte row.
-  auto flush = [&](int slot, char* g, int64_t ld, int rows, int cols) {
-    wave_sync();
-    const int c = lane & 7;
-#pragma unroll 4
-    for (int t = 0; t < WM / 8; ++t) {
-      const int r = t * 8 + (lane >> 3);
-      const uint4 v = *reinterpret_cast<const uint4*>(wa + slot * kSlot + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
-      if (r < rows && c * 8 < cols) *reinterpret_cast<uint4*>(g + r * ld + c * 16) = v;
-    }
-    wave_sync();
-  };
-  const int mrow = (MODE == WGRAD ? m0 : row0) + wm * WM;   // first row of this wave's block
-  const int rows = (MODE == WGRAD) ? WM : max(0, min(WM, row_end - mrow));
-  auto acc4 = [&](int j, int i, int q) {
-    return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
-  };
-
-  if constexpr (MODE == FWD_GU) {
-    // Gate blocks [0, NB/2) and up blocks [NB/2, NB) cover the same NB*16 f-columns.
-    constexpr int GC = NB * 16;
-    const int col0 = nt * (BN / 2) + wn * (WN / 2);
-    const int64_t ld = p.ldc * 2;
-    char* G = static_cast<char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
-    char* U = static_cast<char*>(p.c1) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
-    char* H = static_cast<char*>(p.c2) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
-    // Pass 1: G and H (= silu(G) U) from the gate and up accumulators; pass 2: U.
-    static_for<MB>([&](auto I) {
-      static_for<NB / 2>([&](auto JJ) {
-        static_for<4>([&](auto Q) {
-          const int r = I * 32 + l32, col = JJ * 32 + 8 * Q + 4 * hl;
-          float h[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float g = acc[JJ][I][4 * Q + c], u = acc[JJ + NB / 2][I][4 * Q + c];
-            h[c] = g * sigmoid_f(g) * u;
-          }
-          put4(0, r, col, acc4(JJ, I, Q));
-          put4(1, r, col, pack4(h[0], h[1], h[2], h[3]));
-        });
-      });
-    });
-    flush(0, G, ld, rows, GC);
-    flush(1, H, ld, rows, GC);
-    static_for<MB>([&](auto I) {
-      static_for<NB / 2>([&](auto JJ) {
-        static_for<4>([&](auto Q) { put4(0, I * 32 + l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JJ + NB / 2, I, Q)); });
-      });
-    });
-    flush(0, U, ld, rows, GC);
-  } else if constexpr (MODE == BWD_DOWN) {
-    // dH -> dG = dH U sig(G) (1 + G (1 - sig(G))), dU = dH G sig(G); a row of
-    // dGU is [dG (f) | dU (f)]. Column groups of 64 (NB = 1: 32).
-    constexpr int GC = NB >= 2 ? 64 : 32;
-    constexpr int JG = NB >= 2 ? 2 : 1;  // 32-column blocks per group
-    const int64_t ld = p.ldc * 2, lds_ = static_cast<int64_t>(p.f) * 2;
-    static_for<NB / JG>([&](auto JP) {
-      const int col0 = n0 + wn * WN + JP * 64;
-      // Saved G, U of this group -> staging tiles 0, 1 (rows past the end read 0).
-      const int64_t sbase = (static_cast<int64_t>(mrow) * p.f + col0) * 2;
-      const int64_t sbytes = static_cast<int64_t>(rows) * p.f * 2;
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const auto rs = make_rsrc(static_cast<const char*>(sl ? p.e1 : p.e0) + sbase, sbytes);
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wa + sl * kSlot));
-#pragma unroll
-        for (int t = 0; t < WM / 8; ++t) {
-          const int r = t * 8 + (lane >> 3);
-          const int c = (lane & 7) ^ ((r >> 1) & 7);   // logical chunk held by this lane's slot
-          const uint32_t voff = (c * 8 < GC) ? static_cast<uint32_t>(r * lds_ + c * 16) : 0x80000000u;
-          load_lds16(rs, voff, dst + t * 1024);
-        }
-      }
-      wait_vmcnt<0>();
-      wave_sync();
-      static_for<MB>([&](auto I) {
-        static_for<JG>([&](auto JJ) {
-          static_for<4>([&](auto Q) {
-            constexpr int j = JP * JG + JJ;
-            const int r = I * 32 + l32, col = JJ * 32 + 8 * Q + 4 * hl;
-            float g[4], u[4], dg[4], du[4];
-            unpack4(get4(0, r, col), g);
-            unpack4(get4(1, r, col), u);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float dh = acc[j][I][4 * Q + c];
-              const float sg = sigmoid_f(g[c]);
-              du[c] = dh * g[c] * sg;
-              dg[c] = dh * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
-            }
-            put4(0, r, col, pack4(dg[0], dg[1], dg[2], dg[3]));
-            put4(1, r, col, pack4(du[0], du[1], du[2], du[3]));
-          });
-        });
-      });
-      char* C = static_cast<char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
-      flush(0, C, ld, rows, GC);
-      flush(1, C + static_cast<int64_t>(p.f) * 2, ld, rows, GC);
-    });
-  } else {
-    // FWD_DOWN, BWD_GU: C[row][n]; WGRAD: C[e][m][n], columns >= f of the
-    // gate|up weight gradient go to the second output (dw_up).
-    char* out = static_cast<char*>(p.c0);
-    int cn0 = n0;
-    if constexpr (MODE == WGRAD) {
-      if (p.c1 != nullptr && n0 >= p.f) { out = static_cast<char*>(p.c1); cn0 = n0 - p.f; }
-      out += static_cast<int64_t>(e) * p.cstride * 2;
-    }
-    constexpr int GC = NB >= 2 ? 64 : 32;
-    constexpr int JG = NB >= 2 ? 2 : 1;
-    const int64_t ld = p.ldc * 2;
-    static_for<NB / JG>([&](auto JP) {
-      static_for<MB>([&](auto I) {
-        static_for<JG>([&](auto JJ) {
-          static_for<4>([&](auto Q) {
-            put4(JP & 1, I * 32 + l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JP * JG + JJ, I, Q));
-          });
-        });
-      });
-      const int col0 = cn0 + wn * WN + JP * 64;
-      flush(JP & 1, out + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2, ld, rows, GC);
-    });
-  }
+  epilogue<MODE, BM, BN>(p, acc, smem, wave, lane, tc);
 }
 
 template <int MODE, int BM, int BN>

@@ -1,0 +1,265 @@
+// MXFP8 grouped GEMMs of the expert SwiGLU FFN for gfx950: E4M3 operands with
+// one E8M0 scale per 32 elements along K, fp32 accumulation, bf16 outputs.
+//
+// The pages train the experts in MXFP8 and credit it with most of the gain of
+// the expert computation and of the data moved for it ("Olmo-core 3 é
+// lançado com infraestrutura para treinar modelos MoE", section "Otimizações e
+// testes em escala de trilhões"; "Ai2 rilascia Olmo-Core 3...", section
+// "Parallelismo, precisione e tecniche di memoria"). The grouped GEMM is the
+// same device-scheduled one as the bf16 path (tile schedule and epilogues are
+// shared, gemm_device.h); what changes is the main loop:
+//  - both operands are K-major E4M3 (the quantisers write every operand that
+//    way, transposing where the bf16 tensor is row-contiguous), so a slab of
+//    64 k is a [rows][64 bytes] tile, loaded by LDS DMA exactly like the
+//    bf16 kernel's 32-k slabs;
+//  - each slab also carries the E8M0 scale tiles (2 bytes per row: the two
+//    32-blocks of the slab), one 1 KB DMA per wave;
+//  - v_mfma_scale_f32_32x32x64_f8f6f4 multiplies a 32 x 64 by a 64 x 32 block
+//    with the block scales applied in the matrix core. Lane l supplies row
+//    l%32 with k = 16 (l/32) .. +15 and 32 + 16 (l/32) .. +15 (two 16-byte
+//    LDS reads) and the scale of (row l%32, 32-block l/32).
+// Ring: 4 slots of one slab each. Iteration kt: wait for slab kt+1, barrier
+// (slot kt's fragments are in registers), refill slot kt with slab kt+4, then
+// read slab kt+1's fragments while slab kt's MFMAs run.
+#include "common.h"
+#include "gemm_device.h"
+#include "grouped_gemm.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+using namespace gemm;
+
+constexpr int kStagesX = 4;
+constexpr int kScaleArea = 1024;  // LDS bytes per wave for the scale DMA
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// 32 bytes of fragment (32 rows x 64 k of E4M3) from a [rows][64 B] tile.
+__device__ __forceinline__ v8i frag_mx(const char* t, int rb, int lane) {
+  const bf16x8 lo = frag_kmajor(t, rb, 0, lane);
+  const bf16x8 hi = frag_kmajor(t, rb, 1, lane);
+  v8i v;
+  __builtin_memcpy(&v, &lo, 16);
+  __builtin_memcpy(reinterpret_cast<char*>(&v) + 16, &hi, 16);
+  return v;
+}
+
+template <int MODE, int BM, int BN>
+__global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int TILE_M = BM * 64, TILE_N = BN * 64;
+  constexpr int SCALES = 4 * kScaleArea;             // per slot: [M scales | N scales | up scales | spare]
+  constexpr int STAGE = TILE_M + TILE_N + SCALES;
+  static_assert(MODE != FWD_GU || NB % 2 == 0, "SwiGLU pairing needs gate and up blocks in every wave");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_info[8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const TileCoord tc = tile_schedule<MODE, BM, BN>(p, s_info, wave, lane);
+  if (tc.e < 0) return;
+  const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, nt = tc.nt, m0 = tc.m0;
+  const int n0 = nt * BN;
+  // WGRAD: [row0, row_end) is the expert's padded K range (a multiple of 64).
+  const int nk = (MODE == WGRAD) ? (row_end - row0) / 64 : p.K / 64;
+  const int64_t bexp = static_cast<int64_t>(e) * p.bstride;
+  const int64_t bsexp = static_cast<int64_t>(e) * p.bs_estride;
+  const uint8_t* A = static_cast<const uint8_t*>(p.a);
+  const uint8_t* B0 = static_cast<const uint8_t*>(p.b0);
+  const uint8_t* B1 = static_cast<const uint8_t*>(p.b1);
+
+  // ---- HBM -> LDS for slab kt (empty descriptors at or past the end) -------------------
+  auto stage = [&](int kt, uint32_t slot) {
+    const bool live = kt < nk;
+    const uint32_t sc = slot + TILE_M + TILE_N + wave * kScaleArea;
+    const uint32_t voff = static_cast<uint32_t>(lane * 16);
+    // M side (rows of the A operand) and its scales (wave 0).
+    if constexpr (MODE == WGRAD) {
+      const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
+      stage_rows64<BM>(make_rsrc(A + m0 * p.lda + k0, live ? BM * p.lda : 0), p.lda, slot, wave, lane);
+      if (wave == 0) load_lds16(make_rsrc(p.as + (k0 / 64) * p.as_slab + m0 * 2, live ? BM * 2 : 0), voff, sc);
+    } else {
+      const int valid = live ? min(BM, row_end - row0) : 0;
+      stage_rows64<BM>(make_rsrc(A + static_cast<int64_t>(row0) * p.lda + kt * 64, static_cast<int64_t>(valid) * p.lda),
+                       p.lda, slot, wave, lane);
+      // Buffer range checks are per dword: round the range up to whole dwords
+      // or an odd row count loses its last row's scales. The extra bytes are
+      // the scales of a row whose data reads as zero (it is never written).
+      if (wave == 0)
+        load_lds16(make_rsrc(p.as + static_cast<int64_t>(kt) * p.as_slab + row0 * 2, (valid * 2 + 3) & ~3), voff,
+                   sc);
+    }
+    // N side and its scales (waves 1, 2); wave 3 (and 2 outside FWD_GU) loads nothing.
+    const uint32_t tn = slot + TILE_M;
+    if constexpr (MODE == FWD_GU) {
+      const int fb = nt * (BN / 2);
+      const int64_t off = bexp + static_cast<int64_t>(fb) * p.ldb + kt * 64;
+      const int64_t bytes = live ? static_cast<int64_t>(BN / 2) * p.ldb : 0;
+      stage_rows64<BN / 2>(make_rsrc(B0 + off, bytes), p.ldb, tn, wave, lane);
+      stage_rows64<BN / 2>(make_rsrc(B1 + off, bytes), p.ldb, tn + TILE_N / 2, wave, lane);
+      const int64_t so = bsexp + static_cast<int64_t>(kt) * p.bs_slab + fb * 2;
+      if (wave == 1) load_lds16(make_rsrc(p.bs0 + so, live ? BN : 0), voff, sc);
+      if (wave == 2) load_lds16(make_rsrc(p.bs1 + so, live ? BN : 0), voff, sc);
+    } else if constexpr (MODE == WGRAD) {
+      const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
+      stage_rows64<BN>(make_rsrc(B0 + n0 * p.ldb + k0, live ? BN * p.ldb : 0), p.ldb, tn, wave, lane);
+      if (wave == 1) load_lds16(make_rsrc(p.bs0 + (k0 / 64) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff, sc);
+    } else {  // FWD_DOWN, BWD_DOWN, BWD_GU: B stored [n][k] per expert
+      const uint8_t* src = B0;
+      const uint8_t* ssrc = p.bs0;
+      int ks = kt;
+      if constexpr (MODE == BWD_GU) {
+        if (kt * 64 >= p.f) { src = B1; ssrc = p.bs1; ks = kt - p.f / 64; }
+      }
+      stage_rows64<BN>(make_rsrc(src + bexp + static_cast<int64_t>(n0) * p.ldb + ks * 64,
+                                 live ? static_cast<int64_t>(BN) * p.ldb : 0),
+                       p.ldb, tn, wave, lane);
+      if (wave == 1)
+        load_lds16(make_rsrc(ssrc + bsexp + static_cast<int64_t>(ks) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff,
+                   sc);
+    }
+    // Every wave issues the same number of loads per slab (the vmcnt waits
+    // count them): the remaining waves load nothing into their own area.
+    const bool extra = (wave == 3) || (wave == 2 && MODE != FWD_GU);
+    if (extra) load_lds16(make_rsrc(p.as, 0), voff, sc);
+  };
+  constexpr int kLoads = BM / 64 + BN / 64 + 1;  // per wave per slab
+
+  floatx16 acc[NB][MB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+  struct Frags {
+    v8i m[MB], n[NB];
+    int sm[MB], sn[NB];
+  };
+  auto read_frags = [&](const char* slotp, Frags& F) {
+    const char* tm = slotp;
+    const char* tn = slotp + TILE_M;
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(slotp + TILE_M + TILE_N);
+    const int r32 = lane & 31, kb = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int row = wm * WM + i * 32;
+      F.m[i] = frag_mx(tm, row, lane);
+      F.sm[i] = sc[(row + r32) * 2 + kb];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (MODE == FWD_GU) {
+        const int half = j / (NB / 2), jj = j % (NB / 2);
+        const int row = wn * (WN / 2) + jj * 32;
+        F.n[j] = frag_mx(tn + half * (TILE_N / 2), row, lane);
+        F.sn[j] = sc[(1 + half) * kScaleArea + (row + r32) * 2 + kb];
+      } else {
+        const int row = wn * WN + j * 32;
+        F.n[j] = frag_mx(tn, row, lane);
+        F.sn[j] = sc[kScaleArea + (row + r32) * 2 + kb];
+      }
+    }
+  };
+  auto mfma_all = [&](const Frags& F) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.n[j], F.m[i], acc[j][i], 0, 0, 0, F.sn[j], 0,
+                                                                   F.sm[i]);
+  };
+  constexpr int kReads = 2 * (MB + NB) + (MB + NB);  // data halves + scale bytes
+  constexpr int kMfma = MB * NB;
+
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+#pragma unroll
+  for (int s0 = 0; s0 < kStagesX; ++s0) stage(s0, ring + s0 * STAGE);
+  Frags F[2];
+  wait_vmcnt<kLoads * (kStagesX - 1)>();
+  __syncthreads();
+  read_frags(smem, F[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<kLoads * (kStagesX - 2)>();   // slab kt+1 has landed
+    __syncthreads();                          // slot kt is read out; slab kt+1 is visible
+    stage(kt + kStagesX, ring + (kt % kStagesX) * STAGE);
+    read_frags(smem + ((kt + 1) % kStagesX) * STAGE, F[(kt + 1) & 1]);
+    mfma_all(F[kt & 1]);
+    constexpr int inter = kReads < kMfma ? kReads : kMfma;
+#pragma unroll
+    for (int r = 0; r < inter; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+    if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with the ring
+  epilogue<MODE, BM, BN>(p, acc, smem, wave, lane, tc);
+}
+
+template <int MODE, int BM, int BN>
+hipError_t launch_tile(const GemmParams& p, int grid, hipStream_t s) {
+  constexpr int ring = kStagesX * (BM * 64 + BN * 64 + 4 * kScaleArea), stage = 4 * 2 * (BM / 2) * 128;
+  constexpr int lds = ring > stage ? ring : stage;
+  auto kern = gg_mx_kernel<MODE, BM, BN>;
+  static bool attr_set = false;  // benign race: idempotent attribute write
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
+int ragged_grid(int S, int E, int BM, int NT) {
+  return round8((static_cast<int64_t>((S + BM - 1) / BM) + E) * NT);
+}
+
+template <int MODE>
+hipError_t ragged_mode(const GemmParams& p, hipStream_t s) {
+  // N is a multiple of 128 (MXFP8 layers need d, f multiples of 128).
+  const bool big = static_cast<int64_t>(p.S) >= 1024LL * p.E;
+  if (p.N % 256 == 0 && (MODE != FWD_GU || p.f % 128 == 0)) {
+    if (big) return launch_tile<MODE, 256, 256>(p, ragged_grid(p.S, p.E, 256, p.N / 256), s);
+    return launch_tile<MODE, 128, 256>(p, ragged_grid(p.S, p.E, 128, p.N / 256), s);
+  }
+  if (big) return launch_tile<MODE, 256, 128>(p, ragged_grid(p.S, p.E, 256, p.N / 128), s);
+  return launch_tile<MODE, 128, 128>(p, ragged_grid(p.S, p.E, 128, p.N / 128), s);
+}
+
+}  // namespace
+
+hipError_t launch_mx_ragged(int mode, const GemmParams& p, hipStream_t s) {
+  switch (mode) {
+    case FWD_GU: return ragged_mode<FWD_GU>(p, s);
+    case FWD_DOWN: return ragged_mode<FWD_DOWN>(p, s);
+    case BWD_DOWN: return ragged_mode<BWD_DOWN>(p, s);
+    case BWD_GU: return ragged_mode<BWD_GU>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_mx_wgrad(const GemmParams& p, hipStream_t s) {
+  const int nsplit = p.c1 ? p.f : p.N;
+  const bool m256 = p.M % 256 == 0, n256 = p.N % 256 == 0 && nsplit % 256 == 0;
+  auto grid = [&](int bm, int bn) { return round8(static_cast<int64_t>(p.E) * (p.M / bm) * (p.N / bn)); };
+  if (m256 && n256) return launch_tile<WGRAD, 256, 256>(p, grid(256, 256), s);
+  if (m256) return launch_tile<WGRAD, 256, 128>(p, grid(256, 128), s);
+  if (n256) return launch_tile<WGRAD, 128, 256>(p, grid(128, 256), s);
+  return launch_tile<WGRAD, 128, 128>(p, grid(128, 128), s);
+}
+
+}  // namespace moe

@@ -33,10 +33,24 @@ struct GemmParams {
   int N, K;           // logical N (FWD_GU: 2f) and K (ragged modes)
   int f;              // split point: FWD_GU/BWD_GU/WGRAD(gate|up)
   int cstride;        // WGRAD: elements between experts in c0/c1
+  // MXFP8 operands: a, b0, b1 hold E4M3 bytes (row strides lda, ldb in
+  // bytes); their E8M0 scales are slab-major, 2 bytes (two blocks of 32) per
+  // row per 64-k slab: scale(row, k) = s[(k / 64) * slab + row * 2 + (k / 32) % 2].
+  const uint8_t* as;  // scales of a
+  const uint8_t* bs0; // scales of b0
+  const uint8_t* bs1; // scales of b1
+  int64_t as_slab;    // bytes between slabs of as
+  int64_t bs_slab;    // bytes between slabs of bs0/bs1
+  int64_t bs_estride; // bytes between experts in bs0/bs1
 };
 
 // bf16 grouped GEMMs (gemm_bf16.hip).
 hipError_t launch_bf16_ragged(int mode, const GemmParams& p, hipStream_t s);
 hipError_t launch_bf16_wgrad(const GemmParams& p, hipStream_t s);
+
+// MXFP8 grouped GEMMs (gemm_mx.hip): both operands K-major E4M3 with slab-major
+// E8M0 scales; WGRAD takes p.offsets = per-expert K ranges padded to 64.
+hipError_t launch_mx_ragged(int mode, const GemmParams& p, hipStream_t s);
+hipError_t launch_mx_wgrad(const GemmParams& p, hipStream_t s);
 
 }  // namespace moe

@@ -65,5 +65,21 @@ hipError_t launch_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, cons
 // MXFP8 (mxfp8.hip)
 hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,
                                  uint8_t* scale, hipStream_t s);
+// Into the grouped GEMM's layout (E4M3 K-major, scales [K/64][rows][2]):
+// K along the columns of in [R][C] (batched)...
+hipError_t launch_mx_kmajor(const void* in, int R, int C, int batches, int64_t in_bstride, uint8_t* q,
+                            int64_t q_bstride, uint8_t* s, int64_t s_bstride, hipStream_t st);
+// ... or K along the rows, transposed to q [C][P], blocked inside the row
+// groups of offsets (padded to 64 rows as poff says), or one group if NULL.
+hipError_t launch_mx_tgroup(const void* in, int R, int C, const int32_t* offsets, const int32_t* poff, int E,
+                            int batches, int64_t in_bstride, uint8_t* q, int64_t P, int64_t q_bstride, uint8_t* s,
+                            int64_t s_bstride, hipStream_t st);
+hipError_t launch_mx_poff(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
+
+// MXFP8 expert FFN (ffn_mx.hip): workspace bytes and launch.
+size_t ffn_mx_fwd_workspace(int S, int d, int f, int E);
+size_t ffn_mx_bwd_workspace(int S, int d, int f, int E);
+hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s);
+hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s);
 
 }  // namespace moe

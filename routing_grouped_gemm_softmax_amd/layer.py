@@ -41,6 +41,7 @@ class MoELayer:
         self.token_of_row = buf(S, dtype=i32)
         self.xp = buf(S, d)
         self.save = torch.empty(L.save_size(self.shape), dtype=torch.uint8, device=dev)
+        self.ws_ffn_fwd = ws(L.MOE_OP_FFN_FWD)
         self.o = buf(S, d)
         self.y = buf(T, d)
         self.ws_dispatch = ws(L.MOE_OP_DISPATCH)
@@ -81,7 +82,8 @@ class MoELayer:
         L.moe_dispatch(x, self.topk_idx, s, self.counts, self.offsets, self.row_of_slot, self.token_of_row,
                        self.xp, self.ws_dispatch, stream)
         mark("moe_dispatch")
-        L.moe_grouped_ffn_fwd(self.xp, w_gate, w_up, w_down, self.offsets, s, self.save, self.o, None, stream)
+        L.moe_grouped_ffn_fwd(self.xp, w_gate, w_up, w_down, self.offsets, s, self.save, self.o, self.ws_ffn_fwd,
+                              stream)
         mark("moe_grouped_ffn_fwd")
         L.moe_combine(self.o, self.topk_gate, self.row_of_slot, s, self.y, stream)
         mark("moe_combine")

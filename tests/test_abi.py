@@ -109,9 +109,14 @@ def test_workspace_too_small():
     assert L.workspace_size(L.MOE_OP_ROUTE, s) == 0 and L.workspace_size(L.MOE_OP_ROUTE, sb) == 16 * 64 * 2
 
 
-def test_mxfp8_layer_gemm_reported_unsupported():
+def test_mxfp8_layer_needs_multiples_of_128_and_a_workspace():
     lib = L.load()
-    s = shape(dtype="mxfp8", d=128)
     p = ctypes.c_void_p(0x100000)
-    rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, ctypes.byref(s), p, 1 << 40, p, None, 0, None)
+    s = shape(dtype="mxfp8", d=64)
+    rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, ctypes.byref(s), p, 1 << 40, p, p, 1 << 40, None)
     assert rc == L.MOE_ERR_UNSUPPORTED
+    s = shape(dtype="mxfp8", d=128)
+    assert L.workspace_size(L.MOE_OP_FFN_FWD, s) > 0
+    assert L.workspace_size(L.MOE_OP_FFN_BWD, s) > L.workspace_size(L.MOE_OP_FFN_BWD, shape(dtype="bf16", d=128))
+    rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, ctypes.byref(s), p, 1 << 40, p, p, 16, None)
+    assert rc == L.MOE_ERR_WORKSPACE

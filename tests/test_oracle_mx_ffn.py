@@ -11,6 +11,7 @@ the two axes have very different magnitudes.
 """
 import numpy as np
 import pytest
+import torch
 
 from oracle import moe_oracle as O
 
@@ -79,6 +80,11 @@ def _q_cols_grouped(a, offsets):  # per expert range, zero-padded to 32
     return out
 
 
+def _bf16(a):
+    """Round to bf16 (torch's cast: round to nearest even) and back."""
+    return torch.tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def _brute_ffn(xp, wg, wu, wd, off, do):
     E = len(off) - 1
     S, d = xp.shape
@@ -94,7 +100,7 @@ def _brute_ffn(xp, wg, wu, wd, off, do):
                 G[r, c] = sum(xq[r, i] * qg[i, c] for i in range(d))
                 U[r, c] = sum(xq[r, i] * qu[i, c] for i in range(d))
                 H[r, c] = G[r, c] * sig(G[r, c]) * U[r, c]
-    hq = _q_rows(H)
+    hq = _q_rows(_bf16(H))
     for e in range(E):
         lo, hi = off[e], off[e + 1]
         qd = _q_cols(wd[e])
@@ -102,7 +108,7 @@ def _brute_ffn(xp, wg, wu, wd, off, do):
             for c in range(d):
                 Ov[r, c] = sum(hq[r, i] * qd[i, c] for i in range(f))
     # backward
-    doq = _q_rows(do)
+    doq = _q_rows(_bf16(do))
     dG = np.zeros((S, f)); dU = np.zeros((S, f))
     for e in range(E):
         lo, hi = off[e], off[e + 1]
@@ -110,13 +116,13 @@ def _brute_ffn(xp, wg, wu, wd, off, do):
         for r in range(lo, hi):
             for c in range(f):
                 dh = sum(doq[r, i] * qdk[c, i] for i in range(d))
-                g, u = G[r, c], U[r, c]
+                g, u = _bf16(G[r, c]), _bf16(U[r, c])
                 s = sig(g)
                 dU[r, c] = dh * g * s
                 dG[r, c] = dh * u * s * (1 + g * (1 - s))
-    dgq, duq = _q_rows(dG), _q_rows(dU)
-    hg, dog, xg = _q_cols_grouped(H, off), _q_cols_grouped(do, off), _q_cols_grouped(xp, off)
-    dgg, dug = _q_cols_grouped(dG, off), _q_cols_grouped(dU, off)
+    dgq, duq = _q_rows(_bf16(dG)), _q_rows(_bf16(dU))
+    hg, dog, xg = _q_cols_grouped(_bf16(H), off), _q_cols_grouped(_bf16(do), off), _q_cols_grouped(xp, off)
+    dgg, dug = _q_cols_grouped(_bf16(dG), off), _q_cols_grouped(_bf16(dU), off)
     dxp = np.zeros((S, d)); dwg = np.zeros((E, d, f)); dwu = np.zeros((E, d, f)); dwd = np.zeros((E, f, d))
     for e in range(E):
         lo, hi = off[e], off[e + 1]
@@ -205,3 +211,10 @@ def test_grouped_rows_pad_inside_each_range():
     g = O.mx_rows_grouped(a, off)
     assert np.array_equal(g[:20], O.mx_roundtrip(np.vstack([a[:20], np.zeros((12, 64))]), "rows")[:20])
     assert np.array_equal(g[20:], O.mx_roundtrip(np.vstack([a[20:], np.zeros((2, 64))]), "rows")[:30])
+
+
+def test_bf16_rne_matches_torch_cast():
+    rng = np.random.default_rng(2)
+    a = np.concatenate([rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000)),
+                        [0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 65504.0]])
+    assert np.array_equal(O.bf16_rne(a), _bf16(a))
