@@ -182,16 +182,16 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 #pragma unroll
   for (int s0 = 0; s0 < kStagesX; ++s0) stage(s0, ring + s0 * STAGE);
-  Frags F[2];
-  wait_vmcnt<kLoads * (kStagesX - 1)>();
-  __syncthreads();
-  read_frags(smem, F[0]);
-  for (int kt = 0; kt < nk; ++kt) {
+  // One slab: wait for slab kt+1, barrier, refill slot kt with slab kt+4, read
+  // slab kt+1 into `nxt` while slab kt's MFMAs run on `cur`. Two register sets
+  // with fixed names (the loop is unrolled by two: a runtime index would put
+  // them in scratch memory).
+  auto step = [&](int kt, const Frags& cur, Frags& nxt) {
     wait_vmcnt<kLoads * (kStagesX - 2)>();   // slab kt+1 has landed
     __syncthreads();                          // slot kt is read out; slab kt+1 is visible
     stage(kt + kStagesX, ring + (kt % kStagesX) * STAGE);
-    read_frags(smem + ((kt + 1) % kStagesX) * STAGE, F[(kt + 1) & 1]);
-    mfma_all(F[kt & 1]);
+    read_frags(smem + ((kt + 1) % kStagesX) * STAGE, nxt);
+    mfma_all(cur);
     constexpr int inter = kReads < kMfma ? kReads : kMfma;
 #pragma unroll
     for (int r = 0; r < inter; ++r) {
@@ -200,6 +200,14 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
     }
     if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
     if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+  };
+  Frags f0, f1;
+  wait_vmcnt<kLoads * (kStagesX - 1)>();
+  __syncthreads();
+  read_frags(smem, f0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, f0, f1);
+    if (kt + 1 < nk) step(kt + 1, f1, f0);
   }
   wait_vmcnt<0>();
   __syncthreads();  // every wave is done with the ring
@@ -228,15 +236,13 @@ int ragged_grid(int S, int E, int BM, int NT) {
   return round8((static_cast<int64_t>((S + BM - 1) / BM) + E) * NT);
 }
 
+// Tiles are at most 256 x 128: two register sets of 32-byte fragments for a
+// 128 x 128 wave block do not fit beside its 256 accumulators.
 template <int MODE>
 hipError_t ragged_mode(const GemmParams& p, hipStream_t s) {
   // N is a multiple of 128 (MXFP8 layers need d, f multiples of 128).
-  const bool big = static_cast<int64_t>(p.S) >= 1024LL * p.E;
-  if (p.N % 256 == 0 && (MODE != FWD_GU || p.f % 128 == 0)) {
-    if (big) return launch_tile<MODE, 256, 256>(p, ragged_grid(p.S, p.E, 256, p.N / 256), s);
-    return launch_tile<MODE, 128, 256>(p, ragged_grid(p.S, p.E, 128, p.N / 256), s);
-  }
-  if (big) return launch_tile<MODE, 256, 128>(p, ragged_grid(p.S, p.E, 256, p.N / 128), s);
+  if (static_cast<int64_t>(p.S) >= 1024LL * p.E)
+    return launch_tile<MODE, 256, 128>(p, ragged_grid(p.S, p.E, 256, p.N / 128), s);
   return launch_tile<MODE, 128, 128>(p, ragged_grid(p.S, p.E, 128, p.N / 128), s);
 }
 
@@ -253,12 +259,8 @@ hipError_t launch_mx_ragged(int mode, const GemmParams& p, hipStream_t s) {
 }
 
 hipError_t launch_mx_wgrad(const GemmParams& p, hipStream_t s) {
-  const int nsplit = p.c1 ? p.f : p.N;
-  const bool m256 = p.M % 256 == 0, n256 = p.N % 256 == 0 && nsplit % 256 == 0;
   auto grid = [&](int bm, int bn) { return round8(static_cast<int64_t>(p.E) * (p.M / bm) * (p.N / bn)); };
-  if (m256 && n256) return launch_tile<WGRAD, 256, 256>(p, grid(256, 256), s);
-  if (m256) return launch_tile<WGRAD, 256, 128>(p, grid(256, 128), s);
-  if (n256) return launch_tile<WGRAD, 128, 256>(p, grid(128, 256), s);
+  if (p.M % 256 == 0) return launch_tile<WGRAD, 256, 128>(p, grid(256, 128), s);
   return launch_tile<WGRAD, 128, 128>(p, grid(128, 128), s);
 }
 

@@ -26,20 +26,22 @@ __device__ __forceinline__ int mx_scale_code(float amax) {
   return c < 0 ? 0 : (c > 254 ? 254 : c);
 }
 
-// E4M3 code of y (already divided by the block scale; exact in fp32).
+// E4M3 code of y (already divided by the block scale; exact in fp32 and
+// |y| < 512, which the block scale guarantees). Normal range (|y| >= 2^-6):
+// round the fp32 significand to 3 bits, ties to even, by integer addition on
+// the bit pattern, rebias the exponent (127 -> 7) and saturate at 448 (code
+// 0x7E; 480 would be the NaN code). Below 2^-6 the E4M3 spacing is 2^-9:
+// code = rint(|y| * 512), 0..8. The sign is kept.
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
   uint32_t code;
-  if (a < 0.015625f) {                       // below 2^-6: subnormal spacing 2^-9
-    code = static_cast<uint32_t>(rintf(a * 512.0f));   // 0..8 (8 is the smallest normal)
+  if (a < 0x3C800000u) {
+    code = static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.0f));
   } else {
-    const int ex = floor_log2_f32(a);
-    float r = rintf(ldexpf(a, 3 - ex));      // significand with 3 fraction bits, in [8, 16]
-    int e2 = ex;
-    if (r >= 16.0f) { r = 8.0f; e2 = ex + 1; }
-    if (e2 > 8 || (e2 == 8 && r > 14.0f)) { e2 = 8; r = 14.0f; }  // saturate to 448
-    code = static_cast<uint32_t>((e2 + 7) << 3) | static_cast<uint32_t>(r - 8.0f);
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+    code = min(r - 0x3C0u, 0x7Eu);
   }
   return sign | code;
 }

@@ -108,3 +108,29 @@ def test_mxfp8_layer_matches_mx_oracle(case):
     print("vs unquantised layer: y", f"{rel_err(host(layer.y), plain['y']):.2e}", flush=True)
     for e in np.nonzero(ref["counts"] == 0)[0]:
         assert not host(layer.dw_gate)[e].any() and not host(layer.dw_down)[e].any()
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_quantize_bit_exact(axis):
+    """mxfp8_quantize (the public entry; the GEMM-layout quantisers share its
+    encoder) gives the oracle's E4M3 codes and E8M0 scales bit for bit."""
+    import routing_grouped_gemm_softmax_amd as M
+    from moe_inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    rng = np.random.default_rng(7)
+    rows, cols = 256, 512
+    a = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-40, 40, size=(rows, 1)))
+    if axis == 1:
+        a = a * np.exp2(rng.integers(-40, 40, size=(1, cols)))
+    a[0, :] = 0.0                                   # all-zero blocks
+    a[1, :64] = 1e-39                               # bf16 subnormals
+    a[2, :32] = np.linspace(440, 520, 32)           # block maximum saturates
+    a[3, 5] = -3.0e38                               # near the bf16 maximum
+    x = bf16_bits_to_f32(f32_to_bf16_bits(a.astype(np.float32))).astype(np.float64)
+    xt = torch.from_numpy(x.astype(np.float32)).to("cuda", torch.bfloat16)
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(rows * cols // 32, dtype=torch.uint8, device="cuda")
+    M.mxfp8_quantize(xt, axis, q, sc)
+    torch.cuda.synchronize()
+    rq, rs = O.mx_quantize(x, "cols" if axis == 0 else "rows")
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    np.testing.assert_array_equal(sc.cpu().numpy().reshape(rs.shape), rs)
