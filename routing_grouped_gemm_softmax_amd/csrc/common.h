@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moe {
 
 constexpr int kWave = 64;
@@ -117,5 +119,21 @@ __device__ __forceinline__ uint64_t match_any(int key, bool valid, int bits) {
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---- host helpers -------------------------------------------------------------
+// Compute units of the current device (cached per device; 0 if the query fails).
+inline int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 }  // namespace moe

@@ -6,9 +6,11 @@
 // escala el entrenamiento de mixture-of-experts a billones de parámetros",
 // section "Cómo funciona"; "Ai2 rilascia Olmo-Core 3...", section
 // "Parallelismo, precisione e tecniche di memoria"). Every workgroup reads the
-// E+1 offsets, derives the per-expert tile counts with a wave scan and maps
-// its id to (expert, row tile, column tile); the grid is sized on the host
-// from the count-free bound ceil(S/BM) + E row tiles.
+// E+1 offsets and maps its id to (expert, row tile, column tile) with a wave
+// scan over the per-expert tile counts; the grid is sized on the host from
+// the count-free bound ceil(S/BM) + E row tiles. The weight gradients, whose
+// tiles cost as much as their expert has rows, run on a persistent grid with
+// XCD ranges cut by cost when the load is skewed (gemm_device.h).
 //
 // Tile: 256 threads = 4 waves in 2 x 2; a BM x BN output tile, each wave a
 // (BM/2) x (BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16) with
@@ -40,6 +42,7 @@ using namespace gemm;
 
 constexpr int kBK = 32;     // K elements per slab (64 bytes of bf16)
 constexpr int kStages = 4;  // LDS ring depth: slabs kt+1..kt+3 fly while kt is multiplied
+constexpr int kEpiWork = 8; // a tile's epilogue costs about as much as this many slabs
 
 template <int MODE, int BM, int BN>
 __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
@@ -58,181 +61,208 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  const TileCoord tc = tile_schedule<MODE, BM, BN>(p, s_info, wave, lane);
-  if (tc.e < 0) return;
-  const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, nt = tc.nt, m0 = tc.m0;
-  const int n0 = nt * BN;
-  const int nk = (MODE == WGRAD) ? (row_end - row0 + kBK - 1) / kBK : p.K / kBK;
+  auto run_tile = [&](const TileCoord& tc) {
+    const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, nt = tc.nt, m0 = tc.m0;
+    const int n0 = nt * BN;
+    const int nk = (MODE == WGRAD) ? (row_end - row0 + kBK - 1) / kBK : p.K / kBK;
 
-  const char* const A = static_cast<const char*>(p.a);
-  const int64_t bexp = static_cast<int64_t>(e) * p.bstride;
+    const char* const A = static_cast<const char*>(p.a);
+    const int64_t bexp = static_cast<int64_t>(e) * p.bstride;
 
-  // ---- HBM -> LDS for slab kt ---------------------------------------------------------
-  // A slab at or past the end (kt == nk) gets empty descriptors: its loads
-  // read nothing and only zero-fill the LDS stage nobody reads again.
-  auto stage_m = [&](int kt, uint32_t dst) {
-    const bool live = kt < nk;
-    if constexpr (!M_MN) {
-      const char* base = A + (static_cast<int64_t>(row0) * p.lda + kt * kBK) * 2;
-      const int valid = live ? min(BM, row_end - row0) : 0;
-      stage_kmajor<BM>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, dst, wave, lane);
-    } else {
-      const int k0 = row0 + kt * kBK;
-      const char* base = A + (static_cast<int64_t>(k0) * p.lda + m0) * 2;
-      const int valid = live ? min(kBK, row_end - k0) : 0;
-      stage_mnmajor<BM>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, dst, wave, lane);
-    }
-  };
-  auto stage_n = [&](int kt, uint32_t dst) {
-    const bool live = kt < nk;
-    if constexpr (MODE == FWD_GU) {
-      // Two sub-tiles [64 k][BN/2]: gate columns then the same up columns.
-      const int fb = nt * (BN / 2);
-      const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + fb) * 2;
-      const int64_t bytes = live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0;
-      stage_mnmajor<BN / 2>(make_rsrc(static_cast<const char*>(p.b0) + off, bytes), p.ldb, dst, wave, lane);
-      stage_mnmajor<BN / 2>(make_rsrc(static_cast<const char*>(p.b1) + off, bytes), p.ldb, dst + TILE_N / 2, wave,
-                            lane);
-    } else if constexpr (MODE == FWD_DOWN) {
-      const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + n0) * 2;
-      const int64_t bytes = live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0;
-      stage_mnmajor<BN>(make_rsrc(static_cast<const char*>(p.b0) + off, bytes), p.ldb, dst, wave, lane);
-    } else if constexpr (MODE == WGRAD) {
-      const int k0 = row0 + kt * kBK;
-      const int valid = live ? min(kBK, row_end - k0) : 0;
-      stage_mnmajor<BN>(make_rsrc(static_cast<const char*>(p.b0) + (static_cast<int64_t>(k0) * p.ldb + n0) * 2,
-                                  static_cast<int64_t>(valid) * p.ldb * 2),
-                        p.ldb, dst, wave, lane);
-    } else {  // BWD_DOWN, BWD_GU: B stored [n][k]
-      const char* src = static_cast<const char*>(p.b0);
-      int kcol = kt * kBK;
-      if constexpr (MODE == BWD_GU) {
-        if (kcol >= p.f) { src = static_cast<const char*>(p.b1); kcol -= p.f; }
-      }
-      const char* base = src + (bexp + static_cast<int64_t>(n0) * p.ldb + kcol) * 2;
-      const int64_t bytes = live ? static_cast<int64_t>(BN) * p.ldb * 2 : 0;
-      stage_kmajor<BN>(make_rsrc(base, bytes), p.ldb, dst, wave, lane);
-    }
-  };
-
-  floatx16 acc[NB][MB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
-
-  // Fragments of one 16-deep k step: MB from the M side, NB from the N side.
-  struct Frags {
-    bf16x8 m[MB], n[NB];
-  };
-  auto read_frags = [&](const char* tm, const char* tn, int kk, Frags& F) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      if constexpr (M_MN) F.m[i] = frag_mnmajor<BM>(tm, wm * WM + i * 32, kk, lane);
-      else F.m[i] = frag_kmajor(tm, wm * WM + i * 32, kk, lane);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if constexpr (MODE == FWD_GU) {
-        // Blocks [0, NB/2) are gate columns, [NB/2, NB) the same up columns.
-        const int half = j / (NB / 2), jj = j % (NB / 2);
-        F.n[j] = frag_mnmajor<BN / 2>(tn + half * (TILE_N / 2), wn * (WN / 2) + jj * 32, kk, lane);
-      } else if constexpr (N_MN) {
-        F.n[j] = frag_mnmajor<BN>(tn, wn * WN + j * 32, kk, lane);
+    // ---- HBM -> LDS for slab kt ---------------------------------------------------------
+    // A slab at or past the end (kt == nk) gets empty descriptors: its loads
+    // read nothing and only zero-fill the LDS stage nobody reads again.
+    // W: wait states of the loads (load_lds16): 4 where the descriptor may have
+    // just been written by a VALU instruction, 0 in the steady-state loop.
+    auto stage_m = [&](int kt, uint32_t dst, auto w) {
+      constexpr int W = decltype(w)::value;
+      const bool live = kt < nk;
+      if constexpr (!M_MN) {
+        const char* base = A + (static_cast<int64_t>(row0) * p.lda + kt * kBK) * 2;
+        const int valid = live ? min(BM, row_end - row0) : 0;
+        stage_kmajor<BM, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, dst, wave, lane);
       } else {
-        F.n[j] = frag_kmajor(tn, wn * WN + j * 32, kk, lane);
+        const int k0 = row0 + kt * kBK;
+        const char* base = A + (static_cast<int64_t>(k0) * p.lda + m0) * 2;
+        const int valid = live ? min(kBK, row_end - k0) : 0;
+        stage_mnmajor<BM, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, dst, wave, lane);
       }
-    }
-  };
-  auto mfma_all = [&](const Frags& F) {
+    };
+    auto stage_n = [&](int kt, uint32_t dst, auto w) {
+      constexpr int W = decltype(w)::value;
+      const bool live = kt < nk;
+      if constexpr (MODE == FWD_GU) {
+        // Two sub-tiles [64 k][BN/2]: gate columns then the same up columns.
+        const int fb = nt * (BN / 2);
+        const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + fb) * 2;
+        const int64_t bytes = live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0;
+        stage_mnmajor<BN / 2, W>(make_rsrc(static_cast<const char*>(p.b0) + off, bytes), p.ldb, dst, wave, lane);
+        stage_mnmajor<BN / 2, W>(make_rsrc(static_cast<const char*>(p.b1) + off, bytes), p.ldb, dst + TILE_N / 2, wave,
+                              lane);
+      } else if constexpr (MODE == FWD_DOWN) {
+        const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + n0) * 2;
+        const int64_t bytes = live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0;
+        stage_mnmajor<BN, W>(make_rsrc(static_cast<const char*>(p.b0) + off, bytes), p.ldb, dst, wave, lane);
+      } else if constexpr (MODE == WGRAD) {
+        const int k0 = row0 + kt * kBK;
+        const int valid = live ? min(kBK, row_end - k0) : 0;
+        stage_mnmajor<BN, W>(make_rsrc(static_cast<const char*>(p.b0) + (static_cast<int64_t>(k0) * p.ldb + n0) * 2,
+                                    static_cast<int64_t>(valid) * p.ldb * 2),
+                          p.ldb, dst, wave, lane);
+      } else {  // BWD_DOWN, BWD_GU: B stored [n][k]
+        const char* src = static_cast<const char*>(p.b0);
+        int kcol = kt * kBK;
+        if constexpr (MODE == BWD_GU) {
+          if (kcol >= p.f) { src = static_cast<const char*>(p.b1); kcol -= p.f; }
+        }
+        const char* base = src + (bexp + static_cast<int64_t>(n0) * p.ldb + kcol) * 2;
+        const int64_t bytes = live ? static_cast<int64_t>(BN) * p.ldb * 2 : 0;
+        stage_kmajor<BN, W>(make_rsrc(base, bytes), p.ldb, dst, wave, lane);
+      }
+    };
+
+    floatx16 acc[NB][MB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.n[j], F.m[i], acc[j][i], 0, 0, 0);
-  };
-  // LDS reads per k step and buffer loads per slab, for the schedule hints.
-  constexpr int kReads = MB * (M_MN ? 2 : 1) + NB * (N_MN ? 2 : 1);
-  constexpr int kMfma = MB * NB;
-  constexpr int kLoads = (BM + BN) / 64;  // per thread per slab
-
-  // ---- main loop -------------------------------------------------------------------------
-  // Ring of kStages = 4 slots, one slab (32 k) each; each slab is two 16-deep
-  // k steps. Iteration kt:
-  //   MFMAs of step 0 of slab kt, interleaved with the LDS reads of step 1;
-  //   wait until slab kt+1 has landed (slabs kt+2, kt+3 may still fly) and
-  //   barrier: everyone is done reading slot kt, and slab kt+1 is visible;
-  //   issue the loads of slab kt+4 into slot kt (empty past the end);
-  //   MFMAs of step 1 of slab kt, interleaved with the reads of step 0 of
-  //   slab kt+1.
-  // So the load of a slab has three slabs of MFMAs to land in, and no LDS
-  // read latency is exposed at slab boundaries.
-  static_assert(kStages == 4 && kBK == 32, "schedule written for a 4-slot ring of 2-step slabs");
-  auto interleave = [&]() {
-    constexpr int inter = kReads < kMfma ? kReads : kMfma;
 #pragma unroll
-    for (int r = 0; r < inter; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+    // Fragments of one 16-deep k step: MB from the M side, NB from the N side.
+    struct Frags {
+      bf16x8 m[MB], n[NB];
+    };
+    auto read_frags = [&](const char* tm, const char* tn, int kk, Frags& F) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        if constexpr (M_MN) F.m[i] = frag_mnmajor<BM>(tm, wm * WM + i * 32, kk, lane);
+        else F.m[i] = frag_kmajor(tm, wm * WM + i * 32, kk, lane);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (MODE == FWD_GU) {
+          // Blocks [0, NB/2) are gate columns, [NB/2, NB) the same up columns.
+          const int half = j / (NB / 2), jj = j % (NB / 2);
+          F.n[j] = frag_mnmajor<BN / 2>(tn + half * (TILE_N / 2), wn * (WN / 2) + jj * 32, kk, lane);
+        } else if constexpr (N_MN) {
+          F.n[j] = frag_mnmajor<BN>(tn, wn * WN + j * 32, kk, lane);
+        } else {
+          F.n[j] = frag_kmajor(tn, wn * WN + j * 32, kk, lane);
+        }
+      }
+    };
+    auto mfma_all = [&](const Frags& F) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.n[j], F.m[i], acc[j][i], 0, 0, 0);
+    };
+    // LDS reads per k step and buffer loads per slab, for the schedule hints.
+    constexpr int kReads = MB * (M_MN ? 2 : 1) + NB * (N_MN ? 2 : 1);
+    constexpr int kMfma = MB * NB;
+    constexpr int kLoads = (BM + BN) / 64;  // per thread per slab
+
+    // ---- main loop -------------------------------------------------------------------------
+    // Ring of kStages = 4 slots, one slab (32 k) each; each slab is two 16-deep
+    // k steps. Iteration kt:
+    //   MFMAs of step 0 of slab kt, interleaved with the LDS reads of step 1;
+    //   wait until slab kt+1 has landed (slabs kt+2, kt+3 may still fly) and
+    //   barrier: everyone is done reading slot kt, and slab kt+1 is visible;
+    //   issue the loads of slab kt+4 into slot kt (empty past the end);
+    //   MFMAs of step 1 of slab kt, interleaved with the reads of step 0 of
+    //   slab kt+1.
+    // So the load of a slab has three slabs of MFMAs to land in, and no LDS
+    // read latency is exposed at slab boundaries.
+    static_assert(kStages == 4 && kBK == 32, "schedule written for a 4-slot ring of 2-step slabs");
+    auto interleave = [&]() {
+      constexpr int inter = kReads < kMfma ? kReads : kMfma;
+#pragma unroll
+      for (int r = 0; r < inter; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+      if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+    };
+    const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+#pragma unroll
+    for (int s0 = 0; s0 < kStages; ++s0) {
+      stage_m(s0, ring + s0 * STAGE, std::integral_constant<int, 4>{});
+      stage_n(s0, ring + s0 * STAGE + TILE_M, std::integral_constant<int, 4>{});
     }
-    if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
-    if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
-  };
-  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-#pragma unroll
-  for (int s0 = 0; s0 < kStages; ++s0) {
-    stage_m(s0, ring + s0 * STAGE);
-    stage_n(s0, ring + s0 * STAGE + TILE_M);
-  }
-  Frags F[2];
-  wait_vmcnt<kLoads * (kStages - 1)>();
-  __syncthreads();
-  read_frags(smem, smem + TILE_M, 0, F[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = smem + (kt % kStages) * STAGE;
-    const char* nxt = smem + ((kt + 1) % kStages) * STAGE;
-    read_frags(cur, cur + TILE_M, 1, F[1]);
-    mfma_all(F[0]);
-    interleave();
-    wait_vmcnt<kLoads * (kStages - 2)>();
+    Frags F[2];
+    wait_vmcnt<kLoads * (kStages - 1)>();
     __syncthreads();
-    const uint32_t slot = ring + (kt % kStages) * STAGE;
-    stage_m(kt + kStages, slot);
-    stage_n(kt + kStages, slot + TILE_M);
-    read_frags(nxt, nxt + TILE_M, 0, F[0]);
-    mfma_all(F[1]);
-    interleave();
-  }
-  // Drain the (empty) loads still in flight before the LDS is reused or the
-  // wave ends.
-  wait_vmcnt<0>();
+    read_frags(smem, smem + TILE_M, 0, F[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = smem + (kt % kStages) * STAGE;
+      const char* nxt = smem + ((kt + 1) % kStages) * STAGE;
+      read_frags(cur, cur + TILE_M, 1, F[1]);
+      mfma_all(F[0]);
+      interleave();
+      wait_vmcnt<kLoads * (kStages - 2)>();
+      __syncthreads();
+      const uint32_t slot = ring + (kt % kStages) * STAGE;
+      stage_m(kt + kStages, slot, std::integral_constant<int, 0>{});
+      stage_n(kt + kStages, slot + TILE_M, std::integral_constant<int, 0>{});
+      read_frags(nxt, nxt + TILE_M, 0, F[0]);
+      mfma_all(F[1]);
+      interleave();
+    }
+    // Drain the (empty) loads still in flight before the LDS is reused or the
+    // wave ends.
+    wait_vmcnt<0>();
 
-  __syncthreads();  // every wave is done with the ring
-  epilogue<MODE, BM, BN>(p, acc, smem, wave, lane, tc);
+    __syncthreads();  // every wave is done with the ring
+    epilogue<MODE, BM, BN>(p, acc, smem, wave, lane, tc);
+  };
+  if constexpr (MODE == WGRAD) {
+    wgrad_sched<BM, BN, kBK, kEpiWork>(p, s_info, wave, lane);
+    const int t_first = __builtin_amdgcn_readfirstlane(s_info[0]);
+    const int t_end = __builtin_amdgcn_readfirstlane(s_info[1]);
+    const int t_stride = __builtin_amdgcn_readfirstlane(s_info[2]);
+    for (int t = t_first; t < t_end; t += t_stride) {
+      run_tile(wgrad_tile<BM, BN>(p, t));
+      __syncthreads();  // the staging area is the next tile's ring
+    }
+  } else {
+    const TileCoord tc = ragged_tile<BM, BN>(p, s_info, wave, lane);
+    if (tc.e < 0) return;
+    run_tile(tc);
+  }
 }
 
+int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
+
 template <int MODE, int BM, int BN>
-hipError_t launch_tile(const GemmParams& p, int grid, hipStream_t s) {
+hipError_t launch_tile(const GemmParams& p, int tiles, hipStream_t s) {
   // The ring, reused by the epilogue's per-wave staging (4 waves x 2 tiles of
   // (BM/2) x 64 bf16).
   constexpr int ring = kStages * (BM + BN) * kBK * 2, stage = 4 * 2 * (BM / 2) * 128;
   constexpr int lds = ring > stage ? ring : stage;
   auto kern = gg_bf16_kernel<MODE, BM, BN>;
-  static bool attr_set = false;  // benign race: idempotent attribute write
-  if (!attr_set) {
+  static std::atomic<int> per_cu{0};  // resident workgroups per CU (idempotent)
+  if (per_cu.load() == 0) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (err != hipSuccess) return err;
-    attr_set = true;
+    int n = 0;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kern), 256, lds);
+    if (err != hipSuccess) return err;
+    per_cu.store(n > 0 ? n : 1);
   }
-  if (grid <= 0) return hipSuccess;
+  if (tiles <= 0) return hipSuccess;
+  // Row-ragged modes: one workgroup per tile of the count-free bound (the
+  // surplus exits at once). Weight gradients: a persistent grid, as many
+  // workgroups as run at once (a multiple of 8: one share per XCD).
+  const int cap = max(8, device_cu_count() * per_cu.load() / 8 * 8);
+  const int grid = MODE == WGRAD ? min(cap, round8(tiles)) : round8(tiles);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
-int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
 
 // Grid bound for row-ragged modes: sum_e ceil(n_e/BM) <= ceil(S/BM) + E.
 int ragged_grid(int S, int E, int BM, int NT) {

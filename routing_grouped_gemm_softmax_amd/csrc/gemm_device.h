@@ -26,16 +26,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
 // One 16-byte load per lane into LDS: lane i writes lds_wave + 16 i (lds_wave
 // is wave-uniform and goes to M0). Issued as inline assembly so the compiler,
 // which cannot tell the ring slots apart, does not add a full vmcnt(0) wait in
 // front of every LDS read; the kernel waits for these loads itself
 // (wait_vmcnt before the barrier that publishes a slab).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
+// The compiler does not look inside the assembly for hazards either, so the
+// load carries its own wait states (s_nop W gives W + 1): a vector memory
+// instruction must not read an SGPR (here the descriptor) within 5 wait states
+// of a VALU write to it (v_readfirstlane, or v_readlane restoring a spilled
+// SGPR), nor M0 within 1 of the SALU write that sets it. W = 4 covers both and
+// is the default; W = 0 is only for loads whose descriptors are known to come
+// from SALU arithmetic (the steady-state main loops), which a test checks on
+// the built code object.
+template <int W = 4>
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_wave) {
-  asm volatile("buffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "{m0}"(lds_wave), "s"(r) : "memory");
+  static_assert(W == 0 || W == 4, "wait states: 1 (M0 only) or 5 (M0 and descriptor)");
+  if constexpr (W == 4)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "{m0}"(lds_wave), "s"(r)
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "{m0}"(lds_wave), "s"(r)
+                 : "memory");
 }
 
 // K-contiguous tiles: rows of 64 bytes (4 chunks of 16); a 16-lane quarter of
@@ -53,7 +69,7 @@ __device__ __forceinline__ int swz_k(int k) { return R >= 128 ? (k & 3) << 2 : (
 // [0, R) of a descriptor whose base is the tile's first row at the slab's
 // first k. One wave-wide load fills 16 rows. stage_kmajor takes the row
 // stride in bf16 elements, stage_rows64 in bytes.
-template <int R>
+template <int R, int W = 4>
 __device__ __forceinline__ void stage_rows64(__amdgpu_buffer_rsrc_t r, int64_t ld_bytes, uint32_t dst, int wave,
                                              int lane) {
 #pragma unroll
@@ -61,17 +77,17 @@ __device__ __forceinline__ void stage_rows64(__amdgpu_buffer_rsrc_t r, int64_t l
     const int rbase = (q * 4 + wave) * 16;
     const int row = rbase + (lane >> 2);
     const int g = (lane & 3) ^ swz_row(row);
-    load_lds16(r, static_cast<uint32_t>(row * ld_bytes + g * 16), dst + rbase * 64);
+    load_lds16<W>(r, static_cast<uint32_t>(row * ld_bytes + g * 16), dst + rbase * 64);
   }
 }
-template <int R>
+template <int R, int W = 4>
 __device__ __forceinline__ void stage_kmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane) {
-  stage_rows64<R>(r, ld * 2, dst, wave, lane);
+  stage_rows64<R, W>(r, ld * 2, dst, wave, lane);
 }
 
 // Row-contiguous tile: 32 k-rows of R elements; descriptor base at (slab's
 // first k, tile's first column).
-template <int R>
+template <int R, int W = 4>
 __device__ __forceinline__ void stage_mnmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane) {
   constexpr int RB = R * 2;
 #pragma unroll
@@ -80,7 +96,7 @@ __device__ __forceinline__ void stage_mnmajor(__amdgpu_buffer_rsrc_t r, int64_t 
     const int byte = byte0 + lane * 16;
     const int k = byte / RB;
     const int g = ((byte % RB) >> 4) ^ swz_k<R>(k);
-    load_lds16(r, static_cast<uint32_t>(k * ld * 2 + g * 16), dst + byte0);
+    load_lds16<W>(r, static_cast<uint32_t>(k * ld * 2 + g * 16), dst + byte0);
   }
 }
 
@@ -156,92 +172,159 @@ __device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rc
 
 
 struct TileCoord {
-  int e;        // expert (-1: this workgroup has no tile)
+  int e;        // expert (-1: no tile)
   int row0;     // ragged modes: first row of the tile; WGRAD: first K row of the expert
   int row_end;  // end of the expert's row range (K range for WGRAD)
   int nt;       // column tile
   int m0;       // WGRAD: first row of the weight-gradient tile
 };
 
-// Maps this workgroup's id to (expert, row tile, column tile) from the
-// per-expert row offsets on the device: wave 0 scans the per-expert tile
-// counts; the result is broadcast through LDS and kept wave-uniform.
-template <int MODE, int BM, int BN>
-__device__ __forceinline__ TileCoord tile_schedule(const GemmParams& p, int* s_info, int wave, int lane) {
+// Row-ragged modes: one tile per workgroup. Maps this workgroup's id to
+// (expert, row tile, column tile) from the per-expert row offsets on the
+// device: wave 0 scans the per-expert tile counts; the result is broadcast
+// through LDS and kept wave-uniform (e < 0: no tile). Each XCD (id % 8) takes
+// a contiguous range of tiles; inside it, groups of 8 row tiles sweep the
+// column tiles so concurrently running tiles share operands in its L2.
+template <int BM, int BN>
+__device__ __forceinline__ TileCoord ragged_tile(const GemmParams& p, int* s_info, int wave, int lane) {
   const int bid = blockIdx.x;
   const int NT = p.N / BN;
   if (wave == 0) {
-    int e_sel = -1, row0 = 0, row_end = 0, nt = 0, m0 = 0;
-    if constexpr (MODE == WGRAD) {
-      const int MT = p.M / BM;
-      const int R = p.E * MT * NT;
-      if (bid < R) {
-        const int q = R / 8, rmd = R % 8, x = bid % 8, i = bid / 8;
-        const int logical = x * q + min(x, rmd) + i;
-        e_sel = logical / (MT * NT);
-        const int rest = logical % (MT * NT);
-        m0 = (rest / NT) * BM;
-        nt = rest % NT;
-        row0 = p.offsets[e_sel];
-        row_end = p.offsets[e_sel + 1];
-      }
-    } else {
-      int tq[4], tsum = 0;
+    int e_sel = -1, row0 = 0, row_end = 0, nt = 0;
+    int tq[4], tsum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      const int n = (e < p.E) ? (p.offsets[e + 1] - p.offsets[e]) : 0;
+      tq[q] = (n + BM - 1) / BM;
+      tsum += tq[q];
+    }
+    const int excl = wave_exclusive_scan(tsum);
+    const int RM = __shfl(excl + tsum, 63, kWave);
+    const int R = RM * NT;
+    if (bid < R) {
+      const int q = R / 8, rmd = R % 8, x = bid % 8, i = bid / 8;
+      const int logical = x * q + min(x, rmd) + i;
+      constexpr int GM = 8;
+      const int g = logical / (GM * NT);
+      const int gm = min(GM, RM - g * GM);
+      const int local = logical - g * GM * NT;
+      const int mt = g * GM + local % gm;
+      nt = local / gm;
+      int run = excl;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = lane * 4 + q;
-        const int n = (e < p.E) ? (p.offsets[e + 1] - p.offsets[e]) : 0;
-        tq[q] = (n + BM - 1) / BM;
-        tsum += tq[q];
-      }
-      const int excl = wave_exclusive_scan(tsum);
-      const int RM = __shfl(excl + tsum, 63, kWave);
-      const int R = RM * NT;
-      if (bid < R) {
-        // Each XCD (bid % 8) takes a contiguous range of tiles; inside it,
-        // groups of GM row tiles sweep the column tiles so concurrently
-        // running tiles share operands in that XCD's L2.
-        const int q = R / 8, rmd = R % 8, x = bid % 8, i = bid / 8;
-        const int logical = x * q + min(x, rmd) + i;
-        constexpr int GM = 8;
-        const int g = logical / (GM * NT);
-        const int gm = min(GM, RM - g * GM);
-        const int local = logical - g * GM * NT;
-        const int mt = g * GM + local % gm;
-        nt = local / gm;
-        int run = excl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = lane * 4 + q;
-          if (mt >= run && mt < run + tq[q]) {
-            e_sel = e;
-            row0 = p.offsets[e] + (mt - run) * BM;
-            row_end = p.offsets[e + 1];
-          }
-          run += tq[q];
+        if (mt >= run && mt < run + tq[q]) {
+          e_sel = e;
+          row0 = p.offsets[e] + (mt - run) * BM;
+          row_end = p.offsets[e + 1];
         }
-        const uint64_t who = __ballot(e_sel >= 0);
-        const int src = who ? __ffsll(static_cast<long long>(who)) - 1 : 0;
-        e_sel = __shfl(e_sel, src, kWave);
-        row0 = __shfl(row0, src, kWave);
-        row_end = __shfl(row_end, src, kWave);
-        if (!who) e_sel = -1;
+        run += tq[q];
       }
+      const uint64_t who = __ballot(e_sel >= 0);
+      const int src = who ? __ffsll(static_cast<long long>(who)) - 1 : 0;
+      e_sel = __shfl(e_sel, src, kWave);
+      row0 = __shfl(row0, src, kWave);
+      row_end = __shfl(row_end, src, kWave);
+      if (!who) e_sel = -1;
     }
     if (lane == 0) {
-      s_info[0] = e_sel; s_info[1] = row0; s_info[2] = row_end; s_info[3] = nt; s_info[4] = m0;
+      s_info[0] = e_sel; s_info[1] = row0; s_info[2] = row_end; s_info[3] = nt;
     }
   }
   __syncthreads();
-  // The tile coordinates are workgroup-uniform: keep them (and every address
-  // and buffer descriptor derived from them) in scalar registers.
   TileCoord t;
   t.e = __builtin_amdgcn_readfirstlane(s_info[0]);
   t.row0 = __builtin_amdgcn_readfirstlane(s_info[1]);
   t.row_end = __builtin_amdgcn_readfirstlane(s_info[2]);
   t.nt = __builtin_amdgcn_readfirstlane(s_info[3]);
-  t.m0 = __builtin_amdgcn_readfirstlane(s_info[4]);
+  t.m0 = 0;
   return t;
+}
+
+// Weight gradients: persistent workgroups (a multiple of 8; workgroup b runs
+// on XCD b % 8). Tiles are (expert, M tile, N tile), numbered expert by
+// expert, with K = the expert's rows, so their cost follows the load. Each XCD
+// owns a contiguous range of the tile list (tiles sharing operands stay in
+// one L2) and its workgroups take the range's tiles in turn. Ranges are cut at
+// equal tile counts, unless that leaves some XCD more than 5/4 of the mean
+// cost (K slabs + kEpiWork per tile): then they are cut at equal shares of the
+// cost, so a hot expert's tiles spread over several XCDs. s_info receives
+// {first tile, end, stride}.
+template <int BM, int BN, int KB, int kEpiWork>
+__device__ __forceinline__ void wgrad_sched(const GemmParams& p, int* s_info, int wave, int lane) {
+  const int bid = blockIdx.x, x = bid % 8, i = bid / 8, wpx = gridDim.x / 8;
+  if (wave == 0) {
+    const int TE = (p.M / BM) * (p.N / BN);
+    const int R = p.E * TE;
+    int w[4], wsum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      w[q] = e < p.E ? (p.offsets[e + 1] - p.offsets[e] + KB - 1) / KB + kEpiWork : 0;
+      wsum += w[q];
+    }
+    const int excl = wave_exclusive_scan(wsum);
+    const int total = __shfl(excl + wsum, 63, kWave);
+    // Count cuts and the cost of the XCD that gets the most.
+    auto count_cut = [&](int xx) { return xx * (R / 8) + min(xx, R % 8); };
+    int64_t worst = 0;
+    for (int xx = 0; xx < 8; ++xx) {
+      const int a = count_cut(xx), b = count_cut(xx + 1);
+      int64_t c = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane * 4 + q;
+        const int lo = max(a, e * TE), hi = min(b, (e + 1) * TE);
+        if (w[q] > 0 && hi > lo) c += static_cast<int64_t>(hi - lo) * w[q];
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
+      worst = max(worst, c);
+    }
+    int first, end;
+    if (worst * 32 <= static_cast<int64_t>(TE) * total * 5) {  // worst <= 5/4 of the mean (TE * total / 8)
+      first = count_cut(x);
+      end = count_cut(x + 1);
+    } else {
+      // First tile whose cost-start is at or past xx/8 of the summed cost.
+      auto bound = [&](int xx) -> int {
+        if (xx >= 8) return R;
+        const int64_t B = static_cast<int64_t>(TE) * total * xx / 8;
+        int t = -1, run = excl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t P = static_cast<int64_t>(TE) * run;
+          if (w[q] > 0 && B >= P && B < P + static_cast<int64_t>(TE) * w[q])
+            t = (lane * 4 + q) * TE + static_cast<int>((B - P + w[q] - 1) / w[q]);
+          run += w[q];
+        }
+        const uint64_t who = __ballot(t >= 0);
+        return who ? __shfl(t, __ffsll(static_cast<long long>(who)) - 1, kWave) : R;
+      };
+      first = bound(x);
+      end = bound(x + 1);
+    }
+    if (lane == 0) {
+      s_info[0] = first + i; s_info[1] = end; s_info[2] = wpx;
+    }
+  }
+  __syncthreads();
+}
+
+// Coordinates of weight-gradient tile t (wave-uniform).
+template <int BM, int BN>
+__device__ __forceinline__ TileCoord wgrad_tile(const GemmParams& p, int t) {
+  const int NT = p.N / BN, TE = (p.M / BM) * NT;
+  const int e = t / TE, j = t % TE;
+  TileCoord tc;
+  tc.e = __builtin_amdgcn_readfirstlane(e);
+  tc.m0 = __builtin_amdgcn_readfirstlane((j / NT) * BM);
+  tc.nt = __builtin_amdgcn_readfirstlane(j % NT);
+  tc.row0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
+  tc.row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+  return tc;
 }
 
 // Writes the accumulators of one BM x BN tile (and, for BWD_DOWN, reads the

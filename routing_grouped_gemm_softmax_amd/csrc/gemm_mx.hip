@@ -32,6 +32,7 @@ namespace {
 using namespace gemm;
 
 constexpr int kStagesX = 4;
+constexpr int kEpiWorkX = 4;    // a tile's epilogue costs about as much as this many slabs
 constexpr int kScaleArea = 1024;  // LDS bytes per wave for the scale DMA
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -62,176 +63,201 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  const TileCoord tc = tile_schedule<MODE, BM, BN>(p, s_info, wave, lane);
-  if (tc.e < 0) return;
-  const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, nt = tc.nt, m0 = tc.m0;
-  const int n0 = nt * BN;
-  // WGRAD: [row0, row_end) is the expert's padded K range (a multiple of 64).
-  const int nk = (MODE == WGRAD) ? (row_end - row0) / 64 : p.K / 64;
-  const int64_t bexp = static_cast<int64_t>(e) * p.bstride;
-  const int64_t bsexp = static_cast<int64_t>(e) * p.bs_estride;
-  const uint8_t* A = static_cast<const uint8_t*>(p.a);
-  const uint8_t* B0 = static_cast<const uint8_t*>(p.b0);
-  const uint8_t* B1 = static_cast<const uint8_t*>(p.b1);
+  auto run_tile = [&](const TileCoord& tc) {
+    const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, nt = tc.nt, m0 = tc.m0;
+    const int n0 = nt * BN;
+    // WGRAD: [row0, row_end) is the expert's padded K range (a multiple of 64).
+    const int nk = (MODE == WGRAD) ? (row_end - row0) / 64 : p.K / 64;
+    const int64_t bexp = static_cast<int64_t>(e) * p.bstride;
+    const int64_t bsexp = static_cast<int64_t>(e) * p.bs_estride;
+    const uint8_t* A = static_cast<const uint8_t*>(p.a);
+    const uint8_t* B0 = static_cast<const uint8_t*>(p.b0);
+    const uint8_t* B1 = static_cast<const uint8_t*>(p.b1);
 
-  // ---- HBM -> LDS for slab kt (empty descriptors at or past the end) -------------------
-  auto stage = [&](int kt, uint32_t slot) {
-    const bool live = kt < nk;
-    const uint32_t sc = slot + TILE_M + TILE_N + wave * kScaleArea;
-    const uint32_t voff = static_cast<uint32_t>(lane * 16);
-    // M side (rows of the A operand) and its scales (wave 0).
-    if constexpr (MODE == WGRAD) {
-      const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
-      stage_rows64<BM>(make_rsrc(A + m0 * p.lda + k0, live ? BM * p.lda : 0), p.lda, slot, wave, lane);
-      if (wave == 0) load_lds16(make_rsrc(p.as + (k0 / 64) * p.as_slab + m0 * 2, live ? BM * 2 : 0), voff, sc);
-    } else {
-      const int valid = live ? min(BM, row_end - row0) : 0;
-      stage_rows64<BM>(make_rsrc(A + static_cast<int64_t>(row0) * p.lda + kt * 64, static_cast<int64_t>(valid) * p.lda),
-                       p.lda, slot, wave, lane);
-      // Buffer range checks are per dword: round the range up to whole dwords
-      // or an odd row count loses its last row's scales. The extra bytes are
-      // the scales of a row whose data reads as zero (it is never written).
-      if (wave == 0)
-        load_lds16(make_rsrc(p.as + static_cast<int64_t>(kt) * p.as_slab + row0 * 2, (valid * 2 + 3) & ~3), voff,
-                   sc);
-    }
-    // N side and its scales (waves 1, 2); wave 3 (and 2 outside FWD_GU) loads nothing.
-    const uint32_t tn = slot + TILE_M;
-    if constexpr (MODE == FWD_GU) {
-      const int fb = nt * (BN / 2);
-      const int64_t off = bexp + static_cast<int64_t>(fb) * p.ldb + kt * 64;
-      const int64_t bytes = live ? static_cast<int64_t>(BN / 2) * p.ldb : 0;
-      stage_rows64<BN / 2>(make_rsrc(B0 + off, bytes), p.ldb, tn, wave, lane);
-      stage_rows64<BN / 2>(make_rsrc(B1 + off, bytes), p.ldb, tn + TILE_N / 2, wave, lane);
-      const int64_t so = bsexp + static_cast<int64_t>(kt) * p.bs_slab + fb * 2;
-      if (wave == 1) load_lds16(make_rsrc(p.bs0 + so, live ? BN : 0), voff, sc);
-      if (wave == 2) load_lds16(make_rsrc(p.bs1 + so, live ? BN : 0), voff, sc);
-    } else if constexpr (MODE == WGRAD) {
-      const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
-      stage_rows64<BN>(make_rsrc(B0 + n0 * p.ldb + k0, live ? BN * p.ldb : 0), p.ldb, tn, wave, lane);
-      if (wave == 1) load_lds16(make_rsrc(p.bs0 + (k0 / 64) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff, sc);
-    } else {  // FWD_DOWN, BWD_DOWN, BWD_GU: B stored [n][k] per expert
-      const uint8_t* src = B0;
-      const uint8_t* ssrc = p.bs0;
-      int ks = kt;
-      if constexpr (MODE == BWD_GU) {
-        if (kt * 64 >= p.f) { src = B1; ssrc = p.bs1; ks = kt - p.f / 64; }
-      }
-      stage_rows64<BN>(make_rsrc(src + bexp + static_cast<int64_t>(n0) * p.ldb + ks * 64,
-                                 live ? static_cast<int64_t>(BN) * p.ldb : 0),
-                       p.ldb, tn, wave, lane);
-      if (wave == 1)
-        load_lds16(make_rsrc(ssrc + bsexp + static_cast<int64_t>(ks) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff,
-                   sc);
-    }
-    // Every wave issues the same number of loads per slab (the vmcnt waits
-    // count them): the remaining waves load nothing into their own area.
-    const bool extra = (wave == 3) || (wave == 2 && MODE != FWD_GU);
-    if (extra) load_lds16(make_rsrc(p.as, 0), voff, sc);
-  };
-  constexpr int kLoads = BM / 64 + BN / 64 + 1;  // per wave per slab
-
-  floatx16 acc[NB][MB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
-
-  struct Frags {
-    v8i m[MB], n[NB];
-    int sm[MB], sn[NB];
-  };
-  auto read_frags = [&](const char* slotp, Frags& F) {
-    const char* tm = slotp;
-    const char* tn = slotp + TILE_M;
-    const uint8_t* sc = reinterpret_cast<const uint8_t*>(slotp + TILE_M + TILE_N);
-    const int r32 = lane & 31, kb = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int row = wm * WM + i * 32;
-      F.m[i] = frag_mx(tm, row, lane);
-      F.sm[i] = sc[(row + r32) * 2 + kb];
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if constexpr (MODE == FWD_GU) {
-        const int half = j / (NB / 2), jj = j % (NB / 2);
-        const int row = wn * (WN / 2) + jj * 32;
-        F.n[j] = frag_mx(tn + half * (TILE_N / 2), row, lane);
-        F.sn[j] = sc[(1 + half) * kScaleArea + (row + r32) * 2 + kb];
+    // ---- HBM -> LDS for slab kt (empty descriptors at or past the end) -------------------
+    // W: wait states of the loads (load_lds16): 4 where a descriptor may have
+    // just been written by a VALU instruction, 0 in the steady-state loop.
+    auto stage = [&](int kt, uint32_t slot, auto w) {
+      constexpr int W = decltype(w)::value;
+      const bool live = kt < nk;
+      const uint32_t sc = slot + TILE_M + TILE_N + wave * kScaleArea;
+      const uint32_t voff = static_cast<uint32_t>(lane * 16);
+      // M side (rows of the A operand) and its scales (wave 0).
+      if constexpr (MODE == WGRAD) {
+        const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
+        stage_rows64<BM, W>(make_rsrc(A + m0 * p.lda + k0, live ? BM * p.lda : 0), p.lda, slot, wave, lane);
+        if (wave == 0) load_lds16<W>(make_rsrc(p.as + (k0 / 64) * p.as_slab + m0 * 2, live ? BM * 2 : 0), voff, sc);
       } else {
-        const int row = wn * WN + j * 32;
-        F.n[j] = frag_mx(tn, row, lane);
-        F.sn[j] = sc[kScaleArea + (row + r32) * 2 + kb];
+        const int valid = live ? min(BM, row_end - row0) : 0;
+        stage_rows64<BM, W>(make_rsrc(A + static_cast<int64_t>(row0) * p.lda + kt * 64, static_cast<int64_t>(valid) * p.lda),
+                         p.lda, slot, wave, lane);
+        // Buffer range checks are per dword: round the range up to whole dwords
+        // or an odd row count loses its last row's scales. The extra bytes are
+        // the scales of a row whose data reads as zero (it is never written).
+        if (wave == 0)
+          load_lds16<W>(make_rsrc(p.as + static_cast<int64_t>(kt) * p.as_slab + row0 * 2, (valid * 2 + 3) & ~3), voff,
+                     sc);
       }
-    }
-  };
-  auto mfma_all = [&](const Frags& F) {
+      // N side and its scales (waves 1, 2); wave 3 (and 2 outside FWD_GU) loads nothing.
+      const uint32_t tn = slot + TILE_M;
+      if constexpr (MODE == FWD_GU) {
+        const int fb = nt * (BN / 2);
+        const int64_t off = bexp + static_cast<int64_t>(fb) * p.ldb + kt * 64;
+        const int64_t bytes = live ? static_cast<int64_t>(BN / 2) * p.ldb : 0;
+        stage_rows64<BN / 2, W>(make_rsrc(B0 + off, bytes), p.ldb, tn, wave, lane);
+        stage_rows64<BN / 2, W>(make_rsrc(B1 + off, bytes), p.ldb, tn + TILE_N / 2, wave, lane);
+        const int64_t so = bsexp + static_cast<int64_t>(kt) * p.bs_slab + fb * 2;
+        if (wave == 1) load_lds16<W>(make_rsrc(p.bs0 + so, live ? BN : 0), voff, sc);
+        if (wave == 2) load_lds16<W>(make_rsrc(p.bs1 + so, live ? BN : 0), voff, sc);
+      } else if constexpr (MODE == WGRAD) {
+        const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
+        stage_rows64<BN, W>(make_rsrc(B0 + n0 * p.ldb + k0, live ? BN * p.ldb : 0), p.ldb, tn, wave, lane);
+        if (wave == 1) load_lds16<W>(make_rsrc(p.bs0 + (k0 / 64) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff, sc);
+      } else {  // FWD_DOWN, BWD_DOWN, BWD_GU: B stored [n][k] per expert
+        const uint8_t* src = B0;
+        const uint8_t* ssrc = p.bs0;
+        int ks = kt;
+        if constexpr (MODE == BWD_GU) {
+          if (kt * 64 >= p.f) { src = B1; ssrc = p.bs1; ks = kt - p.f / 64; }
+        }
+        stage_rows64<BN, W>(make_rsrc(src + bexp + static_cast<int64_t>(n0) * p.ldb + ks * 64,
+                                   live ? static_cast<int64_t>(BN) * p.ldb : 0),
+                         p.ldb, tn, wave, lane);
+        if (wave == 1)
+          load_lds16<W>(make_rsrc(ssrc + bsexp + static_cast<int64_t>(ks) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff,
+                     sc);
+      }
+      // Every wave issues the same number of loads per slab (the vmcnt waits
+      // count them): the remaining waves load nothing into their own area.
+      const bool extra = (wave == 3) || (wave == 2 && MODE != FWD_GU);
+      if (extra) load_lds16<W>(make_rsrc(p.as, 0), voff, sc);
+    };
+    constexpr int kLoads = BM / 64 + BN / 64 + 1;  // per wave per slab
+
+    floatx16 acc[NB][MB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.n[j], F.m[i], acc[j][i], 0, 0, 0, F.sn[j], 0,
-                                                                   F.sm[i]);
-  };
-  constexpr int kReads = 2 * (MB + NB) + (MB + NB);  // data halves + scale bytes
-  constexpr int kMfma = MB * NB;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    struct Frags {
+      v8i m[MB], n[NB];
+      int sm[MB], sn[NB];
+    };
+    auto read_frags = [&](const char* slotp, Frags& F) {
+      const char* tm = slotp;
+      const char* tn = slotp + TILE_M;
+      const uint8_t* sc = reinterpret_cast<const uint8_t*>(slotp + TILE_M + TILE_N);
+      const int r32 = lane & 31, kb = lane >> 5;
 #pragma unroll
-  for (int s0 = 0; s0 < kStagesX; ++s0) stage(s0, ring + s0 * STAGE);
-  // One slab: wait for slab kt+1, barrier, refill slot kt with slab kt+4, read
-  // slab kt+1 into `nxt` while slab kt's MFMAs run on `cur`. Two register sets
-  // with fixed names (the loop is unrolled by two: a runtime index would put
-  // them in scratch memory).
-  auto step = [&](int kt, const Frags& cur, Frags& nxt) {
-    wait_vmcnt<kLoads * (kStagesX - 2)>();   // slab kt+1 has landed
-    __syncthreads();                          // slot kt is read out; slab kt+1 is visible
-    stage(kt + kStagesX, ring + (kt % kStagesX) * STAGE);
-    read_frags(smem + ((kt + 1) % kStagesX) * STAGE, nxt);
-    mfma_all(cur);
-    constexpr int inter = kReads < kMfma ? kReads : kMfma;
+      for (int i = 0; i < MB; ++i) {
+        const int row = wm * WM + i * 32;
+        F.m[i] = frag_mx(tm, row, lane);
+        F.sm[i] = sc[(row + r32) * 2 + kb];
+      }
 #pragma unroll
-    for (int r = 0; r < inter; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (MODE == FWD_GU) {
+          const int half = j / (NB / 2), jj = j % (NB / 2);
+          const int row = wn * (WN / 2) + jj * 32;
+          F.n[j] = frag_mx(tn + half * (TILE_N / 2), row, lane);
+          F.sn[j] = sc[(1 + half) * kScaleArea + (row + r32) * 2 + kb];
+        } else {
+          const int row = wn * WN + j * 32;
+          F.n[j] = frag_mx(tn, row, lane);
+          F.sn[j] = sc[kScaleArea + (row + r32) * 2 + kb];
+        }
+      }
+    };
+    auto mfma_all = [&](const Frags& F) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.n[j], F.m[i], acc[j][i], 0, 0, 0, F.sn[j], 0,
+                                                                     F.sm[i]);
+    };
+    constexpr int kReads = 2 * (MB + NB) + (MB + NB);  // data halves + scale bytes
+    constexpr int kMfma = MB * NB;
+
+    const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+#pragma unroll
+    for (int s0 = 0; s0 < kStagesX; ++s0) stage(s0, ring + s0 * STAGE, std::integral_constant<int, 4>{});
+    // One slab: wait for slab kt+1, barrier, refill slot kt with slab kt+4, read
+    // slab kt+1 into `nxt` while slab kt's MFMAs run on `cur`. Two register sets
+    // with fixed names (the loop is unrolled by two: a runtime index would put
+    // them in scratch memory).
+    auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+      wait_vmcnt<kLoads * (kStagesX - 2)>();   // slab kt+1 has landed
+      __syncthreads();                          // slot kt is read out; slab kt+1 is visible
+      stage(kt + kStagesX, ring + (kt % kStagesX) * STAGE, std::integral_constant<int, 0>{});
+      read_frags(smem + ((kt + 1) % kStagesX) * STAGE, nxt);
+      mfma_all(cur);
+      constexpr int inter = kReads < kMfma ? kReads : kMfma;
+#pragma unroll
+      for (int r = 0; r < inter; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+      if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+    };
+    Frags f0, f1;
+    wait_vmcnt<kLoads * (kStagesX - 1)>();
+    __syncthreads();
+    read_frags(smem, f0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, f0, f1);
+      if (kt + 1 < nk) step(kt + 1, f1, f0);
     }
-    if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
-    if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with the ring
+    epilogue<MODE, BM, BN>(p, acc, smem, wave, lane, tc);
   };
-  Frags f0, f1;
-  wait_vmcnt<kLoads * (kStagesX - 1)>();
-  __syncthreads();
-  read_frags(smem, f0);
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, f0, f1);
-    if (kt + 1 < nk) step(kt + 1, f1, f0);
+  if constexpr (MODE == WGRAD) {
+    wgrad_sched<BM, BN, 64, kEpiWorkX>(p, s_info, wave, lane);
+    const int t_first = __builtin_amdgcn_readfirstlane(s_info[0]);
+    const int t_end = __builtin_amdgcn_readfirstlane(s_info[1]);
+    const int t_stride = __builtin_amdgcn_readfirstlane(s_info[2]);
+    for (int t = t_first; t < t_end; t += t_stride) {
+      run_tile(wgrad_tile<BM, BN>(p, t));
+      __syncthreads();  // the staging area is the next tile's ring
+    }
+  } else {
+    const TileCoord tc = ragged_tile<BM, BN>(p, s_info, wave, lane);
+    if (tc.e < 0) return;
+    run_tile(tc);
   }
-  wait_vmcnt<0>();
-  __syncthreads();  // every wave is done with the ring
-  epilogue<MODE, BM, BN>(p, acc, smem, wave, lane, tc);
 }
 
+int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
+
 template <int MODE, int BM, int BN>
-hipError_t launch_tile(const GemmParams& p, int grid, hipStream_t s) {
+hipError_t launch_tile(const GemmParams& p, int tiles, hipStream_t s) {
   constexpr int ring = kStagesX * (BM * 64 + BN * 64 + 4 * kScaleArea), stage = 4 * 2 * (BM / 2) * 128;
   constexpr int lds = ring > stage ? ring : stage;
   auto kern = gg_mx_kernel<MODE, BM, BN>;
-  static bool attr_set = false;  // benign race: idempotent attribute write
-  if (!attr_set) {
+  static std::atomic<int> per_cu{0};  // resident workgroups per CU (idempotent)
+  if (per_cu.load() == 0) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (err != hipSuccess) return err;
-    attr_set = true;
+    int n = 0;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kern), 256, lds);
+    if (err != hipSuccess) return err;
+    per_cu.store(n > 0 ? n : 1);
   }
-  if (grid <= 0) return hipSuccess;
+  if (tiles <= 0) return hipSuccess;
+  // One workgroup per tile for the row-ragged modes, a persistent grid for
+  // the weight gradients (as in the bf16 kernel).
+  const int cap = max(8, device_cu_count() * per_cu.load() / 8 * 8);
+  const int grid = MODE == WGRAD ? min(cap, round8(tiles)) : round8(tiles);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
-int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
 int ragged_grid(int S, int E, int BM, int NT) {
   return round8((static_cast<int64_t>((S + BM - 1) / BM) + E) * NT);
 }

@@ -173,8 +173,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// LDS DMA of 16 bytes per lane (lane i -> lds_wave + 16 i). The s_nop gives
+// the wait states the compiler does not insert before inline assembly: 5
+// after a VALU write of the descriptor SGPRs, 1 after the write of M0.
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_wave) {
-  asm volatile("buffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "{m0}"(lds_wave), "s"(r) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "{m0}"(lds_wave), "s"(r)
+               : "memory");
 }
 
 template <int EB>
