@@ -69,46 +69,38 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
     const char* const A = static_cast<const char*>(p.a);
     const int64_t bexp = static_cast<int64_t>(e) * p.bstride;
 
-    // ---- HBM -> LDS for slab kt ---------------------------------------------------------
-    // A slab at or past the end (kt == nk) gets empty descriptors: its loads
-    // read nothing and only zero-fill the LDS stage nobody reads again.
-    // W: wait states of the loads (load_lds16): 4 where the descriptor may have
-    // just been written by a VALU instruction, 0 in the steady-state loop.
-    auto stage_m = [&](int kt, uint32_t dst, auto w) {
-      constexpr int W = decltype(w)::value;
+    // ---- HBM -> LDS ------------------------------------------------------------------------
+    // Descriptors of slab kt. A slab at or past the end (kt >= nk) gets empty
+    // descriptors: its loads read nothing and only zero-fill a ring slot that
+    // nobody reads again.
+    auto rsrc_m = [&](int kt) {
       const bool live = kt < nk;
       if constexpr (!M_MN) {
         const char* base = A + (static_cast<int64_t>(row0) * p.lda + kt * kBK) * 2;
         const int valid = live ? min(BM, row_end - row0) : 0;
-        stage_kmajor<BM, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, dst, wave, lane);
+        return make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2);
       } else {
         const int k0 = row0 + kt * kBK;
         const char* base = A + (static_cast<int64_t>(k0) * p.lda + m0) * 2;
         const int valid = live ? min(kBK, row_end - k0) : 0;
-        stage_mnmajor<BM, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, dst, wave, lane);
+        return make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2);
       }
     };
-    auto stage_n = [&](int kt, uint32_t dst, auto w) {
-      constexpr int W = decltype(w)::value;
+    auto rsrc_n = [&](int kt, int half) {
       const bool live = kt < nk;
       if constexpr (MODE == FWD_GU) {
-        // Two sub-tiles [64 k][BN/2]: gate columns then the same up columns.
-        const int fb = nt * (BN / 2);
-        const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + fb) * 2;
-        const int64_t bytes = live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0;
-        stage_mnmajor<BN / 2, W>(make_rsrc(static_cast<const char*>(p.b0) + off, bytes), p.ldb, dst, wave, lane);
-        stage_mnmajor<BN / 2, W>(make_rsrc(static_cast<const char*>(p.b1) + off, bytes), p.ldb, dst + TILE_N / 2, wave,
-                              lane);
+        // Two sub-tiles [32 k][BN/2]: gate columns (half 0), the same up columns (half 1).
+        const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + nt * (BN / 2)) * 2;
+        const char* src = static_cast<const char*>(half ? p.b1 : p.b0);
+        return make_rsrc(src + off, live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0);
       } else if constexpr (MODE == FWD_DOWN) {
         const int64_t off = (bexp + static_cast<int64_t>(kt) * kBK * p.ldb + n0) * 2;
-        const int64_t bytes = live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0;
-        stage_mnmajor<BN, W>(make_rsrc(static_cast<const char*>(p.b0) + off, bytes), p.ldb, dst, wave, lane);
+        return make_rsrc(static_cast<const char*>(p.b0) + off, live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0);
       } else if constexpr (MODE == WGRAD) {
         const int k0 = row0 + kt * kBK;
         const int valid = live ? min(kBK, row_end - k0) : 0;
-        stage_mnmajor<BN, W>(make_rsrc(static_cast<const char*>(p.b0) + (static_cast<int64_t>(k0) * p.ldb + n0) * 2,
-                                    static_cast<int64_t>(valid) * p.ldb * 2),
-                          p.ldb, dst, wave, lane);
+        return make_rsrc(static_cast<const char*>(p.b0) + (static_cast<int64_t>(k0) * p.ldb + n0) * 2,
+                         static_cast<int64_t>(valid) * p.ldb * 2);
       } else {  // BWD_DOWN, BWD_GU: B stored [n][k]
         const char* src = static_cast<const char*>(p.b0);
         int kcol = kt * kBK;
@@ -116,8 +108,27 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
           if (kcol >= p.f) { src = static_cast<const char*>(p.b1); kcol -= p.f; }
         }
         const char* base = src + (bexp + static_cast<int64_t>(n0) * p.ldb + kcol) * 2;
-        const int64_t bytes = live ? static_cast<int64_t>(BN) * p.ldb * 2 : 0;
-        stage_kmajor<BN, W>(make_rsrc(base, bytes), p.ldb, dst, wave, lane);
+        return make_rsrc(base, live ? static_cast<int64_t>(BN) * p.ldb * 2 : 0);
+      }
+    };
+    // Load L of a slab (each wave issues kLoads per slab): [0, LM) fill the M
+    // tile, [LM, kLoads) the N tile. W: wait states (load_lds16).
+    constexpr int LM = BM / 64, LN = BN / 64, kLoads = LM + LN;
+    auto issue = [&](int kt, uint32_t slot, auto L, auto w) {
+      constexpr int l = decltype(L)::value, W = decltype(w)::value;
+      if constexpr (l < LM) {
+        if constexpr (M_MN) load_mnmajor<BM, W>(rsrc_m(kt), p.lda, slot, wave, lane, l);
+        else load_rows64<BM, W>(rsrc_m(kt), p.lda * 2, slot, wave, lane, l);
+      } else {
+        constexpr int q = l - LM;
+        if constexpr (MODE == FWD_GU) {
+          constexpr int half = q / (LN / 2), qq = q % (LN / 2);
+          load_mnmajor<BN / 2, W>(rsrc_n(kt, half), p.ldb, slot + TILE_M + half * (TILE_N / 2), wave, lane, qq);
+        } else if constexpr (N_MN) {
+          load_mnmajor<BN, W>(rsrc_n(kt, 0), p.ldb, slot + TILE_M, wave, lane, q);
+        } else {
+          load_rows64<BN, W>(rsrc_n(kt, 0), p.ldb * 2, slot + TILE_M, wave, lane, q);
+        }
       }
     };
 
@@ -133,17 +144,19 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
     struct Frags {
       bf16x8 m[MB], n[NB];
     };
-    auto read_frags = [&](const char* tm, const char* tn, int kk, Frags& F) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if constexpr (M_MN) F.m[i] = frag_mnmajor<BM>(tm, wm * WM + i * 32, kk, lane);
-        else F.m[i] = frag_kmajor(tm, wm * WM + i * 32, kk, lane);
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
+    // Fragment FI (compile time): [0, MB) M side, [MB, MB + NB) N side.
+    auto read_frag = [&](const char* slotp, int kk, Frags& F, auto FI) {
+      constexpr int fi = decltype(FI)::value;
+      const char* tm = slotp;
+      const char* tn = slotp + TILE_M;
+      if constexpr (fi < MB) {
+        if constexpr (M_MN) F.m[fi] = frag_mnmajor<BM>(tm, wm * WM + fi * 32, kk, lane);
+        else F.m[fi] = frag_kmajor(tm, wm * WM + fi * 32, kk, lane);
+      } else {
+        constexpr int j = fi - MB;
         if constexpr (MODE == FWD_GU) {
           // Blocks [0, NB/2) are gate columns, [NB/2, NB) the same up columns.
-          const int half = j / (NB / 2), jj = j % (NB / 2);
+          constexpr int half = j / (NB / 2), jj = j % (NB / 2);
           F.n[j] = frag_mnmajor<BN / 2>(tn + half * (TILE_N / 2), wn * (WN / 2) + jj * 32, kk, lane);
         } else if constexpr (N_MN) {
           F.n[j] = frag_mnmajor<BN>(tn, wn * WN + j * 32, kk, lane);
@@ -152,29 +165,29 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
         }
       }
     };
-    auto mfma_all = [&](const Frags& F) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.n[j], F.m[i], acc[j][i], 0, 0, 0);
+    auto read_frags = [&](const char* slotp, int kk, Frags& F) {
+      static_for<MB + NB>([&](auto FI) { read_frag(slotp, kk, F, FI); });
     };
-    // LDS reads per k step and buffer loads per slab, for the schedule hints.
+    auto mfma_one = [&](const Frags& F, auto MI) {
+      constexpr int mi = decltype(MI)::value, j = mi / MB, i = mi % MB;
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.n[j], F.m[i], acc[j][i], 0, 0, 0);
+    };
+    // LDS reads per k step, for the schedule hints.
     constexpr int kReads = MB * (M_MN ? 2 : 1) + NB * (N_MN ? 2 : 1);
     constexpr int kMfma = MB * NB;
-    constexpr int kLoads = (BM + BN) / 64;  // per thread per slab
+    constexpr int kFrags = MB + NB;
 
     // ---- main loop -------------------------------------------------------------------------
     // Ring of kStages = 4 slots, one slab (32 k) each; each slab is two 16-deep
     // k steps. Iteration kt:
-    //   MFMAs of step 0 of slab kt, interleaved with the LDS reads of step 1;
+    //   A: MFMAs of step 0 of slab kt, interleaved with the LDS reads of step 1;
     //   wait until slab kt+1 has landed (slabs kt+2, kt+3 may still fly) and
     //   barrier: everyone is done reading slot kt, and slab kt+1 is visible;
-    //   issue the loads of slab kt+4 into slot kt (empty past the end);
-    //   MFMAs of step 1 of slab kt, interleaved with the reads of step 0 of
-    //   slab kt+1.
-    // So the load of a slab has three slabs of MFMAs to land in, and no LDS
-    // read latency is exposed at slab boundaries.
+    //   B: MFMAs of step 1 of slab kt, with the reads of step 0 of slab kt+1
+    //   and the kLoads loads of slab kt+4 into slot kt spread between them.
+    // A load has three slabs of MFMAs to land in. Spreading the loads keeps the
+    // texture-address unit, which takes a 1 KB LDS-DMA load in many cycles,
+    // from backing up into the issue of the MFMAs behind a burst of loads.
     static_assert(kStages == 4 && kBK == 32, "schedule written for a 4-slot ring of 2-step slabs");
     auto interleave = [&]() {
       constexpr int inter = kReads < kMfma ? kReads : kMfma;
@@ -188,28 +201,30 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
     };
     const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 #pragma unroll
-    for (int s0 = 0; s0 < kStages; ++s0) {
-      stage_m(s0, ring + s0 * STAGE, std::integral_constant<int, 4>{});
-      stage_n(s0, ring + s0 * STAGE + TILE_M, std::integral_constant<int, 4>{});
-    }
+    for (int s0 = 0; s0 < kStages; ++s0)
+      static_for<kLoads>([&](auto L) { issue(s0, ring + s0 * STAGE, L, std::integral_constant<int, 4>{}); });
     Frags F[2];
     wait_vmcnt<kLoads * (kStages - 1)>();
     __syncthreads();
-    read_frags(smem, smem + TILE_M, 0, F[0]);
+    read_frags(smem, 0, F[0]);
     for (int kt = 0; kt < nk; ++kt) {
       const char* cur = smem + (kt % kStages) * STAGE;
       const char* nxt = smem + ((kt + 1) % kStages) * STAGE;
-      read_frags(cur, cur + TILE_M, 1, F[1]);
-      mfma_all(F[0]);
+      read_frags(cur, 1, F[1]);
+      static_for<kMfma>([&](auto MI) { mfma_one(F[0], MI); });
       interleave();
       wait_vmcnt<kLoads * (kStages - 2)>();
       __syncthreads();
       const uint32_t slot = ring + (kt % kStages) * STAGE;
-      stage_m(kt + kStages, slot, std::integral_constant<int, 0>{});
-      stage_n(kt + kStages, slot + TILE_M, std::integral_constant<int, 0>{});
-      read_frags(nxt, nxt + TILE_M, 0, F[0]);
-      mfma_all(F[1]);
-      interleave();
+      static_for<kLoads>([&](auto S) {
+        constexpr int sg = decltype(S)::value;
+        constexpr int m_lo = sg * kMfma / kLoads, m_hi = (sg + 1) * kMfma / kLoads;
+        constexpr int f_lo = sg * kFrags / kLoads, f_hi = (sg + 1) * kFrags / kLoads;
+        static_for<m_hi - m_lo>([&](auto D) { mfma_one(F[1], std::integral_constant<int, m_lo + decltype(D)::value>{}); });
+        static_for<f_hi - f_lo>([&](auto D) { read_frag(nxt, 0, F[0], std::integral_constant<int, f_lo + decltype(D)::value>{}); });
+        issue(kt + kStages, slot, S, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
     // Drain the (empty) loads still in flight before the LDS is reused or the
     // wave ends.

@@ -65,20 +65,24 @@ __device__ __forceinline__ int swz_row(int row) { return (row >> 2) & 3; }
 template <int R>
 __device__ __forceinline__ int swz_k(int k) { return R >= 128 ? (k & 3) << 2 : (k & 3) << 1; }
 
-// K-contiguous tile of R rows x 64 bytes (32 bf16 or 64 fp8 of k): stage rows
+// K-contiguous tile of R rows x 64 bytes (32 bf16 or 64 fp8 of k): rows
 // [0, R) of a descriptor whose base is the tile's first row at the slab's
-// first k. One wave-wide load fills 16 rows. stage_kmajor takes the row
-// stride in bf16 elements, stage_rows64 in bytes.
+// first k. Load q (of R / 64) of a wave fills 16 rows. *_kmajor take the row
+// stride in bf16 elements, *_rows64 in bytes; load_* issue one load, stage_*
+// all of them.
+template <int R, int W = 4>
+__device__ __forceinline__ void load_rows64(__amdgpu_buffer_rsrc_t r, int64_t ld_bytes, uint32_t dst, int wave,
+                                            int lane, int q) {
+  const int rbase = (q * 4 + wave) * 16;
+  const int row = rbase + (lane >> 2);
+  const int g = (lane & 3) ^ swz_row(row);
+  load_lds16<W>(r, static_cast<uint32_t>(row * ld_bytes + g * 16), dst + rbase * 64);
+}
 template <int R, int W = 4>
 __device__ __forceinline__ void stage_rows64(__amdgpu_buffer_rsrc_t r, int64_t ld_bytes, uint32_t dst, int wave,
                                              int lane) {
 #pragma unroll
-  for (int q = 0; q < R / 64; ++q) {
-    const int rbase = (q * 4 + wave) * 16;
-    const int row = rbase + (lane >> 2);
-    const int g = (lane & 3) ^ swz_row(row);
-    load_lds16<W>(r, static_cast<uint32_t>(row * ld_bytes + g * 16), dst + rbase * 64);
-  }
+  for (int q = 0; q < R / 64; ++q) load_rows64<R, W>(r, ld_bytes, dst, wave, lane, q);
 }
 template <int R, int W = 4>
 __device__ __forceinline__ void stage_kmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane) {
@@ -86,18 +90,21 @@ __device__ __forceinline__ void stage_kmajor(__amdgpu_buffer_rsrc_t r, int64_t l
 }
 
 // Row-contiguous tile: 32 k-rows of R elements; descriptor base at (slab's
-// first k, tile's first column).
+// first k, tile's first column). Load q (of R / 64) of a wave fills 1 KB.
+template <int R, int W = 4>
+__device__ __forceinline__ void load_mnmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane,
+                                             int q) {
+  constexpr int RB = R * 2;
+  const int byte0 = (q * 4 + wave) * 1024;
+  const int byte = byte0 + lane * 16;
+  const int k = byte / RB;
+  const int g = ((byte % RB) >> 4) ^ swz_k<R>(k);
+  load_lds16<W>(r, static_cast<uint32_t>(k * ld * 2 + g * 16), dst + byte0);
+}
 template <int R, int W = 4>
 __device__ __forceinline__ void stage_mnmajor(__amdgpu_buffer_rsrc_t r, int64_t ld, uint32_t dst, int wave, int lane) {
-  constexpr int RB = R * 2;
 #pragma unroll
-  for (int q = 0; q < R / 64; ++q) {
-    const int byte0 = (q * 4 + wave) * 1024;
-    const int byte = byte0 + lane * 16;
-    const int k = byte / RB;
-    const int g = ((byte % RB) >> 4) ^ swz_k<R>(k);
-    load_lds16<W>(r, static_cast<uint32_t>(k * ld * 2 + g * 16), dst + byte0);
-  }
+  for (int q = 0; q < R / 64; ++q) load_mnmajor<R, W>(r, ld, dst, wave, lane, q);
 }
 
 // Fragment (32 rows x 16 k) of a K-contiguous tile: lane -> row rb + lane%32,
