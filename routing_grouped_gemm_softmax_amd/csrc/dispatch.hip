@@ -369,7 +369,9 @@ __global__ void transpose_router_kernel(const T* __restrict__ w, int d, int E, T
 }
 
 // dx[t] = sum_j dxp[row(t,j)] (+ sum_{e: dl[t][e] != 0} dl[t][e] * W_rT[e]).
-// dl is zero off the chosen set, so only those k columns are read.
+// dl is zero off the chosen set, so only those (at most k) columns are read.
+// When a token has whole waves (lpt >= 64) each wave finds them with one
+// ballot per 64 experts; narrower rows scan the E values per lane.
 template <typename T>
 __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__ dxp, const int32_t* __restrict__ row_of_slot,
                                                            const float* __restrict__ dl, const T* __restrict__ wt,
@@ -383,6 +385,36 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
   int rows[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) rows[j] = j < k ? row_of_slot[static_cast<int64_t>(t) * k + j] : -1;
+  // The token's router columns: (expert, dl) pairs, at most 8.
+  int ce[8];
+  float cv[8];
+  int nr = 0;
+  if (dl != nullptr) {
+    const float* dlt = dl + static_cast<int64_t>(t) * E;
+    if (lpt >= kWave) {
+      const int lane = threadIdx.x & (kWave - 1);
+      for (int c0 = 0; c0 < E; c0 += kWave) {
+        const float c = (c0 + lane < E) ? dlt[c0 + lane] : 0.0f;
+        uint64_t m = __ballot(c != 0.0f);
+        while (m != 0 && nr < 8) {
+          const int b = __ffsll(static_cast<long long>(m)) - 1;
+          m &= m - 1;
+          ce[nr] = c0 + b;
+          cv[nr] = __shfl(c, b, kWave);
+          ++nr;
+        }
+      }
+    } else {
+      for (int e = 0; e < E && nr < 8; ++e) {
+        const float c = dlt[e];
+        if (c != 0.0f) {
+          ce[nr] = e;
+          cv[nr] = c;
+          ++nr;
+        }
+      }
+    }
+  }
   for (int v = sub; v < nvec; v += lpt) {
     float acc[VE];
 #pragma unroll
@@ -395,16 +427,11 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
 #pragma unroll
       for (int i = 0; i < VE; ++i) acc[i] += gv[i];
     }
-    if (dl != nullptr) {
-      const float* dlt = dl + static_cast<int64_t>(t) * E;
-      for (int e = 0; e < E; ++e) {
-        const float c = dlt[e];
-        if (c == 0.0f) continue;
-        float wv[VE];
-        unpack16(ld16(wt + e * re + v * VE), wv);
+    for (int r = 0; r < nr; ++r) {
+      float wv[VE];
+      unpack16(ld16(wt + ce[r] * re + v * VE), wv);
 #pragma unroll
-        for (int i = 0; i < VE; ++i) acc[i] = fmaf(c, wv[i], acc[i]);
-      }
+      for (int i = 0; i < VE; ++i) acc[i] = fmaf(cv[r], wv[i], acc[i]);
     }
     st16(dx + t * re + v * VE, pack16(acc));
   }
