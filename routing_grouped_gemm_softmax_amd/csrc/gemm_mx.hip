@@ -75,64 +75,86 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
     const uint8_t* B1 = static_cast<const uint8_t*>(p.b1);
 
     // ---- HBM -> LDS for slab kt (empty descriptors at or past the end) -------------------
+    // Each wave issues kLoads loads per slab: [0, LM) the M tile, [LM, LM + LN)
+    // the N tile, then one 1 KB scale load: wave 0 the M side's scales, wave 1
+    // the N side's (the gate half for FWD_GU), wave 2 the up half's for FWD_GU;
+    // the remaining waves load nothing into their own area, so every wave
+    // issues the same count (the vmcnt waits count them).
+    constexpr int LM = BM / 64, LN = BN / 64, kLoads = LM + LN + 1;
     // W: wait states of the loads (load_lds16): 4 where a descriptor may have
     // just been written by a VALU instruction, 0 in the steady-state loop.
-    auto stage = [&](int kt, uint32_t slot, auto w) {
-      constexpr int W = decltype(w)::value;
+    auto issue = [&](int kt, uint32_t slot, auto L, auto w) {
+      constexpr int l = decltype(L)::value, W = decltype(w)::value;
       const bool live = kt < nk;
-      const uint32_t sc = slot + TILE_M + TILE_N + wave * kScaleArea;
-      const uint32_t voff = static_cast<uint32_t>(lane * 16);
-      // M side (rows of the A operand) and its scales (wave 0).
-      if constexpr (MODE == WGRAD) {
-        const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
-        stage_rows64<BM, W>(make_rsrc(A + m0 * p.lda + k0, live ? BM * p.lda : 0), p.lda, slot, wave, lane);
-        if (wave == 0) load_lds16<W>(make_rsrc(p.as + (k0 / 64) * p.as_slab + m0 * 2, live ? BM * 2 : 0), voff, sc);
-      } else {
-        const int valid = live ? min(BM, row_end - row0) : 0;
-        stage_rows64<BM, W>(make_rsrc(A + static_cast<int64_t>(row0) * p.lda + kt * 64, static_cast<int64_t>(valid) * p.lda),
-                         p.lda, slot, wave, lane);
-        // Buffer range checks are per dword: round the range up to whole dwords
-        // or an odd row count loses its last row's scales. The extra bytes are
-        // the scales of a row whose data reads as zero (it is never written).
-        if (wave == 0)
-          load_lds16<W>(make_rsrc(p.as + static_cast<int64_t>(kt) * p.as_slab + row0 * 2, (valid * 2 + 3) & ~3), voff,
-                     sc);
-      }
-      // N side and its scales (waves 1, 2); wave 3 (and 2 outside FWD_GU) loads nothing.
-      const uint32_t tn = slot + TILE_M;
-      if constexpr (MODE == FWD_GU) {
-        const int fb = nt * (BN / 2);
-        const int64_t off = bexp + static_cast<int64_t>(fb) * p.ldb + kt * 64;
-        const int64_t bytes = live ? static_cast<int64_t>(BN / 2) * p.ldb : 0;
-        stage_rows64<BN / 2, W>(make_rsrc(B0 + off, bytes), p.ldb, tn, wave, lane);
-        stage_rows64<BN / 2, W>(make_rsrc(B1 + off, bytes), p.ldb, tn + TILE_N / 2, wave, lane);
-        const int64_t so = bsexp + static_cast<int64_t>(kt) * p.bs_slab + fb * 2;
-        if (wave == 1) load_lds16<W>(make_rsrc(p.bs0 + so, live ? BN : 0), voff, sc);
-        if (wave == 2) load_lds16<W>(make_rsrc(p.bs1 + so, live ? BN : 0), voff, sc);
-      } else if constexpr (MODE == WGRAD) {
-        const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
-        stage_rows64<BN, W>(make_rsrc(B0 + n0 * p.ldb + k0, live ? BN * p.ldb : 0), p.ldb, tn, wave, lane);
-        if (wave == 1) load_lds16<W>(make_rsrc(p.bs0 + (k0 / 64) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff, sc);
-      } else {  // FWD_DOWN, BWD_DOWN, BWD_GU: B stored [n][k] per expert
-        const uint8_t* src = B0;
-        const uint8_t* ssrc = p.bs0;
-        int ks = kt;
-        if constexpr (MODE == BWD_GU) {
-          if (kt * 64 >= p.f) { src = B1; ssrc = p.bs1; ks = kt - p.f / 64; }
+      if constexpr (l < LM) {
+        if constexpr (MODE == WGRAD) {
+          const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
+          load_rows64<BM, W>(make_rsrc(A + m0 * p.lda + k0, live ? BM * p.lda : 0), p.lda, slot, wave, lane, l);
+        } else {
+          const int valid = live ? min(BM, row_end - row0) : 0;
+          load_rows64<BM, W>(make_rsrc(A + static_cast<int64_t>(row0) * p.lda + kt * 64,
+                                       static_cast<int64_t>(valid) * p.lda),
+                             p.lda, slot, wave, lane, l);
         }
-        stage_rows64<BN, W>(make_rsrc(src + bexp + static_cast<int64_t>(n0) * p.ldb + ks * 64,
-                                   live ? static_cast<int64_t>(BN) * p.ldb : 0),
-                         p.ldb, tn, wave, lane);
-        if (wave == 1)
-          load_lds16<W>(make_rsrc(ssrc + bsexp + static_cast<int64_t>(ks) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff,
-                     sc);
+      } else if constexpr (l < LM + LN) {
+        constexpr int q = l - LM;
+        const uint32_t tn = slot + TILE_M;
+        if constexpr (MODE == FWD_GU) {
+          constexpr int half = q / (LN / 2), qq = q % (LN / 2);
+          const int64_t off = bexp + static_cast<int64_t>(nt * (BN / 2)) * p.ldb + kt * 64;
+          const int64_t bytes = live ? static_cast<int64_t>(BN / 2) * p.ldb : 0;
+          load_rows64<BN / 2, W>(make_rsrc((half ? B1 : B0) + off, bytes), p.ldb, tn + half * (TILE_N / 2), wave,
+                                 lane, qq);
+        } else if constexpr (MODE == WGRAD) {
+          const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
+          load_rows64<BN, W>(make_rsrc(B0 + n0 * p.ldb + k0, live ? BN * p.ldb : 0), p.ldb, tn, wave, lane, q);
+        } else {  // FWD_DOWN, BWD_DOWN, BWD_GU: B stored [n][k] per expert
+          const uint8_t* src = B0;
+          int ks = kt;
+          if constexpr (MODE == BWD_GU) {
+            if (kt * 64 >= p.f) { src = B1; ks = kt - p.f / 64; }
+          }
+          load_rows64<BN, W>(make_rsrc(src + bexp + static_cast<int64_t>(n0) * p.ldb + ks * 64,
+                                       live ? static_cast<int64_t>(BN) * p.ldb : 0),
+                             p.ldb, tn, wave, lane, q);
+        }
+      } else {
+        const uint32_t sc = slot + TILE_M + TILE_N + wave * kScaleArea;
+        const uint32_t voff = static_cast<uint32_t>(lane * 16);
+        if (wave == 0) {
+          if constexpr (MODE == WGRAD) {
+            const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
+            load_lds16<W>(make_rsrc(p.as + (k0 / 64) * p.as_slab + m0 * 2, live ? BM * 2 : 0), voff, sc);
+          } else {
+            // Buffer range checks are per dword: round the range up to whole
+            // dwords or an odd row count loses its last row's scales. The extra
+            // bytes are the scales of a row whose data reads as zero (it is
+            // never written).
+            const int valid = live ? min(BM, row_end - row0) : 0;
+            load_lds16<W>(make_rsrc(p.as + static_cast<int64_t>(kt) * p.as_slab + row0 * 2, (valid * 2 + 3) & ~3),
+                          voff, sc);
+          }
+        } else if (wave == 1 || (wave == 2 && MODE == FWD_GU)) {
+          if constexpr (MODE == FWD_GU) {
+            const int64_t so = bsexp + static_cast<int64_t>(kt) * p.bs_slab + nt * (BN / 2) * 2;
+            load_lds16<W>(make_rsrc((wave == 1 ? p.bs0 : p.bs1) + so, live ? BN : 0), voff, sc);
+          } else if constexpr (MODE == WGRAD) {
+            const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
+            load_lds16<W>(make_rsrc(p.bs0 + (k0 / 64) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff, sc);
+          } else {
+            const uint8_t* ssrc = p.bs0;
+            int ks = kt;
+            if constexpr (MODE == BWD_GU) {
+              if (kt * 64 >= p.f) { ssrc = p.bs1; ks = kt - p.f / 64; }
+            }
+            load_lds16<W>(make_rsrc(ssrc + bsexp + static_cast<int64_t>(ks) * p.bs_slab + n0 * 2, live ? BN * 2 : 0),
+                          voff, sc);
+          }
+        } else {
+          load_lds16<W>(make_rsrc(p.as, 0), voff, sc);
+        }
       }
-      // Every wave issues the same number of loads per slab (the vmcnt waits
-      // count them): the remaining waves load nothing into their own area.
-      const bool extra = (wave == 3) || (wave == 2 && MODE != FWD_GU);
-      if (extra) load_lds16<W>(make_rsrc(p.as, 0), voff, sc);
     };
-    constexpr int kLoads = BM / 64 + BN / 64 + 1;  // per wave per slab
 
     floatx16 acc[NB][MB];
 #pragma unroll
@@ -146,21 +168,21 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
       v8i m[MB], n[NB];
       int sm[MB], sn[NB];
     };
-    auto read_frags = [&](const char* slotp, Frags& F) {
+    // Fragment FI (compile time) and its scale: [0, MB) M side, [MB, MB + NB) N side.
+    auto read_frag = [&](const char* slotp, Frags& F, auto FI) {
+      constexpr int fi = decltype(FI)::value;
       const char* tm = slotp;
       const char* tn = slotp + TILE_M;
       const uint8_t* sc = reinterpret_cast<const uint8_t*>(slotp + TILE_M + TILE_N);
       const int r32 = lane & 31, kb = lane >> 5;
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int row = wm * WM + i * 32;
-        F.m[i] = frag_mx(tm, row, lane);
-        F.sm[i] = sc[(row + r32) * 2 + kb];
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
+      if constexpr (fi < MB) {
+        const int row = wm * WM + fi * 32;
+        F.m[fi] = frag_mx(tm, row, lane);
+        F.sm[fi] = sc[(row + r32) * 2 + kb];
+      } else {
+        constexpr int j = fi - MB;
         if constexpr (MODE == FWD_GU) {
-          const int half = j / (NB / 2), jj = j % (NB / 2);
+          constexpr int half = j / (NB / 2), jj = j % (NB / 2);
           const int row = wn * (WN / 2) + jj * 32;
           F.n[j] = frag_mx(tn + half * (TILE_N / 2), row, lane);
           F.sn[j] = sc[(1 + half) * kScaleArea + (row + r32) * 2 + kb];
@@ -171,43 +193,42 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
         }
       }
     };
-    auto mfma_all = [&](const Frags& F) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.n[j], F.m[i], acc[j][i], 0, 0, 0, F.sn[j], 0,
-                                                                     F.sm[i]);
+    auto mfma_one = [&](const Frags& F, auto MI) {
+      constexpr int mi = decltype(MI)::value, j = mi / MB, i = mi % MB;
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.n[j], F.m[i], acc[j][i], 0, 0, 0, F.sn[j], 0,
+                                                                 F.sm[i]);
     };
-    constexpr int kReads = 2 * (MB + NB) + (MB + NB);  // data halves + scale bytes
-    constexpr int kMfma = MB * NB;
+    constexpr int kMfma = MB * NB, kFrags = MB + NB;
 
     const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 #pragma unroll
-    for (int s0 = 0; s0 < kStagesX; ++s0) stage(s0, ring + s0 * STAGE, std::integral_constant<int, 4>{});
-    // One slab: wait for slab kt+1, barrier, refill slot kt with slab kt+4, read
-    // slab kt+1 into `nxt` while slab kt's MFMAs run on `cur`. Two register sets
-    // with fixed names (the loop is unrolled by two: a runtime index would put
-    // them in scratch memory).
+    for (int s0 = 0; s0 < kStagesX; ++s0)
+      static_for<kLoads>([&](auto L) { issue(s0, ring + s0 * STAGE, L, std::integral_constant<int, 4>{}); });
+    // One slab: wait for slab kt+1, barrier, then slab kt's MFMAs on `cur`
+    // with the reads of slab kt+1 into `nxt` and the loads of slab kt+4 into
+    // slot kt spread between them (a burst of LDS-DMA loads would back up the
+    // texture-address unit into the issue of the MFMAs behind it). Two
+    // register sets with fixed names (the loop is unrolled by two: a runtime
+    // index would put them in scratch memory).
     auto step = [&](int kt, const Frags& cur, Frags& nxt) {
       wait_vmcnt<kLoads * (kStagesX - 2)>();   // slab kt+1 has landed
       __syncthreads();                          // slot kt is read out; slab kt+1 is visible
-      stage(kt + kStagesX, ring + (kt % kStagesX) * STAGE, std::integral_constant<int, 0>{});
-      read_frags(smem + ((kt + 1) % kStagesX) * STAGE, nxt);
-      mfma_all(cur);
-      constexpr int inter = kReads < kMfma ? kReads : kMfma;
-#pragma unroll
-      for (int r = 0; r < inter; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
-      if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+      const char* nslot = smem + ((kt + 1) % kStagesX) * STAGE;
+      const uint32_t slot = ring + (kt % kStagesX) * STAGE;
+      static_for<kLoads>([&](auto S) {
+        constexpr int sg = decltype(S)::value;
+        constexpr int m_lo = sg * kMfma / kLoads, m_hi = (sg + 1) * kMfma / kLoads;
+        constexpr int f_lo = sg * kFrags / kLoads, f_hi = (sg + 1) * kFrags / kLoads;
+        static_for<m_hi - m_lo>([&](auto D) { mfma_one(cur, std::integral_constant<int, m_lo + decltype(D)::value>{}); });
+        static_for<f_hi - f_lo>([&](auto D) { read_frag(nslot, nxt, std::integral_constant<int, f_lo + decltype(D)::value>{}); });
+        issue(kt + kStagesX, slot, S, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
     Frags f0, f1;
     wait_vmcnt<kLoads * (kStagesX - 1)>();
     __syncthreads();
-    read_frags(smem, f0);
+    static_for<kFrags>([&](auto FI) { read_frag(smem, f0, FI); });
     for (int kt = 0; kt < nk; kt += 2) {
       step(kt, f0, f1);
       if (kt + 1 < nk) step(kt + 1, f1, f0);
