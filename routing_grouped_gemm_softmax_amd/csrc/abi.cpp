@@ -77,8 +77,12 @@ int check_ffn_dtype(const moe_shape* s, const char* who) {
     if (_e != hipSuccess) return hip_fail(_e, __func__);      \
   } while (0)
 
+// G, U, H planes; MXFP8 layers add the backward's quantised weight copies.
+size_t save_planes(const moe_shape* s) {
+  return ((size_t)3 * s->T * s->k * s->f * elem_bytes(s->dtype) + 255) & ~(size_t)255;
+}
 size_t save_bytes_for(const moe_shape* s) {
-  return (size_t)3 * s->T * s->k * s->f * elem_bytes(s->dtype);
+  return save_planes(s) + (s->dtype == MOE_MXFP8 ? moe::ffn_mx_save_extra((int)s->d, (int)s->f, (int)s->E) : 0);
 }
 
 }  // namespace
@@ -185,6 +189,7 @@ int moe_grouped_ffn_fwd(const void* xp, const void* w_gate, const void* w_up, co
   a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
   const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
   a.G = save; a.U = static_cast<char*>(save) + plane; a.H = static_cast<char*>(save) + 2 * plane;
+  a.mx_save = static_cast<char*>(save) + save_planes(s);
   a.o = o_out;
   if (s->dtype == MOE_MXFP8)
     LAUNCH(moe::launch_ffn_mx_fwd(a, ws, as_stream(stream)));
@@ -227,6 +232,7 @@ int moe_grouped_ffn_bwd(const void* d_o, const void* xp, const void* w_gate, con
   const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
   char* sv = const_cast<char*>(static_cast<const char*>(save));
   a.G = sv; a.U = sv + plane; a.H = sv + 2 * plane;
+  a.mx_save = sv + save_planes(s);
   a.d_o = d_o; a.dgu = ws; a.dxp = dxp_out; a.dw_gate = dw_gate_out; a.dw_up = dw_up_out; a.dw_down = dw_down_out;
   if (s->dtype == MOE_MXFP8) {
     const size_t dgu = ((size_t)a.S * 2 * a.f * 2 + 255) & ~(size_t)255;

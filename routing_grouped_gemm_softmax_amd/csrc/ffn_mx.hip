@@ -55,9 +55,26 @@ FwdWs carve_fwd(char* base, int S, int d, int f, int E, size_t* total) {
   return o;
 }
 
+// Save-buffer region of an MXFP8 layer: the columns-blocked weight copies the
+// backward's dgrad GEMMs use, written by the forward's weight pass.
+struct SaveMx {
+  uint8_t *wgq, *wgs, *wuq, *wus, *wdq, *wds;
+};
+SaveMx carve_save(char* base, int d, int f, int E, size_t* total) {
+  Carve c{base};
+  const size_t w = static_cast<size_t>(E) * d * f;
+  SaveMx o;
+  o.wgq = c.take(w); o.wgs = c.take(w / 32);
+  o.wuq = c.take(w); o.wus = c.take(w / 32);
+  o.wdq = c.take(w); o.wds = c.take(w / 32);
+  if (total) *total = c.used;
+  return o;
+}
+
 struct BwdWs {
-  uint8_t *doq, *dos, *wdq, *wds, *dguq, *dgus, *wgq, *wgs, *wuq, *wus;
+  uint8_t *doq, *dos, *dguq, *dgus;
   int32_t* poff;
+  uint8_t* blk;  // block table of the grouped transposing quantiser
   uint8_t *ht, *hts, *dot, *dots, *xt, *xts, *dgut, *dguts;
 };
 BwdWs carve_bwd(char* base, int S, int d, int f, int E, size_t* total) {
@@ -67,11 +84,9 @@ BwdWs carve_bwd(char* base, int S, int d, int f, int E, size_t* total) {
   const size_t P = static_cast<size_t>(padded_rows(S, E));
   BwdWs o;
   o.doq = c.take(sd); o.dos = c.take(sd / 32);
-  o.wdq = c.take(w); o.wds = c.take(w / 32);
   o.dguq = c.take(s2f); o.dgus = c.take(s2f / 32);
-  o.wgq = c.take(w); o.wgs = c.take(w / 32);
-  o.wuq = c.take(w); o.wus = c.take(w / 32);
   o.poff = reinterpret_cast<int32_t*>(c.take(static_cast<size_t>(E + 1) * 4));
+  o.blk = c.take(P / 64 * 8);
   o.ht = c.take(P * f); o.hts = c.take(P * f / 32);
   o.dot = c.take(P * d); o.dots = c.take(P * d / 32);
   o.xt = c.take(P * d); o.xts = c.take(P * d / 32);
@@ -94,6 +109,12 @@ size_t ffn_mx_fwd_workspace(int S, int d, int f, int E) {
   return n;
 }
 
+size_t ffn_mx_save_extra(int d, int f, int E) {
+  size_t n = 0;
+  carve_save(nullptr, d, f, E, &n);
+  return n;
+}
+
 size_t ffn_mx_bwd_workspace(int S, int d, int f, int E) {
   size_t n = 0;
   carve_bwd(nullptr, S, d, f, E, &n);
@@ -104,10 +125,15 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
   const int S = a.S, d = a.d, f = a.f, E = a.E;
   const FwdWs w = carve_fwd(static_cast<char*>(ws), S, d, f, E, nullptr);
   const int64_t wsz = static_cast<int64_t>(d) * f;
-  // Operands: Xp along d; W_gate, W_up along d, transposed to [f][d].
+  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), d, f, E, nullptr);
+  // Operands: Xp along d; W_gate, W_up along d, transposed to [f][d]. The same
+  // read of each weight also writes its copy blocked along f ([d][f], in the
+  // save buffer) for the backward's dXp GEMM.
   TRY(launch_mx_kmajor(a.xp, S, d, 1, 0, w.xq, 0, w.xs, 0, s));
-  TRY(launch_mx_tgroup(a.w_gate, d, f, nullptr, nullptr, 1, E, wsz, w.wgq, d, wsz, w.wgs, wsz / 32, s));
-  TRY(launch_mx_tgroup(a.w_up, d, f, nullptr, nullptr, 1, E, wsz, w.wuq, d, wsz, w.wus, wsz / 32, s));
+  TRY(launch_mx_tgroup(a.w_gate, d, f, nullptr, E, wsz, w.wgq, d, wsz, w.wgs, wsz / 32, s, sv.wgq,
+                       sv.wgs));
+  TRY(launch_mx_tgroup(a.w_up, d, f, nullptr, E, wsz, w.wuq, d, wsz, w.wus, wsz / 32, s, sv.wuq,
+                       sv.wus));
   {
     GemmParams p{};
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
@@ -117,9 +143,11 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
     p.c0 = a.G; p.c1 = a.U; p.c2 = a.H; p.ldc = f; p.N = 2 * f; p.K = d;
     TRY(launch_mx_ragged(FWD_GU, p, s));
   }
-  // Operands: H along f; W_down along f, transposed to [d][f].
+  // Operands: H along f; W_down along f, transposed to [d][f] (and its copy
+  // blocked along d, [f][d], for the backward's dH GEMM).
   TRY(launch_mx_kmajor(a.H, S, f, 1, 0, w.hq, 0, w.hs, 0, s));
-  TRY(launch_mx_tgroup(a.w_down, f, d, nullptr, nullptr, 1, E, wsz, w.wdq, f, wsz, w.wds, wsz / 32, s));
+  TRY(launch_mx_tgroup(a.w_down, f, d, nullptr, E, wsz, w.wdq, f, wsz, w.wds, wsz / 32, s, sv.wdq,
+                       sv.wds));
   GemmParams q{};
   q.offsets = a.offsets; q.E = E; q.S = S; q.f = f;
   q.a = w.hq; q.lda = f; q.as = w.hs; q.as_slab = 2LL * S;
@@ -131,35 +159,36 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
 hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
   const int S = a.S, d = a.d, f = a.f, E = a.E;
   const BwdWs w = carve_bwd(static_cast<char*>(ws), S, d, f, E, nullptr);
+  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), d, f, E, nullptr);
   const int64_t wsz = static_cast<int64_t>(d) * f;
   const int64_t P = padded_rows(S, E);
-  {  // dGU = SwiGLU'(q(dO) q(W_down)^T): dO and W_down [f][d] along d.
+  {  // dGU = SwiGLU'(q(dO) q(W_down)^T): dO along d; W_down [f][d] along d
+     // was quantised by the forward.
     TRY(launch_mx_kmajor(a.d_o, S, d, 1, 0, w.doq, 0, w.dos, 0, s));
-    TRY(launch_mx_kmajor(a.w_down, f, d, E, wsz, w.wdq, wsz, w.wds, wsz / 32, s));
     GemmParams p{};
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
     p.a = w.doq; p.lda = d; p.as = w.dos; p.as_slab = 2LL * S;
-    p.b0 = w.wdq; p.ldb = d; p.bstride = wsz; p.bs0 = w.wds; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
+    p.b0 = sv.wdq; p.ldb = d; p.bstride = wsz; p.bs0 = sv.wds; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
     p.c0 = a.dgu; p.ldc = 2 * f; p.e0 = a.G; p.e1 = a.U; p.N = f; p.K = d;
     TRY(launch_mx_ragged(BWD_DOWN, p, s));
   }
-  {  // dXp = q(dGU) q([W_gate | W_up])^T: dGU and the weights [d][f] along f.
+  {  // dXp = q(dGU) q([W_gate | W_up])^T: dGU along f; the weights [d][f]
+     // along f were quantised by the forward.
     TRY(launch_mx_kmajor(a.dgu, S, 2 * f, 1, 0, w.dguq, 0, w.dgus, 0, s));
-    TRY(launch_mx_kmajor(a.w_gate, d, f, E, wsz, w.wgq, wsz, w.wgs, wsz / 32, s));
-    TRY(launch_mx_kmajor(a.w_up, d, f, E, wsz, w.wuq, wsz, w.wus, wsz / 32, s));
     GemmParams p{};
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
     p.a = w.dguq; p.lda = 2 * f; p.as = w.dgus; p.as_slab = 2LL * S;
-    p.b0 = w.wgq; p.b1 = w.wuq; p.ldb = f; p.bstride = wsz;
-    p.bs0 = w.wgs; p.bs1 = w.wus; p.bs_slab = 2LL * d; p.bs_estride = wsz / 32;
+    p.b0 = sv.wgq; p.b1 = sv.wuq; p.ldb = f; p.bstride = wsz;
+    p.bs0 = sv.wgs; p.bs1 = sv.wus; p.bs_slab = 2LL * d; p.bs_estride = wsz / 32;
     p.c0 = a.dxp; p.ldc = d; p.N = d; p.K = 2 * f;
     TRY(launch_mx_ragged(BWD_GU, p, s));
   }
   // Weight gradients: every operand along the expert's tokens, transposed.
   TRY(launch_mx_poff(a.offsets, E, w.poff, s));
+  TRY(launch_mx_blocks(a.offsets, w.poff, E, P, w.blk, s));
   {  // dW_down[e] = q(H_e)^T q(dO_e)
-    TRY(launch_mx_tgroup(a.H, S, f, a.offsets, w.poff, E, 1, 0, w.ht, P, 0, w.hts, 0, s));
-    TRY(launch_mx_tgroup(a.d_o, S, d, a.offsets, w.poff, E, 1, 0, w.dot, P, 0, w.dots, 0, s));
+    TRY(launch_mx_tgroup(a.H, S, f, w.blk, 1, 0, w.ht, P, 0, w.hts, 0, s));
+    TRY(launch_mx_tgroup(a.d_o, S, d, w.blk, 1, 0, w.dot, P, 0, w.dots, 0, s));
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
     p.a = w.ht; p.lda = P; p.as = w.hts; p.as_slab = 2LL * f;
@@ -168,8 +197,8 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
     TRY(launch_mx_wgrad(p, s));
   }
   {  // [dW_gate | dW_up][e] = q(Xp_e)^T q(dGU_e)
-    TRY(launch_mx_tgroup(a.xp, S, d, a.offsets, w.poff, E, 1, 0, w.xt, P, 0, w.xts, 0, s));
-    TRY(launch_mx_tgroup(a.dgu, S, 2 * f, a.offsets, w.poff, E, 1, 0, w.dgut, P, 0, w.dguts, 0, s));
+    TRY(launch_mx_tgroup(a.xp, S, d, w.blk, 1, 0, w.xt, P, 0, w.xts, 0, s));
+    TRY(launch_mx_tgroup(a.dgu, S, 2 * f, w.blk, 1, 0, w.dgut, P, 0, w.dguts, 0, s));
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
     p.a = w.xt; p.lda = P; p.as = w.xts; p.as_slab = 2LL * d;

@@ -25,6 +25,9 @@ struct FfnArgs {
   void* dw_gate;
   void* dw_up;
   void* dw_down;
+  // MXFP8: the save-buffer region the forward fills with the backward's
+  // quantised weight copies (ffn_mx_save_extra bytes).
+  void* mx_save;
 };
 
 hipError_t launch_ffn_fwd(const FfnArgs& a, bool is_f32, hipStream_t s);
@@ -71,13 +74,20 @@ hipError_t launch_mx_kmajor(const void* in, int R, int C, int batches, int64_t i
                             int64_t q_bstride, uint8_t* s, int64_t s_bstride, hipStream_t st);
 // ... or K along the rows, transposed to q [C][P], blocked inside the row
 // groups of offsets (padded to 64 rows as poff says), or one group if NULL.
-hipError_t launch_mx_tgroup(const void* in, int R, int C, const int32_t* offsets, const int32_t* poff, int E,
-                            int batches, int64_t in_bstride, uint8_t* q, int64_t P, int64_t q_bstride, uint8_t* s,
-                            int64_t s_bstride, hipStream_t st);
+// blk: the block table of launch_mx_blocks (nullptr: one group of R rows).
+// qk, sk (optional, one group only): also write the columns-blocked copy in
+// launch_mx_kmajor's layout from the same read.
+hipError_t launch_mx_tgroup(const void* in, int R, int C, const void* blk, int batches, int64_t in_bstride,
+                            uint8_t* q, int64_t P, int64_t q_bstride, uint8_t* s, int64_t s_bstride, hipStream_t st,
+                            uint8_t* qk = nullptr, uint8_t* sk = nullptr);
+// Block table of the grouped transposing quantiser (P/64 entries of 8 bytes).
+hipError_t launch_mx_blocks(const int32_t* offsets, const int32_t* poff, int E, int64_t P, void* blk, hipStream_t st);
 hipError_t launch_mx_poff(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
 
 // MXFP8 expert FFN (ffn_mx.hip): workspace bytes and launch.
 size_t ffn_mx_fwd_workspace(int S, int d, int f, int E);
+// Extra save-buffer bytes of an MXFP8 layer (the backward's weight copies).
+size_t ffn_mx_save_extra(int d, int f, int E);
 size_t ffn_mx_bwd_workspace(int S, int d, int f, int E);
 hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s);

@@ -1,8 +1,9 @@
 // MXFP8 element and scale encoding (OCP Microscaling Formats v1.0): E4M3
 // ("FN": bias 7, max 448, no infinities) elements with one E8M0 scale
-// 2^(floor(log2 amax) - 8) per block of 32, written with exact operations
-// only (power-of-two scaling, round-half-even to an integer, comparisons).
-// Shared by every quantiser so they all produce the same bytes.
+// 2^(floor(log2 amax) - 8) per block of 32. e4m3_encode spells the element
+// rounding out with exact integer operations; the quantisers use the
+// hardware conversion (e4m3_encode4), which gives the same bytes on their
+// inputs. Shared by every quantiser so they all produce the same bytes.
 #pragma once
 
 #include <math.h>
@@ -46,18 +47,28 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | code;
 }
 
+// E4M3 codes of four values already divided by their block scale (|y| <
+// 512), packed little-endian: the hardware conversion (round to nearest even)
+// of each value clamped to +-448. On every such value that is a bf16 number
+// times a power of two (all inputs here) this gives e4m3_encode's byte,
+// signed zero included; the GPU tests pin it against the oracle's encoder.
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+  auto sat = [](float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), lo, true));
+}
+
 // Scale code and the 32 E4M3 codes of one block (v[] in fp32).
 __device__ __forceinline__ int mx_encode_block(const float (&v)[32], uint32_t (&w)[8]) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const int c = mx_scale_code(amax);
+  const int sh = 127 - c;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    w[i] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[i] |= e4m3_encode(ldexpf(v[i * 4 + j], 127 - c)) << (8 * j);
-  }
+  for (int i = 0; i < 8; ++i)
+    w[i] = e4m3_encode4(ldexpf(v[i * 4], sh), ldexpf(v[i * 4 + 1], sh), ldexpf(v[i * 4 + 2], sh),
+                        ldexpf(v[i * 4 + 3], sh));
   return c;
 }
 

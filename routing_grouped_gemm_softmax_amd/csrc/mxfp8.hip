@@ -82,95 +82,160 @@ hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int
 // slab-major (per 64-k slab, 2 bytes per row: the slab's two 32-blocks).
 // ---------------------------------------------------------------------------------
 
-// K along the columns: in [R][C] -> q [R][C], s [C/64][R][2]. One thread per
-// 64-column chunk of a row; consecutive threads take consecutive rows so the
-// 2-byte scale pairs land contiguously. Batched (weights: one batch per expert).
-__global__ __launch_bounds__(256) void mx_kmajor_kernel(const bf16_t* __restrict__ in, int R, int C, int64_t n,
+// Eight consecutive values of one block (block scale code c) -> 8 E4M3 bytes.
+__device__ __forceinline__ uint2 encode8(const float (&v)[8], int c) {
+  const int sh = 127 - c;
+  return make_uint2(e4m3_encode4(ldexpf(v[0], sh), ldexpf(v[1], sh), ldexpf(v[2], sh), ldexpf(v[3], sh)),
+                    e4m3_encode4(ldexpf(v[4], sh), ldexpf(v[5], sh), ldexpf(v[6], sh), ldexpf(v[7], sh)));
+}
+
+// Block scale code of a 32-block held by 4 consecutive lanes (8 values each,
+// lane groups aligned to 4): the maximum over the group, by two butterflies.
+__device__ __forceinline__ int group4_code(const float (&v)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  return mx_scale_code(amax);
+}
+
+// K along the columns: in [R][C] -> q [R][C], s [C/64][R][2], batched (one
+// batch per expert for the weights). A wave covers tiles of 8 rows x 64
+// columns: lane l takes row l / 8, columns 8 (l % 8) .. +7, so each load is
+// 8 rows x 128 contiguous bytes, the 4 lanes of a 32-block find its maximum
+// by butterflies and each lane stores its 8 codes; lane 8r writes row r's two
+// scale bytes. Each wave takes kTilesPerWave consecutive tiles (row-major:
+// column slabs fastest), loading all of them before encoding any.
+constexpr int kTilesPerWave = 4;
+__global__ __launch_bounds__(256) void mx_kmajor_kernel(const bf16_t* __restrict__ in, int R, int C, int64_t ntiles,
                                                         int64_t in_bstride, uint8_t* __restrict__ q,
                                                         int64_t q_bstride, uint8_t* __restrict__ s,
                                                         int64_t s_bstride) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int64_t per = static_cast<int64_t>(R) * (C / 64);
-  const int64_t b = i / per, rem = i % per;
-  const int c64 = static_cast<int>(rem / R), r = static_cast<int>(rem % R);
-  const bf16_t* src = in + b * in_bstride + static_cast<int64_t>(r) * C + c64 * 64;
-  uint8_t* dq = q + b * q_bstride + static_cast<int64_t>(r) * C + c64 * 64;
-  int code[2];
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t per_batch = static_cast<int64_t>(R / 8) * (C / 64);
+  const int rl = lane >> 3, ch = lane & 7;
+  uint4 raw[kTilesPerWave];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float v[32];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float t[8];
-      unpack16(ld16(src + h * 32 + j * 8), t);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[j * 8 + u] = t[u];
-    }
-    uint32_t w[8];
-    code[h] = mx_encode_block(v, w);
-    uint4* d4 = reinterpret_cast<uint4*>(dq + h * 32);
-    d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  for (int u = 0; u < kTilesPerWave; ++u) {
+    const int64_t t = wave * kTilesPerWave + u;
+    if (t >= ntiles) continue;
+    const int64_t b = t / per_batch, rem = t % per_batch;
+    const int row = static_cast<int>(rem / (C / 64)) * 8 + rl, c64 = static_cast<int>(rem % (C / 64));
+    raw[u] = ld16(in + b * in_bstride + static_cast<int64_t>(row) * C + c64 * 64 + ch * 8);
   }
-  *reinterpret_cast<uint16_t*>(s + b * s_bstride + (static_cast<int64_t>(c64) * R + r) * 2) =
-      static_cast<uint16_t>(code[0] | (code[1] << 8));
+#pragma unroll
+  for (int u = 0; u < kTilesPerWave; ++u) {
+    const int64_t t = wave * kTilesPerWave + u;
+    if (t >= ntiles) continue;  // wave-uniform
+    const int64_t b = t / per_batch, rem = t % per_batch;
+    const int row = static_cast<int>(rem / (C / 64)) * 8 + rl, c64 = static_cast<int>(rem % (C / 64));
+    float v[8];
+    unpack16(raw[u], v);
+    const int code = group4_code(v);
+    *reinterpret_cast<uint2*>(q + b * q_bstride + static_cast<int64_t>(row) * C + c64 * 64 + ch * 8) =
+        encode8(v, code);
+    const int code_hi = __shfl(code, (lane & ~7) + 4, kWave);
+    if (ch == 0)
+      *reinterpret_cast<uint16_t*>(s + b * s_bstride + (static_cast<int64_t>(c64) * R + row) * 2) =
+          static_cast<uint16_t>(code | (code_hi << 8));
+  }
 }
 
 // K along the rows, written transposed: in [R][C] -> q [C][P], s [P/64][C][2],
-// blocked inside row groups. With `offsets` (E+1 ints) and `poff` (the same
-// groups padded to 64 rows, E+1 ints) group e's rows offsets[e].. land at
-// q columns poff[e].. and the padding reads as zeros; without them the batch
-// is one group of R rows (R a multiple of 64). One workgroup per (64 padded
-// rows, 64 columns): the tile goes through LDS so loads and stores are
-// row-contiguous.
-__global__ __launch_bounds__(128) void mx_tgroup_kernel(const bf16_t* __restrict__ in, int R, int C,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ poff, int E,
-                                                        int64_t in_bstride, uint8_t* __restrict__ q, int64_t P,
+// blocked inside row groups. With the block table `blk` (mx_blocks_kernel:
+// for each 64-column block of q, its first source row and how many of its
+// rows are real) group e's rows land at q columns poff[e].. (poff: the groups
+// padded to 64 rows) and the padding reads as zeros; without it the batch is
+// one group of R rows (R a multiple of 64). With qk != nullptr (one group
+// only) the same pass also writes the columns-blocked copy qk [R][C], sk
+// [C/64][R][2] (mx_kmajor_kernel's layout), so a weight is read once for both
+// of its GEMM layouts.
+//
+// One workgroup per (128 padded rows, 64 columns), each 64-row half resolving
+// its own group: the tile goes through LDS; each wave reads one 32-row block
+// of all 64 columns (thread = one column, 32 conflict-free 2-byte reads),
+// encodes it into an LDS output tile [64 columns][128 bytes], which then
+// leaves as full 128-byte rows of q.
+__global__ __launch_bounds__(256) void mx_tgroup_kernel(const bf16_t* __restrict__ in, int R, int C,
+                                                        const int2* __restrict__ blk, int64_t in_bstride, uint8_t* __restrict__ q, int64_t P,
                                                         int64_t q_bstride, uint8_t* __restrict__ s,
-                                                        int64_t s_bstride) {
-  __shared__ __attribute__((aligned(16))) bf16_t tile[64][64 + 8];
-  __shared__ int s_grp[2];
-  const int tid = threadIdx.x, sb = blockIdx.x, cc = blockIdx.y, b = blockIdx.z;
-  const int64_t p0 = static_cast<int64_t>(sb) * 64;
-  int src0 = 0, valid = 0;
-  if (poff == nullptr) {
-    src0 = static_cast<int>(p0);
-    valid = static_cast<int>(min(static_cast<int64_t>(64), static_cast<int64_t>(R) - p0));
-  } else {
-    // The group g with poff[g] <= p0 < poff[g+1] (at most one: empty groups
-    // have poff[g] == poff[g+1]).
-    if (tid == 0) s_grp[0] = -1;
-    __syncthreads();
-    for (int e = tid; e < E; e += 128)
-      if (poff[e] <= p0 && p0 < poff[e + 1]) s_grp[0] = e;
-    __syncthreads();
-    const int g = s_grp[0];
-    if (g < 0) return;  // past the last group: never read by the GEMM
-    src0 = offsets[g] + static_cast<int>(p0 - poff[g]);
-    valid = min(64, offsets[g + 1] - src0);
-  }
-  const bf16_t* src = in + static_cast<int64_t>(b) * in_bstride;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int id = tid + 128 * j, row = id >> 3, part = id & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < valid) v = ld16(src + static_cast<int64_t>(src0 + row) * C + cc * 64 + part * 8);
-    *reinterpret_cast<uint4*>(&tile[row][part * 8]) = v;
+                                                        int64_t s_bstride, uint8_t* __restrict__ qk,
+                                                        uint8_t* __restrict__ sk) {
+  constexpr int kLd = 64 + 8;      // bf16 per LDS input row (16-byte aligned rows)
+  constexpr int kLdq = 128 + 16;   // bytes per LDS output row
+  __shared__ __attribute__((aligned(16))) bf16_t tile[128][kLd];
+  __shared__ __attribute__((aligned(16))) uint8_t qt[64][kLdq];
+  __shared__ int s_src[2], s_valid[2];
+  const int tid = threadIdx.x, b = blockIdx.z;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const int c0 = blockIdx.y * 64;
+  if (tid < 2) {
+    const int64_t ph = p0 + 64 * tid;
+    int src = 0, valid = 0;
+    if (ph < P) {
+      if (blk == nullptr) {
+        src = static_cast<int>(ph);
+        valid = static_cast<int>(min(static_cast<int64_t>(64), static_cast<int64_t>(R) - ph));
+      } else {
+        const int2 t = blk[ph >> 6];
+        src = t.x;
+        valid = t.y;
+      }
+    }
+    s_src[tid] = src;
+    s_valid[tid] = valid;
   }
   __syncthreads();
-  const int c = tid & 63, blk = tid >> 6;
-  float v[32];
+  const bf16_t* src = in + static_cast<int64_t>(b) * in_bstride;
+  const int ch = tid & 7;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(tile[blk * 32 + i][c]);
-  uint32_t w[8];
-  const int code = mx_encode_block(v, w);
-  const int64_t col = static_cast<int64_t>(cc) * 64 + c;
-  uint4* dq = reinterpret_cast<uint4*>(q + static_cast<int64_t>(b) * q_bstride + col * P + p0 + blk * 32);
-  dq[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  dq[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  s[static_cast<int64_t>(b) * s_bstride + (static_cast<int64_t>(sb) * C + col) * 2 + blk] = static_cast<uint8_t>(code);
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (rr < s_valid[h]) v = ld16(src + static_cast<int64_t>(s_src[h] + rr) * C + c0 + ch * 8);
+    *reinterpret_cast<uint4*>(&tile[r][ch * 8]) = v;
+    if (qk != nullptr && p0 + r < P) {  // uniform per wave (a wave's 8 rows share a 64-row half)
+      // Columns-blocked copy straight from the registers (one group: row p0 + r).
+      float f[8];
+      unpack16(v, f);
+      const int code = group4_code(f);
+      const int64_t row = p0 + r;
+      *reinterpret_cast<uint2*>(qk + static_cast<int64_t>(b) * q_bstride + row * C + c0 + ch * 8) = encode8(f, code);
+      const int code_hi = __shfl(code, (tid & 56) + 4, kWave);
+      if (ch == 0)
+        *reinterpret_cast<uint16_t*>(sk + static_cast<int64_t>(b) * s_bstride +
+                                     (static_cast<int64_t>(c0 / 64) * R + row) * 2) =
+            static_cast<uint16_t>(code | (code_hi << 8));
+    }
+  }
+  __syncthreads();
+  {
+    const int col = tid & 63, block = tid >> 6;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(tile[block * 32 + i][col]);
+    uint32_t w[8];
+    const int code = mx_encode_block(v, w);
+    uint4* d = reinterpret_cast<uint4*>(&qt[col][block * 32]);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    if (p0 + block * 32 < P) {
+      const int64_t sb = (p0 >> 6) + (block >> 1);
+      s[static_cast<int64_t>(b) * s_bstride + (sb * C + c0 + col) * 2 + (block & 1)] = static_cast<uint8_t>(code);
+    }
+  }
+  __syncthreads();
+  // 64 columns x 128 bytes -> q rows, 8 lanes per 128-byte row.
+  const int64_t pvalid = min(static_cast<int64_t>(128), P - p0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = i * 32 + (tid >> 3), c16 = tid & 7;
+    if (c16 * 16 < pvalid)
+      *reinterpret_cast<uint4*>(q + static_cast<int64_t>(b) * q_bstride + static_cast<int64_t>(c0 + row) * P + p0 +
+                                c16 * 16) = *reinterpret_cast<const uint4*>(&qt[row][c16 * 16]);
+  }
 }
 
 // poff[e] = sum over e' < e of ceil(n_e' / 64) * 64 (one wave; E <= 256).
@@ -194,20 +259,52 @@ __global__ __launch_bounds__(64) void mx_poff_kernel(const int32_t* __restrict__
   if (lane == 63) poff[E] = run;
 }
 
-hipError_t launch_mx_kmajor(const void* in, int R, int C, int batches, int64_t in_bstride, uint8_t* q,
-                            int64_t q_bstride, uint8_t* s, int64_t s_bstride, hipStream_t st) {
-  const int64_t n = static_cast<int64_t>(batches) * R * (C / 64);
-  hipLaunchKernelGGL(mx_kmajor_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(in), R, C, n, in_bstride, q, q_bstride, s, s_bstride);
+// Block table of the grouped transposing quantiser: for padded 64-row block
+// b (b < P/64), the group e with poff[e] <= 64 b < poff[e+1] (binary search;
+// empty groups have poff[e] == poff[e+1]) gives x = offsets[e] + 64 b -
+// poff[e], y = min(64, offsets[e+1] - x); blocks past the last group get y = 0.
+__global__ __launch_bounds__(256) void mx_blocks_kernel(const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ poff, int E, int nblk,
+                                                        int2* __restrict__ blk) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  const int p = b * 64;
+  int2 t = make_int2(0, 0);
+  if (p < poff[E]) {
+    int lo = 0, hi = E;  // poff[lo] <= p < poff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (poff[mid] <= p) lo = mid; else hi = mid;
+    }
+    t.x = offsets[lo] + (p - poff[lo]);
+    t.y = min(64, offsets[lo + 1] - t.x);
+  }
+  blk[b] = t;
+}
+
+hipError_t launch_mx_blocks(const int32_t* offsets, const int32_t* poff, int E, int64_t P, void* blk, hipStream_t st) {
+  const int nblk = static_cast<int>(P / 64);
+  hipLaunchKernelGGL(mx_blocks_kernel, dim3((nblk + 255) / 256), dim3(256), 0, st, offsets, poff, E, nblk,
+                     static_cast<int2*>(blk));
   return hipGetLastError();
 }
 
-hipError_t launch_mx_tgroup(const void* in, int R, int C, const int32_t* offsets, const int32_t* poff, int E,
-                            int batches, int64_t in_bstride, uint8_t* q, int64_t P, int64_t q_bstride, uint8_t* s,
-                            int64_t s_bstride, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(P / 64), static_cast<unsigned>(C / 64), static_cast<unsigned>(batches));
-  hipLaunchKernelGGL(mx_tgroup_kernel, grid, dim3(128), 0, st, static_cast<const bf16_t*>(in), R, C, offsets, poff,
-                     E, in_bstride, q, P, q_bstride, s, s_bstride);
+hipError_t launch_mx_kmajor(const void* in, int R, int C, int batches, int64_t in_bstride, uint8_t* q,
+                            int64_t q_bstride, uint8_t* s, int64_t s_bstride, hipStream_t st) {
+  const int64_t ntiles = static_cast<int64_t>(batches) * (R / 8) * (C / 64);
+  const int64_t waves = (ntiles + kTilesPerWave - 1) / kTilesPerWave;
+  hipLaunchKernelGGL(mx_kmajor_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(in), R, C, ntiles, in_bstride, q, q_bstride, s, s_bstride);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_tgroup(const void* in, int R, int C, const void* blk, int batches, int64_t in_bstride,
+                            uint8_t* q, int64_t P, int64_t q_bstride, uint8_t* s, int64_t s_bstride, hipStream_t st,
+                            uint8_t* qk, uint8_t* sk) {
+  const dim3 grid(static_cast<unsigned>((P + 127) / 128), static_cast<unsigned>(C / 64),
+                  static_cast<unsigned>(batches));
+  hipLaunchKernelGGL(mx_tgroup_kernel, grid, dim3(256), 0, st, static_cast<const bf16_t*>(in), R, C,
+                     static_cast<const int2*>(blk), in_bstride, q, P, q_bstride, s, s_bstride, qk, sk);
   return hipGetLastError();
 }
 
