@@ -113,8 +113,11 @@ const char* moe_last_error_message(void);
  * calls except the device status word written by moe_dispatch. */
 size_t moe_workspace_size(int op, const moe_shape* shape);
 
-/* Bytes of the buffer that moe_grouped_ffn_fwd fills with the activations the
- * backward needs (G, U, H: three [S][f] tensors in the layer dtype). */
+/* Bytes of the buffer that moe_grouped_ffn_fwd fills with what the backward
+ * needs: G, U, H (three [S][f] tensors in the layer dtype, bf16 for MXFP8
+ * layers) and, for MXFP8 layers, the E4M3 copies (with their E8M0 scales) of
+ * w_gate, w_up and w_down in the layouts of the backward's dgrad GEMMs, which
+ * the forward writes from the same read that quantises its own copies. */
 size_t moe_save_size(const moe_shape* shape);
 
 /* Router: logits[T][E] (fp32) = x[T][d] · w_router[d][E] with fp32
@@ -157,7 +160,8 @@ int moe_read_device_status(const void* ws, void* stream);
  * of its rows r: G = xp[r] · w_gate[e], U = xp[r] · w_up[e],
  * H = silu(G) * U with silu(z) = z / (1 + exp(-z)), o[r] = H · w_down[e];
  * fp32 accumulation, one rounding to the layer dtype per stored value.
- * save (>= moe_save_size bytes) receives G, U, H for the backward.
+ * save (>= moe_save_size bytes) receives G, U, H (and, for MXFP8 layers, the
+ * backward's quantised weight copies) for the backward.
  * ws: moe_workspace_size(MOE_OP_FFN_FWD) bytes (may be 0 -> NULL allowed).
  * Passage: bytechap.com page, "Cómo funciona" (grouped GEMM combining many
  * small expert computations); unite.ai page, "Parallelismo, precisione e
