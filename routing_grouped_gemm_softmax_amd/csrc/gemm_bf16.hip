@@ -251,8 +251,26 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
 
 int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
 
+// The quarter tiles of a launch whose tile list ends in a short round
+// (p.tail = 1): at most p.cus workgroups.
 template <int MODE, int BM, int BN>
-hipError_t launch_tile(const GemmParams& p, int tiles, hipStream_t s) {
+hipError_t launch_tail(const GemmParams& p, int grid, hipStream_t s) {
+  constexpr int ring = kStages * (BM + BN) * kBK * 2, stage = 4 * 2 * (BM / 2) * 128;
+  constexpr int lds = ring > stage ? ring : stage;
+  auto kern = gg_bf16_kernel<MODE, BM, BN>;
+  static std::atomic<int> attr{0};
+  if (attr.load() == 0) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr.store(1);
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int MODE, int BM, int BN>
+hipError_t launch_tile(const GemmParams& p0, int tiles, hipStream_t s) {
   // The ring, reused by the epilogue's per-wave staging (4 waves x 2 tiles of
   // (BM/2) x 64 bf16).
   constexpr int ring = kStages * (BM + BN) * kBK * 2, stage = 4 * 2 * (BM / 2) * 128;
@@ -269,15 +287,31 @@ hipError_t launch_tile(const GemmParams& p, int tiles, hipStream_t s) {
     per_cu.store(n > 0 ? n : 1);
   }
   if (tiles <= 0) return hipSuccess;
-  // Row-ragged modes: one workgroup per tile of the count-free bound (the
-  // surplus exits at once). Weight gradients: a persistent grid, as many
-  // workgroups as run at once (a multiple of 8: one share per XCD).
   const int cap = max(8, device_cu_count() * per_cu.load() / 8 * 8);
-  const int grid = MODE == WGRAD ? min(cap, round8(tiles)) : round8(tiles);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
-  return hipGetLastError();
+  if constexpr (MODE == WGRAD) {
+    // A persistent grid: as many workgroups as run at once (a multiple of 8:
+    // one share per XCD).
+    hipLaunchKernelGGL(kern, dim3(min(cap, round8(tiles))), dim3(256), lds, s, p0);
+    return hipGetLastError();
+  } else {
+    // One workgroup per tile of the count-free bound (the surplus exits at
+    // once). The full-size tiles leave a short last round to quarter tiles
+    // (see ragged_tile): a second launch of the half-size kernel.
+    constexpr bool kQuarters = (BM == 256 && BN == 256);
+    GemmParams p = p0;
+    p.cus = kQuarters ? cap : 0;
+    p.tail = 0;
+    hipLaunchKernelGGL(kern, dim3(round8(tiles)), dim3(256), lds, s, p);
+    hipError_t err = hipGetLastError();
+    if constexpr (kQuarters) {
+      if (err == hipSuccess) {
+        p.tail = 1;
+        err = launch_tail<MODE, BM / 2, BN / 2>(p, cap, s);
+      }
+    }
+    return err;
+  }
 }
-
 
 // Grid bound for row-ragged modes: sum_e ceil(n_e/BM) <= ceil(S/BM) + E.
 int ragged_grid(int S, int E, int BM, int NT) {

@@ -186,16 +186,25 @@ struct TileCoord {
   int m0;       // WGRAD: first row of the weight-gradient tile
 };
 
-// Row-ragged modes: one tile per workgroup. Maps this workgroup's id to
-// (expert, row tile, column tile) from the per-expert row offsets on the
-// device: wave 0 scans the per-expert tile counts; the result is broadcast
-// through LDS and kept wave-uniform (e < 0: no tile). Each XCD (id % 8) takes
-// a contiguous range of tiles; inside it, groups of 8 row tiles sweep the
-// column tiles so concurrently running tiles share operands in its L2.
+// Row-ragged modes: one tile per workgroup, mapped from the workgroup id and
+// the per-expert row offsets on the device: wave 0 scans the per-expert tile
+// counts; the result is broadcast through LDS and kept wave-uniform (e < 0:
+// no tile).
+//
+// Tiles are numbered by a logical index L: groups of 8 row tiles sweep the
+// column tiles, so tiles close in L share operands in L2; each XCD (id % 8)
+// takes a contiguous range of L. With R tiles and p.cus workgroups running at
+// once, the rem = R % cus tiles past the last full round would keep the chip
+// mostly idle for a whole tile time. When 4 rem <= cus they are left out of
+// this launch (p.tail = 0) and a second launch (p.tail = 1) of a kernel with
+// half-height, half-width tiles takes each of them as 4 quarters, all in one
+// round of a quarter of the time. Both launches derive the same tile list
+// from the full-size tiles (BM, BN here; 2 BM, 2 BN in the tail launch).
 template <int BM, int BN>
 __device__ __forceinline__ TileCoord ragged_tile(const GemmParams& p, int* s_info, int wave, int lane) {
   const int bid = blockIdx.x;
-  const int NT = p.N / BN;
+  const int tbm = p.tail ? 2 * BM : BM, tbn = p.tail ? 2 * BN : BN;  // tiles of the list
+  const int NT = p.N / tbn;
   if (wave == 0) {
     int e_sel = -1, row0 = 0, row_end = 0, nt = 0;
     int tq[4], tsum = 0;
@@ -203,19 +212,33 @@ __device__ __forceinline__ TileCoord ragged_tile(const GemmParams& p, int* s_inf
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
       const int n = (e < p.E) ? (p.offsets[e + 1] - p.offsets[e]) : 0;
-      tq[q] = (n + BM - 1) / BM;
+      tq[q] = (n + tbm - 1) / tbm;
       tsum += tq[q];
     }
     const int excl = wave_exclusive_scan(tsum);
     const int RM = __shfl(excl + tsum, 63, kWave);
     const int R = RM * NT;
-    if (bid < R) {
-      const int q = R / 8, rmd = R % 8, x = bid % 8, i = bid / 8;
-      const int logical = x * q + min(x, rmd) + i;
+    int rem = 0;
+    if (p.cus > 0 && R > 0) {
+      rem = R >= p.cus ? R % p.cus : R;
+      if (4 * rem > p.cus) rem = 0;  // no quarter tiles: the last round stays as it is
+    }
+    const int rmain = R - rem;
+    int L = -1, quarter = 0;
+    if (!p.tail) {
+      if (bid < rmain) {
+        const int q = rmain / 8, rmd = rmain % 8, x = bid % 8, i = bid / 8;
+        L = x * q + min(x, rmd) + i;
+      }
+    } else if (bid < 4 * rem) {
+      L = rmain + bid / 4;
+      quarter = bid % 4;
+    }
+    if (L >= 0) {
       constexpr int GM = 8;
-      const int g = logical / (GM * NT);
+      const int g = L / (GM * NT);
       const int gm = min(GM, RM - g * GM);
-      const int local = logical - g * GM * NT;
+      const int local = L - g * GM * NT;
       const int mt = g * GM + local % gm;
       nt = local / gm;
       int run = excl;
@@ -224,7 +247,7 @@ __device__ __forceinline__ TileCoord ragged_tile(const GemmParams& p, int* s_inf
         const int e = lane * 4 + q;
         if (mt >= run && mt < run + tq[q]) {
           e_sel = e;
-          row0 = p.offsets[e] + (mt - run) * BM;
+          row0 = p.offsets[e] + (mt - run) * tbm;
           row_end = p.offsets[e + 1];
         }
         run += tq[q];
@@ -235,6 +258,11 @@ __device__ __forceinline__ TileCoord ragged_tile(const GemmParams& p, int* s_inf
       row0 = __shfl(row0, src, kWave);
       row_end = __shfl(row_end, src, kWave);
       if (!who) e_sel = -1;
+      if (p.tail) {  // quarter (row half, column half) of the full-size tile
+        row0 += (quarter >> 1) * BM;
+        nt = nt * 2 + (quarter & 1);
+        if (row0 >= row_end) e_sel = -1;
+      }
     }
     if (lane == 0) {
       s_info[0] = e_sel; s_info[1] = row0; s_info[2] = row_end; s_info[3] = nt;

@@ -42,6 +42,11 @@ struct GemmParams {
   int64_t as_slab;    // bytes between slabs of as
   int64_t bs_slab;    // bytes between slabs of bs0/bs1
   int64_t bs_estride; // bytes between experts in bs0/bs1
+  // Row-ragged modes: with cus > 0 (workgroups that run at once) the tiles
+  // past the last full round are left to a second launch (tail = 1) of
+  // half-height, half-width tiles; see ragged_tile.
+  int cus;
+  int tail;
 };
 
 // bf16 grouped GEMMs (gemm_bf16.hip).
