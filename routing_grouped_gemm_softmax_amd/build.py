@@ -28,6 +28,14 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# Per-source additions. The MXFP8 GEMM's 128 x 128 wave blocks hold 256 fp32
+# accumulators beside two sets of 32-byte fragments: with the accumulators
+# allowed in ordinary VGPRs (MFMA "VGPR form") the register allocator places
+# the fragments in AGPRs and nothing spills to scratch; with the default form
+# it spills a few hundred registers.
+EXTRA_FLAGS = {
+    "gemm_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def hipcc() -> str:
@@ -39,7 +47,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -283,13 +283,16 @@ int ragged_grid(int S, int E, int BM, int NT) {
   return round8((static_cast<int64_t>((S + BM - 1) / BM) + E) * NT);
 }
 
-// Tiles are at most 256 x 128: two register sets of 32-byte fragments for a
-// 128 x 128 wave block do not fit beside its 256 accumulators.
+// 256 x 256 tiles where N allows: a slab then moves 36 KB (data and scales)
+// per 1024 MFMA cycles of each SIMD, against 28 KB per 512 cycles for
+// 256 x 128 tiles, which saturates the LDS and the texture path.
 template <int MODE>
 hipError_t ragged_mode(const GemmParams& p, hipStream_t s) {
   // N is a multiple of 128 (MXFP8 layers need d, f multiples of 128).
-  if (static_cast<int64_t>(p.S) >= 1024LL * p.E)
+  if (static_cast<int64_t>(p.S) >= 1024LL * p.E) {
+    if (p.N % 256 == 0) return launch_tile<MODE, 256, 256>(p, ragged_grid(p.S, p.E, 256, p.N / 256), s);
     return launch_tile<MODE, 256, 128>(p, ragged_grid(p.S, p.E, 256, p.N / 128), s);
+  }
   return launch_tile<MODE, 128, 128>(p, ragged_grid(p.S, p.E, 128, p.N / 128), s);
 }
 
@@ -307,6 +310,9 @@ hipError_t launch_mx_ragged(int mode, const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_mx_wgrad(const GemmParams& p, hipStream_t s) {
   auto grid = [&](int bm, int bn) { return round8(static_cast<int64_t>(p.E) * (p.M / bm) * (p.N / bn)); };
+  // A column tile must not straddle the gate|up split at column f.
+  const int nsplit = p.c1 ? p.f : p.N;
+  if (p.M % 256 == 0 && p.N % 256 == 0 && nsplit % 256 == 0) return launch_tile<WGRAD, 256, 256>(p, grid(256, 256), s);
   if (p.M % 256 == 0) return launch_tile<WGRAD, 256, 128>(p, grid(256, 128), s);
   return launch_tile<WGRAD, 128, 128>(p, grid(128, 128), s);
 }
