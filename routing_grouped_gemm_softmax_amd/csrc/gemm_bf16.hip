@@ -249,6 +249,213 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
   }
 }
 
+// FWD_DOWN with 256 x 256 tiles, as a persistent grid of p.cus workgroups
+// that streams slabs across tiles: each workgroup owns tiles lo, lo + wpx,
+// ... of its XCD's range, and the ring never drains between them. The loads
+// of the next tile's first slabs go out during the current tile's last
+// slabs, and the epilogue (staged through a per-wave LDS area beside the
+// ring, written with buffer stores) runs while they fly. At K = d_ff this
+// mode has only 32 slabs per tile; measured at T = 8192, d = 2048, E = 8,
+// k = 4, d_ff = 1024 it runs in 156 us against 176 us with one tile per
+// workgroup. The same scheme gained nothing for the dgrad of the gate/up
+// projection (64 slabs per tile), and the SwiGLU epilogue of the gate/up
+// forward does not fit its registers beside the stream state.
+//
+// Wait counts: vmcnt counts loads and stores together, in issue order. In the
+// three slabs after an epilogue the slab being waited for was issued before
+// that epilogue's kEpiStores stores, so those waits allow kEpiStores more
+// outstanding operations (a smaller count would only wait longer). Every
+// epilogue issues exactly kEpiStores stores (buffer stores: rows past an
+// expert's end are dropped by the range check, not by a branch), and tiles
+// have at least kStages slabs, so epilogues are at least that many slabs
+// apart.
+template <int MODE>
+__global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, MB = 4, NB = 4;
+  static_assert(MODE == FWD_DOWN, "streaming mode");
+  constexpr int TILE_M = BM * kBK * 2, TILE_N = BN * kBK * 2;
+  constexpr int STAGE = TILE_M + TILE_N;
+  constexpr int RING = kStages * STAGE;
+  constexpr int kStg = 64 * 128;  // per-wave staging tile: 64 rows x 64 bf16
+  constexpr int kEpiStores = 4 * 8;
+  constexpr int LM = BM / 64, LN = BN / 64, kLoads = LM + LN;
+  constexpr int kWaitSteady = kLoads * (kStages - 2);
+  constexpr int kWaitEpi = kWaitSteady + kEpiStores < 63 ? kWaitSteady + kEpiStores : 63;
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  RowTileMap map;
+  map.init(p, BM, BN, lane);
+  const int rmain = map.main_tiles(p.cus);
+  const int x = blockIdx.x % 8, wi = blockIdx.x / 8, wpx = gridDim.x / 8;
+  const int lo = xcd_cut(rmain, x) + wi, hi = xcd_cut(rmain, x + 1);
+  const int ntiles = lo < hi ? (hi - lo + wpx - 1) / wpx : 0;
+  if (ntiles == 0) return;
+  const int nk = p.K / kBK;
+  const char* const A = static_cast<const char*>(p.a);
+
+  // ---- HBM -> LDS: load L of slab kt of tile tc (empty descriptors if !live) --------------
+  auto issue = [&](const TileCoord& tc, int kt, bool live, uint32_t slot, auto L, auto w) {
+    constexpr int l = decltype(L)::value, W = decltype(w)::value;
+    if constexpr (l < LM) {
+      const char* base = A + (static_cast<int64_t>(tc.row0) * p.lda + kt * kBK) * 2;
+      const int valid = live ? min(BM, tc.row_end - tc.row0) : 0;
+      load_rows64<BM, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda * 2, slot, wave, lane, l);
+    } else {
+      // W_down [f][d] of the tile's expert: rows k, columns n.
+      constexpr int q = l - LM;
+      const int64_t off = (static_cast<int64_t>(tc.e) * p.bstride + static_cast<int64_t>(kt) * kBK * p.ldb + tc.nt * BN) * 2;
+      load_mnmajor<BN, W>(make_rsrc(static_cast<const char*>(p.b0) + off, live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0),
+                          p.ldb, slot + TILE_M, wave, lane, q);
+    }
+  };
+
+  floatx16 acc[NB][MB];
+  struct Frags {
+    bf16x8 m[MB], n[NB];
+  };
+  auto read_frag = [&](const char* slotp, int kk, Frags& F, auto FI) {
+    constexpr int fi = decltype(FI)::value;
+    const char* tm = slotp;
+    const char* tn = slotp + TILE_M;
+    if constexpr (fi < MB) {
+      F.m[fi] = frag_kmajor(tm, wm * WM + fi * 32, kk, lane);
+    } else {
+      F.n[fi - MB] = frag_mnmajor<BN>(tn, wn * WN + (fi - MB) * 32, kk, lane);
+    }
+  };
+  auto read_frags = [&](const char* slotp, int kk, Frags& F) {
+    static_for<MB + NB>([&](auto FI) { read_frag(slotp, kk, F, FI); });
+  };
+  auto mfma_one = [&](const Frags& F, auto MI) {
+    constexpr int mi = decltype(MI)::value, j = mi / MB, i = mi % MB;
+    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.n[j], F.m[i], acc[j][i], 0, 0, 0);
+  };
+  constexpr int kReads = MB + NB * 2;
+  constexpr int kMfma = MB * NB;
+  constexpr int kFrags = MB + NB;
+  auto interleave = [&]() {
+    constexpr int inter = kReads < kMfma ? kReads : kMfma;
+#pragma unroll
+    for (int r = 0; r < inter; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+    if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+  };
+
+  // ---- epilogue: this wave's 128 x 128 block through its 8 KB staging tile ----------------
+  char* const wa = smem + RING + wave * kStg;
+  const int hl = lane >> 5, l32 = lane & 31;
+  auto st_off = [](int r, int col) { return r * 128 + ((((col >> 3) ^ (r >> 1)) & 7) << 4) + ((col & 4) << 1); };
+  auto put4 = [&](int r, int col, uint2 v) { *reinterpret_cast<uint2*>(wa + st_off(r, col)) = v; };
+  auto wave_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+  };
+  // Staging rows [0, 64) -> global rows g + r * ld for r < rows (8 buffer stores).
+  auto flush = [&](const char* g, int64_t ld, int rows) {
+    __builtin_amdgcn_sched_barrier(0);
+    wave_sync();
+    const auto rs = make_rsrc(g, static_cast<int64_t>(max(0, min(64, rows))) * ld);
+    const int c = lane & 7;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = t * 8 + (lane >> 3);
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wa + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<uint32_t>(r * ld + c * 16), 0, 0);
+    }
+    wave_sync();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto acc4 = [&](int j, int i, int q) {
+    return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
+  };
+  auto epilogue = [&](const TileCoord& tc) {
+    const int mrow = tc.row0 + wm * WM;
+    const int rows = tc.row_end - mrow;  // may be <= 0 or > WM: flush clamps
+    const int64_t ld = p.ldc * 2;
+    const char* out = static_cast<const char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + tc.nt * BN + wn * WN) * 2;
+    static_for<2>([&](auto JP) {
+      static_for<2>([&](auto HH) {
+        constexpr int h = decltype(HH)::value;
+        static_for<2>([&](auto II) {
+          static_for<2>([&](auto JJ) {
+            static_for<4>([&](auto Q) {
+              put4(II * 32 + l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JP * 2 + JJ, 2 * h + II, Q));
+            });
+          });
+        });
+        flush(out + static_cast<int64_t>(h) * 64 * ld + JP * 128, ld, rows - 64 * h);
+      });
+    });
+  };
+
+  // ---- the slab stream ------------------------------------------------------------------
+  TileCoord cur = map.at(lo, lane);
+  TileCoord ltc = cur;  // tile of the next slab to load
+  int lj = 0, lkt = 0;  // its index among this workgroup's tiles, and slab
+  auto advance = [&]() {
+    if (++lkt == nk) {
+      lkt = 0;
+      if (++lj < ntiles) ltc = map.at(lo + lj * wpx, lane);
+    }
+  };
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+#pragma unroll
+  for (int s0 = 0; s0 < kStages; ++s0) {
+    static_for<kLoads>([&](auto L) { issue(ltc, lkt, lj < ntiles, ring + s0 * STAGE, L, std::integral_constant<int, 4>{}); });
+    advance();
+  }
+  Frags F[2];
+  wait_vmcnt<kLoads * (kStages - 1)>();
+  __syncthreads();
+  read_frags(smem, 0, F[0]);
+  int gk = 0;  // slabs consumed: slab gk sits in slot gk % kStages
+  for (int j = 0; j < ntiles; ++j) {
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[jj][i][r] = 0.0f;
+    for (int kt = 0; kt < nk; ++kt, ++gk) {
+      const int sc = gk % kStages;
+      const char* curp = smem + sc * STAGE;
+      const char* nxtp = smem + ((gk + 1) % kStages) * STAGE;
+      read_frags(curp, 1, F[1]);
+      static_for<kMfma>([&](auto MI) { mfma_one(F[0], MI); });
+      interleave();
+      if (j > 0 && kt < kStages - 1) wait_vmcnt<kWaitEpi>();
+      else wait_vmcnt<kWaitSteady>();
+      __syncthreads();
+      const uint32_t slot = ring + sc * STAGE;
+      const bool live = lj < ntiles;
+      static_for<kLoads>([&](auto S) {
+        constexpr int sg = decltype(S)::value;
+        constexpr int m_lo = sg * kMfma / kLoads, m_hi = (sg + 1) * kMfma / kLoads;
+        constexpr int f_lo = sg * kFrags / kLoads, f_hi = (sg + 1) * kFrags / kLoads;
+        static_for<m_hi - m_lo>([&](auto D) { mfma_one(F[1], std::integral_constant<int, m_lo + decltype(D)::value>{}); });
+        static_for<f_hi - f_lo>([&](auto D) { read_frag(nxtp, 0, F[0], std::integral_constant<int, f_lo + decltype(D)::value>{}); });
+        issue(ltc, lkt, live, slot, S, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      advance();
+    }
+    // F[0] already holds the first fragments of the next tile (read during
+    // the last slab), whose slot is not refilled before the next barrier.
+    epilogue(cur);
+    if (j + 1 < ntiles) cur = map.at(lo + (j + 1) * wpx, lane);
+  }
+  // Drain the (empty) loads and the stores still in flight before the wave ends.
+  wait_vmcnt<0>();
+}
+
 int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
 
 // The quarter tiles of a launch whose tile list ends in a short round
@@ -267,6 +474,33 @@ hipError_t launch_tail(const GemmParams& p, int grid, hipStream_t s) {
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
+}
+
+// The streaming kernel on as many workgroups as run at once, then the
+// quarter tiles of its short last round (both launches split the tile list
+// with the same p.cus).
+template <int MODE>
+hipError_t launch_stream(GemmParams p, hipStream_t s) {
+  constexpr int lds = kStages * (256 + 256) * kBK * 2 + 4 * 64 * 128;
+  auto kern = gg_bf16_stream_kernel<MODE>;
+  static std::atomic<int> per_cu{0};
+  if (per_cu.load() == 0) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    int n = 0;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kern), 256, lds);
+    if (err != hipSuccess) return err;
+    per_cu.store(n > 0 ? n : 1);
+  }
+  const int cap = max(8, device_cu_count() * per_cu.load() / 8 * 8);
+  p.cus = cap;
+  p.tail = 0;
+  hipLaunchKernelGGL(kern, dim3(cap), dim3(256), lds, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  p.tail = 1;
+  return launch_tail<MODE, 128, 128>(p, cap, s);
 }
 
 template <int MODE, int BM, int BN>
@@ -295,12 +529,16 @@ hipError_t launch_tile(const GemmParams& p0, int tiles, hipStream_t s) {
     return hipGetLastError();
   } else {
     // One workgroup per tile of the count-free bound (the surplus exits at
-    // once). The full-size tiles leave a short last round to quarter tiles
-    // (see ragged_tile): a second launch of the half-size kernel.
+    // once), or the streaming kernel. The full-size tiles leave a short last
+    // round to quarter tiles (see RowTileMap): a second launch of the
+    // half-size kernel.
     constexpr bool kQuarters = (BM == 256 && BN == 256);
     GemmParams p = p0;
     p.cus = kQuarters ? cap : 0;
     p.tail = 0;
+    if constexpr (kQuarters && MODE == FWD_DOWN) {
+      if (p.K / kBK >= kStages) return launch_stream<MODE>(p, s);
+    }
     hipLaunchKernelGGL(kern, dim3(round8(tiles)), dim3(256), lds, s, p);
     hipError_t err = hipGetLastError();
     if constexpr (kQuarters) {

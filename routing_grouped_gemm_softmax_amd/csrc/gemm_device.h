@@ -186,86 +186,107 @@ struct TileCoord {
   int m0;       // WGRAD: first row of the weight-gradient tile
 };
 
-// Row-ragged modes: one tile per workgroup, mapped from the workgroup id and
-// the per-expert row offsets on the device: wave 0 scans the per-expert tile
-// counts; the result is broadcast through LDS and kept wave-uniform (e < 0:
-// no tile).
+// Row tiles of the ragged modes, held per wave: lane l keeps experts 4l..4l+3
+// (row ranges and tile counts of `tbm` rows) and the exclusive prefix of the
+// tile counts, so any wave maps a tile index to its coordinates with
+// lane-local compares and one ballot (no LDS, no barrier).
 //
 // Tiles are numbered by a logical index L: groups of 8 row tiles sweep the
-// column tiles, so tiles close in L share operands in L2; each XCD (id % 8)
-// takes a contiguous range of L. With R tiles and p.cus workgroups running at
-// once, the rem = R % cus tiles past the last full round would keep the chip
-// mostly idle for a whole tile time. When 4 rem <= cus they are left out of
-// this launch (p.tail = 0) and a second launch (p.tail = 1) of a kernel with
-// half-height, half-width tiles takes each of them as 4 quarters, all in one
-// round of a quarter of the time. Both launches derive the same tile list
-// from the full-size tiles (BM, BN here; 2 BM, 2 BN in the tail launch).
-template <int BM, int BN>
-__device__ __forceinline__ TileCoord ragged_tile(const GemmParams& p, int* s_info, int wave, int lane) {
-  const int bid = blockIdx.x;
-  const int tbm = p.tail ? 2 * BM : BM, tbn = p.tail ? 2 * BN : BN;  // tiles of the list
-  const int NT = p.N / tbn;
-  if (wave == 0) {
-    int e_sel = -1, row0 = 0, row_end = 0, nt = 0;
-    int tq[4], tsum = 0;
+// column tiles, so tiles close in L share operands in L2. With R tiles and
+// `cus` workgroups running at once, the rem = R % cus tiles past the last full
+// round would keep the chip mostly idle for a whole tile time; when 4 rem <=
+// cus they are left to a second launch (p.tail = 1) of a kernel with
+// half-height, half-width tiles that takes each as 4 quarters, all in one
+// round of a quarter of the time. Every launch derives the same tile list
+// from the full-size tiles.
+struct RowTileMap {
+  int beg[4], end[4], tq[4], excl;  // per lane
+  int RM, NT, tbm;                  // wave-uniform
+  __device__ __forceinline__ void init(const GemmParams& p, int tbm_, int tbn, int lane) {
+    tbm = tbm_;
+    NT = p.N / tbn;
+    int tsum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      const int n = (e < p.E) ? (p.offsets[e + 1] - p.offsets[e]) : 0;
-      tq[q] = (n + tbm - 1) / tbm;
+      beg[q] = e < p.E ? p.offsets[e] : 0;
+      end[q] = e < p.E ? p.offsets[e + 1] : 0;
+      tq[q] = (end[q] - beg[q] + tbm - 1) / tbm;
       tsum += tq[q];
     }
-    const int excl = wave_exclusive_scan(tsum);
-    const int RM = __shfl(excl + tsum, 63, kWave);
+    excl = wave_exclusive_scan(tsum);
+    RM = __builtin_amdgcn_readfirstlane(__shfl(excl + tsum, 63, kWave));
+  }
+  __device__ __forceinline__ int tiles() const { return RM * NT; }
+  // Tiles [0, main(cus)) go to full-size tiles; the rest, if any, to quarters.
+  __device__ __forceinline__ int main_tiles(int cus) const {
     const int R = RM * NT;
-    int rem = 0;
-    if (p.cus > 0 && R > 0) {
-      rem = R >= p.cus ? R % p.cus : R;
-      if (4 * rem > p.cus) rem = 0;  // no quarter tiles: the last round stays as it is
+    if (cus <= 0 || R <= 0) return R;
+    const int rem = R >= cus ? R % cus : R;
+    return 4 * rem > cus ? R : R - rem;
+  }
+  // Coordinates of tile L (wave-uniform; e = -1 if L is past the end).
+  __device__ __forceinline__ TileCoord at(int L, int lane) const {
+    constexpr int GM = 8;
+    const int g = L / (GM * NT);
+    const int gm = min(GM, RM - g * GM);
+    const int local = L - g * GM * NT;
+    const int mt = g * GM + local % gm;
+    int e_sel = -1, row0 = 0, row_end = 0, run = excl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (mt >= run && mt < run + tq[q]) {
+        e_sel = lane * 4 + q;
+        row0 = beg[q] + (mt - run) * tbm;
+        row_end = end[q];
+      }
+      run += tq[q];
     }
-    const int rmain = R - rem;
+    const uint64_t who = __ballot(e_sel >= 0);
+    const int src = who ? __ffsll(static_cast<long long>(who)) - 1 : 0;
+    TileCoord t;
+    t.e = who ? __builtin_amdgcn_readfirstlane(__shfl(e_sel, src, kWave)) : -1;
+    t.row0 = __builtin_amdgcn_readfirstlane(__shfl(row0, src, kWave));
+    t.row_end = __builtin_amdgcn_readfirstlane(__shfl(row_end, src, kWave));
+    t.nt = __builtin_amdgcn_readfirstlane(local / gm);
+    t.m0 = 0;
+    return t;
+  }
+};
+
+// First tile of XCD x's contiguous range when R tiles are cut into 8.
+__device__ __forceinline__ int xcd_cut(int R, int x) { return x * (R / 8) + min(x, R % 8); }
+
+// Row-ragged modes, one tile per workgroup: workgroup b runs on XCD b % 8,
+// and each XCD takes a contiguous range of the main tiles. In the quarter
+// launch (p.tail), workgroup b takes quarter b % 4 of tail tile b / 4.
+// Wave 0 maps the id; the result is broadcast through LDS and kept
+// wave-uniform (e < 0: no tile).
+template <int BM, int BN>
+__device__ __forceinline__ TileCoord ragged_tile(const GemmParams& p, int* s_info, int wave, int lane) {
+  const int bid = blockIdx.x;
+  if (wave == 0) {
+    RowTileMap map;
+    map.init(p, p.tail ? 2 * BM : BM, p.tail ? 2 * BN : BN, lane);
+    const int rmain = map.main_tiles(p.cus);
     int L = -1, quarter = 0;
     if (!p.tail) {
-      if (bid < rmain) {
-        const int q = rmain / 8, rmd = rmain % 8, x = bid % 8, i = bid / 8;
-        L = x * q + min(x, rmd) + i;
-      }
-    } else if (bid < 4 * rem) {
+      if (bid < rmain) L = xcd_cut(rmain, bid % 8) + bid / 8;
+    } else if (bid < 4 * (map.tiles() - rmain)) {
       L = rmain + bid / 4;
       quarter = bid % 4;
     }
+    TileCoord t{-1, 0, 0, 0, 0};
     if (L >= 0) {
-      constexpr int GM = 8;
-      const int g = L / (GM * NT);
-      const int gm = min(GM, RM - g * GM);
-      const int local = L - g * GM * NT;
-      const int mt = g * GM + local % gm;
-      nt = local / gm;
-      int run = excl;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane * 4 + q;
-        if (mt >= run && mt < run + tq[q]) {
-          e_sel = e;
-          row0 = p.offsets[e] + (mt - run) * tbm;
-          row_end = p.offsets[e + 1];
-        }
-        run += tq[q];
-      }
-      const uint64_t who = __ballot(e_sel >= 0);
-      const int src = who ? __ffsll(static_cast<long long>(who)) - 1 : 0;
-      e_sel = __shfl(e_sel, src, kWave);
-      row0 = __shfl(row0, src, kWave);
-      row_end = __shfl(row_end, src, kWave);
-      if (!who) e_sel = -1;
-      if (p.tail) {  // quarter (row half, column half) of the full-size tile
-        row0 += (quarter >> 1) * BM;
-        nt = nt * 2 + (quarter & 1);
-        if (row0 >= row_end) e_sel = -1;
+      t = map.at(L, lane);
+      if (p.tail && t.e >= 0) {  // quarter (row half, column half) of the full-size tile
+        t.row0 += (quarter >> 1) * BM;
+        t.nt = t.nt * 2 + (quarter & 1);
+        if (t.row0 >= t.row_end) t.e = -1;
       }
     }
     if (lane == 0) {
-      s_info[0] = e_sel; s_info[1] = row0; s_info[2] = row_end; s_info[3] = nt;
+      s_info[0] = t.e; s_info[1] = t.row0; s_info[2] = t.row_end; s_info[3] = t.nt;
     }
   }
   __syncthreads();

@@ -30,6 +30,12 @@ CASES = {
     "bf16_zipf_empty_experts": ("bf16_zipf", dict(T=256, d=128, E=16, f=128),
                                 [1, 0, 2, 1, 1, 0, 3, 1, 1, 1, 0, 1, 2, 1, 1, 0]),
     "bf16_balanced": ("mxfp8_balanced", dict(T=256, d=128, E=16, f=128, dtype="bf16"), None),
+    # 256 x 256 tiles on the persistent streaming kernels: several tiles per
+    # workgroup (512 tiles in FWD_GU and FWD_DOWN), ragged expert ends, and a
+    # short last round left to quarter tiles.
+    "bf16_stream_multi_tile": ("bf16_e8", dict(T=16384, d=1024, E=4, k=2, f=512), None),
+    # 256 x 256 tiles with an empty expert.
+    "bf16_stream_empty_expert": ("bf16_zipf", dict(T=4096, d=512, E=4, k=2, f=512), [1, 0, 2, 1]),
 }
 
 
