@@ -141,11 +141,12 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
     p.b0 = w.wgq; p.b1 = w.wuq; p.ldb = d; p.bstride = wsz;
     p.bs0 = w.wgs; p.bs1 = w.wus; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
     p.c0 = a.G; p.c1 = a.U; p.c2 = a.H; p.ldc = f; p.N = 2 * f; p.K = d;
+    // The epilogue also writes H along f (the next GEMM's A operand).
+    p.mxq = w.hq; p.mxs = w.hs; p.mxq_ld = f; p.mxs_slab = 2LL * S;
     TRY(launch_mx_ragged(FWD_GU, p, s));
   }
-  // Operands: H along f; W_down along f, transposed to [d][f] (and its copy
-  // blocked along d, [f][d], for the backward's dH GEMM).
-  TRY(launch_mx_kmajor(a.H, S, f, 1, 0, w.hq, 0, w.hs, 0, s));
+  // Operands: H along f (above); W_down along f, transposed to [d][f] (and
+  // its copy blocked along d, [f][d], for the backward's dH GEMM).
   TRY(launch_mx_tgroup(a.w_down, f, d, nullptr, E, wsz, w.wdq, f, wsz, w.wds, wsz / 32, s, sv.wdq,
                        sv.wds));
   GemmParams q{};
@@ -170,11 +171,12 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
     p.a = w.doq; p.lda = d; p.as = w.dos; p.as_slab = 2LL * S;
     p.b0 = sv.wdq; p.ldb = d; p.bstride = wsz; p.bs0 = sv.wds; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
     p.c0 = a.dgu; p.ldc = 2 * f; p.e0 = a.G; p.e1 = a.U; p.N = f; p.K = d;
+    // The epilogue also writes dGU along 2f (the next GEMM's A operand).
+    p.mxq = w.dguq; p.mxs = w.dgus; p.mxq_ld = 2LL * f; p.mxs_slab = 2LL * S;
     TRY(launch_mx_ragged(BWD_DOWN, p, s));
   }
-  {  // dXp = q(dGU) q([W_gate | W_up])^T: dGU along f; the weights [d][f]
-     // along f were quantised by the forward.
-    TRY(launch_mx_kmajor(a.dgu, S, 2 * f, 1, 0, w.dguq, 0, w.dgus, 0, s));
+  {  // dXp = q(dGU) q([W_gate | W_up])^T: dGU along 2f (above); the weights
+     // [d][f] along f were quantised by the forward.
     GemmParams p{};
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
     p.a = w.dguq; p.lda = 2 * f; p.as = w.dgus; p.as_slab = 2LL * S;

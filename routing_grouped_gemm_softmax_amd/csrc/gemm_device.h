@@ -5,6 +5,7 @@
 
 #include "common.h"
 #include "grouped_gemm.h"
+#include "mx_encode.h"
 
 #include <type_traits>
 
@@ -386,7 +387,11 @@ __device__ __forceinline__ TileCoord wgrad_tile(const GemmParams& p, int t) {
 // Writes the accumulators of one BM x BN tile (and, for BWD_DOWN, reads the
 // saved G, U it needs) through a per-wave LDS area of smem, which must hold
 // 4 x 2 x (BM/2) x 128 bytes and be free of other use.
-template <int MODE, int BM, int BN>
+// With QUANT (the MXFP8 kernels), the bf16 rows of H (FWD_GU) and of dG, dU
+// (BWD_DOWN) are also written as the next GEMM's K-major MXFP8 operand
+// (p.mxq, p.mxs): the same staged 16-byte pieces, 4 lanes per 32-block,
+// encoded exactly as mx_kmajor_kernel encodes a row read back from memory.
+template <int MODE, int BM, int BN, bool QUANT = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN / 64][BM / 64], char* smem,
                                          int wave, int lane, const TileCoord& tc) {
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -417,20 +422,35 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
   };
+  const int mrow = (MODE == WGRAD ? m0 : row0) + wm * WM;   // first row of this wave's block
   // Rows [0, rows) and columns [0, cols) of staging tile `slot` -> global
-  // rows g + r*ld (bytes), 16 bytes per lane, 8 lanes per 128-byte row.
-  auto flush = [&](int slot, char* g, int64_t ld, int rows, int cols) {
+  // rows g + r*ld (bytes), 16 bytes per lane, 8 lanes per 128-byte row. With
+  // QUANT and qcol >= 0, also E4M3 codes to p.mxq row mrow + r, columns qcol
+  // + 8 c .. + 7, and each 32-block's E8M0 code to p.mxs.
+  auto flush = [&](int slot, char* g, int64_t ld, int rows, int cols, int qcol = -1) {
     wave_sync();
     const int c = lane & 7;
 #pragma unroll 4
     for (int t = 0; t < WM / 8; ++t) {
       const int r = t * 8 + (lane >> 3);
       const uint4 v = *reinterpret_cast<const uint4*>(wa + slot * kSlot + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
-      if (r < rows && c * 8 < cols) *reinterpret_cast<uint4*>(g + r * ld + c * 16) = v;
+      const bool live = r < rows && c * 8 < cols;
+      if (live) *reinterpret_cast<uint4*>(g + r * ld + c * 16) = v;
+      if constexpr (QUANT) {
+        if (qcol >= 0) {
+          float x[8];
+          unpack16(v, x);
+          const int code = mx_group4_code(x);  // every lane: butterflies
+          if (live) {
+            const int64_t row = mrow + r, col = qcol + c * 8;
+            *reinterpret_cast<uint2*>(p.mxq + row * p.mxq_ld + col) = mx_encode8(x, code);
+            if ((c & 3) == 0) p.mxs[(col / 64) * p.mxs_slab + row * 2 + (col / 32) % 2] = static_cast<uint8_t>(code);
+          }
+        }
+      }
     }
     wave_sync();
   };
-  const int mrow = (MODE == WGRAD ? m0 : row0) + wm * WM;   // first row of this wave's block
   const int rows = (MODE == WGRAD) ? WM : max(0, min(WM, row_end - mrow));
   auto acc4 = [&](int j, int i, int q) {
     return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
@@ -461,7 +481,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
       });
     });
     flush(0, G, ld, rows, GC);
-    flush(1, H, ld, rows, GC);
+    flush(1, H, ld, rows, GC, col0);
     static_for<MB>([&](auto I) {
       static_for<NB / 2>([&](auto JJ) {
         static_for<4>([&](auto Q) { put4(0, I * 32 + l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JJ + NB / 2, I, Q)); });
@@ -514,8 +534,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
         });
       });
       char* C = static_cast<char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
-      flush(0, C, ld, rows, GC);
-      flush(1, C + static_cast<int64_t>(p.f) * 2, ld, rows, GC);
+      flush(0, C, ld, rows, GC, col0);
+      flush(1, C + static_cast<int64_t>(p.f) * 2, ld, rows, GC, p.f + col0);
     });
   } else {
     // FWD_DOWN, BWD_GU: C[row][n]; WGRAD: C[e][m][n], columns >= f of the

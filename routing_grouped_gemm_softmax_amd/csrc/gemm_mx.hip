@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
     }
     wait_vmcnt<0>();
     __syncthreads();  // every wave is done with the ring
-    epilogue<MODE, BM, BN>(p, acc, smem, wave, lane, tc);
+    epilogue<MODE, BM, BN, true>(p, acc, smem, wave, lane, tc);
   };
   if constexpr (MODE == WGRAD) {
     wgrad_sched<BM, BN, 64, kEpiWorkX>(p, s_info, wave, lane);

@@ -47,6 +47,13 @@ struct GemmParams {
   // half-height, half-width tiles; see ragged_tile.
   int cus;
   int tail;
+  // MXFP8 kernels, FWD_GU and BWD_DOWN: the epilogue also writes its bf16
+  // output rows (H; dG | dU) as the next GEMM's K-major E4M3 operand, q [S][ld]
+  // and slab-major scales (as p.as above, slab = mxs_slab bytes).
+  uint8_t* mxq;
+  uint8_t* mxs;
+  int64_t mxq_ld;
+  int64_t mxs_slab;
 };
 
 // bf16 grouped GEMMs (gemm_bf16.hip).

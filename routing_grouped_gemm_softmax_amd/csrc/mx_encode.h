@@ -72,4 +72,23 @@ __device__ __forceinline__ int mx_encode_block(const float (&v)[32], uint32_t (&
   return c;
 }
 
+// Eight consecutive values of one block (block scale code c) -> 8 E4M3 bytes.
+__device__ __forceinline__ uint2 mx_encode8(const float (&v)[8], int c) {
+  const int sh = 127 - c;
+  return make_uint2(e4m3_encode4(ldexpf(v[0], sh), ldexpf(v[1], sh), ldexpf(v[2], sh), ldexpf(v[3], sh)),
+                    e4m3_encode4(ldexpf(v[4], sh), ldexpf(v[5], sh), ldexpf(v[6], sh), ldexpf(v[7], sh)));
+}
+
+// Block scale code of a 32-block held by 4 consecutive lanes (8 values each,
+// lane groups aligned to 4): the maximum over the group, by two butterflies.
+// Every lane of the wave must execute it.
+__device__ __forceinline__ int mx_group4_code(const float (&v)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  return mx_scale_code(amax);
+}
+
 }  // namespace moe

@@ -82,24 +82,6 @@ hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int
 // slab-major (per 64-k slab, 2 bytes per row: the slab's two 32-blocks).
 // ---------------------------------------------------------------------------------
 
-// Eight consecutive values of one block (block scale code c) -> 8 E4M3 bytes.
-__device__ __forceinline__ uint2 encode8(const float (&v)[8], int c) {
-  const int sh = 127 - c;
-  return make_uint2(e4m3_encode4(ldexpf(v[0], sh), ldexpf(v[1], sh), ldexpf(v[2], sh), ldexpf(v[3], sh)),
-                    e4m3_encode4(ldexpf(v[4], sh), ldexpf(v[5], sh), ldexpf(v[6], sh), ldexpf(v[7], sh)));
-}
-
-// Block scale code of a 32-block held by 4 consecutive lanes (8 values each,
-// lane groups aligned to 4): the maximum over the group, by two butterflies.
-__device__ __forceinline__ int group4_code(const float (&v)[8]) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-  return mx_scale_code(amax);
-}
-
 // K along the columns: in [R][C] -> q [R][C], s [C/64][R][2], batched (one
 // batch per expert for the weights). A wave covers tiles of 8 rows x 64
 // columns: lane l takes row l / 8, columns 8 (l % 8) .. +7, so each load is
@@ -133,9 +115,9 @@ __global__ __launch_bounds__(256) void mx_kmajor_kernel(const bf16_t* __restrict
     const int row = static_cast<int>(rem / (C / 64)) * 8 + rl, c64 = static_cast<int>(rem % (C / 64));
     float v[8];
     unpack16(raw[u], v);
-    const int code = group4_code(v);
+    const int code = mx_group4_code(v);
     *reinterpret_cast<uint2*>(q + b * q_bstride + static_cast<int64_t>(row) * C + c64 * 64 + ch * 8) =
-        encode8(v, code);
+        mx_encode8(v, code);
     const int code_hi = __shfl(code, (lane & ~7) + 4, kWave);
     if (ch == 0)
       *reinterpret_cast<uint16_t*>(s + b * s_bstride + (static_cast<int64_t>(c64) * R + row) * 2) =
@@ -200,9 +182,9 @@ __global__ __launch_bounds__(256) void mx_tgroup_kernel(const bf16_t* __restrict
       // Columns-blocked copy straight from the registers (one group: row p0 + r).
       float f[8];
       unpack16(v, f);
-      const int code = group4_code(f);
+      const int code = mx_group4_code(f);
       const int64_t row = p0 + r;
-      *reinterpret_cast<uint2*>(qk + static_cast<int64_t>(b) * q_bstride + row * C + c0 + ch * 8) = encode8(f, code);
+      *reinterpret_cast<uint2*>(qk + static_cast<int64_t>(b) * q_bstride + row * C + c0 + ch * 8) = mx_encode8(f, code);
       const int code_hi = __shfl(code, (tid & 56) + 4, kWave);
       if (ch == 0)
         *reinterpret_cast<uint16_t*>(sk + static_cast<int64_t>(b) * s_bstride +
