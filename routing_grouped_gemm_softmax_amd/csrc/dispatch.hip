@@ -12,23 +12,29 @@
 //
 // Placement order inside an expert is increasing token index, which makes
 // the permutation unique; it is computed without atomics on the slot order:
-//   1. count:  per chunk of kChunkTok tokens, an LDS histogram of expert ids;
-//   2. scan:   one workgroup turns the [chunk][expert] counts into counts,
-//              offsets and the first row of every (chunk, expert) pair;
-//   3. place:  per chunk, waves walk the slots in order; a ballot-based
-//              match gives each slot its rank among equal experts of the
-//              wave, and per-wave totals in LDS give the ranks across waves.
+//   1. count:  per chunk of tokens, an LDS histogram of expert ids;
+//   2. place:  per chunk, the workgroup first sums the [chunk][expert] counts
+//              of all chunks (expert totals, offsets by a block scan) and of
+//              the chunks before its own (its first row per expert); then
+//              waves walk the slots in order, a ballot-based match gives each
+//              slot its rank among equal experts of the wave, and per-wave
+//              totals in LDS give the ranks across waves. Workgroup 0 also
+//              writes counts, offsets and the status word.
+// Chunks are 128 tokens while the [chunk][expert] table stays small (few
+// tokens: more workgroups), else 512.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kChunkTok = 512;  // tokens per histogram chunk
+// Tokens per histogram chunk.
+static int chunk_tokens(int T, int E) {
+  return static_cast<int64_t>((T + 127) / 128) * E <= 4096 ? 128 : 512;
+}
 
 struct DispatchWs {
   int32_t* status;       // 1 int (padded to 256 B)
   int32_t* chunk_counts; // [nch][E]
-  int32_t* chunk_base;   // [nch][E]
   int32_t* chunk_bad;    // [nch]
 };
 
@@ -39,26 +45,26 @@ static DispatchWs carve(void* ws, int nch, int E) {
   DispatchWs w;
   w.status = reinterpret_cast<int32_t*>(p); p += 256;
   w.chunk_counts = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * nch * E);
-  w.chunk_base = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * nch * E);
   w.chunk_bad = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
 size_t dispatch_workspace(int T, int E) {
-  const int nch = (T + kChunkTok - 1) / kChunkTok;
-  return 256 + 2 * align256(sizeof(int32_t) * nch * E) + align256(sizeof(int32_t) * nch);
+  const int ct = chunk_tokens(T, E);
+  const int nch = (T + ct - 1) / ct;
+  return 256 + align256(sizeof(int32_t) * nch * E) + align256(sizeof(int32_t) * nch);
 }
 
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
-                                                             DispatchWs w) {
+                                                             int ct, DispatchWs w) {
   __shared__ int hist[256];
   __shared__ int bad;
   const int c = blockIdx.x, tid = threadIdx.x;
   hist[tid] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
-  const int64_t s0 = static_cast<int64_t>(c) * kChunkTok * k;
-  const int64_t s1 = min(static_cast<int64_t>(T), static_cast<int64_t>(c + 1) * kChunkTok) * k;
+  const int64_t s0 = static_cast<int64_t>(c) * ct * k;
+  const int64_t s1 = min(static_cast<int64_t>(T), static_cast<int64_t>(c + 1) * ct) * k;
   int my_bad = 0;
   for (int64_t s = s0 + tid; s < s1; s += 256) {
     const int e = idx[s];
@@ -71,84 +77,61 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   if (tid == 0) w.chunk_bad[c] = bad;
 }
 
-// Single workgroup: counts, offsets, and chunk_base[c][e] = offsets[e] + rows
-// of expert e in chunks before c. Also writes the device status word.
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int nch, int E, DispatchWs w, int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets) {
-  __shared__ int segsum[1024];
-  __shared__ int tot[256];
-  __shared__ int off[257];
-  const int tid = threadIdx.x;
-  const int nseg = max(1, min(nch, 1024 / E));
-  const int cps = (nch + nseg - 1) / nseg;
-  const int seg = tid / E, e = tid % E;
-  const bool mine = seg < nseg;
-  if (mine) {
-    int sum = 0;
-    const int c1 = min(nch, (seg + 1) * cps);
-    for (int c = seg * cps; c < c1; ++c) sum += w.chunk_counts[static_cast<int64_t>(c) * E + e];
-    segsum[seg * E + e] = sum;
-  }
-  __syncthreads();
-  if (tid < E) {
-    int run = 0;
-    for (int s = 0; s < nseg; ++s) {
-      const int v = segsum[s * E + tid];
-      segsum[s * E + tid] = run;
-      run += v;
-    }
-    tot[tid] = run;
-  }
-  __syncthreads();
-  if (tid < 64) {  // exclusive scan over experts: 4 experts per lane
-    int v[4], sum = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ee = tid * 4 + q;
-      v[q] = ee < E ? tot[ee] : 0;
-      sum += v[q];
-    }
-    int run = wave_exclusive_scan(sum);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ee = tid * 4 + q;
-      if (ee < E) off[ee] = run;
-      run += v[q];
-    }
-    if (tid == 63) off[E] = run;
-  }
-  __syncthreads();
-  if (tid < E) counts[tid] = tot[tid];
-  if (tid <= E) offsets[tid] = off[tid];
-  if (mine) {
-    int base = off[e] + segsum[seg * E + e];
-    const int c1 = min(nch, (seg + 1) * cps);
-    for (int c = seg * cps; c < c1; ++c) {
-      w.chunk_base[static_cast<int64_t>(c) * E + e] = base;
-      base += w.chunk_counts[static_cast<int64_t>(c) * E + e];
-    }
-  }
-  if (tid == 0) {
-    int bad = 0;
-    for (int c = 0; c < nch; ++c) bad |= w.chunk_bad[c];
-    w.status[0] = bad ? 1 : 0;
-  }
-}
-
 __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
-                                                             int bits, DispatchWs w, int32_t* __restrict__ row_of_slot,
+                                                             int bits, int ct, int nch, DispatchWs w,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ row_of_slot,
                                                              int32_t* __restrict__ token_of_row) {
+  constexpr int kTab = 4096;  // ints of the [chunk][expert] table staged at a time
+  __shared__ int tab[kTab];
   __shared__ int base[256];
   __shared__ int wcnt[4][256];
+  __shared__ int wsum[4];
   const int c = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  // Expert tid: total rows, and rows in the chunks before this one. The
+  // table goes through LDS in pieces of whole chunk rows, read by all threads.
+  int tot = 0, before = 0;
+  const int rows_per = kTab / E;
+  for (int c0 = 0; c0 < nch; c0 += rows_per) {
+    const int nrow = min(rows_per, nch - c0);
+    for (int i = tid; i < nrow * E; i += 256) tab[i] = w.chunk_counts[static_cast<int64_t>(c0) * E + i];
+    __syncthreads();
+    if (tid < E) {
+      for (int r = 0; r < nrow; ++r) {
+        const int n = tab[r * E + tid];
+        tot += n;
+        if (c0 + r < c) before += n;
+      }
+    }
+    __syncthreads();
+  }
+  // Exclusive scan of the totals over experts: waves, then their sums.
+  const int incl_w = wave_exclusive_scan(tot) + tot;
+  if ((tid & 63) == 63) wsum[wave] = incl_w;
+  __syncthreads();
+  int off = incl_w - tot;
+  for (int q = 0; q < wave; ++q) off += wsum[q];
   if (tid < E) {
-    base[tid] = w.chunk_base[static_cast<int64_t>(c) * E + tid];
+    base[tid] = off + before;
 #pragma unroll
     for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
   }
+  if (c == 0) {
+    if (tid < E) {
+      counts[tid] = tot;
+      offsets[tid] = off;
+    }
+    if (tid == E - 1) offsets[E] = off + tot;
+    if (tid == 0) {
+      int bad = 0;
+      for (int cc = 0; cc < nch; ++cc) bad |= w.chunk_bad[cc];
+      w.status[0] = bad ? 1 : 0;
+    }
+  }
   __syncthreads();
-  const int64_t s0 = static_cast<int64_t>(c) * kChunkTok * k;
-  const int64_t s1 = min(static_cast<int64_t>(T), static_cast<int64_t>(c + 1) * kChunkTok) * k;
+  const int64_t s0 = static_cast<int64_t>(c) * ct * k;
+  const int64_t s1 = min(static_cast<int64_t>(T), static_cast<int64_t>(c + 1) * ct) * k;
   for (int64_t sb = s0; sb < s1; sb += 256) {
     const int64_t s = sb + tid;
     const bool in = s < s1;
@@ -205,17 +188,16 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E, int k,
                            int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
                            void* xp, void* ws, hipStream_t s) {
-  const int nch = (T + kChunkTok - 1) / kChunkTok;
+  const int ct = chunk_tokens(T, E);
+  const int nch = (T + ct - 1) / ct;
   DispatchWs w = carve(ws, nch, E);
   int bits = 0;
   while ((1 << bits) < E) ++bits;
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(256), 0, s, topk_idx, T, E, k, w);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(256), 0, s, topk_idx, T, E, k, ct, w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, nch, E, w, counts, offsets);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_place_kernel, dim3(nch), dim3(256), 0, s, topk_idx, T, E, k, bits, w, row_of_slot,
-                     token_of_row);
+  hipLaunchKernelGGL(dispatch_place_kernel, dim3(nch), dim3(256), 0, s, topk_idx, T, E, k, bits, ct, nch, w, counts,
+                     offsets, row_of_slot, token_of_row);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int nvec = d * elem_bytes / 16;
   const int lpt = lanes_per_token(nvec);
