@@ -249,67 +249,112 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
   }
 }
 
-// FWD_DOWN with 256 x 256 tiles, as a persistent grid of p.cus workgroups
-// that streams slabs across tiles: each workgroup owns tiles lo, lo + wpx,
-// ... of its XCD's range, and the ring never drains between them. The loads
+// FWD_DOWN and the weight gradients with 256 x 256 tiles, as a persistent
+// grid that streams slabs across tiles: each workgroup owns a strided share
+// of its XCD's tile range (FWD_DOWN: lo, lo + wpx, ...; WGRAD: the range
+// wgrad_sched gives it), and the ring never drains between tiles. The loads
 // of the next tile's first slabs go out during the current tile's last
 // slabs, and the epilogue (staged through a per-wave LDS area beside the
-// ring, written with buffer stores) runs while they fly. At K = d_ff this
-// mode has only 32 slabs per tile; measured at T = 8192, d = 2048, E = 8,
-// k = 4, d_ff = 1024 it runs in 156 us against 176 us with one tile per
-// workgroup. The same scheme gained nothing for the dgrad of the gate/up
-// projection (64 slabs per tile), and the SwiGLU epilogue of the gate/up
-// forward does not fit its registers beside the stream state.
+// ring, written with buffer stores) runs while they fly. Both modes have few
+// slabs per tile: FWD_DOWN has K = d_ff; a weight gradient has K = its
+// expert's rows, often under 16 slabs, and an empty expert has none (its
+// tile is all epilogue, writing zeros). Measured at T = 8192, d = 2048, E =
+// 8, k = 4, d_ff = 1024, FWD_DOWN runs in 156 us against 176 us with one tile
+// per workgroup; with E = 128 (256 rows per expert) the two weight
+// gradients take 229 + 441 us against 254 + 490 us. The same scheme gained
+// nothing for the dgrad of the gate/up projection (64 slabs per tile), and
+// the SwiGLU epilogue of the gate/up forward does not fit its registers
+// beside the stream state.
 //
-// Wait counts: vmcnt counts loads and stores together, in issue order. In the
-// three slabs after an epilogue the slab being waited for was issued before
-// that epilogue's kEpiStores stores, so those waits allow kEpiStores more
-// outstanding operations (a smaller count would only wait longer). Every
-// epilogue issues exactly kEpiStores stores (buffer stores: rows past an
-// expert's end are dropped by the range check, not by a branch), and tiles
-// have at least kStages slabs, so epilogues are at least that many slabs
-// apart.
+// Wait counts: vmcnt counts loads and stores together, in issue order. The
+// wait for slab g+1 must allow exactly the operations issued after that
+// slab's loads: the loads of slabs g+2 and g+3, and kEpiStores stores for
+// each epilogue since (every epilogue issues exactly that many: buffer
+// stores, whose range check, not a branch, drops rows past the end). The
+// kernel counts those epilogues per slab in flight; past two it waits for
+// 63, which only waits longer.
 template <int MODE>
 __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, MB = 4, NB = 4;
-  static_assert(MODE == FWD_DOWN, "streaming mode");
+  static_assert(MODE == FWD_DOWN || MODE == WGRAD, "streaming modes");
+  constexpr bool M_MN = (MODE == WGRAD);  // A stored [k][m]
   constexpr int TILE_M = BM * kBK * 2, TILE_N = BN * kBK * 2;
   constexpr int STAGE = TILE_M + TILE_N;
   constexpr int RING = kStages * STAGE;
   constexpr int kStg = 64 * 128;  // per-wave staging tile: 64 rows x 64 bf16
   constexpr int kEpiStores = 4 * 8;
   constexpr int LM = BM / 64, LN = BN / 64, kLoads = LM + LN;
-  constexpr int kWaitSteady = kLoads * (kStages - 2);
-  constexpr int kWaitEpi = kWaitSteady + kEpiStores < 63 ? kWaitSteady + kEpiStores : 63;
+  constexpr int kWait0 = kLoads * (kStages - 2);
+  constexpr int kWait1 = kWait0 + kEpiStores < 63 ? kWait0 + kEpiStores : 63;
+  static_assert(kStages == 4, "epilogue accounting written for slabs g+1..g+3 in flight");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
+  // ---- this workgroup's tiles ------------------------------------------------------------
   RowTileMap map;
-  map.init(p, BM, BN, lane);
-  const int rmain = map.main_tiles(p.cus);
-  const int x = blockIdx.x % 8, wi = blockIdx.x / 8, wpx = gridDim.x / 8;
-  const int lo = xcd_cut(rmain, x) + wi, hi = xcd_cut(rmain, x + 1);
-  const int ntiles = lo < hi ? (hi - lo + wpx - 1) / wpx : 0;
+  int lo, step, ntiles;
+  if constexpr (MODE == FWD_DOWN) {
+    map.init(p, BM, BN, lane);
+    const int rmain = map.main_tiles(p.cus);
+    const int x = blockIdx.x % 8, wpx = gridDim.x / 8;
+    lo = xcd_cut(rmain, x) + blockIdx.x / 8;
+    const int hi = xcd_cut(rmain, x + 1);
+    step = wpx;
+    ntiles = lo < hi ? (hi - lo + wpx - 1) / wpx : 0;
+  } else {
+    int* s_info = reinterpret_cast<int*>(smem + RING);  // the staging area, free until the first epilogue
+    wgrad_sched<BM, BN, kBK, kEpiWork>(p, s_info, wave, lane);
+    lo = __builtin_amdgcn_readfirstlane(s_info[0]);
+    const int hi = __builtin_amdgcn_readfirstlane(s_info[1]);
+    step = __builtin_amdgcn_readfirstlane(s_info[2]);
+    ntiles = lo < hi ? (hi - lo + step - 1) / step : 0;
+    __syncthreads();  // s_info is read out before any wave's epilogue stages there
+  }
   if (ntiles == 0) return;
-  const int nk = p.K / kBK;
+  auto tile_at = [&](int j) -> TileCoord {
+    if constexpr (MODE == FWD_DOWN) return map.at(lo + j * step, lane);
+    else return wgrad_tile<BM, BN>(p, lo + j * step);
+  };
+  auto slabs_of = [&](const TileCoord& tc) -> int {
+    if constexpr (MODE == FWD_DOWN) return p.K / kBK;
+    else return (tc.row_end - tc.row0 + kBK - 1) / kBK;
+  };
   const char* const A = static_cast<const char*>(p.a);
 
   // ---- HBM -> LDS: load L of slab kt of tile tc (empty descriptors if !live) --------------
   auto issue = [&](const TileCoord& tc, int kt, bool live, uint32_t slot, auto L, auto w) {
     constexpr int l = decltype(L)::value, W = decltype(w)::value;
-    if constexpr (l < LM) {
-      const char* base = A + (static_cast<int64_t>(tc.row0) * p.lda + kt * kBK) * 2;
-      const int valid = live ? min(BM, tc.row_end - tc.row0) : 0;
-      load_rows64<BM, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda * 2, slot, wave, lane, l);
+    if constexpr (MODE == FWD_DOWN) {
+      if constexpr (l < LM) {
+        const char* base = A + (static_cast<int64_t>(tc.row0) * p.lda + kt * kBK) * 2;
+        const int valid = live ? min(BM, tc.row_end - tc.row0) : 0;
+        load_rows64<BM, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda * 2, slot, wave, lane, l);
+      } else {
+        // W_down [f][d] of the tile's expert: rows k, columns n.
+        constexpr int q = l - LM;
+        const int64_t off =
+            (static_cast<int64_t>(tc.e) * p.bstride + static_cast<int64_t>(kt) * kBK * p.ldb + tc.nt * BN) * 2;
+        load_mnmajor<BN, W>(
+            make_rsrc(static_cast<const char*>(p.b0) + off, live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0),
+            p.ldb, slot + TILE_M, wave, lane, q);
+      }
     } else {
-      // W_down [f][d] of the tile's expert: rows k, columns n.
-      constexpr int q = l - LM;
-      const int64_t off = (static_cast<int64_t>(tc.e) * p.bstride + static_cast<int64_t>(kt) * kBK * p.ldb + tc.nt * BN) * 2;
-      load_mnmajor<BN, W>(make_rsrc(static_cast<const char*>(p.b0) + off, live ? static_cast<int64_t>(kBK) * p.ldb * 2 : 0),
-                          p.ldb, slot + TILE_M, wave, lane, q);
+      // Both operands [k][m] / [k][n] over the expert's rows; rows past its
+      // end read as zero.
+      const int k0 = tc.row0 + kt * kBK;
+      const int valid = live ? min(kBK, tc.row_end - k0) : 0;
+      if constexpr (l < LM) {
+        const char* base = A + (static_cast<int64_t>(k0) * p.lda + tc.m0) * 2;
+        load_mnmajor<BM, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.lda * 2), p.lda, slot, wave, lane, l);
+      } else {
+        constexpr int q = l - LM;
+        const char* base = static_cast<const char*>(p.b0) + (static_cast<int64_t>(k0) * p.ldb + tc.nt * BN) * 2;
+        load_mnmajor<BN, W>(make_rsrc(base, static_cast<int64_t>(valid) * p.ldb * 2), p.ldb, slot + TILE_M, wave,
+                            lane, q);
+      }
     }
   };
 
@@ -322,7 +367,8 @@ __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
     const char* tm = slotp;
     const char* tn = slotp + TILE_M;
     if constexpr (fi < MB) {
-      F.m[fi] = frag_kmajor(tm, wm * WM + fi * 32, kk, lane);
+      if constexpr (M_MN) F.m[fi] = frag_mnmajor<BM>(tm, wm * WM + fi * 32, kk, lane);
+      else F.m[fi] = frag_kmajor(tm, wm * WM + fi * 32, kk, lane);
     } else {
       F.n[fi - MB] = frag_mnmajor<BN>(tn, wn * WN + (fi - MB) * 32, kk, lane);
     }
@@ -334,7 +380,7 @@ __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
     constexpr int mi = decltype(MI)::value, j = mi / MB, i = mi % MB;
     acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.n[j], F.m[i], acc[j][i], 0, 0, 0);
   };
-  constexpr int kReads = MB + NB * 2;
+  constexpr int kReads = MB * (M_MN ? 2 : 1) + NB * 2;
   constexpr int kMfma = MB * NB;
   constexpr int kFrags = MB + NB;
   auto interleave = [&]() {
@@ -377,10 +423,23 @@ __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
     return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
   };
   auto epilogue = [&](const TileCoord& tc) {
-    const int mrow = tc.row0 + wm * WM;
-    const int rows = tc.row_end - mrow;  // may be <= 0 or > WM: flush clamps
     const int64_t ld = p.ldc * 2;
-    const char* out = static_cast<const char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + tc.nt * BN + wn * WN) * 2;
+    const char* out;
+    int rows;
+    if constexpr (MODE == FWD_DOWN) {
+      const int mrow = tc.row0 + wm * WM;
+      rows = tc.row_end - mrow;  // may be <= 0 or > WM: flush clamps
+      out = static_cast<const char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + tc.nt * BN + wn * WN) * 2;
+    } else {
+      // dW[e] rows m0.., columns n0..; columns >= f of the gate|up gradient
+      // go to the second output (dw_up).
+      const char* base = static_cast<const char*>(p.c0);
+      int cn0 = tc.nt * BN;
+      if (p.c1 != nullptr && cn0 >= p.f) { base = static_cast<const char*>(p.c1); cn0 -= p.f; }
+      rows = WM;
+      out = base + (static_cast<int64_t>(tc.e) * p.cstride +
+                    static_cast<int64_t>(tc.m0 + wm * WM) * p.ldc + cn0 + wn * WN) * 2;
+    }
     static_for<2>([&](auto JP) {
       static_for<2>([&](auto HH) {
         constexpr int h = decltype(HH)::value;
@@ -397,15 +456,28 @@ __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
   };
 
   // ---- the slab stream ------------------------------------------------------------------
-  TileCoord cur = map.at(lo, lane);
-  TileCoord ltc = cur;  // tile of the next slab to load
-  int lj = 0, lkt = 0;  // its index among this workgroup's tiles, and slab
-  auto advance = [&]() {
-    if (++lkt == nk) {
+  // Load side: tile index lj, its slab lkt and slab count lnk (tiles without
+  // slabs are skipped here; they still get their epilogue below).
+  int lj = 0, lkt = 0;
+  TileCoord ltc = tile_at(0);
+  int lnk = slabs_of(ltc);
+  auto skip_empty = [&]() {
+    while (lkt >= lnk && lj < ntiles) {
       lkt = 0;
-      if (++lj < ntiles) ltc = map.at(lo + lj * wpx, lane);
+      if (++lj < ntiles) {
+        ltc = tile_at(lj);
+        lnk = slabs_of(ltc);
+      }
     }
   };
+  skip_empty();
+  auto advance = [&]() {
+    ++lkt;
+    skip_empty();
+  };
+  // Epilogues issued after the loads of slabs g+1, g+2, g+3 (g: the slab
+  // being multiplied).
+  int ep1 = 0, ep2 = 0, ep3 = 0;
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 #pragma unroll
   for (int s0 = 0; s0 < kStages; ++s0) {
@@ -418,6 +490,8 @@ __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
   read_frags(smem, 0, F[0]);
   int gk = 0;  // slabs consumed: slab gk sits in slot gk % kStages
   for (int j = 0; j < ntiles; ++j) {
+    const TileCoord cur = tile_at(j);
+    const int nk = slabs_of(cur);
 #pragma unroll
     for (int jj = 0; jj < NB; ++jj)
 #pragma unroll
@@ -431,8 +505,9 @@ __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
       read_frags(curp, 1, F[1]);
       static_for<kMfma>([&](auto MI) { mfma_one(F[0], MI); });
       interleave();
-      if (j > 0 && kt < kStages - 1) wait_vmcnt<kWaitEpi>();
-      else wait_vmcnt<kWaitSteady>();
+      if (ep1 == 0) wait_vmcnt<kWait0>();
+      else if (ep1 == 1) wait_vmcnt<kWait1>();
+      else wait_vmcnt<63>();
       __syncthreads();
       const uint32_t slot = ring + sc * STAGE;
       const bool live = lj < ntiles;
@@ -446,11 +521,13 @@ __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
       });
       advance();
+      ep1 = ep2; ep2 = ep3; ep3 = 0;  // slab gk+4 was just issued
     }
-    // F[0] already holds the first fragments of the next tile (read during
-    // the last slab), whose slot is not refilled before the next barrier.
+    // F[0] already holds the first fragments of the next tile with slabs
+    // (read during the last slab), whose slot is not refilled before the next
+    // barrier.
     epilogue(cur);
-    if (j + 1 < ntiles) cur = map.at(lo + (j + 1) * wpx, lane);
+    ++ep1; ++ep2; ++ep3;
   }
   // Drain the (empty) loads and the stores still in flight before the wave ends.
   wait_vmcnt<0>();
@@ -476,11 +553,11 @@ hipError_t launch_tail(const GemmParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The streaming kernel on as many workgroups as run at once, then the
-// quarter tiles of its short last round (both launches split the tile list
-// with the same p.cus).
+// The streaming kernel on as many workgroups as run at once (WGRAD: at most
+// one per tile); for FWD_DOWN then the quarter tiles of its short last round
+// (both launches split the tile list with the same p.cus).
 template <int MODE>
-hipError_t launch_stream(GemmParams p, hipStream_t s) {
+hipError_t launch_stream(GemmParams p, int tiles, hipStream_t s) {
   constexpr int lds = kStages * (256 + 256) * kBK * 2 + 4 * 64 * 128;
   auto kern = gg_bf16_stream_kernel<MODE>;
   static std::atomic<int> per_cu{0};
@@ -494,13 +571,18 @@ hipError_t launch_stream(GemmParams p, hipStream_t s) {
     per_cu.store(n > 0 ? n : 1);
   }
   const int cap = max(8, device_cu_count() * per_cu.load() / 8 * 8);
-  p.cus = cap;
-  p.tail = 0;
-  hipLaunchKernelGGL(kern, dim3(cap), dim3(256), lds, s, p);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  p.tail = 1;
-  return launch_tail<MODE, 128, 128>(p, cap, s);
+  if constexpr (MODE == WGRAD) {
+    hipLaunchKernelGGL(kern, dim3(min(cap, round8(tiles))), dim3(256), lds, s, p);
+    return hipGetLastError();
+  } else {
+    p.cus = cap;
+    p.tail = 0;
+    hipLaunchKernelGGL(kern, dim3(cap), dim3(256), lds, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    p.tail = 1;
+    return launch_tail<MODE, 128, 128>(p, cap, s);
+  }
 }
 
 template <int MODE, int BM, int BN>
@@ -524,7 +606,14 @@ hipError_t launch_tile(const GemmParams& p0, int tiles, hipStream_t s) {
   const int cap = max(8, device_cu_count() * per_cu.load() / 8 * 8);
   if constexpr (MODE == WGRAD) {
     // A persistent grid: as many workgroups as run at once (a multiple of 8:
-    // one share per XCD).
+    // one share per XCD). 256 x 256 tiles stream their slabs when experts
+    // average under 512 rows (16 slabs per tile); with longer tiles the
+    // stream's bookkeeping costs more than the tile turnover it hides
+    // (measured: -9% at 256 rows per expert, +5% at 4096 and on the Zipf
+    // layer's hot experts).
+    if constexpr (BM == 256 && BN == 256) {
+      if (static_cast<int64_t>(p0.S) < 512LL * p0.E) return launch_stream<WGRAD>(p0, tiles, s);
+    }
     hipLaunchKernelGGL(kern, dim3(min(cap, round8(tiles))), dim3(256), lds, s, p0);
     return hipGetLastError();
   } else {
@@ -537,7 +626,7 @@ hipError_t launch_tile(const GemmParams& p0, int tiles, hipStream_t s) {
     p.cus = kQuarters ? cap : 0;
     p.tail = 0;
     if constexpr (kQuarters && MODE == FWD_DOWN) {
-      if (p.K / kBK >= kStages) return launch_stream<MODE>(p, s);
+      if (p.K / kBK >= kStages) return launch_stream<MODE>(p, 0, s);
     }
     hipLaunchKernelGGL(kern, dim3(round8(tiles)), dim3(256), lds, s, p);
     hipError_t err = hipGetLastError();

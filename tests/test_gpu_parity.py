@@ -36,6 +36,11 @@ CASES = {
     "bf16_stream_multi_tile": ("bf16_e8", dict(T=16384, d=1024, E=4, k=2, f=512), None),
     # 256 x 256 tiles with an empty expert.
     "bf16_stream_empty_expert": ("bf16_zipf", dict(T=4096, d=512, E=4, k=2, f=512), [1, 0, 2, 1]),
+    # Streaming weight gradients (experts average 64 rows): tiles of 0 to a few
+    # slabs, several epilogues within three slabs, two tiles per workgroup.
+    # Eight experts get no rows.
+    "bf16_wgrad_stream_short_tiles": ("bf16_zipf", dict(T=4096, d=512, E=128, k=2, f=256),
+                                      [0 if e % 16 == 5 else 1 + e % 7 for e in range(128)]),
 }
 
 
