@@ -7,24 +7,26 @@
 // section "Cómo funciona"; "Ai2 rilascia Olmo-Core 3...", section
 // "Parallelismo, precisione e tecniche di memoria"). Every workgroup reads the
 // E+1 offsets and maps its id to (expert, row tile, column tile) with a wave
-// scan over the per-expert tile counts; the grid is sized on the host from
-// the count-free bound ceil(S/BM) + E row tiles. The weight gradients, whose
-// tiles cost as much as their expert has rows, run on a persistent grid with
-// XCD ranges cut by cost when the load is skewed (gemm_device.h).
+// scan over the per-expert tile counts (RowTileMap); the grid is sized on the
+// host from the count-free bound ceil(S/BM) + E row tiles. The weight
+// gradients, whose tiles cost as much as their expert has rows, run on a
+// persistent grid with XCD ranges cut by cost when the load is skewed
+// (gemm_device.h). FWD_DOWN, and the weight gradients of small experts, run
+// as persistent grids that stream slabs across tiles (gg_bf16_stream_kernel).
 //
 // Tile: 256 threads = 4 waves in 2 x 2; a BM x BN output tile, each wave a
 // (BM/2) x (BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16) with
-// the accumulators in AGPRs. K advances in slabs of 64 elements.
+// the accumulators in AGPRs. K advances in slabs of 32 elements (64 bytes).
 //
 // Operands move HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
-// VGPR staging), double-buffered: the loads of slab kt+1 fly while slab kt is
-// multiplied. The buffer range check zero-fills rows past an expert's end,
-// which both masks ragged row tiles and gives the weight gradients their
-// ragged K for free. LDS layouts:
-//  - K-contiguous operand: [row][64 k] rows of 128 B, 16-byte chunks
+// VGPR staging) into a ring of 4 slab slots: the loads of slabs kt+1..kt+3
+// fly while slab kt is multiplied. The buffer range check zero-fills rows
+// past an expert's end, which both masks ragged row tiles and gives the
+// weight gradients their ragged K for free. LDS layouts:
+//  - K-contiguous operand: [row][32 k] rows of 64 B, 16-byte chunks
 //    XOR-swizzled by the row; fragments are one ds_read_b128 per lane.
 //  - row-contiguous operand ([k][rows] in HBM: the weights in the forward and
-//    both operands of the weight gradients): [64 k][rows] as stored, chunks
+//    both operands of the weight gradients): [32 k][rows] as stored, chunks
 //    XOR-swizzled by k; fragments are two ds_read_b64_tr_b16 per lane, which
 //    transpose 16 x 4 blocks on the way out of LDS.
 // The N-side fragment is the MFMA's first operand, so every lane ends up with

@@ -44,7 +44,7 @@ struct GemmParams {
   int64_t bs_estride; // bytes between experts in bs0/bs1
   // Row-ragged modes: with cus > 0 (workgroups that run at once) the tiles
   // past the last full round are left to a second launch (tail = 1) of
-  // half-height, half-width tiles; see ragged_tile.
+  // half-height, half-width tiles; see RowTileMap.
   int cus;
   int tail;
   // MXFP8 kernels, FWD_GU and BWD_DOWN: the epilogue also writes its bf16
