@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const bf16_t* __restric
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_gate) {
   constexpr int E16 = EB * 16;
-  constexpr int U = EB >= 8 ? 1 : 8 / EB;  // k steps in flight per wave
+  constexpr int U = EB >= 16 ? 1 : 16 / EB;  // k steps in flight per wave
   __shared__ float buf[16][E16 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * 16;
@@ -190,6 +190,9 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restr
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int dc0 = blockIdx.x * 64, tc0 = blockIdx.y * kTokChunk;
+  const int cw = wave * 16;                 // this wave's 16 columns of the tile
+  const int g = lane >> 4, sl = lane & 15;  // 16-lane group, lane inside it
+  const int64_t brow = static_cast<int64_t>(sl) * Tp + tc0 + 8 * g;
   {
     const int valid = max(0, min(kTokChunk, T - tc0));  // rows past T read as zero
     const int64_t bytes = static_cast<int64_t>(valid) * d * 2;
@@ -200,20 +203,34 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restr
     for (int q = 0; q < kTokChunk * 128 / 4096; ++q) {
       const int byte0 = (q * 4 + wave) * 1024;
       const int kr = (byte0 >> 7) + (lane >> 3);
-      const int g = (lane & 7) ^ xt_swz(kr);
-      load_lds16(rs, static_cast<uint32_t>(kr * d * 2 + g * 16), base + byte0);
+      const int ch = (lane & 7) ^ xt_swz(kr);
+      load_lds16(rs, static_cast<uint32_t>(kr * d * 2 + ch * 16), base + byte0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0070 | (15 << 8));  // vmcnt(0)
-    __syncthreads();
   }
+  // With few expert blocks, all of the chunk's dl^T operands (EB x 8 steps x
+  // hi, lo: 16 bytes each) are requested while the x tile lands, so the
+  // loop below does not wait on memory.
+  constexpr bool kPrefetch = EB <= 2;
+  constexpr int kSteps = kTokChunk / 32;
+  bf16x8 pre_h[kPrefetch ? EB : 1][kPrefetch ? kSteps : 1], pre_l[kPrefetch ? EB : 1][kPrefetch ? kSteps : 1];
+  if constexpr (kPrefetch) {
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+      for (int kk = 0; kk < kSteps; ++kk) {
+        const int64_t o = static_cast<int64_t>(eb) * 16 * Tp + brow + kk * 32;
+        pre_h[eb][kk] = *reinterpret_cast<const bf16x8*>(dlt_hi + o);
+        pre_l[eb][kk] = *reinterpret_cast<const bf16x8*>(dlt_lo + o);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070 | (15 << 8));  // vmcnt(0): the x tile (and the dl^T operands)
+  __syncthreads();
+
   floatx4 acc[EB];
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) acc[eb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int cw = wave * 16;                 // this wave's 16 columns of the tile
-  const int g = lane >> 4, sl = lane & 15;  // 16-lane group, lane inside it
-  const int64_t brow = static_cast<int64_t>(sl) * Tp + tc0 + 8 * g;
-#pragma unroll 2
-  for (int kk = 0; kk < kTokChunk / 32; ++kk) {
+#pragma unroll
+  for (int kk = 0; kk < kSteps; ++kk) {
     // Row operand = x^T: lane -> column cw + lane%16, tokens 32 kk + 8 g .. +7.
     v4s h[2];
 #pragma unroll
@@ -227,9 +244,15 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restr
     __builtin_memcpy(&a, h, 16);
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb) {
-      const int64_t o = static_cast<int64_t>(eb) * 16 * Tp + brow + kk * 32;
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(dlt_hi + o);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(dlt_lo + o);
+      bf16x8 bh, bl;
+      if constexpr (kPrefetch) {
+        bh = pre_h[eb][kk];
+        bl = pre_l[eb][kk];
+      } else {
+        const int64_t o = static_cast<int64_t>(eb) * 16 * Tp + brow + kk * 32;
+        bh = *reinterpret_cast<const bf16x8*>(dlt_hi + o);
+        bl = *reinterpret_cast<const bf16x8*>(dlt_lo + o);
+      }
       acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[eb], 0, 0, 0);
       acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[eb], 0, 0, 0);
     }
@@ -245,13 +268,22 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restr
   }
 }
 
-// dW_r[i][e] = sum over token chunks c (in order) of part[c][i][e].
+// dW_r[i][e] = sum over token chunks c (in order) of part[c][i][e]. The
+// loads of 8 chunks are issued before their in-order sum.
 __global__ void reduce_router_chunks_kernel(const float* __restrict__ part, int nchunks, int64_t n,
                                             bf16_t* __restrict__ out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float s = 0.0f;
-  for (int c = 0; c < nchunks; ++c) s += part[c * n + i];
+  int c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(c + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; c < nchunks; ++c) s += part[c * n + i];
   out[i] = f32_to_bf16(s);
 }
 
