@@ -120,6 +120,37 @@ def dispatch_plan(topk_idx, E: int):
             row_of_slot.reshape(T, k).astype(np.int32), token_of_row.astype(np.int32))
 
 
+# Expert-load diagnostics from the routed counts. [P2] "Detalles clave" and
+# [P3] "Risultati Documentati" report that a score meant to favour balanced
+# routing can improve while the real per-expert load grows less balanced;
+# these figures measure the real load itself. The pages define no statistic;
+# the reading here: p_e = n_e / S, entropy in nats with 0 ln 0 = 0.
+LOAD_STATS = ("max", "min", "mean", "max_over_mean", "entropy", "entropy_norm", "empty", "cv")
+
+
+def load_stats(counts) -> np.ndarray:
+    """fp64 [8] in LOAD_STATS order: max n_e, min n_e, mean S/E, max/mean
+    (0 when S = 0), entropy -sum p_e ln p_e (0 when S = 0), entropy / ln E
+    (1 when E = 1; 0 when S = 0), experts with no rows, and the coefficient of
+    variation std(n)/mean(n) with the population std (0 when S = 0)."""
+    n = _f64(counts)
+    E = n.size
+    S = n.sum()
+    mean = S / E
+    out = np.zeros(8, dtype=F64)
+    out[0], out[1], out[2] = n.max(), n.min(), mean
+    out[6] = float((n == 0).sum())
+    if S > 0:
+        p = n / S
+        nz = p > 0
+        ent = -(p[nz] * np.log(p[nz])).sum()
+        out[3] = n.max() / mean
+        out[4] = ent
+        out[5] = ent / np.log(E) if E > 1 else 1.0
+        out[7] = np.sqrt(((n - mean) ** 2).mean()) / mean
+    return out
+
+
 def gather_rows(x, token_of_row) -> np.ndarray:
     """Xp[r] = x[token_of_row[r]] (a pure copy; fp64 here)."""
     return _f64(x)[np.asarray(token_of_row, dtype=np.int64)]
