@@ -38,8 +38,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_work(wl):
-    """FLOPs and HBM bytes the method must move, per library call, per step."""
+def algorithmic_work(wl, recompute=False):
+    """FLOPs and HBM bytes the method must move, per library call, per step.
+    With activation recompute the backward also runs the gate/up GEMM again
+    (flops_recompute); TFLOP/s figures count only the method's 18*S*d*f."""
     T, d, E, k, f = wl.T, wl.d, wl.E, wl.k, wl.f
     S = T * k
     b = 4 if wl.dtype == "f32" else 2
@@ -52,6 +54,13 @@ def algorithmic_work(wl):
         "moe_combine_bwd": {"bytes": (1 + 2 * k) * T * d * b},
         "moe_dispatch_bwd": {"bytes": (1 + k) * T * d * b},
     }
+    if wl.dtype == "mxfp8":
+        # dispatch and combine backward also write the MXFP8 images of xp and
+        # d_o: one E4M3 byte per element plus one E8M0 byte per 32.
+        for n in ("moe_dispatch", "moe_combine_bwd"):
+            work[n]["bytes"] += S * d + S * d // 32
+    if recompute:
+        work["moe_grouped_ffn_bwd"]["flops_recompute"] = 4 * S * d * f
     if wl.routing == "learned":
         work["moe_route"] = {"flops": 2 * T * d * E}
         work["moe_route_bwd"] = {"flops": 2 * T * d * E}
@@ -109,6 +118,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--as-bf16", action="store_true",
                     help="run an MXFP8 workload's shape on the bf16 path (for the MXFP8/bf16 ratio)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation recompute: save no G, U, H; the backward recomputes them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (to scale HBM counters)")
     args = ap.parse_args()
@@ -152,7 +163,7 @@ def main():
     else:
         t["topk_idx"] = dev(inp["topk_idx"], torch.int32)
         t["topk_gate"] = dev(inp["topk_gate"], torch.float32)
-    layer = M.MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, wl.dtype, learned_routing=learned)
+    layer = M.MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, wl.dtype, learned_routing=learned, recompute=args.recompute)
     stream = torch.cuda.current_stream()
 
     def step(mark=None):
@@ -195,7 +206,7 @@ def main():
             per_call.setdefault(name, []).append(a.elapsed_time(b))
     avg_ms = {n: sum(v) / len(v) for n, v in per_call.items()}
 
-    work = algorithmic_work(wl)
+    work = algorithmic_work(wl, args.recompute)
     gemm_ms = avg_ms["moe_grouped_ffn_fwd"] + avg_ms["moe_grouped_ffn_bwd"]
     gemm_flops = work["moe_grouped_ffn_fwd"]["flops"] + work["moe_grouped_ffn_bwd"]["flops"]
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
@@ -229,7 +240,14 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
-        "config": dict(wl.describe(), parallelism="none (1 GPU)"),
+        "config": dict(wl.describe(), parallelism="none (1 GPU)",
+                       **({"recompute": True} if args.recompute else {})),
+        # bytes held between forward and backward beyond the inputs: the save
+        # buffer (G, U, H unless recomputed; MXFP8 weight copies), xp, o, and
+        # for MXFP8 the xp image.
+        "saved_bytes": {"save": layer.save.numel(), "xp": layer.xp.numel() * layer.xp.element_size(),
+                        "o": layer.o.numel() * layer.o.element_size(),
+                        "xp_mx": 0 if layer.xp_mx is None else layer.xp_mx.numel()},
         "grouped_gemm": {"tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / peak, 4),
                          "peak_tflops": peak, "ms": round(gemm_ms, 4)},
         "dispatch_combine": {"gbs": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),

@@ -11,7 +11,8 @@
  *             the device from the offsets array          [moe_grouped_ffn_fwd]
  *   combine   y[t] = sum_j gate[t,j] * o[row_of_slot[t,j]] [moe_combine]
  *   backward  moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd,
- *             moe_dispatch_bwd; MXFP8 operands via mxfp8_quantize.
+ *             moe_dispatch_bwd; MXFP8 operands via mxfp8_quantize, or
+ *             written by dispatch and combine backward as MXFP8 images.
  *
  * Sources. The pages that describe the method say, in words only:
  *  - each token activates 4 of the E experts — "Olmo-core 3 é lançado com
@@ -68,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 enum moe_status {
   MOE_OK = 0,
@@ -94,6 +95,20 @@ enum moe_op {
 /* Device-side status bits, read back with moe_read_device_status. */
 enum moe_device_status { MOE_DEV_OK = 0, MOE_DEV_BAD_EXPERT = 1 };
 
+/* Layer options, bits of moe_shape.flags. */
+enum moe_flags {
+  /* Activation recompute (fp32 and bf16 layers). moe_grouped_ffn_fwd keeps
+   * G, U, H in its workspace only and saves nothing (moe_save_size is 0);
+   * moe_grouped_ffn_bwd runs the gate/up grouped GEMM again from xp into its
+   * own workspace before the backward GEMMs. This trades one extra
+   * 4*S*d*f-flop GEMM per step for the 3*S*f activations that otherwise
+   * stay live between forward and backward. Results are bit-identical to
+   * the layer without the flag. unite.ai page, "Parallelismo, precisione e
+   * tecniche di memoria" (recomputing activations cuts activation memory at
+   * some cost in throughput). */
+  MOE_FLAG_RECOMPUTE = 1
+};
+
 typedef struct moe_shape {
   int64_t T;     /* tokens on this GPU (>= 1) */
   int64_t d;     /* model width (multiple of 64) */
@@ -101,7 +116,7 @@ typedef struct moe_shape {
   int64_t k;     /* experts per token (1..min(E, 8)) */
   int64_t f;     /* expert FFN width d_ff (multiple of 64) */
   int32_t dtype; /* enum moe_dtype */
-  int32_t reserved; /* must be 0 */
+  int32_t flags; /* enum moe_flags bits (0: none); other bits must be 0 */
 } moe_shape;
 
 int moe_abi_version(void);
@@ -117,8 +132,21 @@ size_t moe_workspace_size(int op, const moe_shape* shape);
  * needs: G, U, H (three [S][f] tensors in the layer dtype, bf16 for MXFP8
  * layers) and, for MXFP8 layers, the E4M3 copies (with their E8M0 scales) of
  * w_gate, w_up and w_down in the layouts of the backward's dgrad GEMMs, which
- * the forward writes from the same read that quantises its own copies. */
+ * the forward writes from the same read that quantises its own copies.
+ * 0 with MOE_FLAG_RECOMPUTE (then `save` may be NULL in the FFN calls). */
 size_t moe_save_size(const moe_shape* shape);
+
+/* Bytes of the MXFP8 image of a bf16 matrix [rows][cols] quantised along
+ * cols (cols % 64 == 0), in the layout the MXFP8 grouped GEMMs read their
+ * row operand in: rows*cols E4M3 codes, row-major; then the E8M0 scales as
+ * [cols/64][rows][2] (the two 32-blocks of each 64-column piece of a row side
+ * by side). Each part starts 256-byte aligned and is followed by at least 16
+ * bytes of slack. Codes and scales are those of mxfp8_quantize with axis 0.
+ * moe_dispatch and moe_combine_bwd write the images of xp and d_o ([S][d])
+ * for MXFP8 layers, and the grouped FFN calls read them, so neither row
+ * matrix is read again only to be quantised. Returns (size_t)-1 for
+ * rows < 1 or cols not a positive multiple of 64. */
+size_t moe_mx_image_size(int64_t rows, int64_t cols);
 
 /* Router: logits[T][E] (fp32) = x[T][d] · w_router[d][E] with fp32
  * accumulation; then per token the k largest logits in decreasing order,
@@ -141,14 +169,17 @@ int moe_route(const void* x, const void* w_router, const moe_shape* shape,
  * inverse; xp[S][d] (layer dtype) is x gathered into that order.
  * An expert id outside [0, E) is not routed (its row_of_slot is -1), and the
  * device status word in `ws` is set to MOE_DEV_BAD_EXPERT.
+ * xp_mx_out (MXFP8 layers only; NULL to skip): receives the MXFP8 image of
+ * xp (moe_mx_image_size(S, d) bytes, 256-byte aligned), written by the same
+ * pass that writes xp's rows. Must be NULL for fp32 and bf16 layers.
  * ws: at least moe_workspace_size(MOE_OP_DISPATCH) bytes, 256-byte aligned.
  * Passage: bytechap.com page, "Cómo funciona"; unite.ai page, "Parallelismo,
  * precisione e tecniche di memoria" (rows written straight into the experts'
  * input buffers; routing metadata stays on the GPU). */
 int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* shape,
                  int32_t* counts_out, int32_t* offsets_out, int32_t* row_of_slot_out,
-                 int32_t* token_of_row_out, void* xp_out, void* ws, size_t ws_bytes,
-                 void* stream);
+                 int32_t* token_of_row_out, void* xp_out, uint8_t* xp_mx_out, void* ws,
+                 size_t ws_bytes, void* stream);
 
 /* Reads the device status word that the last moe_dispatch on `ws` wrote.
  * Synchronises `stream`. For debugging and tests; returns MOE_DEV_* bits, or a
@@ -163,10 +194,12 @@ int moe_read_device_status(const void* ws, void* stream);
  * save (>= moe_save_size bytes) receives G, U, H (and, for MXFP8 layers, the
  * backward's quantised weight copies) for the backward.
  * ws: moe_workspace_size(MOE_OP_FFN_FWD) bytes (may be 0 -> NULL allowed).
+ * xp_mx (MXFP8 layers only; NULL = quantise xp here): the MXFP8 image of xp
+ * that moe_dispatch wrote; it must hold the current xp's codes.
  * Passage: bytechap.com page, "Cómo funciona" (grouped GEMM combining many
  * small expert computations); unite.ai page, "Parallelismo, precisione e
  * tecniche di memoria" (matmuls scheduled on the device). */
-int moe_grouped_ffn_fwd(const void* xp, const void* w_gate, const void* w_up,
+int moe_grouped_ffn_fwd(const void* xp, const uint8_t* xp_mx, const void* w_gate, const void* w_up,
                         const void* w_down, const int32_t* offsets, const moe_shape* shape,
                         void* save, size_t save_bytes, void* o_out, void* ws, size_t ws_bytes,
                         void* stream);
@@ -178,10 +211,12 @@ int moe_combine(const void* o, const float* topk_gate, const int32_t* row_of_slo
                 const moe_shape* shape, void* y_out, void* stream);
 
 /* Combine backward: d_o[row_of_slot[t,j]] = topk_gate[t,j] * dy[t] (layer
- * dtype) and dgate[t,j] (fp32) = <dy[t], o[row_of_slot[t,j]]>. */
+ * dtype) and dgate[t,j] (fp32) = <dy[t], o[row_of_slot[t,j]]>.
+ * d_o_mx_out (MXFP8 layers only; NULL to skip): receives the MXFP8 image of
+ * the stored (bf16) d_o, moe_mx_image_size(S, d) bytes, 256-byte aligned. */
 int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
                     const int32_t* row_of_slot, const moe_shape* shape, void* d_o_out,
-                    float* dgate_out, void* stream);
+                    uint8_t* d_o_mx_out, float* dgate_out, void* stream);
 
 /* Grouped FFN backward, per expert e on its rows:
  *   dH = d_o · w_down[e]^T;  dU = dH * silu(G);
@@ -189,9 +224,12 @@ int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
  *   dxp = dG · w_gate[e]^T + dU · w_up[e]^T
  *   dw_down[e] = H^T · d_o;  dw_gate[e] = xp^T · dG;  dw_up[e] = xp^T · dU
  * Weight gradients of experts with no rows are written as zeros. All outputs
- * in the layer dtype. ws: moe_workspace_size(MOE_OP_FFN_BWD) bytes. */
-int moe_grouped_ffn_bwd(const void* d_o, const void* xp, const void* w_gate, const void* w_up,
-                        const void* w_down, const int32_t* offsets, const moe_shape* shape,
+ * in the layer dtype. ws: moe_workspace_size(MOE_OP_FFN_BWD) bytes.
+ * d_o_mx (MXFP8 layers only; NULL = quantise d_o here): the MXFP8 image of
+ * d_o that moe_combine_bwd wrote. */
+int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, const void* w_gate,
+                        const void* w_up, const void* w_down, const int32_t* offsets,
+                        const moe_shape* shape,
                         const void* save, void* dxp_out, void* dw_gate_out, void* dw_up_out,
                         void* dw_down_out, void* ws, size_t ws_bytes, void* stream);
 
@@ -214,6 +252,21 @@ int moe_route_bwd(const void* x, const void* w_router, const int32_t* topk_idx,
 int moe_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* dlogits,
                      const void* w_router, const moe_shape* shape, void* dx_out, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* Expert-load diagnostics of one step, computed on the device from the
+ * counts[E] that moe_dispatch wrote (device int32; never read by the host).
+ * stats_out (device, 8 doubles): [0] max n_e, [1] min n_e, [2] mean S/E,
+ * [3] max/mean, [4] entropy -sum_e p_e ln p_e with p_e = n_e / S (nats,
+ * 0 ln 0 = 0), [5] entropy / ln E (1 when E = 1), [6] experts with no rows,
+ * [7] std/mean of the counts (population std). With S = 0, entries 3, 4, 5
+ * and 7 are 0. Deterministic (fixed reduction order). Errors:
+ * MOE_ERR_INVALID_ARG for a NULL pointer or E outside 1..256,
+ * MOE_ERR_MISALIGNED for a pointer not 16-byte aligned.
+ * Passage: bytechap.com page, "Detalles clave"; unite.ai page, "Risultati
+ * Documentati" (a routing score meant to favour balance can improve while
+ * the real per-expert load becomes less balanced: these figures measure the
+ * real load). */
+int moe_load_stats(const int32_t* counts, int64_t E, double* stats_out, void* stream);
 
 /* MXFP8 quantisation of a bf16 matrix in_bf16[rows][cols]:
  * axis 0: blocks of 32 consecutive elements along a row (cols % 32 == 0);

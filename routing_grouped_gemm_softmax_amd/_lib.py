@@ -19,6 +19,7 @@ MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
  MOE_OP_ROUTE_BWD, MOE_OP_DISPATCH_BWD) = range(6)
 MOE_DEV_BAD_EXPERT = 1
+MOE_FLAG_RECOMPUTE = 1
 
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.bfloat16}
@@ -27,12 +28,12 @@ TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torc
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
                 ("k", ctypes.c_int64), ("f", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, T, d, E, k, f, dtype) -> "MoeShape":
+    def make(cls, T, d, E, k, f, dtype, flags: int = 0) -> "MoeShape":
         code = DTYPE_CODE[dtype] if isinstance(dtype, str) else int(dtype)
-        return cls(int(T), int(d), int(E), int(k), int(f), code, 0)
+        return cls(int(T), int(d), int(E), int(k), int(f), code, int(flags))
 
 
 class MoeError(RuntimeError):
@@ -52,15 +53,17 @@ SIGNATURES = {
     "moe_last_error_message": (ctypes.c_char_p, []),
     "moe_workspace_size": (_SZ, [ctypes.c_int, _SHAPE]),
     "moe_save_size": (_SZ, [_SHAPE]),
+    "moe_mx_image_size": (_SZ, [ctypes.c_int64, ctypes.c_int64]),
     "moe_route": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _SZ, _P]),
-    "moe_dispatch": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_dispatch": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_read_device_status": (ctypes.c_int, [_P, _P]),
-    "moe_grouped_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _SHAPE, _P, _SZ, _P, _P, _SZ, _P]),
+    "moe_grouped_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SHAPE, _P, _SZ, _P, _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _SHAPE, _P, _P]),
-    "moe_combine_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _P]),
-    "moe_grouped_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_combine_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _P, _P]),
+    "moe_grouped_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_route_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _SZ, _P]),
     "moe_dispatch_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _SZ, _P]),
+    "moe_load_stats": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
     "mxfp8_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P]),
 }
 
@@ -135,6 +138,14 @@ def save_size(shape: MoeShape) -> int:
     return n
 
 
+def mx_image_size(rows: int, cols: int) -> int:
+    """Bytes of the MXFP8 image of a bf16 [rows][cols] matrix (moe_mx_image_size)."""
+    n = load().moe_mx_image_size(int(rows), int(cols))
+    if n == ctypes.c_size_t(-1).value:
+        raise MoeError("moe_mx_image_size", MOE_ERR_INVALID_ARG, last_error())
+    return n
+
+
 def moe_route(x, w_router, shape, logits, topk_idx, topk_gate, ws=None, stream=None):
     T, E, k = shape.T, shape.E, shape.k
     _expect(logits, torch.float32, T * E, "logits")
@@ -144,13 +155,13 @@ def moe_route(x, w_router, shape, logits, topk_idx, topk_gate, ws=None, stream=N
                                          _ptr(topk_idx), _ptr(topk_gate), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_dispatch(x, topk_idx, shape, counts, offsets, row_of_slot, token_of_row, xp, ws, stream=None):
+def moe_dispatch(x, topk_idx, shape, counts, offsets, row_of_slot, token_of_row, xp, ws, stream=None, xp_mx=None):
     _expect(topk_idx, torch.int32, shape.T * shape.k, "topk_idx")
     _expect(counts, torch.int32, shape.E, "counts")
     _expect(offsets, torch.int32, shape.E + 1, "offsets")
     _check("moe_dispatch", load().moe_dispatch(
         _ptr(x), _ptr(topk_idx), ctypes.byref(shape), _ptr(counts), _ptr(offsets), _ptr(row_of_slot),
-        _ptr(token_of_row), _ptr(xp), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(token_of_row), _ptr(xp), _ptr(xp_mx), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_read_device_status(ws, stream=None) -> int:
@@ -160,9 +171,9 @@ def moe_read_device_status(ws, stream=None) -> int:
     return rc
 
 
-def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, shape, save, o, ws=None, stream=None):
+def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, shape, save, o, ws=None, stream=None, xp_mx=None):
     _check("moe_grouped_ffn_fwd", load().moe_grouped_ffn_fwd(
-        _ptr(xp), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(offsets), ctypes.byref(shape), _ptr(save),
+        _ptr(xp), _ptr(xp_mx), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(offsets), ctypes.byref(shape), _ptr(save),
         save.numel() * save.element_size(), _ptr(o), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
 
@@ -172,16 +183,17 @@ def moe_combine(o, topk_gate, row_of_slot, shape, y, stream=None):
                                              _ptr(y), _stream(stream)))
 
 
-def moe_combine_bwd(dy, o, topk_gate, row_of_slot, shape, d_o, dgate, stream=None):
+def moe_combine_bwd(dy, o, topk_gate, row_of_slot, shape, d_o, dgate, stream=None, d_o_mx=None):
     _expect(dgate, torch.float32, shape.T * shape.k, "dgate")
     _check("moe_combine_bwd", load().moe_combine_bwd(_ptr(dy), _ptr(o), _ptr(topk_gate), _ptr(row_of_slot),
-                                                     ctypes.byref(shape), _ptr(d_o), _ptr(dgate), _stream(stream)))
+                                                     ctypes.byref(shape), _ptr(d_o), _ptr(d_o_mx), _ptr(dgate),
+                                                     _stream(stream)))
 
 
 def moe_grouped_ffn_bwd(d_o, xp, w_gate, w_up, w_down, offsets, shape, save, dxp, dw_gate, dw_up, dw_down, ws,
-                        stream=None):
+                        stream=None, d_o_mx=None):
     _check("moe_grouped_ffn_bwd", load().moe_grouped_ffn_bwd(
-        _ptr(d_o), _ptr(xp), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(offsets), ctypes.byref(shape),
+        _ptr(d_o), _ptr(d_o_mx), _ptr(xp), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(offsets), ctypes.byref(shape),
         _ptr(save), _ptr(dxp), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -207,3 +219,15 @@ def mxfp8_quantize(x, axis, q, scale, stream=None):
     _expect(scale, torch.uint8, rows * cols // 32, "scale")
     _check("mxfp8_quantize", load().mxfp8_quantize(_ptr(x), rows, cols, int(axis), _ptr(q), _ptr(scale),
                                                    _stream(stream)))
+
+
+LOAD_STATS = ("max", "min", "mean", "max_over_mean", "entropy", "entropy_norm", "empty", "cv")
+
+
+def moe_load_stats(counts, out, stream=None):
+    """Expert-load diagnostics from the device counts into out (8 float64 on
+    the device, in LOAD_STATS order)."""
+    _expect(out, torch.float64, 8, "out")
+    if counts.dtype != torch.int32:
+        raise TypeError("counts must be int32")
+    _check("moe_load_stats", load().moe_load_stats(_ptr(counts), counts.numel(), _ptr(out), _stream(stream)))

@@ -34,7 +34,9 @@ int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 // Shape checks shared by every layer entry point.
 int check_shape(const moe_shape* s) {
   if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
-  if (s->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "shape.reserved must be 0");
+  if (s->flags & ~MOE_FLAG_RECOMPUTE) return fail(MOE_ERR_INVALID_ARG, "unknown bits in shape.flags (%d)", s->flags);
+  if (s->dtype == MOE_MXFP8 && (s->flags & MOE_FLAG_RECOMPUTE))
+    return fail(MOE_ERR_UNSUPPORTED, "activation recompute is available for fp32 and bf16 layers");
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8)
     return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
   if (s->T < 1 || s->d < 1 || s->E < 1 || s->k < 1 || s->f < 1)
@@ -71,16 +73,32 @@ int check_ffn_dtype(const moe_shape* s, const char* who) {
     if (!aligned16(ptr)) return fail(MOE_ERR_MISALIGNED, "%s: %s is not 16-byte aligned", __func__, #ptr); \
   } while (0)
 
+// An optional MXFP8 image argument: MXFP8 layers only, 256-byte aligned.
+#define MX_IMAGE_OK(ptr, s)                                                                      \
+  do {                                                                                           \
+    if ((ptr) != nullptr) {                                                                      \
+      if ((s)->dtype != MOE_MXFP8)                                                               \
+        return fail(MOE_ERR_INVALID_ARG, "%s: %s is only for MXFP8 layers", __func__, #ptr);     \
+      if ((reinterpret_cast<uintptr_t>(ptr) & 255u) != 0)                                        \
+        return fail(MOE_ERR_MISALIGNED, "%s: %s is not 256-byte aligned", __func__, #ptr);       \
+    }                                                                                            \
+  } while (0)
+
 #define LAUNCH(call)                                          \
   do {                                                        \
     hipError_t _e = (call);                                   \
     if (_e != hipSuccess) return hip_fail(_e, __func__);      \
   } while (0)
 
-// G, U, H planes; MXFP8 layers add the backward's quantised weight copies.
-size_t save_planes(const moe_shape* s) {
+bool recompute(const moe_shape* s) { return (s->flags & MOE_FLAG_RECOMPUTE) != 0; }
+
+// G, U, H: three [S][f] planes in the layer dtype.
+size_t gu_h_bytes(const moe_shape* s) {
   return ((size_t)3 * s->T * s->k * s->f * elem_bytes(s->dtype) + 255) & ~(size_t)255;
 }
+// Saved G, U, H planes (none with recompute); MXFP8 layers add the backward's
+// quantised weight copies.
+size_t save_planes(const moe_shape* s) { return recompute(s) ? 0 : gu_h_bytes(s); }
 size_t save_bytes_for(const moe_shape* s) {
   return save_planes(s) + (s->dtype == MOE_MXFP8 ? moe::ffn_mx_save_extra((int)s->d, (int)s->f, (int)s->E) : 0);
 }
@@ -112,16 +130,26 @@ size_t moe_workspace_size(int op, const moe_shape* s) {
     case MOE_OP_ROUTE: return s->dtype == MOE_F32 ? 0 : moe::route_bf16_workspace(d, E);
     case MOE_OP_DISPATCH: return moe::dispatch_workspace(T, E);
     case MOE_OP_FFN_FWD:
-      return s->dtype == MOE_MXFP8 ? moe::ffn_mx_fwd_workspace(T * k, d, f, E) : 0;
+      if (s->dtype == MOE_MXFP8) return moe::ffn_mx_fwd_workspace(T * k, d, f, E);
+      return recompute(s) ? gu_h_bytes(s) : 0;  // recompute: G, U, H live here
     case MOE_OP_FFN_BWD: {
       const size_t dgu = ((size_t)T * k * 2 * f * elem_bytes(s->dtype) + 255) & ~(size_t)255;  // dG|dU rows
-      return dgu + (s->dtype == MOE_MXFP8 ? moe::ffn_mx_bwd_workspace(T * k, d, f, E) : 0);
+      if (s->dtype == MOE_MXFP8) return dgu + moe::ffn_mx_bwd_workspace(T * k, d, f, E);
+      return dgu + (recompute(s) ? gu_h_bytes(s) : 0);  // recompute: G, U, H after dG|dU
     }
     case MOE_OP_ROUTE_BWD:
       return s->dtype == MOE_F32 ? moe::route_bwd_workspace(T, d, E) : moe::route_bwd_bf16_workspace(T, d, E);
     case MOE_OP_DISPATCH_BWD: return moe::dispatch_bwd_workspace(d, E, s->dtype == MOE_F32);
     default: fail(MOE_ERR_INVALID_ARG, "unknown op %d", op); return (size_t)-1;
   }
+}
+
+size_t moe_mx_image_size(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 64 || cols % 64 || rows * cols > ((int64_t)1 << 40)) {
+    fail(MOE_ERR_INVALID_ARG, "moe_mx_image_size: need rows >= 1 and cols a positive multiple of 64");
+    return (size_t)-1;
+  }
+  return moe::mx_image_bytes(rows, cols);
 }
 
 size_t moe_save_size(const moe_shape* s) {
@@ -148,17 +176,23 @@ int moe_route(const void* x, const void* w_router, const moe_shape* s, float* lo
 }
 
 int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* s, int32_t* counts_out,
-                 int32_t* offsets_out, int32_t* row_of_slot_out, int32_t* token_of_row_out, void* xp_out, void* ws,
-                 size_t ws_bytes, void* stream) {
+                 int32_t* offsets_out, int32_t* row_of_slot_out, int32_t* token_of_row_out, void* xp_out,
+                 uint8_t* xp_mx_out, void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_shape(s));
   NEED(x); NEED(topk_idx); NEED(counts_out); NEED(offsets_out); NEED(row_of_slot_out); NEED(token_of_row_out);
   NEED(xp_out); NEED(ws);
+  MX_IMAGE_OK(xp_mx_out, s);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MOE_ERR_MISALIGNED, "moe_dispatch: ws must be 256-byte aligned");
   const size_t need = moe::dispatch_workspace((int)s->T, (int)s->E);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_dispatch: workspace %zu < %zu bytes", ws_bytes, need);
-  LAUNCH(moe::launch_dispatch(x, topk_idx, elem_bytes(s->dtype), (int)s->T, (int)s->d, (int)s->E, (int)s->k,
-                              counts_out, offsets_out, row_of_slot_out, token_of_row_out, xp_out, ws,
-                              as_stream(stream)));
+  if (xp_mx_out)
+    LAUNCH(moe::launch_dispatch_mx(x, topk_idx, (int)s->T, (int)s->d, (int)s->E, (int)s->k, counts_out, offsets_out,
+                                   row_of_slot_out, token_of_row_out, xp_out,
+                                   moe::mx_image(xp_mx_out, s->T * s->k, s->d), ws, as_stream(stream)));
+  else
+    LAUNCH(moe::launch_dispatch(x, topk_idx, elem_bytes(s->dtype), (int)s->T, (int)s->d, (int)s->E, (int)s->k,
+                                counts_out, offsets_out, row_of_slot_out, token_of_row_out, xp_out, ws,
+                                as_stream(stream)));
   return MOE_OK;
 }
 
@@ -171,12 +205,14 @@ int moe_read_device_status(const void* ws, void* stream) {
   return v;
 }
 
-int moe_grouped_ffn_fwd(const void* xp, const void* w_gate, const void* w_up, const void* w_down,
-                        const int32_t* offsets, const moe_shape* s, void* save, size_t save_bytes, void* o_out,
-                        void* ws, size_t ws_bytes, void* stream) {
+int moe_grouped_ffn_fwd(const void* xp, const uint8_t* xp_mx, const void* w_gate, const void* w_up,
+                        const void* w_down, const int32_t* offsets, const moe_shape* s, void* save, size_t save_bytes,
+                        void* o_out, void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_shape(s));
   CHECK(check_ffn_dtype(s, "moe_grouped_ffn_fwd"));
-  NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(save); NEED(o_out);
+  NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(o_out);
+  if (save_bytes_for(s) > 0) NEED(save);
+  MX_IMAGE_OK(xp_mx, s);
   const size_t need = moe_workspace_size(MOE_OP_FFN_FWD, s);
   if (need) {
     NEED(ws);
@@ -186,9 +222,10 @@ int moe_grouped_ffn_fwd(const void* xp, const void* w_gate, const void* w_up, co
     return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_fwd: save buffer %zu < %zu bytes", save_bytes, save_bytes_for(s));
   moe::FfnArgs a{};
   a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
-  a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
+  a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down; a.xp_mx = xp_mx;
   const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
-  a.G = save; a.U = static_cast<char*>(save) + plane; a.H = static_cast<char*>(save) + 2 * plane;
+  char* gu_h = static_cast<char*>(recompute(s) ? ws : save);  // G, U, H
+  a.G = gu_h; a.U = gu_h + plane; a.H = gu_h + 2 * plane;
   a.mx_save = static_cast<char*>(save) + save_planes(s);
   a.o = o_out;
   if (s->dtype == MOE_MXFP8)
@@ -208,32 +245,44 @@ int moe_combine(const void* o, const float* topk_gate, const int32_t* row_of_slo
 }
 
 int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate, const int32_t* row_of_slot,
-                    const moe_shape* s, void* d_o_out, float* dgate_out, void* stream) {
+                    const moe_shape* s, void* d_o_out, uint8_t* d_o_mx_out, float* dgate_out, void* stream) {
   CHECK(check_shape(s));
   NEED(dy); NEED(o); NEED(topk_gate); NEED(row_of_slot); NEED(d_o_out); NEED(dgate_out);
+  MX_IMAGE_OK(d_o_mx_out, s);
+  if (d_o_mx_out) {
+    LAUNCH(moe::launch_combine_bwd_mx(dy, o, topk_gate, row_of_slot, (int)s->T, (int)s->d, (int)s->k, d_o_out,
+                                      moe::mx_image(d_o_mx_out, s->T * s->k, s->d), dgate_out, as_stream(stream)));
+    return MOE_OK;
+  }
   LAUNCH(moe::launch_combine_bwd(dy, o, topk_gate, row_of_slot, s->dtype == MOE_F32, (int)s->T, (int)s->d, (int)s->k,
                                  d_o_out, dgate_out, as_stream(stream)));
   return MOE_OK;
 }
 
-int moe_grouped_ffn_bwd(const void* d_o, const void* xp, const void* w_gate, const void* w_up, const void* w_down,
-                        const int32_t* offsets, const moe_shape* s, const void* save, void* dxp_out,
-                        void* dw_gate_out, void* dw_up_out, void* dw_down_out, void* ws, size_t ws_bytes,
-                        void* stream) {
+int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, const void* w_gate,
+                        const void* w_up, const void* w_down, const int32_t* offsets, const moe_shape* s,
+                        const void* save, void* dxp_out, void* dw_gate_out, void* dw_up_out, void* dw_down_out,
+                        void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_shape(s));
   CHECK(check_ffn_dtype(s, "moe_grouped_ffn_bwd"));
-  NEED(d_o); NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(save); NEED(dxp_out);
+  NEED(d_o); NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(dxp_out);
   NEED(dw_gate_out); NEED(dw_up_out); NEED(dw_down_out); NEED(ws);
+  if (save_bytes_for(s) > 0) NEED(save);
+  MX_IMAGE_OK(d_o_mx, s);
   const size_t need = moe_workspace_size(MOE_OP_FFN_BWD, s);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_bwd: workspace %zu < %zu bytes", ws_bytes, need);
   moe::FfnArgs a{};
   a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
   a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
   const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
+  const size_t dgu_bytes = ((size_t)a.S * 2 * a.f * elem_bytes(s->dtype) + 255) & ~(size_t)255;
   char* sv = const_cast<char*>(static_cast<const char*>(save));
-  a.G = sv; a.U = sv + plane; a.H = sv + 2 * plane;
+  // Recompute: G, U, H are rebuilt in the workspace, after the dG|dU rows.
+  char* gu_h = recompute(s) ? static_cast<char*>(ws) + dgu_bytes : sv;
+  a.G = gu_h; a.U = gu_h + plane; a.H = gu_h + 2 * plane;
+  a.recompute = recompute(s);
   a.mx_save = sv + save_planes(s);
-  a.d_o = d_o; a.dgu = ws; a.dxp = dxp_out; a.dw_gate = dw_gate_out; a.dw_up = dw_up_out; a.dw_down = dw_down_out;
+  a.d_o = d_o; a.d_o_mx = d_o_mx; a.dgu = ws; a.dxp = dxp_out; a.dw_gate = dw_gate_out; a.dw_up = dw_up_out; a.dw_down = dw_down_out;
   if (s->dtype == MOE_MXFP8) {
     const size_t dgu = ((size_t)a.S * 2 * a.f * 2 + 255) & ~(size_t)255;
     LAUNCH(moe::launch_ffn_mx_bwd(a, static_cast<char*>(ws) + dgu, as_stream(stream)));
@@ -274,6 +323,13 @@ int moe_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* d
   }
   LAUNCH(moe::launch_dispatch_bwd(dxp, row_of_slot, dlogits, w_router, s->dtype == MOE_F32, (int)s->T, (int)s->d,
                                   (int)s->E, (int)s->k, dx_out, ws, as_stream(stream)));
+  return MOE_OK;
+}
+
+int moe_load_stats(const int32_t* counts, int64_t E, double* stats_out, void* stream) {
+  NEED(counts); NEED(stats_out);
+  if (E < 1 || E > 256) return fail(MOE_ERR_INVALID_ARG, "moe_load_stats: E must be in 1..256 (got %lld)", (long long)E);
+  LAUNCH(moe::launch_load_stats(counts, (int)E, stats_out, as_stream(stream)));
   return MOE_OK;
 }
 

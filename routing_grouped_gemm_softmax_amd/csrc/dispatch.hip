@@ -24,6 +24,9 @@
 // tokens: more workgroups), else 512.
 #include "common.h"
 #include "kernels.h"
+#include "mx_encode.h"
+
+#include <climits>
 
 namespace moe {
 
@@ -166,9 +169,37 @@ static int lanes_per_token(int nvec) {
   return l;
 }
 
+// Writes the MXFP8 image of one 16-byte piece (8 bf16 values, vector v of a
+// row of d = 8 * nvec values) to `rows`: E4M3 codes in q [S][d], E8M0 scales
+// in sc [d/64][S][2]. The 4 lanes holding a 32-block (lanes aligned to 4)
+// share its scale by two butterflies; the first lane of each 64-column piece
+// (8 lanes) writes both of its scale bytes. Every lane of the 8-lane group
+// must execute it.
+template <int NR>
+__device__ __forceinline__ void mx_store_piece(const uint4& val, int v, int d, const int (&rows)[NR], int nr,
+                                               uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
+  float f[8];
+  unpack16(val, f);
+  const int code = mx_group4_code(f);
+  const uint2 codes = mx_encode8(f, code);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int code_hi = __shfl(code, (lane & ~7) + 4, kWave);
+  const uint16_t sv = static_cast<uint16_t>(code | (code_hi << 8));
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    if (j >= nr || rows[j] < 0) continue;
+    *reinterpret_cast<uint2*>(q + static_cast<int64_t>(rows[j]) * d + v * 8) = codes;
+    if ((v & 7) == 0)
+      *reinterpret_cast<uint16_t*>(sc + (static_cast<int64_t>(v >> 3) * S + rows[j]) * 2) = sv;
+  }
+}
+
 // xp[row_of_slot[t][j]] = x[t]: read the token row once, write it k times.
+// MX: bf16 rows, and the same pass writes xp's MXFP8 image (q, sc; S rows).
+template <bool MX>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ x, const int32_t* __restrict__ row_of_slot,
-                                                          int T, int k, int nvec, int lpt, char* __restrict__ xp) {
+                                                          int T, int k, int nvec, int lpt, char* __restrict__ xp,
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
   const int tpw = 256 / lpt;
   const int t = blockIdx.x * tpw + threadIdx.x / lpt;
   const int sub = threadIdx.x % lpt;
@@ -182,12 +213,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (rows[j] >= 0) st16(xp + rows[j] * rb + v * 16, val);
+    if constexpr (MX) mx_store_piece<8>(val, v, nvec * 8, rows, k, q, sc, S);
   }
 }
 
-hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E, int k,
-                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
-                           void* xp, void* ws, hipStream_t s) {
+static hipError_t dispatch_impl(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E, int k,
+                                int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
+                                void* xp, const MxImage* mx, void* ws, hipStream_t s) {
   const int ct = chunk_tokens(T, E);
   const int nch = (T + ct - 1) / ct;
   DispatchWs w = carve(ws, nch, E);
@@ -202,9 +234,27 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_byte
   const int nvec = d * elem_bytes / 16;
   const int lpt = lanes_per_token(nvec);
   const int tpw = 256 / lpt;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((T + tpw - 1) / tpw), dim3(256), 0, s,
-                     static_cast<const char*>(x), row_of_slot, T, k, nvec, lpt, static_cast<char*>(xp));
+  const dim3 grid((T + tpw - 1) / tpw);
+  if (mx != nullptr)
+    hipLaunchKernelGGL(gather_rows_kernel<true>, grid, dim3(256), 0, s, static_cast<const char*>(x), row_of_slot, T, k,
+                       nvec, lpt, static_cast<char*>(xp), mx->q, mx->s, T * k);
+  else
+    hipLaunchKernelGGL(gather_rows_kernel<false>, grid, dim3(256), 0, s, static_cast<const char*>(x), row_of_slot, T,
+                       k, nvec, lpt, static_cast<char*>(xp), nullptr, nullptr, T * k);
   return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E, int k,
+                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
+                           void* xp, void* ws, hipStream_t s) {
+  return dispatch_impl(x, topk_idx, elem_bytes, T, d, E, k, counts, offsets, row_of_slot, token_of_row, xp, nullptr,
+                       ws, s);
+}
+
+hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int32_t* counts,
+                              int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row, void* xp,
+                              MxImage xp_mx, void* ws, hipStream_t s) {
+  return dispatch_impl(x, topk_idx, 2, T, d, E, k, counts, offsets, row_of_slot, token_of_row, xp, &xp_mx, ws, s);
 }
 
 // y[t] = sum_j gate[t][j] * o[row_of_slot[t][j]]  (fp32, slot order, one rounding).
@@ -243,12 +293,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
 
 // d_o[row(t,j)] = gate[t][j] * dy[t];  dgate[t][j] = <dy[t], o[row(t,j)]> (fp32,
 // fixed reduction tree: per-thread partials, lane butterfly, then waves in order).
-template <typename T>
+// MX (bf16 only): the same pass writes d_o's MXFP8 image (q, sc; S rows),
+// quantised from the stored bf16 values.
+template <typename T, bool MX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ o,
                                                           const float* __restrict__ gate,
                                                           const int32_t* __restrict__ row_of_slot, int Tn, int k,
                                                           int nvec, int lpt, T* __restrict__ d_o,
-                                                          float* __restrict__ dgate) {
+                                                          float* __restrict__ dgate, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ sc, int S) {
   constexpr int VE = Vec16<T>::N;
   __shared__ float red[4][8];
   const int tpw = 256 / lpt;
@@ -278,7 +331,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
           part[j] = fmaf(dv[i], ov[i], part[j]);
           sv[i] = g[j] * dv[i];
         }
-        st16(d_o + rows[j] * re + v * VE, pack16(sv));
+        const uint4 pk = pack16(sv);
+        st16(d_o + rows[j] * re + v * VE, pk);
+        if constexpr (MX) {
+          const int one[1] = {rows[j]};
+          mx_store_piece<1>(pk, v, nvec * VE, one, 1, q, sc, S);
+        }
       }
     }
   }
@@ -331,13 +389,24 @@ hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate, 
   const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
   if (is_f32)
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(dy),
+    hipLaunchKernelGGL((combine_bwd_kernel<float, false>), grid, dim3(256), 0, s, static_cast<const float*>(dy),
                        static_cast<const float*>(o), gate, row_of_slot, T, k, nvec, lpt, static_cast<float*>(d_o),
-                       dgate);
+                       dgate, nullptr, nullptr, T * k);
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(dy),
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, false>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(dy),
                        static_cast<const bf16_t*>(o), gate, row_of_slot, T, k, nvec, lpt,
-                       static_cast<bf16_t*>(d_o), dgate);
+                       static_cast<bf16_t*>(d_o), dgate, nullptr, nullptr, T * k);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gate, const int32_t* row_of_slot, int T,
+                                 int d, int k, void* d_o, MxImage d_o_mx, float* dgate, hipStream_t s) {
+  const int nvec = d * 2 / 16;
+  const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
+  const dim3 grid((T + tpw - 1) / tpw);
+  hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, true>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(dy),
+                     static_cast<const bf16_t*>(o), gate, row_of_slot, T, k, nvec, lpt, static_cast<bf16_t*>(d_o),
+                     dgate, d_o_mx.q, d_o_mx.s, T * k);
   return hipGetLastError();
 }
 
@@ -450,6 +519,77 @@ hipError_t launch_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, cons
     hipLaunchKernelGGL(dispatch_bwd_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(dxp),
                        row_of_slot, dl, static_cast<const bf16_t*>(ws), T, E, k, nvec, lpt,
                        static_cast<bf16_t*>(dx));
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// Expert-load diagnostics from the routed counts (the real load, which a
+// routing score meant to favour balance need not track: "Olmo-core 3 escala
+// el entrenamiento...", section "Detalles clave"; "Ai2 rilascia Olmo-Core
+// 3...", section "Risultati Documentati"). One workgroup, one thread per
+// expert. Integer figures are exact; the two fp64 sums (entropy terms
+// -p ln p with p = n/S, squared deviations from the mean) use a fixed LDS
+// tree, so reruns are bit-identical. out: max, min, mean, max/mean, entropy
+// (nats), entropy / ln E, empty experts, std/mean; the S = 0 and E = 1 cases
+// as documented in moe.h.
+__global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restrict__ counts, int E,
+                                                         double* __restrict__ out) {
+  __shared__ long long s_sum[256];
+  __shared__ int s_max[256], s_min[256], s_empty[256];
+  __shared__ double s_ent[256], s_var[256];
+  const int t = threadIdx.x;
+  const int n = t < E ? counts[t] : 0;
+  s_sum[t] = n;
+  s_max[t] = t < E ? n : INT_MIN;
+  s_min[t] = t < E ? n : INT_MAX;
+  s_empty[t] = (t < E && n == 0) ? 1 : 0;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (t < h) {
+      s_sum[t] += s_sum[t + h];
+      s_max[t] = max(s_max[t], s_max[t + h]);
+      s_min[t] = min(s_min[t], s_min[t + h]);
+      s_empty[t] += s_empty[t + h];
+    }
+    __syncthreads();
+  }
+  const long long S = s_sum[0];
+  const double mean = static_cast<double>(S) / E;
+  double ent = 0.0, var = 0.0;
+  if (t < E && S > 0) {
+    const double p = static_cast<double>(n) / static_cast<double>(S);
+    ent = n > 0 ? -p * log(p) : 0.0;
+    const double dv = static_cast<double>(n) - mean;
+    var = dv * dv;
+  }
+  s_ent[t] = ent;
+  s_var[t] = var;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (t < h) {
+      s_ent[t] += s_ent[t + h];
+      s_var[t] += s_var[t + h];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    const bool any = S > 0;
+    out[0] = s_max[0];
+    out[1] = s_min[0];
+    out[2] = mean;
+    out[3] = any ? s_max[0] / mean : 0.0;
+    out[4] = any ? s_ent[0] : 0.0;
+    out[5] = any ? (E > 1 ? s_ent[0] / log(static_cast<double>(E)) : 1.0) : 0.0;
+    out[6] = s_empty[0];
+    out[7] = any ? sqrt(s_var[0] / E) / mean : 0.0;
+  }
+}
+
+hipError_t launch_load_stats(const int32_t* counts, int E, double* out, hipStream_t s) {
+  hipLaunchKernelGGL(load_stats_kernel, dim3(1), dim3(256), 0, s, counts, E, out);
   return hipGetLastError();
 }
 

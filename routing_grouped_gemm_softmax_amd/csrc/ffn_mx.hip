@@ -13,6 +13,8 @@
 //             dXp = q(dGU) q([W_gate|W_up])^T   K = 2f
 //   wgrad     dW_down = q(H)^T q(dO), [dW_gate|dW_up] = q(Xp)^T q(dGU), K =
 //             an expert's tokens, each expert's range padded to 64 rows.
+// q(Xp) and q(dO) along d can arrive ready-made from the dispatch and
+// combine-backward passes, which write them beside their bf16 rows.
 #include "common.h"
 #include "grouped_gemm.h"
 #include "kernels.h"
@@ -129,7 +131,14 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
   // Operands: Xp along d; W_gate, W_up along d, transposed to [f][d]. The same
   // read of each weight also writes its copy blocked along f ([d][f], in the
   // save buffer) for the backward's dXp GEMM.
-  TRY(launch_mx_kmajor(a.xp, S, d, 1, 0, w.xq, 0, w.xs, 0, s));
+  uint8_t *xq = w.xq, *xs = w.xs;
+  if (a.xp_mx != nullptr) {  // written by the dispatch pass
+    const MxImage im = mx_image(a.xp_mx, S, d);
+    xq = im.q;
+    xs = im.s;
+  } else {
+    TRY(launch_mx_kmajor(a.xp, S, d, 1, 0, xq, 0, xs, 0, s));
+  }
   TRY(launch_mx_tgroup(a.w_gate, d, f, nullptr, E, wsz, w.wgq, d, wsz, w.wgs, wsz / 32, s, sv.wgq,
                        sv.wgs));
   TRY(launch_mx_tgroup(a.w_up, d, f, nullptr, E, wsz, w.wuq, d, wsz, w.wus, wsz / 32, s, sv.wuq,
@@ -137,7 +146,7 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
   {
     GemmParams p{};
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
-    p.a = w.xq; p.lda = d; p.as = w.xs; p.as_slab = 2LL * S;
+    p.a = xq; p.lda = d; p.as = xs; p.as_slab = 2LL * S;
     p.b0 = w.wgq; p.b1 = w.wuq; p.ldb = d; p.bstride = wsz;
     p.bs0 = w.wgs; p.bs1 = w.wus; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
     p.c0 = a.G; p.c1 = a.U; p.c2 = a.H; p.ldc = f; p.N = 2 * f; p.K = d;
@@ -165,10 +174,17 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
   const int64_t P = padded_rows(S, E);
   {  // dGU = SwiGLU'(q(dO) q(W_down)^T): dO along d; W_down [f][d] along d
      // was quantised by the forward.
-    TRY(launch_mx_kmajor(a.d_o, S, d, 1, 0, w.doq, 0, w.dos, 0, s));
+    uint8_t *doq = w.doq, *dos = w.dos;
+    if (a.d_o_mx != nullptr) {  // written by the combine backward pass
+      const MxImage im = mx_image(a.d_o_mx, S, d);
+      doq = im.q;
+      dos = im.s;
+    } else {
+      TRY(launch_mx_kmajor(a.d_o, S, d, 1, 0, doq, 0, dos, 0, s));
+    }
     GemmParams p{};
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
-    p.a = w.doq; p.lda = d; p.as = w.dos; p.as_slab = 2LL * S;
+    p.a = doq; p.lda = d; p.as = dos; p.as_slab = 2LL * S;
     p.b0 = sv.wdq; p.ldb = d; p.bstride = wsz; p.bs0 = sv.wds; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
     p.c0 = a.dgu; p.ldc = 2 * f; p.e0 = a.G; p.e1 = a.U; p.N = f; p.K = d;
     // The epilogue also writes dGU along 2f (the next GEMM's A operand).

@@ -478,16 +478,23 @@ static hipError_t wgrad(const GemmParams& p, hipStream_t s) {
   else return launch_bf16_wgrad(p, s);
 }
 
+// G, U, H = SwiGLU(xp W_gate, xp W_up): the forward's first GEMM, and the
+// backward's recomputation of its activations.
 template <typename T>
-static hipError_t ffn_fwd_t(const FfnArgs& a, hipStream_t s) {
-  const int S = a.S, d = a.d, f = a.f;
+static hipError_t gate_up_t(const FfnArgs& a, hipStream_t s) {
+  const int d = a.d, f = a.f;
   GemmParams p{};
-  p.offsets = a.offsets; p.E = a.E; p.S = S; p.f = f;
-  // G, U, H = SwiGLU(xp W_gate, xp W_up)
+  p.offsets = a.offsets; p.E = a.E; p.S = a.S; p.f = f;
   p.a = a.xp; p.lda = d; p.b0 = a.w_gate; p.b1 = a.w_up; p.ldb = f;
   p.bstride = static_cast<int64_t>(d) * f;
   p.c0 = a.G; p.c1 = a.U; p.c2 = a.H; p.ldc = f; p.N = 2 * f; p.K = d;
-  hipError_t err = ragged<T>(FWD_GU, p, s);
+  return ragged<T>(FWD_GU, p, s);
+}
+
+template <typename T>
+static hipError_t ffn_fwd_t(const FfnArgs& a, hipStream_t s) {
+  const int S = a.S, d = a.d, f = a.f;
+  hipError_t err = gate_up_t<T>(a, s);
   if (err != hipSuccess) return err;
   // O = H W_down
   GemmParams q{};
@@ -501,6 +508,9 @@ template <typename T>
 static hipError_t ffn_bwd_t(const FfnArgs& a, hipStream_t s) {
   const int S = a.S, d = a.d, f = a.f;
   hipError_t err;
+  // Activation recompute: G, U, H come back from the gate/up GEMM, bit for
+  // bit what the forward computed (same kernel, same operands).
+  if (a.recompute && (err = gate_up_t<T>(a, s)) != hipSuccess) return err;
   {  // dGU = SwiGLU'(dO W_down^T)
     GemmParams p{};
     p.offsets = a.offsets; p.E = a.E; p.S = S; p.f = f;

@@ -28,6 +28,12 @@ struct FfnArgs {
   // MXFP8: the save-buffer region the forward fills with the backward's
   // quantised weight copies (ffn_mx_save_extra bytes).
   void* mx_save;
+  // MXFP8, optional: the operand images (mx_image layout) of xp and d_o that
+  // moe_dispatch / moe_combine_bwd already wrote; NULL = quantise here.
+  const void* xp_mx;
+  const void* d_o_mx;
+  // Backward only: recompute G, U, H (into the G, U, H pointers) first.
+  bool recompute;
 };
 
 hipError_t launch_ffn_fwd(const FfnArgs& a, bool is_f32, hipStream_t s);
@@ -64,6 +70,37 @@ size_t dispatch_bwd_workspace(int d, int E, bool is_f32);
 hipError_t launch_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* dlogits,
                                const void* w_router, bool is_f32, int T, int d, int E, int k,
                                void* dx, void* ws, hipStream_t s);
+
+// Expert-load diagnostics from the routed counts (dispatch.hip): 8 doubles.
+hipError_t launch_load_stats(const int32_t* counts, int E, double* out, hipStream_t s);
+
+// MXFP8 operand image of a bf16 [rows][cols] matrix quantised along cols, in
+// the grouped GEMM's A-operand layout: E4M3 codes [rows][cols], then E8M0
+// scales [cols/64][rows][2]. Each part starts 256-byte aligned and keeps 16
+// bytes of slack (a scale tile of a ragged row range is read up to the next
+// whole dword).
+struct MxImage {
+  uint8_t* q;
+  uint8_t* s;
+};
+inline size_t mx_part_bytes(size_t n) { return (n + 16 + 255) & ~static_cast<size_t>(255); }
+inline size_t mx_image_bytes(int64_t rows, int64_t cols) {
+  const size_t n = static_cast<size_t>(rows) * static_cast<size_t>(cols);
+  return mx_part_bytes(n) + mx_part_bytes(n / 32);
+}
+inline MxImage mx_image(const void* base, int64_t rows, int64_t cols) {
+  uint8_t* p = static_cast<uint8_t*>(const_cast<void*>(base));
+  return MxImage{p, p + mx_part_bytes(static_cast<size_t>(rows) * static_cast<size_t>(cols))};
+}
+
+// Dispatch and combine backward that also write the MXFP8 image of their bf16
+// output rows (xp, d_o) from the values they already hold; d = cols, S = rows.
+hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
+                              int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                              int32_t* token_of_row, void* xp, MxImage xp_mx, void* ws, hipStream_t s);
+hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gate,
+                                 const int32_t* row_of_slot, int T, int d, int k, void* d_o,
+                                 MxImage d_o_mx, float* dgate, hipStream_t s);
 
 // MXFP8 (mxfp8.hip)
 hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,

@@ -14,9 +14,16 @@ from . import _lib as L
 
 class MoELayer:
     def __init__(self, T: int, d: int, E: int, k: int, f: int, dtype: str = "bf16",
-                 learned_routing: bool = True, device: str = "cuda"):
+                 learned_routing: bool = True, device: str = "cuda", mx_images: bool = True,
+                 recompute: bool = False):
+        """``mx_images`` (MXFP8 layers): dispatch and combine-backward also write
+        the MXFP8 images of xp and d_o, which the grouped FFN calls then read;
+        False leaves the quantisation of both to the FFN calls.
+        ``recompute`` (fp32/bf16 layers): save no G, U, H between forward and
+        backward; the backward recomputes them (MOE_FLAG_RECOMPUTE)."""
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
-        self.shape = L.MoeShape.make(T, d, E, k, f, dtype)
+        self.shape = L.MoeShape.make(T, d, E, k, f, dtype, L.MOE_FLAG_RECOMPUTE if recompute else 0)
+        self.recompute = recompute
         self.dtype = L.TORCH_DTYPE[self.shape.dtype]
         self.learned = learned_routing
         S = T * k
@@ -40,6 +47,9 @@ class MoELayer:
         self.row_of_slot = buf(T, k, dtype=i32)
         self.token_of_row = buf(S, dtype=i32)
         self.xp = buf(S, d)
+        use_mx = mx_images and self.shape.dtype == L.MOE_MXFP8
+        self.xp_mx = torch.empty(L.mx_image_size(S, d), dtype=torch.uint8, device=dev) if use_mx else None
+        self.d_o_mx = torch.empty(L.mx_image_size(S, d), dtype=torch.uint8, device=dev) if use_mx else None
         self.save = torch.empty(L.save_size(self.shape), dtype=torch.uint8, device=dev)
         self.ws_ffn_fwd = ws(L.MOE_OP_FFN_FWD)
         self.o = buf(S, d)
@@ -61,10 +71,25 @@ class MoELayer:
             self.ws_dispatch_bwd = ws(L.MOE_OP_DISPATCH_BWD)
 
     def saved(self):
-        """(G, U, H) views of the save buffer, each [S][f]."""
+        """(G, U, H), each [S][f]: views of the save buffer or, for a recompute
+        layer, of the planes its last backward rebuilt in the backward
+        workspace (after the dG|dU rows)."""
         S, f = self.T * self.k, self.f
-        flat = self.save.view(self.dtype)
+        if self.recompute:
+            eb = self.xp.element_size()
+            off = (S * 2 * f * eb + 255) // 256 * 256
+            flat = self.ws_ffn_bwd[off:off + 3 * S * f * eb].view(self.dtype)
+        else:
+            flat = self.save.view(self.dtype)
         return tuple(flat[i * S * f:(i + 1) * S * f].view(S, f) for i in range(3))
+
+    def load_stats(self, stream=None):
+        """Enqueue the expert-load diagnostics of the last dispatch (moe_load_stats)
+        and return the device tensor of 8 float64 (LOAD_STATS order)."""
+        if not hasattr(self, "stats"):
+            self.stats = torch.empty(8, dtype=torch.float64, device=self.counts.device)
+        L.moe_load_stats(self.counts, self.stats, stream)
+        return self.stats
 
     def forward(self, x, w_gate, w_up, w_down, w_router=None, topk_idx=None, topk_gate=None, stream=None,
                 mark=None):
@@ -80,10 +105,10 @@ class MoELayer:
             self.topk_idx.copy_(topk_idx)
             self.topk_gate.copy_(topk_gate)
         L.moe_dispatch(x, self.topk_idx, s, self.counts, self.offsets, self.row_of_slot, self.token_of_row,
-                       self.xp, self.ws_dispatch, stream)
+                       self.xp, self.ws_dispatch, stream, xp_mx=self.xp_mx)
         mark("moe_dispatch")
         L.moe_grouped_ffn_fwd(self.xp, w_gate, w_up, w_down, self.offsets, s, self.save, self.o, self.ws_ffn_fwd,
-                              stream)
+                              stream, xp_mx=self.xp_mx)
         mark("moe_grouped_ffn_fwd")
         L.moe_combine(self.o, self.topk_gate, self.row_of_slot, s, self.y, stream)
         mark("moe_combine")
@@ -92,10 +117,12 @@ class MoELayer:
     def backward(self, dy, stream=None, mark=None):
         s = self.shape
         mark = mark or (lambda name: None)
-        L.moe_combine_bwd(dy, self.o, self.topk_gate, self.row_of_slot, s, self.d_o, self.dgate, stream)
+        L.moe_combine_bwd(dy, self.o, self.topk_gate, self.row_of_slot, s, self.d_o, self.dgate, stream,
+                          d_o_mx=self.d_o_mx)
         mark("moe_combine_bwd")
         L.moe_grouped_ffn_bwd(self.d_o, self.xp, self.w_gate, self.w_up, self.w_down, self.offsets, s, self.save,
-                              self.dxp, self.dw_gate, self.dw_up, self.dw_down, self.ws_ffn_bwd, stream)
+                              self.dxp, self.dw_gate, self.dw_up, self.dw_down, self.ws_ffn_bwd, stream,
+                              d_o_mx=self.d_o_mx)
         mark("moe_grouped_ffn_bwd")
         if self.learned:
             L.moe_route_bwd(self.x, self.w_router, self.topk_idx, self.topk_gate, self.dgate, s, self.dlogits,

@@ -37,12 +37,12 @@ def torch_dtype(wl):
     return torch.float32 if wl.dtype == "f32" else torch.bfloat16
 
 
-def run_layer(wl, inp, fwd_only=False):
+def run_layer(wl, inp, fwd_only=False, recompute=False):
     """Forward (+ backward) of the HIP layer on inputs from moe_inputs."""
     from routing_grouped_gemm_softmax_amd import MoELayer
     dt = torch_dtype(wl)
     learned = "w_router" in inp
-    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, wl.dtype, learned_routing=learned)
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, wl.dtype, learned_routing=learned, recompute=recompute)
     t = {n: dev(inp[n], dt) for n in ("x", "dy", "w_gate", "w_up", "w_down")}
     if learned:
         t["w_router"] = dev(inp["w_router"], dt)

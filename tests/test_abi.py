@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
                        (-3, b"MOE_ERR_MISALIGNED"), (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == name
@@ -93,13 +93,13 @@ def test_workspace_too_small():
     lib = L.load()
     s = shape()
     p = ctypes.c_void_p(0x100000)
-    rc = lib.moe_dispatch(p, p, ctypes.byref(s), p, p, p, p, p, p, 16, None)
+    rc = lib.moe_dispatch(p, p, ctypes.byref(s), p, p, p, p, p, None, p, 16, None)
     assert rc == L.MOE_ERR_WORKSPACE
-    rc = lib.moe_dispatch(p, p, ctypes.byref(s), p, p, p, p, p, ctypes.c_void_p(0x100010), 1 << 20, None)
+    rc = lib.moe_dispatch(p, p, ctypes.byref(s), p, p, p, p, p, None, ctypes.c_void_p(0x100010), 1 << 20, None)
     assert rc == L.MOE_ERR_MISALIGNED  # ws must be 256-byte aligned
-    rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, ctypes.byref(s), p, 10, p, None, 0, None)
+    rc = lib.moe_grouped_ffn_fwd(p, None, p, p, p, p, ctypes.byref(s), p, 10, p, None, 0, None)
     assert rc == L.MOE_ERR_WORKSPACE
-    rc = lib.moe_grouped_ffn_bwd(p, p, p, p, p, p, ctypes.byref(s), p, p, p, p, p, p, 10, None)
+    rc = lib.moe_grouped_ffn_bwd(p, None, p, p, p, p, p, ctypes.byref(s), p, p, p, p, p, p, 10, None)
     assert rc == L.MOE_ERR_WORKSPACE
     rc = lib.moe_route_bwd(p, p, p, p, p, ctypes.byref(s), p, p, p, 0, None)
     assert rc == L.MOE_ERR_WORKSPACE
@@ -113,10 +113,71 @@ def test_mxfp8_layer_needs_multiples_of_128_and_a_workspace():
     lib = L.load()
     p = ctypes.c_void_p(0x100000)
     s = shape(dtype="mxfp8", d=64)
-    rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, ctypes.byref(s), p, 1 << 40, p, p, 1 << 40, None)
+    rc = lib.moe_grouped_ffn_fwd(p, None, p, p, p, p, ctypes.byref(s), p, 1 << 40, p, p, 1 << 40, None)
     assert rc == L.MOE_ERR_UNSUPPORTED
     s = shape(dtype="mxfp8", d=128)
     assert L.workspace_size(L.MOE_OP_FFN_FWD, s) > 0
     assert L.workspace_size(L.MOE_OP_FFN_BWD, s) > L.workspace_size(L.MOE_OP_FFN_BWD, shape(dtype="bf16", d=128))
-    rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, ctypes.byref(s), p, 1 << 40, p, p, 16, None)
+    rc = lib.moe_grouped_ffn_fwd(p, None, p, p, p, p, ctypes.byref(s), p, 1 << 40, p, p, 16, None)
     assert rc == L.MOE_ERR_WORKSPACE
+
+
+def test_mx_image_arguments_are_checked_on_the_host():
+    """The MXFP8 images of xp and d_o: sized by moe_mx_image_size, accepted only
+    for MXFP8 layers and only 256-byte aligned; nothing is enqueued on error."""
+    lib = L.load()
+    assert L.mx_image_size(1024, 4096) == (1024 * 4096 + 16 + 255) // 256 * 256 + (1024 * 128 + 16 + 255) // 256 * 256
+    assert lib.moe_mx_image_size(0, 64) == ctypes.c_size_t(-1).value
+    assert lib.moe_mx_image_size(32, 96) == ctypes.c_size_t(-1).value
+    p = ctypes.c_void_p(0x100000)
+    bf = shape(dtype="bf16", d=128)
+    mx = shape(dtype="mxfp8", d=128, f=128)
+    ws = L.workspace_size(L.MOE_OP_DISPATCH, mx)
+    rc = lib.moe_dispatch(p, p, ctypes.byref(bf), p, p, p, p, p, p, p, 1 << 20, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "MXFP8" in L.last_error()
+    rc = lib.moe_dispatch(p, p, ctypes.byref(mx), p, p, p, p, p, ctypes.c_void_p(0x100080), p, ws, None)
+    assert rc == L.MOE_ERR_MISALIGNED
+    rc = lib.moe_combine_bwd(p, p, p, p, ctypes.byref(bf), p, p, p, None)
+    assert rc == L.MOE_ERR_INVALID_ARG
+    rc = lib.moe_combine_bwd(p, p, p, p, ctypes.byref(mx), p, ctypes.c_void_p(0x100010), p, None)
+    assert rc == L.MOE_ERR_MISALIGNED
+    rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, p, ctypes.byref(bf), p, 1 << 40, p, p, 1 << 40, None)
+    assert rc == L.MOE_ERR_INVALID_ARG
+    rc = lib.moe_grouped_ffn_bwd(p, ctypes.c_void_p(0x100040), p, p, p, p, p, ctypes.byref(mx), p, p, p, p, p, p,
+                                 1 << 40, None)
+    assert rc == L.MOE_ERR_MISALIGNED
+
+
+def test_recompute_flag_sizes_and_checks():
+    """MOE_FLAG_RECOMPUTE moves G, U, H from the save buffer into the FFN
+    workspaces; unknown flag bits and MXFP8 recompute are rejected."""
+    T, d, E, k, f = 256, 128, 8, 4, 128
+    S = T * k
+    for dt, b in (("f32", 4), ("bf16", 2)):
+        plain = shape(T=T, d=d, E=E, k=k, f=f, dtype=dt)
+        rec = L.MoeShape.make(T, d, E, k, f, dt, L.MOE_FLAG_RECOMPUTE)
+        guh = (3 * S * f * b + 255) // 256 * 256
+        assert L.save_size(plain) == guh and L.save_size(rec) == 0
+        assert L.workspace_size(L.MOE_OP_FFN_FWD, plain) == 0
+        assert L.workspace_size(L.MOE_OP_FFN_FWD, rec) == guh
+        assert L.workspace_size(L.MOE_OP_FFN_BWD, rec) == L.workspace_size(L.MOE_OP_FFN_BWD, plain) + guh
+    lib = L.load()
+    bad = L.MoeShape.make(T, d, E, k, f, "bf16", 2)
+    assert lib.moe_save_size(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+    mxr = L.MoeShape.make(T, d, E, k, f, "mxfp8", L.MOE_FLAG_RECOMPUTE)
+    assert lib.moe_workspace_size(L.MOE_OP_FFN_FWD, ctypes.byref(mxr)) == ctypes.c_size_t(-1).value
+    assert "recompute" in L.last_error()
+    # A recompute layer's forward needs its workspace (G, U, H live there).
+    rec = L.MoeShape.make(T, d, E, k, f, "bf16", L.MOE_FLAG_RECOMPUTE)
+    p = ctypes.c_void_p(0x100000)
+    rc = lib.moe_grouped_ffn_fwd(p, None, p, p, p, p, ctypes.byref(rec), None, 0, p, p, 16, None)
+    assert rc == L.MOE_ERR_WORKSPACE
+
+
+def test_load_stats_argument_checks():
+    lib = L.load()
+    p = ctypes.c_void_p(0x100000)
+    assert lib.moe_load_stats(None, 8, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(p, 0, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(p, 257, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(p, 8, ctypes.c_void_p(0x100008), None) == L.MOE_ERR_MISALIGNED

@@ -134,3 +134,50 @@ def test_quantize_bit_exact(axis):
     rq, rs = O.mx_quantize(x, "cols" if axis == 0 else "rows")
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
     np.testing.assert_array_equal(sc.cpu().numpy().reshape(rs.shape), rs)
+
+
+def _image(buf, rows, cols):
+    """Split an MXFP8 image (codes [rows][cols], then scales [cols/64][rows][2])
+    into codes [rows][cols] and scales [rows][cols/32] (mxfp8_quantize's order)."""
+    import routing_grouped_gemm_softmax_amd as M
+    raw = buf.cpu().numpy()
+    assert raw.size >= M.mx_image_size(rows, cols)
+    n = rows * cols
+    q = raw[:n].reshape(rows, cols)
+    off = (n + 16 + 255) // 256 * 256
+    s = raw[off:off + n // 32].reshape(cols // 64, rows, 2).transpose(1, 0, 2).reshape(rows, cols // 32)
+    return q, s
+
+
+@pytest.mark.parametrize("over", [dict(T=384, d=384, E=16, f=128), dict(T=200, d=4224, E=8, f=128)],
+                         ids=["ragged_empty_d384", "three_row_passes_d4224"])
+def test_dispatch_and_combine_bwd_mx_images(over):
+    """The MXFP8 images that moe_dispatch and moe_combine_bwd write beside xp and
+    d_o carry the oracle's codes and scales of the stored bf16 rows bit for
+    bit, and a layer that reads them gives bit-identical outputs to one that
+    quantises xp and d_o inside the grouped FFN calls."""
+    from routing_grouped_gemm_softmax_amd import MoELayer
+    wl = WORKLOADS["bf16_zipf"].with_shape(dtype="mxfp8", **over)
+    pop = [1, 0, 2, 1, 1, 0, 3, 1, 1, 1, 0, 1, 2, 1, 1, 0][:wl.E]
+    inp = make_inputs(wl, 1, popularity=pop)
+    print(f"[gpu] mx images: T={wl.T} d={wl.d} E={wl.E} k={wl.k} f={wl.f}", flush=True)
+    bf = torch.bfloat16
+    t = {n: dev(inp[n], bf) for n in ("x", "dy", "w_gate", "w_up", "w_down")}
+    idx, gate = dev(inp["topk_idx"], torch.int32), dev(inp["topk_gate"], torch.float32)
+    layers = {}
+    for fused in (True, False):
+        layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, "mxfp8", learned_routing=False, mx_images=fused)
+        layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=idx, topk_gate=gate)
+        layer.backward(t["dy"])
+        layers[fused] = layer
+    torch.cuda.synchronize()
+    a, b = layers[True], layers[False]
+    assert a.xp_mx is not None and b.xp_mx is None
+    S, d = wl.T * wl.k, wl.d
+    for name, img, rows in (("xp", a.xp_mx, a.xp), ("d_o", a.d_o_mx, a.d_o)):
+        q, s = _image(img, S, d)
+        rq, rs = O.mx_quantize(host(rows).astype(np.float64), "cols")
+        np.testing.assert_array_equal(q, rq, err_msg=f"{name} codes")
+        np.testing.assert_array_equal(s, rs, err_msg=f"{name} scales")
+    for n in ("xp", "o", "y", "d_o", "dgate", "dxp", "dw_gate", "dw_up", "dw_down", "dx"):
+        assert torch.equal(getattr(a, n), getattr(b, n)), n
