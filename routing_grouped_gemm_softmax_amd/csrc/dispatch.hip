@@ -27,6 +27,7 @@
 #include "mx_encode.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace moe {
 
@@ -257,35 +258,61 @@ hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int
   return dispatch_impl(x, topk_idx, 2, T, d, E, k, counts, offsets, row_of_slot, token_of_row, xp, &xp_mx, ws, s);
 }
 
+// Row kernels take the slot count K as a template argument and issue the
+// loads of all K rows of a piece before using any of them: with a runtime k
+// and a branch per slot, each row's load waited for the one before it.
+// A slot with row -1 (an expert id outside [0, E)) loads row 0 and leaves
+// its contribution out by a select, which gives the same bits as skipping it.
+template <typename F>
+static hipError_t with_k(int k, F&& f) {
+  switch (k) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 3: return f(std::integral_constant<int, 3>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 5: return f(std::integral_constant<int, 5>{});
+    case 6: return f(std::integral_constant<int, 6>{});
+    case 7: return f(std::integral_constant<int, 7>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // y[t] = sum_j gate[t][j] * o[row_of_slot[t][j]]  (fp32, slot order, one rounding).
-template <typename T>
+template <typename T, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, const float* __restrict__ gate,
-                                                      const int32_t* __restrict__ row_of_slot, int Tn, int k,
-                                                      int nvec, int lpt, T* __restrict__ y) {
+                                                      const int32_t* __restrict__ row_of_slot, int Tn, int nvec,
+                                                      int lpt, T* __restrict__ y) {
   constexpr int VE = Vec16<T>::N;
   const int tpw = 256 / lpt;
   const int t = blockIdx.x * tpw + threadIdx.x / lpt;
   const int sub = threadIdx.x % lpt;
   if (t >= Tn) return;
   const int64_t re = static_cast<int64_t>(nvec) * VE;  // elements per row
-  int rows[8];
-  float g[8];
+  int rows[K];
+  float g[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    rows[j] = j < k ? row_of_slot[static_cast<int64_t>(t) * k + j] : -1;
-    g[j] = j < k ? gate[static_cast<int64_t>(t) * k + j] : 0.0f;
+  for (int j = 0; j < K; ++j) {
+    rows[j] = row_of_slot[static_cast<int64_t>(t) * K + j];
+    g[j] = gate[static_cast<int64_t>(t) * K + j];
   }
   for (int v = sub; v < nvec; v += lpt) {
+    uint4 raw[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) raw[j] = ld16(o + max(rows[j], 0) * re + v * VE);
     float acc[VE];
 #pragma unroll
     for (int i = 0; i < VE; ++i) acc[i] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (rows[j] < 0) continue;
+    for (int j = 0; j < K; ++j) {
       float ov[VE];
-      unpack16(ld16(o + rows[j] * re + v * VE), ov);
+      unpack16(raw[j], ov);
+      const bool ok = rows[j] >= 0;
 #pragma unroll
-      for (int i = 0; i < VE; ++i) acc[i] = fmaf(g[j], ov[i], acc[i]);
+      for (int i = 0; i < VE; ++i) {
+        const float a = fmaf(g[j], ov[i], acc[i]);
+        acc[i] = ok ? a : acc[i];
+      }
     }
     st16(y + t * re + v * VE, pack16(acc));
   }
@@ -295,42 +322,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
 // fixed reduction tree: per-thread partials, lane butterfly, then waves in order).
 // MX (bf16 only): the same pass writes d_o's MXFP8 image (q, sc; S rows),
 // quantised from the stored bf16 values.
-template <typename T, bool MX>
+template <typename T, bool MX, int K>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ o,
                                                           const float* __restrict__ gate,
-                                                          const int32_t* __restrict__ row_of_slot, int Tn, int k,
-                                                          int nvec, int lpt, T* __restrict__ d_o,
-                                                          float* __restrict__ dgate, uint8_t* __restrict__ q,
-                                                          uint8_t* __restrict__ sc, int S) {
+                                                          const int32_t* __restrict__ row_of_slot, int Tn, int nvec,
+                                                          int lpt, T* __restrict__ d_o, float* __restrict__ dgate,
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
   constexpr int VE = Vec16<T>::N;
-  __shared__ float red[4][8];
+  __shared__ float red[4][K];
   const int tpw = 256 / lpt;
   const int t = blockIdx.x * tpw + threadIdx.x / lpt;
   const int sub = threadIdx.x % lpt;
   const bool live = t < Tn;
   const int64_t re = static_cast<int64_t>(nvec) * VE;
-  int rows[8];
-  float g[8], part[8];
+  int rows[K];
+  float g[K], part[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    rows[j] = (live && j < k) ? row_of_slot[static_cast<int64_t>(t) * k + j] : -1;
-    g[j] = (live && j < k) ? gate[static_cast<int64_t>(t) * k + j] : 0.0f;
+  for (int j = 0; j < K; ++j) {
+    rows[j] = live ? row_of_slot[static_cast<int64_t>(t) * K + j] : -1;
+    g[j] = live ? gate[static_cast<int64_t>(t) * K + j] : 0.0f;
     part[j] = 0.0f;
   }
   if (live) {
     for (int v = sub; v < nvec; v += lpt) {
-      float dv[VE];
-      unpack16(ld16(dy + t * re + v * VE), dv);
+      const uint4 draw = ld16(dy + t * re + v * VE);
+      uint4 raw[K];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (rows[j] < 0) continue;
+      for (int j = 0; j < K; ++j) raw[j] = ld16(o + max(rows[j], 0) * re + v * VE);
+      float dv[VE];
+      unpack16(draw, dv);
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        // Every row's value is used outside the branch below, so no load is
+        // sunk into it (part[j] of a row -1 is never written out).
         float ov[VE], sv[VE];
-        unpack16(ld16(o + rows[j] * re + v * VE), ov);
+        unpack16(raw[j], ov);
 #pragma unroll
         for (int i = 0; i < VE; ++i) {
           part[j] = fmaf(dv[i], ov[i], part[j]);
           sv[i] = g[j] * dv[i];
         }
+        if (rows[j] < 0) continue;  // the same for every lane of the token
         const uint4 pk = pack16(sv);
         st16(d_o + rows[j] * re + v * VE, pk);
         if constexpr (MX) {
@@ -343,27 +375,25 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
   // Reduce part[j] over the lpt lanes of the token.
   const int width = lpt < 64 ? lpt : 64;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < K; ++j)
     for (int off = width >> 1; off > 0; off >>= 1) part[j] += __shfl_xor(part[j], off, kWave);
   if (lpt <= 64) {
     if (live && sub == 0)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < k) dgate[static_cast<int64_t>(t) * k + j] = rows[j] >= 0 ? part[j] : 0.0f;
+      for (int j = 0; j < K; ++j) dgate[static_cast<int64_t>(t) * K + j] = rows[j] >= 0 ? part[j] : 0.0f;
   } else {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (lane == 0)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) red[wave][j] = part[j];
+      for (int j = 0; j < K; ++j) red[wave][j] = part[j];
     __syncthreads();
     if (live && sub == 0) {
       const int w0 = (threadIdx.x / lpt) * (lpt / 64);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;
+      for (int j = 0; j < K; ++j) {
         float s = 0.0f;
-        for (int q = 0; q < lpt / 64; ++q) s += red[w0 + q][j];
-        dgate[static_cast<int64_t>(t) * k + j] = rows[j] >= 0 ? s : 0.0f;
+        for (int w = 0; w < lpt / 64; ++w) s += red[w0 + w][j];
+        dgate[static_cast<int64_t>(t) * K + j] = rows[j] >= 0 ? s : 0.0f;
       }
     }
   }
@@ -374,13 +404,16 @@ hipError_t launch_combine(const void* o, const float* gate, const int32_t* row_o
   const int nvec = d * (is_f32 ? 4 : 2) / 16;
   const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
-  if (is_f32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(o), gate, row_of_slot,
-                       T, k, nvec, lpt, static_cast<float*>(y));
-  else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(o), gate,
-                       row_of_slot, T, k, nvec, lpt, static_cast<bf16_t*>(y));
-  return hipGetLastError();
+  return with_k(k, [&](auto KC) {
+    constexpr int K = decltype(KC)::value;
+    if (is_f32)
+      hipLaunchKernelGGL((combine_kernel<float, K>), grid, dim3(256), 0, s, static_cast<const float*>(o), gate,
+                         row_of_slot, T, nvec, lpt, static_cast<float*>(y));
+    else
+      hipLaunchKernelGGL((combine_kernel<bf16_t, K>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(o), gate,
+                         row_of_slot, T, nvec, lpt, static_cast<bf16_t*>(y));
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate, const int32_t* row_of_slot,
@@ -388,15 +421,18 @@ hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate, 
   const int nvec = d * (is_f32 ? 4 : 2) / 16;
   const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
-  if (is_f32)
-    hipLaunchKernelGGL((combine_bwd_kernel<float, false>), grid, dim3(256), 0, s, static_cast<const float*>(dy),
-                       static_cast<const float*>(o), gate, row_of_slot, T, k, nvec, lpt, static_cast<float*>(d_o),
-                       dgate, nullptr, nullptr, T * k);
-  else
-    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, false>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(dy),
-                       static_cast<const bf16_t*>(o), gate, row_of_slot, T, k, nvec, lpt,
-                       static_cast<bf16_t*>(d_o), dgate, nullptr, nullptr, T * k);
-  return hipGetLastError();
+  return with_k(k, [&](auto KC) {
+    constexpr int K = decltype(KC)::value;
+    if (is_f32)
+      hipLaunchKernelGGL((combine_bwd_kernel<float, false, K>), grid, dim3(256), 0, s, static_cast<const float*>(dy),
+                         static_cast<const float*>(o), gate, row_of_slot, T, nvec, lpt, static_cast<float*>(d_o),
+                         dgate, nullptr, nullptr, T * k);
+    else
+      hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, false, K>), grid, dim3(256), 0, s,
+                         static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec,
+                         lpt, static_cast<bf16_t*>(d_o), dgate, nullptr, nullptr, T * k);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gate, const int32_t* row_of_slot, int T,
@@ -404,10 +440,13 @@ hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gat
   const int nvec = d * 2 / 16;
   const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
-  hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, true>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(dy),
-                     static_cast<const bf16_t*>(o), gate, row_of_slot, T, k, nvec, lpt, static_cast<bf16_t*>(d_o),
-                     dgate, d_o_mx.q, d_o_mx.s, T * k);
-  return hipGetLastError();
+  return with_k(k, [&](auto KC) {
+    constexpr int K = decltype(KC)::value;
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, true, K>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(dy),
+                       static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec, lpt, static_cast<bf16_t*>(d_o),
+                       dgate, d_o_mx.q, d_o_mx.s, T * k);
+    return hipGetLastError();
+  });
 }
 
 // W_r [d][E] -> W_rT [E][d] (same dtype), so the router term of dx reads rows.
@@ -423,22 +462,22 @@ __global__ void transpose_router_kernel(const T* __restrict__ w, int d, int E, T
 // dl is zero off the chosen set, so only those (at most k) columns are read.
 // When a token has whole waves (lpt >= 64) each wave finds them with one
 // ballot per 64 experts; narrower rows scan the E values per lane.
-template <typename T>
+template <typename T, int K>
 __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__ dxp, const int32_t* __restrict__ row_of_slot,
                                                            const float* __restrict__ dl, const T* __restrict__ wt,
-                                                           int Tn, int E, int k, int nvec, int lpt, T* __restrict__ dx) {
+                                                           int Tn, int E, int nvec, int lpt, T* __restrict__ dx) {
   constexpr int VE = Vec16<T>::N;
   const int tpw = 256 / lpt;
   const int t = blockIdx.x * tpw + threadIdx.x / lpt;
   const int sub = threadIdx.x % lpt;
   if (t >= Tn) return;
   const int64_t re = static_cast<int64_t>(nvec) * VE;
-  int rows[8];
+  int rows[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) rows[j] = j < k ? row_of_slot[static_cast<int64_t>(t) * k + j] : -1;
-  // The token's router columns: (expert, dl) pairs, at most 8.
-  int ce[8];
-  float cv[8];
+  for (int j = 0; j < K; ++j) rows[j] = row_of_slot[static_cast<int64_t>(t) * K + j];
+  // The token's router columns: (expert, dl) pairs, at most K.
+  int ce[K];
+  float cv[K];
   int nr = 0;
   if (dl != nullptr) {
     const float* dlt = dl + static_cast<int64_t>(t) * E;
@@ -447,7 +486,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
       for (int c0 = 0; c0 < E; c0 += kWave) {
         const float c = (c0 + lane < E) ? dlt[c0 + lane] : 0.0f;
         uint64_t m = __ballot(c != 0.0f);
-        while (m != 0 && nr < 8) {
+        while (m != 0 && nr < K) {
           const int b = __ffsll(static_cast<long long>(m)) - 1;
           m &= m - 1;
           ce[nr] = c0 + b;
@@ -456,7 +495,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
         }
       }
     } else {
-      for (int e = 0; e < E && nr < 8; ++e) {
+      for (int e = 0; e < E && nr < K; ++e) {
         const float c = dlt[e];
         if (c != 0.0f) {
           ce[nr] = e;
@@ -467,22 +506,38 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
     }
   }
   for (int v = sub; v < nvec; v += lpt) {
+    // The router term has at most K non-zero columns (dl is zero off the
+    // token's chosen set); slots past nr load row 0 and are selected out.
+    uint4 raw[K], wraw[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) raw[j] = ld16(dxp + max(rows[j], 0) * re + v * VE);
+    if (dl != nullptr) {
+#pragma unroll
+      for (int r = 0; r < K; ++r) wraw[r] = ld16(wt + (r < nr ? ce[r] : 0) * re + v * VE);
+    }
     float acc[VE];
 #pragma unroll
     for (int i = 0; i < VE; ++i) acc[i] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (rows[j] < 0) continue;
+    for (int j = 0; j < K; ++j) {
       float gv[VE];
-      unpack16(ld16(dxp + rows[j] * re + v * VE), gv);
+      unpack16(raw[j], gv);
+      const bool ok = rows[j] >= 0;
 #pragma unroll
-      for (int i = 0; i < VE; ++i) acc[i] += gv[i];
+      for (int i = 0; i < VE; ++i) acc[i] = ok ? acc[i] + gv[i] : acc[i];
     }
-    for (int r = 0; r < nr; ++r) {
-      float wv[VE];
-      unpack16(ld16(wt + ce[r] * re + v * VE), wv);
+    if (dl != nullptr) {
 #pragma unroll
-      for (int i = 0; i < VE; ++i) acc[i] = fmaf(cv[r], wv[i], acc[i]);
+      for (int r = 0; r < K; ++r) {
+        float wv[VE];
+        unpack16(wraw[r], wv);
+        const bool ok = r < nr;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) {
+          const float a = fmaf(cv[r], wv[i], acc[i]);
+          acc[i] = ok ? a : acc[i];
+        }
+      }
     }
     st16(dx + t * re + v * VE, pack16(acc));
   }
@@ -512,14 +567,16 @@ hipError_t launch_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, cons
   const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
   const float* dl = router ? dlogits : nullptr;
-  if (is_f32)
-    hipLaunchKernelGGL(dispatch_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(dxp), row_of_slot,
-                       dl, static_cast<const float*>(ws), T, E, k, nvec, lpt, static_cast<float*>(dx));
-  else
-    hipLaunchKernelGGL(dispatch_bwd_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(dxp),
-                       row_of_slot, dl, static_cast<const bf16_t*>(ws), T, E, k, nvec, lpt,
-                       static_cast<bf16_t*>(dx));
-  return hipGetLastError();
+  return with_k(k, [&](auto KC) {
+    constexpr int K = decltype(KC)::value;
+    if (is_f32)
+      hipLaunchKernelGGL((dispatch_bwd_kernel<float, K>), grid, dim3(256), 0, s, static_cast<const float*>(dxp),
+                         row_of_slot, dl, static_cast<const float*>(ws), T, E, nvec, lpt, static_cast<float*>(dx));
+    else
+      hipLaunchKernelGGL((dispatch_bwd_kernel<bf16_t, K>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(dxp),
+                         row_of_slot, dl, static_cast<const bf16_t*>(ws), T, E, nvec, lpt, static_cast<bf16_t*>(dx));
+    return hipGetLastError();
+  });
 }
 
 }  // namespace moe
