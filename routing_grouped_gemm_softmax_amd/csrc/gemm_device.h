@@ -488,6 +488,127 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
       });
     });
     flush(0, U, ld, rows, GC);
+  } else if constexpr (MODE == BWD_DOWN && !QUANT && NB % 2 == 0 && MB % 2 == 0) {
+    // dH -> dG = dH U sig(G) (1 + G (1 - sig(G))), dU = dH G sig(G); a row of
+    // dGU is [dG (f) | dU (f)]. Pipelined over units (column group jp of 64,
+    // row half h): the saved G, U of a unit come in by LDS DMA into rows
+    // [h WM/2, (h+1) WM/2) of staging tiles 0, 1 while the unit before it is
+    // computed and written; a unit's results leave as range-checked buffer
+    // stores before the next unit's loads overwrite its rows. Every load and
+    // store is issued whatever
+    // the row count (the descriptors drop rows past the end), so the vmcnt
+    // waits below count exactly: unit u waits for every operation issued
+    // before the one issued after its loads.
+    constexpr int HR = WM / 2, TL = HR / 8, L = 2 * TL;  // L: loads (or stores) per unit
+    static_assert(2 * L < 64, "vmcnt range");
+    const int64_t ld = p.ldc * 2, lds_ = static_cast<int64_t>(p.f) * 2;
+    auto load_unit = [&](auto JP, auto H) {
+      constexpr int jp = decltype(JP)::value, h = decltype(H)::value;
+      const int col0 = n0 + wn * WN + jp * 64;
+      const int64_t sbase = (static_cast<int64_t>(mrow) * p.f + col0) * 2;
+      const int64_t sbytes = static_cast<int64_t>(rows) * p.f * 2;
+      // Offsets are rebuilt from an opaque copy of the lane id in every unit:
+      // kept live across units they cost registers the accumulators need.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const auto rs = make_rsrc(static_cast<const char*>(sl ? p.e1 : p.e0) + sbase, sbytes);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wa + sl * kSlot));
+#pragma unroll
+        for (int tt = 0; tt < TL; ++tt) {
+          const int t = h * TL + tt, r = t * 8 + (ln >> 3);
+          const int cc = (ln & 7) ^ ((r >> 1) & 7);  // logical chunk held by this lane's slot
+          load_lds16(rs, static_cast<uint32_t>(r * lds_ + cc * 16), dst + t * 1024);
+        }
+      }
+    };
+    auto compute_unit = [&](auto JP, auto H) {
+      constexpr int jp = decltype(JP)::value, h = decltype(H)::value;
+      static_for<MB / 2>([&](auto II) {
+        constexpr int I = h * (MB / 2) + decltype(II)::value;
+        static_for<2>([&](auto JJ) {
+          static_for<4>([&](auto Q) {
+            constexpr int j = jp * 2 + JJ;
+            const int r = I * 32 + l32, col = JJ * 32 + 8 * Q + 4 * hl;
+            float g[4], u[4], dg[4], du[4];
+            unpack4(get4(0, r, col), g);
+            unpack4(get4(1, r, col), u);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float dh = acc[j][I][4 * Q + q];
+              const float sg = sigmoid_f(g[q]);
+              du[q] = dh * g[q] * sg;
+              dg[q] = dh * u[q] * sg * (1.0f + g[q] * (1.0f - sg));
+            }
+            put4(0, r, col, pack4(dg[0], dg[1], dg[2], dg[3]));
+            put4(1, r, col, pack4(du[0], du[1], du[2], du[3]));
+          });
+        });
+      });
+    };
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    // Store unit (jp, h): dG and dU rows out of staging as L range-checked
+    // buffer stores; each store consumes its LDS read, so once they are
+    // issued the rows of half h are free and `next` may issue the loads of
+    // the unit that reuses them.
+    auto drain_unit = [&](auto JP, auto H, auto next) {
+      constexpr int jp = decltype(JP)::value, h = decltype(H)::value;
+      wave_sync();  // the unit's results are in staging
+      const int col0 = n0 + wn * WN + jp * 64;
+      const char* C = static_cast<const char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
+      const auto rg = make_rsrc(C, static_cast<int64_t>(rows) * ld);
+      const auto ru = make_rsrc(C + static_cast<int64_t>(p.f) * 2, static_cast<int64_t>(rows) * ld);
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int cl = ln & 7;
+#pragma unroll
+      for (int tt = 0; tt < TL; ++tt) {
+        const int r = (h * TL + tt) * 8 + (ln >> 3);
+        const int off = r * 128 + ((cl ^ (r >> 1)) & 7) * 16;
+        const u32x4_t vg = *reinterpret_cast<const u32x4_t*>(wa + off);
+        const u32x4_t vu = *reinterpret_cast<const u32x4_t*>(wa + kSlot + off);
+        __builtin_amdgcn_raw_buffer_store_b128(vg, rg, static_cast<uint32_t>(r * ld + cl * 16), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vu, ru, static_cast<uint32_t>(r * ld + cl * 16), 0, 0);
+      }
+      next();
+    };
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
+    auto none = [] {};
+    static_assert(NB / 2 == 1 || NB / 2 == 2, "one or two column groups of 64 per wave");
+    if constexpr (NB / 2 == 2) {
+      // Issue order: L(0,0) L(0,1) | S(0,0) L(1,0) | S(0,1) L(1,1) | S(1,0) | S(1,1).
+      load_unit(Z{}, Z{});
+      load_unit(Z{}, O{});
+      wait_vmcnt<L>();  // (0,0) landed
+      wave_sync();
+      compute_unit(Z{}, Z{});
+      drain_unit(Z{}, Z{}, [&] { load_unit(O{}, Z{}); });
+      wait_vmcnt<2 * L>();  // (0,1) landed: S(0,0), L(1,0) may fly
+      wave_sync();
+      compute_unit(Z{}, O{});
+      drain_unit(Z{}, O{}, [&] { load_unit(O{}, O{}); });
+      wait_vmcnt<2 * L>();  // (1,0) landed: S(0,1), L(1,1) may fly
+      wave_sync();
+      compute_unit(O{}, Z{});
+      drain_unit(O{}, Z{}, none);
+      wait_vmcnt<L>();  // (1,1) landed: S(1,0) may fly
+      wave_sync();
+      compute_unit(O{}, O{});
+      drain_unit(O{}, O{}, none);
+    } else {
+      load_unit(Z{}, Z{});
+      load_unit(Z{}, O{});
+      wait_vmcnt<L>();
+      wave_sync();
+      compute_unit(Z{}, Z{});
+      drain_unit(Z{}, Z{}, none);
+      wait_vmcnt<L>();  // (0,1) landed: S(0,0) may fly
+      wave_sync();
+      compute_unit(Z{}, O{});
+      drain_unit(Z{}, O{}, none);
+    }
   } else if constexpr (MODE == BWD_DOWN) {
     // dH -> dG = dH U sig(G) (1 + G (1 - sig(G))), dU = dH G sig(G); a row of
     // dGU is [dG (f) | dU (f)]. Column groups of 64 (NB = 1: 32).
