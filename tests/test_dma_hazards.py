@@ -28,7 +28,10 @@ TOOLS = ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump")
 
 def _disassemble(tmp_path):
     fb = tmp_path / "fatbin.bin"
-    subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fb}", LIB], check=True)
+    # An explicit output file: with the input alone, llvm-objcopy rewrites
+    # the library in place.
+    subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fb}", LIB, str(tmp_path / "lib_copy.so")],
+                   check=True)
     data = fb.read_bytes()
     magic = b"__CLANG_OFFLOAD_BUNDLE__"
     starts = [m.start() for m in re.finditer(re.escape(magic), data)]
