@@ -172,11 +172,20 @@ __global__ __launch_bounds__(256) void mx_tgroup_kernel(const bf16_t* __restrict
   __syncthreads();
   const bf16_t* src = in + static_cast<int64_t>(b) * in_bstride;
   const int ch = tid & 7;
+  // All four loads go out before any is used: rows past a group's end load
+  // row 0 (always in bounds) and are replaced by zeros.
+  uint4 raw[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (rr < s_valid[h]) v = ld16(src + static_cast<int64_t>(s_src[h] + rr) * C + c0 + ch * 8);
+    const int64_t row = rr < s_valid[h] ? s_src[h] + rr : 0;
+    raw[i] = ld16(src + row * C + c0 + ch * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
+    const bool ok = rr < s_valid[h];
+    const uint4 v = make_uint4(ok ? raw[i].x : 0u, ok ? raw[i].y : 0u, ok ? raw[i].z : 0u, ok ? raw[i].w : 0u);
     *reinterpret_cast<uint4*>(&tile[r][ch * 8]) = v;
     if (qk != nullptr && p0 + r < P) {  // uniform per wave (a wave's 8 rows share a 64-row half)
       // Columns-blocked copy straight from the registers (one group: row p0 + r).
