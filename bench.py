@@ -139,13 +139,22 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.copy_calibration:
+        # A plain device copy of known size: scales the HBM counters, and its
+        # rate is the practical read+write bandwidth the copy kernels face.
         n = args.copy_calibration << 20
         a = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(args.steps):
             b.copy_(a)
+        e1.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps + 1, "ms_per_copy": round(ms, 4),
+                          "read_plus_write_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     if args.as_bf16:

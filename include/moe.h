@@ -284,6 +284,24 @@ int moe_load_stats(const int32_t* counts, int64_t E, double* stats_out, void* st
 int mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, int axis, uint8_t* q_out,
                    uint8_t* scale_out, void* stream);
 
+/* MXFP8 quantisation along rows inside row groups (the layout of a
+ * weight-gradient operand, whose K runs over one expert's tokens): blocks of
+ * 32 consecutive rows of one column within each group [group_offsets[g],
+ * group_offsets[g+1]), a group's last block completed with zero rows, which
+ * change no scale. Scale code and element rounding as in mxfp8_quantize.
+ * in_bf16 [rows][cols]; q_out [rows][cols] (codes of every row of a group);
+ * scale_out [rows/32 + groups][cols], block-major: the blocks of group 0 in
+ * row order, then those of group 1, ...; rows past the last block are not
+ * written. group_offsets: device int32 [groups + 1], nondecreasing from 0 to
+ * rows (never read by the host; values are clamped into [0, rows], so a
+ * malformed table gives wrong codes, not an access out of bounds).
+ * Errors: MOE_ERR_INVALID_ARG (NULL pointer, rows or cols < 1, groups outside
+ * 1..256), MOE_ERR_UNSUPPORTED (rows >= 2^31 or rows * cols > 2^40).
+ * Passage: as for mxfp8_quantize; the grouping follows the experts' row
+ * ranges of the grouped GEMM (bytechap.com page, "Cómo funciona"). */
+int mxfp8_quantize_grouped(const void* in_bf16, int64_t rows, int64_t cols, const int32_t* group_offsets,
+                           int64_t groups, uint8_t* q_out, uint8_t* scale_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,7 @@ SIGNATURES = {
     "moe_route_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _SZ, _P]),
     "moe_dispatch_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _SZ, _P]),
     "moe_load_stats": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
+    "mxfp8_quantize_grouped": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, _P, ctypes.c_int64, _P, _P, _P]),
     "mxfp8_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P]),
 }
 
@@ -231,3 +232,18 @@ def moe_load_stats(counts, out, stream=None):
     if counts.dtype != torch.int32:
         raise TypeError("counts must be int32")
     _check("moe_load_stats", load().moe_load_stats(_ptr(counts), counts.numel(), _ptr(out), _stream(stream)))
+
+
+def mxfp8_quantize_grouped(x, group_offsets, q, scale, stream=None):
+    """MXFP8 along rows inside the row groups of group_offsets (device int32,
+    groups + 1 entries): q [rows][cols] uint8, scale [rows // 32 + groups][cols]."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("mxfp8_quantize_grouped takes a 2-D bf16 tensor")
+    rows, cols = x.shape
+    groups = group_offsets.numel() - 1
+    if group_offsets.dtype != torch.int32:
+        raise TypeError("group_offsets must be int32")
+    _expect(q, torch.uint8, rows * cols, "q")
+    _expect(scale, torch.uint8, (rows // 32 + groups) * cols, "scale")
+    _check("mxfp8_quantize_grouped", load().mxfp8_quantize_grouped(
+        _ptr(x), rows, cols, _ptr(group_offsets), groups, _ptr(q), _ptr(scale), _stream(stream)))

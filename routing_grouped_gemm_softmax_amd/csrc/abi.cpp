@@ -347,4 +347,18 @@ int mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, int axis, ui
   return MOE_OK;
 }
 
+int mxfp8_quantize_grouped(const void* in_bf16, int64_t rows, int64_t cols, const int32_t* group_offsets,
+                           int64_t groups, uint8_t* q_out, uint8_t* scale_out, void* stream) {
+  if (!in_bf16 || !group_offsets || !q_out || !scale_out)
+    return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_grouped: NULL pointer");
+  if (rows < 1 || cols < 1) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_grouped: rows and cols must be >= 1");
+  if (groups < 1 || groups > 256)
+    return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_grouped: groups must be in 1..256 (got %lld)", (long long)groups);
+  if (rows >= ((int64_t)1 << 31) || rows * cols > ((int64_t)1 << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "mxfp8_quantize_grouped: too large");
+  LAUNCH(moe::launch_mxfp8_quantize_grouped(in_bf16, rows, cols, group_offsets, (int)groups, q_out, scale_out,
+                                            as_stream(stream)));
+  return MOE_OK;
+}
+
 }  // extern "C"

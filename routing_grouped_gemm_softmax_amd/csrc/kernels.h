@@ -105,6 +105,8 @@ hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gat
 // MXFP8 (mxfp8.hip)
 hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,
                                  uint8_t* scale, hipStream_t s);
+hipError_t launch_mxfp8_quantize_grouped(const void* in, int64_t rows, int64_t cols, const int32_t* off, int G,
+                                         uint8_t* q, uint8_t* scale, hipStream_t s);
 // Into the grouped GEMM's layout (E4M3 K-major, scales [K/64][rows][2]):
 // K along the columns of in [R][C] (batched)...
 hipError_t launch_mx_kmajor(const void* in, int R, int C, int batches, int64_t in_bstride, uint8_t* q,

@@ -62,6 +62,73 @@ __global__ __launch_bounds__(256) void mxfp8_cols_kernel(const bf16_t* __restric
   scale[i] = static_cast<uint8_t>(c);
 }
 
+// Blocks of 32 consecutive rows inside row groups [off[g], off[g+1]), each
+// group's last block completed with zero rows (which change no scale): the
+// layout of a weight-gradient operand, whose K runs over one expert's tokens.
+// One workgroup per (32-row block of the group-major block list, 256
+// columns): grid x over blocks, y over column tiles. Every workgroup scans the group sizes in LDS to find its block's
+// group; workgroups past the last block exit. Offsets are clamped into
+// [0, rows], so a malformed table cannot make an access out of bounds.
+__global__ __launch_bounds__(256) void mxfp8_grouped_kernel(const bf16_t* __restrict__ in, int64_t rows, int64_t cols,
+                                                            const int32_t* __restrict__ off, int G,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+  __shared__ int s_lo[256], s_hi[256], s_first[257];
+  const int tid = threadIdx.x;
+  // Group bounds and blocks per group (clamped), then a block-start scan.
+  int nb = 0;
+  if (tid < G) {
+    const int64_t lo = min(max(static_cast<int64_t>(off[tid]), int64_t{0}), rows);
+    const int64_t hi = min(max(static_cast<int64_t>(off[tid + 1]), lo), rows);
+    s_lo[tid] = static_cast<int>(lo);
+    s_hi[tid] = static_cast<int>(hi);
+    nb = static_cast<int>((hi - lo + 31) / 32);
+  }
+  __shared__ int s_wave[4];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int incl = wave_exclusive_scan(nb) + nb;
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wave[w];
+  if (tid < G) s_first[tid + 1] = base + incl;
+  if (tid == 0) s_first[0] = 0;
+  __syncthreads();
+  const int b = blockIdx.x;
+  if (b >= s_first[G]) return;  // uniform: past the last block
+  int lo = 0, hi = G;           // s_first[lo] <= b < s_first[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_first[mid] <= b) lo = mid; else hi = mid;
+  }
+  const int64_t r0 = s_lo[lo] + static_cast<int64_t>(b - s_first[lo]) * 32;
+  const int n = static_cast<int>(min(static_cast<int64_t>(32), s_hi[lo] - r0));
+  const int64_t col = static_cast<int64_t>(blockIdx.y) * 256 + tid;
+  if (col >= cols) return;
+  const bf16_t* src = in + r0 * cols + col;
+  float v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const float x = bf16_to_f32(src[min(r, n - 1) * cols]);  // rows past the group end: in bounds, zeroed
+    v[r] = r < n ? x : 0.0f;
+  }
+  uint32_t w[8];
+  const int c = mx_encode_block(v, w);
+  uint8_t* dst = q + r0 * cols + col;
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+    if (r < n) dst[r * cols] = static_cast<uint8_t>(w[r / 4] >> (8 * (r % 4)));
+  scale[static_cast<int64_t>(b) * cols + col] = static_cast<uint8_t>(c);
+}
+
+hipError_t launch_mxfp8_quantize_grouped(const void* in, int64_t rows, int64_t cols, const int32_t* off, int G,
+                                         uint8_t* q, uint8_t* scale, hipStream_t s) {
+  const int64_t nb_max = rows / 32 + G;  // >= the sum over groups of ceil(n_g / 32)
+  const dim3 grid(static_cast<unsigned>(nb_max), static_cast<unsigned>((cols + 255) / 256));
+  hipLaunchKernelGGL(mxfp8_grouped_kernel, grid, dim3(256), 0, s, static_cast<const bf16_t*>(in), rows, cols, off, G,
+                     q, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q, uint8_t* scale,
                                  hipStream_t s) {
   const bf16_t* src = static_cast<const bf16_t*>(in);

@@ -181,3 +181,13 @@ def test_load_stats_argument_checks():
     assert lib.moe_load_stats(p, 0, p, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_load_stats(p, 257, p, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_load_stats(p, 8, ctypes.c_void_p(0x100008), None) == L.MOE_ERR_MISALIGNED
+
+
+def test_grouped_quantize_argument_checks():
+    lib = L.load()
+    p = ctypes.c_void_p(0x100000)
+    assert lib.mxfp8_quantize_grouped(None, 64, 64, p, 2, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.mxfp8_quantize_grouped(p, 0, 64, p, 2, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.mxfp8_quantize_grouped(p, 64, 64, p, 0, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.mxfp8_quantize_grouped(p, 64, 64, p, 257, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.mxfp8_quantize_grouped(p, 1 << 31, 1, p, 1, p, p, None) == L.MOE_ERR_UNSUPPORTED

@@ -181,3 +181,51 @@ def test_dispatch_and_combine_bwd_mx_images(over):
         np.testing.assert_array_equal(s, rs, err_msg=f"{name} scales")
     for n in ("xp", "o", "y", "d_o", "dgate", "dxp", "dw_gate", "dw_up", "dw_down", "dx"):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
+
+
+@pytest.mark.parametrize("sizes,cols", [([0, 37, 64, 1, 0, 198], 200), ([300], 512), ([5] * 40 + [0] * 3, 260)],
+                         ids=["ragged_empty_groups", "one_group", "many_short_groups"])
+def test_grouped_quantize_bit_exact(sizes, cols):
+    """mxfp8_quantize_grouped: per group, the oracle's row-blocked codes and
+    scales of the group padded with zero rows to a multiple of 32, bit for
+    bit; dequantised, exactly the oracle's mx_rows_grouped."""
+    import routing_grouped_gemm_softmax_amd as M
+    from moe_inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    rows = sum(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rng = np.random.default_rng(11)
+    a = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-30, 30, size=(rows, 1)))
+    a[:, 3] = 0.0
+    x = bf16_bits_to_f32(f32_to_bf16_bits(a.astype(np.float32))).astype(np.float64)
+    print(f"[gpu] grouped quantize rows={rows} cols={cols} groups={len(sizes)}", flush=True)
+    xt = torch.from_numpy(x.astype(np.float32)).to("cuda", torch.bfloat16)
+    q = torch.zeros(rows, cols, dtype=torch.uint8, device="cuda")
+    sc = torch.full(((rows // 32 + len(sizes)) * cols,), 0xAB, dtype=torch.uint8, device="cuda")
+    M.mxfp8_quantize_grouped(xt, dev(off, torch.int32), q, sc)
+    torch.cuda.synchronize()
+    gq, gs = q.cpu().numpy(), sc.cpu().numpy().reshape(-1, cols)
+    rq, rs = np.zeros((rows, cols), np.uint8), []
+    for g in range(len(sizes)):
+        lo, hi = off[g], off[g + 1]
+        if hi == lo:
+            continue
+        n = hi - lo
+        pad = np.zeros(((n + 31) // 32 * 32, cols))
+        pad[:n] = x[lo:hi]
+        cq, cs = O.mx_quantize(pad, "rows")
+        rq[lo:hi] = cq[:n]
+        rs.append(cs)
+    rs = np.concatenate(rs)
+    np.testing.assert_array_equal(gq, rq)
+    np.testing.assert_array_equal(gs[:len(rs)], rs)
+    assert (gs[len(rs):] == 0xAB).all()  # blocks past the last one are not written
+    # Dequantised: exactly the oracle's grouped round trip.
+    deq = np.zeros((rows, cols))
+    b = 0
+    for g in range(len(sizes)):
+        lo, hi = off[g], off[g + 1]
+        for r0 in range(lo, hi, 32):
+            r1 = min(r0 + 32, hi)
+            deq[r0:r1] = O.e4m3_decode(gq[r0:r1]) * O.e8m0_decode(gs[b])[None, :]
+            b += 1
+    np.testing.assert_array_equal(deq, O.mx_rows_grouped(x, off))
