@@ -267,6 +267,10 @@ def main():
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": load_traffic(wl.name, dom)},
     }
+    # Expert-load diagnostics of the last step's routing (moe_load_stats, after
+    # the timed region).
+    stats = layer.load_stats().cpu().tolist()
+    out["expert_load"] = {n: round(v, 4) for n, v in zip(M.LOAD_STATS, stats)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(out), flush=True)

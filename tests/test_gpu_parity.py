@@ -41,6 +41,12 @@ CASES = {
     # Eight experts get no rows.
     "bf16_wgrad_stream_short_tiles": ("bf16_zipf", dict(T=4096, d=512, E=128, k=2, f=256),
                                       [0 if e % 16 == 5 else 1 + e % 7 for e in range(128)]),
+    # The largest expert count and top-k the library takes, learned routing:
+    # about 9 rows per expert, 16 router column blocks, eight slots per token.
+    "bf16_max_E256_k8": ("bf16_e8", dict(T=300, d=128, E=256, k=8, f=128), None),
+    # One token.
+    "bf16_single_token": ("bf16_e8", dict(T=1, d=128, E=8, k=4, f=64), None),
+    "f32_single_token_k8": ("tiny_f32", dict(T=1, E=8, k=8), None),
 }
 
 
