@@ -1,0 +1,37 @@
+"""bench.py's command-line contract on a host without a GPU: more than one
+GPU is refused with a message (this build has no multi-GPU path), and the
+algorithmic work it reports per call follows the layer's formulas."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_work_formulas():
+    import bench
+    from moe_inputs import WORKLOADS
+    wl = WORKLOADS["bf16_e8"]
+    T, d, E, k, f = wl.T, wl.d, wl.E, wl.k, wl.f
+    S = T * k
+    w = bench.algorithmic_work(wl)
+    assert w["moe_grouped_ffn_fwd"]["flops"] + w["moe_grouped_ffn_bwd"]["flops"] == 18 * S * d * f
+    assert w["moe_dispatch"]["bytes"] == (1 + k) * T * d * 2
+    assert w["moe_combine_bwd"]["bytes"] == (1 + 2 * k) * T * d * 2
+    assert w["moe_route"]["flops"] == 2 * T * d * E
+    mx = bench.algorithmic_work(WORKLOADS["mxfp8_balanced"])
+    wm = WORKLOADS["mxfp8_balanced"]
+    Sm = wm.T * wm.k
+    # the MXFP8 images of xp and d_o: one byte per element plus one per 32
+    assert mx["moe_dispatch"]["bytes"] == (1 + wm.k) * wm.T * wm.d * 2 + Sm * wm.d + Sm * wm.d // 32
+    assert "moe_route" not in mx
+    rc = bench.algorithmic_work(wl, recompute=True)
+    assert rc["moe_grouped_ffn_bwd"]["flops_recompute"] == 4 * S * d * f
