@@ -67,6 +67,22 @@ def algorithmic_work(wl, recompute=False):
     return work
 
 
+def gemm_compulsory_bytes(wl):
+    """HBM bytes the two grouped-FFN calls cannot avoid in one forward+backward
+    (bf16 and fp32 layers; every tensor read or written once per use):
+    forward   read Xp, W_gate, W_up, W_down, H (down GEMM); write G, U, H, O;
+    backward  read dO, G, U, the three weights, dG|dU (gate/up dgrad), H and
+              dO (dW_down), Xp and dG|dU (dW_gate|dW_up); write dG|dU, dXp and
+              the three weight gradients."""
+    T, d, E, k, f = wl.T, wl.d, wl.E, wl.k, wl.f
+    S, b = T * k, (4 if wl.dtype == "f32" else 2)
+    W = 3 * E * d * f
+    fwd = S * d + W + S * f + 3 * S * f + S * d
+    bwd = (S * d + 2 * S * f + W + 2 * S * f + S * f + S * d + S * d + 2 * S * f
+           + 2 * S * f + S * d + W)
+    return (fwd + bwd) * b
+
+
 def cpu_baseline(wl, inp, budget_s: float = 20.0):
     """The fp64 oracle (as it stands) on the same workload, on the host cores.
 
@@ -233,6 +249,16 @@ def main():
     dc_bytes = sum(work[n]["bytes"] for n in dc_names)
     dc_ms = sum(avg_ms[n] for n in dc_names)
 
+    # Against the combined roofline max(flops / MFMA peak, compulsory bytes /
+    # HBM peak) of the two FFN calls (bf16 and fp32 layers: the MXFP8 calls
+    # also quantise, which this count does not model).
+    gemm_roof = None
+    if wl.dtype != "mxfp8":
+        gbytes = gemm_compulsory_bytes(wl)
+        floor_ms = max(gemm_flops / (peak * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+        gemm_roof = {"compulsory_bytes": gbytes, "floor_ms": round(floor_ms, 4),
+                     "bound": "mfma" if gemm_flops / (peak * 1e12) >= gbytes / (PEAK_HBM_GBS * 1e9) else "hbm",
+                     "frac": round(floor_ms / gemm_ms, 4)}
     dom = max(("moe_grouped_ffn_fwd", "moe_grouped_ffn_bwd"), key=lambda n: avg_ms[n])
     achieved = work[dom]["flops"] / (avg_ms[dom] * 1e-3) / 1e12
     ms_per_step = elapsed / args.steps * 1e3
@@ -258,7 +284,8 @@ def main():
                         "o": layer.o.numel() * layer.o.element_size(),
                         "xp_mx": 0 if layer.xp_mx is None else layer.xp_mx.numel()},
         "grouped_gemm": {"tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / peak, 4),
-                         "peak_tflops": peak, "ms": round(gemm_ms, 4)},
+                         "peak_tflops": peak, "ms": round(gemm_ms, 4), "combined_roofline": gemm_roof},
+
         "dispatch_combine": {"gbs": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
                              "frac_of_hbm": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                              "ms": round(dc_ms, 4)},

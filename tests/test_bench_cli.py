@@ -35,3 +35,16 @@ def test_algorithmic_work_formulas():
     assert "moe_route" not in mx
     rc = bench.algorithmic_work(wl, recompute=True)
     assert rc["moe_grouped_ffn_bwd"]["flops_recompute"] == 4 * S * d * f
+
+
+def test_gemm_combined_roofline_floors():
+    """The 128-expert layer's grouped GEMMs are HBM-bound (floor 0.814 ms: the
+    weights read twice and their gradients written, plus activations) while
+    the 8-expert layer's are MFMA-bound (0.495 ms)."""
+    import bench
+    from moe_inputs import WORKLOADS
+    e8, e128 = WORKLOADS["bf16_e8"], WORKLOADS["bf16_e128"]
+    fl = 18 * e8.T * e8.k * e8.d * e8.f
+    assert abs(fl / 2.5e15 * 1e3 - 0.4948) < 1e-3
+    assert bench.gemm_compulsory_bytes(e8) / 8e12 < fl / 2.5e15
+    assert abs(bench.gemm_compulsory_bytes(e128) / 8e12 * 1e3 - 0.8137) < 1e-3
