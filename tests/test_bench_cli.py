@@ -1,5 +1,5 @@
 """bench.py's command-line contract on a host without a GPU: more than one
-GPU is refused with a message (this build has no multi-GPU path), and the
+GPU is refused with a message (the library has no multi-GPU path), and the
 algorithmic work it reports per call follows the layer's formulas."""
 import os
 import subprocess
