@@ -298,6 +298,25 @@ def main():
     # the timed region).
     stats = layer.load_stats().cpu().tolist()
     out["expert_load"] = {n: round(v, 4) for n, v in zip(M.LOAD_STATS, stats)}
+    # Cold caches: before each of K further steps a 1 GiB fill (untimed)
+    # evicts the 256 MB MALL and the L2s; the step is timed by events around
+    # it alone. The timed region above runs with the caches as the previous
+    # step left them (warm).
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    cold_ms = sorted(a.elapsed_time(b) for a, b in cold)
+    med = cold_ms[len(cold_ms) // 2]
+    out["cold_cache"] = {"ms_per_step_median": round(med, 4), "tokens_per_s": round(wl.T / (med * 1e-3), 1),
+                         "flush_bytes": 1 << 30}
+    del flush
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(out), flush=True)
