@@ -38,6 +38,9 @@ CASES = {
     "zipf_ragged_empty": ("bf16_zipf", dict(T=384, d=256, E=16, f=128, dtype="mxfp8"),
                           [1, 0, 2, 1, 1, 0, 3, 1, 1, 1, 0, 1, 2, 1, 1, 0]),
     "wide_tiles": ("mxfp8_balanced", dict(T=1024, d=512, E=4, f=512), None),
+    # The largest expert count and top-k: 16 rows per expert, each padded to
+    # 64 in the weight-gradient layouts.
+    "max_E256_k8": ("mxfp8_balanced", dict(T=512, d=128, E=256, k=8, f=128), None),
 }
 
 
