@@ -11,14 +11,17 @@
 //
 // Forward: a workgroup takes 16 tokens; its 4 waves split K, each computes
 // 16 x E16 partial logits (E16 = E rounded up to 16 x a power of two) from x
-// rows and a transposed, zero-padded router weight W_r^T [E16][d] (written by
-// router_wt_kernel into the workspace), then the partials are added in wave
+// rows and a transposed, zero-padded router weight W_r^T (written by
+// router_wt_kernel into the workspace, fragment-major like the dl^T terms
+// below: one contiguous kilobyte per 16 experts x 32 k step), then the partials are added in wave
 // order in LDS, written out as fp32 logits, and each wave selects the top-k of
 // 4 tokens with the rule of topk.h.
 //
 // Backward: dlogits (fp32, [T][E]) and its transpose split into two bf16
 // terms, hi = bf16(dl) and lo = bf16(dl - hi), so the bf16 MFMA sees dl to
-// about 16 bits. dW_r^T's partial over a chunk of 256 tokens and 64 columns of
+// about 16 bits. The two terms are stored fragment-major: the 16 x 32 block
+// (16 experts, 32 tokens) one MFMA step reads is 1 KB, lane l's 16 bytes at
+// 16 l, so each operand load is one contiguous kilobyte. dW_r^T's partial over a chunk of 256 tokens and 64 columns of
 // d is one workgroup: the x tile [256 tok][64 col] is staged in LDS by DMA
 // and read transposed (ds_read_b64_tr_b16) as the MFMA's row operand; the
 // per-chunk partials are summed over chunks in order (deterministic).
@@ -41,11 +44,17 @@ int pow2_blocks(int E) {
   return eb;  // E16 = 16 * eb
 }
 
-// W_r [d][E] -> W_rT [E16][d], rows >= E zero.
+// W_r [d][E] -> W_r^T fragment-major, experts >= E zero: element i is
+// expert 16 eb + (i / 8) % 16, row 32 s + 8 ((i / 128) % 4) + i % 8 of W_r,
+// with eb, s = (i / 512) / (d / 32), (i / 512) % (d / 32): the MFMA operand
+// of lane (i / 8) % 64 in k step s for experts 16 eb .. 16 eb + 15.
 __global__ void router_wt_kernel(const bf16_t* __restrict__ w, int d, int E, int E16, bf16_t* __restrict__ wt) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<int64_t>(E16) * d) return;
-  const int e = static_cast<int>(i / d), r = static_cast<int>(i % d);
+  const int ln = static_cast<int>((i >> 3) & 63), ns = d >> 5;
+  const int blk = static_cast<int>(i >> 9);
+  const int e = (blk / ns) * 16 + (ln & 15);
+  const int r = (blk % ns) * 32 + 8 * (ln >> 4) + static_cast<int>(i & 7);
   wt[i] = e < E ? w[static_cast<int64_t>(r) * E + e] : static_cast<bf16_t>(0);
 }
 
@@ -55,14 +64,18 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const bf16_t* __restric
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_gate) {
   constexpr int E16 = EB * 16;
-  constexpr int U = EB >= 16 ? 1 : 16 / EB;  // k steps in flight per wave
+  // k steps in flight per wave: every load of a group is issued before its
+  // first MFMA (the scheduler would otherwise interleave them and keep only
+  // a third of the group in flight).
+  constexpr int U = EB >= 16 ? 1 : (EB == 8 ? 4 : 16 / EB);
   __shared__ float buf[16][E16 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * 16;
   // MFMA operands: lane -> row (token) / column (expert) lane%16, k = 8 (lane/16) .. +7.
   const int row = min(t0 + (lane & 15), T - 1);  // rows past T are computed and dropped
   const bf16_t* xr = x + static_cast<int64_t>(row) * d + 8 * (lane >> 4);
-  const bf16_t* wr = wt + static_cast<int64_t>(lane & 15) * d + 8 * (lane >> 4);
+  const bf16_t* wr = wt + 8 * lane;  // k step s of expert block eb: 512 (eb d / 32 + s) elements on
+  const int64_t wstep = static_cast<int64_t>(d >> 5) * 512;
   floatx4 acc[EB];
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) acc[eb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -75,8 +88,9 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const bf16_t* __restric
       a[u] = *reinterpret_cast<const bf16x8*>(xr + (s + 4 * u) * 32);
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb)
-        b[u][eb] = *reinterpret_cast<const bf16x8*>(wr + static_cast<int64_t>(eb) * 16 * d + (s + 4 * u) * 32);
+        b[u][eb] = *reinterpret_cast<const bf16x8*>(wr + eb * wstep + (s + 4 * u) * 512);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -87,7 +101,7 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const bf16_t* __restric
     const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + s * 32);
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(wr + static_cast<int64_t>(eb) * 16 * d + s * 32);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(wr + eb * wstep + s * 512);
       acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[eb], 0, 0, 0);
     }
   }
@@ -132,14 +146,20 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const bf16_t* __restric
 }
 
 // dlogits[t][e] = g_te (dgate_te - sum_j g_tj dgate_tj) on the chosen set,
-// else 0; plus dl^T as two bf16 terms [E16][Tp] (zero for e >= E or t >= T).
+// else 0; plus dl^T as two bf16 terms (zero for e >= E or t >= T). Element
+// i of a term is expert e = 16 eb + (i / 8) % 16, token t = 32 ks + 8 ((i / 128) % 4) + i % 8,
+// with eb, ks = (i / 512) / (Tp / 32), (i / 512) % (Tp / 32): the operand
+// of lane (i / 8) % 64 in MFMA step ks for experts 16 eb .. 16 eb + 15.
 __global__ void dlogits_split_kernel(const int32_t* __restrict__ idx, const float* __restrict__ gate,
                                      const float* __restrict__ dgate, int T, int Tp, int E, int E16, int k,
                                      float* __restrict__ dl, bf16_t* __restrict__ dlt_hi,
                                      bf16_t* __restrict__ dlt_lo) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<int64_t>(Tp) * E16) return;
-  const int e = static_cast<int>(i / Tp), t = static_cast<int>(i % Tp);
+  const int ln = static_cast<int>((i >> 3) & 63), nks = Tp >> 5;
+  const int64_t blk = i >> 9;
+  const int e = static_cast<int>(blk / nks) * 16 + (ln & 15);
+  const int t = static_cast<int>(blk % nks) * 32 + 8 * (ln >> 4) + static_cast<int>(i & 7);
   float out = 0.0f;
   if (t < T && e < E) {
     const int32_t* it = idx + static_cast<int64_t>(t) * k;
@@ -192,7 +212,10 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restr
   const int dc0 = blockIdx.x * 64, tc0 = blockIdx.y * kTokChunk;
   const int cw = wave * 16;                 // this wave's 16 columns of the tile
   const int g = lane >> 4, sl = lane & 15;  // 16-lane group, lane inside it
-  const int64_t brow = static_cast<int64_t>(sl) * Tp + tc0 + 8 * g;
+  // dl^T operands: step kk of expert block eb is the kilobyte at
+  // 512 (eb Tp / 32 + tc0 / 32 + kk) elements; this lane's 8 at 8 lane.
+  const int64_t fbase = (static_cast<int64_t>(tc0 >> 5) * 64 + lane) * 8;
+  auto dl_off = [&](int eb, int kk) { return fbase + (static_cast<int64_t>(eb) * (Tp >> 5) + kk) * 512; };
   {
     const int valid = max(0, min(kTokChunk, T - tc0));  // rows past T read as zero
     const int64_t bytes = static_cast<int64_t>(valid) * d * 2;
@@ -218,7 +241,7 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restr
     for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
       for (int kk = 0; kk < kSteps; ++kk) {
-        const int64_t o = static_cast<int64_t>(eb) * 16 * Tp + brow + kk * 32;
+        const int64_t o = dl_off(eb, kk);
         pre_h[eb][kk] = *reinterpret_cast<const bf16x8*>(dlt_hi + o);
         pre_l[eb][kk] = *reinterpret_cast<const bf16x8*>(dlt_lo + o);
       }
@@ -229,8 +252,30 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restr
   floatx4 acc[EB];
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) acc[eb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Without the prefetch, step kk + 1's dl^T operands are requested before
+  // step kk's MFMAs, so each step waits on loads issued one step earlier.
+  bf16x8 nx_h[kPrefetch ? 1 : EB], nx_l[kPrefetch ? 1 : EB];
+  auto load_dl = [&](int kk) {
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) {
+      const int64_t o = dl_off(eb, kk);
+      nx_h[eb] = *reinterpret_cast<const bf16x8*>(dlt_hi + o);
+      nx_l[eb] = *reinterpret_cast<const bf16x8*>(dlt_lo + o);
+    }
+  };
+  if constexpr (!kPrefetch) load_dl(0);
 #pragma unroll
   for (int kk = 0; kk < kSteps; ++kk) {
+    bf16x8 cu_h[kPrefetch ? 1 : EB], cu_l[kPrefetch ? 1 : EB];
+    if constexpr (!kPrefetch) {
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) {
+        cu_h[eb] = nx_h[eb];
+        cu_l[eb] = nx_l[eb];
+      }
+      if (kk + 1 < kSteps) load_dl(kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // Row operand = x^T: lane -> column cw + lane%16, tokens 32 kk + 8 g .. +7.
     v4s h[2];
 #pragma unroll
@@ -249,9 +294,8 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restr
         bh = pre_h[eb][kk];
         bl = pre_l[eb][kk];
       } else {
-        const int64_t o = static_cast<int64_t>(eb) * 16 * Tp + brow + kk * 32;
-        bh = *reinterpret_cast<const bf16x8*>(dlt_hi + o);
-        bl = *reinterpret_cast<const bf16x8*>(dlt_lo + o);
+        bh = cu_h[eb];
+        bl = cu_l[eb];
       }
       acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[eb], 0, 0, 0);
       acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[eb], 0, 0, 0);
