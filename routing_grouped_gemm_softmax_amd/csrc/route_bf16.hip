@@ -79,16 +79,18 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const bf16_t* __restric
   floatx4 acc[EB];
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) acc[eb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int nsteps = d / 32;
-  int s = wave;
-  for (; s + 4 * (U - 1) < nsteps; s += 4 * U) {
+  // Wave w takes the w-th quarter of the k steps, so a row's consecutive
+  // 64-byte pieces are read by one wave, back to back.
+  const int nsteps = d / 32, s_hi = nsteps * (wave + 1) / 4;
+  int s = nsteps * wave / 4;
+  for (; s + U <= s_hi; s += U) {
     bf16x8 a[U], b[U][EB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      a[u] = *reinterpret_cast<const bf16x8*>(xr + (s + 4 * u) * 32);
+      a[u] = *reinterpret_cast<const bf16x8*>(xr + (s + u) * 32);
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb)
-        b[u][eb] = *reinterpret_cast<const bf16x8*>(wr + eb * wstep + (s + 4 * u) * 512);
+        b[u][eb] = *reinterpret_cast<const bf16x8*>(wr + eb * wstep + (s + u) * 512);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const bf16_t* __restric
       for (int eb = 0; eb < EB; ++eb)
         acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][eb], acc[eb], 0, 0, 0);
   }
-  for (; s < nsteps; s += 4) {
+  for (; s < s_hi; ++s) {
     const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + s * 32);
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb) {
