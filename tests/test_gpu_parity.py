@@ -44,6 +44,10 @@ CASES = {
     # The largest expert count and top-k the library takes, learned routing:
     # about 9 rows per expert, 16 router column blocks, eight slots per token.
     "bf16_max_E256_k8": ("bf16_e8", dict(T=300, d=128, E=256, k=8, f=128), None),
+    # The router at wider d: a ragged last block of 16 tokens at d = 512, and
+    # d = 4096 with eight 16-expert blocks (32 k steps per wave).
+    "bf16_router_ragged_d512": ("bf16_e8", dict(T=300, d=512, E=8, k=2, f=128), None),
+    "bf16_router_d4096_E128": ("bf16_e128", dict(T=77, d=4096, E=128, f=64), None),
     # One token.
     "bf16_single_token": ("bf16_e8", dict(T=1, d=128, E=8, k=4, f=64), None),
     "f32_single_token_k8": ("tiny_f32", dict(T=1, E=8, k=8), None),
