@@ -15,7 +15,7 @@
 // router_wt_kernel into the workspace, fragment-major like the dl^T terms
 // below: one contiguous kilobyte per 16 experts x 32 k step), then the partials are added in wave
 // order in LDS, written out as fp32 logits, and each wave selects the top-k of
-// 4 tokens with the rule of topk.h.
+// its 4 tokens at once (16 lanes per token) with the rule of topk.h.
 //
 // Backward: dlogits (fp32, [T][E]) and its transpose split into two bf16
 // terms, hi = bf16(dl) and lo = bf16(dl - hi), so the bf16 MFMA sees dl to
@@ -121,31 +121,30 @@ __global__ __launch_bounds__(256) void router_fwd_kernel(const bf16_t* __restric
     }
     __syncthreads();
   }
-  // Logits out, then top-k and gates: wave w takes tokens 4w .. 4w+3.
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int ti = wave * 4 + q4, t = t0 + ti;
-    if (t >= T) break;
-    float v[4];
-    bool live[4];
+  // Logits out, then top-k and gates: wave w takes tokens 4w .. 4w+3 in
+  // parallel, 16 lanes each; lane l holds experts 16 q + l % 16.
+  const int ti = wave * 4 + (lane >> 4), t = t0 + ti, sub = lane & 15;
+  float v[EB];
+  bool live[EB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = q * 64 + lane;
-      live[q] = e < E;
-      v[q] = live[q] ? buf[ti][e] : 0.0f;
-      if (live[q]) logits[static_cast<int64_t>(t) * E + e] = v[q];
-    }
-    float sel_v[8], g[8];
-    int sel_i[8];
-    wave_topk(v, live, k, lane, sel_v, sel_i);
-    topk_gates(sel_v, k, g);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k && lane == j) {
-        topk_idx[static_cast<int64_t>(t) * k + j] = sel_i[j];
-        topk_gate[static_cast<int64_t>(t) * k + j] = g[j];
-      }
+  for (int q = 0; q < EB; ++q) {
+    const int e = 16 * q + sub;
+    live[q] = e < E;  // tokens past T are selected for and not stored
+    v[q] = live[q] ? buf[ti][e] : 0.0f;
+    if (live[q] && t < T) logits[static_cast<int64_t>(t) * E + e] = v[q];
   }
+  float sel_v[8], g[8];
+  int sel_i[8];
+  group16_topk(v, live, k, lane, sel_v, sel_i);
+  topk_gates(sel_v, k, g);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < k && sub == j && t < T) {
+      topk_idx[static_cast<int64_t>(t) * k + j] = sel_i[j];
+      topk_gate[static_cast<int64_t>(t) * k + j] = g[j];
+    }
 }
+
 
 // dlogits[t][e] = g_te (dgate_te - sum_j g_tj dgate_tj) on the chosen set,
 // else 0; plus dl^T as two bf16 terms (zero for e >= E or t >= T). Element

@@ -42,6 +42,38 @@ __device__ __forceinline__ void wave_topk(float (&v)[4], bool (&live)[4], int k,
   }
 }
 
+// The same rule over 16-lane groups, one token per group: lane l holds
+// v[q], live[q] of expert 16 q + l % 16 (E <= 16 NQ). Each lane first takes
+// its best (ascending q, strict >), then four merges across the group. The
+// order (larger value, then lower index) is total for non-NaN logits, so the
+// choice equals wave_topk's.
+template <int NQ>
+__device__ __forceinline__ void group16_topk(const float (&v)[NQ], bool (&live)[NQ], int k, int lane,
+                                             float (&sel_v)[8], int (&sel_i)[8]) {
+  const int sub = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    float bv = 0.0f;
+    int bi = -1;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (live[q] && (bi < 0 || v[q] > bv)) { bv = v[q]; bi = 16 * q + sub; }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 16);
+      const int oi = __shfl_xor(bi, o, 16);
+      const bool take = (oi >= 0) && (bi < 0 || ov > bv || (ov == bv && oi < bi));
+      if (take) { bv = ov; bi = oi; }
+    }
+    sel_v[j] = bv;
+    sel_i[j] = bi;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (bi == 16 * q + sub) live[q] = false;
+  }
+}
+
 // Softmax over the chosen logits (sel_v[0] is the largest).
 __device__ __forceinline__ void topk_gates(const float (&sel_v)[8], int k, float (&g)[8]) {
   float ex[8], sum = 0.0f;
