@@ -430,22 +430,12 @@ def mx_dequantize(codes, scales, along: str = "cols") -> np.ndarray:
 # then exact on the dequantised values (accumulation in fp64 here). For the
 # weight gradients the reduction runs over one expert's tokens, so those
 # operands are blocked along the rows inside each expert's range, the range
-# zero-padded to a multiple of 32. Elementwise steps (SwiGLU and its
-# derivative) use the unquantised GEMM results. A computed operand (H, dO,
-# dG, dU) is stored in bf16 by the layer and quantised from that stored
-# value: the E4M3 codes are integers decided in floating point, taken here in
-# the same precision as on the device (bf16_rne, then quantise); for the same
-# reason the backward's SwiGLU derivative reads G and U as stored (bf16).
+# zero-padded to a multiple of 32. Every quantised operand is taken at its
+# exact value: the inputs as stored, the computed operands (H, dO, dG, dU)
+# exactly as the definition gives them (fp64, never rounded to a storage
+# type first); the elementwise steps (SwiGLU and its derivative) use the
+# exact GEMM results.
 # --------------------------------------------------------------------------
-
-def bf16_rne(a) -> np.ndarray:
-    """Nearest bf16 value of each element (round to nearest, ties to even),
-    via fp32 as a device that rounds an fp32 accumulator does."""
-    f = np.ascontiguousarray(_f64(a).astype(np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).astype(F64)
-
 
 def mx_roundtrip(a, along: str) -> np.ndarray:
     """Exact fp64 value of a after MXFP8 quantisation in blocks of 32 along
@@ -473,8 +463,8 @@ def mx_rows_grouped(a, offsets) -> np.ndarray:
 def ffn_forward_mx(xp, w_gate, w_up, w_down, offsets, h_in=None):
     """ffn_forward with MXFP8 GEMM operands: Xp and H along the row (K = d,
     f), W_gate, W_up along d and W_down along f (down their columns).
-    The down GEMM quantises bf16_rne(H), or h_in if given (comparing stage
-    by stage feeds the device's own stored H).
+    The down GEMM quantises the exact H, or h_in if given (a stage-by-stage
+    comparison feeds a device's own stored H).
     Returns (G, U, H, O)."""
     E = len(offsets) - 1
     xq = mx_roundtrip(xp, "cols")
@@ -487,7 +477,7 @@ def ffn_forward_mx(xp, w_gate, w_up, w_down, offsets, h_in=None):
         G[a:b] = xq[a:b] @ mx_roundtrip(w_gate[e], "rows")
         U[a:b] = xq[a:b] @ mx_roundtrip(w_up[e], "rows")
         H[a:b] = G[a:b] * sigmoid(G[a:b]) * U[a:b]
-    hq = mx_roundtrip(bf16_rne(H) if h_in is None else h_in, "cols")
+    hq = mx_roundtrip(H if h_in is None else h_in, "cols")
     O = np.zeros((S, np.shape(w_down)[2]))
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
@@ -501,29 +491,30 @@ def ffn_backward_mx(d_o, xp, w_gate, w_up, w_down, offsets, G, U, H, dgdu_in=Non
     dH = q(dO) q(W_down)^T (both along d); dXp = q(dG) q(W_gate)^T +
     q(dU) q(W_up)^T (along f); dW_down = q(H)^T q(dO), dW_gate = q(Xp)^T
     q(dG), dW_up = q(Xp)^T q(dU), each along the expert's tokens.
-    dO, dG, dU, H are quantised from their bf16 values, and the SwiGLU
-    derivative reads G, U as stored (bf16); dgdu_in, if given,
-    replaces (bf16 dG, bf16 dU) for the later GEMMs (stage-by-stage
-    comparison with the device's own stored values).
+    dO, dG, dU and H are quantised at the values given (the exact ones
+    from ffn_forward_mx and combine_backward), and the SwiGLU derivative
+    reads G and U as given; dgdu_in, if given, replaces (dG, dU) for the
+    later GEMMs (a stage-by-stage comparison feeds a device's own stored
+    values).
     Returns (dXp, dW_gate, dW_up, dW_down, dG, dU)."""
     E = len(offsets) - 1
     S, d = np.shape(xp)
     f = np.shape(w_gate)[2]
-    d_o16 = bf16_rne(d_o)
-    doq = mx_roundtrip(d_o16, "cols")
+    d_o = _f64(d_o)
+    doq = mx_roundtrip(d_o, "cols")
     dG = np.zeros((S, f)); dU = np.zeros((S, f))
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if a == b:
             continue
-        g, u = bf16_rne(G[a:b]), bf16_rne(U[a:b])   # as stored by the forward
+        g, u = _f64(G[a:b]), _f64(U[a:b])
         s = sigmoid(g)
         dh = doq[a:b] @ mx_roundtrip(w_down[e], "cols").T
         dU[a:b] = dh * g * s
         dG[a:b] = dh * u * s * (1.0 + g * (1.0 - s))
-    dg_in, du_in = (bf16_rne(dG), bf16_rne(dU)) if dgdu_in is None else dgdu_in
+    dg_in, du_in = (dG, dU) if dgdu_in is None else dgdu_in
     dgq, duq = mx_roundtrip(dg_in, "cols"), mx_roundtrip(du_in, "cols")
-    hg, dog = mx_rows_grouped(bf16_rne(H), offsets), mx_rows_grouped(d_o16, offsets)
+    hg, dog = mx_rows_grouped(H, offsets), mx_rows_grouped(d_o, offsets)
     xg, dgg, dug = mx_rows_grouped(xp, offsets), mx_rows_grouped(dg_in, offsets), mx_rows_grouped(du_in, offsets)
     dxp = np.zeros((S, d))
     dwg = np.zeros((E, d, f)); dwu = np.zeros((E, d, f)); dwd = np.zeros((E, f, np.shape(w_down)[2]))
