@@ -43,7 +43,10 @@
  *    offsets and the permutation never leave the device.
  *  - Tensors are dense row-major. Sizes are int64_t. Floating tensors are in
  *    the layer dtype `shape->dtype` (MOE_F32 or MOE_BF16; MXFP8 layers keep
- *    bf16 master tensors) unless the argument says fp32. Weights:
+ *    bf16 inputs and outputs) unless the argument says fp32. MXFP8 layers
+ *    keep their computed GEMM operands in fp32 (G, U, H in the save buffer,
+ *    d_o, dG | dU in the backward workspace), so that every E4M3 code is
+ *    decided on the fp32 value rather than on a bf16 rounding of it. Weights:
  *    w_router [d][E]; w_gate, w_up [E][d][f]; w_down [E][f][d].
  *  - Row counts: S = T*k routed rows. Index tensors are int32.
  *  - Validation is host-side only and never reads device memory. Errors:
@@ -69,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum moe_status {
   MOE_OK = 0,
@@ -129,19 +132,20 @@ const char* moe_last_error_message(void);
 size_t moe_workspace_size(int op, const moe_shape* shape);
 
 /* Bytes of the buffer that moe_grouped_ffn_fwd fills with what the backward
- * needs: G, U, H (three [S][f] tensors in the layer dtype, bf16 for MXFP8
+ * needs: G, U, H (three [S][f] tensors in the layer dtype, fp32 for MXFP8
  * layers) and, for MXFP8 layers, the E4M3 copies (with their E8M0 scales) of
  * w_gate, w_up and w_down in the layouts of the backward's dgrad GEMMs, which
  * the forward writes from the same read that quantises its own copies.
  * 0 with MOE_FLAG_RECOMPUTE (then `save` may be NULL in the FFN calls). */
 size_t moe_save_size(const moe_shape* shape);
 
-/* Bytes of the MXFP8 image of a bf16 matrix [rows][cols] quantised along
+/* Bytes of the MXFP8 image of a matrix [rows][cols] quantised along
  * cols (cols % 64 == 0), in the layout the MXFP8 grouped GEMMs read their
  * row operand in: rows*cols E4M3 codes, row-major; then the E8M0 scales as
  * [cols/64][rows][2] (the two 32-blocks of each 64-column piece of a row side
  * by side). Each part starts 256-byte aligned and is followed by at least 16
- * bytes of slack. Codes and scales are those of mxfp8_quantize with axis 0.
+ * bytes of slack. Codes and scales are those of mxfp8_quantize with axis 0
+ * (the OCP MX v1.0 conversion) of the values the image is made from.
  * moe_dispatch and moe_combine_bwd write the images of xp and d_o ([S][d])
  * for MXFP8 layers, and the grouped FFN calls read them, so neither row
  * matrix is read again only to be quantised. Returns (size_t)-1 for
@@ -211,9 +215,14 @@ int moe_combine(const void* o, const float* topk_gate, const int32_t* row_of_slo
                 const moe_shape* shape, void* y_out, void* stream);
 
 /* Combine backward: d_o[row_of_slot[t,j]] = topk_gate[t,j] * dy[t] (layer
- * dtype) and dgate[t,j] (fp32) = <dy[t], o[row_of_slot[t,j]]>.
+ * dtype; fp32 for MXFP8 layers, the fp32 product) and dgate[t,j] (fp32) =
+ * <dy[t], o[row_of_slot[t,j]]>, summed in fp32.
  * d_o_mx_out (MXFP8 layers only; NULL to skip): receives the MXFP8 image of
- * the stored (bf16) d_o, moe_mx_image_size(S, d) bytes, 256-byte aligned. */
+ * the stored fp32 d_o, moe_mx_image_size(S, d) bytes, 256-byte aligned.
+ * Passage: the gate-weighted combine of the layer specification ("a
+ * gate-weighted combine back to token order", forward and backward); the
+ * MXFP8 image is the data moved to the experts in MXFP8 (unite.ai page,
+ * "Parallelismo, precisione e tecniche di memoria"). */
 int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
                     const int32_t* row_of_slot, const moe_shape* shape, void* d_o_out,
                     uint8_t* d_o_mx_out, float* dgate_out, void* stream);
@@ -224,9 +233,17 @@ int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
  *   dxp = dG · w_gate[e]^T + dU · w_up[e]^T
  *   dw_down[e] = H^T · d_o;  dw_gate[e] = xp^T · dG;  dw_up[e] = xp^T · dU
  * Weight gradients of experts with no rows are written as zeros. All outputs
- * in the layer dtype. ws: moe_workspace_size(MOE_OP_FFN_BWD) bytes.
+ * in the layer dtype (d_o is fp32 for MXFP8 layers, as moe_combine_bwd
+ * writes it). ws: moe_workspace_size(MOE_OP_FFN_BWD) bytes; it starts with
+ * the dG | dU rows ([S][2f], fp32 for MXFP8 layers, else the layer dtype).
+ * MXFP8 layers quantise every operand along its GEMM's K (the weight
+ * gradients along each expert's tokens, the range padded with zero rows).
  * d_o_mx (MXFP8 layers only; NULL = quantise d_o here): the MXFP8 image of
- * d_o that moe_combine_bwd wrote. */
+ * d_o that moe_combine_bwd wrote.
+ * Passage: the backward of the expert FFN (dgrad and wgrad grouped GEMMs) of
+ * the layer specification; the grouped, device-scheduled GEMM of the
+ * bytechap.com page, "Cómo funciona", and of the unite.ai page,
+ * "Parallelismo, precisione e tecniche di memoria". */
 int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, const void* w_gate,
                         const void* w_up, const void* w_down, const int32_t* offsets,
                         const moe_shape* shape,
@@ -301,6 +318,32 @@ int mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, int axis, ui
  * ranges of the grouped GEMM (bytechap.com page, "Cómo funciona"). */
 int mxfp8_quantize_grouped(const void* in_bf16, int64_t rows, int64_t cols, const int32_t* group_offsets,
                            int64_t groups, uint8_t* q_out, uint8_t* scale_out, void* stream);
+
+/* Grouped-GEMM steps of the expert FFN, for moe_kernel_timer. */
+enum moe_gemm_mode {
+  MOE_GEMM_FWD_GU = 0,   /* G, U = xp w_gate, xp w_up; H = silu(G) U   */
+  MOE_GEMM_FWD_DOWN = 1, /* o = H w_down                                */
+  MOE_GEMM_BWD_DOWN = 2, /* dG | dU from d_o w_down^T and the saved G, U */
+  MOE_GEMM_BWD_GU = 3,   /* dxp = [dG | dU] [w_gate | w_up]^T           */
+  MOE_GEMM_WGRAD = 4     /* dw_down, then [dw_gate | dw_up]: two launches per backward */
+};
+
+/* Kernel timing for benchmarks: brackets each of the next launches of one
+ * grouped-GEMM step (gemm_mode, any layer dtype) with HIP events that the
+ * caller created, recorded on the stream that step runs on, so that each
+ * launch's duration can be read with hipEventElapsedTime. start and stop are
+ * host arrays of `capacity` hipEvent_t handles; launches past `capacity` are
+ * not recorded. Where a step runs as a main launch plus a short quarter-tile
+ * launch (a small last round of tiles), one event pair brackets both.
+ * capacity 0 (start and stop may then be NULL) disarms the timer. Returns
+ * MOE_OK or MOE_ERR_INVALID_ARG (mode out of range, capacity < 0, NULL
+ * arrays). Process-wide state: arm, run and read from one thread.
+ * For the profiling of this library's own kernels; it is not part of the
+ * layer's computation. */
+int moe_kernel_timer(int gemm_mode, void* const* start, void* const* stop, int capacity);
+
+/* Event pairs recorded since moe_kernel_timer last armed the timer. */
+int moe_kernel_timer_count(void);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
  MOE_OP_ROUTE_BWD, MOE_OP_DISPATCH_BWD) = range(6)
 MOE_DEV_BAD_EXPERT = 1
 MOE_FLAG_RECOMPUTE = 1
+GEMM_MODES = ("fwd_gu", "fwd_down", "bwd_down", "bwd_gu", "wgrad")  # enum moe_gemm_mode order
 
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.bfloat16}
@@ -66,6 +67,8 @@ SIGNATURES = {
     "moe_load_stats": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
     "mxfp8_quantize_grouped": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, _P, ctypes.c_int64, _P, _P, _P]),
     "mxfp8_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P]),
+    "moe_kernel_timer": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.c_int]),
+    "moe_kernel_timer_count": (ctypes.c_int, []),
 }
 
 _lib = None
@@ -247,3 +250,21 @@ def mxfp8_quantize_grouped(x, group_offsets, q, scale, stream=None):
     _expect(scale, torch.uint8, (rows // 32 + groups) * cols, "scale")
     _check("mxfp8_quantize_grouped", load().mxfp8_quantize_grouped(
         _ptr(x), rows, cols, _ptr(group_offsets), groups, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def moe_kernel_timer(mode: int, starts=None, stops=None) -> None:
+    """Arm the kernel timer for grouped-GEMM step `mode` (GEMM_MODES index)
+    with torch.cuda.Event lists (each event must have been recorded once, so
+    that it exists); no lists disarm it."""
+    starts, stops = starts or [], stops or []
+    if len(starts) != len(stops):
+        raise ValueError("start and stop lists differ in length")
+    n = len(starts)
+    arr = (_P * max(n, 1))
+    a = arr(*[e.cuda_event for e in starts]) if n else None
+    b = arr(*[e.cuda_event for e in stops]) if n else None
+    _check("moe_kernel_timer", load().moe_kernel_timer(int(mode), a, b, n))
+
+
+def moe_kernel_timer_count() -> int:
+    return load().moe_kernel_timer_count()

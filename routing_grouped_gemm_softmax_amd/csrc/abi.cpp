@@ -2,9 +2,12 @@
 // Validation never touches device memory; on any error nothing is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -29,7 +32,11 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Bytes of an element of the layer's input and output tensors (MXFP8 layers:
+// bf16) and of its computed activations G, U, H, dO, dG | dU (MXFP8 layers
+// keep those in fp32, so every E4M3 code is decided on the fp32 value).
 int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+int act_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
 // Shape checks shared by every layer entry point.
 int check_shape(const moe_shape* s) {
@@ -92,9 +99,13 @@ int check_ffn_dtype(const moe_shape* s, const char* who) {
 
 bool recompute(const moe_shape* s) { return (s->flags & MOE_FLAG_RECOMPUTE) != 0; }
 
-// G, U, H: three [S][f] planes in the layer dtype.
+// G, U, H: three [S][f] planes (act_bytes each element).
 size_t gu_h_bytes(const moe_shape* s) {
-  return ((size_t)3 * s->T * s->k * s->f * elem_bytes(s->dtype) + 255) & ~(size_t)255;
+  return ((size_t)3 * s->T * s->k * s->f * act_bytes(s->dtype) + 255) & ~(size_t)255;
+}
+// dG | dU rows of the backward workspace: [S][2f] (act_bytes each element).
+size_t dgu_bytes_for(const moe_shape* s) {
+  return ((size_t)s->T * s->k * 2 * s->f * act_bytes(s->dtype) + 255) & ~(size_t)255;
 }
 // Saved G, U, H planes (none with recompute); MXFP8 layers add the backward's
 // quantised weight copies.
@@ -103,7 +114,38 @@ size_t save_bytes_for(const moe_shape* s) {
   return save_planes(s) + (s->dtype == MOE_MXFP8 ? moe::ffn_mx_save_extra((int)s->d, (int)s->f, (int)s->E) : 0);
 }
 
+// moe_kernel_timer's state: the armed mode (-1: none) and the caller's
+// events. The mode is read without the lock on every GEMM launch.
+struct KernelTimer {
+  std::mutex mu;
+  std::vector<hipEvent_t> start, stop;
+  int n = 0;
+};
+KernelTimer& kernel_timer() {
+  static KernelTimer t;
+  return t;
+}
+std::atomic<int> g_timer_mode{-1};
+
 }  // namespace
+
+namespace moe {
+
+void ktimer_begin(int mode, hipStream_t s) {
+  if (g_timer_mode.load(std::memory_order_acquire) != mode) return;
+  KernelTimer& t = kernel_timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (t.n < static_cast<int>(t.start.size())) (void)hipEventRecord(t.start[t.n], s);
+}
+
+void ktimer_end(int mode, hipStream_t s) {
+  if (g_timer_mode.load(std::memory_order_acquire) != mode) return;
+  KernelTimer& t = kernel_timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (t.n < static_cast<int>(t.stop.size())) (void)hipEventRecord(t.stop[t.n++], s);
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -133,7 +175,7 @@ size_t moe_workspace_size(int op, const moe_shape* s) {
       if (s->dtype == MOE_MXFP8) return moe::ffn_mx_fwd_workspace(T * k, d, f, E);
       return recompute(s) ? gu_h_bytes(s) : 0;  // recompute: G, U, H live here
     case MOE_OP_FFN_BWD: {
-      const size_t dgu = ((size_t)T * k * 2 * f * elem_bytes(s->dtype) + 255) & ~(size_t)255;  // dG|dU rows
+      const size_t dgu = dgu_bytes_for(s);  // dG|dU rows
       if (s->dtype == MOE_MXFP8) return dgu + moe::ffn_mx_bwd_workspace(T * k, d, f, E);
       return dgu + (recompute(s) ? gu_h_bytes(s) : 0);  // recompute: G, U, H after dG|dU
     }
@@ -223,7 +265,7 @@ int moe_grouped_ffn_fwd(const void* xp, const uint8_t* xp_mx, const void* w_gate
   moe::FfnArgs a{};
   a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
   a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down; a.xp_mx = xp_mx;
-  const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
+  const size_t plane = (size_t)a.S * a.f * act_bytes(s->dtype);
   char* gu_h = static_cast<char*>(recompute(s) ? ws : save);  // G, U, H
   a.G = gu_h; a.U = gu_h + plane; a.H = gu_h + 2 * plane;
   a.mx_save = static_cast<char*>(save) + save_planes(s);
@@ -254,7 +296,8 @@ int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate, const
                                       moe::mx_image(d_o_mx_out, s->T * s->k, s->d), dgate_out, as_stream(stream)));
     return MOE_OK;
   }
-  LAUNCH(moe::launch_combine_bwd(dy, o, topk_gate, row_of_slot, s->dtype == MOE_F32, (int)s->T, (int)s->d, (int)s->k,
+  const int kind = s->dtype == MOE_F32 ? 0 : (s->dtype == MOE_BF16 ? 1 : 2);
+  LAUNCH(moe::launch_combine_bwd(dy, o, topk_gate, row_of_slot, kind, (int)s->T, (int)s->d, (int)s->k,
                                  d_o_out, dgate_out, as_stream(stream)));
   return MOE_OK;
 }
@@ -274,8 +317,8 @@ int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, 
   moe::FfnArgs a{};
   a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
   a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
-  const size_t plane = (size_t)a.S * a.f * elem_bytes(s->dtype);
-  const size_t dgu_bytes = ((size_t)a.S * 2 * a.f * elem_bytes(s->dtype) + 255) & ~(size_t)255;
+  const size_t plane = (size_t)a.S * a.f * act_bytes(s->dtype);
+  const size_t dgu_bytes = dgu_bytes_for(s);
   char* sv = const_cast<char*>(static_cast<const char*>(save));
   // Recompute: G, U, H are rebuilt in the workspace, after the dG|dU rows.
   char* gu_h = recompute(s) ? static_cast<char*>(ws) + dgu_bytes : sv;
@@ -284,8 +327,7 @@ int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, 
   a.mx_save = sv + save_planes(s);
   a.d_o = d_o; a.d_o_mx = d_o_mx; a.dgu = ws; a.dxp = dxp_out; a.dw_gate = dw_gate_out; a.dw_up = dw_up_out; a.dw_down = dw_down_out;
   if (s->dtype == MOE_MXFP8) {
-    const size_t dgu = ((size_t)a.S * 2 * a.f * 2 + 255) & ~(size_t)255;
-    LAUNCH(moe::launch_ffn_mx_bwd(a, static_cast<char*>(ws) + dgu, as_stream(stream)));
+    LAUNCH(moe::launch_ffn_mx_bwd(a, static_cast<char*>(ws) + dgu_bytes, as_stream(stream)));
   } else {
     LAUNCH(moe::launch_ffn_bwd(a, s->dtype == MOE_F32, as_stream(stream)));
   }
@@ -324,6 +366,32 @@ int moe_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* d
   LAUNCH(moe::launch_dispatch_bwd(dxp, row_of_slot, dlogits, w_router, s->dtype == MOE_F32, (int)s->T, (int)s->d,
                                   (int)s->E, (int)s->k, dx_out, ws, as_stream(stream)));
   return MOE_OK;
+}
+
+int moe_kernel_timer(int gemm_mode, void* const* start, void* const* stop, int capacity) {
+  if (gemm_mode < MOE_GEMM_FWD_GU || gemm_mode > MOE_GEMM_WGRAD)
+    return fail(MOE_ERR_INVALID_ARG, "moe_kernel_timer: unknown gemm_mode %d", gemm_mode);
+  if (capacity < 0 || (capacity > 0 && (!start || !stop)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_kernel_timer: need capacity >= 0 and, above 0, both event arrays");
+  KernelTimer& t = kernel_timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  g_timer_mode.store(-1, std::memory_order_release);
+  t.start.clear();
+  t.stop.clear();
+  t.n = 0;
+  for (int i = 0; i < capacity; ++i) {
+    if (!start[i] || !stop[i]) return fail(MOE_ERR_INVALID_ARG, "moe_kernel_timer: NULL event %d", i);
+    t.start.push_back(static_cast<hipEvent_t>(start[i]));
+    t.stop.push_back(static_cast<hipEvent_t>(stop[i]));
+  }
+  if (capacity > 0) g_timer_mode.store(gemm_mode, std::memory_order_release);
+  return MOE_OK;
+}
+
+int moe_kernel_timer_count(void) {
+  KernelTimer& t = kernel_timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  return t.n;
 }
 
 int moe_load_stats(const int32_t* counts, int64_t E, double* stats_out, void* stream) {

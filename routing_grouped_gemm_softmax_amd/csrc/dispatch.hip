@@ -170,19 +170,18 @@ static int lanes_per_token(int nvec) {
   return l;
 }
 
-// Writes the MXFP8 image of one 16-byte piece (8 bf16 values, vector v of a
-// row of d = 8 * nvec values) to `rows`: E4M3 codes in q [S][d], E8M0 scales
-// in sc [d/64][S][2]. The 4 lanes holding a 32-block (lanes aligned to 4)
-// share its scale by two butterflies; the first lane of each 64-column piece
-// (8 lanes) writes both of its scale bytes. Every lane of the 8-lane group
-// must execute it.
-template <int NR>
-__device__ __forceinline__ void mx_store_piece(const uint4& val, int v, int d, const int (&rows)[NR], int nr,
-                                               uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
-  float f[8];
-  unpack16(val, f);
+// Writes the MXFP8 image of one piece of 8 values (vector v of a row of d =
+// 8 * nvec values) to `rows`: E4M3 codes in q [S][d], E8M0 scales in sc
+// [d/64][S][2]. The 4 lanes holding a 32-block (lanes aligned to 4) share its
+// scale by two butterflies; the first lane of each 64-column piece (8 lanes)
+// writes both of its scale bytes. Every lane of the 8-lane group must
+// execute it. kExact: fp32 values, encoded with the exact encoder (bf16
+// values may take the hardware conversion).
+template <int NR, bool kExact>
+__device__ __forceinline__ void mx_store_vals(const float (&f)[8], int v, int d, const int (&rows)[NR], int nr,
+                                              uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
   const int code = mx_group4_code(f);
-  const uint2 codes = mx_encode8(f, code);
+  const uint2 codes = kExact ? mx_encode8_exact(f, code) : mx_encode8(f, code);
   const int lane = threadIdx.x & (kWave - 1);
   const int code_hi = __shfl(code, (lane & ~7) + 4, kWave);
   const uint16_t sv = static_cast<uint16_t>(code | (code_hi << 8));
@@ -193,6 +192,13 @@ __device__ __forceinline__ void mx_store_piece(const uint4& val, int v, int d, c
     if ((v & 7) == 0)
       *reinterpret_cast<uint16_t*>(sc + (static_cast<int64_t>(v >> 3) * S + rows[j]) * 2) = sv;
   }
+}
+template <int NR>
+__device__ __forceinline__ void mx_store_piece(const uint4& val, int v, int d, const int (&rows)[NR], int nr,
+                                               uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
+  float f[8];
+  unpack16(val, f);
+  mx_store_vals<NR, false>(f, v, d, rows, nr, q, sc, S);
 }
 
 // xp[row_of_slot[t][j]] = x[t]: read the token row once, write it k times.
@@ -320,15 +326,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
 
 // d_o[row(t,j)] = gate[t][j] * dy[t];  dgate[t][j] = <dy[t], o[row(t,j)]> (fp32,
 // fixed reduction tree: per-thread partials, lane butterfly, then waves in order).
-// MX (bf16 only): the same pass writes d_o's MXFP8 image (q, sc; S rows),
-// quantised from the stored bf16 values.
-template <typename T, bool MX, int K>
+// DO is the type of d_o: T, or float for MXFP8 layers (bf16 T), whose d_o
+// keeps the fp32 products. MX (DO = float only): the same pass writes d_o's
+// MXFP8 image (q, sc; S rows), each code decided on the fp32 value stored.
+template <typename T, typename DO, bool MX, int K>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ o,
                                                           const float* __restrict__ gate,
                                                           const int32_t* __restrict__ row_of_slot, int Tn, int nvec,
-                                                          int lpt, T* __restrict__ d_o, float* __restrict__ dgate,
+                                                          int lpt, DO* __restrict__ d_o, float* __restrict__ dgate,
                                                           uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
   constexpr int VE = Vec16<T>::N;
+  static_assert(!MX || (sizeof(DO) == 4 && VE == 8), "MXFP8 images come from fp32 d_o of bf16 layers");
   __shared__ float red[4][K];
   const int tpw = 256 / lpt;
   const int t = blockIdx.x * tpw + threadIdx.x / lpt;
@@ -363,11 +371,17 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
           sv[i] = g[j] * dv[i];
         }
         if (rows[j] < 0) continue;  // the same for every lane of the token
-        const uint4 pk = pack16(sv);
-        st16(d_o + rows[j] * re + v * VE, pk);
-        if constexpr (MX) {
-          const int one[1] = {rows[j]};
-          mx_store_piece<1>(pk, v, nvec * VE, one, 1, q, sc, S);
+        DO* dst = d_o + rows[j] * re + v * VE;
+        if constexpr (sizeof(DO) == sizeof(T)) {
+          st16(dst, pack16(sv));
+        } else {  // bf16 dy, fp32 d_o: the 8 products as two 16-byte pieces
+          const float lo[4] = {sv[0], sv[1], sv[2], sv[3]}, hi[4] = {sv[4], sv[5], sv[6], sv[7]};
+          st16(dst, pack16(lo));
+          st16(dst + 4, pack16(hi));
+          if constexpr (MX) {
+            const int one[1] = {rows[j]};
+            mx_store_vals<1, true>(sv, v, nvec * VE, one, 1, q, sc, S);
+          }
         }
       }
     }
@@ -417,20 +431,24 @@ hipError_t launch_combine(const void* o, const float* gate, const int32_t* row_o
 }
 
 hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate, const int32_t* row_of_slot,
-                              bool is_f32, int T, int d, int k, void* d_o, float* dgate, hipStream_t s) {
-  const int nvec = d * (is_f32 ? 4 : 2) / 16;
+                              int kind, int T, int d, int k, void* d_o, float* dgate, hipStream_t s) {
+  const int nvec = d * (kind == 0 ? 4 : 2) / 16;
   const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
   return with_k(k, [&](auto KC) {
     constexpr int K = decltype(KC)::value;
-    if (is_f32)
-      hipLaunchKernelGGL((combine_bwd_kernel<float, false, K>), grid, dim3(256), 0, s, static_cast<const float*>(dy),
-                         static_cast<const float*>(o), gate, row_of_slot, T, nvec, lpt, static_cast<float*>(d_o),
-                         dgate, nullptr, nullptr, T * k);
-    else
-      hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, false, K>), grid, dim3(256), 0, s,
+    if (kind == 0)
+      hipLaunchKernelGGL((combine_bwd_kernel<float, float, false, K>), grid, dim3(256), 0, s,
+                         static_cast<const float*>(dy), static_cast<const float*>(o), gate, row_of_slot, T, nvec, lpt,
+                         static_cast<float*>(d_o), dgate, nullptr, nullptr, T * k);
+    else if (kind == 1)
+      hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, bf16_t, false, K>), grid, dim3(256), 0, s,
                          static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec,
                          lpt, static_cast<bf16_t*>(d_o), dgate, nullptr, nullptr, T * k);
+    else
+      hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float, false, K>), grid, dim3(256), 0, s,
+                         static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec,
+                         lpt, static_cast<float*>(d_o), dgate, nullptr, nullptr, T * k);
     return hipGetLastError();
   });
 }
@@ -442,9 +460,9 @@ hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gat
   const dim3 grid((T + tpw - 1) / tpw);
   return with_k(k, [&](auto KC) {
     constexpr int K = decltype(KC)::value;
-    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, true, K>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(dy),
-                       static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec, lpt, static_cast<bf16_t*>(d_o),
-                       dgate, d_o_mx.q, d_o_mx.s, T * k);
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float, true, K>), grid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec, lpt,
+                       static_cast<float*>(d_o), dgate, d_o_mx.q, d_o_mx.s, T * k);
     return hipGetLastError();
   });
 }

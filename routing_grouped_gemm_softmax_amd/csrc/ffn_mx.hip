@@ -4,9 +4,11 @@
 // The pages use MXFP8 for the expert computation ("Olmo-core 3 é lançado com
 // infraestrutura para treinar modelos MoE", section "Otimizações e testes em
 // escala de trilhões"; "Ai2 rilascia Olmo-Core 3...", section "Parallelismo,
-// precisione e tecniche di memoria"). The layer's bf16 tensors stay the
-// masters (G, U, H, O, dGU, dXp and the weight gradients are bf16); each GEMM
-// consumes E4M3 copies with one E8M0 scale per 32 elements along its K:
+// precisione e tecniche di memoria"). Inputs, O, dXp and the weight
+// gradients are bf16; the computed GEMM operands G, U, H, dO and dG | dU are
+// kept in fp32, so every E4M3 code is decided on the fp32 value (each
+// quantiser of an fp32 operand uses the exact encoder). Each GEMM consumes
+// E4M3 copies with one E8M0 scale per 32 elements along its K:
 //   forward   G,U = q(Xp) q(W_gate), q(W_up)   K = d  (weights transposed)
 //             O   = q(H) q(W_down)              K = f  (weight transposed)
 //   dgrad     dGU = SwiGLU'(q(dO) q(W_down)^T)  K = d
@@ -14,7 +16,8 @@
 //   wgrad     dW_down = q(H)^T q(dO), [dW_gate|dW_up] = q(Xp)^T q(dGU), K =
 //             an expert's tokens, each expert's range padded to 64 rows.
 // q(Xp) and q(dO) along d can arrive ready-made from the dispatch and
-// combine-backward passes, which write them beside their bf16 rows.
+// combine-backward passes, which write them beside their rows; q(H) and
+// q(dGU) along K come from the epilogues of the GEMMs that produce them.
 #include "common.h"
 #include "grouped_gemm.h"
 #include "kernels.h"
@@ -180,7 +183,7 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
       doq = im.q;
       dos = im.s;
     } else {
-      TRY(launch_mx_kmajor(a.d_o, S, d, 1, 0, doq, 0, dos, 0, s));
+      TRY(launch_mx_kmajor_f32(a.d_o, S, d, doq, dos, s));
     }
     GemmParams p{};
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
@@ -205,23 +208,23 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
   TRY(launch_mx_poff(a.offsets, E, w.poff, s));
   TRY(launch_mx_blocks(a.offsets, w.poff, E, P, w.blk, s));
   {  // dW_down[e] = q(H_e)^T q(dO_e)
-    TRY(launch_mx_tgroup(a.H, S, f, w.blk, 1, 0, w.ht, P, 0, w.hts, 0, s));
-    TRY(launch_mx_tgroup(a.d_o, S, d, w.blk, 1, 0, w.dot, P, 0, w.dots, 0, s));
+    TRY(launch_mx_tgroup_f32(a.H, S, f, w.blk, w.ht, P, w.hts, s));
+    TRY(launch_mx_tgroup_f32(a.d_o, S, d, w.blk, w.dot, P, w.dots, s));
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
     p.a = w.ht; p.lda = P; p.as = w.hts; p.as_slab = 2LL * f;
     p.b0 = w.dot; p.ldb = P; p.bs0 = w.dots; p.bs_slab = 2LL * d;
-    p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = f * d; p.M = f; p.N = d; p.f = d;
+    p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = static_cast<int64_t>(f) * d; p.M = f; p.N = d; p.f = d;
     TRY(launch_mx_wgrad(p, s));
   }
   {  // [dW_gate | dW_up][e] = q(Xp_e)^T q(dGU_e)
     TRY(launch_mx_tgroup(a.xp, S, d, w.blk, 1, 0, w.xt, P, 0, w.xts, 0, s));
-    TRY(launch_mx_tgroup(a.dgu, S, 2 * f, w.blk, 1, 0, w.dgut, P, 0, w.dguts, 0, s));
+    TRY(launch_mx_tgroup_f32(a.dgu, S, 2 * f, w.blk, w.dgut, P, w.dguts, s));
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
     p.a = w.xt; p.lda = P; p.as = w.xts; p.as_slab = 2LL * d;
     p.b0 = w.dgut; p.ldb = P; p.bs0 = w.dguts; p.bs_slab = 4LL * f;
-    p.c0 = a.dw_gate; p.c1 = a.dw_up; p.ldc = f; p.cstride = d * f; p.M = d; p.N = 2 * f; p.f = f;
+    p.c0 = a.dw_gate; p.c1 = a.dw_up; p.ldc = f; p.cstride = static_cast<int64_t>(d) * f; p.M = d; p.N = 2 * f; p.f = f;
     TRY(launch_mx_wgrad(p, s));
   }
   return hipSuccess;

@@ -11,13 +11,16 @@
 // own id to (expert, row tile, column tile). The grid is sized on the host
 // from a bound that needs no counts: ceil(S/BM) + E row tiles.
 //
-// Tiles: 256 threads (4 waves, 2x2), BM x BN output tile, each wave owns a
-// (BM/2) x (BN/2) sub-tile of 32x32 MFMA blocks. K advances in slabs of 128
-// bytes (64 bf16 or 32 fp32). LDS holds both operands as [row][128 B] with
-// the 16-byte chunks XOR-swizzled by the row, double-buffered. Operands whose
-// contiguous dimension in HBM is not K (the weights in the forward, both
-// operands of the weight gradients) are transposed in registers on their way
-// into LDS, so every MFMA fragment is one 16-byte LDS read per lane.
+// This file holds the kernel of fp32 layers (v_mfma_f32_32x32x2f32) and the
+// host side of every FFN call; bf16 layers run the kernels of gemm_bf16.hip,
+// MXFP8 layers those of gemm_mx.hip. Tiles: 256 threads (4 waves, 2x2), BM x
+// BN output tile, each wave owns a (BM/2) x (BN/2) sub-tile of 32x32 MFMA
+// blocks. K advances in slabs of 128 bytes (32 fp32). LDS holds both operands
+// as [row][128 B] with the 16-byte chunks XOR-swizzled by the row,
+// double-buffered through registers. Operands whose contiguous dimension in
+// HBM is not K (the weights in the forward, both operands of the weight
+// gradients) are transposed in registers on their way into LDS, so every
+// MFMA fragment comes from 16-byte LDS reads.
 #include "common.h"
 #include "grouped_gemm.h"
 #include "kernels.h"
@@ -39,36 +42,24 @@ __device__ __forceinline__ int lds_off(int row, int k) {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Pack element `nn` of KR 16-byte vectors into KR*EB contiguous bytes.
+// Pack element `nn` of KR 16-byte vectors of fp32 into KR*4 contiguous bytes.
 template <int EB, int KR>
 __device__ __forceinline__ void store_transposed(char* dst, const uint4 (&v)[KR], int nn) {
-  if constexpr (EB == 2) {
-    uint32_t h[KR];
+  static_assert(EB == 4, "fp32 layers only");
+  uint32_t h[KR];
 #pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const uint32_t w = (nn >> 1) == 0 ? v[r].x : (nn >> 1) == 1 ? v[r].y : (nn >> 1) == 2 ? v[r].z : v[r].w;
-      h[r] = (nn & 1) ? (w >> 16) : (w & 0xffffu);
-    }
-    if constexpr (KR == 4) {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    } else {
-      *reinterpret_cast<uint32_t*>(dst) = h[0] | (h[1] << 16);
-    }
+  for (int r = 0; r < KR; ++r)
+    h[r] = nn == 0 ? v[r].x : nn == 1 ? v[r].y : nn == 2 ? v[r].z : v[r].w;
+  if constexpr (KR == 4) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
   } else {
-    uint32_t h[KR];
-#pragma unroll
-    for (int r = 0; r < KR; ++r)
-      h[r] = nn == 0 ? v[r].x : nn == 1 ? v[r].y : nn == 2 ? v[r].z : v[r].w;
-    if constexpr (KR == 4) {
-      *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
-    } else {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(h[0], h[1]);
-    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(h[0], h[1]);
   }
 }
 
 template <typename T, int MODE, int BM, int BN>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
+  static_assert(std::is_same<T, float>::value, "fp32 layers only: bf16 and MXFP8 layers have their own kernels");
   constexpr int EB = sizeof(T);
   constexpr int BK = 128 / EB;      // K elements per slab
   constexpr int VE = 16 / EB;       // elements per 16-byte vector
@@ -269,20 +260,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int k = kk * 16 + h * 8;
-      if constexpr (EB == 2) {
-        bf16x8 fa[MB], fb[NB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-          fa[i] = *reinterpret_cast<const bf16x8*>(al + lds_off<EB>(wm * (BM / 2) + i * 32 + l32, k));
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          fb[j] = *reinterpret_cast<const bf16x8*>(bl + lds_off<EB>(wn * (BN / 2) + j * 32 + l32, k));
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      } else {
+      {
         floatx4 fa[MB][2], fb[NB][2];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
@@ -414,12 +392,12 @@ template <typename T, int MODE, int BM, int BN>
 static hipError_t launch_mode(const GemmParams& p, int grid, hipStream_t s) {
   constexpr int lds = 2 * (BM + BN) * 128;
   auto kern = grouped_gemm_kernel<T, MODE, BM, BN>;
-  static bool attr_set = false;  // benign race: idempotent attribute write
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // the attribute write is idempotent
+  if (!attr_set.load(std::memory_order_acquire)) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (err != hipSuccess) return err;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_release);
   }
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
@@ -458,7 +436,7 @@ static hipError_t launch_wgrad(const GemmParams& p, hipStream_t s) {
 
 // fp32 layers use the kernel above; bf16 layers the kernel of gemm_bf16.hip.
 template <typename T>
-static hipError_t ragged(int mode, const GemmParams& p, hipStream_t s) {
+static hipError_t ragged_launch(int mode, const GemmParams& p, hipStream_t s) {
   if constexpr (std::is_same<T, float>::value) {
     switch (mode) {
       case FWD_GU: return launch_ragged<T, FWD_GU>(p, s);
@@ -473,9 +451,21 @@ static hipError_t ragged(int mode, const GemmParams& p, hipStream_t s) {
 }
 
 template <typename T>
+static hipError_t ragged(int mode, const GemmParams& p, hipStream_t s) {
+  ktimer_begin(mode, s);
+  const hipError_t err = ragged_launch<T>(mode, p, s);
+  ktimer_end(mode, s);
+  return err;
+}
+
+template <typename T>
 static hipError_t wgrad(const GemmParams& p, hipStream_t s) {
-  if constexpr (std::is_same<T, float>::value) return launch_wgrad<T>(p, s);
-  else return launch_bf16_wgrad(p, s);
+  ktimer_begin(WGRAD, s);
+  hipError_t err;
+  if constexpr (std::is_same<T, float>::value) err = launch_wgrad<T>(p, s);
+  else err = launch_bf16_wgrad(p, s);
+  ktimer_end(WGRAD, s);
+  return err;
 }
 
 // G, U, H = SwiGLU(xp W_gate, xp W_up): the forward's first GEMM, and the
@@ -530,14 +520,14 @@ static hipError_t ffn_bwd_t(const FfnArgs& a, hipStream_t s) {
     GemmParams p{};
     p.offsets = a.offsets; p.E = a.E; p.S = S;
     p.a = a.H; p.lda = f; p.b0 = a.d_o; p.ldb = d;
-    p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = f * d; p.M = f; p.N = d; p.f = d;
+    p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = static_cast<int64_t>(f) * d; p.M = f; p.N = d; p.f = d;
     if ((err = wgrad<T>(p, s)) != hipSuccess) return err;
   }
   {  // [dW_gate | dW_up][e] = Xp_e^T [dG | dU]_e   ([d][2f] split at column f)
     GemmParams p{};
     p.offsets = a.offsets; p.E = a.E; p.S = S;
     p.a = a.xp; p.lda = d; p.b0 = a.dgu; p.ldb = 2 * f;
-    p.c0 = a.dw_gate; p.c1 = a.dw_up; p.ldc = f; p.cstride = d * f; p.M = d; p.N = 2 * f; p.f = f;
+    p.c0 = a.dw_gate; p.c1 = a.dw_up; p.ldc = f; p.cstride = static_cast<int64_t>(d) * f; p.M = d; p.N = 2 * f; p.f = f;
     if ((err = wgrad<T>(p, s)) != hipSuccess) return err;
   }
   return hipSuccess;

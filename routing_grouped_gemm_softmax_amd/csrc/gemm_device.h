@@ -387,10 +387,11 @@ __device__ __forceinline__ TileCoord wgrad_tile(const GemmParams& p, int t) {
 // Writes the accumulators of one BM x BN tile (and, for BWD_DOWN, reads the
 // saved G, U it needs) through a per-wave LDS area of smem, which must hold
 // 4 x 2 x (BM/2) x 128 bytes and be free of other use.
-// With QUANT (the MXFP8 kernels), the bf16 rows of H (FWD_GU) and of dG, dU
-// (BWD_DOWN) are also written as the next GEMM's K-major MXFP8 operand
-// (p.mxq, p.mxs): the same staged 16-byte pieces, 4 lanes per 32-block,
-// encoded exactly as mx_kmajor_kernel encodes a row read back from memory.
+// With QUANT (the MXFP8 kernels), G, U, H (FWD_GU) and dG | dU (BWD_DOWN) are
+// fp32 tensors (BWD_DOWN also reads G, U as fp32), and H and dG | dU are
+// also written as the next GEMM's K-major MXFP8 operand (p.mxq, p.mxs): each
+// 32-block of a row is encoded from its fp32 values, 8 lanes per block, with
+// the exact encoder, so every E4M3 code is decided on the fp32 value.
 template <int MODE, int BM, int BN, bool QUANT = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN / 64][BM / 64], char* smem,
                                          int wave, int lane, const TileCoord& tc) {
@@ -424,28 +425,48 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
   };
   const int mrow = (MODE == WGRAD ? m0 : row0) + wm * WM;   // first row of this wave's block
   // Rows [0, rows) and columns [0, cols) of staging tile `slot` -> global
-  // rows g + r*ld (bytes), 16 bytes per lane, 8 lanes per 128-byte row. With
-  // QUANT and qcol >= 0, also E4M3 codes to p.mxq row mrow + r, columns qcol
-  // + 8 c .. + 7, and each 32-block's E8M0 code to p.mxs.
-  auto flush = [&](int slot, char* g, int64_t ld, int rows, int cols, int qcol = -1) {
+  // rows g + r*ld (bytes), 16 bytes per lane, 8 lanes per 128-byte row.
+  auto flush = [&](int slot, char* g, int64_t ld, int rows, int cols) {
     wave_sync();
     const int c = lane & 7;
 #pragma unroll 4
     for (int t = 0; t < WM / 8; ++t) {
       const int r = t * 8 + (lane >> 3);
       const uint4 v = *reinterpret_cast<const uint4*>(wa + slot * kSlot + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
-      const bool live = r < rows && c * 8 < cols;
+      if (r < rows && c * 8 < cols) *reinterpret_cast<uint4*>(g + r * ld + c * 16) = v;
+    }
+    wave_sync();
+  };
+  // fp32 staging (QUANT): a staging row holds 32 fp32 columns, logical
+  // 16-byte chunk c of row r at chunk c ^ ((r / 2) % 8).
+  auto put4f = [&](int slot, int r, int col, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(wa + slot * kSlot + r * 128 + ((((col >> 2) ^ (r >> 1)) & 7) << 4)) =
+        make_float4(a, b, c, d);
+  };
+  auto get4f = [&](int slot, int r, int col) -> float4 {
+    return *reinterpret_cast<const float4*>(wa + slot * kSlot + r * 128 + ((((col >> 2) ^ (r >> 1)) & 7) << 4));
+  };
+  // Rows [0, rows) of fp32 staging tile `slot` (32 columns) -> global rows
+  // g + r*ld (bytes). With qcol >= 0 (wave-uniform), also each row's 32-block
+  // as E4M3 codes to p.mxq row mrow + r, columns qcol .. qcol + 31, and its
+  // E8M0 code to p.mxs; the 8 lanes of a row hold the block.
+  auto flush32 = [&](int slot, char* g, int64_t ld, int rows, int qcol) {
+    wave_sync();
+    const int c = lane & 7;
+#pragma unroll 4
+    for (int t = 0; t < WM / 8; ++t) {
+      const int r = t * 8 + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4*>(wa + slot * kSlot + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
+      const bool live = r < rows;
       if (live) *reinterpret_cast<uint4*>(g + r * ld + c * 16) = v;
-      if constexpr (QUANT) {
-        if (qcol >= 0) {
-          float x[8];
-          unpack16(v, x);
-          const int code = mx_group4_code(x);  // every lane: butterflies
-          if (live) {
-            const int64_t row = mrow + r, col = qcol + c * 8;
-            *reinterpret_cast<uint2*>(p.mxq + row * p.mxq_ld + col) = mx_encode8(x, code);
-            if ((c & 3) == 0) p.mxs[(col / 64) * p.mxs_slab + row * 2 + (col / 32) % 2] = static_cast<uint8_t>(code);
-          }
+      if (qcol >= 0) {
+        float x[4];
+        unpack16(v, x);
+        const int code = mx_group8_code(x);  // every lane: butterflies
+        if (live) {
+          const int64_t row = mrow + r, col = qcol + c * 4;
+          *reinterpret_cast<uint32_t*>(p.mxq + row * p.mxq_ld + col) = mx_encode4_exact(x, code);
+          if (c == 0) p.mxs[(col / 64) * p.mxs_slab + row * 2 + (col / 32) % 2] = static_cast<uint8_t>(code);
         }
       }
     }
@@ -456,7 +477,83 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
   };
 
-  if constexpr (MODE == FWD_GU) {
+  if constexpr (MODE == FWD_GU && QUANT) {
+    // fp32 G, U, H in 32-column groups: gate block JJ and up block JJ + NB/2
+    // cover the same 32 f-columns.
+    const int64_t ld = p.ldc * 4;
+    static_for<NB / 2>([&](auto JJ) {
+      const int col0 = nt * (BN / 2) + wn * (WN / 2) + JJ * 32;
+      const int64_t base = (static_cast<int64_t>(mrow) * p.ldc + col0) * 4;
+      static_for<MB>([&](auto I) {
+        static_for<4>([&](auto Q) {
+          const int r = I * 32 + l32, col = 8 * Q + 4 * hl;
+          float g[4], h[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            g[c] = acc[JJ][I][4 * Q + c];
+            const float u = acc[JJ + NB / 2][I][4 * Q + c];
+            h[c] = g[c] * sigmoid_f(g[c]) * u;
+          }
+          put4f(0, r, col, g[0], g[1], g[2], g[3]);
+          put4f(1, r, col, h[0], h[1], h[2], h[3]);
+        });
+      });
+      flush32(0, static_cast<char*>(p.c0) + base, ld, rows, -1);
+      flush32(1, static_cast<char*>(p.c2) + base, ld, rows, col0);
+      static_for<MB>([&](auto I) {
+        static_for<4>([&](auto Q) {
+          constexpr int j = JJ + NB / 2;
+          put4f(0, I * 32 + l32, 8 * Q + 4 * hl, acc[j][I][4 * Q], acc[j][I][4 * Q + 1], acc[j][I][4 * Q + 2],
+                acc[j][I][4 * Q + 3]);
+        });
+      });
+      flush32(0, static_cast<char*>(p.c1) + base, ld, rows, -1);
+    });
+  } else if constexpr (MODE == BWD_DOWN && QUANT) {
+    // dH -> dG = dH U sig(G) (1 + G (1 - sig(G))), dU = dH G sig(G) in fp32
+    // from the fp32 saved G, U; a row of dGU is [dG (f) | dU (f)], fp32.
+    // One 32-column block at a time: its G, U come in by LDS DMA (rows past
+    // the end read 0), then dG and dU leave through flush32 with their codes.
+    const int64_t ld = p.ldc * 4, lds_ = static_cast<int64_t>(p.f) * 4;
+    static_for<NB>([&](auto J) {
+      const int col0 = n0 + wn * WN + J * 32;
+      const int64_t sbase = (static_cast<int64_t>(mrow) * p.f + col0) * 4;
+      const int64_t sbytes = static_cast<int64_t>(rows) * p.f * 4;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const auto rs = make_rsrc(static_cast<const char*>(sl ? p.e1 : p.e0) + sbase, sbytes);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wa + sl * kSlot));
+#pragma unroll
+        for (int t = 0; t < WM / 8; ++t) {
+          const int r = t * 8 + (lane >> 3);
+          const int c = (lane & 7) ^ ((r >> 1) & 7);   // logical chunk held by this lane's slot
+          load_lds16(rs, static_cast<uint32_t>(r * lds_ + c * 16), dst + t * 1024);
+        }
+      }
+      wait_vmcnt<0>();
+      wave_sync();
+      static_for<MB>([&](auto I) {
+        static_for<4>([&](auto Q) {
+          const int r = I * 32 + l32, col = 8 * Q + 4 * hl;
+          const float4 g4 = get4f(0, r, col), u4 = get4f(1, r, col);
+          const float g[4] = {g4.x, g4.y, g4.z, g4.w}, u[4] = {u4.x, u4.y, u4.z, u4.w};
+          float dg[4], du[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float dh = acc[J][I][4 * Q + c];
+            const float sg = sigmoid_f(g[c]);
+            du[c] = dh * g[c] * sg;
+            dg[c] = dh * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
+          }
+          put4f(0, r, col, dg[0], dg[1], dg[2], dg[3]);
+          put4f(1, r, col, du[0], du[1], du[2], du[3]);
+        });
+      });
+      char* C = static_cast<char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 4;
+      flush32(0, C, ld, rows, col0);
+      flush32(1, C + static_cast<int64_t>(p.f) * 4, ld, rows, p.f + col0);
+    });
+  } else if constexpr (MODE == FWD_GU) {
     // Gate blocks [0, NB/2) and up blocks [NB/2, NB) cover the same NB*16 f-columns.
     constexpr int GC = NB * 16;
     const int col0 = nt * (BN / 2) + wn * (WN / 2);
@@ -481,7 +578,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
       });
     });
     flush(0, G, ld, rows, GC);
-    flush(1, H, ld, rows, GC, col0);
+    flush(1, H, ld, rows, GC);
     static_for<MB>([&](auto I) {
       static_for<NB / 2>([&](auto JJ) {
         static_for<4>([&](auto Q) { put4(0, I * 32 + l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JJ + NB / 2, I, Q)); });
@@ -655,8 +752,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
         });
       });
       char* C = static_cast<char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 2;
-      flush(0, C, ld, rows, GC, col0);
-      flush(1, C + static_cast<int64_t>(p.f) * 2, ld, rows, GC, p.f + col0);
+      flush(0, C, ld, rows, GC);
+      flush(1, C + static_cast<int64_t>(p.f) * 2, ld, rows, GC);
     });
   } else {
     // FWD_DOWN, BWD_GU: C[row][n]; WGRAD: C[e][m][n], columns >= f of the

@@ -299,22 +299,33 @@ hipError_t ragged_mode(const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_mx_ragged(int mode, const GemmParams& p, hipStream_t s) {
+  ktimer_begin(mode, s);
+  hipError_t err;
   switch (mode) {
-    case FWD_GU: return ragged_mode<FWD_GU>(p, s);
-    case FWD_DOWN: return ragged_mode<FWD_DOWN>(p, s);
-    case BWD_DOWN: return ragged_mode<BWD_DOWN>(p, s);
-    case BWD_GU: return ragged_mode<BWD_GU>(p, s);
-    default: return hipErrorInvalidValue;
+    case FWD_GU: err = ragged_mode<FWD_GU>(p, s); break;
+    case FWD_DOWN: err = ragged_mode<FWD_DOWN>(p, s); break;
+    case BWD_DOWN: err = ragged_mode<BWD_DOWN>(p, s); break;
+    case BWD_GU: err = ragged_mode<BWD_GU>(p, s); break;
+    default: err = hipErrorInvalidValue;
   }
+  ktimer_end(mode, s);
+  return err;
 }
 
-hipError_t launch_mx_wgrad(const GemmParams& p, hipStream_t s) {
+static hipError_t mx_wgrad(const GemmParams& p, hipStream_t s) {
   auto grid = [&](int bm, int bn) { return round8(static_cast<int64_t>(p.E) * (p.M / bm) * (p.N / bn)); };
   // A column tile must not straddle the gate|up split at column f.
   const int nsplit = p.c1 ? p.f : p.N;
   if (p.M % 256 == 0 && p.N % 256 == 0 && nsplit % 256 == 0) return launch_tile<WGRAD, 256, 256>(p, grid(256, 256), s);
   if (p.M % 256 == 0) return launch_tile<WGRAD, 256, 128>(p, grid(256, 128), s);
   return launch_tile<WGRAD, 128, 128>(p, grid(128, 128), s);
+}
+
+hipError_t launch_mx_wgrad(const GemmParams& p, hipStream_t s) {
+  ktimer_begin(WGRAD, s);
+  const hipError_t err = mx_wgrad(p, s);
+  ktimer_end(WGRAD, s);
+  return err;
 }
 
 }  // namespace moe

@@ -32,7 +32,7 @@ struct GemmParams {
   int M;              // WGRAD: rows of each weight gradient
   int N, K;           // logical N (FWD_GU: 2f) and K (ragged modes)
   int f;              // split point: FWD_GU/BWD_GU/WGRAD(gate|up)
-  int cstride;        // WGRAD: elements between experts in c0/c1
+  int64_t cstride;    // WGRAD: elements between experts in c0/c1
   // MXFP8 operands: a, b0, b1 hold E4M3 bytes (row strides lda, ldb in
   // bytes); their E8M0 scales are slab-major, 2 bytes (two blocks of 32) per
   // row per 64-k slab: scale(row, k) = s[(k / 64) * slab + row * 2 + (k / 32) % 2].

@@ -36,6 +36,11 @@ struct FfnArgs {
   bool recompute;
 };
 
+// Kernel timing hook (moe_kernel_timer): the launcher of grouped-GEMM step
+// `mode` calls ktimer_begin before its launch(es) and ktimer_end after.
+void ktimer_begin(int mode, hipStream_t s);
+void ktimer_end(int mode, hipStream_t s);
+
 hipError_t launch_ffn_fwd(const FfnArgs& a, bool is_f32, hipStream_t s);
 hipError_t launch_ffn_bwd(const FfnArgs& a, bool is_f32, hipStream_t s);
 
@@ -63,8 +68,9 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_byte
                            int32_t* token_of_row, void* xp, void* ws, hipStream_t s);
 hipError_t launch_combine(const void* o, const float* gate, const int32_t* row_of_slot, bool is_f32,
                           int T, int d, int k, void* y, hipStream_t s);
+// kind: 0 fp32 layer, 1 bf16 layer, 2 MXFP8 layer (bf16 dy and o, fp32 d_o).
 hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate,
-                              const int32_t* row_of_slot, bool is_f32, int T, int d, int k,
+                              const int32_t* row_of_slot, int kind, int T, int d, int k,
                               void* d_o, float* dgate, hipStream_t s);
 size_t dispatch_bwd_workspace(int d, int E, bool is_f32);
 hipError_t launch_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* dlogits,
@@ -93,8 +99,9 @@ inline MxImage mx_image(const void* base, int64_t rows, int64_t cols) {
   return MxImage{p, p + mx_part_bytes(static_cast<size_t>(rows) * static_cast<size_t>(cols))};
 }
 
-// Dispatch and combine backward that also write the MXFP8 image of their bf16
-// output rows (xp, d_o) from the values they already hold; d = cols, S = rows.
+// Dispatch and combine backward that also write the MXFP8 image of their
+// output rows (xp bf16, d_o fp32) from the values they already hold; d =
+// cols, S = rows.
 hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
                               int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                               int32_t* token_of_row, void* xp, MxImage xp_mx, void* ws, hipStream_t s);
@@ -119,6 +126,12 @@ hipError_t launch_mx_kmajor(const void* in, int R, int C, int batches, int64_t i
 hipError_t launch_mx_tgroup(const void* in, int R, int C, const void* blk, int batches, int64_t in_bstride,
                             uint8_t* q, int64_t P, int64_t q_bstride, uint8_t* s, int64_t s_bstride, hipStream_t st,
                             uint8_t* qk = nullptr, uint8_t* sk = nullptr);
+// The fp32 forms (an MXFP8 layer's fp32 operands H, dO, dG | dU): K along the
+// columns of in [R][C] (one batch), and K along the rows inside the row
+// groups of blk (one batch), each encoded exactly from the fp32 values.
+hipError_t launch_mx_kmajor_f32(const void* in, int R, int C, uint8_t* q, uint8_t* s, hipStream_t st);
+hipError_t launch_mx_tgroup_f32(const void* in, int R, int C, const void* blk, uint8_t* q, int64_t P, uint8_t* s,
+                                hipStream_t st);
 // Block table of the grouped transposing quantiser (P/64 entries of 8 bytes).
 hipError_t launch_mx_blocks(const int32_t* offsets, const int32_t* poff, int E, int64_t P, void* blk, hipStream_t st);
 hipError_t launch_mx_poff(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);

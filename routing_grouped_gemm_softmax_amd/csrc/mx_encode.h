@@ -1,9 +1,10 @@
 // MXFP8 element and scale encoding (OCP Microscaling Formats v1.0): E4M3
 // ("FN": bias 7, max 448, no infinities) elements with one E8M0 scale
 // 2^(floor(log2 amax) - 8) per block of 32. e4m3_encode spells the element
-// rounding out with exact integer operations; the quantisers use the
-// hardware conversion (e4m3_encode4), which gives the same bytes on their
-// inputs. Shared by every quantiser so they all produce the same bytes.
+// rounding out with exact integer operations and serves every fp32 input; the
+// quantisers of bf16 inputs use the hardware conversion (e4m3_encode4), which
+// gives the same bytes on those. Shared by every quantiser so they all
+// produce the same bytes.
 #pragma once
 
 #include <math.h>
@@ -88,6 +89,45 @@ __device__ __forceinline__ int mx_group4_code(const float (&v)[8]) {
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
   amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  return mx_scale_code(amax);
+}
+
+// The same for fp32 values, which carry more significand bits than the
+// hardware conversion was checked on: four codes by the exact encoder.
+__device__ __forceinline__ uint32_t mx_encode4_exact(const float (&v)[4], int c) {
+  const int sh = 127 - c;
+  return e4m3_encode(ldexpf(v[0], sh)) | (e4m3_encode(ldexpf(v[1], sh)) << 8) |
+         (e4m3_encode(ldexpf(v[2], sh)) << 16) | (e4m3_encode(ldexpf(v[3], sh)) << 24);
+}
+
+// Eight consecutive fp32 values of one block (code c) -> 8 E4M3 bytes, exactly.
+__device__ __forceinline__ uint2 mx_encode8_exact(const float (&v)[8], int c) {
+  const float a[4] = {v[0], v[1], v[2], v[3]}, b[4] = {v[4], v[5], v[6], v[7]};
+  return make_uint2(mx_encode4_exact(a, c), mx_encode4_exact(b, c));
+}
+
+// Scale code and the 32 E4M3 codes of one block of fp32 values (exact encoder).
+__device__ __forceinline__ int mx_encode_block_exact(const float (&v)[32], uint32_t (&w)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int c = mx_scale_code(amax);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q[4] = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    w[i] = mx_encode4_exact(q, c);
+  }
+  return c;
+}
+
+// Block scale code of a 32-block of fp32 values held by 8 consecutive lanes
+// (4 values each, lane groups aligned to 8): three butterflies. Every lane of
+// the wave must execute it.
+__device__ __forceinline__ int mx_group8_code(const float (&v)[4]) {
+  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
   return mx_scale_code(amax);
 }
 

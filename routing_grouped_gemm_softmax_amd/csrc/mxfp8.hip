@@ -197,24 +197,31 @@ __global__ __launch_bounds__(256) void mx_kmajor_kernel(const bf16_t* __restrict
 // for each 64-column block of q, its first source row and how many of its
 // rows are real) group e's rows land at q columns poff[e].. (poff: the groups
 // padded to 64 rows) and the padding reads as zeros; without it the batch is
-// one group of R rows (R a multiple of 64). With qk != nullptr (one group
-// only) the same pass also writes the columns-blocked copy qk [R][C], sk
-// [C/64][R][2] (mx_kmajor_kernel's layout), so a weight is read once for both
-// of its GEMM layouts.
+// one group of R rows (R a multiple of 64). With qk != nullptr (bf16 input,
+// one group only) the same pass also writes the columns-blocked copy qk
+// [R][C], sk [C/64][R][2] (mx_kmajor_kernel's layout), so a weight is read
+// once for both of its GEMM layouts. T is bf16_t (weights, xp) or float (the
+// fp32 operands H, dO, dG | dU of an MXFP8 layer, encoded exactly).
 //
 // One workgroup per (128 padded rows, 64 columns), each 64-row half resolving
 // its own group: the tile goes through LDS; each wave reads one 32-row block
-// of all 64 columns (thread = one column, 32 conflict-free 2-byte reads),
-// encodes it into an LDS output tile [64 columns][128 bytes], which then
-// leaves as full 128-byte rows of q.
-__global__ __launch_bounds__(256) void mx_tgroup_kernel(const bf16_t* __restrict__ in, int R, int C,
+// of all 64 columns (thread = one column, 32 conflict-free reads), encodes it
+// into an LDS output tile [64 columns][128 bytes], which then leaves as full
+// 128-byte rows of q.
+template <typename T>
+__global__ __launch_bounds__(256) void mx_tgroup_kernel(const T* __restrict__ in, int R, int C,
                                                         const int2* __restrict__ blk, int64_t in_bstride, uint8_t* __restrict__ q, int64_t P,
                                                         int64_t q_bstride, uint8_t* __restrict__ s,
                                                         int64_t s_bstride, uint8_t* __restrict__ qk,
                                                         uint8_t* __restrict__ sk) {
-  constexpr int kLd = 64 + 8;      // bf16 per LDS input row (16-byte aligned rows)
-  constexpr int kLdq = 128 + 16;   // bytes per LDS output row
-  __shared__ __attribute__((aligned(16))) bf16_t tile[128][kLd];
+  constexpr bool kF32 = sizeof(T) == 4;
+  constexpr int VE = 16 / sizeof(T);  // elements per 16-byte load
+  constexpr int LPR = 64 / VE;        // lanes per 64-column row
+  constexpr int RPP = 256 / LPR;      // rows per pass of the workgroup
+  constexpr int NP = 128 / RPP;       // passes over the 128 rows
+  constexpr int kLd = 64 + VE;        // elements per LDS input row (16-byte aligned rows)
+  constexpr int kLdq = 128 + 16;      // bytes per LDS output row
+  __shared__ __attribute__((aligned(16))) T tile[128][kLd];
   __shared__ __attribute__((aligned(16))) uint8_t qt[64][kLdq];
   __shared__ int s_src[2], s_valid[2];
   const int tid = threadIdx.x, b = blockIdx.z;
@@ -237,45 +244,55 @@ __global__ __launch_bounds__(256) void mx_tgroup_kernel(const bf16_t* __restrict
     s_valid[tid] = valid;
   }
   __syncthreads();
-  const bf16_t* src = in + static_cast<int64_t>(b) * in_bstride;
-  const int ch = tid & 7;
-  // All four loads go out before any is used: rows past a group's end load
-  // row 0 (always in bounds) and are replaced by zeros.
-  uint4 raw[4];
+  const T* src = in + static_cast<int64_t>(b) * in_bstride;
+  const int ch = tid % LPR;
+  // All loads go out before any is used: rows past a group's end load row 0
+  // (always in bounds) and are replaced by zeros.
+  uint4 raw[NP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
+  for (int i = 0; i < NP; ++i) {
+    const int r = i * RPP + tid / LPR, h = r >> 6, rr = r & 63;
     const int64_t row = rr < s_valid[h] ? s_src[h] + rr : 0;
-    raw[i] = ld16(src + row * C + c0 + ch * 8);
+    raw[i] = ld16(src + row * C + c0 + ch * VE);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
+  for (int i = 0; i < NP; ++i) {
+    const int r = i * RPP + tid / LPR, h = r >> 6, rr = r & 63;
     const bool ok = rr < s_valid[h];
     const uint4 v = make_uint4(ok ? raw[i].x : 0u, ok ? raw[i].y : 0u, ok ? raw[i].z : 0u, ok ? raw[i].w : 0u);
-    *reinterpret_cast<uint4*>(&tile[r][ch * 8]) = v;
-    if (qk != nullptr && p0 + r < P) {  // uniform per wave (a wave's 8 rows share a 64-row half)
-      // Columns-blocked copy straight from the registers (one group: row p0 + r).
-      float f[8];
-      unpack16(v, f);
-      const int code = mx_group4_code(f);
-      const int64_t row = p0 + r;
-      *reinterpret_cast<uint2*>(qk + static_cast<int64_t>(b) * q_bstride + row * C + c0 + ch * 8) = mx_encode8(f, code);
-      const int code_hi = __shfl(code, (tid & 56) + 4, kWave);
-      if (ch == 0)
-        *reinterpret_cast<uint16_t*>(sk + static_cast<int64_t>(b) * s_bstride +
-                                     (static_cast<int64_t>(c0 / 64) * R + row) * 2) =
-            static_cast<uint16_t>(code | (code_hi << 8));
+    *reinterpret_cast<uint4*>(&tile[r][ch * VE]) = v;
+    if constexpr (!kF32) {
+      if (qk != nullptr && p0 + r < P) {  // uniform per wave (a wave's 8 rows share a 64-row half)
+        // Columns-blocked copy straight from the registers (one group: row p0 + r).
+        float f[8];
+        unpack16(v, f);
+        const int code = mx_group4_code(f);
+        const int64_t row = p0 + r;
+        *reinterpret_cast<uint2*>(qk + static_cast<int64_t>(b) * q_bstride + row * C + c0 + ch * 8) =
+            mx_encode8(f, code);
+        const int code_hi = __shfl(code, (tid & 56) + 4, kWave);
+        if (ch == 0)
+          *reinterpret_cast<uint16_t*>(sk + static_cast<int64_t>(b) * s_bstride +
+                                       (static_cast<int64_t>(c0 / 64) * R + row) * 2) =
+              static_cast<uint16_t>(code | (code_hi << 8));
+      }
     }
   }
   __syncthreads();
   {
     const int col = tid & 63, block = tid >> 6;
     float v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(tile[block * 32 + i][col]);
     uint32_t w[8];
-    const int code = mx_encode_block(v, w);
+    int code;
+    if constexpr (kF32) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = tile[block * 32 + i][col];
+      code = mx_encode_block_exact(v, w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(tile[block * 32 + i][col]);
+      code = mx_encode_block(v, w);
+    }
     uint4* d = reinterpret_cast<uint4*>(&qt[col][block * 32]);
     d[0] = make_uint4(w[0], w[1], w[2], w[3]);
     d[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -293,6 +310,25 @@ __global__ __launch_bounds__(256) void mx_tgroup_kernel(const bf16_t* __restrict
     if (c16 * 16 < pvalid)
       *reinterpret_cast<uint4*>(q + static_cast<int64_t>(b) * q_bstride + static_cast<int64_t>(c0 + row) * P + p0 +
                                 c16 * 16) = *reinterpret_cast<const uint4*>(&qt[row][c16 * 16]);
+  }
+}
+
+// K along the columns of an fp32 matrix [R][C] (an MXFP8 layer's dO) -> q
+// [R][C], s [C/64][R][2]: 8 lanes per 32-block of a row, 4 values each,
+// encoded exactly.
+__global__ __launch_bounds__(256) void mx_kmajor_f32_kernel(const float* __restrict__ in, int R, int C, int64_t nblk,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t g = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 3;
+  const int c = threadIdx.x & 7;
+  const bool live = g < nblk;  // the same for the 8 lanes of a block
+  const int64_t gg = live ? g : 0;
+  const int64_t row = gg / (C / 32), cb = gg % (C / 32);
+  float x[4];
+  unpack16(ld16(in + row * C + cb * 32 + c * 4), x);
+  const int code = mx_group8_code(x);  // every lane: butterflies
+  if (live) {
+    *reinterpret_cast<uint32_t*>(q + row * C + cb * 32 + c * 4) = mx_encode4_exact(x, code);
+    if (c == 0) s[((cb >> 1) * R + row) * 2 + (cb & 1)] = static_cast<uint8_t>(code);
   }
 }
 
@@ -347,6 +383,13 @@ hipError_t launch_mx_blocks(const int32_t* offsets, const int32_t* poff, int E, 
   return hipGetLastError();
 }
 
+hipError_t launch_mx_kmajor_f32(const void* in, int R, int C, uint8_t* q, uint8_t* s, hipStream_t st) {
+  const int64_t nblk = static_cast<int64_t>(R) * (C / 32);
+  hipLaunchKernelGGL(mx_kmajor_f32_kernel, dim3(static_cast<unsigned>((nblk * 8 + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const float*>(in), R, C, nblk, q, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_kmajor(const void* in, int R, int C, int batches, int64_t in_bstride, uint8_t* q,
                             int64_t q_bstride, uint8_t* s, int64_t s_bstride, hipStream_t st) {
   const int64_t ntiles = static_cast<int64_t>(batches) * (R / 8) * (C / 64);
@@ -361,8 +404,16 @@ hipError_t launch_mx_tgroup(const void* in, int R, int C, const void* blk, int b
                             uint8_t* qk, uint8_t* sk) {
   const dim3 grid(static_cast<unsigned>((P + 127) / 128), static_cast<unsigned>(C / 64),
                   static_cast<unsigned>(batches));
-  hipLaunchKernelGGL(mx_tgroup_kernel, grid, dim3(256), 0, st, static_cast<const bf16_t*>(in), R, C,
+  hipLaunchKernelGGL(mx_tgroup_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(in), R, C,
                      static_cast<const int2*>(blk), in_bstride, q, P, q_bstride, s, s_bstride, qk, sk);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_tgroup_f32(const void* in, int R, int C, const void* blk, uint8_t* q, int64_t P, uint8_t* s,
+                                hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((P + 127) / 128), static_cast<unsigned>(C / 64), 1);
+  hipLaunchKernelGGL(mx_tgroup_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(in), R, C,
+                     static_cast<const int2*>(blk), 0, q, P, 0, s, 0, nullptr, nullptr);
   return hipGetLastError();
 }
 

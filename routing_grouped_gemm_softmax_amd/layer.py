@@ -25,6 +25,9 @@ class MoELayer:
         self.shape = L.MoeShape.make(T, d, E, k, f, dtype, L.MOE_FLAG_RECOMPUTE if recompute else 0)
         self.recompute = recompute
         self.dtype = L.TORCH_DTYPE[self.shape.dtype]
+        # G, U, H, d_o and dG|dU: fp32 for MXFP8 layers (their E4M3 codes are
+        # decided on the fp32 values), else the layer dtype.
+        self.act_dtype = torch.float32 if self.shape.dtype == L.MOE_MXFP8 else self.dtype
         self.learned = learned_routing
         S = T * k
         dev = torch.device(device)
@@ -56,7 +59,7 @@ class MoELayer:
         self.y = buf(T, d)
         self.ws_dispatch = ws(L.MOE_OP_DISPATCH)
         # backward
-        self.d_o = buf(S, d)
+        self.d_o = buf(S, d, dtype=self.act_dtype)
         self.dgate = buf(T, k, dtype=f32)
         self.dxp = buf(S, d)
         self.dw_gate = buf(E, d, f)
@@ -71,17 +74,25 @@ class MoELayer:
             self.ws_dispatch_bwd = ws(L.MOE_OP_DISPATCH_BWD)
 
     def saved(self):
-        """(G, U, H), each [S][f]: views of the save buffer or, for a recompute
-        layer, of the planes its last backward rebuilt in the backward
-        workspace (after the dG|dU rows)."""
+        """(G, U, H), each [S][f] (fp32 for MXFP8 layers): views of the save
+        buffer or, for a recompute layer, of the planes its last backward
+        rebuilt in the backward workspace (after the dG|dU rows)."""
         S, f = self.T * self.k, self.f
+        eb = torch.empty((), dtype=self.act_dtype).element_size()
         if self.recompute:
-            eb = self.xp.element_size()
             off = (S * 2 * f * eb + 255) // 256 * 256
-            flat = self.ws_ffn_bwd[off:off + 3 * S * f * eb].view(self.dtype)
+            flat = self.ws_ffn_bwd[off:off + 3 * S * f * eb].view(self.act_dtype)
         else:
-            flat = self.save.view(self.dtype)
+            flat = self.save[:3 * S * f * eb].view(self.act_dtype)
         return tuple(flat[i * S * f:(i + 1) * S * f].view(S, f) for i in range(3))
+
+    def dgu(self):
+        """(dG, dU), each [S][f] (fp32 for MXFP8 layers): views of the dG|dU
+        rows the last backward left at the start of its workspace."""
+        S, f = self.T * self.k, self.f
+        eb = torch.empty((), dtype=self.act_dtype).element_size()
+        rows = self.ws_ffn_bwd[:S * 2 * f * eb].view(self.act_dtype).view(S, 2 * f)
+        return rows[:, :f], rows[:, f:]
 
     def load_stats(self, stream=None):
         """Enqueue the expert-load diagnostics of the last dispatch (moe_load_stats)

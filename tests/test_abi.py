@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
                        (-3, b"MOE_ERR_MISALIGNED"), (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == name
@@ -53,6 +53,10 @@ def test_workspace_queries():
     assert L.workspace_size(L.MOE_OP_FFN_BWD, s) == 256 * 4 * 2 * 128 * 4
     assert L.save_size(s) == 3 * 256 * 4 * 128 * 4
     assert L.save_size(shape(dtype="bf16")) == 3 * 256 * 4 * 128 * 2
+    # MXFP8 layers keep G, U, H (and dG|dU) in fp32, beside the weight copies.
+    mx = shape(dtype="mxfp8", d=128)
+    assert L.save_size(mx) > 3 * 256 * 4 * 128 * 4
+    assert L.workspace_size(L.MOE_OP_FFN_BWD, mx) > 256 * 4 * 2 * 128 * 4
     with pytest.raises(L.MoeError):
         L.workspace_size(L.MOE_OP_DISPATCH, shape(k=9, E=16))
     assert L.load().moe_workspace_size(99, ctypes.byref(s)) == ctypes.c_size_t(-1).value

@@ -48,3 +48,25 @@ def test_gemm_combined_roofline_floors():
     assert abs(fl / 2.5e15 * 1e3 - 0.4948) < 1e-3
     assert bench.gemm_compulsory_bytes(e8) / 8e12 < fl / 2.5e15
     assert abs(bench.gemm_compulsory_bytes(e128) / 8e12 * 1e3 - 0.8137) < 1e-3
+
+
+def test_gemm_step_flops_sum_to_the_layer():
+    """The five grouped-GEMM steps the kernel timer surveys add up to the
+    layer's 18*S*d*f (22*S*d*f with the recomputed gate/up GEMM)."""
+    import bench
+    from moe_inputs import WORKLOADS
+    wl = WORKLOADS["mxfp8_balanced"]
+    u = wl.T * wl.k * wl.d * wl.f
+    assert sum(bench.gemm_mode_flops(wl).values()) == 18 * u
+    assert sum(bench.gemm_mode_flops(wl, recompute=True).values()) == 22 * u
+    assert bench.GEMM_MODE_NAMES == tuple(__import__("routing_grouped_gemm_softmax_amd").GEMM_MODES)
+
+
+def test_cpu_baseline_mxfp8_sample_runs():
+    """The per-expert MXFP8 sample of the CPU baseline, on a small shape."""
+    import bench
+    from moe_inputs import WORKLOADS, make_inputs
+    wl = WORKLOADS["mxfp8_balanced"].with_shape(T=256, d=128, E=16, f=128)
+    r = bench.cpu_baseline(wl, make_inputs(wl, 0), budget_s=1.0)
+    assert r["value"] > 0 and r["kind"] == "oracle" and r["cores"] >= 1 and r["cpu_model"]
+    assert "whole experts" in r["sample"]

@@ -4,16 +4,20 @@ E=128, k=4, f=1536) and the MXFP8 layer (T=32768, d=4096, E=128, k=4,
 f=1536), in the launch configuration the benchmark times.
 
 Checked in full (bit-exact): counts, offsets, row_of_slot, token_of_row, and
-zero weight gradients of every empty expert. Sampled against the oracle:
-the xp bytes of 512 random rows; every output of two whole experts (the
-coldest non-empty one and a median one: G, U, H, O, dO, dXp rows and the
-expert's three weight gradients); the forward rows of 128 random rows of the
-hottest expert; y and dx of 24 random tokens through all k of their experts.
-Each piece is an exact sub-problem of the full layer: rows are independent in
-the forward and in dXp (every row operand is quantised along its own row),
-and an expert's weight gradients use only that expert's rows. Tolerances as
-for the small cases: 2e-2 for bf16; for MXFP8 2e-2 stage by stage (the oracle
-fed the device's stored bf16 intermediates) and 6e-2 end to end.
+zero weight gradients of every empty expert. Against the oracle computed
+from the inputs alone (end to end): every output of whole experts (G, U, H,
+O, dO, dG, dU, every dXp row and the expert's three weight gradients) - for
+the Zipf layer the coldest non-empty expert, a median one and the hottest
+one (about 12k rows: the longest K of the weight-gradient GEMMs and the
+cost-cut schedule), for the MXFP8 layer two experts; y and dx of 24 random
+tokens through all k of their experts; the xp bytes of 512 random rows. For
+the MXFP8 layer also stage by stage (the oracle fed the device's stored fp32
+intermediates, 2e-2) and, byte for byte, the E4M3 images of the two experts'
+rows (K-major H and dG | dU; token-major H, dO, Xp, dG | dU). Each piece is
+an exact sub-problem of the full layer: rows are independent in the forward
+and in dXp (every row operand is quantised along its own row), and an
+expert's weight gradients use only that expert's rows. Tolerances: 2e-2 for
+bf16, 6e-2 for MXFP8 end to end.
 """
 import numpy as np
 import pytest
@@ -23,6 +27,7 @@ from moe_inputs import WORKLOADS, make_inputs
 from oracle import moe_oracle as O
 
 from gpu_util import dev, host, rel_err
+import mx_layout as ML
 
 pytestmark = pytest.mark.gpu
 
@@ -77,36 +82,61 @@ class _Full:
         return O.ffn_backward(d_o, xp, *self.w(e), one, G, U, H)
 
 
-def _check_expert(F, e):
-    """Every output of expert e's rows and its weight gradients."""
+def _expert_device(F, e):
+    """Expert e's rows of the device's stored tensors (host, fp64)."""
     L = F.layer
     a, b = int(F.offsets[e]), int(F.offsets[e + 1])
     rows = np.arange(a, b)
-    xp = F.xp(rows)
     G, U, H = (_rows(t, rows) for t in L.saved())
-    f, S = F.wl.f, F.wl.T * F.wl.k
-    dgu = L.ws_ffn_bwd[:S * 2 * f * 2].view(torch.bfloat16).view(S, 2 * f)
-    dgu_rows = _rows(dgu, rows)
-    dG, dU = dgu_rows[:, :f], dgu_rows[:, f:]
-    d_o_gpu = _rows(L.d_o, rows)
+    dG, dU = (_rows(t, rows) for t in L.dgu())
+    return rows, dict(G=G, U=U, H=H, O=_rows(L.o, rows), dO=_rows(L.d_o, rows), dG=dG, dU=dU,
+                      dXp=_rows(L.dxp, rows), dW_gate=host(L.dw_gate[e]), dW_up=host(L.dw_up[e]),
+                      dW_down=host(L.dw_down[e]))
+
+
+def _check_expert(F, e):
+    """Every output of expert e's rows and its weight gradients, against the
+    oracle's forward and backward of those rows from the inputs alone."""
+    rows, dv = _expert_device(F, e)
+    xp = F.xp(rows)
     d_o_ref = F.d_o(rows)
-    Gr, Ur, Hr, Or = F.fwd(xp, e, h_in=H if F.mx else None)
-    if F.mx:  # stage by stage on the device's own stored dO, G, U, H, dG, dU
-        bwd = F.bwd(d_o_gpu, xp, e, G, U, H, dgdu_in=(dG, dU))
-    else:
-        bwd = F.bwd(d_o_ref, xp, e, Gr, Ur, Hr)
-    return {"G": rel_err(G, Gr), "U": rel_err(U, Ur), "H": rel_err(H, Hr), "O": rel_err(_rows(L.o, rows), Or),
-            "dO": rel_err(d_o_gpu, d_o_ref), "dG": rel_err(dG, bwd[4]), "dU": rel_err(dU, bwd[5]),
-            "dXp": rel_err(_rows(L.dxp, rows), bwd[0]),
-            "dW_gate": rel_err(host(L.dw_gate[e]), bwd[1][0]), "dW_up": rel_err(host(L.dw_up[e]), bwd[2][0]),
-            "dW_down": rel_err(host(L.dw_down[e]), bwd[3][0])}
+    Gr, Ur, Hr, Or = F.fwd(xp, e)
+    bwd = F.bwd(d_o_ref, xp, e, Gr, Ur, Hr)
+    ref = dict(G=Gr, U=Ur, H=Hr, O=Or, dO=d_o_ref, dG=bwd[4], dU=bwd[5], dXp=bwd[0],
+               dW_gate=bwd[1][0], dW_up=bwd[2][0], dW_down=bwd[3][0])
+    return {n: rel_err(dv[n], ref[n]) for n in ref}, (rows, dv, xp)
+
+
+def _check_expert_stage(F, e, rows, dv, xp):
+    """MXFP8: each GEMM stage of expert e on the device's own stored inputs."""
+    Gr, Ur, Hr, Or = F.fwd(xp, e, h_in=dv["H"])
+    bwd = F.bwd(dv["dO"], xp, e, dv["G"], dv["U"], dv["H"], dgdu_in=(dv["dG"], dv["dU"]))
+    ref = dict(G=Gr, U=Ur, H=Hr, O=Or, dG=bwd[4], dU=bwd[5], dXp=bwd[0],
+               dW_gate=bwd[1][0], dW_up=bwd[2][0], dW_down=bwd[3][0])
+    return {n: rel_err(dv[n], ref[n]) for n in ref}
+
+
+def _check_expert_images(F, e, rows, dv, xp):
+    """MXFP8: the E4M3 images of expert e's rows, byte for byte against the
+    oracle's encoding of the device's stored values."""
+    L, wl = F.layer, F.wl
+    S, d, f, E = wl.T * wl.k, wl.d, wl.f, wl.E
+    pf, pb = ML.fwd_pieces(S, d, f, E), ML.bwd_pieces(S, d, f, E)
+    a = int(rows[0])
+    dgu = np.concatenate([dv["dG"], dv["dU"]], axis=1)
+    ML.check_kmajor(L.ws_ffn_fwd, pf, "hq", "hs", dv["H"], f"q(H) expert {e}", S=S, row0=a)
+    ML.check_kmajor(L.ws_ffn_bwd, pb, "dguq", "dgus", dgu, f"q(dG|dU) expert {e}", S=S, row0=a)
+    for q, s_, vals in (("ht", "hts", dv["H"]), ("dot", "dots", dv["dO"]), ("xt", "xts", xp),
+                        ("dgut", "dguts", dgu)):
+        ML.check_token_major(L.ws_ffn_bwd, pb, q, s_, vals, F.offsets, f"q({q})", experts=[e], S=S,
+                             C=vals.shape[1])
 
 
 def _check_rows_fwd(F, e, rows):
     L = F.layer
     xp = F.xp(rows)
     G, U, H = (_rows(t, rows) for t in L.saved())
-    Gr, Ur, Hr, Or = F.fwd(xp, e, h_in=H if F.mx else None)
+    Gr, Ur, Hr, Or = F.fwd(xp, e)
     return {"G": rel_err(G, Gr), "U": rel_err(U, Ur), "H": rel_err(H, Hr), "O": rel_err(_rows(L.o, rows), Or)}
 
 
@@ -149,25 +179,34 @@ def _run_checks(name):
         assert not host(L.dw_gate[e]).any() and not host(L.dw_up[e]).any() and not host(L.dw_down[e]).any()
     print(f"counts: min {F.counts.min()} max {F.counts.max()} empty {len(empty)}", flush=True)
 
-    tol_stage = 2e-2
+    tol = 6e-2 if F.mx else 2e-2
     nonempty = np.nonzero(F.counts)[0]
     order = nonempty[np.argsort(F.counts[nonempty], kind="stable")]
-    for e in (int(order[0]), int(order[len(order) // 2])):
-        errs = _check_expert(F, e)
-        print(f"expert {e} (n={F.counts[e]}):", {n: f"{v:.2e}" for n, v in errs.items()}, flush=True)
-        bad = {n: v for n, v in errs.items() if not v <= tol_stage}
+    experts = [int(order[0]), int(order[len(order) // 2])]
+    if not F.mx:
+        experts.append(int(order[-1]))  # the hottest expert: every row, its weight gradients
+    for e in experts:
+        errs, (rows, dv, xp) = _check_expert(F, e)
+        print(f"expert {e} (n={F.counts[e]}), end to end:", {n: f"{v:.2e}" for n, v in errs.items()}, flush=True)
+        bad = {n: v for n, v in errs.items() if not v <= tol}
         assert not bad, (e, bad)
-    hot = int(order[-1])
-    hot_rows = np.sort(F.offsets[hot] + rng.choice(F.counts[hot], min(128, F.counts[hot]), replace=False))
-    errs = _check_rows_fwd(F, hot, hot_rows)
-    print(f"hottest expert {hot} (n={F.counts[hot]}), {len(hot_rows)} rows:",
-          {n: f"{v:.2e}" for n, v in errs.items()}, flush=True)
-    assert all(v <= tol_stage for v in errs.values()), errs
+        if F.mx:
+            stage = _check_expert_stage(F, e, rows, dv, xp)
+            print(f"expert {e}, stage by stage:", {n: f"{v:.2e}" for n, v in stage.items()}, flush=True)
+            bad = {n: v for n, v in stage.items() if not v <= 2e-2}
+            assert not bad, (e, bad)
+            _check_expert_images(F, e, rows, dv, xp)
+        del dv, xp
+    if F.mx:
+        hot = int(order[-1])
+        hot_rows = np.sort(F.offsets[hot] + rng.choice(F.counts[hot], min(128, F.counts[hot]), replace=False))
+        errs = _check_rows_fwd(F, hot, hot_rows)
+        print(f"expert {hot}, {len(hot_rows)} rows:", {n: f"{v:.2e}" for n, v in errs.items()}, flush=True)
+        assert all(v <= tol for v in errs.values()), errs
 
     toks = np.sort(rng.choice(wl.T, 24, replace=False))
     e2e = _check_tokens(F, toks)
     print("24 sampled tokens:", {n: f"{v:.2e}" for n, v in e2e.items()}, flush=True)
-    tol = 6e-2 if F.mx else 2e-2
     assert all(v <= tol for v in e2e.values()), e2e
 
 
