@@ -3,13 +3,15 @@
 One step = the whole hot path on one batch: route, dispatch, grouped SwiGLU
 FFN forward, combine, then combine backward, grouped FFN backward (dgrad and
 wgrad), router backward and dispatch backward. Inputs are seeded synthetic
-tensors already resident in HBM. The default workload is the bf16 layer with
-8 experts (T=8192, d_model=2048, top-4, d_ff=1024).
+tensors already resident in HBM. The default workload is the largest
+single-GPU configuration: the MXFP8 layer with 128 experts and balanced
+random routing (T=32768, d_model=4096, top-4, d_ff=1536), with the bf16 path
+of the same shape timed beside it for the MXFP8/bf16 ratio.
 
-Prints one JSON line: tokens/s for the step, plus the grouped-GEMM TFLOP/s,
-dispatch/combine GB/s, a roofline object for the dominant library call
-(timed with HIP events on the stream it runs on) and the fp64 oracle timed
-on the host cores.
+Prints one JSON line: tokens/s for the step, the grouped-GEMM TFLOP/s,
+dispatch/combine GB/s, a roofline object for the dominant grouped-GEMM
+kernel (its launches timed with HIP events that the library records on the
+stream it launches on) and the fp64 oracle timed on the host cores.
 """
 from __future__ import annotations
 
@@ -29,13 +31,38 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA / packed vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=None) -> str:
+    """Hash of the library's kernel sources (all of csrc, or the listed files
+    plus the build script, whose flags shape the code)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "routing_grouped_gemm_softmax_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
+    pkg = os.path.join(ROOT, "routing_grouped_gemm_softmax_amd")
+    csrc = os.path.join(pkg, "csrc")
+    names = sorted(os.listdir(csrc)) if files is None else sorted(files)
+    for n in names:
         with open(os.path.join(csrc, n), "rb") as fh:
             h.update(n.encode() + fh.read())
+    if files is not None:
+        with open(os.path.join(pkg, "build.py"), "rb") as fh:
+            h.update(b"build.py" + fh.read())
     return h.hexdigest()[:16]
+
+
+# Sources each grouped-GEMM kernel family is compiled from.
+GEMM_SOURCES = {
+    "mxfp8": ["gemm_mx.hip", "gemm_device.h", "grouped_gemm.h", "common.h", "mx_encode.h", "kernels.h"],
+    "bf16": ["gemm_bf16.hip", "gemm_device.h", "grouped_gemm.h", "common.h", "mx_encode.h", "kernels.h"],
+    "f32": ["gemm.hip", "grouped_gemm.h", "common.h", "kernels.h"],
+}
+GEMM_MODE_NAMES = ("fwd_gu", "fwd_down", "bwd_down", "bwd_gu", "wgrad")
+
+
+def gemm_mode_flops(wl, recompute=False):
+    """Algorithmic flops per step of each grouped-GEMM step (both weight
+    gradients together for wgrad; the recomputed gate/up GEMM adds to fwd_gu)."""
+    S, d, f = wl.T * wl.k, wl.d, wl.f
+    u = S * d * f
+    return {"fwd_gu": (8 if recompute else 4) * u, "fwd_down": 2 * u, "bwd_down": 2 * u, "bwd_gu": 4 * u,
+            "wgrad": 6 * u}
 
 
 def algorithmic_work(wl, recompute=False):
@@ -83,46 +110,283 @@ def gemm_compulsory_bytes(wl):
     return (fwd + bwd) * b
 
 
-def cpu_baseline(wl, inp, budget_s: float = 20.0):
-    """The fp64 oracle (as it stands) on the same workload, on the host cores.
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    When a full forward+backward would take far longer than ``budget_s`` of
-    CPU time, the oracle runs on the first T' tokens of the same inputs (same
-    d, E, k, f and weights; T' chosen from its measured fp64 rate) and the
-    rate is reported per token."""
+
+def cpu_baseline(wl, inp, budget_s: float = 20.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the same
+    workload, on the host cores; the rate is scaled to whole-layer tokens/s.
+
+    bf16 and fp32 layers: when a full forward+backward would take far longer
+    than ``budget_s`` of CPU time, the oracle runs on the first T' tokens of
+    the same inputs (same d, E, k, f and weights; T' from an fp64 rate
+    estimate). MXFP8 layers quantise every expert's weights in every call
+    whatever T', so the sample is per expert instead: the oracle's MXFP8 FFN
+    forward and backward of a few whole experts' rows with their weights,
+    plus the layer's token-level steps (dispatch plan, gather, combine and
+    their backward) on the same share of the tokens, scaled by E / experts."""
     from threadpoolctl import threadpool_info
 
     from moe_inputs import make_inputs
     from oracle import moe_oracle as O
+    import numpy as np
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    mx = wl.dtype == "mxfp8"
+    host = {"cores": threads, "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    if wl.dtype == "mxfp8":
+        E, k, T = wl.E, wl.k, wl.T
+        idx, gates = inp["topk_idx"], inp["topk_gate"].astype(np.float64)
+        t0 = time.perf_counter()
+        counts, offsets, row_of_slot, token_of_row = O.dispatch_plan(idx, E)
+        t_plan = time.perf_counter() - t0
+        n_e, t_ffn, e = 0, 0.0, 0
+        while e < E and (n_e < 2 or t_ffn < budget_s * 0.5) and n_e < 8:
+            a, b = int(offsets[e]), int(offsets[e + 1])
+            if a < b:
+                rows = np.arange(a, b)
+                tok = token_of_row[rows]
+                slot = np.argmax(row_of_slot[tok] == rows[:, None], axis=1)
+                one = np.array([0, b - a])
+                w = tuple(inp[n][e:e + 1] for n in ("w_gate", "w_up", "w_down"))
+                t1 = time.perf_counter()
+                xp = O.gather_rows(inp["x"], tok)
+                G, U, H, Ov = O.ffn_forward_mx(xp, *w, one)
+                d_o = gates[tok, slot][:, None] * np.asarray(inp["dy"][tok], dtype=np.float64)
+                O.ffn_backward_mx(d_o, xp, *w, one, G, U, H)
+                t_ffn += time.perf_counter() - t1
+                n_e += 1
+            e += 1
+        # Token-level steps on the same share of tokens (values do not change
+        # their cost): combine, combine backward and dispatch backward.
+        Ts = max(1, T * n_e // E)
+        sub_rows = row_of_slot[:Ts]
+        rr = np.arange(Ts * k).reshape(Ts, k)
+        o_sub = np.asarray(inp["x"][np.repeat(np.arange(Ts), k)], dtype=np.float64)
+        t1 = time.perf_counter()
+        O.combine(o_sub, gates[:Ts], rr)
+        O.combine_backward(inp["dy"][:Ts], o_sub, gates[:Ts], rr)
+        O.dispatch_backward(o_sub, rr)
+        t_tok = time.perf_counter() - t1
+        total = (t_ffn + t_tok) * E / n_e + t_plan
+        return {"value": T / total, "unit": "tokens/s", "kind": "oracle", **host,
+                "sample": f"fp64 MXFP8 oracle: FFN forward+backward of {n_e} whole experts' rows "
+                          f"({int(counts[:e].max())} rows each; {t_ffn:.1f} s) plus combine, combine backward and "
+                          f"dispatch backward on {Ts} tokens ({t_tok:.1f} s), scaled by E/{n_e} = {E / n_e:g}, "
+                          f"plus the dispatch plan of all {T} tokens ({t_plan:.2f} s); {wl.name}, T={T}"}
     sub, Ts = inp, wl.T
     flops = 18.0 * wl.T * wl.k * wl.d * wl.f
-    est_rate = 20e9 * threads  # fp64 flop/s, a first guess refined below
+    est_rate = 20e9 * threads  # fp64 flop/s, a first guess
     if flops / est_rate > budget_s:
         Ts = max(256, int(wl.T * budget_s * est_rate / flops) // 64 * 64)
         sub = make_inputs(wl.with_shape(T=Ts), 0)
     t0 = time.perf_counter()
-    fwd = O.layer_forward(sub, wl.k, mx=mx)
-    O.layer_backward(sub, fwd, mx=mx)
+    fwd = O.layer_forward(sub, wl.k)
+    O.layer_backward(sub, fwd)
     dt = time.perf_counter() - t0
     what = "the whole workload" if Ts == wl.T else f"the first {Ts} tokens of the workload's inputs"
-    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"one fp64 forward+backward ({'MXFP8 ' if mx else ''}oracle) of {what} "
-                      f"({wl.name}, T={wl.T}) on the host CPU, {dt:.1f} s"}
+    return {"value": Ts / dt, "unit": "tokens/s", "kind": "oracle", **host,
+            "sample": f"one fp64 forward+backward (oracle) of {what} ({wl.name}, T={wl.T}) on the host CPU, "
+                      f"{dt:.1f} s"}
 
 
-def load_traffic(workload: str, call: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+def load_traffic(workload: str, dtype: str, mode: str):
+    """HBM bytes per launch of grouped-GEMM step `mode` from the committed
+    rocprofv3 counter summary, if it was taken on the current sources of that
+    kernel family; else None."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as fh:
         rec = json.load(fh)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    k = rec.get("gemm_kernels", {}).get(mode)
+    if not k or k.get("kernel_source_hash") != kernel_source_hash(GEMM_SOURCES[dtype]):
         return None
-    return rec.get("calls", {}).get(call, {}).get("hbm_bytes")
+    return k.get("hbm_bytes_per_launch")
+
+
+def run_layer(wl, inp, args, M, torch, np):
+    """Time one layer: warmup, a survey of the grouped-GEMM steps (one step
+    each, kernel timer armed, untimed), the timed steps with the dominant
+    GEMM step's launches bracketed by events, then cold-cache steps.
+    Returns the figures of the JSON line for this layer."""
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+    def dev(a, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype)
+
+    t = {n: dev(inp[n]) for n in ("x", "dy", "w_gate", "w_up", "w_down")}
+    learned = wl.routing == "learned"
+    if learned:
+        t["w_router"] = dev(inp["w_router"])
+    else:
+        t["topk_idx"] = dev(inp["topk_idx"], torch.int32)
+        t["topk_gate"] = dev(inp["topk_gate"], torch.float32)
+    layer = M.MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, wl.dtype, learned_routing=learned, recompute=args.recompute)
+    stream = torch.cuda.current_stream()
+
+    def step(mark=None):
+        if learned:
+            layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_router=t["w_router"], mark=mark)
+        else:
+            layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=t["topk_idx"],
+                          topk_gate=t["topk_gate"], mark=mark)
+        layer.backward(t["dy"], mark=mark)
+
+    def events(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in ev:
+            e.record(stream)  # creates the HIP event the library will re-record
+        return ev
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Survey: each grouped-GEMM step's launch time, one untimed step each.
+    mode_flops = gemm_mode_flops(wl, args.recompute)
+    survey = {}
+    for mi, mode in enumerate(GEMM_MODE_NAMES):
+        st, sp = events(4), events(4)
+        torch.cuda.synchronize()
+        M.moe_kernel_timer(mi, st, sp)
+        step()
+        torch.cuda.synchronize()
+        n = M.moe_kernel_timer_count()
+        M.moe_kernel_timer(mi)
+        ms = sum(a.elapsed_time(b) for a, b in zip(st[:n], sp[:n]))
+        survey[mode] = {"launches_per_step": n, "ms_per_step": round(ms, 4),
+                        "tflops": round(mode_flops[mode] / (ms * 1e-3) / 1e12, 1) if ms > 0 else None}
+    dom = max(survey, key=lambda m: survey[m]["ms_per_step"])
+    dom_i = GEMM_MODE_NAMES.index(dom)
+    launches = survey[dom]["launches_per_step"]
+
+    # Events on the stream the library launches on, one after each call; the
+    # dominant GEMM step's launches bracketed by the library.
+    marks = []  # per step: list of (name, event)
+
+    def recorder(lst):
+        def mark(name):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            lst.append((name, ev))
+        return mark
+
+    kst, ksp = events(launches * args.steps), events(launches * args.steps)
+    torch.cuda.synchronize()
+    M.moe_kernel_timer(dom_i, kst, ksp)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        lst = []
+        start = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        lst.append(("start", start))
+        step(recorder(lst))
+        marks.append(lst)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    nk = M.moe_kernel_timer_count()
+    M.moe_kernel_timer(dom_i)
+    kdur = [a.elapsed_time(b) for a, b in zip(kst[:nk], ksp[:nk])]
+
+    per_call = {}
+    for lst in marks:
+        for (_, a), (name, b) in zip(lst[:-1], lst[1:]):
+            per_call.setdefault(name, []).append(a.elapsed_time(b))
+    avg_ms = {n: sum(v) / len(v) for n, v in per_call.items()}
+
+    work = algorithmic_work(wl, args.recompute)
+    gemm_ms = avg_ms["moe_grouped_ffn_fwd"] + avg_ms["moe_grouped_ffn_bwd"]
+    gemm_flops = work["moe_grouped_ffn_fwd"]["flops"] + work["moe_grouped_ffn_bwd"]["flops"]
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    peak = {"f32": PEAK_F32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS}[wl.dtype]
+    calls = {}
+    for n, ms in avg_ms.items():
+        rec = {"ms": round(ms, 4)}
+        if "flops" in work.get(n, {}):
+            rec["tflops"] = round(work[n]["flops"] / (ms * 1e-3) / 1e12, 2)
+        if "bytes" in work.get(n, {}):
+            rec["gbs"] = round(work[n]["bytes"] / (ms * 1e-3) / 1e9, 1)
+            rec["hbm_frac"] = round(rec["gbs"] / PEAK_HBM_GBS, 3)
+        calls[n] = rec
+    dc_names = [n for n in ("moe_dispatch", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd") if n in avg_ms]
+    dc_bytes = sum(work[n]["bytes"] for n in dc_names)
+    dc_ms = sum(avg_ms[n] for n in dc_names)
+
+    # Against the combined roofline max(flops / MFMA peak, compulsory bytes /
+    # HBM peak) of the two FFN calls (bf16 and fp32 layers: the MXFP8 calls
+    # also quantise, which this count does not model).
+    gemm_roof = None
+    if wl.dtype != "mxfp8":
+        gbytes = gemm_compulsory_bytes(wl)
+        floor_ms = max(gemm_flops / (peak * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+        gemm_roof = {"compulsory_bytes": gbytes, "floor_ms": round(floor_ms, 4),
+                     "bound": "mfma" if gemm_flops / (peak * 1e12) >= gbytes / (PEAK_HBM_GBS * 1e9) else "hbm",
+                     "frac": round(floor_ms / gemm_ms, 4)}
+    # The dominant kernel: algorithmic flops per launch (the step's flops
+    # over its launches per step) / the average launch duration over the
+    # timed region.
+    flops_per_launch = mode_flops[dom] / launches
+    avg_launch_ms = sum(kdur) / len(kdur)
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    traffic = load_traffic(wl.name, wl.dtype, dom) if not args.as_bf16 else None
+    kname = {"mxfp8": "gg_mx_kernel", "bf16": "gg_bf16_kernel", "f32": "grouped_gemm_kernel"}[wl.dtype]
+    roofline = {"kernel": f"{kname} ({dom}: {launches} launch(es) per step)", "bound": "mfma",
+                "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_launch_ms, 4),
+                "launches_timed": len(kdur)}
+    ms_per_step = elapsed / args.steps * 1e3
+    res = {
+        "value": round(wl.T * args.steps / elapsed, 1), "ms_per_step": round(ms_per_step, 4),
+        # bytes held between forward and backward beyond the inputs: the save
+        # buffer (G, U, H unless recomputed; MXFP8 weight copies), xp, o, and
+        # for MXFP8 the xp image.
+        "saved_bytes": {"save": layer.save.numel(), "xp": layer.xp.numel() * layer.xp.element_size(),
+                        "o": layer.o.numel() * layer.o.element_size(),
+                        "xp_mx": 0 if layer.xp_mx is None else layer.xp_mx.numel()},
+        "grouped_gemm": {"tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / peak, 4),
+                         "peak_tflops": peak, "ms": round(gemm_ms, 4), "combined_roofline": gemm_roof,
+                         "steps": survey},
+        "dispatch_combine": {"gbs": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
+                             "frac_of_hbm": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "ms": round(dc_ms, 4)},
+        "calls": calls,
+        "roofline": roofline,
+    }
+    # Expert-load diagnostics of the last step's routing (moe_load_stats, after
+    # the timed region).
+    stats = layer.load_stats().cpu().tolist()
+    res["expert_load"] = {n: round(v, 4) for n, v in zip(M.LOAD_STATS, stats)}
+    # Cold caches: before each of K further steps a 1 GiB fill (untimed)
+    # evicts the 256 MB MALL and the L2s; the step is timed by events around
+    # it alone. The timed region above runs with the caches as the previous
+    # step left them (warm).
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    cold_ms = sorted(a.elapsed_time(b) for a, b in cold)
+    med = cold_ms[len(cold_ms) // 2]
+    res["cold_cache"] = {"ms_per_step_median": round(med, 4), "tokens_per_s": round(wl.T / (med * 1e-3), 1),
+                         "flush_bytes": 1 << 30}
+    del flush, layer, t
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -130,10 +394,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bf16_e8")
+    ap.add_argument("--workload", default="mxfp8_balanced")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-twin", action="store_true",
+                    help="MXFP8 workloads: skip the bf16 run of the same shape")
     ap.add_argument("--as-bf16", action="store_true",
-                    help="run an MXFP8 workload's shape on the bf16 path (for the MXFP8/bf16 ratio)")
+                    help="run an MXFP8 workload's shape on the bf16 path only")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute: save no G, U, H; the backward recomputes them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -175,101 +441,16 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.as_bf16:
         wl = wl.with_shape(dtype="bf16")
-    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     inp = make_inputs(wl, 0)
-
-    def dev(a, dtype=dt):
-        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype)
-
-    t = {n: dev(inp[n]) for n in ("x", "dy", "w_gate", "w_up", "w_down")}
-    learned = wl.routing == "learned"
-    if learned:
-        t["w_router"] = dev(inp["w_router"])
-    else:
-        t["topk_idx"] = dev(inp["topk_idx"], torch.int32)
-        t["topk_gate"] = dev(inp["topk_gate"], torch.float32)
-    layer = M.MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, wl.dtype, learned_routing=learned, recompute=args.recompute)
-    stream = torch.cuda.current_stream()
-
-    def step(mark=None):
-        if learned:
-            layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_router=t["w_router"], mark=mark)
-        else:
-            layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=t["topk_idx"],
-                          topk_gate=t["topk_gate"], mark=mark)
-        layer.backward(t["dy"], mark=mark)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Events on the stream the library launches on, one after each call.
-    marks = []  # per step: list of (name, event)
-
-    def recorder(lst):
-        def mark(name):
-            ev = torch.cuda.Event(enable_timing=True)
-            ev.record(stream)
-            lst.append((name, ev))
-        return mark
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        lst = []
-        start = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        lst.append(("start", start))
-        step(recorder(lst))
-        marks.append(lst)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    per_call = {}
-    for lst in marks:
-        for (_, a), (name, b) in zip(lst[:-1], lst[1:]):
-            per_call.setdefault(name, []).append(a.elapsed_time(b))
-    avg_ms = {n: sum(v) / len(v) for n, v in per_call.items()}
-
-    work = algorithmic_work(wl, args.recompute)
-    gemm_ms = avg_ms["moe_grouped_ffn_fwd"] + avg_ms["moe_grouped_ffn_bwd"]
-    gemm_flops = work["moe_grouped_ffn_fwd"]["flops"] + work["moe_grouped_ffn_bwd"]["flops"]
-    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    peak = {"f32": PEAK_F32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS}[wl.dtype]
-    calls = {}
-    for n, ms in avg_ms.items():
-        rec = {"ms": round(ms, 4)}
-        if "flops" in work.get(n, {}):
-            rec["tflops"] = round(work[n]["flops"] / (ms * 1e-3) / 1e12, 2)
-        if "bytes" in work.get(n, {}):
-            rec["gbs"] = round(work[n]["bytes"] / (ms * 1e-3) / 1e9, 1)
-            rec["hbm_frac"] = round(rec["gbs"] / PEAK_HBM_GBS, 3)
-        calls[n] = rec
-    dc_names = [n for n in ("moe_dispatch", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd") if n in avg_ms]
-    dc_bytes = sum(work[n]["bytes"] for n in dc_names)
-    dc_ms = sum(avg_ms[n] for n in dc_names)
-
-    # Against the combined roofline max(flops / MFMA peak, compulsory bytes /
-    # HBM peak) of the two FFN calls (bf16 and fp32 layers: the MXFP8 calls
-    # also quantise, which this count does not model).
-    gemm_roof = None
-    if wl.dtype != "mxfp8":
-        gbytes = gemm_compulsory_bytes(wl)
-        floor_ms = max(gemm_flops / (peak * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e3
-        gemm_roof = {"compulsory_bytes": gbytes, "floor_ms": round(floor_ms, 4),
-                     "bound": "mfma" if gemm_flops / (peak * 1e12) >= gbytes / (PEAK_HBM_GBS * 1e9) else "hbm",
-                     "frac": round(floor_ms / gemm_ms, 4)}
-    dom = max(("moe_grouped_ffn_fwd", "moe_grouped_ffn_bwd"), key=lambda n: avg_ms[n])
-    achieved = work[dom]["flops"] / (avg_ms[dom] * 1e-3) / 1e12
-    ms_per_step = elapsed / args.steps * 1e3
+    res = run_layer(wl, inp, args, M, torch, np)
     out = {
         "metric": "MoE layer fwd+bwd tokens/s and grouped-GEMM TFLOP/s (% MFMA peak), 1 GPU",
-        "value": round(wl.T * args.steps / elapsed, 1),
+        "value": res.pop("value"),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": res.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -277,46 +458,18 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": dict(wl.describe(), parallelism="none (1 GPU)",
                        **({"recompute": True} if args.recompute else {})),
-        # bytes held between forward and backward beyond the inputs: the save
-        # buffer (G, U, H unless recomputed; MXFP8 weight copies), xp, o, and
-        # for MXFP8 the xp image.
-        "saved_bytes": {"save": layer.save.numel(), "xp": layer.xp.numel() * layer.xp.element_size(),
-                        "o": layer.o.numel() * layer.o.element_size(),
-                        "xp_mx": 0 if layer.xp_mx is None else layer.xp_mx.numel()},
-        "grouped_gemm": {"tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / peak, 4),
-                         "peak_tflops": peak, "ms": round(gemm_ms, 4), "combined_roofline": gemm_roof},
-
-        "dispatch_combine": {"gbs": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
-                             "frac_of_hbm": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                             "ms": round(dc_ms, 4)},
-        "calls": calls,
-        "roofline": {"kernel": f"{dom} (its grouped GEMM kernels, back to back)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": load_traffic(wl.name, dom)},
     }
-    # Expert-load diagnostics of the last step's routing (moe_load_stats, after
-    # the timed region).
-    stats = layer.load_stats().cpu().tolist()
-    out["expert_load"] = {n: round(v, 4) for n, v in zip(M.LOAD_STATS, stats)}
-    # Cold caches: before each of K further steps a 1 GiB fill (untimed)
-    # evicts the 256 MB MALL and the L2s; the step is timed by events around
-    # it alone. The timed region above runs with the caches as the previous
-    # step left them (warm).
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    cold = []
-    for _ in range(args.steps):
-        flush.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        step()
-        b.record(stream)
-        cold.append((a, b))
-    torch.cuda.synchronize()
-    cold_ms = sorted(a.elapsed_time(b) for a, b in cold)
-    med = cold_ms[len(cold_ms) // 2]
-    out["cold_cache"] = {"ms_per_step_median": round(med, 4), "tokens_per_s": round(wl.T / (med * 1e-3), 1),
-                         "flush_bytes": 1 << 30}
-    del flush
+    out.update(res)
+    if wl.dtype == "mxfp8" and not args.no_twin:
+        # The bf16 path of the same shape and inputs (bf16 values), for the
+        # MXFP8/bf16 ratio; its own timed steps, after the MXFP8 layer's.
+        tw = run_layer(wl.with_shape(dtype="bf16"), inp, args, M, torch, np)
+        out["bf16_twin"] = {"value": tw["value"], "unit": "tokens/s", "ms_per_step": tw["ms_per_step"],
+                            "grouped_gemm": {k: tw["grouped_gemm"][k] for k in ("tflops", "frac_of_peak", "ms",
+                                                                                "peak_tflops", "steps")},
+                            "dispatch_combine": tw["dispatch_combine"], "calls": tw["calls"],
+                            "roofline": tw["roofline"], "cold_cache": tw["cold_cache"]}
+        out["mxfp8_over_bf16"] = round(out["value"] / tw["value"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(out), flush=True)

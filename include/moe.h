@@ -96,7 +96,7 @@ enum moe_op {
 };
 
 /* Device-side status bits, read back with moe_read_device_status. */
-enum moe_device_status { MOE_DEV_OK = 0, MOE_DEV_BAD_EXPERT = 1 };
+enum moe_device_status { MOE_DEV_OK = 0, MOE_DEV_BAD_EXPERT = 1, MOE_DEV_DUP_EXPERT = 2 };
 
 /* Layer options, bits of moe_shape.flags. */
 enum moe_flags {
@@ -172,7 +172,9 @@ int moe_route(const void* x, const void* w_router, const moe_shape* shape,
  * row_of_slot[T][k] gives the row of every (token, slot); token_of_row[S] the
  * inverse; xp[S][d] (layer dtype) is x gathered into that order.
  * An expert id outside [0, E) is not routed (its row_of_slot is -1), and the
- * device status word in `ws` is set to MOE_DEV_BAD_EXPERT.
+ * device status word in `ws` gets MOE_DEV_BAD_EXPERT. A token that names the
+ * same expert in two slots sets MOE_DEV_DUP_EXPERT (both slots are routed,
+ * to consecutive rows of that expert).
  * xp_mx_out (MXFP8 layers only; NULL to skip): receives the MXFP8 image of
  * xp (moe_mx_image_size(S, d) bytes, 256-byte aligned), written by the same
  * pass that writes xp's rows. Must be NULL for fp32 and bf16 layers.
@@ -186,8 +188,9 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* shape,
                  size_t ws_bytes, void* stream);
 
 /* Reads the device status word that the last moe_dispatch on `ws` wrote.
- * Synchronises `stream`. For debugging and tests; returns MOE_DEV_* bits, or a
- * negative moe_status on failure. */
+ * Synchronises `stream`. For debugging and tests; returns MOE_DEV_* bits
+ * (0 when every token names k distinct experts in [0, E)), or a negative
+ * moe_status on failure. */
 int moe_read_device_status(const void* ws, void* stream);
 
 /* Grouped SwiGLU FFN forward over the per-expert row ranges in `offsets`
@@ -255,17 +258,29 @@ int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, 
  *   set of token t, 0 elsewhere (fp32 [T][E]);
  *   dw_router[d][E] (layer dtype) = x^T · dlogits, reduced over T in a fixed
  *   order (deterministic split over token blocks).
- * ws: moe_workspace_size(MOE_OP_ROUTE_BWD) bytes. */
+ * ws: moe_workspace_size(MOE_OP_ROUTE_BWD) bytes.
+ * Passage: the router gradient of the layer specification (softmax over the
+ * router logits with the top-k gates renormalised, differentiated); the
+ * router itself: noticiarioia.com page, "Mudança de arquitetura e ganhos de
+ * desempenho" (4 of E experts per token). */
 int moe_route_bwd(const void* x, const void* w_router, const int32_t* topk_idx,
                   const float* topk_gate, const float* dgate, const moe_shape* shape,
                   float* dlogits_out, void* dw_router_out, void* ws, size_t ws_bytes,
                   void* stream);
 
 /* Dispatch backward: dx[t] = sum_j dxp[row_of_slot[t,j]]
- * (+ sum_e dlogits[t,e] * w_router[:,e] when dlogits and w_router are both
- * non-NULL), accumulated in fp32, one rounding to the layer dtype.
+ * (+ sum_e dlogits[t,e] * w_router[:,e] over every non-zero dlogits[t,e]
+ * when dlogits and w_router are both non-NULL), accumulated in fp32 (the k
+ * rows in slot order, then the router columns in increasing expert order),
+ * one rounding to the layer dtype. dlogits may be dense; rows with at most
+ * k non-zeros (as moe_route_bwd writes them) take a faster path with the
+ * same result. Slots with row -1 contribute nothing.
  * ws: moe_workspace_size(MOE_OP_DISPATCH_BWD) bytes (needed only with the
- * router term). */
+ * router term).
+ * Passage: the adjoint of the placement of routed rows into the experts'
+ * input buffers (bytechap.com page, "Cómo funciona"; unite.ai page,
+ * "Parallelismo, precisione e tecniche di memoria"), plus the router term
+ * of the layer specification's router gradient. */
 int moe_dispatch_bwd(const void* dxp, const int32_t* row_of_slot, const float* dlogits,
                      const void* w_router, const moe_shape* shape, void* dx_out, void* ws,
                      size_t ws_bytes, void* stream);

@@ -18,7 +18,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WO
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
  MOE_OP_ROUTE_BWD, MOE_OP_DISPATCH_BWD) = range(6)
-MOE_DEV_BAD_EXPERT = 1
+MOE_DEV_BAD_EXPERT, MOE_DEV_DUP_EXPERT = 1, 2
 MOE_FLAG_RECOMPUTE = 1
 GEMM_MODES = ("fwd_gu", "fwd_down", "bwd_down", "bwd_gu", "wgrad")  # enum moe_gemm_mode order
 

@@ -59,6 +59,9 @@ size_t dispatch_workspace(int T, int E) {
   return 256 + align256(sizeof(int32_t) * nch * E) + align256(sizeof(int32_t) * nch);
 }
 
+// Per chunk: the LDS histogram of expert ids, and the chunk's fault bits
+// (MOE_DEV_BAD_EXPERT: an id outside [0, E); MOE_DEV_DUP_EXPERT: one token
+// names the same expert in two slots). One thread per token.
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
                                                              int ct, DispatchWs w) {
   __shared__ int hist[256];
@@ -67,15 +70,24 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   hist[tid] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
-  const int64_t s0 = static_cast<int64_t>(c) * ct * k;
-  const int64_t s1 = min(static_cast<int64_t>(T), static_cast<int64_t>(c + 1) * ct) * k;
+  const int64_t t0 = static_cast<int64_t>(c) * ct;
+  const int64_t t1 = min(static_cast<int64_t>(T), static_cast<int64_t>(c + 1) * ct);
   int my_bad = 0;
-  for (int64_t s = s0 + tid; s < s1; s += 256) {
-    const int e = idx[s];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);  // integer counts: order-independent
-    else my_bad = 1;
+  for (int64_t t = t0 + tid; t < t1; t += 256) {
+    int ids[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ids[j] = j < k ? idx[t * k + j] : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      const int e = ids[j];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);  // integer counts: order-independent
+      else my_bad |= 1;
+#pragma unroll
+      for (int i = 0; i < j; ++i) my_bad |= (ids[i] == e) ? 2 : 0;
+    }
   }
-  if (my_bad) bad = 1;
+  if (my_bad) atomicOr(&bad, my_bad);
   __syncthreads();
   if (tid < E) w.chunk_counts[static_cast<int64_t>(c) * E + tid] = hist[tid];
   if (tid == 0) w.chunk_bad[c] = bad;
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
     if (tid == 0) {
       int bad = 0;
       for (int cc = 0; cc < nch; ++cc) bad |= w.chunk_bad[cc];
-      w.status[0] = bad ? 1 : 0;
+      w.status[0] = bad;
     }
   }
   __syncthreads();
@@ -226,10 +238,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 
 static hipError_t dispatch_impl(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E, int k,
                                 int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
-                                void* xp, const MxImage* mx, void* ws, hipStream_t s) {
+                                void* xp, const MxImage* mx, void* ws, hipStream_t s, int32_t* status = nullptr) {
   const int ct = chunk_tokens(T, E);
   const int nch = (T + ct - 1) / ct;
   DispatchWs w = carve(ws, nch, E);
+  if (status != nullptr) w.status = status;  // the caller's status word instead of the workspace's
   int bits = 0;
   while ((1 << bits) < E) ++bits;
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(256), 0, s, topk_idx, T, E, k, ct, w);
@@ -477,9 +490,13 @@ __global__ void transpose_router_kernel(const T* __restrict__ w, int d, int E, T
 }
 
 // dx[t] = sum_j dxp[row(t,j)] (+ sum_{e: dl[t][e] != 0} dl[t][e] * W_rT[e]).
-// dl is zero off the chosen set, so only those (at most k) columns are read.
-// When a token has whole waves (lpt >= 64) each wave finds them with one
-// ballot per 64 experts; narrower rows scan the E values per lane.
+// The router backward leaves dl zero off the token's chosen set, so a token
+// has at most K non-zero columns: those are found once (when a token has
+// whole waves, lpt >= 64, with one ballot per 64 experts; narrower rows scan
+// the E values per lane) and their W_rT rows loaded beside the dxp rows. A
+// token with more non-zero columns (a caller's dense dlogits, e.g. from an
+// added loss term) takes every non-zero column in increasing expert order,
+// which is also the order of the first path, so both give the same bits.
 template <typename T, int K>
 __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__ dxp, const int32_t* __restrict__ row_of_slot,
                                                            const float* __restrict__ dl, const T* __restrict__ wt,
@@ -493,17 +510,19 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
   int rows[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) rows[j] = row_of_slot[static_cast<int64_t>(t) * K + j];
-  // The token's router columns: (expert, dl) pairs, at most K.
+  // The token's router columns: (expert, dl) pairs, the first K of them, and
+  // how many there are in all.
   int ce[K];
   float cv[K];
-  int nr = 0;
+  int nr = 0, nnz = 0;
+  const float* dlt = dl != nullptr ? dl + static_cast<int64_t>(t) * E : nullptr;
   if (dl != nullptr) {
-    const float* dlt = dl + static_cast<int64_t>(t) * E;
     if (lpt >= kWave) {
       const int lane = threadIdx.x & (kWave - 1);
       for (int c0 = 0; c0 < E; c0 += kWave) {
         const float c = (c0 + lane < E) ? dlt[c0 + lane] : 0.0f;
         uint64_t m = __ballot(c != 0.0f);
+        nnz += __popcll(m);
         while (m != 0 && nr < K) {
           const int b = __ffsll(static_cast<long long>(m)) - 1;
           m &= m - 1;
@@ -513,23 +532,26 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
         }
       }
     } else {
-      for (int e = 0; e < E && nr < K; ++e) {
+      for (int e = 0; e < E; ++e) {
         const float c = dlt[e];
         if (c != 0.0f) {
-          ce[nr] = e;
-          cv[nr] = c;
-          ++nr;
+          if (nr < K) {
+            ce[nr] = e;
+            cv[nr] = c;
+            ++nr;
+          }
+          ++nnz;
         }
       }
     }
   }
+  const bool dense = nnz > K;  // the same for every lane of the token
   for (int v = sub; v < nvec; v += lpt) {
-    // The router term has at most K non-zero columns (dl is zero off the
-    // token's chosen set); slots past nr load row 0 and are selected out.
+    // Slots past nr load row 0 and are selected out.
     uint4 raw[K], wraw[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) raw[j] = ld16(dxp + max(rows[j], 0) * re + v * VE);
-    if (dl != nullptr) {
+    if (dl != nullptr && !dense) {
 #pragma unroll
       for (int r = 0; r < K; ++r) wraw[r] = ld16(wt + (r < nr ? ce[r] : 0) * re + v * VE);
     }
@@ -544,7 +566,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
 #pragma unroll
       for (int i = 0; i < VE; ++i) acc[i] = ok ? acc[i] + gv[i] : acc[i];
     }
-    if (dl != nullptr) {
+    if (dl != nullptr && !dense) {
 #pragma unroll
       for (int r = 0; r < K; ++r) {
         float wv[VE];
@@ -555,6 +577,15 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
           const float a = fmaf(cv[r], wv[i], acc[i]);
           acc[i] = ok ? a : acc[i];
         }
+      }
+    } else if (dense) {
+      for (int e = 0; e < E; ++e) {
+        const float c = dlt[e];
+        if (c == 0.0f) continue;
+        float wv[VE];
+        unpack16(ld16(wt + e * re + v * VE), wv);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) acc[i] = fmaf(c, wv[i], acc[i]);
       }
     }
     st16(dx + t * re + v * VE, pack16(acc));

@@ -14,7 +14,7 @@ on the exact fp64 value. Checks, max|gpu - ref| / max|ref| per tensor:
 * end to end against the oracle's MXFP8 layer from the inputs alone (6e-2,
   the bound set for MXFP8 layers), every tensor;
 * the distance from the unquantised layer, per tensor, printed and held under
-  the bound that follows from the E4M3 rounding error (0.2; see the oracle's
+  the bound that follows from the E4M3 rounding error (0.25; see the oracle's
   pins): E4M3 keeps 3 mantissa bits, so the quantised layer itself sits 4-14%
   from the unquantised one.
 """
@@ -32,7 +32,7 @@ pytestmark = pytest.mark.gpu
 
 STAGE_TOL = 2e-2
 E2E_TOL = 6e-2
-MX_LAYER_BOUND = 0.2  # distance of any MXFP8 layer from the unquantised one
+MX_LAYER_BOUND = 0.25  # distance of any MXFP8 layer from the unquantised one (measured up to 0.19)
 
 CASES = {
     # name: (workload, shape overrides, popularity override for Zipf routing)

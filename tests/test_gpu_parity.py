@@ -129,3 +129,76 @@ def test_recompute_matches_oracle_and_saved_layer(case):
         assert torch.equal(getattr(rec, n), getattr(ref, n)), n
     for a, b in zip(rec.saved(), ref.saved()):
         assert torch.equal(a, b)
+
+
+def test_duplicate_expert_in_a_token_sets_status():
+    """A token that names one expert in two slots sets MOE_DEV_DUP_EXPERT; both
+    slots are still routed, to consecutive rows of that expert, as the
+    oracle's stable counting sort places them. An out-of-range id beside it
+    sets MOE_DEV_BAD_EXPERT too."""
+    import routing_grouped_gemm_softmax_amd as M
+    wl = WORKLOADS["bf16_zipf"].with_shape(T=700, d=64, E=8, f=64)
+    inp = make_inputs(wl, 5, weights=False)
+    idx = inp["topk_idx"].copy()
+    idx[9] = [3, 3, 1, 2]
+    idx[650] = [0, 5, 7, 5]
+    layer = M.MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, "bf16", learned_routing=False)
+    x = dev(inp["x"], torch.bfloat16)
+
+    def run(ids):
+        M.moe_dispatch(x, dev(ids, torch.int32), layer.shape, layer.counts, layer.offsets, layer.row_of_slot,
+                       layer.token_of_row, layer.xp, layer.ws_dispatch)
+        return M.moe_read_device_status(layer.ws_dispatch)
+
+    assert run(idx) == M._lib.MOE_DEV_DUP_EXPERT
+    counts, offsets, rs, tor = O.dispatch_plan(idx, wl.E)
+    np.testing.assert_array_equal(host(layer.counts), counts)
+    np.testing.assert_array_equal(host(layer.row_of_slot), rs)
+    np.testing.assert_array_equal(host(layer.token_of_row), tor)
+    assert host(layer.row_of_slot)[9, 1] == host(layer.row_of_slot)[9, 0] + 1
+    idx2 = idx.copy()
+    idx2[100, 3] = 8
+    assert run(idx2) == M._lib.MOE_DEV_DUP_EXPERT | M._lib.MOE_DEV_BAD_EXPERT
+    assert run(inp["topk_idx"]) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,E", [(64, 8), (512, 128)], ids=["narrow_rows", "wave_rows_E128"])
+def test_dispatch_bwd_dense_dlogits(dtype, d, E):
+    """moe_dispatch_bwd with dlogits rows that have more than k non-zeros (a
+    caller's dense router gradient): dx = sum_j dxp[row(t,j)] + dlogits[t] W_r^T
+    over every column. Rows with k or fewer non-zeros take the fast path;
+    rows with exactly k + 1 and with all E non-zero take the dense one."""
+    import routing_grouped_gemm_softmax_amd as M
+    k = 4
+    wl = WORKLOADS["bf16_e8"].with_shape(T=300, d=d, E=E, k=k, f=64, dtype=dtype)
+    inp = make_inputs(wl, 6, weights=False)
+    rng = np.random.default_rng(6)
+    logits = rng.standard_normal((wl.T, E))
+    idx = O.topk_experts(logits, k)
+    counts, offsets, rs, tor = O.dispatch_plan(idx, E)
+    S = wl.T * k
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dxp = rng.standard_normal((S, d)).astype(np.float32)
+    if dtype == "bf16":
+        from moe_inputs import bf16_round
+        dxp = bf16_round(dxp)
+    dl = np.zeros((wl.T, E), dtype=np.float32)
+    np.put_along_axis(dl, idx.astype(np.int64), rng.standard_normal((wl.T, k)).astype(np.float32), axis=1)
+    dl[0::3] = rng.standard_normal((len(dl[0::3]), E)).astype(np.float32)           # all E non-zero
+    extra = [t for t in range(1, wl.T, 3)]
+    for t in extra:                                                                   # exactly k + 1
+        off = [e for e in range(E) if e not in idx[t]][0]
+        dl[t, off] = 0.5
+    shape = M.MoeShape.make(wl.T, d, E, k, 64, dtype)
+    ws = torch.empty(max(M.workspace_size(M._lib.MOE_OP_DISPATCH_BWD, shape), 256), dtype=torch.uint8,
+                     device="cuda")
+    dx = torch.empty(wl.T, d, dtype=tdt, device="cuda")
+    print(f"[gpu] dense dlogits {dtype} d={d} E={E}", flush=True)
+    M.moe_dispatch_bwd(dev(dxp, tdt), dev(rs, torch.int32), dev(dl, torch.float32), dev(inp["w_router"], tdt),
+                       shape, dx, ws)
+    torch.cuda.synchronize()
+    want = O.dispatch_backward(dxp, rs, dl.astype(np.float64) @ np.asarray(inp["w_router"], np.float64).T)
+    err = rel_err(host(dx), want)
+    print(f"dx err {err:.2e}", flush=True)
+    assert err <= TOL[dtype], err

@@ -231,11 +231,12 @@ def test_stage_inputs_replace_the_computed_operands():
 # of about 2.6% per operand, and every output passes through two to four
 # quantised GEMM operands (y: Xp, W_gate|W_up, H, W_down; the weight
 # gradients add dO and dG|dU), with the SwiGLU nonlinearity between. The
-# measured distances at these shapes are 4-13% (G, U, H smallest; the
-# weight gradients, whose K runs over few tokens per expert, largest). A
-# mis-scaled block exponent, a dropped quantisation or a wrong operand shows
-# as a distance of 0.2 and more, or as exactly zero.
-MX_LAYER_BOUND = 0.2
+# measured distances are 4-13% at these shapes and up to 19% for weight
+# gradients whose K runs over only 16 tokens per expert (fewer terms to
+# average the rounding errors out). A dropped quantisation shows as exactly
+# zero; a mis-scaled block exponent or a wrong operand is caught exactly by
+# the brute-force pin above, this bound only catches gross departures.
+MX_LAYER_BOUND = 0.25
 
 
 @pytest.mark.parametrize("over", [dict(T=256, d=128, E=8, f=128), dict(T=512, d=256, E=16, f=256)],
