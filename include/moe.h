@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 enum moe_status {
   MOE_OK = 0,
@@ -186,6 +186,23 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* shape,
                  int32_t* counts_out, int32_t* offsets_out, int32_t* row_of_slot_out,
                  int32_t* token_of_row_out, void* xp_out, uint8_t* xp_mx_out, void* ws,
                  size_t ws_bytes, void* stream);
+
+/* moe_dispatch for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, outputs and errors as moe_dispatch, minus ws / ws_bytes:
+ * the workspace is a 1 MiB array inside the library, one per GPU, held until
+ * the process ends. The call allocates and frees nothing. It fails with
+ * MOE_ERR_WORKSPACE, enqueuing nothing, when moe_workspace_size(
+ * MOE_OP_DISPATCH, shape) exceeds 1 MiB (above 2,064,384 tokens at E = 64,
+ * 1,039,872 at E = 128, 521,728 at E = 256), and with MOE_ERR_HIP when
+ * `stream` belongs to a device
+ * other than the current one. Every call on one GPU shares that GPU's
+ * array: calls that may overlap there (other streams, other host threads)
+ * race, so the caller serialises them. The device status word lives in the
+ * array and cannot be read back; callers that need it use moe_dispatch. */
+int moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, const moe_shape* shape,
+                         int32_t* counts_out, int32_t* offsets_out, int32_t* row_of_slot_out,
+                         int32_t* token_of_row_out, void* xp_out, uint8_t* xp_mx_out, void* stream);
 
 /* Reads the device status word that the last moe_dispatch on `ws` wrote.
  * Synchronises `stream`. For debugging and tests; returns MOE_DEV_* bits

@@ -57,6 +57,7 @@ SIGNATURES = {
     "moe_mx_image_size": (_SZ, [ctypes.c_int64, ctypes.c_int64]),
     "moe_route": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _SZ, _P]),
     "moe_dispatch": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_dispatch_noalloc": (ctypes.c_int, [_P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _P]),
     "moe_read_device_status": (ctypes.c_int, [_P, _P]),
     "moe_grouped_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SHAPE, _P, _SZ, _P, _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _SHAPE, _P, _P]),
@@ -166,6 +167,16 @@ def moe_dispatch(x, topk_idx, shape, counts, offsets, row_of_slot, token_of_row,
     _check("moe_dispatch", load().moe_dispatch(
         _ptr(x), _ptr(topk_idx), ctypes.byref(shape), _ptr(counts), _ptr(offsets), _ptr(row_of_slot),
         _ptr(token_of_row), _ptr(xp), _ptr(xp_mx), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_dispatch_noalloc(x, topk_idx, shape, counts, offsets, row_of_slot, token_of_row, xp, stream=None,
+                         xp_mx=None):
+    _expect(topk_idx, torch.int32, shape.T * shape.k, "topk_idx")
+    _expect(counts, torch.int32, shape.E, "counts")
+    _expect(offsets, torch.int32, shape.E + 1, "offsets")
+    _check("moe_dispatch_noalloc", load().moe_dispatch_noalloc(
+        _ptr(x), _ptr(topk_idx), ctypes.byref(shape), _ptr(counts), _ptr(offsets), _ptr(row_of_slot),
+        _ptr(token_of_row), _ptr(xp), _ptr(xp_mx), _stream(stream)))
 
 
 def moe_read_device_status(ws, stream=None) -> int:

@@ -238,6 +238,26 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* s, int
   return MOE_OK;
 }
 
+int moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, const moe_shape* s, int32_t* counts_out,
+                         int32_t* offsets_out, int32_t* row_of_slot_out, int32_t* token_of_row_out, void* xp_out,
+                         uint8_t* xp_mx_out, void* stream) {
+  CHECK(check_shape(s));
+  NEED(x); NEED(topk_idx); NEED(counts_out); NEED(offsets_out); NEED(row_of_slot_out); NEED(token_of_row_out);
+  NEED(xp_out);
+  MX_IMAGE_OK(xp_mx_out, s);
+  const size_t need = moe::dispatch_workspace((int)s->T, (int)s->E), have = moe::dispatch_noalloc_max();
+  if (need > have)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_dispatch_noalloc: this shape needs %zu bytes of scratch; the library's array holds %zu "
+                "(use moe_dispatch with a workspace)", need, have);
+  moe::MxImage im{nullptr, nullptr};
+  if (xp_mx_out) im = moe::mx_image(xp_mx_out, s->T * s->k, s->d);
+  LAUNCH(moe::launch_dispatch_noalloc(x, topk_idx, elem_bytes(s->dtype), (int)s->T, (int)s->d, (int)s->E,
+                                      (int)s->k, counts_out, offsets_out, row_of_slot_out, token_of_row_out, xp_out,
+                                      im, as_stream(stream)));
+  return MOE_OK;
+}
+
 int moe_read_device_status(const void* ws, void* stream) {
   if (!ws) return fail(MOE_ERR_INVALID_ARG, "moe_read_device_status: ws is NULL");
   int32_t v = 0;

@@ -27,6 +27,7 @@
 #include "mx_encode.h"
 
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 namespace moe {
@@ -275,6 +276,59 @@ hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int
                               int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row, void* xp,
                               MxImage xp_mx, void* ws, hipStream_t s) {
   return dispatch_impl(x, topk_idx, 2, T, d, E, k, counts, offsets, row_of_slot, token_of_row, xp, &xp_mx, ws, s);
+}
+
+// The allocation-free dispatch's workspace: one array per GPU (each device
+// holds its own copy of a __device__ variable), alive until the process
+// ends. Host code never passes the array's name to a kernel: on the host the
+// name is only a stand-in, so each device's address is looked up once with
+// that device current and kept. Nothing in it must start at zero: the count
+// pass writes every [chunk][expert] entry and every chunk's fault bits, and
+// the placement pass writes the status word. Calls that overlap on one GPU
+// (other streams, other host threads) share the array and race.
+constexpr size_t kNoAllocBytes = size_t(1) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+
+size_t dispatch_noalloc_max() { return kNoAllocBytes; }
+
+static hipError_t scratch_on_current_device(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_dispatch_noalloc(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E,
+                                   int k, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                                   int32_t* token_of_row, void* xp, MxImage xp_mx, hipStream_t s) {
+  if (dispatch_workspace(T, E) > kNoAllocBytes) return hipErrorInvalidValue;
+  // The array's address is the current device's: a stream of another device
+  // would run the kernels there with this device's address.
+  if (s != nullptr) {
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != cur) return hipErrorInvalidDevice;
+  }
+  void* ws = nullptr;
+  const hipError_t err = scratch_on_current_device(&ws);
+  if (err != hipSuccess) return err;
+  return dispatch_impl(x, topk_idx, elem_bytes, T, d, E, k, counts, offsets, row_of_slot, token_of_row, xp,
+                       xp_mx.q != nullptr ? &xp_mx : nullptr, ws, s);
 }
 
 // Row kernels take the slot count K as a template argument and issue the

@@ -109,6 +109,15 @@ hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gat
                                  const int32_t* row_of_slot, int T, int d, int k, void* d_o,
                                  MxImage d_o_mx, float* dgate, hipStream_t s);
 
+// Dispatch whose workspace is the library's own device array (one per GPU,
+// dispatch_noalloc_max() bytes) instead of a caller buffer: no allocation.
+// xp_mx.q == nullptr: no MXFP8 image. Returns hipErrorInvalidValue when the
+// shape needs more than the array holds, or when hipGetSymbolAddress fails.
+size_t dispatch_noalloc_max();
+hipError_t launch_dispatch_noalloc(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E,
+                                   int k, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                                   int32_t* token_of_row, void* xp, MxImage xp_mx, hipStream_t s);
+
 // MXFP8 (mxfp8.hip)
 hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,
                                  uint8_t* scale, hipStream_t s);

@@ -109,6 +109,21 @@ int main() {
                   reinterpret_cast<uint8_t*>(buf(12288 + 16)), buf(8192), big, s), MOE_ERR_MISALIGNED);
   RC(moe_dispatch(buf(0), ibuf(256), &mx, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), buf(4096),
                   reinterpret_cast<uint8_t*>(buf(12288)), buf(8192), big, s), MOE_OK);
+  // moe_dispatch_noalloc: no workspace argument; shapes whose dispatch
+  // workspace exceeds the library's 1 MiB array are refused on the host.
+  RC(moe_dispatch_noalloc(buf(0), ibuf(256), &ok, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), buf(4096), nullptr,
+                          s), MOE_OK);
+  EXPECT(stub::last_T == 256 && stub::last_E == 8);
+  RC(moe_dispatch_noalloc(buf(0), ibuf(256), &ok, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), buf(4096),
+                          reinterpret_cast<uint8_t*>(buf(12288)), s), MOE_ERR_INVALID_ARG);
+  RC(moe_dispatch_noalloc(buf(0), ibuf(256), &mx, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), buf(4096),
+                          reinterpret_cast<uint8_t*>(buf(12288)), s), MOE_OK);
+  RC(moe_dispatch_noalloc(buf(0), nullptr, &ok, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), buf(4096), nullptr, s),
+     MOE_ERR_INVALID_ARG);
+  const moe_shape huge = shape(int64_t(1) << 22, 128, 256, 4, 128, MOE_BF16);  // 8 MiB of chunk counts
+  RC(moe_dispatch_noalloc(buf(0), ibuf(256), &huge, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), buf(4096), nullptr,
+                          s), MOE_ERR_WORKSPACE);
+  EXPECT(std::strstr(moe_last_error_message(), "1048576") != nullptr);
   EXPECT(moe_read_device_status(nullptr, s) == MOE_ERR_INVALID_ARG);
   EXPECT(moe_read_device_status(buf(8192), s) == 0);
 

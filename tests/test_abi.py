@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
                        (-3, b"MOE_ERR_MISALIGNED"), (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == name
