@@ -44,9 +44,10 @@
  *  - Tensors are dense row-major. Sizes are int64_t. Floating tensors are in
  *    the layer dtype `shape->dtype` (MOE_F32 or MOE_BF16; MXFP8 layers keep
  *    bf16 inputs and outputs) unless the argument says fp32. MXFP8 layers
- *    keep their computed GEMM operands in fp32 (G, U, H in the save buffer,
- *    d_o, dG | dU in the backward workspace), so that every E4M3 code is
- *    decided on the fp32 value rather than on a bf16 rounding of it. Weights:
+ *    decide every E4M3 code of a computed GEMM operand on its fp32 value
+ *    rather than on a bf16 rounding of it: G, U, H (save buffer) and d_o are
+ *    fp32, and dG | dU exist only as the E4M3 operands the backward writes
+ *    from fp32 values in registers. Weights:
  *    w_router [d][E]; w_gate, w_up [E][d][f]; w_down [E][f][d].
  *  - Row counts: S = T*k routed rows. Index tensors are int32.
  *  - Validation is host-side only and never reads device memory. Errors:
@@ -254,8 +255,8 @@ int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
  *   dw_down[e] = H^T · d_o;  dw_gate[e] = xp^T · dG;  dw_up[e] = xp^T · dU
  * Weight gradients of experts with no rows are written as zeros. All outputs
  * in the layer dtype (d_o is fp32 for MXFP8 layers, as moe_combine_bwd
- * writes it). ws: moe_workspace_size(MOE_OP_FFN_BWD) bytes; it starts with
- * the dG | dU rows ([S][2f], fp32 for MXFP8 layers, else the layer dtype).
+ * writes it). ws: moe_workspace_size(MOE_OP_FFN_BWD) bytes; for fp32 and
+ * bf16 layers it starts with the dG | dU rows ([S][2f], layer dtype).
  * MXFP8 layers quantise every operand along its GEMM's K (the weight
  * gradients along each expert's tokens, the range padded with zero rows).
  * d_o_mx (MXFP8 layers only; NULL = quantise d_o here): the MXFP8 image of

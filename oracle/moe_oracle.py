@@ -486,16 +486,19 @@ def ffn_forward_mx(xp, w_gate, w_up, w_down, offsets, h_in=None):
     return G, U, H, O
 
 
-def ffn_backward_mx(d_o, xp, w_gate, w_up, w_down, offsets, G, U, H, dgdu_in=None):
+def ffn_backward_mx(d_o, xp, w_gate, w_up, w_down, offsets, G, U, H, dgdu_in=None, dgdu_w_in=None):
     """ffn_backward with MXFP8 GEMM operands, each along its GEMM's K:
     dH = q(dO) q(W_down)^T (both along d); dXp = q(dG) q(W_gate)^T +
     q(dU) q(W_up)^T (along f); dW_down = q(H)^T q(dO), dW_gate = q(Xp)^T
     q(dG), dW_up = q(Xp)^T q(dU), each along the expert's tokens.
     dO, dG, dU and H are quantised at the values given (the exact ones
     from ffn_forward_mx and combine_backward), and the SwiGLU derivative
-    reads G and U as given; dgdu_in, if given, replaces (dG, dU) for the
-    later GEMMs (a stage-by-stage comparison feeds a device's own stored
-    values).
+    reads G and U as given. For stage-by-stage comparisons with a device
+    that keeps its own operands: dgdu_in, if given, replaces (dG, dU) for
+    the later GEMMs, and dgdu_w_in, if given, replaces them for the weight
+    gradients only (the dXp GEMM then takes dgdu_in or the computed values).
+    Values that are already MXFP8 numbers in the same blocking (a device's
+    dequantised operand) pass through the quantisation unchanged.
     Returns (dXp, dW_gate, dW_up, dW_down, dG, dU)."""
     E = len(offsets) - 1
     S, d = np.shape(xp)
@@ -513,9 +516,10 @@ def ffn_backward_mx(d_o, xp, w_gate, w_up, w_down, offsets, G, U, H, dgdu_in=Non
         dU[a:b] = dh * g * s
         dG[a:b] = dh * u * s * (1.0 + g * (1.0 - s))
     dg_in, du_in = (dG, dU) if dgdu_in is None else dgdu_in
+    dg_w, du_w = (dg_in, du_in) if dgdu_w_in is None else dgdu_w_in
     dgq, duq = mx_roundtrip(dg_in, "cols"), mx_roundtrip(du_in, "cols")
     hg, dog = mx_rows_grouped(H, offsets), mx_rows_grouped(d_o, offsets)
-    xg, dgg, dug = mx_rows_grouped(xp, offsets), mx_rows_grouped(dg_in, offsets), mx_rows_grouped(du_in, offsets)
+    xg, dgg, dug = mx_rows_grouped(xp, offsets), mx_rows_grouped(dg_w, offsets), mx_rows_grouped(du_w, offsets)
     dxp = np.zeros((S, d))
     dwg = np.zeros((E, d, f)); dwu = np.zeros((E, d, f)); dwd = np.zeros((E, f, np.shape(w_down)[2]))
     for e in range(E):

@@ -33,8 +33,9 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Bytes of an element of the layer's input and output tensors (MXFP8 layers:
-// bf16) and of its computed activations G, U, H, dO, dG | dU (MXFP8 layers
-// keep those in fp32, so every E4M3 code is decided on the fp32 value).
+// bf16) and of its stored computed activations G, U, H, dO, dG | dU (MXFP8
+// layers keep G, U, H, dO in fp32, so every E4M3 code is decided on the fp32
+// value; their dG | dU never leave the down-dgrad epilogue in fp32).
 int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 int act_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
@@ -105,6 +106,9 @@ size_t gu_h_bytes(const moe_shape* s) {
 }
 // dG | dU rows of the backward workspace: [S][2f] (act_bytes each element).
 size_t dgu_bytes_for(const moe_shape* s) {
+  // MXFP8 layers keep dG | dU only as the E4M3 operands the down-dgrad
+  // epilogue writes into their own workspace.
+  if (s->dtype == MOE_MXFP8) return 0;
   return ((size_t)s->T * s->k * 2 * s->f * act_bytes(s->dtype) + 255) & ~(size_t)255;
 }
 // Saved G, U, H planes (none with recompute); MXFP8 layers add the backward's

@@ -5,9 +5,10 @@
 // infraestrutura para treinar modelos MoE", section "Otimizações e testes em
 // escala de trilhões"; "Ai2 rilascia Olmo-Core 3...", section "Parallelismo,
 // precisione e tecniche di memoria"). Inputs, O, dXp and the weight
-// gradients are bf16; the computed GEMM operands G, U, H, dO and dG | dU are
-// kept in fp32, so every E4M3 code is decided on the fp32 value (each
-// quantiser of an fp32 operand uses the exact encoder). Each GEMM consumes
+// gradients are bf16; every E4M3 code of a computed GEMM operand (G, U, H,
+// dO, dG | dU) is decided on its fp32 value: G, U, H and dO are kept in
+// fp32, and dG | dU exist only inside the down-dgrad epilogue, which writes
+// both of their E4M3 operand layouts. Each GEMM consumes
 // E4M3 copies with one E8M0 scale per 32 elements along its K:
 //   forward   G,U = q(Xp) q(W_gate), q(W_up)   K = d  (weights transposed)
 //             O   = q(H) q(W_down)              K = f  (weight transposed)
@@ -17,7 +18,8 @@
 //             an expert's tokens, each expert's range padded to 64 rows.
 // q(Xp) and q(dO) along d can arrive ready-made from the dispatch and
 // combine-backward passes, which write them beside their rows; q(H) and
-// q(dGU) along K come from the epilogues of the GEMMs that produce them.
+// q(dGU) along K, and q(dGU) along the tokens, come from the epilogues of the
+// GEMMs that produce them.
 #include "common.h"
 #include "grouped_gemm.h"
 #include "kernels.h"
@@ -175,6 +177,9 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
   const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), d, f, E, nullptr);
   const int64_t wsz = static_cast<int64_t>(d) * f;
   const int64_t P = padded_rows(S, E);
+  // Per-expert padded offsets of the token-major (weight-gradient) layouts.
+  TRY(launch_mx_poff(a.offsets, E, w.poff, s));
+  TRY(launch_mx_blocks(a.offsets, w.poff, E, P, w.blk, s));
   {  // dGU = SwiGLU'(q(dO) q(W_down)^T): dO along d; W_down [f][d] along d
      // was quantised by the forward.
     uint8_t *doq = w.doq, *dos = w.dos;
@@ -189,9 +194,11 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
     p.a = doq; p.lda = d; p.as = dos; p.as_slab = 2LL * S;
     p.b0 = sv.wdq; p.ldb = d; p.bstride = wsz; p.bs0 = sv.wds; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
-    p.c0 = a.dgu; p.ldc = 2 * f; p.e0 = a.G; p.e1 = a.U; p.N = f; p.K = d;
-    // The epilogue also writes dGU along 2f (the next GEMM's A operand).
+    p.ldc = 2 * f; p.e0 = a.G; p.e1 = a.U; p.N = f; p.K = d;
+    // dG | dU leave the epilogue only as E4M3 operands: along 2f (the dXp
+    // GEMM's A operand) and along the expert's tokens (the weight gradient's).
     p.mxq = w.dguq; p.mxs = w.dgus; p.mxq_ld = 2LL * f; p.mxs_slab = 2LL * S;
+    p.tq = w.dgut; p.ts = w.dguts; p.tq_ld = P; p.ts_slab = 4LL * f; p.poff = w.poff;
     TRY(launch_mx_ragged(BWD_DOWN, p, s));
   }
   {  // dXp = q(dGU) q([W_gate | W_up])^T: dGU along 2f (above); the weights
@@ -205,8 +212,6 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
     TRY(launch_mx_ragged(BWD_GU, p, s));
   }
   // Weight gradients: every operand along the expert's tokens, transposed.
-  TRY(launch_mx_poff(a.offsets, E, w.poff, s));
-  TRY(launch_mx_blocks(a.offsets, w.poff, E, P, w.blk, s));
   {  // dW_down[e] = q(H_e)^T q(dO_e)
     TRY(launch_mx_tgroup_f32(a.H, S, f, w.blk, w.ht, P, w.hts, s));
     TRY(launch_mx_tgroup_f32(a.d_o, S, d, w.blk, w.dot, P, w.dots, s));
@@ -219,7 +224,6 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
   }
   {  // [dW_gate | dW_up][e] = q(Xp_e)^T q(dGU_e)
     TRY(launch_mx_tgroup(a.xp, S, d, w.blk, 1, 0, w.xt, P, 0, w.xts, 0, s));
-    TRY(launch_mx_tgroup_f32(a.dgu, S, 2 * f, w.blk, w.dgut, P, w.dguts, s));
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
     p.a = w.xt; p.lda = P; p.as = w.xts; p.as_slab = 2LL * d;

@@ -511,47 +511,151 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     });
   } else if constexpr (MODE == BWD_DOWN && QUANT) {
     // dH -> dG = dH U sig(G) (1 + G (1 - sig(G))), dU = dH G sig(G) in fp32
-    // from the fp32 saved G, U; a row of dGU is [dG (f) | dU (f)], fp32.
-    // One 32-column block at a time: its G, U come in by LDS DMA (rows past
-    // the end read 0), then dG and dU leave through flush32 with their codes.
-    const int64_t ld = p.ldc * 4, lds_ = static_cast<int64_t>(p.f) * 4;
-    static_for<NB>([&](auto J) {
+    // from the fp32 saved G, U, one 32 x 32 block (J, I) at a time. The saved
+    // G, U of a block come straight into registers in the accumulator layout
+    // (lane: row 32 I + l%32, columns 8 Q + 4 (l/32) .. +3), one block ahead
+    // of its use; rows past the expert's end read 0, so dG, dU are 0 there.
+    // dG and dU leave only as the next GEMMs' E4M3 operands, each code
+    // decided on the fp32 value:
+    //  - K-major along 2f (dG in columns [0, f), dU in [f, 2f)): a row's
+    //    32-block sits in lanes l and l ^ 32; one exchange gives its scale,
+    //    a second gives each lane 16 consecutive codes;
+    //  - token-major [2f][P] for the weight gradient: the block goes through
+    //    LDS column-major (dG then dU, 36-dword columns: conflict-free 16-byte
+    //    reads; two buffers, alternating by block, so a block's transpose
+    //    overlaps the next block's arithmetic), and lane L encodes column
+    //    L % 32 of tensor L / 32: 32 tokens, the 32-row block of that channel
+    //    inside the expert's padded range.
+    // Lane-half exchanges use v_permlane32_swap (a VALU op, no LDS round trip):
+    // swap(x, y) leaves lanes 0..31 of x and lanes 32..63 of y in place and
+    // exchanges lanes 32..63 of x with lanes 0..31 of y.
+    const int64_t lds_ = static_cast<int64_t>(p.f) * 4;
+    const int e_first = p.offsets[e];
+    const int rel0 = mrow - e_first;                       // first row of the block, inside the expert
+    const int n64 = (row_end - e_first + 63) & ~63;        // the expert's rows padded to 64
+    const int64_t pt0 = static_cast<int64_t>(p.poff[e]) + rel0;
+    const auto rG = make_rsrc(static_cast<const char*>(p.e0) + static_cast<int64_t>(mrow) * lds_, rows * lds_);
+    const auto rU = make_rsrc(static_cast<const char*>(p.e1) + static_cast<int64_t>(mrow) * lds_, rows * lds_);
+    const auto rQ = make_rsrc(p.mxq + static_cast<int64_t>(mrow) * p.mxq_ld, rows * p.mxq_ld);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kAhead = 2;       // blocks of G, U in flight ahead of the one in use
+    f32x4 gu[kAhead + 1][2][4];     // [buffer][G, U][Q]
+    auto load_block = [&](auto B, int J, int I) {
+      constexpr int b = decltype(B)::value;
       const int col0 = n0 + wn * WN + J * 32;
-      const int64_t sbase = (static_cast<int64_t>(mrow) * p.f + col0) * 4;
-      const int64_t sbytes = static_cast<int64_t>(rows) * p.f * 4;
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const auto rs = make_rsrc(static_cast<const char*>(sl ? p.e1 : p.e0) + sbase, sbytes);
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wa + sl * kSlot));
+      for (int Q = 0; Q < 4; ++Q) {
+        const uint32_t off = static_cast<uint32_t>((I * 32 + l32) * lds_ + (col0 + 8 * Q + 4 * hl) * 4);
+        gu[b][0][Q] = __builtin_amdgcn_raw_buffer_load_b128(rG, off, 0, 0);
+        gu[b][1][Q] = __builtin_amdgcn_raw_buffer_load_b128(rU, off, 0, 0);
+      }
+    };
+    // Per-wave LDS: two transpose buffers [2 tensors][32 columns][36].
+    constexpr int kTgFloats = 2 * 32 * 36;
+    float* const tgw = reinterpret_cast<float*>(smem + wave * (2 * kTgFloats * 4));
+    static_for<kAhead>([&](auto B0) {
+      constexpr int b0 = decltype(B0)::value;
+      if constexpr (b0 < NB * MB) load_block(B0, b0 / MB, b0 % MB);
+    });
+    static_for<NB * MB>([&](auto BI) {
+      constexpr int bi = decltype(BI)::value, J = bi / MB, I = bi % MB, b = bi % (kAhead + 1);
+      if constexpr (bi + kAhead < NB * MB)
+        load_block(std::integral_constant<int, (bi + kAhead) % (kAhead + 1)>{}, (bi + kAhead) / MB,
+                   (bi + kAhead) % MB);
+      float* const tg = tgw + (bi & 1) * kTgFloats;
+      const int col0 = n0 + wn * WN + J * 32;
+      float dg[16], du[16];
 #pragma unroll
-        for (int t = 0; t < WM / 8; ++t) {
-          const int r = t * 8 + (lane >> 3);
-          const int c = (lane & 7) ^ ((r >> 1) & 7);   // logical chunk held by this lane's slot
-          load_lds16(rs, static_cast<uint32_t>(r * lds_ + c * 16), dst + t * 1024);
+      for (int r = 0; r < 16; ++r) {
+        const float g = gu[b][0][r / 4][r % 4], u = gu[b][1][r / 4][r % 4];
+        const float dh = acc[J][I][r];
+        const float sg = sigmoid_f(g);
+        du[r] = dh * g * sg;
+        dg[r] = dh * u * sg * (1.0f + g * (1.0f - sg));
+      }
+      // Token-major: stage column-major, then one column per lane.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r / 4) + 4 * hl + r % 4;
+        tg[c * 36 + l32] = dg[r];
+        tg[32 * 36 + c * 36 + l32] = du[r];
+      }
+      // K-major: the row's 32-block is in lanes l32 and l32 + 32.
+      {
+        float mg = 0.0f, mu = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          mg = fmaxf(mg, fabsf(dg[r]));
+          mu = fmaxf(mu, fabsf(du[r]));
+        }
+        auto half_max = [](float m) {  // max over lanes l and l ^ 32
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        };
+        mg = half_max(mg);
+        mu = half_max(mu);
+        const int cg = mx_scale_code(mg), cu = mx_scale_code(mu);
+        uint32_t wg[4], wu[4];
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q) {
+          wg[Q] = e4m3_encode4(ldexpf(dg[4 * Q], 127 - cg), ldexpf(dg[4 * Q + 1], 127 - cg),
+                               ldexpf(dg[4 * Q + 2], 127 - cg), ldexpf(dg[4 * Q + 3], 127 - cg));
+          wu[Q] = e4m3_encode4(ldexpf(du[4 * Q], 127 - cu), ldexpf(du[4 * Q + 1], 127 - cu),
+                               ldexpf(du[4 * Q + 2], 127 - cu), ldexpf(du[4 * Q + 3], 127 - cu));
+        }
+        // Lane half 0 holds columns 8Q..8Q+3, half 1 columns 8Q+4..8Q+7: two
+        // swaps give half 0 columns 0..15 and half 1 columns 16..31 (swap(w0,
+        // w2): half 0 keeps its w0 and receives half 1's w0, half 1 receives
+        // half 0's w2 and keeps its own; likewise w1, w3).
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        auto pack16 = [&](const uint32_t (&w)[4]) -> u32x4_t {
+          const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+          const auto c = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+          return u32x4_t{a[0], a[1], c[0], c[1]};
+        };
+        const u32x4_t vg = pack16(wg), vu = pack16(wu);
+        const uint32_t qoff = static_cast<uint32_t>((I * 32 + l32) * p.mxq_ld + col0 + 16 * hl);
+        __builtin_amdgcn_raw_buffer_store_b128(vg, rQ, qoff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vu, rQ, qoff + static_cast<uint32_t>(p.f), 0, 0);
+        // Scales: row r's byte of 32-block col / 32 (rows past the end dropped).
+        const auto rS = make_rsrc(p.mxs + static_cast<int64_t>(col0 / 64) * p.mxs_slab + static_cast<int64_t>(mrow) * 2,
+                                  static_cast<int64_t>(rows) * 2);
+        const auto rS2 = make_rsrc(p.mxs + static_cast<int64_t>((p.f + col0) / 64) * p.mxs_slab +
+                                       static_cast<int64_t>(mrow) * 2,
+                                   static_cast<int64_t>(rows) * 2);
+        if (hl == 0) {
+          const uint32_t so = static_cast<uint32_t>((I * 32 + l32) * 2 + (col0 / 32) % 2);
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(cg), rS, so, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(cu), rS2,
+                                               static_cast<uint32_t>((I * 32 + l32) * 2 + ((p.f + col0) / 32) % 2), 0, 0);
         }
       }
-      wait_vmcnt<0>();
-      wave_sync();
-      static_for<MB>([&](auto I) {
-        static_for<4>([&](auto Q) {
-          const int r = I * 32 + l32, col = 8 * Q + 4 * hl;
-          const float4 g4 = get4f(0, r, col), u4 = get4f(1, r, col);
-          const float g[4] = {g4.x, g4.y, g4.z, g4.w}, u[4] = {u4.x, u4.y, u4.z, u4.w};
-          float dg[4], du[4];
+      // Token-major: lane L takes column L % 32 of dG (L < 32) or dU.
+      if (rel0 + I * 32 < n64) {
+        const float* col = tg + (lane >> 5) * 32 * 36 + (lane & 31) * 36;
+        float v[32];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float dh = acc[J][I][4 * Q + c];
-            const float sg = sigmoid_f(g[c]);
-            du[c] = dh * g[c] * sg;
-            dg[c] = dh * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
-          }
-          put4f(0, r, col, dg[0], dg[1], dg[2], dg[3]);
-          put4f(1, r, col, du[0], du[1], du[2], du[3]);
-        });
-      });
-      char* C = static_cast<char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + col0) * 4;
-      flush32(0, C, ld, rows, col0);
-      flush32(1, C + static_cast<int64_t>(p.f) * 4, ld, rows, p.f + col0);
+        for (int t = 0; t < 8; ++t) {
+          const float4 x = *reinterpret_cast<const float4*>(col + 4 * t);
+          v[4 * t] = x.x; v[4 * t + 1] = x.y; v[4 * t + 2] = x.z; v[4 * t + 3] = x.w;
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 32; ++t) m = fmaxf(m, fabsf(v[t]));
+        const int code = mx_scale_code(m);
+        uint32_t w[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          w[t] = e4m3_encode4(ldexpf(v[4 * t], 127 - code), ldexpf(v[4 * t + 1], 127 - code),
+                              ldexpf(v[4 * t + 2], 127 - code), ldexpf(v[4 * t + 3], 127 - code));
+        const int64_t ch = (lane >> 5) * static_cast<int64_t>(p.f) + col0 + (lane & 31);
+        const int64_t pt = pt0 + I * 32;
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        uint8_t* dst = p.tq + ch * p.tq_ld + pt;
+        *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4_t*>(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+        p.ts[(pt / 64) * p.ts_slab + ch * 2 + (pt / 32) % 2] = static_cast<uint8_t>(code);
+      }
     });
   } else if constexpr (MODE == FWD_GU) {
     // Gate blocks [0, NB/2) and up blocks [NB/2, NB) cover the same NB*16 f-columns.

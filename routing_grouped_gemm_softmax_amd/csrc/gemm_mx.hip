@@ -253,6 +253,328 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
   }
 }
 
+
+// FWD_DOWN, BWD_GU and the weight gradients with 256 x 256 tiles as a
+// persistent grid that streams slabs across tiles (one workgroup per CU):
+// each workgroup owns a strided share of its XCD's tile range (the ragged
+// modes: lo, lo + wpx, ...; WGRAD: the range wgrad_sched gives it) and its
+// ring never drains between tiles. The loads of the next tile's first slabs
+// go out during the current tile's last slabs, and the epilogue (bf16
+// outputs, staged through a per-wave 4 KB LDS area beside the ring and
+// written with range-checked buffer stores) runs while they fly. With one
+// tile per workgroup every CU reached its epilogue at the same moment, so the
+// stores of all of them ran as one burst with the matrix cores idle.
+//
+// LDS: 4 ring slots of [A 256 x 64 B | B 256 x 64 B | A scales 1 KB | B
+// scales 1 KB] (scale loads: wave 0 the A side, wave 1 the B side; waves 2
+// and 3 issue a zero-range load into a shared dump area, so that every wave
+// issues the same count), then the staging areas, then the dump area.
+//
+// Wait counts: vmcnt counts loads and stores together, in issue order. The
+// wait for slab g+1 must allow exactly the operations issued after that
+// slab's loads: the loads of slabs g+2 and g+3, and kEpiStores stores for
+// each epilogue since (every epilogue issues exactly that many). Past one
+// epilogue the count exceeds 63 and the wait asks for 63, which only waits
+// longer.
+constexpr int kStreamStages = 4;
+constexpr int kStoreNT = 2;  // buffer store cache policy bits: nt (non-temporal)
+constexpr int kStreamStage = 256 * 64 * 2 + 2 * kScaleArea;
+constexpr int kStreamStg = 32 * 128;  // per-wave staging: 32 rows x 64 bf16
+constexpr int kStreamLds = kStreamStages * kStreamStage + 4 * kStreamStg + kScaleArea;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, MB = 4, NB = 4;
+  static_assert(MODE == FWD_DOWN || MODE == BWD_GU || MODE == WGRAD, "streaming modes");
+  constexpr int TILE_M = BM * 64, TILE_N = BN * 64;
+  constexpr int STAGE = kStreamStage;
+  constexpr int RING = kStreamStages * STAGE;
+  constexpr int kEpiStores = 8 * 4;  // 8 flushes of 4 stores
+  constexpr int LM = BM / 64, LN = BN / 64, kLoads = LM + LN + 1;
+  constexpr int kWait0 = kLoads * (kStreamStages - 2);
+  constexpr int kWait1 = kWait0 + kEpiStores < 63 ? kWait0 + kEpiStores : 63;
+  static_assert(kStreamStages == 4, "epilogue accounting written for slabs g+1..g+3 in flight");
+  static_assert(kStreamLds <= 160 * 1024, "LDS");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- this workgroup's tiles ------------------------------------------------------------
+  RowTileMap map;
+  int lo, step, ntiles;
+  if constexpr (MODE != WGRAD) {
+    map.init(p, BM, BN, lane);
+    const int R = map.tiles();
+    const int x = blockIdx.x % 8, wpx = gridDim.x / 8;
+    lo = xcd_cut(R, x) + blockIdx.x / 8;
+    const int hi = xcd_cut(R, x + 1);
+    step = wpx;
+    ntiles = lo < hi ? (hi - lo + wpx - 1) / wpx : 0;
+  } else {
+    int* s_info = reinterpret_cast<int*>(smem + RING);  // a staging area, free until the first epilogue
+    wgrad_sched<BM, BN, 64, kEpiWorkX>(p, s_info, wave, lane);
+    lo = __builtin_amdgcn_readfirstlane(s_info[0]);
+    const int hi = __builtin_amdgcn_readfirstlane(s_info[1]);
+    step = __builtin_amdgcn_readfirstlane(s_info[2]);
+    ntiles = lo < hi ? (hi - lo + step - 1) / step : 0;
+    __syncthreads();  // s_info is read out before any wave stages there
+  }
+  if (ntiles == 0) return;
+  auto tile_at = [&](int j) -> TileCoord {
+    if constexpr (MODE != WGRAD) return map.at(lo + j * step, lane);
+    else return wgrad_tile<BM, BN>(p, lo + j * step);
+  };
+  // WGRAD: [row0, row_end) is the expert's padded K range (a multiple of 64).
+  auto slabs_of = [&](const TileCoord& tc) -> int {
+    if constexpr (MODE == WGRAD) return (tc.row_end - tc.row0) / 64;
+    else return p.K / 64;
+  };
+  const uint8_t* A = static_cast<const uint8_t*>(p.a);
+  const uint32_t dump = __builtin_amdgcn_readfirstlane(lds_addr(smem + RING + 4 * kStreamStg));
+
+  // ---- HBM -> LDS: load L of slab kt of tile tc (empty descriptors if !live) --------------
+  auto issue = [&](const TileCoord& tc, int kt, bool live, uint32_t slot, auto L, auto w) {
+    constexpr int l = decltype(L)::value, W = decltype(w)::value;
+    const int n0 = tc.nt * BN;
+    if constexpr (l < LM) {
+      if constexpr (MODE == WGRAD) {
+        const int64_t k0 = tc.row0 + static_cast<int64_t>(kt) * 64;
+        load_rows64<BM, W>(make_rsrc(A + tc.m0 * p.lda + k0, live ? BM * p.lda : 0), p.lda, slot, wave, lane, l);
+      } else {
+        const int valid = live ? min(BM, tc.row_end - tc.row0) : 0;
+        load_rows64<BM, W>(make_rsrc(A + static_cast<int64_t>(tc.row0) * p.lda + kt * 64,
+                                     static_cast<int64_t>(valid) * p.lda),
+                           p.lda, slot, wave, lane, l);
+      }
+    } else if constexpr (l < LM + LN) {
+      constexpr int q = l - LM;
+      const uint32_t tn = slot + TILE_M;
+      if constexpr (MODE == WGRAD) {
+        const int64_t k0 = tc.row0 + static_cast<int64_t>(kt) * 64;
+        load_rows64<BN, W>(make_rsrc(static_cast<const uint8_t*>(p.b0) + n0 * p.ldb + k0, live ? BN * p.ldb : 0),
+                           p.ldb, tn, wave, lane, q);
+      } else {  // B stored [n][k] per expert
+        const uint8_t* src = static_cast<const uint8_t*>(p.b0);
+        int ks = kt;
+        if constexpr (MODE == BWD_GU) {
+          if (kt * 64 >= p.f) { src = static_cast<const uint8_t*>(p.b1); ks = kt - p.f / 64; }
+        }
+        load_rows64<BN, W>(make_rsrc(src + static_cast<int64_t>(tc.e) * p.bstride + static_cast<int64_t>(n0) * p.ldb +
+                                         ks * 64,
+                                     live ? static_cast<int64_t>(BN) * p.ldb : 0),
+                           p.ldb, tn, wave, lane, q);
+      }
+    } else {
+      const uint32_t voff = static_cast<uint32_t>(lane * 16);
+      if (wave == 0) {
+        const uint32_t sc = slot + TILE_M + TILE_N;
+        if constexpr (MODE == WGRAD) {
+          const int64_t k0 = tc.row0 + static_cast<int64_t>(kt) * 64;
+          load_lds16<W>(make_rsrc(p.as + (k0 / 64) * p.as_slab + tc.m0 * 2, live ? BM * 2 : 0), voff, sc);
+        } else {
+          // Whole dwords: an odd row count keeps its last row's scales.
+          const int valid = live ? min(BM, tc.row_end - tc.row0) : 0;
+          load_lds16<W>(make_rsrc(p.as + static_cast<int64_t>(kt) * p.as_slab + tc.row0 * 2, (valid * 2 + 3) & ~3),
+                        voff, sc);
+        }
+      } else if (wave == 1) {
+        const uint32_t sc = slot + TILE_M + TILE_N + kScaleArea;
+        if constexpr (MODE == WGRAD) {
+          const int64_t k0 = tc.row0 + static_cast<int64_t>(kt) * 64;
+          load_lds16<W>(make_rsrc(p.bs0 + (k0 / 64) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff, sc);
+        } else {
+          const uint8_t* ssrc = p.bs0;
+          int ks = kt;
+          if constexpr (MODE == BWD_GU) {
+            if (kt * 64 >= p.f) { ssrc = p.bs1; ks = kt - p.f / 64; }
+          }
+          load_lds16<W>(make_rsrc(ssrc + static_cast<int64_t>(tc.e) * p.bs_estride +
+                                      static_cast<int64_t>(ks) * p.bs_slab + n0 * 2,
+                                  live ? BN * 2 : 0),
+                        voff, sc);
+        }
+      } else {
+        load_lds16<W>(make_rsrc(p.as, 0), voff, dump);
+      }
+    }
+  };
+
+  floatx16 acc[NB][MB];
+  struct Frags {
+    v8i m[MB], n[NB];
+    int sm[MB], sn[NB];
+  };
+  auto read_frag = [&](const char* slotp, Frags& F, auto FI) {
+    constexpr int fi = decltype(FI)::value;
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(slotp + TILE_M + TILE_N);
+    const int r32 = lane & 31, kb = lane >> 5;
+    if constexpr (fi < MB) {
+      const int row = wm * WM + fi * 32;
+      F.m[fi] = frag_mx(slotp, row, lane);
+      F.sm[fi] = sc[(row + r32) * 2 + kb];
+    } else {
+      constexpr int j = fi - MB;
+      const int row = wn * WN + j * 32;
+      F.n[j] = frag_mx(slotp + TILE_M, row, lane);
+      F.sn[j] = sc[kScaleArea + (row + r32) * 2 + kb];
+    }
+  };
+  auto mfma_one = [&](const Frags& F, auto MI) {
+    constexpr int mi = decltype(MI)::value, j = mi / MB, i = mi % MB;
+    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.n[j], F.m[i], acc[j][i], 0, 0, 0, F.sn[j], 0,
+                                                               F.sm[i]);
+  };
+  constexpr int kMfma = MB * NB, kFrags = MB + NB;
+
+  // ---- epilogue: this wave's 128 x 128 block through its 4 KB staging tile ----------------
+  char* const wa = smem + RING + wave * kStreamStg;
+  const int hl = lane >> 5, l32 = lane & 31;
+  auto st_off = [](int r, int col) { return r * 128 + ((((col >> 3) ^ (r >> 1)) & 7) << 4) + ((col & 4) << 1); };
+  auto put4 = [&](int r, int col, uint2 v) { *reinterpret_cast<uint2*>(wa + st_off(r, col)) = v; };
+  auto wave_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+  };
+  // Staging rows [0, 32) -> global rows g + r * ld for r < rows (4 buffer
+  // stores, non-temporal: the outputs are written once and read by a later
+  // kernel, and the stores complete sooner without allocating in the L2,
+  // which matters because the next slabs' waits count them).
+  auto flush = [&](const char* g, int64_t ld, int rows) {
+    __builtin_amdgcn_sched_barrier(0);
+    wave_sync();
+    const auto rs = make_rsrc(g, static_cast<int64_t>(max(0, min(32, rows))) * ld);
+    const int c = lane & 7;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = t * 8 + (lane >> 3);
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wa + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<uint32_t>(r * ld + c * 16), 0, kStoreNT);
+    }
+    wave_sync();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto acc4 = [&](int j, int i, int q) {
+    return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
+  };
+  auto epilogue = [&](const TileCoord& tc) {
+    const int64_t ld = p.ldc * 2;
+    const char* out;
+    int rows;
+    if constexpr (MODE != WGRAD) {
+      const int mrow = tc.row0 + wm * WM;
+      rows = tc.row_end - mrow;  // may be <= 0 or > WM: flush clamps
+      out = static_cast<const char*>(p.c0) + (static_cast<int64_t>(mrow) * p.ldc + tc.nt * BN + wn * WN) * 2;
+    } else {
+      // dW[e] rows m0.., columns n0..; columns >= f of the gate|up gradient
+      // go to the second output (dw_up).
+      const char* base = static_cast<const char*>(p.c0);
+      int cn0 = tc.nt * BN;
+      if (p.c1 != nullptr && cn0 >= p.f) { base = static_cast<const char*>(p.c1); cn0 -= p.f; }
+      rows = WM;
+      out = base + (static_cast<int64_t>(tc.e) * p.cstride + static_cast<int64_t>(tc.m0 + wm * WM) * p.ldc + cn0 +
+                    wn * WN) * 2;
+    }
+    static_for<2>([&](auto JP) {
+      static_for<MB>([&](auto I) {
+        static_for<2>([&](auto JJ) {
+          static_for<4>([&](auto Q) { put4(l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JP * 2 + JJ, I, Q)); });
+        });
+        flush(out + static_cast<int64_t>(I) * 32 * ld + JP * 128, ld, rows - 32 * I);
+      });
+    });
+  };
+
+  // ---- the slab stream ------------------------------------------------------------------
+  // Load side: tile index lj, its slab lkt and slab count lnk (tiles without
+  // slabs are skipped here; they still get their epilogue below).
+  int lj = 0, lkt = 0;
+  TileCoord ltc = tile_at(0);
+  int lnk = slabs_of(ltc);
+  auto skip_empty = [&]() {
+    while (lkt >= lnk && lj < ntiles) {
+      lkt = 0;
+      if (++lj < ntiles) {
+        ltc = tile_at(lj);
+        lnk = slabs_of(ltc);
+      }
+    }
+  };
+  skip_empty();
+  auto advance = [&]() {
+    ++lkt;
+    skip_empty();
+  };
+  // Epilogues issued after the loads of slabs g+1, g+2, g+3 (g: the slab
+  // being multiplied).
+  int ep1 = 0, ep2 = 0, ep3 = 0;
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+#pragma unroll
+  for (int s0 = 0; s0 < kStreamStages; ++s0) {
+    static_for<kLoads>([&](auto L) {
+      issue(ltc, lkt, lj < ntiles, ring + s0 * STAGE, L, std::integral_constant<int, 4>{});
+    });
+    advance();
+  }
+  // One slab: wait for slab gk+1, barrier, then slab gk's MFMAs on `cur` with
+  // the reads of slab gk+1 into `nxt` and the loads of the stream's next slab
+  // into slot gk spread between them.
+  int gk = 0;  // slabs consumed: slab gk sits in slot gk % kStreamStages
+  auto slab = [&](const Frags& cur, Frags& nxt) {
+    if (ep1 == 0) wait_vmcnt<kWait0>();
+    else if (ep1 == 1) wait_vmcnt<kWait1>();
+    else wait_vmcnt<63>();
+    __syncthreads();  // slot gk is read out; slab gk+1 is visible
+    const int sc = gk % kStreamStages;
+    const char* nxtp = smem + ((gk + 1) % kStreamStages) * STAGE;
+    const uint32_t slot = ring + sc * STAGE;
+    const bool live = lj < ntiles;
+    static_for<kLoads>([&](auto S) {
+      constexpr int sg = decltype(S)::value;
+      constexpr int m_lo = sg * kMfma / kLoads, m_hi = (sg + 1) * kMfma / kLoads;
+      constexpr int f_lo = sg * kFrags / kLoads, f_hi = (sg + 1) * kFrags / kLoads;
+      static_for<m_hi - m_lo>([&](auto D) { mfma_one(cur, std::integral_constant<int, m_lo + decltype(D)::value>{}); });
+      static_for<f_hi - f_lo>([&](auto D) {
+        read_frag(nxtp, nxt, std::integral_constant<int, f_lo + decltype(D)::value>{});
+      });
+      issue(ltc, lkt, live, slot, S, std::integral_constant<int, 0>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    advance();
+    ep1 = ep2; ep2 = ep3; ep3 = 0;  // the stream's next slab was just issued
+    ++gk;
+  };
+  Frags f0, f1;
+  wait_vmcnt<kLoads * (kStreamStages - 1)>();
+  __syncthreads();
+  static_for<kFrags>([&](auto FI) { read_frag(smem, f0, FI); });
+  for (int j = 0; j < ntiles; ++j) {
+    const TileCoord cur = tile_at(j);
+    const int nk = slabs_of(cur);
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[jj][i][r] = 0.0f;
+    // Two register sets with fixed names (a runtime index would put them in
+    // scratch memory): slab kt multiplies f0 for even kt, f1 for odd kt.
+    for (int kt = 0; kt < nk; kt += 2) {
+      slab(f0, f1);
+      if (kt + 1 < nk) slab(f1, f0);
+    }
+    // The next slab's fragments (the next tile with slabs) are in f1 after an
+    // odd slab count; its slot is not refilled before the next barrier.
+    if (nk & 1) f0 = f1;
+    epilogue(cur);
+    ++ep1; ++ep2; ++ep3;
+  }
+  // Drain the (empty) loads and the stores still in flight before the wave ends.
+  wait_vmcnt<0>();
+}
+
 int round8(int64_t g) { return static_cast<int>((g + 7) / 8 * 8); }
 
 template <int MODE, int BM, int BN>
@@ -279,6 +601,21 @@ hipError_t launch_tile(const GemmParams& p, int tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int MODE>
+hipError_t launch_stream(const GemmParams& p, hipStream_t s) {
+  auto kern = gg_mx_stream_kernel<MODE>;
+  static std::atomic<int> set{0};
+  if (set.load() == 0) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kStreamLds);
+    if (err != hipSuccess) return err;
+    set.store(1);
+  }
+  const int grid = max(8, device_cu_count() / 8 * 8);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), kStreamLds, s, p);
+  return hipGetLastError();
+}
+
 int ragged_grid(int S, int E, int BM, int NT) {
   return round8((static_cast<int64_t>((S + BM - 1) / BM) + E) * NT);
 }
@@ -290,6 +627,9 @@ template <int MODE>
 hipError_t ragged_mode(const GemmParams& p, hipStream_t s) {
   // N is a multiple of 128 (MXFP8 layers need d, f multiples of 128).
   if (static_cast<int64_t>(p.S) >= 1024LL * p.E) {
+    if constexpr (MODE == FWD_DOWN || MODE == BWD_GU) {
+      if (p.N % 256 == 0) return launch_stream<MODE>(p, s);
+    }
     if (p.N % 256 == 0) return launch_tile<MODE, 256, 256>(p, ragged_grid(p.S, p.E, 256, p.N / 256), s);
     return launch_tile<MODE, 256, 128>(p, ragged_grid(p.S, p.E, 256, p.N / 128), s);
   }
@@ -316,7 +656,7 @@ static hipError_t mx_wgrad(const GemmParams& p, hipStream_t s) {
   auto grid = [&](int bm, int bn) { return round8(static_cast<int64_t>(p.E) * (p.M / bm) * (p.N / bn)); };
   // A column tile must not straddle the gate|up split at column f.
   const int nsplit = p.c1 ? p.f : p.N;
-  if (p.M % 256 == 0 && p.N % 256 == 0 && nsplit % 256 == 0) return launch_tile<WGRAD, 256, 256>(p, grid(256, 256), s);
+  if (p.M % 256 == 0 && p.N % 256 == 0 && nsplit % 256 == 0) return launch_stream<WGRAD>(p, s);
   if (p.M % 256 == 0) return launch_tile<WGRAD, 256, 128>(p, grid(256, 128), s);
   return launch_tile<WGRAD, 128, 128>(p, grid(128, 128), s);
 }

@@ -54,6 +54,15 @@ struct GemmParams {
   uint8_t* mxs;
   int64_t mxq_ld;
   int64_t mxs_slab;
+  // MXFP8 BWD_DOWN: the epilogue also writes dG | dU as the weight
+  // gradient's token-major operand: codes tq [2f][tq_ld] (tq_ld = P, every
+  // expert's rows padded to a multiple of 64 starting at poff[e]) and
+  // slab-major scales ts (ts_slab bytes per 64 tokens: 2 per channel).
+  uint8_t* tq;
+  uint8_t* ts;
+  int64_t tq_ld;
+  int64_t ts_slab;
+  const int32_t* poff;
 };
 
 // bf16 grouped GEMMs (gemm_bf16.hip).

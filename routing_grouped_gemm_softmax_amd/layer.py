@@ -25,7 +25,7 @@ class MoELayer:
         self.shape = L.MoeShape.make(T, d, E, k, f, dtype, L.MOE_FLAG_RECOMPUTE if recompute else 0)
         self.recompute = recompute
         self.dtype = L.TORCH_DTYPE[self.shape.dtype]
-        # G, U, H, d_o and dG|dU: fp32 for MXFP8 layers (their E4M3 codes are
+        # G, U, H and d_o: fp32 for MXFP8 layers (their E4M3 codes are
         # decided on the fp32 values), else the layer dtype.
         self.act_dtype = torch.float32 if self.shape.dtype == L.MOE_MXFP8 else self.dtype
         self.learned = learned_routing
@@ -87,8 +87,11 @@ class MoELayer:
         return tuple(flat[i * S * f:(i + 1) * S * f].view(S, f) for i in range(3))
 
     def dgu(self):
-        """(dG, dU), each [S][f] (fp32 for MXFP8 layers): views of the dG|dU
-        rows the last backward left at the start of its workspace."""
+        """(dG, dU), each [S][f]: views of the dG|dU rows the last backward
+        left at the start of its workspace (fp32 and bf16 layers; MXFP8
+        layers keep dG | dU only as E4M3 operands)."""
+        if self.shape.dtype == L.MOE_MXFP8:
+            raise ValueError("MXFP8 layers keep no dG | dU rows")
         S, f = self.T * self.k, self.f
         eb = torch.empty((), dtype=self.act_dtype).element_size()
         rows = self.ws_ffn_bwd[:S * 2 * f * eb].view(self.act_dtype).view(S, 2 * f)

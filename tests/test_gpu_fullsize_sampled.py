@@ -75,10 +75,10 @@ class _Full:
             return O.ffn_forward_mx(xp, *self.w(e), one, h_in=h_in)
         return O.ffn_forward(xp, *self.w(e), one)
 
-    def bwd(self, d_o, xp, e, G, U, H, dgdu_in=None):
+    def bwd(self, d_o, xp, e, G, U, H, dgdu_in=None, dgdu_w_in=None):
         one = np.array([0, len(xp)])
         if self.mx:
-            return O.ffn_backward_mx(d_o, xp, *self.w(e), one, G, U, H, dgdu_in=dgdu_in)
+            return O.ffn_backward_mx(d_o, xp, *self.w(e), one, G, U, H, dgdu_in=dgdu_in, dgdu_w_in=dgdu_w_in)
         return O.ffn_backward(d_o, xp, *self.w(e), one, G, U, H)
 
 
@@ -88,10 +88,11 @@ def _expert_device(F, e):
     a, b = int(F.offsets[e]), int(F.offsets[e + 1])
     rows = np.arange(a, b)
     G, U, H = (_rows(t, rows) for t in L.saved())
-    dG, dU = (_rows(t, rows) for t in L.dgu())
-    return rows, dict(G=G, U=U, H=H, O=_rows(L.o, rows), dO=_rows(L.d_o, rows), dG=dG, dU=dU,
-                      dXp=_rows(L.dxp, rows), dW_gate=host(L.dw_gate[e]), dW_up=host(L.dw_up[e]),
-                      dW_down=host(L.dw_down[e]))
+    dv = dict(G=G, U=U, H=H, O=_rows(L.o, rows), dO=_rows(L.d_o, rows), dXp=_rows(L.dxp, rows),
+              dW_gate=host(L.dw_gate[e]), dW_up=host(L.dw_up[e]), dW_down=host(L.dw_down[e]))
+    if not F.mx:  # MXFP8 layers keep dG | dU only as E4M3 operands (checked as images)
+        dv["dG"], dv["dU"] = (_rows(t, rows) for t in L.dgu())
+    return rows, dv
 
 
 def _check_expert(F, e):
@@ -104,32 +105,68 @@ def _check_expert(F, e):
     bwd = F.bwd(d_o_ref, xp, e, Gr, Ur, Hr)
     ref = dict(G=Gr, U=Ur, H=Hr, O=Or, dO=d_o_ref, dG=bwd[4], dU=bwd[5], dXp=bwd[0],
                dW_gate=bwd[1][0], dW_up=bwd[2][0], dW_down=bwd[3][0])
-    return {n: rel_err(dv[n], ref[n]) for n in ref}, (rows, dv, xp)
+    return {n: rel_err(dv[n], ref[n]) for n in ref if n in dv}, (rows, dv, xp)
+
+
+def _dgu_images(F, e, rows):
+    """The device's dG | dU operands of expert e's rows, dequantised: the
+    K-major image (the dXp GEMM's) and the token-major one (the weight
+    gradient's)."""
+    L, wl = F.layer, F.wl
+    S, f = wl.T * wl.k, wl.f
+    pb = ML.bwd_pieces(S, wl.d, f, wl.E)
+    a, b = int(rows[0]), int(rows[-1]) + 1
+    qo, _ = pb["dguq"]
+    so, _ = pb["dgus"]
+    K = 2 * f
+    codes = host(L.ws_ffn_bwd[qo + a * K:qo + b * K]).reshape(b - a, K)
+    sc = host(L.ws_ffn_bwd[so:so + S * K // 32].view(K // 64, S, 2)[:, a:b, :]).transpose(1, 0, 2)
+    k_major = O.mx_dequantize(codes, sc.reshape(b - a, K // 32), "cols")
+    n = np.diff(F.offsets)
+    p0 = int(np.concatenate([[0], np.cumsum((n + 63) // 64 * 64)])[e])
+    P = ML.padded_rows(S, wl.E)
+    qo, _ = pb["dgut"]
+    so, _ = pb["dguts"]
+    n64 = (b - a + 63) // 64 * 64
+    tc = host(L.ws_ffn_bwd[qo:qo + K * P].view(K, P)[:, p0:p0 + n64])
+    ts = host(L.ws_ffn_bwd[so:so + P * K // 32].view(P // 64, K, 2)[p0 // 64:(p0 + n64) // 64])
+    ts = ts.transpose(1, 0, 2).reshape(K, -1)
+    t_major = O.mx_dequantize(tc, ts, "cols")[:, :b - a].T
+    return k_major, t_major
 
 
 def _check_expert_stage(F, e, rows, dv, xp):
-    """MXFP8: each GEMM stage of expert e on the device's own stored inputs."""
+    """MXFP8: each GEMM stage of expert e on the device's own operands: its
+    stored G, U, H, dO, and its dG | dU images for the dXp GEMM and the
+    weight gradients. The oracle's dG, dU from the device's G, U, dO are
+    returned for the image checks."""
+    k_major, t_major = _dgu_images(F, e, rows)
+    f = F.wl.f
     Gr, Ur, Hr, Or = F.fwd(xp, e, h_in=dv["H"])
-    bwd = F.bwd(dv["dO"], xp, e, dv["G"], dv["U"], dv["H"], dgdu_in=(dv["dG"], dv["dU"]))
-    ref = dict(G=Gr, U=Ur, H=Hr, O=Or, dG=bwd[4], dU=bwd[5], dXp=bwd[0],
-               dW_gate=bwd[1][0], dW_up=bwd[2][0], dW_down=bwd[3][0])
-    return {n: rel_err(dv[n], ref[n]) for n in ref}
+    bwd = F.bwd(dv["dO"], xp, e, dv["G"], dv["U"], dv["H"], dgdu_in=(k_major[:, :f], k_major[:, f:]),
+                dgdu_w_in=(t_major[:, :f], t_major[:, f:]))
+    ref = dict(G=Gr, U=Ur, H=Hr, O=Or, dXp=bwd[0], dW_gate=bwd[1][0], dW_up=bwd[2][0], dW_down=bwd[3][0])
+    return {n: rel_err(dv[n], ref[n]) for n in ref}, (bwd[4], bwd[5])
 
 
-def _check_expert_images(F, e, rows, dv, xp):
-    """MXFP8: the E4M3 images of expert e's rows, byte for byte against the
-    oracle's encoding of the device's stored values."""
+def _check_expert_images(F, e, rows, dv, xp, dgdu):
+    """MXFP8: the E4M3 images of expert e's rows against the oracle's encoding:
+    byte for byte where the device stored the values it quantised, and as
+    the same decisions up to fp32 rounding for dG | dU (the oracle's values
+    from the device's stored G, U, dO)."""
     L, wl = F.layer, F.wl
     S, d, f, E = wl.T * wl.k, wl.d, wl.f, wl.E
     pf, pb = ML.fwd_pieces(S, d, f, E), ML.bwd_pieces(S, d, f, E)
     a = int(rows[0])
-    dgu = np.concatenate([dv["dG"], dv["dU"]], axis=1)
+    dgu = np.concatenate(dgdu, axis=1)
+    atol = np.concatenate([np.full(f, 2e-4 * np.abs(dgdu[0]).max()), np.full(f, 2e-4 * np.abs(dgdu[1]).max())])
     ML.check_kmajor(L.ws_ffn_fwd, pf, "hq", "hs", dv["H"], f"q(H) expert {e}", S=S, row0=a)
-    ML.check_kmajor(L.ws_ffn_bwd, pb, "dguq", "dgus", dgu, f"q(dG|dU) expert {e}", S=S, row0=a)
-    for q, s_, vals in (("ht", "hts", dv["H"]), ("dot", "dots", dv["dO"]), ("xt", "xts", xp),
-                        ("dgut", "dguts", dgu)):
+    ML.check_kmajor(L.ws_ffn_bwd, pb, "dguq", "dgus", dgu, f"q(dG|dU) expert {e}", S=S, row0=a, near=True,
+                    atol=atol)
+    for q, s_, vals, near in (("ht", "hts", dv["H"], False), ("dot", "dots", dv["dO"], False),
+                              ("xt", "xts", xp, False), ("dgut", "dguts", dgu, True)):
         ML.check_token_major(L.ws_ffn_bwd, pb, q, s_, vals, F.offsets, f"q({q})", experts=[e], S=S,
-                             C=vals.shape[1])
+                             C=vals.shape[1], near=near, atol=atol if near else None)
 
 
 def _check_rows_fwd(F, e, rows):
@@ -191,11 +228,11 @@ def _run_checks(name):
         bad = {n: v for n, v in errs.items() if not v <= tol}
         assert not bad, (e, bad)
         if F.mx:
-            stage = _check_expert_stage(F, e, rows, dv, xp)
+            stage, dgdu = _check_expert_stage(F, e, rows, dv, xp)
             print(f"expert {e}, stage by stage:", {n: f"{v:.2e}" for n, v in stage.items()}, flush=True)
             bad = {n: v for n, v in stage.items() if not v <= 2e-2}
             assert not bad, (e, bad)
-            _check_expert_images(F, e, rows, dv, xp)
+            _check_expert_images(F, e, rows, dv, xp, dgdu)
         del dv, xp
     if F.mx:
         hot = int(order[-1])

@@ -33,6 +33,11 @@ pytestmark = pytest.mark.gpu
 STAGE_TOL = 2e-2
 E2E_TOL = 6e-2
 MX_LAYER_BOUND = 0.25  # distance of any MXFP8 layer from the unquantised one (measured up to 0.19)
+# The scaled fp8 MFMA's fp32 results differ from fp64 by up to about 3e-5 of
+# the output's largest value (the G, U stages show it), so an E4M3 code the
+# device decides on its own dG, dU may take the neighbouring value where the
+# exact value lies within that of a rounding boundary: allowance per tensor.
+GEMM_ATOL_REL = 2e-4
 
 CASES = {
     # name: (workload, shape overrides, popularity override for Zipf routing)
@@ -40,6 +45,10 @@ CASES = {
     "zipf_ragged_empty": ("bf16_zipf", dict(T=384, d=256, E=16, f=128, dtype="mxfp8"),
                           [1, 0, 2, 1, 1, 0, 3, 1, 1, 1, 0, 1, 2, 1, 1, 0]),
     "wide_tiles": ("mxfp8_balanced", dict(T=1024, d=512, E=4, f=512), None),
+    # 1024 rows per expert on average: the row-ragged down GEMM, the gate/up
+    # dgrad and both weight gradients run as streaming persistent kernels;
+    # ragged row tiles, two empty experts, odd slab counts per tile.
+    "stream_ragged_empty": ("bf16_zipf", dict(T=2048, d=512, E=8, f=256, dtype="mxfp8"), [4, 0, 2, 1, 3, 1, 0, 5]),
     # The largest expert count and top-k: 16 rows per expert, each padded to
     # 64 in the weight-gradient layouts.
     "max_E256_k8": ("mxfp8_balanced", dict(T=512, d=128, E=256, k=8, f=128), None),
@@ -58,14 +67,27 @@ def _run(wl, inp):
     return layer
 
 
+def _dgu_atol(dg, du):
+    """Per-column allowance of the dG | dU code checks (GEMM_ATOL_REL of each
+    tensor's largest value)."""
+    f = dg.shape[1]
+    return np.concatenate([np.full(f, GEMM_ATOL_REL * np.abs(dg).max()),
+                           np.full(f, GEMM_ATOL_REL * np.abs(du).max())])
+
+
 def _check_images(layer, off, xp, H, d_o, dg, du):
-    """Every E4M3 operand image of the last forward and backward, byte for byte."""
+    """Every E4M3 operand image of the last forward and backward: byte for
+    byte against the oracle's encoding of the values the device stored (H,
+    dO, Xp), and as the same decisions up to the GEMM's rounding for dG | dU,
+    which the device keeps only as images (dg, du: the oracle's values from
+    the device's stored G, U, dO)."""
     S, d, f, E = layer.T * layer.k, layer.d, layer.f, layer.E
     pf, pb = ML.fwd_pieces(S, d, f, E), ML.bwd_pieces(S, d, f, E)
     dgu = np.concatenate([dg, du], axis=1)
+    atol = _dgu_atol(dg, du)
     # K-major: H from the gate/up epilogue, dG|dU from the down-dgrad epilogue.
     ML.check_kmajor(layer.ws_ffn_fwd, pf, "hq", "hs", H, "q(H)")
-    ML.check_kmajor(layer.ws_ffn_bwd, pb, "dguq", "dgus", dgu, "q(dG|dU)")
+    ML.check_kmajor(layer.ws_ffn_bwd, pb, "dguq", "dgus", dgu, "q(dG|dU)", near=True, atol=atol)
     # xp and dO along d: the images dispatch and combine backward wrote.
     for name, img, vals in (("xp", layer.xp_mx, xp), ("d_o", layer.d_o_mx, d_o)):
         if img is not None:
@@ -74,8 +96,10 @@ def _check_images(layer, off, xp, H, d_o, dg, du):
             np.testing.assert_array_equal(q, rq, err_msg=f"{name} image codes")
             np.testing.assert_array_equal(sc, rs, err_msg=f"{name} image scales")
     # Token-major weight-gradient operands.
-    for q, s_, vals in (("ht", "hts", H), ("dot", "dots", d_o), ("xt", "xts", xp), ("dgut", "dguts", dgu)):
-        ML.check_token_major(layer.ws_ffn_bwd, pb, q, s_, vals, off, f"q({q})")
+    for q, s_, vals, near in (("ht", "hts", H, False), ("dot", "dots", d_o, False), ("xt", "xts", xp, False),
+                              ("dgut", "dguts", dgu, True)):
+        ML.check_token_major(layer.ws_ffn_bwd, pb, q, s_, vals, off, f"q({q})", near=near,
+                             atol=atol if near else None)
 
 
 @pytest.mark.parametrize("case", list(CASES))
@@ -99,29 +123,36 @@ def test_mxfp8_layer_matches_mx_oracle(case):
     xp = ref["xp"]
     w = (inp["w_gate"], inp["w_up"], inp["w_down"])
     d_o = host(layer.d_o).astype(np.float64)
-    dg, du = (host(t).astype(np.float64) for t in layer.dgu())
-    _check_images(layer, off, xp, H, d_o, dg, du)
-
-    # Stage by stage.
+    # Stage by stage: each GEMM on the device's stored inputs. dG | dU exist
+    # on the device only as E4M3 operands: the oracle's dG, dU from the
+    # device's G, U, dO feed the later GEMMs, and the images are checked
+    # against them.
+    S, f = wl.T * wl.k, wl.f
+    pb = ML.bwd_pieces(S, wl.d, f, wl.E)
+    dgk = ML.read_kmajor(layer.ws_ffn_bwd, pb, "dguq", "dgus", S, 2 * f)
+    dgt = ML.read_token_major(layer.ws_ffn_bwd, pb, "dgut", "dguts", off, S, 2 * f)
     Gr, Ur, Hr, Or = O.ffn_forward_mx(xp, *w, off, h_in=H)
-    bwd = O.ffn_backward_mx(d_o, xp, *w, off, G, U, H, dgdu_in=(dg, du))
+    bwd = O.ffn_backward_mx(d_o, xp, *w, off, G, U, H, dgdu_in=(dgk[:, :f], dgk[:, f:]),
+                            dgdu_w_in=(dgt[:, :f], dgt[:, f:]))
+    dg, du = bwd[4], bwd[5]
     stage = {
         "G": rel_err(G, Gr), "U": rel_err(U, Ur), "H": rel_err(H, Hr), "O": rel_err(host(layer.o), Or),
-        "dG": rel_err(dg, bwd[4]), "dU": rel_err(du, bwd[5]), "dXp": rel_err(host(layer.dxp), bwd[0]),
+        "dXp": rel_err(host(layer.dxp), bwd[0]),
         "dW_gate": rel_err(host(layer.dw_gate), bwd[1]), "dW_up": rel_err(host(layer.dw_up), bwd[2]),
         "dW_down": rel_err(host(layer.dw_down), bwd[3]),
     }
     print("stage:", {n: f"{e:.2e}" for n, e in stage.items()}, flush=True)
     bad = {n: e for n, e in stage.items() if not e <= STAGE_TOL}
     assert not bad, f"stage-wise over {STAGE_TOL}: {bad}"
+    _check_images(layer, off, xp, H, d_o, dg, du)
 
     # End to end against the MXFP8 oracle from the inputs alone.
     refb = O.layer_backward(inp, ref, mx=True)
     gpu = {"G": G, "U": U, "H": H, "O": host(layer.o), "y": host(layer.y), "dO": d_o,
-           "dgate": host(layer.dgate), "dG": dg, "dU": du, "dXp": host(layer.dxp), "dx": host(layer.dx),
+           "dgate": host(layer.dgate), "dXp": host(layer.dxp), "dx": host(layer.dx),
            "dw_gate": host(layer.dw_gate), "dw_up": host(layer.dw_up), "dw_down": host(layer.dw_down)}
     want = {"G": ref["G"], "U": ref["U"], "H": ref["H"], "O": ref["O"], "y": ref["y"], "dO": refb["dO"],
-            "dgate": refb["dgate"], "dG": refb["dG"], "dU": refb["dU"], "dXp": refb["dXp"], "dx": refb["dx"],
+            "dgate": refb["dgate"], "dXp": refb["dXp"], "dx": refb["dx"],
             "dw_gate": refb["dw_gate"], "dw_up": refb["dw_up"], "dw_down": refb["dw_down"]}
     e2e = {n: rel_err(gpu[n], want[n]) for n in gpu}
     print("end to end vs MXFP8 oracle:", {n: f"{e:.2e}" for n, e in e2e.items()}, flush=True)
@@ -133,8 +164,7 @@ def test_mxfp8_layer_matches_mx_oracle(case):
     plain = O.layer_forward(inp, wl.k)
     plainb = O.layer_backward(inp, plain)
     pw = {"G": plain["G"], "U": plain["U"], "H": plain["H"], "O": plain["O"], "y": plain["y"],
-          "dO": plainb["dO"], "dgate": plainb["dgate"], "dG": plainb["dG"], "dU": plainb["dU"],
-          "dXp": plainb["dXp"], "dx": plainb["dx"], "dw_gate": plainb["dw_gate"], "dw_up": plainb["dw_up"],
+          "dO": plainb["dO"], "dgate": plainb["dgate"], "dXp": plainb["dXp"], "dx": plainb["dx"], "dw_gate": plainb["dw_gate"], "dw_up": plainb["dw_up"],
           "dw_down": plainb["dw_down"]}
     dist = {n: rel_err(gpu[n], pw[n]) for n in gpu}
     print("vs unquantised layer:", {n: f"{e:.3f}" for n, e in dist.items()}, flush=True)

@@ -223,6 +223,19 @@ def test_stage_inputs_replace_the_computed_operands():
     b2 = O.ffn_backward_mx(do, xp, wg, wu, wd, off, G, U, H, dgdu_in=(b[4], b[5]))
     for x, y in zip(b, b2):
         assert np.array_equal(x, y)
+    # dgdu_w_in feeds the weight gradients only; MXFP8 numbers in the weight
+    # gradient's blocking (the dequantised token-major operand) pass through.
+    wq = (O.mx_rows_grouped(b[4], off), O.mx_rows_grouped(b[5], off))
+    b3 = O.ffn_backward_mx(do, xp, wg, wu, wd, off, G, U, H, dgdu_w_in=wq)
+    for x, y in zip(b, b3):
+        assert np.array_equal(x, y)
+    b4 = O.ffn_backward_mx(do, xp, wg, wu, wd, off, G, U, H, dgdu_w_in=(b[4] * 1.3, b[5]))
+    assert np.array_equal(b4[0], b[0]) and np.array_equal(b4[2], b[2]) and np.array_equal(b4[3], b[3])
+    assert not np.array_equal(b4[1], b[1])
+    b5 = O.ffn_backward_mx(do, xp, wg, wu, wd, off, G, U, H, dgdu_in=(b[4] * 1.3, b[5]), dgdu_w_in=wq)
+    assert not np.array_equal(b5[0], b[0])
+    for i in (1, 2, 3):
+        assert np.array_equal(b5[i], b[i])
 
 
 # Distance of the MXFP8 layer from the unquantised one, max|mx - exact| /
