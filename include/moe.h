@@ -45,9 +45,9 @@
  *    the layer dtype `shape->dtype` (MOE_F32 or MOE_BF16; MXFP8 layers keep
  *    bf16 inputs and outputs) unless the argument says fp32. MXFP8 layers
  *    decide every E4M3 code of a computed GEMM operand on its fp32 value
- *    rather than on a bf16 rounding of it: G, U, H (save buffer) and d_o are
- *    fp32, and dG | dU exist only as the E4M3 operands the backward writes
- *    from fp32 values in registers. Weights:
+ *    rather than on a bf16 rounding of it: G, U (save buffer) and d_o are
+ *    fp32, and H and dG | dU exist only as the E4M3 operands the GEMM
+ *    epilogues write from fp32 values in registers. Weights:
  *    w_router [d][E]; w_gate, w_up [E][d][f]; w_down [E][f][d].
  *  - Row counts: S = T*k routed rows. Index tensors are int32.
  *  - Validation is host-side only and never reads device memory. Errors:
@@ -133,10 +133,14 @@ const char* moe_last_error_message(void);
 size_t moe_workspace_size(int op, const moe_shape* shape);
 
 /* Bytes of the buffer that moe_grouped_ffn_fwd fills with what the backward
- * needs: G, U, H (three [S][f] tensors in the layer dtype, fp32 for MXFP8
- * layers) and, for MXFP8 layers, the E4M3 copies (with their E8M0 scales) of
- * w_gate, w_up and w_down in the layouts of the backward's dgrad GEMMs, which
- * the forward writes from the same read that quantises its own copies.
+ * needs. fp32 and bf16 layers: G, U, H (three [S][f] tensors in the layer
+ * dtype). MXFP8 layers: G and U in fp32, each in a blocked layout (every
+ * expert's rows padded to a multiple of 64; 32 x 32 blocks of 4 KB), H only
+ * as the W_down weight gradient's E4M3 operand (blocked along each expert's
+ * tokens), and the E4M3 copies (with their E8M0 scales) of w_gate, w_up and
+ * w_down in the layouts of the backward's dgrad GEMMs, which the forward
+ * writes from the same read that quantises its own copies. The layout of
+ * the MXFP8 buffer is internal to the library.
  * 0 with MOE_FLAG_RECOMPUTE (then `save` may be NULL in the FFN calls). */
 size_t moe_save_size(const moe_shape* shape);
 
@@ -216,8 +220,8 @@ int moe_read_device_status(const void* ws, void* stream);
  * of its rows r: G = xp[r] · w_gate[e], U = xp[r] · w_up[e],
  * H = silu(G) * U with silu(z) = z / (1 + exp(-z)), o[r] = H · w_down[e];
  * fp32 accumulation, one rounding to the layer dtype per stored value.
- * save (>= moe_save_size bytes) receives G, U, H (and, for MXFP8 layers, the
- * backward's quantised weight copies) for the backward.
+ * save (>= moe_save_size bytes) receives what the backward needs (see
+ * moe_save_size).
  * ws: moe_workspace_size(MOE_OP_FFN_FWD) bytes (may be 0 -> NULL allowed).
  * xp_mx (MXFP8 layers only; NULL = quantise xp here): the MXFP8 image of xp
  * that moe_dispatch wrote; it must hold the current xp's codes.

@@ -100,8 +100,10 @@ int check_ffn_dtype(const moe_shape* s, const char* who) {
 
 bool recompute(const moe_shape* s) { return (s->flags & MOE_FLAG_RECOMPUTE) != 0; }
 
-// G, U, H: three [S][f] planes (act_bytes each element).
+// G, U, H: three [S][f] planes (act_bytes each element); MXFP8 layers keep
+// only G and U, as two blocked fp32 planes over the rows padded per expert.
 size_t gu_h_bytes(const moe_shape* s) {
+  if (s->dtype == MOE_MXFP8) return 2 * moe::ffn_mx_gu_plane((int)(s->T * s->k), (int)s->f, (int)s->E);
   return ((size_t)3 * s->T * s->k * s->f * act_bytes(s->dtype) + 255) & ~(size_t)255;
 }
 // dG | dU rows of the backward workspace: [S][2f] (act_bytes each element).
@@ -115,7 +117,9 @@ size_t dgu_bytes_for(const moe_shape* s) {
 // quantised weight copies.
 size_t save_planes(const moe_shape* s) { return recompute(s) ? 0 : gu_h_bytes(s); }
 size_t save_bytes_for(const moe_shape* s) {
-  return save_planes(s) + (s->dtype == MOE_MXFP8 ? moe::ffn_mx_save_extra((int)s->d, (int)s->f, (int)s->E) : 0);
+  return save_planes(s) + (s->dtype == MOE_MXFP8
+                               ? moe::ffn_mx_save_extra((int)(s->T * s->k), (int)s->d, (int)s->f, (int)s->E)
+                               : 0);
 }
 
 // moe_kernel_timer's state: the armed mode (-1: none) and the caller's
@@ -289,9 +293,9 @@ int moe_grouped_ffn_fwd(const void* xp, const uint8_t* xp_mx, const void* w_gate
   moe::FfnArgs a{};
   a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
   a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down; a.xp_mx = xp_mx;
-  const size_t plane = (size_t)a.S * a.f * act_bytes(s->dtype);
-  char* gu_h = static_cast<char*>(recompute(s) ? ws : save);  // G, U, H
-  a.G = gu_h; a.U = gu_h + plane; a.H = gu_h + 2 * plane;
+  const size_t plane = s->dtype == MOE_MXFP8 ? gu_h_bytes(s) / 2 : (size_t)a.S * a.f * act_bytes(s->dtype);
+  char* gu_h = static_cast<char*>(recompute(s) ? ws : save);  // G, U, H (MXFP8: blocked G, U)
+  a.G = gu_h; a.U = gu_h + plane; a.H = s->dtype == MOE_MXFP8 ? nullptr : gu_h + 2 * plane;
   a.mx_save = static_cast<char*>(save) + save_planes(s);
   a.o = o_out;
   if (s->dtype == MOE_MXFP8)
@@ -341,12 +345,12 @@ int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, 
   moe::FfnArgs a{};
   a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
   a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
-  const size_t plane = (size_t)a.S * a.f * act_bytes(s->dtype);
+  const size_t plane = s->dtype == MOE_MXFP8 ? gu_h_bytes(s) / 2 : (size_t)a.S * a.f * act_bytes(s->dtype);
   const size_t dgu_bytes = dgu_bytes_for(s);
   char* sv = const_cast<char*>(static_cast<const char*>(save));
   // Recompute: G, U, H are rebuilt in the workspace, after the dG|dU rows.
   char* gu_h = recompute(s) ? static_cast<char*>(ws) + dgu_bytes : sv;
-  a.G = gu_h; a.U = gu_h + plane; a.H = gu_h + 2 * plane;
+  a.G = gu_h; a.U = gu_h + plane; a.H = s->dtype == MOE_MXFP8 ? nullptr : gu_h + 2 * plane;
   a.recompute = recompute(s);
   a.mx_save = sv + save_planes(s);
   a.d_o = d_o; a.d_o_mx = d_o_mx; a.dgu = ws; a.dxp = dxp_out; a.dw_gate = dw_gate_out; a.dw_up = dw_up_out; a.dw_down = dw_down_out;

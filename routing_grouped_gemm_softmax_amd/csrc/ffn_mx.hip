@@ -47,6 +47,7 @@ int64_t padded_rows(int S, int E) { return (static_cast<int64_t>(S) + 63LL * E +
 
 struct FwdWs {
   uint8_t *xq, *xs, *wgq, *wgs, *wuq, *wus, *hq, *hs, *wdq, *wds;
+  int32_t* poff;  // per-expert offsets of the rows padded to 64
 };
 FwdWs carve_fwd(char* base, int S, int d, int f, int E, size_t* total) {
   Carve c{base};
@@ -58,22 +59,27 @@ FwdWs carve_fwd(char* base, int S, int d, int f, int E, size_t* total) {
   o.wuq = c.take(w); o.wus = c.take(w / 32);
   o.hq = c.take(sf); o.hs = c.take(sf / 32);
   o.wdq = c.take(w); o.wds = c.take(w / 32);
+  o.poff = reinterpret_cast<int32_t*>(c.take(static_cast<size_t>(E + 1) * 4));
   if (total) *total = c.used;
   return o;
 }
 
-// Save-buffer region of an MXFP8 layer: the columns-blocked weight copies the
-// backward's dgrad GEMMs use, written by the forward's weight pass.
+// Save-buffer region of an MXFP8 layer after the blocked G, U planes: the
+// columns-blocked weight copies the backward's dgrad GEMMs use, written by
+// the forward's weight pass, and H as the W_down weight gradient's
+// token-major operand, written by the gate/up epilogue.
 struct SaveMx {
-  uint8_t *wgq, *wgs, *wuq, *wus, *wdq, *wds;
+  uint8_t *wgq, *wgs, *wuq, *wus, *wdq, *wds, *ht, *hts;
 };
-SaveMx carve_save(char* base, int d, int f, int E, size_t* total) {
+SaveMx carve_save(char* base, int S, int d, int f, int E, size_t* total) {
   Carve c{base};
   const size_t w = static_cast<size_t>(E) * d * f;
+  const size_t P = static_cast<size_t>(padded_rows(S, E));
   SaveMx o;
   o.wgq = c.take(w); o.wgs = c.take(w / 32);
   o.wuq = c.take(w); o.wus = c.take(w / 32);
   o.wdq = c.take(w); o.wds = c.take(w / 32);
+  o.ht = c.take(P * f); o.hts = c.take(P * f / 32);
   if (total) *total = c.used;
   return o;
 }
@@ -82,7 +88,7 @@ struct BwdWs {
   uint8_t *doq, *dos, *dguq, *dgus;
   int32_t* poff;
   uint8_t* blk;  // block table of the grouped transposing quantiser
-  uint8_t *ht, *hts, *dot, *dots, *xt, *xts, *dgut, *dguts;
+  uint8_t *dot, *dots, *xt, *xts, *dgut, *dguts;
 };
 BwdWs carve_bwd(char* base, int S, int d, int f, int E, size_t* total) {
   Carve c{base};
@@ -94,7 +100,6 @@ BwdWs carve_bwd(char* base, int S, int d, int f, int E, size_t* total) {
   o.dguq = c.take(s2f); o.dgus = c.take(s2f / 32);
   o.poff = reinterpret_cast<int32_t*>(c.take(static_cast<size_t>(E + 1) * 4));
   o.blk = c.take(P / 64 * 8);
-  o.ht = c.take(P * f); o.hts = c.take(P * f / 32);
   o.dot = c.take(P * d); o.dots = c.take(P * d / 32);
   o.xt = c.take(P * d); o.xts = c.take(P * d / 32);
   o.dgut = c.take(P * 2 * f); o.dguts = c.take(P * 2 * f / 32);
@@ -116,10 +121,14 @@ size_t ffn_mx_fwd_workspace(int S, int d, int f, int E) {
   return n;
 }
 
-size_t ffn_mx_save_extra(int d, int f, int E) {
+size_t ffn_mx_save_extra(int S, int d, int f, int E) {
   size_t n = 0;
-  carve_save(nullptr, d, f, E, &n);
+  carve_save(nullptr, S, d, f, E, &n);
   return n;
+}
+
+size_t ffn_mx_gu_plane(int S, int f, int E) {
+  return a256(static_cast<size_t>(padded_rows(S, E)) * f * 4);
 }
 
 size_t ffn_mx_bwd_workspace(int S, int d, int f, int E) {
@@ -132,7 +141,9 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
   const int S = a.S, d = a.d, f = a.f, E = a.E;
   const FwdWs w = carve_fwd(static_cast<char*>(ws), S, d, f, E, nullptr);
   const int64_t wsz = static_cast<int64_t>(d) * f;
-  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), d, f, E, nullptr);
+  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), S, d, f, E, nullptr);
+  const int64_t P = padded_rows(S, E);
+  TRY(launch_mx_poff(a.offsets, E, w.poff, s));
   // Operands: Xp along d; W_gate, W_up along d, transposed to [f][d]. The same
   // read of each weight also writes its copy blocked along f ([d][f], in the
   // save buffer) for the backward's dXp GEMM.
@@ -154,9 +165,12 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
     p.a = xq; p.lda = d; p.as = xs; p.as_slab = 2LL * S;
     p.b0 = w.wgq; p.b1 = w.wuq; p.ldb = d; p.bstride = wsz;
     p.bs0 = w.wgs; p.bs1 = w.wus; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
-    p.c0 = a.G; p.c1 = a.U; p.c2 = a.H; p.ldc = f; p.N = 2 * f; p.K = d;
-    // The epilogue also writes H along f (the next GEMM's A operand).
+    p.c0 = a.G; p.c1 = a.U; p.ldc = f; p.N = 2 * f; p.K = d;
+    // G, U go to the save buffer in the blocked layout of the down-dgrad
+    // epilogue; H leaves only as E4M3 operands: along f (the next GEMM's A
+    // operand) and along the expert's tokens (the W_down weight gradient's).
     p.mxq = w.hq; p.mxs = w.hs; p.mxq_ld = f; p.mxs_slab = 2LL * S;
+    p.tq = sv.ht; p.ts = sv.hts; p.tq_ld = P; p.ts_slab = 2LL * f; p.poff = w.poff;
     TRY(launch_mx_ragged(FWD_GU, p, s));
   }
   // Operands: H along f (above); W_down along f, transposed to [d][f] (and
@@ -174,7 +188,7 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
 hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
   const int S = a.S, d = a.d, f = a.f, E = a.E;
   const BwdWs w = carve_bwd(static_cast<char*>(ws), S, d, f, E, nullptr);
-  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), d, f, E, nullptr);
+  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), S, d, f, E, nullptr);
   const int64_t wsz = static_cast<int64_t>(d) * f;
   const int64_t P = padded_rows(S, E);
   // Per-expert padded offsets of the token-major (weight-gradient) layouts.
@@ -212,12 +226,12 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
     TRY(launch_mx_ragged(BWD_GU, p, s));
   }
   // Weight gradients: every operand along the expert's tokens, transposed.
-  {  // dW_down[e] = q(H_e)^T q(dO_e)
-    TRY(launch_mx_tgroup_f32(a.H, S, f, w.blk, w.ht, P, w.hts, s));
+  {  // dW_down[e] = q(H_e)^T q(dO_e); q(H) along the tokens came from the
+     // forward's gate/up epilogue.
     TRY(launch_mx_tgroup_f32(a.d_o, S, d, w.blk, w.dot, P, w.dots, s));
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
-    p.a = w.ht; p.lda = P; p.as = w.hts; p.as_slab = 2LL * f;
+    p.a = sv.ht; p.lda = P; p.as = sv.hts; p.as_slab = 2LL * f;
     p.b0 = w.dot; p.ldb = P; p.bs0 = w.dots; p.bs_slab = 2LL * d;
     p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = static_cast<int64_t>(f) * d; p.M = f; p.N = d; p.f = d;
     TRY(launch_mx_wgrad(p, s));

@@ -387,11 +387,10 @@ __device__ __forceinline__ TileCoord wgrad_tile(const GemmParams& p, int t) {
 // Writes the accumulators of one BM x BN tile (and, for BWD_DOWN, reads the
 // saved G, U it needs) through a per-wave LDS area of smem, which must hold
 // 4 x 2 x (BM/2) x 128 bytes and be free of other use.
-// With QUANT (the MXFP8 kernels), G, U, H (FWD_GU) and dG | dU (BWD_DOWN) are
-// fp32 tensors (BWD_DOWN also reads G, U as fp32), and H and dG | dU are
-// also written as the next GEMM's K-major MXFP8 operand (p.mxq, p.mxs): each
-// 32-block of a row is encoded from its fp32 values, 8 lanes per block, with
-// the exact encoder, so every E4M3 code is decided on the fp32 value.
+// With QUANT (the MXFP8 kernels), FWD_GU writes fp32 G, U in a blocked
+// layout and H, and BWD_DOWN dG | dU, only as the next GEMMs' E4M3 operands
+// (K-major p.mxq, p.mxs; token-major p.tq, p.ts), every code decided on the
+// fp32 value in registers; BWD_DOWN reads the blocked G, U.
 template <int MODE, int BM, int BN, bool QUANT = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN / 64][BM / 64], char* smem,
                                          int wave, int lane, const TileCoord& tc) {
@@ -437,84 +436,121 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     }
     wave_sync();
   };
-  // fp32 staging (QUANT): a staging row holds 32 fp32 columns, logical
-  // 16-byte chunk c of row r at chunk c ^ ((r / 2) % 8).
-  auto put4f = [&](int slot, int r, int col, float a, float b, float c, float d) {
-    *reinterpret_cast<float4*>(wa + slot * kSlot + r * 128 + ((((col >> 2) ^ (r >> 1)) & 7) << 4)) =
-        make_float4(a, b, c, d);
-  };
-  auto get4f = [&](int slot, int r, int col) -> float4 {
-    return *reinterpret_cast<const float4*>(wa + slot * kSlot + r * 128 + ((((col >> 2) ^ (r >> 1)) & 7) << 4));
-  };
-  // Rows [0, rows) of fp32 staging tile `slot` (32 columns) -> global rows
-  // g + r*ld (bytes). With qcol >= 0 (wave-uniform), also each row's 32-block
-  // as E4M3 codes to p.mxq row mrow + r, columns qcol .. qcol + 31, and its
-  // E8M0 code to p.mxs; the 8 lanes of a row hold the block.
-  auto flush32 = [&](int slot, char* g, int64_t ld, int rows, int qcol) {
-    wave_sync();
-    const int c = lane & 7;
-#pragma unroll 4
-    for (int t = 0; t < WM / 8; ++t) {
-      const int r = t * 8 + (lane >> 3);
-      const uint4 v = *reinterpret_cast<const uint4*>(wa + slot * kSlot + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
-      const bool live = r < rows;
-      if (live) *reinterpret_cast<uint4*>(g + r * ld + c * 16) = v;
-      if (qcol >= 0) {
-        float x[4];
-        unpack16(v, x);
-        const int code = mx_group8_code(x);  // every lane: butterflies
-        if (live) {
-          const int64_t row = mrow + r, col = qcol + c * 4;
-          *reinterpret_cast<uint32_t*>(p.mxq + row * p.mxq_ld + col) = mx_encode4_exact(x, code);
-          if (c == 0) p.mxs[(col / 64) * p.mxs_slab + row * 2 + (col / 32) % 2] = static_cast<uint8_t>(code);
-        }
-      }
-    }
-    wave_sync();
-  };
   const int rows = (MODE == WGRAD) ? WM : max(0, min(WM, row_end - mrow));
   auto acc4 = [&](int j, int i, int q) {
     return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
   };
 
   if constexpr (MODE == FWD_GU && QUANT) {
-    // fp32 G, U, H in 32-column groups: gate block JJ and up block JJ + NB/2
-    // cover the same 32 f-columns.
-    const int64_t ld = p.ldc * 4;
-    static_for<NB / 2>([&](auto JJ) {
+    // G, U and H = G sig(G) U in fp32, one 32 x 32 block (gate block JJ and
+    // up block JJ + NB/2 cover the same 32 f-columns, row block I) at a time,
+    // straight from the accumulators:
+    //  - G and U to the save buffer in the blocked layout the down-dgrad
+    //    epilogue reads back: block (padded row / 32, column / 32), 4 KB, in
+    //    lane order (lane l: row l % 32, columns 8 Q + 4 (l / 32) .. +3 as one
+    //    16-byte piece at Q KB + 16 l), so every store and every later load
+    //    is one contiguous kilobyte. Padded rows are poff[e] + row inside e.
+    //  - H only as E4M3 operands, each code decided on the fp32 value:
+    //    K-major along f (the down GEMM's A operand; a row's 32-block sits in
+    //    lanes l and l ^ 32), and token-major [f][P] for the weight gradient
+    //    of W_down (the block goes through LDS column-major; lane c < 32
+    //    encodes column c, 32 tokens).
+    // Blocks past the expert's rows padded to 64 are left alone (they are
+    // the next expert's); rows past its end inside them are zeros (the A
+    // operand reads 0 there).
+    const int e_first = p.offsets[e];
+    const int rel0 = mrow - e_first;
+    const int n64 = (row_end - e_first + 63) & ~63;
+    const int64_t pt0 = static_cast<int64_t>(p.poff[e]) + rel0;  // a multiple of 32
+    const int fb = p.f / 32;
+    const auto rQ = make_rsrc(p.mxq + static_cast<int64_t>(mrow) * p.mxq_ld, static_cast<int64_t>(rows) * p.mxq_ld);
+    constexpr int kTgFloats = 32 * 36;
+    float* const tgw = reinterpret_cast<float*>(smem + wave * (2 * kTgFloats * 4));
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    static_for<(NB / 2) * MB>([&](auto BI) {
+      constexpr int bi = decltype(BI)::value, JJ = bi / MB, I = bi % MB;
       const int col0 = nt * (BN / 2) + wn * (WN / 2) + JJ * 32;
-      const int64_t base = (static_cast<int64_t>(mrow) * p.ldc + col0) * 4;
-      static_for<MB>([&](auto I) {
-        static_for<4>([&](auto Q) {
-          const int r = I * 32 + l32, col = 8 * Q + 4 * hl;
-          float g[4], h[4];
+      const bool live = rel0 + I * 32 < n64;
+      float h[16];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            g[c] = acc[JJ][I][4 * Q + c];
-            const float u = acc[JJ + NB / 2][I][4 * Q + c];
-            h[c] = g[c] * sigmoid_f(g[c]) * u;
-          }
-          put4f(0, r, col, g[0], g[1], g[2], g[3]);
-          put4f(1, r, col, h[0], h[1], h[2], h[3]);
-        });
-      });
-      flush32(0, static_cast<char*>(p.c0) + base, ld, rows, -1);
-      flush32(1, static_cast<char*>(p.c2) + base, ld, rows, col0);
-      static_for<MB>([&](auto I) {
-        static_for<4>([&](auto Q) {
-          constexpr int j = JJ + NB / 2;
-          put4f(0, I * 32 + l32, 8 * Q + 4 * hl, acc[j][I][4 * Q], acc[j][I][4 * Q + 1], acc[j][I][4 * Q + 2],
-                acc[j][I][4 * Q + 3]);
-        });
-      });
-      flush32(0, static_cast<char*>(p.c1) + base, ld, rows, -1);
+      for (int r = 0; r < 16; ++r) {
+        const float g = acc[JJ][I][r], u = acc[JJ + NB / 2][I][r];
+        h[r] = g * sigmoid_f(g) * u;
+      }
+      if (live) {
+        const int64_t kb = ((pt0 / 32 + I) * fb + col0 / 32) * 4;  // in kilobytes
+        float* const Gb = static_cast<float*>(p.c0) + kb * 256 + lane * 4;
+        float* const Ub = static_cast<float*>(p.c1) + kb * 256 + lane * 4;
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q) {
+          *reinterpret_cast<float4*>(Gb + Q * 256) =
+              make_float4(acc[JJ][I][4 * Q], acc[JJ][I][4 * Q + 1], acc[JJ][I][4 * Q + 2], acc[JJ][I][4 * Q + 3]);
+          *reinterpret_cast<float4*>(Ub + Q * 256) =
+              make_float4(acc[JJ + NB / 2][I][4 * Q], acc[JJ + NB / 2][I][4 * Q + 1], acc[JJ + NB / 2][I][4 * Q + 2],
+                          acc[JJ + NB / 2][I][4 * Q + 3]);
+        }
+      }
+      // Token-major: stage column-major.
+      float* const tg = tgw + (bi & 1) * kTgFloats;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tg[(8 * (r / 4) + 4 * hl + r % 4) * 36 + l32] = h[r];
+      // K-major along f.
+      {
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(h[r]));
+        const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        const int code = mx_scale_code(fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1])));
+        uint32_t w[4];
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q)
+          w[Q] = e4m3_encode4(ldexpf(h[4 * Q], 127 - code), ldexpf(h[4 * Q + 1], 127 - code),
+                              ldexpf(h[4 * Q + 2], 127 - code), ldexpf(h[4 * Q + 3], 127 - code));
+        const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto c = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{a[0], a[1], c[0], c[1]}, rQ,
+                                               static_cast<uint32_t>((I * 32 + l32) * p.mxq_ld + col0 + 16 * hl), 0,
+                                               0);
+        const auto rS = make_rsrc(p.mxs + static_cast<int64_t>(col0 / 64) * p.mxs_slab +
+                                      static_cast<int64_t>(mrow) * 2,
+                                  static_cast<int64_t>(rows) * 2);
+        if (hl == 0)
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rS,
+                                               static_cast<uint32_t>((I * 32 + l32) * 2 + (col0 / 32) % 2), 0, 0);
+      }
+      // Token-major: lane c < 32 encodes column c of the block.
+      if (live && lane < 32) {
+        const float* col = tg + lane * 36;
+        float v[32];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float4 x = *reinterpret_cast<const float4*>(col + 4 * t);
+          v[4 * t] = x.x; v[4 * t + 1] = x.y; v[4 * t + 2] = x.z; v[4 * t + 3] = x.w;
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 32; ++t) m = fmaxf(m, fabsf(v[t]));
+        const int code = mx_scale_code(m);
+        uint32_t w[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          w[t] = e4m3_encode4(ldexpf(v[4 * t], 127 - code), ldexpf(v[4 * t + 1], 127 - code),
+                              ldexpf(v[4 * t + 2], 127 - code), ldexpf(v[4 * t + 3], 127 - code));
+        const int64_t ch = col0 + lane, pt = pt0 + I * 32;
+        uint8_t* dst = p.tq + ch * p.tq_ld + pt;
+        *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4_t*>(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+        p.ts[(pt / 64) * p.ts_slab + ch * 2 + (pt / 32) % 2] = static_cast<uint8_t>(code);
+      }
     });
   } else if constexpr (MODE == BWD_DOWN && QUANT) {
     // dH -> dG = dH U sig(G) (1 + G (1 - sig(G))), dU = dH G sig(G) in fp32
     // from the fp32 saved G, U, one 32 x 32 block (J, I) at a time. The saved
     // G, U of a block come straight into registers in the accumulator layout
-    // (lane: row 32 I + l%32, columns 8 Q + 4 (l/32) .. +3), one block ahead
-    // of its use; rows past the expert's end read 0, so dG, dU are 0 there.
+    // (lane: row 32 I + l%32, columns 8 Q + 4 (l/32) .. +3), as four
+    // contiguous kilobytes each from the blocked layout the gate/up epilogue
+    // wrote, two blocks ahead of their use; rows past the expert's end hold
+    // 0, so dG, dU are 0 there.
     // dG and dU leave only as the next GEMMs' E4M3 operands, each code
     // decided on the fp32 value:
     //  - K-major along 2f (dG in columns [0, f), dU in [f, 2f)): a row's
@@ -529,13 +565,16 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     // Lane-half exchanges use v_permlane32_swap (a VALU op, no LDS round trip):
     // swap(x, y) leaves lanes 0..31 of x and lanes 32..63 of y in place and
     // exchanges lanes 32..63 of x with lanes 0..31 of y.
-    const int64_t lds_ = static_cast<int64_t>(p.f) * 4;
     const int e_first = p.offsets[e];
     const int rel0 = mrow - e_first;                       // first row of the block, inside the expert
     const int n64 = (row_end - e_first + 63) & ~63;        // the expert's rows padded to 64
     const int64_t pt0 = static_cast<int64_t>(p.poff[e]) + rel0;
-    const auto rG = make_rsrc(static_cast<const char*>(p.e0) + static_cast<int64_t>(mrow) * lds_, rows * lds_);
-    const auto rU = make_rsrc(static_cast<const char*>(p.e1) + static_cast<int64_t>(mrow) * lds_, rows * lds_);
+    // G, U in the blocked layout the gate/up epilogue writes (4 KB per 32 x
+    // 32 block, lane order): blocks past the expert's padded rows read 0.
+    const int fb = p.f / 32;
+    const int64_t gb0 = (pt0 / 32) * fb * 4096, gbytes = static_cast<int64_t>(max(0, n64 - rel0) / 32) * fb * 4096;
+    const auto rG = make_rsrc(static_cast<const char*>(p.e0) + gb0, gbytes);
+    const auto rU = make_rsrc(static_cast<const char*>(p.e1) + gb0, gbytes);
     const auto rQ = make_rsrc(p.mxq + static_cast<int64_t>(mrow) * p.mxq_ld, rows * p.mxq_ld);
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int kAhead = 2;       // blocks of G, U in flight ahead of the one in use
@@ -545,7 +584,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
       const int col0 = n0 + wn * WN + J * 32;
 #pragma unroll
       for (int Q = 0; Q < 4; ++Q) {
-        const uint32_t off = static_cast<uint32_t>((I * 32 + l32) * lds_ + (col0 + 8 * Q + 4 * hl) * 4);
+        const uint32_t off = static_cast<uint32_t>(((I * fb + col0 / 32) * 4 + Q) * 1024 + lane * 16);
         gu[b][0][Q] = __builtin_amdgcn_raw_buffer_load_b128(rG, off, 0, 0);
         gu[b][1][Q] = __builtin_amdgcn_raw_buffer_load_b128(rU, off, 0, 0);
       }

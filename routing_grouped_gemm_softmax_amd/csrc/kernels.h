@@ -25,8 +25,10 @@ struct FfnArgs {
   void* dw_gate;
   void* dw_up;
   void* dw_down;
-  // MXFP8: the save-buffer region the forward fills with the backward's
-  // quantised weight copies (ffn_mx_save_extra bytes).
+  // MXFP8: the save-buffer region after the blocked G, U planes that the
+  // forward fills with the backward's quantised weight copies and H's
+  // token-major operand (ffn_mx_save_extra bytes). G, U are then the blocked
+  // planes (ffn_mx_gu_plane bytes each) and H is unused.
   void* mx_save;
   // MXFP8, optional: the operand images (mx_image layout) of xp and d_o that
   // moe_dispatch / moe_combine_bwd already wrote; NULL = quantise here.
@@ -148,7 +150,10 @@ hipError_t launch_mx_poff(const int32_t* offsets, int E, int32_t* poff, hipStrea
 // MXFP8 expert FFN (ffn_mx.hip): workspace bytes and launch.
 size_t ffn_mx_fwd_workspace(int S, int d, int f, int E);
 // Extra save-buffer bytes of an MXFP8 layer (the backward's weight copies).
-size_t ffn_mx_save_extra(int d, int f, int E);
+size_t ffn_mx_save_extra(int S, int d, int f, int E);
+// Bytes of one blocked fp32 G or U plane of an MXFP8 layer: rows padded to 64
+// per expert, 32 x 32 blocks of 4 KB in accumulator lane order.
+size_t ffn_mx_gu_plane(int S, int f, int E);
 size_t ffn_mx_bwd_workspace(int S, int d, int f, int E);
 hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s);

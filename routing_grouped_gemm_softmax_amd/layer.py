@@ -74,9 +74,13 @@ class MoELayer:
             self.ws_dispatch_bwd = ws(L.MOE_OP_DISPATCH_BWD)
 
     def saved(self):
-        """(G, U, H), each [S][f] (fp32 for MXFP8 layers): views of the save
-        buffer or, for a recompute layer, of the planes its last backward
-        rebuilt in the backward workspace (after the dG|dU rows)."""
+        """(G, U, H), each [S][f]: views of the save buffer or, for a
+        recompute layer, of the planes its last backward rebuilt in the
+        backward workspace (after the dG|dU rows). fp32 and bf16 layers only:
+        an MXFP8 layer saves G, U in a blocked layout and H only as an E4M3
+        operand."""
+        if self.shape.dtype == L.MOE_MXFP8:
+            raise ValueError("MXFP8 layers save G, U blocked and H only as an E4M3 operand")
         S, f = self.T * self.k, self.f
         eb = torch.empty((), dtype=self.act_dtype).element_size()
         if self.recompute:

@@ -31,21 +31,62 @@ def padded_rows(S: int, E: int) -> int:
 
 
 def fwd_pieces(S, d, f, E):
-    """Forward workspace: xq, xs, wgq, wgs, wuq, wus, hq, hs, wdq, wds."""
+    """Forward workspace: xq, xs, wgq, wgs, wuq, wus, hq, hs, wdq, wds, poff."""
     w = E * d * f
-    names = ["xq", "xs", "wgq", "wgs", "wuq", "wus", "hq", "hs", "wdq", "wds"]
-    sizes = [S * d, S * d // 32, w, w // 32, w, w // 32, S * f, S * f // 32, w, w // 32]
+    names = ["xq", "xs", "wgq", "wgs", "wuq", "wus", "hq", "hs", "wdq", "wds", "poff"]
+    sizes = [S * d, S * d // 32, w, w // 32, w, w // 32, S * f, S * f // 32, w, w // 32, (E + 1) * 4]
     off, _ = _carve(sizes)
     return {n: (o, s) for n, o, s in zip(names, off, sizes)}
 
 
+def save_pieces(S, d, f, E):
+    """Save buffer of an MXFP8 layer: the blocked fp32 G and U planes, then
+    wgq, wgs, wuq, wus, wdq, wds (the dgrad weight copies) and ht, hts (H
+    along each expert's tokens)."""
+    P = padded_rows(S, E)
+    plane = _a256(P * f * 4)
+    w = E * d * f
+    names = ["wgq", "wgs", "wuq", "wus", "wdq", "wds", "ht", "hts"]
+    sizes = [w, w // 32, w, w // 32, w, w // 32, P * f, P * f // 32]
+    off, _ = _carve(sizes)
+    out = {"G": (0, P * f * 4), "U": (plane, P * f * 4)}
+    out.update({n: (2 * plane + o, s) for n, o, s in zip(names, off, sizes)})
+    return out
+
+
+def padded_offsets(offsets):
+    n = np.diff(np.asarray(offsets))
+    return np.concatenate([[0], np.cumsum((n + 63) // 64 * 64)])
+
+
+def blocked_rows(save, which, rows, offsets, S, f, E):
+    """Rows `rows` (expert-sorted row ids, host array) of the blocked fp32 G
+    or U plane of an MXFP8 layer's save buffer (a uint8 device tensor), as a
+    host fp64 [len(rows)][f] array. Block (padded row / 32, column / 32) is
+    4 KB; lane l of it holds row l % 32, columns 8 Q + 4 (l / 32) .. +3 at
+    Q KB + 16 l."""
+    import torch
+    o, n = save_pieces(S, 1, f, E)[which]
+    plane = save[o:o + n].view(torch.float32)
+    rows = np.asarray(rows)
+    offsets = np.asarray(offsets)
+    e = np.searchsorted(offsets, rows, side="right") - 1
+    pr = padded_offsets(offsets)[e] + rows - offsets[e]
+    c = np.arange(f)
+    fb = f // 32
+    idx = (((pr[:, None] // 32) * fb + c[None, :] // 32) * 4 + (c[None, :] % 32) // 8) * 256 \
+        + (((c[None, :] // 4) % 2) * 32 + pr[:, None] % 32) * 4 + c[None, :] % 4
+    t = torch.from_numpy(idx.reshape(-1).astype(np.int64)).to(plane.device)
+    return plane[t].cpu().numpy().astype(np.float64).reshape(len(rows), f)
+
+
 def bwd_pieces(S, d, f, E):
     """Backward workspace of an MXFP8 layer: doq, dos, dguq, dgus, poff, blk,
-    ht, hts, dot, dots, xt, xts, dgut, dguts."""
+    dot, dots, xt, xts, dgut, dguts."""
     P = padded_rows(S, E)
-    names = ["doq", "dos", "dguq", "dgus", "poff", "blk", "ht", "hts", "dot", "dots", "xt", "xts", "dgut", "dguts"]
+    names = ["doq", "dos", "dguq", "dgus", "poff", "blk", "dot", "dots", "xt", "xts", "dgut", "dguts"]
     sizes = [S * d, S * d // 32, S * 2 * f, S * 2 * f // 32, (E + 1) * 4, P // 64 * 8,
-             P * f, P * f // 32, P * d, P * d // 32, P * d, P * d // 32, P * 2 * f, P * 2 * f // 32]
+             P * d, P * d // 32, P * d, P * d // 32, P * 2 * f, P * 2 * f // 32]
     off, _ = _carve(sizes)
     return {n: (o, s) for n, o, s in zip(names, off, sizes)}
 

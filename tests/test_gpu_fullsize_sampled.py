@@ -87,10 +87,15 @@ def _expert_device(F, e):
     L = F.layer
     a, b = int(F.offsets[e]), int(F.offsets[e + 1])
     rows = np.arange(a, b)
-    G, U, H = (_rows(t, rows) for t in L.saved())
-    dv = dict(G=G, U=U, H=H, O=_rows(L.o, rows), dO=_rows(L.d_o, rows), dXp=_rows(L.dxp, rows),
+    dv = dict(O=_rows(L.o, rows), dO=_rows(L.d_o, rows), dXp=_rows(L.dxp, rows),
               dW_gate=host(L.dw_gate[e]), dW_up=host(L.dw_up[e]), dW_down=host(L.dw_down[e]))
-    if not F.mx:  # MXFP8 layers keep dG | dU only as E4M3 operands (checked as images)
+    if F.mx:
+        # MXFP8: fp32 G, U blocked in the save buffer; H and dG | dU exist
+        # only as E4M3 operands (checked as images).
+        wl = F.wl
+        dv["G"], dv["U"] = (ML.blocked_rows(L.save, n, rows, F.offsets, wl.T * wl.k, wl.f, wl.E) for n in "GU")
+    else:
+        dv["G"], dv["U"], dv["H"] = (_rows(t, rows) for t in L.saved())
         dv["dG"], dv["dU"] = (_rows(t, rows) for t in L.dgu())
     return rows, dv
 
@@ -108,30 +113,31 @@ def _check_expert(F, e):
     return {n: rel_err(dv[n], ref[n]) for n in ref if n in dv}, (rows, dv, xp)
 
 
-def _dgu_images(F, e, rows):
-    """The device's dG | dU operands of expert e's rows, dequantised: the
-    K-major image (the dXp GEMM's) and the token-major one (the weight
-    gradient's)."""
-    L, wl = F.layer, F.wl
-    S, f = wl.T * wl.k, wl.f
-    pb = ML.bwd_pieces(S, wl.d, f, wl.E)
+def _images_of(F, e, rows, ws, pieces, kq, ks, tq, ts, K):
+    """An operand of expert e's rows as the device holds it, dequantised: its
+    K-major image (kq, ks; None to skip) and its token-major one (tq, ts), both
+    in workspace or save buffer `ws`."""
+    wl = F.wl
+    S = wl.T * wl.k
     a, b = int(rows[0]), int(rows[-1]) + 1
-    qo, _ = pb["dguq"]
-    so, _ = pb["dgus"]
-    K = 2 * f
-    codes = host(L.ws_ffn_bwd[qo + a * K:qo + b * K]).reshape(b - a, K)
-    sc = host(L.ws_ffn_bwd[so:so + S * K // 32].view(K // 64, S, 2)[:, a:b, :]).transpose(1, 0, 2)
-    k_major = O.mx_dequantize(codes, sc.reshape(b - a, K // 32), "cols")
-    n = np.diff(F.offsets)
-    p0 = int(np.concatenate([[0], np.cumsum((n + 63) // 64 * 64)])[e])
+    k_major = None
+    if kq is not None:
+        qo, _ = pieces[kq]
+        so, _ = pieces[ks]
+        codes = host(ws[qo + a * K:qo + b * K]).reshape(b - a, K)
+        sc = host(ws[so:so + S * K // 32].view(K // 64, S, 2)[:, a:b, :]).transpose(1, 0, 2)
+        k_major = O.mx_dequantize(codes, sc.reshape(b - a, K // 32), "cols")
+    if tq is None:
+        return k_major, None
+    p0 = int(ML.padded_offsets(F.offsets)[e])
     P = ML.padded_rows(S, wl.E)
-    qo, _ = pb["dgut"]
-    so, _ = pb["dguts"]
+    qo, _ = pieces[tq]
+    so, _ = pieces[ts]
     n64 = (b - a + 63) // 64 * 64
-    tc = host(L.ws_ffn_bwd[qo:qo + K * P].view(K, P)[:, p0:p0 + n64])
-    ts = host(L.ws_ffn_bwd[so:so + P * K // 32].view(P // 64, K, 2)[p0 // 64:(p0 + n64) // 64])
-    ts = ts.transpose(1, 0, 2).reshape(K, -1)
-    t_major = O.mx_dequantize(tc, ts, "cols")[:, :b - a].T
+    tc = host(ws[qo:qo + K * P].view(K, P)[:, p0:p0 + n64])
+    tsc = host(ws[so:so + P * K // 32].view(P // 64, K, 2)[p0 // 64:(p0 + n64) // 64])
+    tsc = tsc.transpose(1, 0, 2).reshape(K, -1)
+    t_major = O.mx_dequantize(tc, tsc, "cols")[:, :b - a].T
     return k_major, t_major
 
 
@@ -140,40 +146,53 @@ def _check_expert_stage(F, e, rows, dv, xp):
     stored G, U, H, dO, and its dG | dU images for the dXp GEMM and the
     weight gradients. The oracle's dG, dU from the device's G, U, dO are
     returned for the image checks."""
-    k_major, t_major = _dgu_images(F, e, rows)
-    f = F.wl.f
-    Gr, Ur, Hr, Or = F.fwd(xp, e, h_in=dv["H"])
-    bwd = F.bwd(dv["dO"], xp, e, dv["G"], dv["U"], dv["H"], dgdu_in=(k_major[:, :f], k_major[:, f:]),
+    L, wl = F.layer, F.wl
+    S, d, f, E = wl.T * wl.k, wl.d, wl.f, wl.E
+    pf, pb, ps = ML.fwd_pieces(S, d, f, E), ML.bwd_pieces(S, d, f, E), ML.save_pieces(S, d, f, E)
+    hk, ht = _images_of(F, e, rows, L.ws_ffn_fwd, pf, "hq", "hs", None, None, f)[0], \
+        _images_of(F, e, rows, L.save, ps, None, None, "ht", "hts", f)[1]
+    k_major, t_major = _images_of(F, e, rows, L.ws_ffn_bwd, pb, "dguq", "dgus", "dgut", "dguts", 2 * f)
+    Gr, Ur, Hr, Or = F.fwd(xp, e, h_in=hk)
+    bwd = F.bwd(dv["dO"], xp, e, dv["G"], dv["U"], ht, dgdu_in=(k_major[:, :f], k_major[:, f:]),
                 dgdu_w_in=(t_major[:, :f], t_major[:, f:]))
-    ref = dict(G=Gr, U=Ur, H=Hr, O=Or, dXp=bwd[0], dW_gate=bwd[1][0], dW_up=bwd[2][0], dW_down=bwd[3][0])
+    ref = dict(G=Gr, U=Ur, O=Or, dXp=bwd[0], dW_gate=bwd[1][0], dW_up=bwd[2][0], dW_down=bwd[3][0])
     return {n: rel_err(dv[n], ref[n]) for n in ref}, (bwd[4], bwd[5])
 
 
 def _check_expert_images(F, e, rows, dv, xp, dgdu):
     """MXFP8: the E4M3 images of expert e's rows against the oracle's encoding:
-    byte for byte where the device stored the values it quantised, and as
-    the same decisions up to fp32 rounding for dG | dU (the oracle's values
-    from the device's stored G, U, dO)."""
+    byte for byte where the device stored the values it quantised (dO, Xp),
+    and as the same decisions up to the device's rounding for H (the exact
+    SwiGLU of the device's G, U) and dG | dU (the oracle's values from the
+    device's stored G, U, dO), which the device keeps only as images."""
     L, wl = F.layer, F.wl
     S, d, f, E = wl.T * wl.k, wl.d, wl.f, wl.E
     pf, pb = ML.fwd_pieces(S, d, f, E), ML.bwd_pieces(S, d, f, E)
     a = int(rows[0])
     dgu = np.concatenate(dgdu, axis=1)
     atol = np.concatenate([np.full(f, 2e-4 * np.abs(dgdu[0]).max()), np.full(f, 2e-4 * np.abs(dgdu[1]).max())])
-    ML.check_kmajor(L.ws_ffn_fwd, pf, "hq", "hs", dv["H"], f"q(H) expert {e}", S=S, row0=a)
+    H = dv["G"] * O.sigmoid(dv["G"]) * dv["U"]  # the exact SwiGLU of the device's G, U
+    atol_h = 1e-5 * np.abs(H).max()
+    ps = ML.save_pieces(S, d, f, E)
+    ML.check_kmajor(L.ws_ffn_fwd, pf, "hq", "hs", H, f"q(H) expert {e}", S=S, row0=a, near=True, atol=atol_h)
+    ML.check_token_major(L.save, ps, "ht", "hts", H, F.offsets, "q(ht)", experts=[e], S=S, C=f, near=True,
+                         atol=np.full(f, atol_h))
     ML.check_kmajor(L.ws_ffn_bwd, pb, "dguq", "dgus", dgu, f"q(dG|dU) expert {e}", S=S, row0=a, near=True,
                     atol=atol)
-    for q, s_, vals, near in (("ht", "hts", dv["H"], False), ("dot", "dots", dv["dO"], False),
-                              ("xt", "xts", xp, False), ("dgut", "dguts", dgu, True)):
+    for q, s_, vals, near in (("dot", "dots", dv["dO"], False), ("xt", "xts", xp, False),
+                              ("dgut", "dguts", dgu, True)):
         ML.check_token_major(L.ws_ffn_bwd, pb, q, s_, vals, F.offsets, f"q({q})", experts=[e], S=S,
                              C=vals.shape[1], near=near, atol=atol if near else None)
 
 
 def _check_rows_fwd(F, e, rows):
-    L = F.layer
+    L, wl = F.layer, F.wl
     xp = F.xp(rows)
-    G, U, H = (_rows(t, rows) for t in L.saved())
     Gr, Ur, Hr, Or = F.fwd(xp, e)
+    if F.mx:
+        G, U = (ML.blocked_rows(L.save, n, rows, F.offsets, wl.T * wl.k, wl.f, wl.E) for n in "GU")
+        return {"G": rel_err(G, Gr), "U": rel_err(U, Ur), "O": rel_err(_rows(L.o, rows), Or)}
+    G, U, H = (_rows(t, rows) for t in L.saved())
     return {"G": rel_err(G, Gr), "U": rel_err(U, Ur), "H": rel_err(H, Hr), "O": rel_err(_rows(L.o, rows), Or)}
 
 
