@@ -82,10 +82,12 @@ def algorithmic_work(wl, recompute=False):
         "moe_dispatch_bwd": {"bytes": (1 + k) * T * d * b},
     }
     if wl.dtype == "mxfp8":
-        # dispatch and combine backward also write the MXFP8 images of xp and
-        # d_o: one E4M3 byte per element plus one E8M0 byte per 32.
-        for n in ("moe_dispatch", "moe_combine_bwd"):
-            work[n]["bytes"] += S * d + S * d // 32
+        # dispatch also writes the MXFP8 image of xp (one E4M3 byte per
+        # element plus one E8M0 byte per 32); combine backward writes dO only
+        # as its two MXFP8 operands (along d, and along each expert's tokens),
+        # not as rows: it reads dy and o and writes the two images.
+        work["moe_dispatch"]["bytes"] += S * d + S * d // 32
+        work["moe_combine_bwd"]["bytes"] = (1 + k) * T * d * b + 2 * (S * d + S * d // 32)
     if recompute:
         work["moe_grouped_ffn_bwd"]["flops_recompute"] = 4 * S * d * f
     if wl.routing == "learned":

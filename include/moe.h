@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 enum moe_status {
   MOE_OK = 0,
@@ -242,15 +242,27 @@ int moe_combine(const void* o, const float* topk_gate, const int32_t* row_of_slo
 /* Combine backward: d_o[row_of_slot[t,j]] = topk_gate[t,j] * dy[t] (layer
  * dtype; fp32 for MXFP8 layers, the fp32 product) and dgate[t,j] (fp32) =
  * <dy[t], o[row_of_slot[t,j]]>, summed in fp32.
- * d_o_mx_out (MXFP8 layers only; NULL to skip): receives the MXFP8 image of
- * the stored fp32 d_o, moe_mx_image_size(S, d) bytes, 256-byte aligned.
+ * d_o_mx_out (MXFP8 layers only; NULL to skip): receives the MXFP8 operands
+ * of d_o for the FFN backward, moe_mx_dout_image_size(shape) bytes, 256-byte
+ * aligned: the image along d (moe_mx_image_size(S, d) bytes, the down-dgrad
+ * GEMM's operand) followed by the image along each expert's tokens (the W_down
+ * weight gradient's operand, each expert's rows padded to a multiple of 64).
+ * Both encode the fp32 products. With d_o_mx_out, token_of_row and offsets
+ * (moe_dispatch's outputs) are required, and d_o_out may be NULL: then no
+ * fp32 d_o is written (the FFN backward needs only the image).
+ * token_of_row, offsets: ignored (may be NULL) without d_o_mx_out.
  * Passage: the gate-weighted combine of the layer specification ("a
  * gate-weighted combine back to token order", forward and backward); the
  * MXFP8 image is the data moved to the experts in MXFP8 (unite.ai page,
  * "Parallelismo, precisione e tecniche di memoria"). */
 int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
-                    const int32_t* row_of_slot, const moe_shape* shape, void* d_o_out,
+                    const int32_t* row_of_slot, const int32_t* token_of_row,
+                    const int32_t* offsets, const moe_shape* shape, void* d_o_out,
                     uint8_t* d_o_mx_out, float* dgate_out, void* stream);
+
+/* Bytes of the d_o_mx buffer of an MXFP8 layer (moe_combine_bwd,
+ * moe_grouped_ffn_bwd); (size_t)-1 for an invalid shape or a non-MXFP8 one. */
+size_t moe_mx_dout_image_size(const moe_shape* shape);
 
 /* Grouped FFN backward, per expert e on its rows:
  *   dH = d_o · w_down[e]^T;  dU = dH * silu(G);
@@ -263,8 +275,9 @@ int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
  * bf16 layers it starts with the dG | dU rows ([S][2f], layer dtype).
  * MXFP8 layers quantise every operand along its GEMM's K (the weight
  * gradients along each expert's tokens, the range padded with zero rows).
- * d_o_mx (MXFP8 layers only; NULL = quantise d_o here): the MXFP8 image of
- * d_o that moe_combine_bwd wrote.
+ * d_o_mx (MXFP8 layers only; NULL = quantise d_o here): the MXFP8 operands
+ * of d_o that moe_combine_bwd wrote (moe_mx_dout_image_size bytes); with it
+ * d_o is not read and may be NULL.
  * Passage: the backward of the expert FFN (dgrad and wgrad grouped GEMMs) of
  * the layer specification; the grouped, device-scheduled GEMM of the
  * bytechap.com page, "Cómo funciona", and of the unite.ai page,

@@ -61,7 +61,8 @@ SIGNATURES = {
     "moe_read_device_status": (ctypes.c_int, [_P, _P]),
     "moe_grouped_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SHAPE, _P, _SZ, _P, _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _SHAPE, _P, _P]),
-    "moe_combine_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _P, _P]),
+    "moe_combine_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _P]),
+    "moe_mx_dout_image_size": (_SZ, [_SHAPE]),
     "moe_grouped_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_route_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _SZ, _P]),
     "moe_dispatch_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _SZ, _P]),
@@ -151,6 +152,14 @@ def mx_image_size(rows: int, cols: int) -> int:
     return n
 
 
+def mx_dout_image_size(shape: MoeShape) -> int:
+    """Bytes of an MXFP8 layer's d_o operand buffer (moe_mx_dout_image_size)."""
+    n = load().moe_mx_dout_image_size(ctypes.byref(shape))
+    if n == ctypes.c_size_t(-1).value:
+        raise MoeError("moe_mx_dout_image_size", MOE_ERR_INVALID_ARG, last_error())
+    return n
+
+
 def moe_route(x, w_router, shape, logits, topk_idx, topk_gate, ws=None, stream=None):
     T, E, k = shape.T, shape.E, shape.k
     _expect(logits, torch.float32, T * E, "logits")
@@ -198,11 +207,12 @@ def moe_combine(o, topk_gate, row_of_slot, shape, y, stream=None):
                                              _ptr(y), _stream(stream)))
 
 
-def moe_combine_bwd(dy, o, topk_gate, row_of_slot, shape, d_o, dgate, stream=None, d_o_mx=None):
+def moe_combine_bwd(dy, o, topk_gate, row_of_slot, shape, d_o, dgate, stream=None, d_o_mx=None,
+                    token_of_row=None, offsets=None):
     _expect(dgate, torch.float32, shape.T * shape.k, "dgate")
     _check("moe_combine_bwd", load().moe_combine_bwd(_ptr(dy), _ptr(o), _ptr(topk_gate), _ptr(row_of_slot),
-                                                     ctypes.byref(shape), _ptr(d_o), _ptr(d_o_mx), _ptr(dgate),
-                                                     _stream(stream)))
+                                                     _ptr(token_of_row), _ptr(offsets), ctypes.byref(shape),
+                                                     _ptr(d_o), _ptr(d_o_mx), _ptr(dgate), _stream(stream)))
 
 
 def moe_grouped_ffn_bwd(d_o, xp, w_gate, w_up, w_down, offsets, shape, save, dxp, dw_gate, dw_up, dw_down, ws,

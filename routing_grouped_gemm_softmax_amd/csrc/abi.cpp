@@ -315,19 +315,30 @@ int moe_combine(const void* o, const float* topk_gate, const int32_t* row_of_slo
 }
 
 int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate, const int32_t* row_of_slot,
-                    const moe_shape* s, void* d_o_out, uint8_t* d_o_mx_out, float* dgate_out, void* stream) {
+                    const int32_t* token_of_row, const int32_t* offsets, const moe_shape* s, void* d_o_out,
+                    uint8_t* d_o_mx_out, float* dgate_out, void* stream) {
   CHECK(check_shape(s));
-  NEED(dy); NEED(o); NEED(topk_gate); NEED(row_of_slot); NEED(d_o_out); NEED(dgate_out);
+  NEED(dy); NEED(o); NEED(topk_gate); NEED(row_of_slot); NEED(dgate_out);
   MX_IMAGE_OK(d_o_mx_out, s);
   if (d_o_mx_out) {
-    LAUNCH(moe::launch_combine_bwd_mx(dy, o, topk_gate, row_of_slot, (int)s->T, (int)s->d, (int)s->k, d_o_out,
-                                      moe::mx_image(d_o_mx_out, s->T * s->k, s->d), dgate_out, as_stream(stream)));
+    NEED(token_of_row); NEED(offsets);
+    if (d_o_out) NEED(d_o_out);
+    LAUNCH(moe::launch_combine_bwd_mx(dy, o, topk_gate, row_of_slot, token_of_row, offsets, (int)s->T, (int)s->d,
+                                      (int)s->E, (int)s->k, d_o_out,
+                                      moe::mx_dout_image(d_o_mx_out, s->T * s->k, s->d, s->E), dgate_out,
+                                      as_stream(stream)));
     return MOE_OK;
   }
+  NEED(d_o_out);
   const int kind = s->dtype == MOE_F32 ? 0 : (s->dtype == MOE_BF16 ? 1 : 2);
   LAUNCH(moe::launch_combine_bwd(dy, o, topk_gate, row_of_slot, kind, (int)s->T, (int)s->d, (int)s->k,
                                  d_o_out, dgate_out, as_stream(stream)));
   return MOE_OK;
+}
+
+size_t moe_mx_dout_image_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK || s->dtype != MOE_MXFP8) return (size_t)-1;
+  return moe::mx_dout_image_bytes(s->T * s->k, s->d, s->E);
 }
 
 int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, const void* w_gate,
@@ -336,7 +347,8 @@ int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, 
                         void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_shape(s));
   CHECK(check_ffn_dtype(s, "moe_grouped_ffn_bwd"));
-  NEED(d_o); NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(dxp_out);
+  if (!d_o_mx || d_o) NEED(d_o);  // with the MXFP8 operands of d_o, d_o itself is not read
+  NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(dxp_out);
   NEED(dw_gate_out); NEED(dw_up_out); NEED(dw_down_out); NEED(ws);
   if (save_bytes_for(s) > 0) NEED(save);
   MX_IMAGE_OK(d_o_mx, s);

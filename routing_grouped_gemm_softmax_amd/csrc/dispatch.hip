@@ -395,7 +395,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
 // fixed reduction tree: per-thread partials, lane butterfly, then waves in order).
 // DO is the type of d_o: T, or float for MXFP8 layers (bf16 T), whose d_o
 // keeps the fp32 products. MX (DO = float only): the same pass writes d_o's
-// MXFP8 image (q, sc; S rows), each code decided on the fp32 value stored.
+// K-major MXFP8 image (q, sc; S rows), each code decided on the fp32 product,
+// and the fp32 d_o rows only if d_o is not null.
 template <typename T, typename DO, bool MX, int K>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ o,
                                                           const float* __restrict__ gate,
@@ -438,16 +439,18 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
           sv[i] = g[j] * dv[i];
         }
         if (rows[j] < 0) continue;  // the same for every lane of the token
-        DO* dst = d_o + rows[j] * re + v * VE;
         if constexpr (sizeof(DO) == sizeof(T)) {
-          st16(dst, pack16(sv));
+          st16(d_o + rows[j] * re + v * VE, pack16(sv));
         } else {  // bf16 dy, fp32 d_o: the 8 products as two 16-byte pieces
-          const float lo[4] = {sv[0], sv[1], sv[2], sv[3]}, hi[4] = {sv[4], sv[5], sv[6], sv[7]};
-          st16(dst, pack16(lo));
-          st16(dst + 4, pack16(hi));
+          if (!MX || d_o != nullptr) {
+            DO* dst = d_o + rows[j] * re + v * VE;
+            const float lo[4] = {sv[0], sv[1], sv[2], sv[3]}, hi[4] = {sv[4], sv[5], sv[6], sv[7]};
+            st16(dst, pack16(lo));
+            st16(dst + 4, pack16(hi));
+          }
           if constexpr (MX) {
             const int one[1] = {rows[j]};
-            mx_store_vals<1, true>(sv, v, nvec * VE, one, 1, q, sc, S);
+            mx_store_vals<1, false>(sv, v, nvec * VE, one, 1, q, sc, S);
           }
         }
       }
@@ -520,16 +523,142 @@ hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate, 
   });
 }
 
-hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gate, const int32_t* row_of_slot, int T,
-                                 int d, int k, void* d_o, MxImage d_o_mx, float* dgate, hipStream_t s) {
+// The token-major MXFP8 image of an MXFP8 layer's dO: row r of expert e is
+// dO[r] = gate(t, j) * dy[t] for its slot (t = token_of_row[r], j the slot
+// with row_of_slot[t][j] = r), the same fp32 product combine_bwd_kernel
+// encodes, blocked in 32 rows down each column inside e's rows padded to 64:
+// codes q [C][P] at columns poff[e].., scales s [P/64][C][2]. dO is rebuilt
+// from dy instead of being stored in fp32 and read back.
+// One workgroup per (128 padded rows, 64 columns). Wave 0 first finds the
+// expert of each 64-row half (the padded offsets by a wave scan over the
+// experts, 4 per lane); each thread then loads 16 bytes of a gathered dy row
+// (all loads before any use), scales them by the row's gate into an fp32 LDS
+// tile, and each thread encodes one 32-row block of one column into an LDS
+// output tile that leaves as full 128-byte rows of q.
+template <int K>
+__global__ __launch_bounds__(256) void dout_tmajor_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ gate,
+                                                          const int32_t* __restrict__ row_of_slot,
+                                                          const int32_t* __restrict__ token_of_row,
+                                                          const int32_t* __restrict__ offsets, int E, int C,
+                                                          int64_t P, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  __shared__ __attribute__((aligned(16))) float tile[128][64 + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t qt[64][128 + 16];
+  __shared__ int s_src[2], s_valid[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const int c0 = blockIdx.y * 64;
+  if (tid < 64) {
+    int beg[4], n[4], pad[4], sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = lane * 4 + u;
+      beg[u] = e < E ? offsets[e] : 0;
+      n[u] = e < E ? offsets[e + 1] - beg[u] : 0;
+      pad[u] = (n[u] + 63) & ~63;
+      sum += pad[u];
+    }
+    const int excl = wave_exclusive_scan(sum);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t ph = p0 + 64 * h;
+      int src = 0, valid = 0, found = 0, run = excl;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (ph >= run && ph < run + pad[u]) {
+          found = 1;
+          src = beg[u] + static_cast<int>(ph - run);
+          valid = min(64, n[u] - static_cast<int>(ph - run));
+        }
+        run += pad[u];
+      }
+      const uint64_t who = __ballot(found);
+      if (who) {
+        const int l0 = __ffsll(static_cast<long long>(who)) - 1;
+        src = __shfl(src, l0, kWave);
+        valid = __shfl(valid, l0, kWave);
+      } else {
+        src = 0;
+        valid = 0;
+      }
+      if (lane == 0) {
+        s_src[h] = src;
+        s_valid[h] = valid;
+      }
+    }
+  }
+  __syncthreads();
+  // 128 rows x 64 columns of dy: 8 lanes per row, 32 rows per pass.
+  const int ch = tid & 7;
+  uint4 raw[4];
+  float g[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
+    const bool ok = rr < s_valid[h];
+    const int rs = ok ? s_src[h] + rr : 0;
+    const int t = ok ? token_of_row[rs] : 0;
+    float gg = 0.0f;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (ok && row_of_slot[static_cast<int64_t>(t) * K + j] == rs) gg = gate[static_cast<int64_t>(t) * K + j];
+    g[i] = gg;
+    raw[i] = ld16(dy + static_cast<int64_t>(t) * C + c0 + ch * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
+    const bool ok = rr < s_valid[h];
+    float f[8];
+    unpack16(raw[i], f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) f[u] = ok ? g[i] * f[u] : 0.0f;
+    *reinterpret_cast<float4*>(&tile[r][ch * 8]) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(&tile[r][ch * 8 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  __syncthreads();
+  {
+    const int col = tid & 63, block = tid >> 6;
+    float v[32];
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = tile[block * 32 + i][col];
+    const int code = mx_encode_block(v, w);
+    uint4* d = reinterpret_cast<uint4*>(&qt[col][block * 32]);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    if (p0 + block * 32 < P) {
+      const int64_t sb = (p0 >> 6) + (block >> 1);
+      s[(sb * C + c0 + col) * 2 + (block & 1)] = static_cast<uint8_t>(code);
+    }
+  }
+  __syncthreads();
+  const int64_t pvalid = min(static_cast<int64_t>(128), P - p0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = i * 32 + (tid >> 3), c16 = tid & 7;
+    if (c16 * 16 < pvalid)
+      *reinterpret_cast<uint4*>(q + static_cast<int64_t>(c0 + row) * P + p0 + c16 * 16) =
+          *reinterpret_cast<const uint4*>(&qt[row][c16 * 16]);
+  }
+}
+
+hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gate, const int32_t* row_of_slot,
+                                 const int32_t* token_of_row, const int32_t* offsets, int T, int d, int E, int k,
+                                 void* d_o, MxDoutImage d_o_mx, float* dgate, hipStream_t s) {
   const int nvec = d * 2 / 16;
   const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
+  const int64_t S = static_cast<int64_t>(T) * k, P = mx_padded_rows(S, E);
   return with_k(k, [&](auto KC) {
     constexpr int K = decltype(KC)::value;
     hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float, true, K>), grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec, lpt,
-                       static_cast<float*>(d_o), dgate, d_o_mx.q, d_o_mx.s, T * k);
+                       static_cast<float*>(d_o), dgate, d_o_mx.k.q, d_o_mx.k.s, T * k);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((dout_tmajor_kernel<K>), dim3(static_cast<unsigned>(P / 128 + (P % 128 ? 1 : 0)), d / 64),
+                       dim3(256), 0, s, static_cast<const bf16_t*>(dy), gate, row_of_slot, token_of_row, offsets, E,
+                       d, P, d_o_mx.t.q, d_o_mx.t.s);
     return hipGetLastError();
   });
 }

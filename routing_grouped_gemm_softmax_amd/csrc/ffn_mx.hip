@@ -198,7 +198,7 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
      // was quantised by the forward.
     uint8_t *doq = w.doq, *dos = w.dos;
     if (a.d_o_mx != nullptr) {  // written by the combine backward pass
-      const MxImage im = mx_image(a.d_o_mx, S, d);
+      const MxImage im = mx_dout_image(a.d_o_mx, S, d, E).k;
       doq = im.q;
       dos = im.s;
     } else {
@@ -227,12 +227,20 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
   }
   // Weight gradients: every operand along the expert's tokens, transposed.
   {  // dW_down[e] = q(H_e)^T q(dO_e); q(H) along the tokens came from the
-     // forward's gate/up epilogue.
-    TRY(launch_mx_tgroup_f32(a.d_o, S, d, w.blk, w.dot, P, w.dots, s));
+     // forward's gate/up epilogue, q(dO) along the tokens from the combine
+     // backward (else from d_o here).
+    uint8_t *dot = w.dot, *dots = w.dots;
+    if (a.d_o_mx != nullptr) {
+      const MxImage im = mx_dout_image(a.d_o_mx, S, d, E).t;
+      dot = im.q;
+      dots = im.s;
+    } else {
+      TRY(launch_mx_tgroup_f32(a.d_o, S, d, w.blk, w.dot, P, w.dots, s));
+    }
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
     p.a = sv.ht; p.lda = P; p.as = sv.hts; p.as_slab = 2LL * f;
-    p.b0 = w.dot; p.ldb = P; p.bs0 = w.dots; p.bs_slab = 2LL * d;
+    p.b0 = dot; p.ldb = P; p.bs0 = dots; p.bs_slab = 2LL * d;
     p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = static_cast<int64_t>(f) * d; p.M = f; p.N = d; p.f = d;
     TRY(launch_mx_wgrad(p, s));
   }

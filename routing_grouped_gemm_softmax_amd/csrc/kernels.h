@@ -107,9 +107,31 @@ inline MxImage mx_image(const void* base, int64_t rows, int64_t cols) {
 hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
                               int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                               int32_t* token_of_row, void* xp, MxImage xp_mx, void* ws, hipStream_t s);
+// The MXFP8 image of an MXFP8 layer's dO: the K-major image (mx_image layout,
+// the down-dgrad GEMM's operand) followed by the token-major one (codes [d][P],
+// scales [P/64][d][2], every expert's rows padded to a multiple of 64 starting
+// at its padded offset: the W_down weight gradient's operand).
+inline int64_t mx_padded_rows(int64_t S, int64_t E) { return (S + 63 * E + 63) / 64 * 64; }
+inline size_t mx_dout_image_bytes(int64_t S, int64_t d, int64_t E) {
+  const size_t pd = static_cast<size_t>(mx_padded_rows(S, E)) * static_cast<size_t>(d);
+  return mx_image_bytes(S, d) + mx_part_bytes(pd) + mx_part_bytes(pd / 32);
+}
+struct MxDoutImage {
+  MxImage k;  // [S][d] along d
+  MxImage t;  // [d][P] along each expert's tokens
+};
+inline MxDoutImage mx_dout_image(const void* base, int64_t S, int64_t d, int64_t E) {
+  uint8_t* p = static_cast<uint8_t*>(const_cast<void*>(base));
+  const size_t pd = static_cast<size_t>(mx_padded_rows(S, E)) * static_cast<size_t>(d);
+  uint8_t* t = p + mx_image_bytes(S, d);
+  return MxDoutImage{mx_image(base, S, d), MxImage{t, t + mx_part_bytes(pd)}};
+}
+// d_o (fp32) may be null: then only the images are written. dO = gate * dy
+// in fp32 is decided once per element and both images encode that value.
 hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gate,
-                                 const int32_t* row_of_slot, int T, int d, int k, void* d_o,
-                                 MxImage d_o_mx, float* dgate, hipStream_t s);
+                                 const int32_t* row_of_slot, const int32_t* token_of_row,
+                                 const int32_t* offsets, int T, int d, int E, int k, void* d_o,
+                                 MxDoutImage d_o_mx, float* dgate, hipStream_t s);
 
 // Dispatch whose workspace is the library's own device array (one per GPU,
 // dispatch_noalloc_max() bytes) instead of a caller buffer: no allocation.

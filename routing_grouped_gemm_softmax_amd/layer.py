@@ -25,7 +25,7 @@ class MoELayer:
         self.shape = L.MoeShape.make(T, d, E, k, f, dtype, L.MOE_FLAG_RECOMPUTE if recompute else 0)
         self.recompute = recompute
         self.dtype = L.TORCH_DTYPE[self.shape.dtype]
-        # G, U, H and d_o: fp32 for MXFP8 layers (their E4M3 codes are
+        # G, U and d_o: fp32 for MXFP8 layers (their E4M3 codes are
         # decided on the fp32 values), else the layer dtype.
         self.act_dtype = torch.float32 if self.shape.dtype == L.MOE_MXFP8 else self.dtype
         self.learned = learned_routing
@@ -52,14 +52,17 @@ class MoELayer:
         self.xp = buf(S, d)
         use_mx = mx_images and self.shape.dtype == L.MOE_MXFP8
         self.xp_mx = torch.empty(L.mx_image_size(S, d), dtype=torch.uint8, device=dev) if use_mx else None
-        self.d_o_mx = torch.empty(L.mx_image_size(S, d), dtype=torch.uint8, device=dev) if use_mx else None
+        self.d_o_mx = torch.empty(L.mx_dout_image_size(self.shape), dtype=torch.uint8, device=dev) if use_mx else None
         self.save = torch.empty(L.save_size(self.shape), dtype=torch.uint8, device=dev)
         self.ws_ffn_fwd = ws(L.MOE_OP_FFN_FWD)
         self.o = buf(S, d)
         self.y = buf(T, d)
         self.ws_dispatch = ws(L.MOE_OP_DISPATCH)
         # backward
-        self.d_o = buf(S, d, dtype=self.act_dtype)
+        # An MXFP8 layer with the operand images keeps no fp32 d_o: the combine
+        # backward writes both of its E4M3 layouts and the FFN backward reads
+        # only those.
+        self.d_o = None if use_mx else buf(S, d, dtype=self.act_dtype)
         self.dgate = buf(T, k, dtype=f32)
         self.dxp = buf(S, d)
         self.dw_gate = buf(E, d, f)
@@ -136,7 +139,7 @@ class MoELayer:
         s = self.shape
         mark = mark or (lambda name: None)
         L.moe_combine_bwd(dy, self.o, self.topk_gate, self.row_of_slot, s, self.d_o, self.dgate, stream,
-                          d_o_mx=self.d_o_mx)
+                          d_o_mx=self.d_o_mx, token_of_row=self.token_of_row, offsets=self.offsets)
         mark("moe_combine_bwd")
         L.moe_grouped_ffn_bwd(self.d_o, self.xp, self.w_gate, self.w_up, self.w_down, self.offsets, s, self.save,
                               self.dxp, self.dw_gate, self.dw_up, self.dw_down, self.ws_ffn_bwd, stream,

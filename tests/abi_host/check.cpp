@@ -162,15 +162,29 @@ int main() {
   // combine and its backward; the MXFP8 backward writes fp32 d_o (kind 2).
   RC(moe_combine(buf(0), fbuf(256), ibuf(512), &ok, buf(1024), s), MOE_OK);
   RC(moe_combine(buf(0), fbuf(256), nullptr, &ok, buf(1024), s), MOE_ERR_INVALID_ARG);
-  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), &ok, buf(1024), nullptr, fbuf(2048), s), MOE_OK);
+  // token_of_row and offsets are read only with the MXFP8 operands of d_o,
+  // and then d_o itself may be NULL.
+  uint8_t* img = reinterpret_cast<uint8_t*>(buf(4096));
+  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), nullptr, nullptr, &ok, buf(1024), nullptr, fbuf(2048),
+                     s), MOE_OK);
   EXPECT(stub::last_kind == 1);
-  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), &mx, buf(1024), nullptr, fbuf(2048), s), MOE_OK);
+  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), nullptr, nullptr, &ok, nullptr, nullptr, fbuf(2048), s),
+     MOE_ERR_INVALID_ARG);
+  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), nullptr, nullptr, &mx, buf(1024), nullptr, fbuf(2048),
+                     s), MOE_OK);
   EXPECT(stub::last_kind == 2);
-  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), &mx, buf(1024), reinterpret_cast<uint8_t*>(buf(4096)),
+  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), ibuf(8192), ibuf(12288), &mx, buf(1024), img,
                      fbuf(2048), s), MOE_OK);
-  EXPECT(stub::last_kind == 3);
-  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), &ok, buf(1024), reinterpret_cast<uint8_t*>(buf(4096)),
+  EXPECT(stub::last_kind == 3 && stub::last_E == 8);
+  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), ibuf(8192), ibuf(12288), &mx, nullptr, img,
+                     fbuf(2048), s), MOE_OK);
+  EXPECT(stub::last_kind == 4);
+  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), nullptr, ibuf(12288), &mx, nullptr, img, fbuf(2048), s),
+     MOE_ERR_INVALID_ARG);
+  RC(moe_combine_bwd(buf(0), buf(256), fbuf(512), ibuf(768), ibuf(8192), ibuf(12288), &ok, buf(1024), img,
                      fbuf(2048), s), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_mx_dout_image_size(&mx) != BAD && moe_mx_dout_image_size(&mx) > moe_mx_image_size(mx.T * mx.k, mx.d));
+  EXPECT(moe_mx_dout_image_size(&ok) == BAD);
 
   // router backward and dispatch backward
   RC(moe_route_bwd(buf(0), buf(256), ibuf(512), fbuf(768), fbuf(1024), &ok, fbuf(2048), buf(4096), buf(8192), big,

@@ -74,10 +74,11 @@ hipError_t launch_dispatch_mx(const void*, const int32_t*, int T, int d, int E, 
 size_t dispatch_noalloc_max() { return size_t(1) << 20; }
 hipError_t launch_dispatch_noalloc(const void*, const int32_t*, int, int T, int d, int E, int k, int32_t*, int32_t*,
                                    int32_t*, int32_t*, void*, MxImage, hipStream_t) { return hit(T, d, E, k); }
-hipError_t launch_combine_bwd_mx(const void*, const void*, const float*, const int32_t*, int T, int d, int k, void*,
-                                 MxImage, float*, hipStream_t) {
-  stub::last_kind = 3;
-  return hit(T, d, 0, k);
+hipError_t launch_combine_bwd_mx(const void*, const void*, const float*, const int32_t*, const int32_t*,
+                                 const int32_t*, int T, int d, int E, int k, void* d_o, MxDoutImage, float*,
+                                 hipStream_t) {
+  stub::last_kind = d_o ? 3 : 4;
+  return hit(T, d, E, k);
 }
 hipError_t launch_mxfp8_quantize(const void*, int64_t rows, int64_t cols, int, uint8_t*, uint8_t*, hipStream_t) {
   return hit(static_cast<int>(rows), static_cast<int>(cols));

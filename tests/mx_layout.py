@@ -54,6 +54,30 @@ def save_pieces(S, d, f, E):
     return out
 
 
+def dout_pieces(S, d, E):
+    """The d_o operand buffer of an MXFP8 layer (moe_combine_bwd's d_o_mx):
+    the K-major image (codes [S][d], scales [d/64][S][2]) then the
+    token-major one: dot (codes [d][P]), dots (scales [P/64][d][2])."""
+    P = padded_rows(S, E)
+    off, _ = _carve([S * d, S * d // 32, P * d, P * d // 32])
+    return {"doq": (off[0], S * d), "dos": (off[1], S * d // 32), "dot": (off[2], P * d), "dots": (off[3], P * d // 32)}
+
+
+def dout_f32(gate, dy, row_of_slot, token_of_row):
+    """The fp32 dO rows an MXFP8 layer encodes, in expert-sorted row order:
+    gate(t, j) * dy[t] for the slot (t, j) of each row, one fp32 rounding of
+    the product of the fp32 gate and the bf16 dy (as fp64 values)."""
+    row_of_slot = np.asarray(row_of_slot)
+    k = row_of_slot.shape[1]
+    flat = row_of_slot.reshape(-1)
+    ok = flat >= 0
+    slot = np.zeros(len(token_of_row), np.int64)
+    slot[flat[ok]] = np.nonzero(ok)[0]
+    t, j = np.divmod(slot, k)
+    g = np.asarray(gate, np.float32)[t, j]
+    return (g[:, None] * np.asarray(dy, np.float32)[t]).astype(np.float64)
+
+
 def padded_offsets(offsets):
     n = np.diff(np.asarray(offsets))
     return np.concatenate([[0], np.cumsum((n + 63) // 64 * 64)])

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
     for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
                        (-3, b"MOE_ERR_MISALIGNED"), (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == name
@@ -141,10 +141,14 @@ def test_mx_image_arguments_are_checked_on_the_host():
     assert rc == L.MOE_ERR_INVALID_ARG and "MXFP8" in L.last_error()
     rc = lib.moe_dispatch(p, p, ctypes.byref(mx), p, p, p, p, p, ctypes.c_void_p(0x100080), p, ws, None)
     assert rc == L.MOE_ERR_MISALIGNED
-    rc = lib.moe_combine_bwd(p, p, p, p, ctypes.byref(bf), p, p, p, None)
+    rc = lib.moe_combine_bwd(p, p, p, p, None, None, ctypes.byref(bf), p, p, p, None)
     assert rc == L.MOE_ERR_INVALID_ARG
-    rc = lib.moe_combine_bwd(p, p, p, p, ctypes.byref(mx), p, ctypes.c_void_p(0x100010), p, None)
+    rc = lib.moe_combine_bwd(p, p, p, p, p, p, ctypes.byref(mx), p, ctypes.c_void_p(0x100010), p, None)
     assert rc == L.MOE_ERR_MISALIGNED
+    # The MXFP8 operands of d_o need the permutation and the offsets.
+    rc = lib.moe_combine_bwd(p, p, p, p, None, p, ctypes.byref(mx), None, p, p, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "token_of_row" in L.last_error()
+    assert L.mx_dout_image_size(mx) > L.mx_image_size(mx.T * mx.k, mx.d)
     rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, p, ctypes.byref(bf), p, 1 << 40, p, p, 1 << 40, None)
     assert rc == L.MOE_ERR_INVALID_ARG
     rc = lib.moe_grouped_ffn_bwd(p, ctypes.c_void_p(0x100040), p, p, p, p, p, ctypes.byref(mx), p, p, p, p, p, p,

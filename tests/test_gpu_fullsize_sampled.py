@@ -87,14 +87,19 @@ def _expert_device(F, e):
     L = F.layer
     a, b = int(F.offsets[e]), int(F.offsets[e + 1])
     rows = np.arange(a, b)
-    dv = dict(O=_rows(L.o, rows), dO=_rows(L.d_o, rows), dXp=_rows(L.dxp, rows),
+    dv = dict(O=_rows(L.o, rows), dXp=_rows(L.dxp, rows),
               dW_gate=host(L.dw_gate[e]), dW_up=host(L.dw_up[e]), dW_down=host(L.dw_down[e]))
     if F.mx:
-        # MXFP8: fp32 G, U blocked in the save buffer; H and dG | dU exist
-        # only as E4M3 operands (checked as images).
+        # MXFP8: fp32 G, U blocked in the save buffer; H, dG | dU and dO
+        # exist only as E4M3 operands (checked as images); dO's values are
+        # the fp32 products of the gates and dy that the device encodes.
         wl = F.wl
+        t, j = np.divmod(F.slot_of_row[rows], wl.k)
+        dv["dO"] = (F.inp["topk_gate"][t, j].astype(np.float32)[:, None]
+                    * F.inp["dy"][t].astype(np.float32)).astype(np.float64)
         dv["G"], dv["U"] = (ML.blocked_rows(L.save, n, rows, F.offsets, wl.T * wl.k, wl.f, wl.E) for n in "GU")
     else:
+        dv["dO"] = _rows(L.d_o, rows)
         dv["G"], dv["U"], dv["H"] = (_rows(t, rows) for t in L.saved())
         dv["dG"], dv["dU"] = (_rows(t, rows) for t in L.dgu())
     return rows, dv
@@ -179,8 +184,9 @@ def _check_expert_images(F, e, rows, dv, xp, dgdu):
                          atol=np.full(f, atol_h))
     ML.check_kmajor(L.ws_ffn_bwd, pb, "dguq", "dgus", dgu, f"q(dG|dU) expert {e}", S=S, row0=a, near=True,
                     atol=atol)
-    for q, s_, vals, near in (("dot", "dots", dv["dO"], False), ("xt", "xts", xp, False),
-                              ("dgut", "dguts", dgu, True)):
+    ML.check_token_major(L.d_o_mx, ML.dout_pieces(S, d, E), "dot", "dots", dv["dO"], F.offsets, "q(dot)",
+                         experts=[e], S=S, C=d)
+    for q, s_, vals, near in (("xt", "xts", xp, False), ("dgut", "dguts", dgu, True)):
         ML.check_token_major(L.ws_ffn_bwd, pb, q, s_, vals, F.offsets, f"q({q})", experts=[e], S=S,
                              C=vals.shape[1], near=near, atol=atol if near else None)
 

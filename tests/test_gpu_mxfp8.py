@@ -103,7 +103,8 @@ def _check_images(layer, off, xp, H, d_o, dg, du):
             np.testing.assert_array_equal(q, rq, err_msg=f"{name} image codes")
             np.testing.assert_array_equal(sc, rs, err_msg=f"{name} image scales")
     # Token-major weight-gradient operands.
-    for q, s_, vals, near in (("dot", "dots", d_o, False), ("xt", "xts", xp, False), ("dgut", "dguts", dgu, True)):
+    ML.check_token_major(layer.d_o_mx, ML.dout_pieces(S, d, E), "dot", "dots", d_o, off, "q(dot)")
+    for q, s_, vals, near in (("xt", "xts", xp, False), ("dgut", "dguts", dgu, True)):
         ML.check_token_major(layer.ws_ffn_bwd, pb, q, s_, vals, off, f"q({q})", near=near,
                              atol=atol if near else None)
 
@@ -125,14 +126,15 @@ def test_mxfp8_layer_matches_mx_oracle(case):
 
     off = ref["offsets"]
     S, f = wl.T * wl.k, wl.f
-    assert layer.d_o.dtype == torch.float32
+    assert layer.d_o is None  # the combine backward writes only dO's E4M3 operands
     # G, U: fp32, blocked in the save buffer. H and dG | dU exist on the
     # device only as E4M3 operands.
     G, U = (ML.blocked_rows(layer.save, n, np.arange(S), off, S, f, wl.E) for n in ("G", "U"))
     H = G * O.sigmoid(G) * U
     xp = ref["xp"]
     w = (inp["w_gate"], inp["w_up"], inp["w_down"])
-    d_o = host(layer.d_o).astype(np.float64)
+    # dO: the fp32 product gate * dy that the device encodes (byte-exact images).
+    d_o = ML.dout_f32(inp["topk_gate"], inp["dy"], host(layer.row_of_slot), host(layer.token_of_row))
     # Stage by stage: each GEMM on the device's own operands (its stored G,
     # U, dO and its H and dG | dU images, dequantised); the oracle's dG, dU
     # from the device's G, U, dO are what the dG | dU images are checked
@@ -228,10 +230,12 @@ def _image(buf, rows, cols):
 @pytest.mark.parametrize("over", [dict(T=384, d=384, E=16, f=128), dict(T=200, d=4224, E=8, f=128)],
                          ids=["ragged_empty_d384", "three_row_passes_d4224"])
 def test_dispatch_and_combine_bwd_mx_images(over):
-    """The MXFP8 images that moe_dispatch and moe_combine_bwd write beside xp
-    (bf16) and d_o (fp32) carry the oracle's codes and scales of the stored
-    rows bit for bit, and a layer that reads them gives bit-identical outputs
-    to one that quantises xp and d_o inside the grouped FFN calls."""
+    """The MXFP8 images that moe_dispatch and moe_combine_bwd write (xp along
+    d; dO along d and along each expert's tokens, from the fp32 products
+    without storing them) carry the oracle's codes and scales of the values
+    bit for bit, and a layer that reads them gives bit-identical outputs to
+    one that stores fp32 dO and quantises xp and dO inside the grouped FFN
+    calls."""
     from routing_grouped_gemm_softmax_amd import MoELayer
     wl = WORKLOADS["bf16_zipf"].with_shape(dtype="mxfp8", **over)
     pop = [1, 0, 2, 1, 1, 0, 3, 1, 1, 1, 0, 1, 2, 1, 1, 0][:wl.E]
@@ -248,14 +252,20 @@ def test_dispatch_and_combine_bwd_mx_images(over):
         layers[fused] = layer
     torch.cuda.synchronize()
     a, b = layers[True], layers[False]
-    assert a.xp_mx is not None and b.xp_mx is None
+    assert a.xp_mx is not None and b.xp_mx is None and a.d_o is None
     S, d = wl.T * wl.k, wl.d
-    for name, img, rows in (("xp", a.xp_mx, a.xp), ("d_o", a.d_o_mx, a.d_o)):
+    # The fp32 dO the second layer stored is the product the first encoded,
+    # and the host's fp32 product of the gate and dy reproduces it exactly.
+    d_o = host(b.d_o).astype(np.float64)
+    np.testing.assert_array_equal(d_o, ML.dout_f32(inp["topk_gate"], inp["dy"], host(a.row_of_slot),
+                                                   host(a.token_of_row)))
+    for name, img, vals in (("xp", a.xp_mx, host(a.xp).astype(np.float64)), ("d_o", a.d_o_mx, d_o)):
         q, s = _image(img, S, d)
-        rq, rs = O.mx_quantize(host(rows).astype(np.float64), "cols")
+        rq, rs = O.mx_quantize(vals, "cols")
         np.testing.assert_array_equal(q, rq, err_msg=f"{name} codes")
         np.testing.assert_array_equal(s, rs, err_msg=f"{name} scales")
-    for n in ("xp", "o", "y", "d_o", "dgate", "dxp", "dw_gate", "dw_up", "dw_down", "dx"):
+    ML.check_token_major(a.d_o_mx, ML.dout_pieces(S, d, wl.E), "dot", "dots", d_o, host(a.offsets), "q(dot)")
+    for n in ("xp", "o", "y", "dgate", "dxp", "dw_gate", "dw_up", "dw_down", "dx"):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
 
 
