@@ -396,13 +396,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o, c
 // DO is the type of d_o: T, or float for MXFP8 layers (bf16 T), whose d_o
 // keeps the fp32 products. MX (DO = float only): the same pass writes d_o's
 // K-major MXFP8 image (q, sc; S rows), each code decided on the fp32 product,
-// and the fp32 d_o rows only if d_o is not null.
+// the gate of every row (gate_of_row, for the token-major pass), and the fp32
+// d_o rows only if d_o is not null.
 template <typename T, typename DO, bool MX, int K>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ o,
                                                           const float* __restrict__ gate,
                                                           const int32_t* __restrict__ row_of_slot, int Tn, int nvec,
                                                           int lpt, DO* __restrict__ d_o, float* __restrict__ dgate,
-                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S,
+                                                          float* __restrict__ gate_of_row) {
   constexpr int VE = Vec16<T>::N;
   static_assert(!MX || (sizeof(DO) == 4 && VE == 8), "MXFP8 images come from fp32 d_o of bf16 layers");
   __shared__ float red[4][K];
@@ -418,6 +420,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
     rows[j] = live ? row_of_slot[static_cast<int64_t>(t) * K + j] : -1;
     g[j] = live ? gate[static_cast<int64_t>(t) * K + j] : 0.0f;
     part[j] = 0.0f;
+  }
+  if constexpr (MX) {
+    if (live && sub == 0)
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        if (rows[j] >= 0) gate_of_row[rows[j]] = g[j];
   }
   if (live) {
     for (int v = sub; v < nvec; v += lpt) {
@@ -510,40 +518,41 @@ hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate, 
     if (kind == 0)
       hipLaunchKernelGGL((combine_bwd_kernel<float, float, false, K>), grid, dim3(256), 0, s,
                          static_cast<const float*>(dy), static_cast<const float*>(o), gate, row_of_slot, T, nvec, lpt,
-                         static_cast<float*>(d_o), dgate, nullptr, nullptr, T * k);
+                         static_cast<float*>(d_o), dgate, nullptr, nullptr, T * k, nullptr);
     else if (kind == 1)
       hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, bf16_t, false, K>), grid, dim3(256), 0, s,
                          static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec,
-                         lpt, static_cast<bf16_t*>(d_o), dgate, nullptr, nullptr, T * k);
+                         lpt, static_cast<bf16_t*>(d_o), dgate, nullptr, nullptr, T * k, nullptr);
     else
       hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float, false, K>), grid, dim3(256), 0, s,
                          static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec,
-                         lpt, static_cast<float*>(d_o), dgate, nullptr, nullptr, T * k);
+                         lpt, static_cast<float*>(d_o), dgate, nullptr, nullptr, T * k, nullptr);
     return hipGetLastError();
   });
 }
 
 // The token-major MXFP8 image of an MXFP8 layer's dO: row r of expert e is
-// dO[r] = gate(t, j) * dy[t] for its slot (t = token_of_row[r], j the slot
-// with row_of_slot[t][j] = r), the same fp32 product combine_bwd_kernel
-// encodes, blocked in 32 rows down each column inside e's rows padded to 64:
-// codes q [C][P] at columns poff[e].., scales s [P/64][C][2]. dO is rebuilt
-// from dy instead of being stored in fp32 and read back.
+// dO[r] = gate_of_row[r] * dy[token_of_row[r]], the same fp32 product
+// combine_bwd_kernel encodes (which also wrote gate_of_row), blocked in 32
+// rows down each column inside e's rows padded to 64: codes q [C][P] at
+// columns poff[e].., scales s [P/64][C][2]. dO is rebuilt from dy instead of
+// being stored in fp32 and read back.
 // One workgroup per (128 padded rows, 64 columns). Wave 0 first finds the
 // expert of each 64-row half (the padded offsets by a wave scan over the
-// experts, 4 per lane); each thread then loads 16 bytes of a gathered dy row
+// experts, 4 per lane), then each of 128 threads resolves one row's token
+// and gate into LDS; each thread then loads 16 bytes of a gathered dy row
 // (all loads before any use), scales them by the row's gate into an fp32 LDS
 // tile, and each thread encodes one 32-row block of one column into an LDS
 // output tile that leaves as full 128-byte rows of q.
-template <int K>
-__global__ __launch_bounds__(256) void dout_tmajor_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ gate,
-                                                          const int32_t* __restrict__ row_of_slot,
+__global__ __launch_bounds__(256) void dout_tmajor_kernel(const bf16_t* __restrict__ dy,
+                                                          const float* __restrict__ gate_of_row,
                                                           const int32_t* __restrict__ token_of_row,
                                                           const int32_t* __restrict__ offsets, int E, int C,
                                                           int64_t P, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) float tile[128][64 + 4];
   __shared__ __attribute__((aligned(16))) uint8_t qt[64][128 + 16];
-  __shared__ int s_src[2], s_valid[2];
+  __shared__ int s_src[2], s_valid[2], s_tok[128];
+  __shared__ float s_gate[128];
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * 128;
   const int c0 = blockIdx.y * 64;
@@ -587,31 +596,31 @@ __global__ __launch_bounds__(256) void dout_tmajor_kernel(const bf16_t* __restri
     }
   }
   __syncthreads();
+  if (tid < 128) {  // row tid: its token and gate (rows past an expert's end: gate 0)
+    const int h = tid >> 6, rr = tid & 63;
+    const bool ok = rr < s_valid[h];
+    const int rs = ok ? s_src[h] + rr : 0;
+    s_tok[tid] = ok ? token_of_row[rs] : 0;
+    s_gate[tid] = ok ? gate_of_row[rs] : 0.0f;
+  }
+  __syncthreads();
   // 128 rows x 64 columns of dy: 8 lanes per row, 32 rows per pass.
   const int ch = tid & 7;
   uint4 raw[4];
-  float g[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
-    const bool ok = rr < s_valid[h];
-    const int rs = ok ? s_src[h] + rr : 0;
-    const int t = ok ? token_of_row[rs] : 0;
-    float gg = 0.0f;
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-      if (ok && row_of_slot[static_cast<int64_t>(t) * K + j] == rs) gg = gate[static_cast<int64_t>(t) * K + j];
-    g[i] = gg;
-    raw[i] = ld16(dy + static_cast<int64_t>(t) * C + c0 + ch * 8);
+    const int r = i * 32 + (tid >> 3);
+    raw[i] = ld16(dy + static_cast<int64_t>(s_tok[r]) * C + c0 + ch * 8);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
     const bool ok = rr < s_valid[h];
+    const float g = s_gate[r];
     float f[8];
     unpack16(raw[i], f);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) f[u] = ok ? g[i] * f[u] : 0.0f;
+    for (int u = 0; u < 8; ++u) f[u] = ok ? g * f[u] : 0.0f;
     *reinterpret_cast<float4*>(&tile[r][ch * 8]) = make_float4(f[0], f[1], f[2], f[3]);
     *reinterpret_cast<float4*>(&tile[r][ch * 8 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
   }
@@ -649,18 +658,18 @@ hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gat
   const int lpt = lanes_per_token(nvec), tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
   const int64_t S = static_cast<int64_t>(T) * k, P = mx_padded_rows(S, E);
-  return with_k(k, [&](auto KC) {
+  const hipError_t err = with_k(k, [&](auto KC) {
     constexpr int K = decltype(KC)::value;
     hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float, true, K>), grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(o), gate, row_of_slot, T, nvec, lpt,
-                       static_cast<float*>(d_o), dgate, d_o_mx.k.q, d_o_mx.k.s, T * k);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((dout_tmajor_kernel<K>), dim3(static_cast<unsigned>(P / 128 + (P % 128 ? 1 : 0)), d / 64),
-                       dim3(256), 0, s, static_cast<const bf16_t*>(dy), gate, row_of_slot, token_of_row, offsets, E,
-                       d, P, d_o_mx.t.q, d_o_mx.t.s);
+                       static_cast<float*>(d_o), dgate, d_o_mx.k.q, d_o_mx.k.s, T * k, d_o_mx.gate_of_row);
     return hipGetLastError();
   });
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dout_tmajor_kernel, dim3(static_cast<unsigned>(P / 128 + (P % 128 ? 1 : 0)), d / 64), dim3(256),
+                     0, s, static_cast<const bf16_t*>(dy), d_o_mx.gate_of_row, token_of_row, offsets, E, d, P,
+                     d_o_mx.t.q, d_o_mx.t.s);
+  return hipGetLastError();
 }
 
 // W_r [d][E] -> W_rT [E][d] (same dtype), so the router term of dx reads rows.

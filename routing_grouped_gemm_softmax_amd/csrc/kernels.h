@@ -112,19 +112,23 @@ hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int
 // scales [P/64][d][2], every expert's rows padded to a multiple of 64 starting
 // at its padded offset: the W_down weight gradient's operand).
 inline int64_t mx_padded_rows(int64_t S, int64_t E) { return (S + 63 * E + 63) / 64 * 64; }
+// A third part holds the gate of every expert row ([S] fp32), which the
+// first pass writes for the second.
 inline size_t mx_dout_image_bytes(int64_t S, int64_t d, int64_t E) {
   const size_t pd = static_cast<size_t>(mx_padded_rows(S, E)) * static_cast<size_t>(d);
-  return mx_image_bytes(S, d) + mx_part_bytes(pd) + mx_part_bytes(pd / 32);
+  return mx_image_bytes(S, d) + mx_part_bytes(pd) + mx_part_bytes(pd / 32) + mx_part_bytes(static_cast<size_t>(S) * 4);
 }
 struct MxDoutImage {
-  MxImage k;  // [S][d] along d
-  MxImage t;  // [d][P] along each expert's tokens
+  MxImage k;         // [S][d] along d
+  MxImage t;         // [d][P] along each expert's tokens
+  float* gate_of_row;  // [S]
 };
 inline MxDoutImage mx_dout_image(const void* base, int64_t S, int64_t d, int64_t E) {
   uint8_t* p = static_cast<uint8_t*>(const_cast<void*>(base));
   const size_t pd = static_cast<size_t>(mx_padded_rows(S, E)) * static_cast<size_t>(d);
   uint8_t* t = p + mx_image_bytes(S, d);
-  return MxDoutImage{mx_image(base, S, d), MxImage{t, t + mx_part_bytes(pd)}};
+  uint8_t* g = t + mx_part_bytes(pd) + mx_part_bytes(pd / 32);
+  return MxDoutImage{mx_image(base, S, d), MxImage{t, t + mx_part_bytes(pd)}, reinterpret_cast<float*>(g)};
 }
 // d_o (fp32) may be null: then only the images are written. dO = gate * dy
 // in fp32 is decided once per element and both images encode that value.
