@@ -101,13 +101,15 @@ enum moe_device_status { MOE_DEV_OK = 0, MOE_DEV_BAD_EXPERT = 1, MOE_DEV_DUP_EXP
 
 /* Layer options, bits of moe_shape.flags. */
 enum moe_flags {
-  /* Activation recompute (fp32 and bf16 layers). moe_grouped_ffn_fwd keeps
-   * G, U, H in its workspace only and saves nothing (moe_save_size is 0);
-   * moe_grouped_ffn_bwd runs the gate/up grouped GEMM again from xp into its
-   * own workspace before the backward GEMMs. This trades one extra
-   * 4*S*d*f-flop GEMM per step for the 3*S*f activations that otherwise
-   * stay live between forward and backward. Results are bit-identical to
-   * the layer without the flag. unite.ai page, "Parallelismo, precisione e
+  /* Activation recompute. moe_grouped_ffn_fwd keeps G, U, H in its
+   * workspace only (MXFP8 layers: G, U and H's token-major operand) and saves
+   * no activations (moe_save_size is 0 for fp32 and bf16 layers; MXFP8 layers
+   * keep only the dgrad weight copies there); moe_grouped_ffn_bwd runs the
+   * gate/up grouped GEMM again from xp into its own workspace before the
+   * backward GEMMs (MXFP8 layers first quantise xp along d and w_gate, w_up
+   * in that GEMM's layout again). This trades one extra 4*S*d*f-flop GEMM
+   * per step for the activations that otherwise stay live between forward
+   * and backward. Results are bit-identical to the layer without the flag. unite.ai page, "Parallelismo, precisione e
    * tecniche di memoria" (recomputing activations cuts activation memory at
    * some cost in throughput). */
   MOE_FLAG_RECOMPUTE = 1

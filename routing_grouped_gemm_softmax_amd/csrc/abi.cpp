@@ -43,8 +43,6 @@ int act_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 int check_shape(const moe_shape* s) {
   if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
   if (s->flags & ~MOE_FLAG_RECOMPUTE) return fail(MOE_ERR_INVALID_ARG, "unknown bits in shape.flags (%d)", s->flags);
-  if (s->dtype == MOE_MXFP8 && (s->flags & MOE_FLAG_RECOMPUTE))
-    return fail(MOE_ERR_UNSUPPORTED, "activation recompute is available for fp32 and bf16 layers");
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8)
     return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
   if (s->T < 1 || s->d < 1 || s->E < 1 || s->k < 1 || s->f < 1)
@@ -117,9 +115,17 @@ size_t dgu_bytes_for(const moe_shape* s) {
 // quantised weight copies.
 size_t save_planes(const moe_shape* s) { return recompute(s) ? 0 : gu_h_bytes(s); }
 size_t save_bytes_for(const moe_shape* s) {
-  return save_planes(s) + (s->dtype == MOE_MXFP8
-                               ? moe::ffn_mx_save_extra((int)(s->T * s->k), (int)s->d, (int)s->f, (int)s->E)
-                               : 0);
+  return save_planes(s) + (s->dtype == MOE_MXFP8 ? moe::ffn_mx_save_extra((int)(s->T * s->k), (int)s->d, (int)s->f,
+                                                                          (int)s->E, recompute(s))
+                                                 : 0);
+}
+// MXFP8 layers: bytes of the FFN workspaces' own pieces, before the G, U
+// planes that recompute places after them.
+size_t mx_fwd_bytes(const moe_shape* s) {
+  return moe::ffn_mx_fwd_workspace((int)(s->T * s->k), (int)s->d, (int)s->f, (int)s->E, recompute(s));
+}
+size_t mx_bwd_bytes(const moe_shape* s) {
+  return moe::ffn_mx_bwd_workspace((int)(s->T * s->k), (int)s->d, (int)s->f, (int)s->E, recompute(s));
 }
 
 // moe_kernel_timer's state: the armed mode (-1: none) and the caller's
@@ -179,13 +185,14 @@ size_t moe_workspace_size(int op, const moe_shape* s) {
   switch (op) {
     case MOE_OP_ROUTE: return s->dtype == MOE_F32 ? 0 : moe::route_bf16_workspace(d, E);
     case MOE_OP_DISPATCH: return moe::dispatch_workspace(T, E);
-    case MOE_OP_FFN_FWD:
-      if (s->dtype == MOE_MXFP8) return moe::ffn_mx_fwd_workspace(T * k, d, f, E);
-      return recompute(s) ? gu_h_bytes(s) : 0;  // recompute: G, U, H live here
+    case MOE_OP_FFN_FWD: {
+      const size_t rec = recompute(s) ? gu_h_bytes(s) : 0;  // recompute: G, U, H live here
+      return (s->dtype == MOE_MXFP8 ? mx_fwd_bytes(s) : 0) + rec;
+    }
     case MOE_OP_FFN_BWD: {
       const size_t dgu = dgu_bytes_for(s);  // dG|dU rows
-      if (s->dtype == MOE_MXFP8) return dgu + moe::ffn_mx_bwd_workspace(T * k, d, f, E);
-      return dgu + (recompute(s) ? gu_h_bytes(s) : 0);  // recompute: G, U, H after dG|dU
+      const size_t rec = recompute(s) ? gu_h_bytes(s) : 0;  // recompute: G, U, H after the rest
+      return dgu + (s->dtype == MOE_MXFP8 ? mx_bwd_bytes(s) : 0) + rec;
     }
     case MOE_OP_ROUTE_BWD:
       return s->dtype == MOE_F32 ? moe::route_bwd_workspace(T, d, E) : moe::route_bwd_bf16_workspace(T, d, E);
@@ -294,8 +301,12 @@ int moe_grouped_ffn_fwd(const void* xp, const uint8_t* xp_mx, const void* w_gate
   a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
   a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down; a.xp_mx = xp_mx;
   const size_t plane = s->dtype == MOE_MXFP8 ? gu_h_bytes(s) / 2 : (size_t)a.S * a.f * act_bytes(s->dtype);
-  char* gu_h = static_cast<char*>(recompute(s) ? ws : save);  // G, U, H (MXFP8: blocked G, U)
+  // G, U, H (MXFP8: blocked G, U): the save buffer, or with recompute the
+  // workspace (after the MXFP8 pieces).
+  char* gu_h = recompute(s) ? static_cast<char*>(ws) + (s->dtype == MOE_MXFP8 ? mx_fwd_bytes(s) : 0)
+                            : static_cast<char*>(save);
   a.G = gu_h; a.U = gu_h + plane; a.H = s->dtype == MOE_MXFP8 ? nullptr : gu_h + 2 * plane;
+  a.recompute = recompute(s);
   a.mx_save = static_cast<char*>(save) + save_planes(s);
   a.o = o_out;
   if (s->dtype == MOE_MXFP8)
@@ -360,8 +371,10 @@ int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, 
   const size_t plane = s->dtype == MOE_MXFP8 ? gu_h_bytes(s) / 2 : (size_t)a.S * a.f * act_bytes(s->dtype);
   const size_t dgu_bytes = dgu_bytes_for(s);
   char* sv = const_cast<char*>(static_cast<const char*>(save));
-  // Recompute: G, U, H are rebuilt in the workspace, after the dG|dU rows.
-  char* gu_h = recompute(s) ? static_cast<char*>(ws) + dgu_bytes : sv;
+  // Recompute: G, U, H are rebuilt in the workspace, after the dG|dU rows
+  // (MXFP8: after the backward's own pieces).
+  char* gu_h = recompute(s) ? static_cast<char*>(ws) + dgu_bytes + (s->dtype == MOE_MXFP8 ? mx_bwd_bytes(s) : 0)
+                            : sv;
   a.G = gu_h; a.U = gu_h + plane; a.H = s->dtype == MOE_MXFP8 ? nullptr : gu_h + 2 * plane;
   a.recompute = recompute(s);
   a.mx_save = sv + save_planes(s);

@@ -47,12 +47,14 @@ int64_t padded_rows(int S, int E) { return (static_cast<int64_t>(S) + 63LL * E +
 
 struct FwdWs {
   uint8_t *xq, *xs, *wgq, *wgs, *wuq, *wus, *hq, *hs, *wdq, *wds;
-  int32_t* poff;  // per-expert offsets of the rows padded to 64
+  int32_t* poff;     // per-expert offsets of the rows padded to 64
+  uint8_t *ht, *hts; // recompute only: H along the tokens (else in the save buffer)
 };
-FwdWs carve_fwd(char* base, int S, int d, int f, int E, size_t* total) {
+FwdWs carve_fwd(char* base, int S, int d, int f, int E, bool rec, size_t* total) {
   Carve c{base};
   const size_t sd = static_cast<size_t>(S) * d, sf = static_cast<size_t>(S) * f;
   const size_t w = static_cast<size_t>(E) * d * f;
+  const size_t P = static_cast<size_t>(padded_rows(S, E));
   FwdWs o;
   o.xq = c.take(sd); o.xs = c.take(sd / 32);
   o.wgq = c.take(w); o.wgs = c.take(w / 32);
@@ -60,6 +62,10 @@ FwdWs carve_fwd(char* base, int S, int d, int f, int E, size_t* total) {
   o.hq = c.take(sf); o.hs = c.take(sf / 32);
   o.wdq = c.take(w); o.wds = c.take(w / 32);
   o.poff = reinterpret_cast<int32_t*>(c.take(static_cast<size_t>(E + 1) * 4));
+  o.ht = o.hts = nullptr;
+  if (rec) {
+    o.ht = c.take(P * f); o.hts = c.take(P * f / 32);
+  }
   if (total) *total = c.used;
   return o;
 }
@@ -67,11 +73,12 @@ FwdWs carve_fwd(char* base, int S, int d, int f, int E, size_t* total) {
 // Save-buffer region of an MXFP8 layer after the blocked G, U planes: the
 // columns-blocked weight copies the backward's dgrad GEMMs use, written by
 // the forward's weight pass, and H as the W_down weight gradient's
-// token-major operand, written by the gate/up epilogue.
+// token-major operand, written by the gate/up epilogue (not with
+// recompute: the backward rebuilds it).
 struct SaveMx {
   uint8_t *wgq, *wgs, *wuq, *wus, *wdq, *wds, *ht, *hts;
 };
-SaveMx carve_save(char* base, int S, int d, int f, int E, size_t* total) {
+SaveMx carve_save(char* base, int S, int d, int f, int E, bool rec, size_t* total) {
   Carve c{base};
   const size_t w = static_cast<size_t>(E) * d * f;
   const size_t P = static_cast<size_t>(padded_rows(S, E));
@@ -79,7 +86,10 @@ SaveMx carve_save(char* base, int S, int d, int f, int E, size_t* total) {
   o.wgq = c.take(w); o.wgs = c.take(w / 32);
   o.wuq = c.take(w); o.wus = c.take(w / 32);
   o.wdq = c.take(w); o.wds = c.take(w / 32);
-  o.ht = c.take(P * f); o.hts = c.take(P * f / 32);
+  o.ht = o.hts = nullptr;
+  if (!rec) {
+    o.ht = c.take(P * f); o.hts = c.take(P * f / 32);
+  }
   if (total) *total = c.used;
   return o;
 }
@@ -107,6 +117,27 @@ BwdWs carve_bwd(char* base, int S, int d, int f, int E, size_t* total) {
   return o;
 }
 
+// Recompute, after the backward's pieces: what the gate/up GEMM needs to run
+// again (q(Xp) along d, q(W_gate)^T and q(W_up)^T along d) and writes (q(H)
+// along f, unused, and along the tokens).
+struct RecWs {
+  uint8_t *xq, *xs, *wgq, *wgs, *wuq, *wus, *hq, *hs, *ht, *hts;
+};
+RecWs carve_rec(char* base, int S, int d, int f, int E, size_t* total) {
+  Carve c{base};
+  const size_t sd = static_cast<size_t>(S) * d, sf = static_cast<size_t>(S) * f;
+  const size_t w = static_cast<size_t>(E) * d * f;
+  const size_t P = static_cast<size_t>(padded_rows(S, E));
+  RecWs o;
+  o.xq = c.take(sd); o.xs = c.take(sd / 32);
+  o.wgq = c.take(w); o.wgs = c.take(w / 32);
+  o.wuq = c.take(w); o.wus = c.take(w / 32);
+  o.hq = c.take(sf); o.hs = c.take(sf / 32);
+  o.ht = c.take(P * f); o.hts = c.take(P * f / 32);
+  if (total) *total = c.used;
+  return o;
+}
+
 #define TRY(x)                                \
   do {                                        \
     hipError_t _e = (x);                      \
@@ -115,15 +146,15 @@ BwdWs carve_bwd(char* base, int S, int d, int f, int E, size_t* total) {
 
 }  // namespace
 
-size_t ffn_mx_fwd_workspace(int S, int d, int f, int E) {
+size_t ffn_mx_fwd_workspace(int S, int d, int f, int E, bool rec) {
   size_t n = 0;
-  carve_fwd(nullptr, S, d, f, E, &n);
+  carve_fwd(nullptr, S, d, f, E, rec, &n);
   return n;
 }
 
-size_t ffn_mx_save_extra(int S, int d, int f, int E) {
+size_t ffn_mx_save_extra(int S, int d, int f, int E, bool rec) {
   size_t n = 0;
-  carve_save(nullptr, S, d, f, E, &n);
+  carve_save(nullptr, S, d, f, E, rec, &n);
   return n;
 }
 
@@ -131,17 +162,18 @@ size_t ffn_mx_gu_plane(int S, int f, int E) {
   return a256(static_cast<size_t>(padded_rows(S, E)) * f * 4);
 }
 
-size_t ffn_mx_bwd_workspace(int S, int d, int f, int E) {
-  size_t n = 0;
+size_t ffn_mx_bwd_workspace(int S, int d, int f, int E, bool rec) {
+  size_t n = 0, r = 0;
   carve_bwd(nullptr, S, d, f, E, &n);
-  return n;
+  if (rec) carve_rec(nullptr, S, d, f, E, &r);
+  return n + r;
 }
 
 hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
   const int S = a.S, d = a.d, f = a.f, E = a.E;
-  const FwdWs w = carve_fwd(static_cast<char*>(ws), S, d, f, E, nullptr);
+  const FwdWs w = carve_fwd(static_cast<char*>(ws), S, d, f, E, a.recompute, nullptr);
   const int64_t wsz = static_cast<int64_t>(d) * f;
-  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), S, d, f, E, nullptr);
+  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), S, d, f, E, a.recompute, nullptr);
   const int64_t P = padded_rows(S, E);
   TRY(launch_mx_poff(a.offsets, E, w.poff, s));
   // Operands: Xp along d; W_gate, W_up along d, transposed to [f][d]. The same
@@ -170,7 +202,8 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
     // epilogue; H leaves only as E4M3 operands: along f (the next GEMM's A
     // operand) and along the expert's tokens (the W_down weight gradient's).
     p.mxq = w.hq; p.mxs = w.hs; p.mxq_ld = f; p.mxs_slab = 2LL * S;
-    p.tq = sv.ht; p.ts = sv.hts; p.tq_ld = P; p.ts_slab = 2LL * f; p.poff = w.poff;
+    p.tq = a.recompute ? w.ht : sv.ht; p.ts = a.recompute ? w.hts : sv.hts;
+    p.tq_ld = P; p.ts_slab = 2LL * f; p.poff = w.poff;
     TRY(launch_mx_ragged(FWD_GU, p, s));
   }
   // Operands: H along f (above); W_down along f, transposed to [d][f] (and
@@ -187,13 +220,36 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
 
 hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
   const int S = a.S, d = a.d, f = a.f, E = a.E;
-  const BwdWs w = carve_bwd(static_cast<char*>(ws), S, d, f, E, nullptr);
-  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), S, d, f, E, nullptr);
+  size_t bwd_bytes = 0;
+  const BwdWs w = carve_bwd(static_cast<char*>(ws), S, d, f, E, &bwd_bytes);
+  const SaveMx sv = carve_save(static_cast<char*>(a.mx_save), S, d, f, E, a.recompute, nullptr);
   const int64_t wsz = static_cast<int64_t>(d) * f;
   const int64_t P = padded_rows(S, E);
   // Per-expert padded offsets of the token-major (weight-gradient) layouts.
   TRY(launch_mx_poff(a.offsets, E, w.poff, s));
   TRY(launch_mx_blocks(a.offsets, w.poff, E, P, w.blk, s));
+  uint8_t *ht = sv.ht, *hts = sv.hts;
+  if (a.recompute) {
+    // The gate/up GEMM again, from xp and the weights as the forward ran it:
+    // the same operand bytes and the same kernel give bit-identical G, U and
+    // H images. Only the layouts that GEMM reads are rebuilt (the dgrad weight
+    // copies are in the save buffer).
+    const RecWs r = carve_rec(static_cast<char*>(ws) + bwd_bytes, S, d, f, E, nullptr);
+    TRY(launch_mx_kmajor(a.xp, S, d, 1, 0, r.xq, 0, r.xs, 0, s));
+    TRY(launch_mx_tgroup(a.w_gate, d, f, nullptr, E, wsz, r.wgq, d, wsz, r.wgs, wsz / 32, s, nullptr, nullptr));
+    TRY(launch_mx_tgroup(a.w_up, d, f, nullptr, E, wsz, r.wuq, d, wsz, r.wus, wsz / 32, s, nullptr, nullptr));
+    GemmParams p{};
+    p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
+    p.a = r.xq; p.lda = d; p.as = r.xs; p.as_slab = 2LL * S;
+    p.b0 = r.wgq; p.b1 = r.wuq; p.ldb = d; p.bstride = wsz;
+    p.bs0 = r.wgs; p.bs1 = r.wus; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
+    p.c0 = a.G; p.c1 = a.U; p.ldc = f; p.N = 2 * f; p.K = d;
+    p.mxq = r.hq; p.mxs = r.hs; p.mxq_ld = f; p.mxs_slab = 2LL * S;
+    p.tq = r.ht; p.ts = r.hts; p.tq_ld = P; p.ts_slab = 2LL * f; p.poff = w.poff;
+    TRY(launch_mx_ragged(FWD_GU, p, s));
+    ht = r.ht;
+    hts = r.hts;
+  }
   {  // dGU = SwiGLU'(q(dO) q(W_down)^T): dO along d; W_down [f][d] along d
      // was quantised by the forward.
     uint8_t *doq = w.doq, *dos = w.dos;
@@ -239,7 +295,7 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
     }
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
-    p.a = sv.ht; p.lda = P; p.as = sv.hts; p.as_slab = 2LL * f;
+    p.a = ht; p.lda = P; p.as = hts; p.as_slab = 2LL * f;
     p.b0 = dot; p.ldb = P; p.bs0 = dots; p.bs_slab = 2LL * d;
     p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = static_cast<int64_t>(f) * d; p.M = f; p.N = d; p.f = d;
     TRY(launch_mx_wgrad(p, s));

@@ -268,6 +268,12 @@ __global__ __launch_bounds__(256) void gg_bf16_kernel(GemmParams p) {
 // the SwiGLU epilogue of the gate/up forward does not fit its registers
 // beside the stream state.
 //
+// Epilogue stores are non-temporal (cache policy nt): the outputs are written
+// once and read by a later kernel, and the stores complete sooner without
+// allocating in the L2, which matters because the next slabs' waits count
+// them.
+constexpr int kStoreNT = 2;
+
 // Wait counts: vmcnt counts loads and stores together, in issue order. The
 // wait for slab g+1 must allow exactly the operations issued after that
 // slab's loads: the loads of slabs g+2 and g+3, and kEpiStores stores for
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(256) void gg_bf16_stream_kernel(GemmParams p) {
       const int r = t * 8 + (lane >> 3);
       typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
       const u32x4 v = *reinterpret_cast<const u32x4*>(wa + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<uint32_t>(r * ld + c * 16), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<uint32_t>(r * ld + c * 16), 0, kStoreNT);
     }
     wave_sync();
     __builtin_amdgcn_sched_barrier(0);

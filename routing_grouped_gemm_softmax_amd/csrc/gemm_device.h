@@ -432,7 +432,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     for (int t = 0; t < WM / 8; ++t) {
       const int r = t * 8 + (lane >> 3);
       const uint4 v = *reinterpret_cast<const uint4*>(wa + slot * kSlot + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
-      if (r < rows && c * 8 < cols) *reinterpret_cast<uint4*>(g + r * ld + c * 16) = v;
+      // Non-temporal: written once, read by a later kernel.
+      typedef unsigned int u32x4nt __attribute__((ext_vector_type(4)));
+      if (r < rows && c * 8 < cols)
+        __builtin_nontemporal_store(u32x4nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4nt*>(g + r * ld + c * 16));
     }
     wave_sync();
   };

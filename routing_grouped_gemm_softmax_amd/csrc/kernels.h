@@ -34,7 +34,9 @@ struct FfnArgs {
   // moe_dispatch / moe_combine_bwd already wrote; NULL = quantise here.
   const void* xp_mx;
   const void* d_o_mx;
-  // Backward only: recompute G, U, H (into the G, U, H pointers) first.
+  // Activation recompute: the forward keeps G, U, H (MXFP8: G, U and H's
+  // images) in its workspace; the backward recomputes them (into the G, U, H
+  // pointers) first.
   bool recompute;
 };
 
@@ -174,13 +176,13 @@ hipError_t launch_mx_blocks(const int32_t* offsets, const int32_t* poff, int E, 
 hipError_t launch_mx_poff(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
 
 // MXFP8 expert FFN (ffn_mx.hip): workspace bytes and launch.
-size_t ffn_mx_fwd_workspace(int S, int d, int f, int E);
+size_t ffn_mx_fwd_workspace(int S, int d, int f, int E, bool recompute);
 // Extra save-buffer bytes of an MXFP8 layer (the backward's weight copies).
-size_t ffn_mx_save_extra(int S, int d, int f, int E);
+size_t ffn_mx_save_extra(int S, int d, int f, int E, bool recompute);
 // Bytes of one blocked fp32 G or U plane of an MXFP8 layer: rows padded to 64
 // per expert, 32 x 32 blocks of 4 KB in accumulator lane order.
 size_t ffn_mx_gu_plane(int S, int f, int E);
-size_t ffn_mx_bwd_workspace(int S, int d, int f, int E);
+size_t ffn_mx_bwd_workspace(int S, int d, int f, int E, bool recompute);
 hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s);
 

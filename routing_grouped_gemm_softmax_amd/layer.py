@@ -19,8 +19,9 @@ class MoELayer:
         """``mx_images`` (MXFP8 layers): dispatch and combine-backward also write
         the MXFP8 images of xp and d_o, which the grouped FFN calls then read;
         False leaves the quantisation of both to the FFN calls.
-        ``recompute`` (fp32/bf16 layers): save no G, U, H between forward and
-        backward; the backward recomputes them (MOE_FLAG_RECOMPUTE)."""
+        ``recompute``: save no G, U, H (MXFP8: G, U and H's token-major
+        operand) between forward and backward; the backward recomputes them
+        (MOE_FLAG_RECOMPUTE)."""
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.shape = L.MoeShape.make(T, d, E, k, f, dtype, L.MOE_FLAG_RECOMPUTE if recompute else 0)
         self.recompute = recompute

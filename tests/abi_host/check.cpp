@@ -74,7 +74,7 @@ int main() {
   EXPECT(moe_save_size(&bad) == BAD);
   bad = ok; bad.T = (int64_t)1 << 40;
   EXPECT(moe_save_size(&bad) == BAD);
-  bad = ok; bad.dtype = MOE_MXFP8; bad.flags = MOE_FLAG_RECOMPUTE;
+  bad = ok; bad.flags = 2;  // an unknown flag bit
   EXPECT(moe_save_size(&bad) == BAD);
   const moe_shape rec = shape(256, 128, 8, 4, 128, MOE_BF16, MOE_FLAG_RECOMPUTE);
   EXPECT(moe_save_size(&rec) == 0);

@@ -87,12 +87,16 @@ hipError_t launch_mxfp8_quantize_grouped(const void*, int64_t rows, int64_t cols
                                          uint8_t*, hipStream_t) {
   return hit(static_cast<int>(rows), static_cast<int>(cols), G);
 }
-size_t ffn_mx_fwd_workspace(int S, int d, int f, int) { return static_cast<size_t>(S) * (d + f) + 4096; }
-size_t ffn_mx_save_extra(int S, int d, int f, int E) {
+size_t ffn_mx_fwd_workspace(int S, int d, int f, int, bool rec) {
+  return static_cast<size_t>(S) * (d + f) + (rec ? static_cast<size_t>(S) * f : 0) + 4096;
+}
+size_t ffn_mx_save_extra(int S, int d, int f, int E, bool) {
   return static_cast<size_t>(E) * d * f * 3 + static_cast<size_t>(S + 64 * E) * f + 4096;
 }
 size_t ffn_mx_gu_plane(int S, int f, int E) { return static_cast<size_t>(S + 64 * E) * f * 4; }
-size_t ffn_mx_bwd_workspace(int S, int d, int f, int) { return static_cast<size_t>(S) * (2 * d + 4 * f) + 4096; }
+size_t ffn_mx_bwd_workspace(int S, int d, int f, int, bool rec) {
+  return static_cast<size_t>(S) * (2 * d + 4 * f) + (rec ? static_cast<size_t>(S) * (d + 2 * f) : 0) + 4096;
+}
 hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void*, hipStream_t) { return hit(a.S, a.d, a.E, 0, a.f); }
 hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void*, hipStream_t) { return hit(a.S, a.d, a.E, 0, a.f); }
 }  // namespace moe

@@ -158,7 +158,8 @@ def test_mx_image_arguments_are_checked_on_the_host():
 
 def test_recompute_flag_sizes_and_checks():
     """MOE_FLAG_RECOMPUTE moves G, U, H from the save buffer into the FFN
-    workspaces; unknown flag bits and MXFP8 recompute are rejected."""
+    workspaces (MXFP8: G, U and H's token-major operand; the save buffer keeps
+    only the dgrad weight copies); unknown flag bits are rejected."""
     T, d, E, k, f = 256, 128, 8, 4, 128
     S = T * k
     for dt, b in (("f32", 4), ("bf16", 2)):
@@ -172,9 +173,14 @@ def test_recompute_flag_sizes_and_checks():
     lib = L.load()
     bad = L.MoeShape.make(T, d, E, k, f, "bf16", 2)
     assert lib.moe_save_size(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+    mxp = L.MoeShape.make(T, d, E, k, f, "mxfp8")
     mxr = L.MoeShape.make(T, d, E, k, f, "mxfp8", L.MOE_FLAG_RECOMPUTE)
-    assert lib.moe_workspace_size(L.MOE_OP_FFN_FWD, ctypes.byref(mxr)) == ctypes.c_size_t(-1).value
-    assert "recompute" in L.last_error()
+    P = (S + 63 * E + 63) // 64 * 64
+    gu = 2 * ((P * f * 4 + 255) // 256 * 256)  # the blocked fp32 G, U planes
+    ht = (P * f + 16 + 255) // 256 * 256 + (P * f // 32 + 16 + 255) // 256 * 256  # H along the tokens
+    assert L.save_size(mxr) == L.save_size(mxp) - gu - ht
+    assert L.workspace_size(L.MOE_OP_FFN_FWD, mxr) == L.workspace_size(L.MOE_OP_FFN_FWD, mxp) + ht + gu
+    assert L.workspace_size(L.MOE_OP_FFN_BWD, mxr) > L.workspace_size(L.MOE_OP_FFN_BWD, mxp) + gu
     # A recompute layer's forward needs its workspace (G, U, H live there).
     rec = L.MoeShape.make(T, d, E, k, f, "bf16", L.MOE_FLAG_RECOMPUTE)
     p = ctypes.c_void_p(0x100000)

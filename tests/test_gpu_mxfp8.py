@@ -59,9 +59,9 @@ CASES = {
 }
 
 
-def _run(wl, inp):
+def _run(wl, inp, recompute=False):
     from routing_grouped_gemm_softmax_amd import MoELayer
-    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, "mxfp8", learned_routing=False)
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, "mxfp8", learned_routing=False, recompute=recompute)
     bf = torch.bfloat16
     t = {n: dev(inp[n], bf) for n in ("x", "dy", "w_gate", "w_up", "w_down")}
     layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=dev(inp["topk_idx"], torch.int32),
@@ -315,3 +315,22 @@ def test_grouped_quantize_bit_exact(sizes, cols):
             deq[r0:r1] = O.e4m3_decode(gq[r0:r1]) * O.e8m0_decode(gs[b])[None, :]
             b += 1
     np.testing.assert_array_equal(deq, O.mx_rows_grouped(x, off))
+
+
+@pytest.mark.parametrize("case", ["balanced", "zipf_ragged_empty", "stream_ragged_empty"])
+def test_mxfp8_recompute_is_bit_identical(case):
+    """MOE_FLAG_RECOMPUTE on an MXFP8 layer: the forward saves no G, U or H
+    image, the backward quantises xp and the gate/up weights again and reruns
+    the gate/up GEMM; every output equals the saving layer's bit for bit, and
+    the save buffer shrinks by the G, U planes and H's token-major operand."""
+    name, over, pop = CASES[case]
+    wl = WORKLOADS[name].with_shape(**over)
+    inp = make_inputs(wl, 0, popularity=pop)
+    print(f"[gpu] mxfp8 recompute {case}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} f={wl.f}", flush=True)
+    ref = _run(wl, inp)
+    rec = _run(wl, inp, recompute=True)
+    for n in ("o", "y", "dgate", "dxp", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(getattr(rec, n), getattr(ref, n)), n
+    S, f = wl.T * wl.k, wl.f
+    P = (S + 63 * wl.E + 63) // 64 * 64
+    assert rec.save.numel() < ref.save.numel() - 2 * P * f * 4
