@@ -198,11 +198,11 @@ def cpu_baseline(wl, inp, budget_s: float = 20.0):
                       f"{dt:.1f} s"}
 
 
-def load_traffic(workload: str, dtype: str, mode: str):
-    """HBM bytes per launch of grouped-GEMM step `mode` from the committed
-    rocprofv3 counter summary, if it was taken on the current sources of that
-    kernel family; else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def load_traffic(name: str, dtype: str, mode: str):
+    """The committed rocprofv3 counter summary of grouped-GEMM step `mode`
+    (profiles/traffic_<name>.json: HBM bytes per launch, kernel names), if it
+    was taken on the current sources of that kernel family; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(p):
         return None
     with open(p) as fh:
@@ -210,7 +210,7 @@ def load_traffic(workload: str, dtype: str, mode: str):
     k = rec.get("gemm_kernels", {}).get(mode)
     if not k or k.get("kernel_source_hash") != kernel_source_hash(GEMM_SOURCES[dtype]):
         return None
-    return k.get("hbm_bytes_per_launch")
+    return k
 
 
 def run_layer(wl, inp, args, M, torch, np):
@@ -338,11 +338,18 @@ def run_layer(wl, inp, args, M, torch, np):
     flops_per_launch = mode_flops[dom] / launches
     avg_launch_ms = sum(kdur) / len(kdur)
     achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
-    traffic = load_traffic(wl.name, wl.dtype, dom) if not args.as_bf16 else None
-    kname = {"mxfp8": "gg_mx_kernel", "bf16": "gg_bf16_kernel", "f32": "grouped_gemm_kernel"}[wl.dtype]
+    # Counters were taken without recompute; an MXFP8 shape run on the bf16
+    # path has its own file.
+    from moe_inputs import WORKLOADS
+    tname = wl.name if wl.dtype == WORKLOADS[wl.name].dtype else f"{wl.name}_as_{wl.dtype}"
+    trec = None if args.recompute else load_traffic(tname, wl.dtype, dom)
+    kname = trec["kernel"] if trec else {"mxfp8": "gg_mx_kernel / gg_mx_stream_kernel",
+                                         "bf16": "gg_bf16_kernel / gg_bf16_stream_kernel",
+                                         "f32": "grouped_gemm_kernel"}[wl.dtype]
     roofline = {"kernel": f"{kname} ({dom}: {launches} launch(es) per step)", "bound": "mfma",
                 "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "frac": round(achieved / peak, 4),
+                "traffic": trec["hbm_bytes_per_launch"] if trec else None,
                 "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_launch_ms, 4),
                 "launches_timed": len(kdur)}
     ms_per_step = elapsed / args.steps * 1e3
