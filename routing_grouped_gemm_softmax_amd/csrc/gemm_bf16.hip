@@ -665,9 +665,20 @@ hipError_t ragged_bn(const GemmParams& p, hipStream_t s) {
 
 template <int MODE>
 hipError_t ragged_mode(const GemmParams& p, hipStream_t s) {
-  // Experts with few rows each waste less of a 128-row tile.
   if (static_cast<int64_t>(p.S) >= 1024LL * p.E) return ragged_bn<MODE, 256>(p, s);
-  return ragged_bn<MODE, 128>(p, s);
+  // Under 512 rows per expert on average: 128-row tiles, which waste less on
+  // short experts (measured: the split below costs 7% at 256 rows per expert).
+  if (static_cast<int64_t>(p.S) < 512LL * p.E) return ragged_bn<MODE, 128>(p, s);
+  // 512 to 1023 rows per expert on average, where loads are usually skewed:
+  // the whole 256-row bands of the experts that have them in 256-row tiles,
+  // the rest of every expert in 128-row tiles, which waste less on a short
+  // remainder (measured on a Zipf-routed layer: row-ragged steps -12%).
+  GemmParams q = p;
+  q.band = 1;
+  hipError_t err = ragged_bn<MODE, 256>(q, s);
+  if (err != hipSuccess) return err;
+  q.band = 2;
+  return ragged_bn<MODE, 128>(q, s);
 }
 
 }  // namespace

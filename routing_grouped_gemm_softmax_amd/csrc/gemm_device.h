@@ -212,6 +212,9 @@ struct RowTileMap {
       const int e = lane * 4 + q;
       beg[q] = e < p.E ? p.offsets[e] : 0;
       end[q] = e < p.E ? p.offsets[e + 1] : 0;
+      const int bands = (end[q] - beg[q]) & ~255;
+      if (p.band == 1) end[q] = beg[q] + bands;
+      if (p.band == 2) beg[q] += bands;
       tq[q] = (end[q] - beg[q] + tbm - 1) / tbm;
       tsum += tq[q];
     }

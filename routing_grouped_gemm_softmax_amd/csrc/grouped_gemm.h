@@ -47,6 +47,11 @@ struct GemmParams {
   // half-height, half-width tiles; see RowTileMap.
   int cus;
   int tail;
+  // Row-ragged modes: the rows of each expert a launch covers. 0: all of
+  // them; 1: only its whole 256-row bands; 2: only the rows after those bands
+  // (so a 256-row-tile launch with band 1 and a 128-row-tile launch with
+  // band 2 together cover every row once).
+  int band;
   // MXFP8 kernels, FWD_GU and BWD_DOWN: the epilogue also writes its bf16
   // output rows (H; dG | dU) as the next GEMM's K-major E4M3 operand, q [S][ld]
   // and slab-major scales (as p.as above, slab = mxs_slab bytes).
