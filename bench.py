@@ -82,11 +82,12 @@ def algorithmic_work(wl, recompute=False):
         "moe_dispatch_bwd": {"bytes": (1 + k) * T * d * b},
     }
     if wl.dtype == "mxfp8":
-        # dispatch also writes the MXFP8 image of xp (one E4M3 byte per
-        # element plus one E8M0 byte per 32); combine backward writes dO only
-        # as its two MXFP8 operands (along d, and along each expert's tokens),
-        # not as rows: it reads dy and o and writes the two images.
-        work["moe_dispatch"]["bytes"] += S * d + S * d // 32
+        # dispatch writes xp only as its two MXFP8 operands (along d, and
+        # along each expert's tokens; one E4M3 byte per element plus one E8M0
+        # byte per 32), not as rows: it reads x and writes the two images.
+        # Likewise combine backward writes dO only as its two operands: it
+        # reads dy and o and writes the two images.
+        work["moe_dispatch"]["bytes"] = T * d * b + 2 * (S * d + S * d // 32)
         work["moe_combine_bwd"]["bytes"] = (1 + k) * T * d * b + 2 * (S * d + S * d // 32)
     if recompute:
         work["moe_grouped_ffn_bwd"]["flops_recompute"] = 4 * S * d * f
@@ -356,9 +357,10 @@ def run_layer(wl, inp, args, M, torch, np):
     res = {
         "value": round(wl.T * args.steps / elapsed, 1), "ms_per_step": round(ms_per_step, 4),
         # bytes held between forward and backward beyond the inputs: the save
-        # buffer (G, U, H unless recomputed; MXFP8 weight copies), xp, o, and
-        # for MXFP8 the xp image.
-        "saved_bytes": {"save": layer.save.numel(), "xp": layer.xp.numel() * layer.xp.element_size(),
+        # buffer (G, U, H unless recomputed; MXFP8 weight copies), xp (bf16
+        # and fp32 layers), o, and for MXFP8 xp's two images.
+        "saved_bytes": {"save": layer.save.numel(),
+                        "xp": 0 if layer.xp is None else layer.xp.numel() * layer.xp.element_size(),
                         "o": layer.o.numel() * layer.o.element_size(),
                         "xp_mx": 0 if layer.xp_mx is None else layer.xp_mx.numel()},
         "grouped_gemm": {"tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / peak, 4),

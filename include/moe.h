@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 enum moe_status {
   MOE_OK = 0,
@@ -106,12 +106,13 @@ enum moe_flags {
    * no activations (moe_save_size is 0 for fp32 and bf16 layers; MXFP8 layers
    * keep only the dgrad weight copies there); moe_grouped_ffn_bwd runs the
    * gate/up grouped GEMM again from xp into its own workspace before the
-   * backward GEMMs (MXFP8 layers first quantise xp along d and w_gate, w_up
-   * in that GEMM's layout again). This trades one extra 4*S*d*f-flop GEMM
-   * per step for the activations that otherwise stay live between forward
-   * and backward. Results are bit-identical to the layer without the flag. unite.ai page, "Parallelismo, precisione e
-   * tecniche di memoria" (recomputing activations cuts activation memory at
-   * some cost in throughput). */
+   * backward GEMMs (MXFP8 layers first quantise w_gate, w_up in that GEMM's
+   * layout again, and xp along d unless xp_mx holds its image). This trades
+   * one extra 4*S*d*f-flop GEMM per step for the activations that otherwise
+   * stay live between forward and backward. Results are bit-identical to the
+   * layer without the flag. Passage: unite.ai page, "Parallelismo,
+   * precisione e tecniche di memoria" (recomputing activations cuts
+   * activation memory at some cost in throughput). */
   MOE_FLAG_RECOMPUTE = 1
 };
 
@@ -153,9 +154,10 @@ size_t moe_save_size(const moe_shape* shape);
  * by side). Each part starts 256-byte aligned and is followed by at least 16
  * bytes of slack. Codes and scales are those of mxfp8_quantize with axis 0
  * (the OCP MX v1.0 conversion) of the values the image is made from.
- * moe_dispatch and moe_combine_bwd write the images of xp and d_o ([S][d])
- * for MXFP8 layers, and the grouped FFN calls read them, so neither row
- * matrix is read again only to be quantised. Returns (size_t)-1 for
+ * moe_dispatch and moe_combine_bwd write images in this layout of xp and
+ * d_o ([S][d]) for MXFP8 layers (as the first part of moe_mx_xp_image_size
+ * and moe_mx_dout_image_size buffers), and the grouped FFN calls read them,
+ * so neither row matrix is read again only to be quantised. Returns (size_t)-1 for
  * rows < 1 or cols not a positive multiple of 64. */
 size_t moe_mx_image_size(int64_t rows, int64_t cols);
 
@@ -182,9 +184,15 @@ int moe_route(const void* x, const void* w_router, const moe_shape* shape,
  * device status word in `ws` gets MOE_DEV_BAD_EXPERT. A token that names the
  * same expert in two slots sets MOE_DEV_DUP_EXPERT (both slots are routed,
  * to consecutive rows of that expert).
- * xp_mx_out (MXFP8 layers only; NULL to skip): receives the MXFP8 image of
- * xp (moe_mx_image_size(S, d) bytes, 256-byte aligned), written by the same
- * pass that writes xp's rows. Must be NULL for fp32 and bf16 layers.
+ * xp_mx_out (MXFP8 layers only; NULL to skip): receives the MXFP8 operands
+ * of xp for the FFN calls, moe_mx_xp_image_size(shape) bytes, 256-byte
+ * aligned: the image along d (moe_mx_image_size(S, d) bytes, the gate/up
+ * GEMM's operand) followed by the image along each expert's tokens (the
+ * dW_gate | dW_up weight gradient's operand, each expert's rows padded to a
+ * multiple of 64), both made from x in one pass over the gathered rows. With
+ * xp_mx_out, xp_out may be NULL: then xp's bf16 rows are not written (the
+ * MXFP8 FFN calls need only the images). Must be NULL for fp32 and bf16
+ * layers.
  * ws: at least moe_workspace_size(MOE_OP_DISPATCH) bytes, 256-byte aligned.
  * Passage: bytechap.com page, "Cómo funciona"; unite.ai page, "Parallelismo,
  * precisione e tecniche di memoria" (rows written straight into the experts'
@@ -225,8 +233,9 @@ int moe_read_device_status(const void* ws, void* stream);
  * save (>= moe_save_size bytes) receives what the backward needs (see
  * moe_save_size).
  * ws: moe_workspace_size(MOE_OP_FFN_FWD) bytes (may be 0 -> NULL allowed).
- * xp_mx (MXFP8 layers only; NULL = quantise xp here): the MXFP8 image of xp
- * that moe_dispatch wrote; it must hold the current xp's codes.
+ * xp_mx (MXFP8 layers only; NULL = quantise xp here): the MXFP8 operands of
+ * xp that moe_dispatch wrote (moe_mx_xp_image_size bytes); it must hold the
+ * current xp's codes, and with it xp is not read and may be NULL.
  * Passage: bytechap.com page, "Cómo funciona" (grouped GEMM combining many
  * small expert computations); unite.ai page, "Parallelismo, precisione e
  * tecniche di memoria" (matmuls scheduled on the device). */
@@ -266,6 +275,11 @@ int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate,
  * moe_grouped_ffn_bwd); (size_t)-1 for an invalid shape or a non-MXFP8 one. */
 size_t moe_mx_dout_image_size(const moe_shape* shape);
 
+/* Bytes of the xp_mx buffer of an MXFP8 layer (moe_dispatch,
+ * moe_dispatch_noalloc, moe_grouped_ffn_fwd, moe_grouped_ffn_bwd); (size_t)-1
+ * for an invalid shape or a non-MXFP8 one. */
+size_t moe_mx_xp_image_size(const moe_shape* shape);
+
 /* Grouped FFN backward, per expert e on its rows:
  *   dH = d_o · w_down[e]^T;  dU = dH * silu(G);
  *   dG = dH * U * sig(G) * (1 + G (1 - sig(G)))   (from the saved G, U, H)
@@ -280,13 +294,16 @@ size_t moe_mx_dout_image_size(const moe_shape* shape);
  * d_o_mx (MXFP8 layers only; NULL = quantise d_o here): the MXFP8 operands
  * of d_o that moe_combine_bwd wrote (moe_mx_dout_image_size bytes); with it
  * d_o is not read and may be NULL.
+ * xp_mx (MXFP8 layers only; NULL = quantise xp here): the MXFP8 operands of
+ * xp that moe_dispatch wrote, as passed to the forward; with it xp is not
+ * read and may be NULL (recompute reads the image along d).
  * Passage: the backward of the expert FFN (dgrad and wgrad grouped GEMMs) of
  * the layer specification; the grouped, device-scheduled GEMM of the
  * bytechap.com page, "Cómo funciona", and of the unite.ai page,
  * "Parallelismo, precisione e tecniche di memoria". */
-int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, const void* w_gate,
-                        const void* w_up, const void* w_down, const int32_t* offsets,
-                        const moe_shape* shape,
+int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, const uint8_t* xp_mx,
+                        const void* w_gate, const void* w_up, const void* w_down,
+                        const int32_t* offsets, const moe_shape* shape,
                         const void* save, void* dxp_out, void* dw_gate_out, void* dw_up_out,
                         void* dw_down_out, void* ws, size_t ws_bytes, void* stream);
 

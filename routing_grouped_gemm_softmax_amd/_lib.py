@@ -63,7 +63,8 @@ SIGNATURES = {
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _SHAPE, _P, _P]),
     "moe_combine_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _P]),
     "moe_mx_dout_image_size": (_SZ, [_SHAPE]),
-    "moe_grouped_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mx_xp_image_size": (_SZ, [_SHAPE]),
+    "moe_grouped_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_route_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _SHAPE, _P, _P, _P, _SZ, _P]),
     "moe_dispatch_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SHAPE, _P, _P, _SZ, _P]),
     "moe_load_stats": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
@@ -160,6 +161,14 @@ def mx_dout_image_size(shape: MoeShape) -> int:
     return n
 
 
+def mx_xp_image_size(shape: MoeShape) -> int:
+    """Bytes of an MXFP8 layer's xp operand buffer (moe_mx_xp_image_size)."""
+    n = load().moe_mx_xp_image_size(ctypes.byref(shape))
+    if n == ctypes.c_size_t(-1).value:
+        raise MoeError("moe_mx_xp_image_size", MOE_ERR_INVALID_ARG, last_error())
+    return n
+
+
 def moe_route(x, w_router, shape, logits, topk_idx, topk_gate, ws=None, stream=None):
     T, E, k = shape.T, shape.E, shape.k
     _expect(logits, torch.float32, T * E, "logits")
@@ -216,9 +225,10 @@ def moe_combine_bwd(dy, o, topk_gate, row_of_slot, shape, d_o, dgate, stream=Non
 
 
 def moe_grouped_ffn_bwd(d_o, xp, w_gate, w_up, w_down, offsets, shape, save, dxp, dw_gate, dw_up, dw_down, ws,
-                        stream=None, d_o_mx=None):
+                        stream=None, d_o_mx=None, xp_mx=None):
     _check("moe_grouped_ffn_bwd", load().moe_grouped_ffn_bwd(
-        _ptr(d_o), _ptr(d_o_mx), _ptr(xp), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(offsets), ctypes.byref(shape),
+        _ptr(d_o), _ptr(d_o_mx), _ptr(xp), _ptr(xp_mx), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(offsets),
+        ctypes.byref(shape),
         _ptr(save), _ptr(dxp), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
 

@@ -237,7 +237,8 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* s, int
                  uint8_t* xp_mx_out, void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_shape(s));
   NEED(x); NEED(topk_idx); NEED(counts_out); NEED(offsets_out); NEED(row_of_slot_out); NEED(token_of_row_out);
-  NEED(xp_out); NEED(ws);
+  if (!xp_mx_out) NEED(xp_out);  // with xp's MXFP8 images, the bf16 rows are optional
+  NEED(ws);
   MX_IMAGE_OK(xp_mx_out, s);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MOE_ERR_MISALIGNED, "moe_dispatch: ws must be 256-byte aligned");
   const size_t need = moe::dispatch_workspace((int)s->T, (int)s->E);
@@ -245,7 +246,7 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, const moe_shape* s, int
   if (xp_mx_out)
     LAUNCH(moe::launch_dispatch_mx(x, topk_idx, (int)s->T, (int)s->d, (int)s->E, (int)s->k, counts_out, offsets_out,
                                    row_of_slot_out, token_of_row_out, xp_out,
-                                   moe::mx_image(xp_mx_out, s->T * s->k, s->d), ws, as_stream(stream)));
+                                   moe::mx_row_images(xp_mx_out, s->T * s->k, s->d, s->E), ws, as_stream(stream)));
   else
     LAUNCH(moe::launch_dispatch(x, topk_idx, elem_bytes(s->dtype), (int)s->T, (int)s->d, (int)s->E, (int)s->k,
                                 counts_out, offsets_out, row_of_slot_out, token_of_row_out, xp_out, ws,
@@ -258,15 +259,15 @@ int moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, const moe_shape
                          uint8_t* xp_mx_out, void* stream) {
   CHECK(check_shape(s));
   NEED(x); NEED(topk_idx); NEED(counts_out); NEED(offsets_out); NEED(row_of_slot_out); NEED(token_of_row_out);
-  NEED(xp_out);
+  if (!xp_mx_out) NEED(xp_out);
   MX_IMAGE_OK(xp_mx_out, s);
   const size_t need = moe::dispatch_workspace((int)s->T, (int)s->E), have = moe::dispatch_noalloc_max();
   if (need > have)
     return fail(MOE_ERR_WORKSPACE,
                 "moe_dispatch_noalloc: this shape needs %zu bytes of scratch; the library's array holds %zu "
                 "(use moe_dispatch with a workspace)", need, have);
-  moe::MxImage im{nullptr, nullptr};
-  if (xp_mx_out) im = moe::mx_image(xp_mx_out, s->T * s->k, s->d);
+  moe::MxRowImages im{{nullptr, nullptr}, {nullptr, nullptr}};
+  if (xp_mx_out) im = moe::mx_row_images(xp_mx_out, s->T * s->k, s->d, s->E);
   LAUNCH(moe::launch_dispatch_noalloc(x, topk_idx, elem_bytes(s->dtype), (int)s->T, (int)s->d, (int)s->E,
                                       (int)s->k, counts_out, offsets_out, row_of_slot_out, token_of_row_out, xp_out,
                                       im, as_stream(stream)));
@@ -287,7 +288,8 @@ int moe_grouped_ffn_fwd(const void* xp, const uint8_t* xp_mx, const void* w_gate
                         void* o_out, void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_shape(s));
   CHECK(check_ffn_dtype(s, "moe_grouped_ffn_fwd"));
-  NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(o_out);
+  if (!xp_mx) NEED(xp);  // with xp's MXFP8 images, xp itself is not read
+  NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(o_out);
   if (save_bytes_for(s) > 0) NEED(save);
   MX_IMAGE_OK(xp_mx, s);
   const size_t need = moe_workspace_size(MOE_OP_FFN_FWD, s);
@@ -347,27 +349,34 @@ int moe_combine_bwd(const void* dy, const void* o, const float* topk_gate, const
   return MOE_OK;
 }
 
+size_t moe_mx_xp_image_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK || s->dtype != MOE_MXFP8) return (size_t)-1;
+  return moe::mx_row_images_bytes(s->T * s->k, s->d, s->E);
+}
+
 size_t moe_mx_dout_image_size(const moe_shape* s) {
   if (check_shape(s) != MOE_OK || s->dtype != MOE_MXFP8) return (size_t)-1;
   return moe::mx_dout_image_bytes(s->T * s->k, s->d, s->E);
 }
 
-int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, const void* w_gate,
-                        const void* w_up, const void* w_down, const int32_t* offsets, const moe_shape* s,
-                        const void* save, void* dxp_out, void* dw_gate_out, void* dw_up_out, void* dw_down_out,
-                        void* ws, size_t ws_bytes, void* stream) {
+int moe_grouped_ffn_bwd(const void* d_o, const uint8_t* d_o_mx, const void* xp, const uint8_t* xp_mx,
+                        const void* w_gate, const void* w_up, const void* w_down, const int32_t* offsets,
+                        const moe_shape* s, const void* save, void* dxp_out, void* dw_gate_out, void* dw_up_out,
+                        void* dw_down_out, void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_shape(s));
   CHECK(check_ffn_dtype(s, "moe_grouped_ffn_bwd"));
   if (!d_o_mx || d_o) NEED(d_o);  // with the MXFP8 operands of d_o, d_o itself is not read
-  NEED(xp); NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(dxp_out);
+  if (!xp_mx || xp) NEED(xp);     // likewise xp with its MXFP8 images
+  NEED(w_gate); NEED(w_up); NEED(w_down); NEED(offsets); NEED(dxp_out);
   NEED(dw_gate_out); NEED(dw_up_out); NEED(dw_down_out); NEED(ws);
   if (save_bytes_for(s) > 0) NEED(save);
   MX_IMAGE_OK(d_o_mx, s);
+  MX_IMAGE_OK(xp_mx, s);
   const size_t need = moe_workspace_size(MOE_OP_FFN_BWD, s);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_bwd: workspace %zu < %zu bytes", ws_bytes, need);
   moe::FfnArgs a{};
   a.S = (int)(s->T * s->k); a.d = (int)s->d; a.f = (int)s->f; a.E = (int)s->E;
-  a.offsets = offsets; a.xp = xp; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
+  a.offsets = offsets; a.xp = xp; a.xp_mx = xp_mx; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
   const size_t plane = s->dtype == MOE_MXFP8 ? gu_h_bytes(s) / 2 : (size_t)a.S * a.f * act_bytes(s->dtype);
   const size_t dgu_bytes = dgu_bytes_for(s);
   char* sv = const_cast<char*>(static_cast<const char*>(save));

@@ -206,20 +206,186 @@ __device__ __forceinline__ void mx_store_vals(const float (&f)[8], int v, int d,
       *reinterpret_cast<uint16_t*>(sc + (static_cast<int64_t>(v >> 3) * S + rows[j]) * 2) = sv;
   }
 }
-template <int NR>
-__device__ __forceinline__ void mx_store_piece(const uint4& val, int v, int d, const int (&rows)[NR], int nr,
-                                               uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
-  float f[8];
-  unpack16(val, f);
-  mx_store_vals<NR, false>(f, v, d, rows, nr, q, sc, S);
+// Rows [p0, p0 + 128) of the padded row space (every expert's rows padded to
+// a multiple of 64, experts in order): for each 64-row half h, the expert row
+// its first padded row holds (src[h]) and how many of its 64 rows are real
+// (valid[h]; 0 past the last expert). Wave 0 computes it (the padded offsets
+// by a wave scan over the experts, 4 per lane); the caller syncs.
+__device__ __forceinline__ void padded_halves(const int32_t* __restrict__ offsets, int E, int64_t p0, int* src_out,
+                                              int* valid_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int beg[4], n[4], pad[4], sum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane * 4 + u;
+    beg[u] = e < E ? offsets[e] : 0;
+    n[u] = e < E ? offsets[e + 1] - beg[u] : 0;
+    pad[u] = (n[u] + 63) & ~63;
+    sum += pad[u];
+  }
+  const int excl = wave_exclusive_scan(sum);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t ph = p0 + 64 * h;
+    int src = 0, valid = 0, found = 0, run = excl;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (ph >= run && ph < run + pad[u]) {
+        found = 1;
+        src = beg[u] + static_cast<int>(ph - run);
+        valid = min(64, n[u] - static_cast<int>(ph - run));
+      }
+      run += pad[u];
+    }
+    const uint64_t who = __ballot(found);
+    if (who) {
+      const int l0 = __ffsll(static_cast<long long>(who)) - 1;
+      src = __shfl(src, l0, kWave);
+      valid = __shfl(valid, l0, kWave);
+    } else {
+      src = 0;
+      valid = 0;
+    }
+    if (lane == 0) {
+      src_out[h] = src;
+      valid_out[h] = valid;
+    }
+  }
+}
+
+// MXFP8 images of an expert-ordered row matrix R [S][C] whose row r is
+// gathered from a token-ordered bf16 matrix: R[r] = src[token_of_row[r]]
+// (xp), or gate_of_row[r] * src[token_of_row[r]] in fp32 (GATE: dO, the
+// product combine_bwd_kernel encodes and whose gates it wrote). Written:
+// the image along each expert's tokens (codes tq [C][P] in e's rows padded
+// to 64 from its padded offset, scales ts [P/64][C][2]: a weight gradient's
+// operand); with KMAJOR also the image along C (codes kq [S][C], scales ks
+// [C/64][S][2]: a row operand) and, where `rows` is not null, R's bf16 rows.
+// Every code is decided on the fp32 value of R. The rows are made from src
+// here instead of being stored and read back.
+// One workgroup per (128 padded rows, kImgColBlocks blocks of 64 columns),
+// column groups fastest in the (1-D) grid, so the workgroups running
+// together read the same gathered rows. Wave 0 finds the experts of the two
+// 64-row halves (padded_halves) and 128 threads resolve each row's token
+// (and gate), once for all the column blocks. Per block, 8 lanes per row
+// load its 128 bytes of src (the next block's loads go out before this
+// block is encoded) into an fp32 LDS tile (zeros past an expert's end);
+// from the tile each thread encodes one 32-block of a row (KMAJOR: 64 bytes
+// of a K-major row per pair of threads) and one 32-row block of a column
+// into an LDS output tile that leaves as full 128-byte rows of tq.
+constexpr int kImgColBlocks = 8;
+template <bool GATE, bool KMAJOR>
+__global__ __launch_bounds__(256) void row_images_kernel(const bf16_t* __restrict__ src,
+                                                         const float* __restrict__ gate_of_row,
+                                                         const int32_t* __restrict__ token_of_row,
+                                                         const int32_t* __restrict__ offsets, int E, int C, int S,
+                                                         int64_t P, bf16_t* __restrict__ rows,
+                                                         uint8_t* __restrict__ kq, uint8_t* __restrict__ ks,
+                                                         uint8_t* __restrict__ tq, uint8_t* __restrict__ ts) {
+  __shared__ __attribute__((aligned(16))) float tile[128][64 + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t qt[64][128 + 16];
+  __shared__ int s_src[2], s_valid[2], s_tok[128], s_row[128];
+  __shared__ float s_gate[128];
+  const int tid = threadIdx.x, ncb = C / 64, ncg = (ncb + kImgColBlocks - 1) / kImgColBlocks;
+  const int cb0 = static_cast<int>(blockIdx.x % ncg) * kImgColBlocks, cb1 = min(cb0 + kImgColBlocks, ncb);
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x / ncg) * 128;
+  if (tid < 64) padded_halves(offsets, E, p0, s_src, s_valid);
+  __syncthreads();
+  if (tid < 128) {  // padded row tid: its expert row (-1 past an expert's end), token and gate
+    const int h = tid >> 6, rr = tid & 63;
+    const bool ok = rr < s_valid[h];
+    const int rs = ok ? s_src[h] + rr : -1;
+    s_row[tid] = rs;
+    s_tok[tid] = ok ? token_of_row[rs] : 0;
+    if constexpr (GATE) s_gate[tid] = ok ? gate_of_row[rs] : 0.0f;
+  }
+  __syncthreads();
+  const int ch = tid & 7;
+  const bf16_t* xr[4];  // this thread's 4 rows of src, at 16-byte piece ch
+  int rrow[4];
+  float rg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 32 + (tid >> 3);
+    xr[i] = src + static_cast<int64_t>(s_tok[r]) * C + ch * 8;
+    rrow[i] = s_row[r];
+    rg[i] = GATE ? s_gate[r] : 1.0f;
+  }
+  const int kr = tid >> 1, kb = tid & 1, krs = s_row[kr];  // along C: row, 32-block
+  const int tcol = tid & 63, tblock = tid >> 6;             // along the tokens: column, 32-row block
+  const int64_t pvalid = min(static_cast<int64_t>(128), P - p0);
+  uint4 cur[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cur[i] = ld16(xr[i] + cb0 * 64);
+  for (int cb = cb0; cb < cb1; ++cb) {
+    const int c0 = cb * 64;
+    __syncthreads();  // the previous block's tile and qt are read out
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = i * 32 + (tid >> 3);
+      float f[8];
+      unpack16(cur[i], f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) f[u] = rrow[i] >= 0 ? (GATE ? rg[i] * f[u] : f[u]) : 0.0f;
+      *reinterpret_cast<float4*>(&tile[r][ch * 8]) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(&tile[r][ch * 8 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+      if (!GATE && rows != nullptr && rrow[i] >= 0)
+        st16(rows + static_cast<int64_t>(rrow[i]) * C + c0 + ch * 8, cur[i]);
+    }
+    if (cb + 1 < cb1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cur[i] = ld16(xr[i] + c0 + 64);
+    }
+    __syncthreads();
+    if constexpr (KMAJOR) {
+      float v[32];
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 t4 = *reinterpret_cast<const float4*>(&tile[kr][kb * 32 + 4 * i]);
+        v[4 * i] = t4.x; v[4 * i + 1] = t4.y; v[4 * i + 2] = t4.z; v[4 * i + 3] = t4.w;
+      }
+      const int code = mx_encode_block(v, w);
+      if (krs >= 0) {
+        uint4* d = reinterpret_cast<uint4*>(kq + static_cast<int64_t>(krs) * C + c0 + kb * 32);
+        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        ks[(static_cast<int64_t>(cb) * S + krs) * 2 + kb] = static_cast<uint8_t>(code);
+      }
+    }
+    {
+      float v[32];
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = tile[tblock * 32 + i][tcol];
+      const int code = mx_encode_block(v, w);
+      uint4* d = reinterpret_cast<uint4*>(&qt[tcol][tblock * 32]);
+      d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      if (p0 + tblock * 32 < P) {
+        const int64_t sb = (p0 >> 6) + (tblock >> 1);
+        ts[(sb * C + c0 + tcol) * 2 + (tblock & 1)] = static_cast<uint8_t>(code);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = i * 32 + (tid >> 3), c16 = tid & 7;
+      if (c16 * 16 < pvalid)
+        *reinterpret_cast<uint4*>(tq + static_cast<int64_t>(c0 + row) * P + p0 + c16 * 16) =
+            *reinterpret_cast<const uint4*>(&qt[row][c16 * 16]);
+    }
+  }
+}
+
+static dim3 row_images_grid(int C, int64_t P) {
+  const int ncg = (C / 64 + kImgColBlocks - 1) / kImgColBlocks;
+  return dim3(static_cast<unsigned>(static_cast<int64_t>(ncg) * ((P + 127) / 128)));
 }
 
 // xp[row_of_slot[t][j]] = x[t]: read the token row once, write it k times.
-// MX: bf16 rows, and the same pass writes xp's MXFP8 image (q, sc; S rows).
-template <bool MX>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ x, const int32_t* __restrict__ row_of_slot,
-                                                          int T, int k, int nvec, int lpt, char* __restrict__ xp,
-                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int S) {
+                                                          int T, int k, int nvec, int lpt, char* __restrict__ xp) {
   const int tpw = 256 / lpt;
   const int t = blockIdx.x * tpw + threadIdx.x / lpt;
   const int sub = threadIdx.x % lpt;
@@ -233,13 +399,12 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (rows[j] >= 0) st16(xp + rows[j] * rb + v * 16, val);
-    if constexpr (MX) mx_store_piece<8>(val, v, nvec * 8, rows, k, q, sc, S);
   }
 }
 
 static hipError_t dispatch_impl(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E, int k,
                                 int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
-                                void* xp, const MxImage* mx, void* ws, hipStream_t s, int32_t* status = nullptr) {
+                                void* xp, const MxRowImages* mx, void* ws, hipStream_t s, int32_t* status = nullptr) {
   const int ct = chunk_tokens(T, E);
   const int nch = (T + ct - 1) / ct;
   DispatchWs w = carve(ws, nch, E);
@@ -256,12 +421,15 @@ static hipError_t dispatch_impl(const void* x, const int32_t* topk_idx, int elem
   const int lpt = lanes_per_token(nvec);
   const int tpw = 256 / lpt;
   const dim3 grid((T + tpw - 1) / tpw);
-  if (mx != nullptr)
-    hipLaunchKernelGGL(gather_rows_kernel<true>, grid, dim3(256), 0, s, static_cast<const char*>(x), row_of_slot, T, k,
-                       nvec, lpt, static_cast<char*>(xp), mx->q, mx->s, T * k);
-  else
-    hipLaunchKernelGGL(gather_rows_kernel<false>, grid, dim3(256), 0, s, static_cast<const char*>(x), row_of_slot, T,
-                       k, nvec, lpt, static_cast<char*>(xp), nullptr, nullptr, T * k);
+  if (mx != nullptr) {
+    const int S = T * k;
+    const int64_t P = mx_padded_rows(S, E);
+    hipLaunchKernelGGL((row_images_kernel<false, true>), row_images_grid(d, P), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(x), nullptr, token_of_row, offsets, E, d, S, P,
+                       static_cast<bf16_t*>(xp), mx->k.q, mx->k.s, mx->t.q, mx->t.s);
+  } else
+    hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(256), 0, s, static_cast<const char*>(x), row_of_slot, T, k,
+                       nvec, lpt, static_cast<char*>(xp));
   return hipGetLastError();
 }
 
@@ -274,7 +442,7 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int elem_byte
 
 hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int32_t* counts,
                               int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row, void* xp,
-                              MxImage xp_mx, void* ws, hipStream_t s) {
+                              MxRowImages xp_mx, void* ws, hipStream_t s) {
   return dispatch_impl(x, topk_idx, 2, T, d, E, k, counts, offsets, row_of_slot, token_of_row, xp, &xp_mx, ws, s);
 }
 
@@ -313,7 +481,7 @@ static hipError_t scratch_on_current_device(void** out) {
 
 hipError_t launch_dispatch_noalloc(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E,
                                    int k, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
-                                   int32_t* token_of_row, void* xp, MxImage xp_mx, hipStream_t s) {
+                                   int32_t* token_of_row, void* xp, MxRowImages xp_mx, hipStream_t s) {
   if (dispatch_workspace(T, E) > kNoAllocBytes) return hipErrorInvalidValue;
   // The array's address is the current device's: a stream of another device
   // would run the kernels there with this device's address.
@@ -328,7 +496,7 @@ hipError_t launch_dispatch_noalloc(const void* x, const int32_t* topk_idx, int e
   const hipError_t err = scratch_on_current_device(&ws);
   if (err != hipSuccess) return err;
   return dispatch_impl(x, topk_idx, elem_bytes, T, d, E, k, counts, offsets, row_of_slot, token_of_row, xp,
-                       xp_mx.q != nullptr ? &xp_mx : nullptr, ws, s);
+                       xp_mx.k.q != nullptr ? &xp_mx : nullptr, ws, s);
 }
 
 // Row kernels take the slot count K as a template argument and issue the
@@ -531,126 +699,6 @@ hipError_t launch_combine_bwd(const void* dy, const void* o, const float* gate, 
   });
 }
 
-// The token-major MXFP8 image of an MXFP8 layer's dO: row r of expert e is
-// dO[r] = gate_of_row[r] * dy[token_of_row[r]], the same fp32 product
-// combine_bwd_kernel encodes (which also wrote gate_of_row), blocked in 32
-// rows down each column inside e's rows padded to 64: codes q [C][P] at
-// columns poff[e].., scales s [P/64][C][2]. dO is rebuilt from dy instead of
-// being stored in fp32 and read back.
-// One workgroup per (128 padded rows, 64 columns). Wave 0 first finds the
-// expert of each 64-row half (the padded offsets by a wave scan over the
-// experts, 4 per lane), then each of 128 threads resolves one row's token
-// and gate into LDS; each thread then loads 16 bytes of a gathered dy row
-// (all loads before any use), scales them by the row's gate into an fp32 LDS
-// tile, and each thread encodes one 32-row block of one column into an LDS
-// output tile that leaves as full 128-byte rows of q.
-__global__ __launch_bounds__(256) void dout_tmajor_kernel(const bf16_t* __restrict__ dy,
-                                                          const float* __restrict__ gate_of_row,
-                                                          const int32_t* __restrict__ token_of_row,
-                                                          const int32_t* __restrict__ offsets, int E, int C,
-                                                          int64_t P, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
-  __shared__ __attribute__((aligned(16))) float tile[128][64 + 4];
-  __shared__ __attribute__((aligned(16))) uint8_t qt[64][128 + 16];
-  __shared__ int s_src[2], s_valid[2], s_tok[128];
-  __shared__ float s_gate[128];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * 128;
-  const int c0 = blockIdx.y * 64;
-  if (tid < 64) {
-    int beg[4], n[4], pad[4], sum = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = lane * 4 + u;
-      beg[u] = e < E ? offsets[e] : 0;
-      n[u] = e < E ? offsets[e + 1] - beg[u] : 0;
-      pad[u] = (n[u] + 63) & ~63;
-      sum += pad[u];
-    }
-    const int excl = wave_exclusive_scan(sum);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t ph = p0 + 64 * h;
-      int src = 0, valid = 0, found = 0, run = excl;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (ph >= run && ph < run + pad[u]) {
-          found = 1;
-          src = beg[u] + static_cast<int>(ph - run);
-          valid = min(64, n[u] - static_cast<int>(ph - run));
-        }
-        run += pad[u];
-      }
-      const uint64_t who = __ballot(found);
-      if (who) {
-        const int l0 = __ffsll(static_cast<long long>(who)) - 1;
-        src = __shfl(src, l0, kWave);
-        valid = __shfl(valid, l0, kWave);
-      } else {
-        src = 0;
-        valid = 0;
-      }
-      if (lane == 0) {
-        s_src[h] = src;
-        s_valid[h] = valid;
-      }
-    }
-  }
-  __syncthreads();
-  if (tid < 128) {  // row tid: its token and gate (rows past an expert's end: gate 0)
-    const int h = tid >> 6, rr = tid & 63;
-    const bool ok = rr < s_valid[h];
-    const int rs = ok ? s_src[h] + rr : 0;
-    s_tok[tid] = ok ? token_of_row[rs] : 0;
-    s_gate[tid] = ok ? gate_of_row[rs] : 0.0f;
-  }
-  __syncthreads();
-  // 128 rows x 64 columns of dy: 8 lanes per row, 32 rows per pass.
-  const int ch = tid & 7;
-  uint4 raw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = i * 32 + (tid >> 3);
-    raw[i] = ld16(dy + static_cast<int64_t>(s_tok[r]) * C + c0 + ch * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = i * 32 + (tid >> 3), h = r >> 6, rr = r & 63;
-    const bool ok = rr < s_valid[h];
-    const float g = s_gate[r];
-    float f[8];
-    unpack16(raw[i], f);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) f[u] = ok ? g * f[u] : 0.0f;
-    *reinterpret_cast<float4*>(&tile[r][ch * 8]) = make_float4(f[0], f[1], f[2], f[3]);
-    *reinterpret_cast<float4*>(&tile[r][ch * 8 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
-  }
-  __syncthreads();
-  {
-    const int col = tid & 63, block = tid >> 6;
-    float v[32];
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = tile[block * 32 + i][col];
-    const int code = mx_encode_block(v, w);
-    uint4* d = reinterpret_cast<uint4*>(&qt[col][block * 32]);
-    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    if (p0 + block * 32 < P) {
-      const int64_t sb = (p0 >> 6) + (block >> 1);
-      s[(sb * C + c0 + col) * 2 + (block & 1)] = static_cast<uint8_t>(code);
-    }
-  }
-  __syncthreads();
-  const int64_t pvalid = min(static_cast<int64_t>(128), P - p0);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = i * 32 + (tid >> 3), c16 = tid & 7;
-    if (c16 * 16 < pvalid)
-      *reinterpret_cast<uint4*>(q + static_cast<int64_t>(c0 + row) * P + p0 + c16 * 16) =
-          *reinterpret_cast<const uint4*>(&qt[row][c16 * 16]);
-  }
-}
-
 hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gate, const int32_t* row_of_slot,
                                  const int32_t* token_of_row, const int32_t* offsets, int T, int d, int E, int k,
                                  void* d_o, MxDoutImage d_o_mx, float* dgate, hipStream_t s) {
@@ -666,9 +714,11 @@ hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gat
     return hipGetLastError();
   });
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dout_tmajor_kernel, dim3(static_cast<unsigned>(P / 128 + (P % 128 ? 1 : 0)), d / 64), dim3(256),
-                     0, s, static_cast<const bf16_t*>(dy), d_o_mx.gate_of_row, token_of_row, offsets, E, d, P,
-                     d_o_mx.t.q, d_o_mx.t.s);
+  // dO along each expert's tokens, rebuilt from dy and the gates the pass
+  // above wrote.
+  hipLaunchKernelGGL((row_images_kernel<true, false>), row_images_grid(d, P), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(dy), d_o_mx.gate_of_row, token_of_row, offsets, E, d,
+                     static_cast<int>(S), P, nullptr, nullptr, nullptr, d_o_mx.t.q, d_o_mx.t.s);
   return hipGetLastError();
 }
 

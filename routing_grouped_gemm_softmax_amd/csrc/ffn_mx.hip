@@ -181,7 +181,7 @@ hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s) {
   // save buffer) for the backward's dXp GEMM.
   uint8_t *xq = w.xq, *xs = w.xs;
   if (a.xp_mx != nullptr) {  // written by the dispatch pass
-    const MxImage im = mx_image(a.xp_mx, S, d);
+    const MxImage im = mx_row_images(a.xp_mx, S, d, E).k;
     xq = im.q;
     xs = im.s;
   } else {
@@ -235,12 +235,19 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
     // H images. Only the layouts that GEMM reads are rebuilt (the dgrad weight
     // copies are in the save buffer).
     const RecWs r = carve_rec(static_cast<char*>(ws) + bwd_bytes, S, d, f, E, nullptr);
-    TRY(launch_mx_kmajor(a.xp, S, d, 1, 0, r.xq, 0, r.xs, 0, s));
+    uint8_t *xq = r.xq, *xs = r.xs;
+    if (a.xp_mx != nullptr) {  // the dispatch pass's image, as the forward read it
+      const MxImage im = mx_row_images(a.xp_mx, S, d, E).k;
+      xq = im.q;
+      xs = im.s;
+    } else {
+      TRY(launch_mx_kmajor(a.xp, S, d, 1, 0, r.xq, 0, r.xs, 0, s));
+    }
     TRY(launch_mx_tgroup(a.w_gate, d, f, nullptr, E, wsz, r.wgq, d, wsz, r.wgs, wsz / 32, s, nullptr, nullptr));
     TRY(launch_mx_tgroup(a.w_up, d, f, nullptr, E, wsz, r.wuq, d, wsz, r.wus, wsz / 32, s, nullptr, nullptr));
     GemmParams p{};
     p.offsets = a.offsets; p.E = E; p.S = S; p.f = f;
-    p.a = r.xq; p.lda = d; p.as = r.xs; p.as_slab = 2LL * S;
+    p.a = xq; p.lda = d; p.as = xs; p.as_slab = 2LL * S;
     p.b0 = r.wgq; p.b1 = r.wuq; p.ldb = d; p.bstride = wsz;
     p.bs0 = r.wgs; p.bs1 = r.wus; p.bs_slab = 2LL * f; p.bs_estride = wsz / 32;
     p.c0 = a.G; p.c1 = a.U; p.ldc = f; p.N = 2 * f; p.K = d;
@@ -300,11 +307,19 @@ hipError_t launch_ffn_mx_bwd(const FfnArgs& a, void* ws, hipStream_t s) {
     p.c0 = a.dw_down; p.c1 = nullptr; p.ldc = d; p.cstride = static_cast<int64_t>(f) * d; p.M = f; p.N = d; p.f = d;
     TRY(launch_mx_wgrad(p, s));
   }
-  {  // [dW_gate | dW_up][e] = q(Xp_e)^T q(dGU_e)
-    TRY(launch_mx_tgroup(a.xp, S, d, w.blk, 1, 0, w.xt, P, 0, w.xts, 0, s));
+  {  // [dW_gate | dW_up][e] = q(Xp_e)^T q(dGU_e); q(Xp) along the tokens
+     // came from the dispatch pass (else from xp here).
+    uint8_t *xt = w.xt, *xts = w.xts;
+    if (a.xp_mx != nullptr) {
+      const MxImage im = mx_row_images(a.xp_mx, S, d, E).t;
+      xt = im.q;
+      xts = im.s;
+    } else {
+      TRY(launch_mx_tgroup(a.xp, S, d, w.blk, 1, 0, w.xt, P, 0, w.xts, 0, s));
+    }
     GemmParams p{};
     p.offsets = w.poff; p.E = E; p.S = S;
-    p.a = w.xt; p.lda = P; p.as = w.xts; p.as_slab = 2LL * d;
+    p.a = xt; p.lda = P; p.as = xts; p.as_slab = 2LL * d;
     p.b0 = w.dgut; p.ldb = P; p.bs0 = w.dguts; p.bs_slab = 4LL * f;
     p.c0 = a.dw_gate; p.c1 = a.dw_up; p.ldc = f; p.cstride = static_cast<int64_t>(d) * f; p.M = d; p.N = 2 * f; p.f = f;
     TRY(launch_mx_wgrad(p, s));

@@ -30,8 +30,9 @@ struct FfnArgs {
   // token-major operand (ffn_mx_save_extra bytes). G, U are then the blocked
   // planes (ffn_mx_gu_plane bytes each) and H is unused.
   void* mx_save;
-  // MXFP8, optional: the operand images (mx_image layout) of xp and d_o that
-  // moe_dispatch / moe_combine_bwd already wrote; NULL = quantise here.
+  // MXFP8, optional: the operand images of xp (mx_row_images layout) and d_o
+  // (mx_dout_image layout) that moe_dispatch / moe_combine_bwd already wrote;
+  // NULL = quantise here. With xp_mx, xp is not read (and may be null).
   const void* xp_mx;
   const void* d_o_mx;
   // Activation recompute: the forward keeps G, U, H (MXFP8: G, U and H's
@@ -103,34 +104,45 @@ inline MxImage mx_image(const void* base, int64_t rows, int64_t cols) {
   return MxImage{p, p + mx_part_bytes(static_cast<size_t>(rows) * static_cast<size_t>(cols))};
 }
 
-// Dispatch and combine backward that also write the MXFP8 image of their
-// output rows (xp bf16, d_o fp32) from the values they already hold; d =
-// cols, S = rows.
+// The two MXFP8 images of an MXFP8 layer's expert-ordered row matrix
+// [S][d] (xp, dO), one per GEMM that reads it: the K-major image (mx_image
+// layout, a row operand) followed by the token-major one (codes [d][P],
+// scales [P/64][d][2], every expert's rows padded to a multiple of 64
+// starting at its padded offset: a weight gradient's operand).
+inline int64_t mx_padded_rows(int64_t S, int64_t E) { return (S + 63 * E + 63) / 64 * 64; }
+struct MxRowImages {
+  MxImage k;  // [S][d] along d
+  MxImage t;  // [d][P] along each expert's tokens
+};
+inline size_t mx_row_images_bytes(int64_t S, int64_t d, int64_t E) {
+  const size_t pd = static_cast<size_t>(mx_padded_rows(S, E)) * static_cast<size_t>(d);
+  return mx_image_bytes(S, d) + mx_part_bytes(pd) + mx_part_bytes(pd / 32);
+}
+inline MxRowImages mx_row_images(const void* base, int64_t S, int64_t d, int64_t E) {
+  uint8_t* t = static_cast<uint8_t*>(const_cast<void*>(base)) + mx_image_bytes(S, d);
+  const size_t pd = static_cast<size_t>(mx_padded_rows(S, E)) * static_cast<size_t>(d);
+  return MxRowImages{mx_image(base, S, d), MxImage{t, t + mx_part_bytes(pd)}};
+}
+
+// Dispatch that writes xp's two images (and xp's bf16 rows unless xp is
+// null) from x directly; d = cols, S = T k rows.
 hipError_t launch_dispatch_mx(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
                               int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
-                              int32_t* token_of_row, void* xp, MxImage xp_mx, void* ws, hipStream_t s);
-// The MXFP8 image of an MXFP8 layer's dO: the K-major image (mx_image layout,
-// the down-dgrad GEMM's operand) followed by the token-major one (codes [d][P],
-// scales [P/64][d][2], every expert's rows padded to a multiple of 64 starting
-// at its padded offset: the W_down weight gradient's operand).
-inline int64_t mx_padded_rows(int64_t S, int64_t E) { return (S + 63 * E + 63) / 64 * 64; }
-// A third part holds the gate of every expert row ([S] fp32), which the
-// first pass writes for the second.
+                              int32_t* token_of_row, void* xp, MxRowImages xp_mx, void* ws, hipStream_t s);
+// dO's images, then the gate of every expert row ([S] fp32), which the
+// combine backward's first pass writes for its second.
 inline size_t mx_dout_image_bytes(int64_t S, int64_t d, int64_t E) {
-  const size_t pd = static_cast<size_t>(mx_padded_rows(S, E)) * static_cast<size_t>(d);
-  return mx_image_bytes(S, d) + mx_part_bytes(pd) + mx_part_bytes(pd / 32) + mx_part_bytes(static_cast<size_t>(S) * 4);
+  return mx_row_images_bytes(S, d, E) + mx_part_bytes(static_cast<size_t>(S) * 4);
 }
 struct MxDoutImage {
-  MxImage k;         // [S][d] along d
-  MxImage t;         // [d][P] along each expert's tokens
+  MxImage k;           // [S][d] along d
+  MxImage t;           // [d][P] along each expert's tokens
   float* gate_of_row;  // [S]
 };
 inline MxDoutImage mx_dout_image(const void* base, int64_t S, int64_t d, int64_t E) {
-  uint8_t* p = static_cast<uint8_t*>(const_cast<void*>(base));
-  const size_t pd = static_cast<size_t>(mx_padded_rows(S, E)) * static_cast<size_t>(d);
-  uint8_t* t = p + mx_image_bytes(S, d);
-  uint8_t* g = t + mx_part_bytes(pd) + mx_part_bytes(pd / 32);
-  return MxDoutImage{mx_image(base, S, d), MxImage{t, t + mx_part_bytes(pd)}, reinterpret_cast<float*>(g)};
+  const MxRowImages r = mx_row_images(base, S, d, E);
+  uint8_t* g = static_cast<uint8_t*>(const_cast<void*>(base)) + mx_row_images_bytes(S, d, E);
+  return MxDoutImage{r.k, r.t, reinterpret_cast<float*>(g)};
 }
 // d_o (fp32) may be null: then only the images are written. dO = gate * dy
 // in fp32 is decided once per element and both images encode that value.
@@ -141,12 +153,12 @@ hipError_t launch_combine_bwd_mx(const void* dy, const void* o, const float* gat
 
 // Dispatch whose workspace is the library's own device array (one per GPU,
 // dispatch_noalloc_max() bytes) instead of a caller buffer: no allocation.
-// xp_mx.q == nullptr: no MXFP8 image. Returns hipErrorInvalidValue when the
+// xp_mx.k.q == nullptr: no MXFP8 images. Returns hipErrorInvalidValue when the
 // shape needs more than the array holds, or when hipGetSymbolAddress fails.
 size_t dispatch_noalloc_max();
 hipError_t launch_dispatch_noalloc(const void* x, const int32_t* topk_idx, int elem_bytes, int T, int d, int E,
                                    int k, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
-                                   int32_t* token_of_row, void* xp, MxImage xp_mx, hipStream_t s);
+                                   int32_t* token_of_row, void* xp, MxRowImages xp_mx, hipStream_t s);
 
 // MXFP8 (mxfp8.hip)
 hipError_t launch_mxfp8_quantize(const void* in, int64_t rows, int64_t cols, int axis, uint8_t* q,

@@ -15,10 +15,12 @@ from . import _lib as L
 class MoELayer:
     def __init__(self, T: int, d: int, E: int, k: int, f: int, dtype: str = "bf16",
                  learned_routing: bool = True, device: str = "cuda", mx_images: bool = True,
-                 recompute: bool = False):
-        """``mx_images`` (MXFP8 layers): dispatch and combine-backward also write
-        the MXFP8 images of xp and d_o, which the grouped FFN calls then read;
-        False leaves the quantisation of both to the FFN calls.
+                 recompute: bool = False, keep_xp: bool = False):
+        """``mx_images`` (MXFP8 layers): dispatch and combine-backward write
+        the MXFP8 operands of xp and d_o, which the grouped FFN calls then
+        read; False leaves the quantisation of both to the FFN calls. With
+        the images the layer keeps neither xp's bf16 rows (unless
+        ``keep_xp``) nor an fp32 d_o.
         ``recompute``: save no G, U, H (MXFP8: G, U and H's token-major
         operand) between forward and backward; the backward recomputes them
         (MOE_FLAG_RECOMPUTE)."""
@@ -50,9 +52,9 @@ class MoELayer:
         self.offsets = buf(E + 1, dtype=i32)
         self.row_of_slot = buf(T, k, dtype=i32)
         self.token_of_row = buf(S, dtype=i32)
-        self.xp = buf(S, d)
         use_mx = mx_images and self.shape.dtype == L.MOE_MXFP8
-        self.xp_mx = torch.empty(L.mx_image_size(S, d), dtype=torch.uint8, device=dev) if use_mx else None
+        self.xp = buf(S, d) if keep_xp or not use_mx else None
+        self.xp_mx = torch.empty(L.mx_xp_image_size(self.shape), dtype=torch.uint8, device=dev) if use_mx else None
         self.d_o_mx = torch.empty(L.mx_dout_image_size(self.shape), dtype=torch.uint8, device=dev) if use_mx else None
         self.save = torch.empty(L.save_size(self.shape), dtype=torch.uint8, device=dev)
         self.ws_ffn_fwd = ws(L.MOE_OP_FFN_FWD)
@@ -144,7 +146,7 @@ class MoELayer:
         mark("moe_combine_bwd")
         L.moe_grouped_ffn_bwd(self.d_o, self.xp, self.w_gate, self.w_up, self.w_down, self.offsets, s, self.save,
                               self.dxp, self.dw_gate, self.dw_up, self.dw_down, self.ws_ffn_bwd, stream,
-                              d_o_mx=self.d_o_mx)
+                              d_o_mx=self.d_o_mx, xp_mx=self.xp_mx)
         mark("moe_grouped_ffn_bwd")
         if self.learned:
             L.moe_route_bwd(self.x, self.w_router, self.topk_idx, self.topk_gate, self.dgate, s, self.dlogits,

@@ -109,6 +109,11 @@ int main() {
                   reinterpret_cast<uint8_t*>(buf(12288 + 16)), buf(8192), big, s), MOE_ERR_MISALIGNED);
   RC(moe_dispatch(buf(0), ibuf(256), &mx, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), buf(4096),
                   reinterpret_cast<uint8_t*>(buf(12288)), buf(8192), big, s), MOE_OK);
+  // With xp's MXFP8 operands the bf16 rows are optional; without them not.
+  RC(moe_dispatch(buf(0), ibuf(256), &mx, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), nullptr,
+                  reinterpret_cast<uint8_t*>(buf(12288)), buf(8192), big, s), MOE_OK);
+  RC(moe_dispatch(buf(0), ibuf(256), &mx, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), nullptr, nullptr,
+                  buf(8192), big, s), MOE_ERR_INVALID_ARG);
   // moe_dispatch_noalloc: no workspace argument; shapes whose dispatch
   // workspace exceeds the library's 1 MiB array are refused on the host.
   RC(moe_dispatch_noalloc(buf(0), ibuf(256), &ok, ibuf(512), ibuf(768), ibuf(1024), ibuf(2048), buf(4096), nullptr,
@@ -144,11 +149,11 @@ int main() {
   const size_t wsb = moe_workspace_size(MOE_OP_FFN_BWD, &ok);
   std::vector<char> wsv(wsb + 256);
   char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(wsv.data()) + 255) & ~uintptr_t(255));
-  RC(moe_grouped_ffn_bwd(buf(0), nullptr, buf(256), buf(512), buf(768), buf(1024), ibuf(1280), &ok, sv, buf(2048),
+  RC(moe_grouped_ffn_bwd(buf(0), nullptr, buf(256), nullptr, buf(512), buf(768), buf(1024), ibuf(1280), &ok, sv, buf(2048),
                          buf(2304), buf(2560), buf(2816), ws, wsb, s), MOE_OK);
-  RC(moe_grouped_ffn_bwd(buf(0), nullptr, buf(256), buf(512), buf(768), buf(1024), ibuf(1280), &ok, sv, buf(2048),
+  RC(moe_grouped_ffn_bwd(buf(0), nullptr, buf(256), nullptr, buf(512), buf(768), buf(1024), ibuf(1280), &ok, sv, buf(2048),
                          buf(2304), buf(2560), buf(2816), ws, wsb - 1, s), MOE_ERR_WORKSPACE);
-  RC(moe_grouped_ffn_bwd(buf(0), nullptr, buf(256), buf(512), buf(768), buf(1024), ibuf(1280), &ok, sv, nullptr,
+  RC(moe_grouped_ffn_bwd(buf(0), nullptr, buf(256), nullptr, buf(512), buf(768), buf(1024), ibuf(1280), &ok, sv, nullptr,
                          buf(2304), buf(2560), buf(2816), ws, wsb, s), MOE_ERR_INVALID_ARG);
   // Recompute layers save nothing: the FFN calls accept a NULL save buffer.
   const size_t wsr = moe_workspace_size(MOE_OP_FFN_FWD, &rec);
@@ -185,6 +190,9 @@ int main() {
                      fbuf(2048), s), MOE_ERR_INVALID_ARG);
   EXPECT(moe_mx_dout_image_size(&mx) != BAD && moe_mx_dout_image_size(&mx) > moe_mx_image_size(mx.T * mx.k, mx.d));
   EXPECT(moe_mx_dout_image_size(&ok) == BAD);
+  EXPECT(moe_mx_xp_image_size(&mx) != BAD && moe_mx_xp_image_size(&mx) < moe_mx_dout_image_size(&mx) &&
+         moe_mx_xp_image_size(&mx) > moe_mx_image_size(mx.T * mx.k, mx.d));
+  EXPECT(moe_mx_xp_image_size(&ok) == BAD);
 
   // router backward and dispatch backward
   RC(moe_route_bwd(buf(0), buf(256), ibuf(512), fbuf(768), fbuf(1024), &ok, fbuf(2048), buf(4096), buf(8192), big,

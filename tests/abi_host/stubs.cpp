@@ -70,10 +70,10 @@ hipError_t launch_dispatch_bwd(const void*, const int32_t*, const float*, const 
                                int k, void*, void*, hipStream_t) { return hit(T, d, E, k); }
 hipError_t launch_load_stats(const int32_t*, int E, double*, hipStream_t) { return hit(0, 0, E); }
 hipError_t launch_dispatch_mx(const void*, const int32_t*, int T, int d, int E, int k, int32_t*, int32_t*, int32_t*,
-                              int32_t*, void*, MxImage, void*, hipStream_t) { return hit(T, d, E, k); }
+                              int32_t*, void*, MxRowImages, void*, hipStream_t) { return hit(T, d, E, k); }
 size_t dispatch_noalloc_max() { return size_t(1) << 20; }
 hipError_t launch_dispatch_noalloc(const void*, const int32_t*, int, int T, int d, int E, int k, int32_t*, int32_t*,
-                                   int32_t*, int32_t*, void*, MxImage, hipStream_t) { return hit(T, d, E, k); }
+                                   int32_t*, int32_t*, void*, MxRowImages, hipStream_t) { return hit(T, d, E, k); }
 hipError_t launch_combine_bwd_mx(const void*, const void*, const float*, const int32_t*, const int32_t*,
                                  const int32_t*, int T, int d, int E, int k, void* d_o, MxDoutImage, float*,
                                  hipStream_t) {

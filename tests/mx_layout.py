@@ -63,6 +63,15 @@ def dout_pieces(S, d, E):
     return {"doq": (off[0], S * d), "dos": (off[1], S * d // 32), "dot": (off[2], P * d), "dots": (off[3], P * d // 32)}
 
 
+def xp_pieces(S, d, E):
+    """The xp operand buffer of an MXFP8 layer (moe_dispatch's xp_mx): the
+    K-major image (xq codes [S][d], xs scales [d/64][S][2]) then the
+    token-major one: xt (codes [d][P]), xts (scales [P/64][d][2]); the
+    layout of the first two parts of the d_o buffer."""
+    p = dout_pieces(S, d, E)
+    return {"xq": p["doq"], "xs": p["dos"], "xt": p["dot"], "xts": p["dots"]}
+
+
 def dout_f32(gate, dy, row_of_slot, token_of_row):
     """The fp32 dO rows an MXFP8 layer encodes, in expert-sorted row order:
     gate(t, j) * dy[t] for the slot (t, j) of each row, one fp32 rounding of

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
     for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
                        (-3, b"MOE_ERR_MISALIGNED"), (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == name
@@ -103,7 +103,7 @@ def test_workspace_too_small():
     assert rc == L.MOE_ERR_MISALIGNED  # ws must be 256-byte aligned
     rc = lib.moe_grouped_ffn_fwd(p, None, p, p, p, p, ctypes.byref(s), p, 10, p, None, 0, None)
     assert rc == L.MOE_ERR_WORKSPACE
-    rc = lib.moe_grouped_ffn_bwd(p, None, p, p, p, p, p, ctypes.byref(s), p, p, p, p, p, p, 10, None)
+    rc = lib.moe_grouped_ffn_bwd(p, None, p, None, p, p, p, p, ctypes.byref(s), p, p, p, p, p, p, 10, None)
     assert rc == L.MOE_ERR_WORKSPACE
     rc = lib.moe_route_bwd(p, p, p, p, p, ctypes.byref(s), p, p, p, 0, None)
     assert rc == L.MOE_ERR_WORKSPACE
@@ -149,10 +149,26 @@ def test_mx_image_arguments_are_checked_on_the_host():
     rc = lib.moe_combine_bwd(p, p, p, p, None, p, ctypes.byref(mx), None, p, p, None)
     assert rc == L.MOE_ERR_INVALID_ARG and "token_of_row" in L.last_error()
     assert L.mx_dout_image_size(mx) > L.mx_image_size(mx.T * mx.k, mx.d)
+    # xp's operands: the image along d, then the one along each expert's
+    # tokens (every expert's rows padded to 64), the layout of d_o's first two.
+    S, P = mx.T * mx.k, (mx.T * mx.k + 63 * mx.E + 63) // 64 * 64
+    part = lambda n: (n + 16 + 255) // 256 * 256  # noqa: E731
+    assert L.mx_xp_image_size(mx) == L.mx_image_size(S, mx.d) + part(P * mx.d) + part(P * mx.d // 32)
+    assert L.mx_dout_image_size(mx) == L.mx_xp_image_size(mx) + part(S * 4)
+    assert lib.moe_mx_xp_image_size(ctypes.byref(bf)) == ctypes.c_size_t(-1).value
+    # xp may be NULL only beside its images.
+    rc = lib.moe_dispatch(p, p, ctypes.byref(mx), p, p, p, p, None, None, p, ws, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "xp_out" in L.last_error()
+    rc = lib.moe_grouped_ffn_fwd(None, None, p, p, p, p, ctypes.byref(mx), p, 1 << 40, p, p, 1 << 40, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "xp" in L.last_error()
+    rc = lib.moe_grouped_ffn_bwd(p, None, None, None, p, p, p, p, ctypes.byref(mx), p, p, p, p, p, p, 1 << 40, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "xp" in L.last_error()
+    rc = lib.moe_grouped_ffn_bwd(p, None, None, p, p, p, p, p, ctypes.byref(bf), p, p, p, p, p, p, 1 << 40, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "MXFP8" in L.last_error()
     rc = lib.moe_grouped_ffn_fwd(p, p, p, p, p, p, ctypes.byref(bf), p, 1 << 40, p, p, 1 << 40, None)
     assert rc == L.MOE_ERR_INVALID_ARG
-    rc = lib.moe_grouped_ffn_bwd(p, ctypes.c_void_p(0x100040), p, p, p, p, p, ctypes.byref(mx), p, p, p, p, p, p,
-                                 1 << 40, None)
+    rc = lib.moe_grouped_ffn_bwd(p, ctypes.c_void_p(0x100040), p, None, p, p, p, p, ctypes.byref(mx), p, p, p, p, p,
+                                 p, 1 << 40, None)
     assert rc == L.MOE_ERR_MISALIGNED
 
 

@@ -31,7 +31,8 @@ def test_algorithmic_work_formulas():
     wm = WORKLOADS["mxfp8_balanced"]
     Sm = wm.T * wm.k
     # the MXFP8 images of xp and d_o: one byte per element plus one per 32
-    assert mx["moe_dispatch"]["bytes"] == (1 + wm.k) * wm.T * wm.d * 2 + Sm * wm.d + Sm * wm.d // 32
+    # x read once; xp written only as its two MXFP8 operands
+    assert mx["moe_dispatch"]["bytes"] == wm.T * wm.d * 2 + 2 * (Sm * wm.d + Sm * wm.d // 32)
     assert "moe_route" not in mx
     rc = bench.algorithmic_work(wl, recompute=True)
     assert rc["moe_grouped_ffn_bwd"]["flops_recompute"] == 4 * S * d * f

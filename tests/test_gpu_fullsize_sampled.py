@@ -10,7 +10,8 @@ O, dO, dG, dU, every dXp row and the expert's three weight gradients) - for
 the Zipf layer the coldest non-empty expert, a median one and the hottest
 one (about 12k rows: the longest K of the weight-gradient GEMMs and the
 cost-cut schedule), for the MXFP8 layer two experts; y and dx of 24 random
-tokens through all k of their experts; the xp bytes of 512 random rows. For
+tokens through all k of their experts; the xp bytes of 512 random rows (for
+the MXFP8 layer, which keeps xp only as E4M3 operands, their codes). For
 the MXFP8 layer also stage by stage (the oracle fed the device's stored fp32
 intermediates, 2e-2) and, byte for byte, the E4M3 images of the two experts'
 rows (K-major H and dG | dU; token-major H, dO, Xp, dG | dU). Each piece is
@@ -186,9 +187,11 @@ def _check_expert_images(F, e, rows, dv, xp, dgdu):
                     atol=atol)
     ML.check_token_major(L.d_o_mx, ML.dout_pieces(S, d, E), "dot", "dots", dv["dO"], F.offsets, "q(dot)",
                          experts=[e], S=S, C=d)
-    for q, s_, vals, near in (("xt", "xts", xp, False), ("dgut", "dguts", dgu, True)):
-        ML.check_token_major(L.ws_ffn_bwd, pb, q, s_, vals, F.offsets, f"q({q})", experts=[e], S=S,
-                             C=vals.shape[1], near=near, atol=atol if near else None)
+    # Xp along the tokens: written by the dispatch pass from x.
+    ML.check_token_major(L.xp_mx, ML.xp_pieces(S, d, E), "xt", "xts", xp, F.offsets, "q(xt)", experts=[e], S=S,
+                         C=d)
+    ML.check_token_major(L.ws_ffn_bwd, pb, "dgut", "dguts", dgu, F.offsets, "q(dgut)", experts=[e], S=S, C=2 * f,
+                         near=True, atol=atol)
 
 
 def _check_rows_fwd(F, e, rows):
@@ -235,7 +238,19 @@ def _run_checks(name):
     rng = np.random.default_rng(0)
     S = wl.T * wl.k
     rows = np.sort(rng.choice(S, 512, replace=False))
-    np.testing.assert_array_equal(_rows(L.xp, rows), F.xp(rows))
+    if L.xp is not None:
+        np.testing.assert_array_equal(_rows(L.xp, rows), F.xp(rows))
+    else:
+        # MXFP8: xp exists only as its two E4M3 operands; these rows of the
+        # one along d, byte for byte (each row is quantised on its own).
+        qo, _ = ML.xp_pieces(S, wl.d, wl.E)["xq"]
+        so, _ = ML.xp_pieces(S, wl.d, wl.E)["xs"]
+        sel = torch.as_tensor(rows, device=L.xp_mx.device)
+        codes = host(L.xp_mx[qo:qo + S * wl.d].view(S, wl.d)[sel])
+        sc = host(L.xp_mx[so:so + S * wl.d // 32].view(wl.d // 64, S, 2)[:, sel, :]).transpose(1, 0, 2)
+        rq, rs = O.mx_quantize(F.xp(rows), "cols")
+        np.testing.assert_array_equal(codes, rq)
+        np.testing.assert_array_equal(sc.reshape(len(rows), -1), rs)
     empty = np.nonzero(F.counts == 0)[0]
     for e in empty:
         assert not host(L.dw_gate[e]).any() and not host(L.dw_up[e]).any() and not host(L.dw_down[e]).any()

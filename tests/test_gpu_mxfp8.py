@@ -102,11 +102,14 @@ def _check_images(layer, off, xp, H, d_o, dg, du):
             rq, rs = O.mx_quantize(vals, "cols")
             np.testing.assert_array_equal(q, rq, err_msg=f"{name} image codes")
             np.testing.assert_array_equal(sc, rs, err_msg=f"{name} image scales")
-    # Token-major weight-gradient operands.
+    # Token-major weight-gradient operands (Xp's from the dispatch pass when
+    # the layer has the images, else from the FFN backward's workspace).
     ML.check_token_major(layer.d_o_mx, ML.dout_pieces(S, d, E), "dot", "dots", d_o, off, "q(dot)")
-    for q, s_, vals, near in (("xt", "xts", xp, False), ("dgut", "dguts", dgu, True)):
-        ML.check_token_major(layer.ws_ffn_bwd, pb, q, s_, vals, off, f"q({q})", near=near,
-                             atol=atol if near else None)
+    if layer.xp_mx is not None:
+        ML.check_token_major(layer.xp_mx, ML.xp_pieces(S, d, E), "xt", "xts", xp, off, "q(xt)")
+    else:
+        ML.check_token_major(layer.ws_ffn_bwd, pb, "xt", "xts", xp, off, "q(xt)")
+    ML.check_token_major(layer.ws_ffn_bwd, pb, "dgut", "dguts", dgu, off, "q(dgut)", near=True, atol=atol)
 
 
 @pytest.mark.parametrize("case", list(CASES))
@@ -122,7 +125,10 @@ def test_mxfp8_layer_matches_mx_oracle(case):
     np.testing.assert_array_equal(host(layer.counts), ref["counts"])
     np.testing.assert_array_equal(host(layer.offsets), ref["offsets"])
     np.testing.assert_array_equal(host(layer.row_of_slot), ref["row_of_slot"])
-    np.testing.assert_array_equal(host(layer.xp), inp["x"][ref["token_of_row"]])
+    np.testing.assert_array_equal(host(layer.token_of_row), ref["token_of_row"])
+    # With the operand images the layer keeps no bf16 xp: the dispatch writes
+    # xp only as its two E4M3 operands (checked byte for byte below).
+    assert layer.xp is None
 
     off = ref["offsets"]
     S, f = wl.T * wl.k, wl.f
@@ -230,12 +236,12 @@ def _image(buf, rows, cols):
 @pytest.mark.parametrize("over", [dict(T=384, d=384, E=16, f=128), dict(T=200, d=4224, E=8, f=128)],
                          ids=["ragged_empty_d384", "three_row_passes_d4224"])
 def test_dispatch_and_combine_bwd_mx_images(over):
-    """The MXFP8 images that moe_dispatch and moe_combine_bwd write (xp along
-    d; dO along d and along each expert's tokens, from the fp32 products
-    without storing them) carry the oracle's codes and scales of the values
-    bit for bit, and a layer that reads them gives bit-identical outputs to
-    one that stores fp32 dO and quantises xp and dO inside the grouped FFN
-    calls."""
+    """The MXFP8 operands that moe_dispatch and moe_combine_bwd write (xp and
+    dO, each along d and along each expert's tokens; dO from the fp32
+    products without storing them) carry the oracle's codes and scales of
+    the values bit for bit, with or without xp's bf16 rows beside them, and
+    layers that read them give bit-identical outputs to one that stores xp
+    and fp32 dO and quantises both inside the grouped FFN calls."""
     from routing_grouped_gemm_softmax_amd import MoELayer
     wl = WORKLOADS["bf16_zipf"].with_shape(dtype="mxfp8", **over)
     pop = [1, 0, 2, 1, 1, 0, 3, 1, 1, 1, 0, 1, 2, 1, 1, 0][:wl.E]
@@ -245,28 +251,37 @@ def test_dispatch_and_combine_bwd_mx_images(over):
     t = {n: dev(inp[n], bf) for n in ("x", "dy", "w_gate", "w_up", "w_down")}
     idx, gate = dev(inp["topk_idx"], torch.int32), dev(inp["topk_gate"], torch.float32)
     layers = {}
-    for fused in (True, False):
-        layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, "mxfp8", learned_routing=False, mx_images=fused)
+    for name, kw in (("rows", dict(keep_xp=True)), ("images", {}), ("plain", dict(mx_images=False))):
+        layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.f, "mxfp8", learned_routing=False, **kw)
         layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=idx, topk_gate=gate)
         layer.backward(t["dy"])
-        layers[fused] = layer
+        layers[name] = layer
     torch.cuda.synchronize()
-    a, b = layers[True], layers[False]
-    assert a.xp_mx is not None and b.xp_mx is None and a.d_o is None
+    a, c, b = layers["rows"], layers["images"], layers["plain"]
+    assert a.xp_mx is not None and c.xp_mx is not None and b.xp_mx is None
+    assert a.xp is not None and c.xp is None and a.d_o is None and c.d_o is None
     S, d = wl.T * wl.k, wl.d
-    # The fp32 dO the second layer stored is the product the first encoded,
+    off = host(a.offsets)
+    # xp's rows, when kept, are x gathered (the plain layer's own gather).
+    xp = inp["x"][host(a.token_of_row)].astype(np.float64)
+    np.testing.assert_array_equal(host(a.xp).astype(np.float64), xp)
+    assert torch.equal(a.xp, b.xp)
+    # The fp32 dO the plain layer stored is the product the others encoded,
     # and the host's fp32 product of the gate and dy reproduces it exactly.
     d_o = host(b.d_o).astype(np.float64)
     np.testing.assert_array_equal(d_o, ML.dout_f32(inp["topk_gate"], inp["dy"], host(a.row_of_slot),
                                                    host(a.token_of_row)))
-    for name, img, vals in (("xp", a.xp_mx, host(a.xp).astype(np.float64)), ("d_o", a.d_o_mx, d_o)):
-        q, s = _image(img, S, d)
-        rq, rs = O.mx_quantize(vals, "cols")
-        np.testing.assert_array_equal(q, rq, err_msg=f"{name} codes")
-        np.testing.assert_array_equal(s, rs, err_msg=f"{name} scales")
-    ML.check_token_major(a.d_o_mx, ML.dout_pieces(S, d, wl.E), "dot", "dots", d_o, host(a.offsets), "q(dot)")
-    for n in ("xp", "o", "y", "dgate", "dxp", "dw_gate", "dw_up", "dw_down", "dx"):
+    for lay in (a, c):
+        for name, img, vals in (("xp", lay.xp_mx, xp), ("d_o", lay.d_o_mx, d_o)):
+            q, s = _image(img, S, d)
+            rq, rs = O.mx_quantize(vals, "cols")
+            np.testing.assert_array_equal(q, rq, err_msg=f"{name} codes")
+            np.testing.assert_array_equal(s, rs, err_msg=f"{name} scales")
+        ML.check_token_major(lay.xp_mx, ML.xp_pieces(S, d, wl.E), "xt", "xts", xp, off, "q(xt)")
+        ML.check_token_major(lay.d_o_mx, ML.dout_pieces(S, d, wl.E), "dot", "dots", d_o, off, "q(dot)")
+    for n in ("o", "y", "dgate", "dxp", "dw_gate", "dw_up", "dw_down", "dx"):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
+        assert torch.equal(getattr(c, n), getattr(b, n)), n
 
 
 @pytest.mark.parametrize("sizes,cols", [([0, 37, 64, 1, 0, 198], 200), ([300], 512), ([5] * 40 + [0] * 3, 260)],
