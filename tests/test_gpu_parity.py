@@ -41,6 +41,12 @@ CASES = {
     # Eight experts get no rows.
     "bf16_wgrad_stream_short_tiles": ("bf16_zipf", dict(T=4096, d=512, E=128, k=2, f=256),
                                       [0 if e % 16 == 5 else 1 + e % 7 for e in range(128)]),
+    # 512 rows per expert on average with skewed loads: every expert's whole
+    # 256-row bands in 256 x 256 tiles, the rest in 128 x 256 tiles (two
+    # launches per row-ragged step): loads from 1991 rows (seven bands) down
+    # to 252 (a remainder only), and an empty expert.
+    "bf16_zipf_row_bands": ("bf16_zipf", dict(T=2048, d=256, E=16, f=256),
+                            [30, 9, 4, 2, 1, 1, 1, 1, 0, 1, 1, 1, 1, 1, 1, 1]),
     # The largest expert count and top-k the library takes, learned routing:
     # about 9 rows per expert, 16 router column blocks, eight slots per token.
     "bf16_max_E256_k8": ("bf16_e8", dict(T=300, d=128, E=256, k=8, f=128), None),
