@@ -334,67 +334,88 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
   const uint8_t* A = static_cast<const uint8_t*>(p.a);
   const uint32_t dump = __builtin_amdgcn_readfirstlane(lds_addr(smem + RING + 4 * kStreamStg));
 
-  // ---- HBM -> LDS: load L of slab kt of tile tc (empty descriptors if !live) --------------
-  auto issue = [&](const TileCoord& tc, int kt, bool live, uint32_t slot, auto L, auto w) {
-    constexpr int l = decltype(L)::value, W = decltype(w)::value;
+  // ---- HBM -> LDS ------------------------------------------------------------------------
+  // The load side's tile keeps its buffer descriptors from the tile's first k
+  // (empty once past the last tile): the A rows, the B rows (BWD_GU: both
+  // sources), and the scale rows' bases at slab 0. A slab then only adds its
+  // k offset to each lane's offset within the tile (row * ld + 16-byte chunk,
+  // fixed for the kernel) and moves the scale bases by whole slabs, instead
+  // of rebuilding every descriptor for every load.
+  struct LoadTile {
+    __amdgpu_buffer_rsrc_t ra, rb, rb1;  // rb1: BWD_GU's second source only
+    const uint8_t* sa;   // A scales at slab 0
+    const uint8_t* sb;   // B scales at slab 0 (BWD_GU: the first source's)
+    const uint8_t* sb1;  // BWD_GU: the second source's at its slab 0
+    int sa_n, sb_n;
+  };
+  auto load_tile = [&](const TileCoord& tc, bool live) -> LoadTile {
+    LoadTile t{};
     const int n0 = tc.nt * BN;
-    if constexpr (l < LM) {
-      if constexpr (MODE == WGRAD) {
-        const int64_t k0 = tc.row0 + static_cast<int64_t>(kt) * 64;
-        load_rows64<BM, W>(make_rsrc(A + tc.m0 * p.lda + k0, live ? BM * p.lda : 0), p.lda, slot, wave, lane, l);
-      } else {
-        const int valid = live ? min(BM, tc.row_end - tc.row0) : 0;
-        load_rows64<BM, W>(make_rsrc(A + static_cast<int64_t>(tc.row0) * p.lda + kt * 64,
-                                     static_cast<int64_t>(valid) * p.lda),
-                           p.lda, slot, wave, lane, l);
+    const uint8_t* B0 = static_cast<const uint8_t*>(p.b0);
+    if constexpr (MODE == WGRAD) {
+      t.ra = make_rsrc(A + tc.m0 * p.lda + tc.row0, live ? BM * p.lda : 0);
+      t.rb = make_rsrc(B0 + n0 * p.ldb + tc.row0, live ? BN * p.ldb : 0);
+      t.sa = p.as + static_cast<int64_t>(tc.row0 / 64) * p.as_slab + tc.m0 * 2;
+      t.sb = p.bs0 + static_cast<int64_t>(tc.row0 / 64) * p.bs_slab + n0 * 2;
+      t.sa_n = live ? BM * 2 : 0;
+      t.sb_n = live ? BN * 2 : 0;
+    } else {
+      const int valid = live ? min(BM, tc.row_end - tc.row0) : 0;
+      t.ra = make_rsrc(A + static_cast<int64_t>(tc.row0) * p.lda, static_cast<int64_t>(valid) * p.lda);
+      const int64_t boff = static_cast<int64_t>(tc.e) * p.bstride + static_cast<int64_t>(n0) * p.ldb;
+      t.rb = make_rsrc(B0 + boff, live ? static_cast<int64_t>(BN) * p.ldb : 0);
+      t.sa = p.as + tc.row0 * 2;
+      t.sb = p.bs0 + static_cast<int64_t>(tc.e) * p.bs_estride + n0 * 2;
+      if constexpr (MODE == BWD_GU) {
+        t.rb1 = make_rsrc(static_cast<const uint8_t*>(p.b1) + boff, live ? static_cast<int64_t>(BN) * p.ldb : 0);
+        t.sb1 = p.bs1 + static_cast<int64_t>(tc.e) * p.bs_estride + n0 * 2;
       }
+      // Whole dwords: an odd row count keeps its last row's scales.
+      t.sa_n = (valid * 2 + 3) & ~3;
+      t.sb_n = live ? BN * 2 : 0;
+    }
+    return t;
+  };
+  // Each lane's byte offset within a tile for A and B load q: row (q * 4 +
+  // wave) * 16 + lane / 4, its 16-byte chunk lane % 4 swizzled by the row.
+  uint32_t voa[LM], vob[LN];
+#pragma unroll
+  for (int q = 0; q < LM; ++q) {
+    const int row = (q * 4 + wave) * 16 + (lane >> 2);
+    voa[q] = static_cast<uint32_t>(row * p.lda + (((lane & 3) ^ swz_row(row)) << 4));
+  }
+#pragma unroll
+  for (int q = 0; q < LN; ++q) {
+    const int row = (q * 4 + wave) * 16 + (lane >> 2);
+    vob[q] = static_cast<uint32_t>(row * p.ldb + (((lane & 3) ^ swz_row(row)) << 4));
+  }
+
+  // Load L of slab kt of the load tile lt.
+  auto issue = [&](const LoadTile& lt, int kt, uint32_t slot, auto L, auto w) {
+    constexpr int l = decltype(L)::value, W = decltype(w)::value;
+    if constexpr (l < LM) {
+      load_lds16<W>(lt.ra, voa[l] + static_cast<uint32_t>(kt * 64), slot + (l * 4 + wave) * 16 * 64);
     } else if constexpr (l < LM + LN) {
       constexpr int q = l - LM;
-      const uint32_t tn = slot + TILE_M;
-      if constexpr (MODE == WGRAD) {
-        const int64_t k0 = tc.row0 + static_cast<int64_t>(kt) * 64;
-        load_rows64<BN, W>(make_rsrc(static_cast<const uint8_t*>(p.b0) + n0 * p.ldb + k0, live ? BN * p.ldb : 0),
-                           p.ldb, tn, wave, lane, q);
-      } else {  // B stored [n][k] per expert
-        const uint8_t* src = static_cast<const uint8_t*>(p.b0);
-        int ks = kt;
-        if constexpr (MODE == BWD_GU) {
-          if (kt * 64 >= p.f) { src = static_cast<const uint8_t*>(p.b1); ks = kt - p.f / 64; }
-        }
-        load_rows64<BN, W>(make_rsrc(src + static_cast<int64_t>(tc.e) * p.bstride + static_cast<int64_t>(n0) * p.ldb +
-                                         ks * 64,
-                                     live ? static_cast<int64_t>(BN) * p.ldb : 0),
-                           p.ldb, tn, wave, lane, q);
+      const uint32_t dst = slot + TILE_M + (q * 4 + wave) * 16 * 64;
+      if constexpr (MODE == BWD_GU) {
+        const bool second = kt * 64 >= p.f;
+        load_lds16<W>(second ? lt.rb1 : lt.rb, vob[q] + static_cast<uint32_t>((second ? kt - p.f / 64 : kt) * 64),
+                      dst);
+      } else {
+        load_lds16<W>(lt.rb, vob[q] + static_cast<uint32_t>(kt * 64), dst);
       }
     } else {
       const uint32_t voff = static_cast<uint32_t>(lane * 16);
       if (wave == 0) {
-        const uint32_t sc = slot + TILE_M + TILE_N;
-        if constexpr (MODE == WGRAD) {
-          const int64_t k0 = tc.row0 + static_cast<int64_t>(kt) * 64;
-          load_lds16<W>(make_rsrc(p.as + (k0 / 64) * p.as_slab + tc.m0 * 2, live ? BM * 2 : 0), voff, sc);
-        } else {
-          // Whole dwords: an odd row count keeps its last row's scales.
-          const int valid = live ? min(BM, tc.row_end - tc.row0) : 0;
-          load_lds16<W>(make_rsrc(p.as + static_cast<int64_t>(kt) * p.as_slab + tc.row0 * 2, (valid * 2 + 3) & ~3),
-                        voff, sc);
-        }
+        load_lds16<W>(make_rsrc(lt.sa + static_cast<int64_t>(kt) * p.as_slab, lt.sa_n), voff,
+                      slot + TILE_M + TILE_N);
       } else if (wave == 1) {
-        const uint32_t sc = slot + TILE_M + TILE_N + kScaleArea;
-        if constexpr (MODE == WGRAD) {
-          const int64_t k0 = tc.row0 + static_cast<int64_t>(kt) * 64;
-          load_lds16<W>(make_rsrc(p.bs0 + (k0 / 64) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff, sc);
-        } else {
-          const uint8_t* ssrc = p.bs0;
-          int ks = kt;
-          if constexpr (MODE == BWD_GU) {
-            if (kt * 64 >= p.f) { ssrc = p.bs1; ks = kt - p.f / 64; }
-          }
-          load_lds16<W>(make_rsrc(ssrc + static_cast<int64_t>(tc.e) * p.bs_estride +
-                                      static_cast<int64_t>(ks) * p.bs_slab + n0 * 2,
-                                  live ? BN * 2 : 0),
-                        voff, sc);
+        const uint8_t* sb = lt.sb + static_cast<int64_t>(kt) * p.bs_slab;
+        if constexpr (MODE == BWD_GU) {
+          if (kt * 64 >= p.f) sb = lt.sb1 + static_cast<int64_t>(kt - p.f / 64) * p.bs_slab;
         }
+        load_lds16<W>(make_rsrc(sb, lt.sb_n), voff, slot + TILE_M + TILE_N + kScaleArea);
       } else {
         load_lds16<W>(make_rsrc(p.as, 0), voff, dump);
       }
@@ -493,6 +514,7 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
   int lj = 0, lkt = 0;
   TileCoord ltc = tile_at(0);
   int lnk = slabs_of(ltc);
+  LoadTile lt = load_tile(ltc, true);
   auto skip_empty = [&]() {
     while (lkt >= lnk && lj < ntiles) {
       lkt = 0;
@@ -500,6 +522,7 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
         ltc = tile_at(lj);
         lnk = slabs_of(ltc);
       }
+      lt = load_tile(ltc, lj < ntiles);
     }
   };
   skip_empty();
@@ -513,9 +536,7 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 #pragma unroll
   for (int s0 = 0; s0 < kStreamStages; ++s0) {
-    static_for<kLoads>([&](auto L) {
-      issue(ltc, lkt, lj < ntiles, ring + s0 * STAGE, L, std::integral_constant<int, 4>{});
-    });
+    static_for<kLoads>([&](auto L) { issue(lt, lkt, ring + s0 * STAGE, L, std::integral_constant<int, 4>{}); });
     advance();
   }
   // One slab: wait for slab gk+1, barrier, then slab gk's MFMAs on `cur` with
@@ -530,7 +551,6 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
     const int sc = gk % kStreamStages;
     const char* nxtp = smem + ((gk + 1) % kStreamStages) * STAGE;
     const uint32_t slot = ring + sc * STAGE;
-    const bool live = lj < ntiles;
     static_for<kLoads>([&](auto S) {
       constexpr int sg = decltype(S)::value;
       constexpr int m_lo = sg * kMfma / kLoads, m_hi = (sg + 1) * kMfma / kLoads;
@@ -539,7 +559,7 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
       static_for<f_hi - f_lo>([&](auto D) {
         read_frag(nxtp, nxt, std::integral_constant<int, f_lo + decltype(D)::value>{});
       });
-      issue(ltc, lkt, live, slot, S, std::integral_constant<int, 0>{});
+      issue(lt, lkt, slot, S, std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_barrier(0);
     });
     advance();
