@@ -67,91 +67,105 @@ __global__ __launch_bounds__(256) void gg_mx_kernel(GemmParams p) {
     const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, nt = tc.nt, m0 = tc.m0;
     const int n0 = nt * BN;
     // WGRAD: [row0, row_end) is the expert's padded K range (a multiple of 64).
-    const int nk = (MODE == WGRAD) ? (row_end - row0) / 64 : p.K / 64;
+    const int nk = __builtin_amdgcn_readfirstlane((MODE == WGRAD) ? (row_end - row0) / 64 : p.K / 64);
     const int64_t bexp = static_cast<int64_t>(e) * p.bstride;
     const int64_t bsexp = static_cast<int64_t>(e) * p.bs_estride;
     const uint8_t* A = static_cast<const uint8_t*>(p.a);
     const uint8_t* B0 = static_cast<const uint8_t*>(p.b0);
     const uint8_t* B1 = static_cast<const uint8_t*>(p.b1);
 
-    // ---- HBM -> LDS for slab kt (empty descriptors at or past the end) -------------------
+    // ---- HBM -> LDS for slab kt ------------------------------------------------------------
     // Each wave issues kLoads loads per slab: [0, LM) the M tile, [LM, LM + LN)
     // the N tile, then one 1 KB scale load: wave 0 the M side's scales, wave 1
     // the N side's (the gate half for FWD_GU), wave 2 the up half's for FWD_GU;
     // the remaining waves load nothing into their own area, so every wave
     // issues the same count (the vmcnt waits count them).
     constexpr int LM = BM / 64, LN = BN / 64, kLoads = LM + LN + 1;
+    // The tile's descriptors from its first k: the A rows, the B rows (FWD_GU
+    // and BWD_GU: both sources, FWD_GU's as two half tiles) and the scale rows'
+    // bases at slab 0. A slab only adds its k offset to each lane's offset
+    // within the tile and moves the scale bases by whole slabs; slabs at or
+    // past the end load from the empty descriptor.
+    constexpr int BR = MODE == FWD_GU ? BN / 2 : BN;  // rows per B source
+    constexpr int LB = BR / 64;                       // loads per B source
+    const __amdgpu_buffer_rsrc_t r0 = make_rsrc(p.as, 0);
+    __amdgpu_buffer_rsrc_t ra, rb, rb1 = r0;
+    const uint8_t *sa, *sb, *sb1 = nullptr;
+    int sa_n;
+    if constexpr (MODE == WGRAD) {
+      ra = make_rsrc(A + m0 * p.lda + row0, BM * p.lda);
+      rb = make_rsrc(B0 + n0 * p.ldb + row0, BN * p.ldb);
+      sa = p.as + static_cast<int64_t>(row0 / 64) * p.as_slab + m0 * 2;
+      sb = p.bs0 + static_cast<int64_t>(row0 / 64) * p.bs_slab + n0 * 2;
+      sa_n = BM * 2;
+    } else {
+      const int valid = min(BM, row_end - row0);
+      ra = make_rsrc(A + static_cast<int64_t>(row0) * p.lda, static_cast<int64_t>(valid) * p.lda);
+      sa = p.as + row0 * 2;
+      // Whole dwords: an odd row count keeps its last row's scales (the extra
+      // bytes are the scales of a row whose data reads as zero).
+      sa_n = (valid * 2 + 3) & ~3;
+      const int nb = MODE == FWD_GU ? nt * BR : n0;
+      const int64_t boff = bexp + static_cast<int64_t>(nb) * p.ldb;
+      rb = make_rsrc(B0 + boff, static_cast<int64_t>(BR) * p.ldb);
+      sb = p.bs0 + bsexp + nb * 2;
+      if constexpr (MODE == FWD_GU || MODE == BWD_GU) {
+        rb1 = make_rsrc(B1 + boff, static_cast<int64_t>(BR) * p.ldb);
+        sb1 = p.bs1 + bsexp + nb * 2;
+      }
+    }
+    // Each lane's byte offset within a tile for load q: row (q * 4 + wave) *
+    // 16 + lane / 4, its 16-byte chunk lane % 4 swizzled by the row.
+    uint32_t voa[LM], vob[LB];
+#pragma unroll
+    for (int q = 0; q < LM; ++q) {
+      const int row = (q * 4 + wave) * 16 + (lane >> 2);
+      voa[q] = static_cast<uint32_t>(row * p.lda + (((lane & 3) ^ swz_row(row)) << 4));
+    }
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int row = (q * 4 + wave) * 16 + (lane >> 2);
+      vob[q] = static_cast<uint32_t>(row * p.ldb + (((lane & 3) ^ swz_row(row)) << 4));
+    }
     // W: wait states of the loads (load_lds16): 4 where a descriptor may have
     // just been written by a VALU instruction, 0 in the steady-state loop.
+    // A slab at or past the end moves every lane's offset past any buffer's
+    // range (descriptors hold at most 2^31 - 1 bytes), so it reads nothing.
+    constexpr uint32_t kDead = 0x80000000u;
     auto issue = [&](int kt, uint32_t slot, auto L, auto w) {
       constexpr int l = decltype(L)::value, W = decltype(w)::value;
       const bool live = kt < nk;
+      const uint32_t kofs = live ? static_cast<uint32_t>(kt * 64) : kDead;
       if constexpr (l < LM) {
-        if constexpr (MODE == WGRAD) {
-          const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
-          load_rows64<BM, W>(make_rsrc(A + m0 * p.lda + k0, live ? BM * p.lda : 0), p.lda, slot, wave, lane, l);
-        } else {
-          const int valid = live ? min(BM, row_end - row0) : 0;
-          load_rows64<BM, W>(make_rsrc(A + static_cast<int64_t>(row0) * p.lda + kt * 64,
-                                       static_cast<int64_t>(valid) * p.lda),
-                             p.lda, slot, wave, lane, l);
-        }
+        load_lds16<W>(ra, voa[l] + kofs, slot + (l * 4 + wave) * 16 * 64);
       } else if constexpr (l < LM + LN) {
         constexpr int q = l - LM;
         const uint32_t tn = slot + TILE_M;
         if constexpr (MODE == FWD_GU) {
-          constexpr int half = q / (LN / 2), qq = q % (LN / 2);
-          const int64_t off = bexp + static_cast<int64_t>(nt * (BN / 2)) * p.ldb + kt * 64;
-          const int64_t bytes = live ? static_cast<int64_t>(BN / 2) * p.ldb : 0;
-          load_rows64<BN / 2, W>(make_rsrc((half ? B1 : B0) + off, bytes), p.ldb, tn + half * (TILE_N / 2), wave,
-                                 lane, qq);
-        } else if constexpr (MODE == WGRAD) {
-          const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
-          load_rows64<BN, W>(make_rsrc(B0 + n0 * p.ldb + k0, live ? BN * p.ldb : 0), p.ldb, tn, wave, lane, q);
-        } else {  // FWD_DOWN, BWD_DOWN, BWD_GU: B stored [n][k] per expert
-          const uint8_t* src = B0;
-          int ks = kt;
-          if constexpr (MODE == BWD_GU) {
-            if (kt * 64 >= p.f) { src = B1; ks = kt - p.f / 64; }
-          }
-          load_rows64<BN, W>(make_rsrc(src + bexp + static_cast<int64_t>(n0) * p.ldb + ks * 64,
-                                       live ? static_cast<int64_t>(BN) * p.ldb : 0),
-                             p.ldb, tn, wave, lane, q);
+          constexpr int half = q / LB, qq = q % LB;
+          load_lds16<W>(half ? rb1 : rb, vob[qq] + kofs, tn + half * (TILE_N / 2) + (qq * 4 + wave) * 16 * 64);
+        } else if constexpr (MODE == BWD_GU) {
+          const bool second = kt * 64 >= p.f;
+          const uint32_t bofs = live ? static_cast<uint32_t>((second ? kt - p.f / 64 : kt) * 64) : kDead;
+          load_lds16<W>(second ? rb1 : rb, vob[q] + bofs, tn + (q * 4 + wave) * 16 * 64);
+        } else {
+          load_lds16<W>(rb, vob[q] + kofs, tn + (q * 4 + wave) * 16 * 64);
         }
       } else {
         const uint32_t sc = slot + TILE_M + TILE_N + wave * kScaleArea;
         const uint32_t voff = static_cast<uint32_t>(lane * 16);
         if (wave == 0) {
-          if constexpr (MODE == WGRAD) {
-            const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
-            load_lds16<W>(make_rsrc(p.as + (k0 / 64) * p.as_slab + m0 * 2, live ? BM * 2 : 0), voff, sc);
-          } else {
-            // Buffer range checks are per dword: round the range up to whole
-            // dwords or an odd row count loses its last row's scales. The extra
-            // bytes are the scales of a row whose data reads as zero (it is
-            // never written).
-            const int valid = live ? min(BM, row_end - row0) : 0;
-            load_lds16<W>(make_rsrc(p.as + static_cast<int64_t>(kt) * p.as_slab + row0 * 2, (valid * 2 + 3) & ~3),
-                          voff, sc);
-          }
+          load_lds16<W>(make_rsrc(sa + static_cast<int64_t>(kt) * p.as_slab, live ? sa_n : 0), voff, sc);
         } else if (wave == 1 || (wave == 2 && MODE == FWD_GU)) {
+          const uint8_t* ssrc = sb + static_cast<int64_t>(kt) * p.bs_slab;
           if constexpr (MODE == FWD_GU) {
-            const int64_t so = bsexp + static_cast<int64_t>(kt) * p.bs_slab + nt * (BN / 2) * 2;
-            load_lds16<W>(make_rsrc((wave == 1 ? p.bs0 : p.bs1) + so, live ? BN : 0), voff, sc);
-          } else if constexpr (MODE == WGRAD) {
-            const int64_t k0 = row0 + static_cast<int64_t>(kt) * 64;
-            load_lds16<W>(make_rsrc(p.bs0 + (k0 / 64) * p.bs_slab + n0 * 2, live ? BN * 2 : 0), voff, sc);
-          } else {
-            const uint8_t* ssrc = p.bs0;
-            int ks = kt;
-            if constexpr (MODE == BWD_GU) {
-              if (kt * 64 >= p.f) { ssrc = p.bs1; ks = kt - p.f / 64; }
-            }
-            load_lds16<W>(make_rsrc(ssrc + bsexp + static_cast<int64_t>(ks) * p.bs_slab + n0 * 2, live ? BN * 2 : 0),
-                          voff, sc);
+            if (wave == 2) ssrc = sb1 + static_cast<int64_t>(kt) * p.bs_slab;
+          } else if constexpr (MODE == BWD_GU) {
+            if (kt * 64 >= p.f) ssrc = sb1 + static_cast<int64_t>(kt - p.f / 64) * p.bs_slab;
           }
+          load_lds16<W>(make_rsrc(ssrc, live ? BR * 2 : 0), voff, sc);
         } else {
-          load_lds16<W>(make_rsrc(p.as, 0), voff, sc);
+          load_lds16<W>(r0, voff, sc);
         }
       }
     };
