@@ -45,9 +45,10 @@
  *    the layer dtype `shape->dtype` (MOE_F32 or MOE_BF16; MXFP8 layers keep
  *    bf16 inputs and outputs) unless the argument says fp32. MXFP8 layers
  *    decide every E4M3 code of a computed GEMM operand on its fp32 value
- *    rather than on a bf16 rounding of it: G, U (save buffer) and d_o are
- *    fp32, and H and dG | dU exist only as the E4M3 operands the GEMM
- *    epilogues write from fp32 values in registers. Weights:
+ *    rather than on a bf16 rounding of it: d_o is fp32, G and U (save
+ *    buffer) are fp32 rounded to 16 mantissa bits, and H and dG | dU exist
+ *    only as the E4M3 operands the GEMM epilogues write from fp32 values in
+ *    registers. Weights:
  *    w_router [d][E]; w_gate, w_up [E][d][f]; w_down [E][f][d].
  *  - Row counts: S = T*k routed rows. Index tensors are int32.
  *  - Validation is host-side only and never reads device memory. Errors:
@@ -73,7 +74,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 enum moe_status {
   MOE_OK = 0,
@@ -137,8 +138,10 @@ size_t moe_workspace_size(int op, const moe_shape* shape);
 
 /* Bytes of the buffer that moe_grouped_ffn_fwd fills with what the backward
  * needs. fp32 and bf16 layers: G, U, H (three [S][f] tensors in the layer
- * dtype). MXFP8 layers: G and U in fp32, each in a blocked layout (every
- * expert's rows padded to a multiple of 64; 32 x 32 blocks of 4 KB), H only
+ * dtype). MXFP8 layers: G and U as fp32 rounded to 16 mantissa bits (to
+ * nearest, ties away from zero) and kept as 24-bit words, each in a blocked
+ * layout (every expert's rows padded to a multiple of 64; 32 x 32 blocks of
+ * 3 KB), H only
  * as the W_down weight gradient's E4M3 operand (blocked along each expert's
  * tokens), and the E4M3 copies (with their E8M0 scales) of w_gate, w_up and
  * w_down in the layouts of the backward's dgrad GEMMs, which the forward

@@ -99,7 +99,7 @@ int check_ffn_dtype(const moe_shape* s, const char* who) {
 bool recompute(const moe_shape* s) { return (s->flags & MOE_FLAG_RECOMPUTE) != 0; }
 
 // G, U, H: three [S][f] planes (act_bytes each element); MXFP8 layers keep
-// only G and U, as two blocked fp32 planes over the rows padded per expert.
+// only G and U, as two blocked 24-bit planes over the rows padded per expert.
 size_t gu_h_bytes(const moe_shape* s) {
   if (s->dtype == MOE_MXFP8) return 2 * moe::ffn_mx_gu_plane((int)(s->T * s->k), (int)s->f, (int)s->E);
   return ((size_t)3 * s->T * s->k * s->f * act_bytes(s->dtype) + 255) & ~(size_t)255;

@@ -5,10 +5,12 @@
 // infraestrutura para treinar modelos MoE", section "Otimizações e testes em
 // escala de trilhões"; "Ai2 rilascia Olmo-Core 3...", section "Parallelismo,
 // precisione e tecniche di memoria"). Inputs, O, dXp and the weight
-// gradients are bf16; every E4M3 code of a computed GEMM operand (G, U, H,
-// dO, dG | dU) is decided on its fp32 value: G, U, H and dO are kept in
-// fp32, and dG | dU exist only inside the down-dgrad epilogue, which writes
-// both of their E4M3 operand layouts. Each GEMM consumes
+// gradients are bf16; every E4M3 code of a computed GEMM operand (H, dO,
+// dG | dU) is decided on its fp32 value: dO is kept in fp32, G and U in
+// fp32 rounded to 16 mantissa bits (24-bit words), H exists only inside the
+// gate/up epilogue (from those G, U) and dG | dU only inside the down-dgrad
+// epilogue, each of which writes both E4M3 operand layouts of its tensor.
+// Each GEMM consumes
 // E4M3 copies with one E8M0 scale per 32 elements along its K:
 //   forward   G,U = q(Xp) q(W_gate), q(W_up)   K = d  (weights transposed)
 //             O   = q(H) q(W_down)              K = f  (weight transposed)
@@ -159,7 +161,7 @@ size_t ffn_mx_save_extra(int S, int d, int f, int E, bool rec) {
 }
 
 size_t ffn_mx_gu_plane(int S, int f, int E) {
-  return a256(static_cast<size_t>(padded_rows(S, E)) * f * 4);
+  return a256(static_cast<size_t>(padded_rows(S, E)) * f * 3);
 }
 
 size_t ffn_mx_bwd_workspace(int S, int d, int f, int E, bool rec) {

@@ -178,6 +178,27 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
 
 __device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// The saved G, U of the MXFP8 layers: fp32 with the low 8 of the 23 mantissa
+// bits rounded off (to nearest, ties away from zero; relative error at most
+// 2^-17, below the fp32 accumulation error of the GEMM that produced them),
+// four values in three dwords. fp24_round gives the fp32 value that is kept.
+typedef unsigned int u32x3_t __attribute__((ext_vector_type(3)));
+__device__ __forceinline__ float fp24_round(float x) {
+  return __uint_as_float((__float_as_uint(x) + 0x80u) & 0xffffff00u);
+}
+// Packs four values already rounded by fp24_round.
+__device__ __forceinline__ u32x3_t fp24_pack4(float a, float b, float c, float d) {
+  const uint32_t t0 = __float_as_uint(a) >> 8, t1 = __float_as_uint(b) >> 8;
+  const uint32_t t2 = __float_as_uint(c) >> 8, t3 = __float_as_uint(d) >> 8;
+  return u32x3_t{t0 | (t1 << 24), (t1 >> 8) | (t2 << 16), (t2 >> 16) | (t3 << 8)};
+}
+__device__ __forceinline__ void fp24_unpack4(u32x3_t w, float (&o)[4]) {
+  o[0] = __uint_as_float(w.x << 8);
+  o[1] = __uint_as_float(((w.x >> 16) & 0xff00u) | (w.y << 16));
+  o[2] = __uint_as_float(((w.y >> 8) & 0xffff00u) | (w.z << 24));
+  o[3] = __uint_as_float(w.z & 0xffffff00u);
+}
+
 
 struct TileCoord {
   int e;        // expert (-1: no tile)
@@ -390,10 +411,10 @@ __device__ __forceinline__ TileCoord wgrad_tile(const GemmParams& p, int t) {
 // Writes the accumulators of one BM x BN tile (and, for BWD_DOWN, reads the
 // saved G, U it needs) through a per-wave LDS area of smem, which must hold
 // 4 x 2 x (BM/2) x 128 bytes and be free of other use.
-// With QUANT (the MXFP8 kernels), FWD_GU writes fp32 G, U in a blocked
-// layout and H, and BWD_DOWN dG | dU, only as the next GEMMs' E4M3 operands
-// (K-major p.mxq, p.mxs; token-major p.tq, p.ts), every code decided on the
-// fp32 value in registers; BWD_DOWN reads the blocked G, U.
+// With QUANT (the MXFP8 kernels), FWD_GU writes G, U (24-bit, fp24_pack4)
+// in a blocked layout and H, and BWD_DOWN dG | dU, only as the next GEMMs'
+// E4M3 operands (K-major p.mxq, p.mxs; token-major p.tq, p.ts), every code
+// decided on the fp32 value in registers; BWD_DOWN reads the blocked G, U.
 template <int MODE, int BM, int BN, bool QUANT = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN / 64][BM / 64], char* smem,
                                          int wave, int lane, const TileCoord& tc) {
@@ -448,14 +469,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
   };
 
   if constexpr (MODE == FWD_GU && QUANT) {
-    // G, U and H = G sig(G) U in fp32, one 32 x 32 block (gate block JJ and
-    // up block JJ + NB/2 cover the same 32 f-columns, row block I) at a time,
-    // straight from the accumulators:
+    // G, U (rounded to the 24 bits they are kept in) and H = G sig(G) U in
+    // fp32 from those values, one 32 x 32 block (gate block JJ and up block
+    // JJ + NB/2 cover the same 32 f-columns, row block I) at a time, straight
+    // from the accumulators:
     //  - G and U to the save buffer in the blocked layout the down-dgrad
-    //    epilogue reads back: block (padded row / 32, column / 32), 4 KB, in
+    //    epilogue reads back: block (padded row / 32, column / 32), 3 KB, in
     //    lane order (lane l: row l % 32, columns 8 Q + 4 (l / 32) .. +3 as one
-    //    16-byte piece at Q KB + 16 l), so every store and every later load
-    //    is one contiguous kilobyte. Padded rows are poff[e] + row inside e.
+    //    12-byte piece at 768 Q + 12 l), so every store and every later load
+    //    is 768 contiguous bytes. Padded rows are poff[e] + row inside e.
     //  - H only as E4M3 operands, each code decided on the fp32 value:
     //    K-major along f (the down GEMM's A operand; a row's 32-block sits in
     //    lanes l and l ^ 32), and token-major [f][P] for the weight gradient
@@ -477,23 +499,24 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
       constexpr int bi = decltype(BI)::value, JJ = bi / MB, I = bi % MB;
       const int col0 = nt * (BN / 2) + wn * (WN / 2) + JJ * 32;
       const bool live = rel0 + I * 32 < n64;
-      float h[16];
+      float gk[16], uk[16], h[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float g = acc[JJ][I][r], u = acc[JJ + NB / 2][I][r];
-        h[r] = g * sigmoid_f(g) * u;
+        gk[r] = fp24_round(acc[JJ][I][r]);
+        uk[r] = fp24_round(acc[JJ + NB / 2][I][r]);
+        h[r] = gk[r] * sigmoid_f(gk[r]) * uk[r];
       }
       if (live) {
-        const int64_t kb = ((pt0 / 32 + I) * fb + col0 / 32) * 4;  // in kilobytes
-        float* const Gb = static_cast<float*>(p.c0) + kb * 256 + lane * 4;
-        float* const Ub = static_cast<float*>(p.c1) + kb * 256 + lane * 4;
+        const int64_t blk = ((pt0 / 32 + I) * fb + col0 / 32) * 3072;  // bytes
+        const auto rGb = make_rsrc(static_cast<char*>(p.c0) + blk, 3072);
+        const auto rUb = make_rsrc(static_cast<char*>(p.c1) + blk, 3072);
 #pragma unroll
         for (int Q = 0; Q < 4; ++Q) {
-          *reinterpret_cast<float4*>(Gb + Q * 256) =
-              make_float4(acc[JJ][I][4 * Q], acc[JJ][I][4 * Q + 1], acc[JJ][I][4 * Q + 2], acc[JJ][I][4 * Q + 3]);
-          *reinterpret_cast<float4*>(Ub + Q * 256) =
-              make_float4(acc[JJ + NB / 2][I][4 * Q], acc[JJ + NB / 2][I][4 * Q + 1], acc[JJ + NB / 2][I][4 * Q + 2],
-                          acc[JJ + NB / 2][I][4 * Q + 3]);
+          const uint32_t off = static_cast<uint32_t>(Q * 768 + lane * 12);
+          __builtin_amdgcn_raw_buffer_store_b96(fp24_pack4(gk[4 * Q], gk[4 * Q + 1], gk[4 * Q + 2], gk[4 * Q + 3]), rGb,
+                                                off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b96(fp24_pack4(uk[4 * Q], uk[4 * Q + 1], uk[4 * Q + 2], uk[4 * Q + 3]), rUb,
+                                                off, 0, 0);
         }
       }
       // Token-major: stage column-major.
@@ -551,12 +574,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     });
   } else if constexpr (MODE == BWD_DOWN && QUANT) {
     // dH -> dG = dH U sig(G) (1 + G (1 - sig(G))), dU = dH G sig(G) in fp32
-    // from the fp32 saved G, U, one 32 x 32 block (J, I) at a time. The saved
-    // G, U of a block come straight into registers in the accumulator layout
+    // from the saved G, U, one 32 x 32 block (J, I) at a time. The saved G, U
+    // of a block come straight into registers in the accumulator layout
     // (lane: row 32 I + l%32, columns 8 Q + 4 (l/32) .. +3), as four
-    // contiguous kilobytes each from the blocked layout the gate/up epilogue
-    // wrote, two blocks ahead of their use; rows past the expert's end hold
-    // 0, so dG, dU are 0 there.
+    // contiguous 768-byte pieces each from the blocked layout the gate/up
+    // epilogue wrote, two blocks ahead of their use; rows past the expert's
+    // end hold 0, so dG, dU are 0 there.
     // dG and dU leave only as the next GEMMs' E4M3 operands, each code
     // decided on the fp32 value:
     //  - K-major along 2f (dG in columns [0, f), dU in [f, 2f)): a row's
@@ -575,24 +598,23 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     const int rel0 = mrow - e_first;                       // first row of the block, inside the expert
     const int n64 = (row_end - e_first + 63) & ~63;        // the expert's rows padded to 64
     const int64_t pt0 = static_cast<int64_t>(p.poff[e]) + rel0;
-    // G, U in the blocked layout the gate/up epilogue writes (4 KB per 32 x
+    // G, U in the blocked layout the gate/up epilogue writes (3 KB per 32 x
     // 32 block, lane order): blocks past the expert's padded rows read 0.
     const int fb = p.f / 32;
-    const int64_t gb0 = (pt0 / 32) * fb * 4096, gbytes = static_cast<int64_t>(max(0, n64 - rel0) / 32) * fb * 4096;
+    const int64_t gb0 = (pt0 / 32) * fb * 3072, gbytes = static_cast<int64_t>(max(0, n64 - rel0) / 32) * fb * 3072;
     const auto rG = make_rsrc(static_cast<const char*>(p.e0) + gb0, gbytes);
     const auto rU = make_rsrc(static_cast<const char*>(p.e1) + gb0, gbytes);
     const auto rQ = make_rsrc(p.mxq + static_cast<int64_t>(mrow) * p.mxq_ld, rows * p.mxq_ld);
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int kAhead = 2;       // blocks of G, U in flight ahead of the one in use
-    f32x4 gu[kAhead + 1][2][4];     // [buffer][G, U][Q]
+    u32x3_t gu[kAhead + 1][2][4];   // [buffer][G, U][Q]
     auto load_block = [&](auto B, int J, int I) {
       constexpr int b = decltype(B)::value;
       const int col0 = n0 + wn * WN + J * 32;
 #pragma unroll
       for (int Q = 0; Q < 4; ++Q) {
-        const uint32_t off = static_cast<uint32_t>(((I * fb + col0 / 32) * 4 + Q) * 1024 + lane * 16);
-        gu[b][0][Q] = __builtin_amdgcn_raw_buffer_load_b128(rG, off, 0, 0);
-        gu[b][1][Q] = __builtin_amdgcn_raw_buffer_load_b128(rU, off, 0, 0);
+        const uint32_t off = static_cast<uint32_t>((I * fb + col0 / 32) * 3072 + Q * 768 + lane * 12);
+        gu[b][0][Q] = __builtin_amdgcn_raw_buffer_load_b96(rG, off, 0, 0);
+        gu[b][1][Q] = __builtin_amdgcn_raw_buffer_load_b96(rU, off, 0, 0);
       }
     };
     // Per-wave LDS: two transpose buffers [2 tensors][32 columns][36].
@@ -609,10 +631,18 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
                    (bi + kAhead) % MB);
       float* const tg = tgw + (bi & 1) * kTgFloats;
       const int col0 = n0 + wn * WN + J * 32;
-      float dg[16], du[16];
+      float dg[16], du[16], gq[16], uq[16];
+#pragma unroll
+      for (int Q = 0; Q < 4; ++Q) {
+        float g4[4], u4[4];
+        fp24_unpack4(gu[b][0][Q], g4);
+        fp24_unpack4(gu[b][1][Q], u4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { gq[4 * Q + c] = g4[c]; uq[4 * Q + c] = u4[c]; }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float g = gu[b][0][r / 4][r % 4], u = gu[b][1][r / 4][r % 4];
+        const float g = gq[r], u = uq[r];
         const float dh = acc[J][I][r];
         const float sg = sigmoid_f(g);
         du[r] = dh * g * sg;

@@ -191,8 +191,9 @@ hipError_t launch_mx_poff(const int32_t* offsets, int E, int32_t* poff, hipStrea
 size_t ffn_mx_fwd_workspace(int S, int d, int f, int E, bool recompute);
 // Extra save-buffer bytes of an MXFP8 layer (the backward's weight copies).
 size_t ffn_mx_save_extra(int S, int d, int f, int E, bool recompute);
-// Bytes of one blocked fp32 G or U plane of an MXFP8 layer: rows padded to 64
-// per expert, 32 x 32 blocks of 4 KB in accumulator lane order.
+// Bytes of one blocked G or U plane of an MXFP8 layer (24-bit words: fp32
+// with 16 mantissa bits): rows padded to 64 per expert, 32 x 32 blocks of
+// 3 KB in accumulator lane order.
 size_t ffn_mx_gu_plane(int S, int f, int E);
 size_t ffn_mx_bwd_workspace(int S, int d, int f, int E, bool recompute);
 hipError_t launch_ffn_mx_fwd(const FfnArgs& a, void* ws, hipStream_t s);

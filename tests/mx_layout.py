@@ -40,16 +40,16 @@ def fwd_pieces(S, d, f, E):
 
 
 def save_pieces(S, d, f, E):
-    """Save buffer of an MXFP8 layer: the blocked fp32 G and U planes, then
-    wgq, wgs, wuq, wus, wdq, wds (the dgrad weight copies) and ht, hts (H
-    along each expert's tokens)."""
+    """Save buffer of an MXFP8 layer: the blocked G and U planes (24-bit
+    words), then wgq, wgs, wuq, wus, wdq, wds (the dgrad weight copies) and
+    ht, hts (H along each expert's tokens)."""
     P = padded_rows(S, E)
-    plane = _a256(P * f * 4)
+    plane = _a256(P * f * 3)
     w = E * d * f
     names = ["wgq", "wgs", "wuq", "wus", "wdq", "wds", "ht", "hts"]
     sizes = [w, w // 32, w, w // 32, w, w // 32, P * f, P * f // 32]
     off, _ = _carve(sizes)
-    out = {"G": (0, P * f * 4), "U": (plane, P * f * 4)}
+    out = {"G": (0, P * f * 3), "U": (plane, P * f * 3)}
     out.update({n: (2 * plane + o, s) for n, o, s in zip(names, off, sizes)})
     return out
 
@@ -93,24 +93,27 @@ def padded_offsets(offsets):
 
 
 def blocked_rows(save, which, rows, offsets, S, f, E):
-    """Rows `rows` (expert-sorted row ids, host array) of the blocked fp32 G
-    or U plane of an MXFP8 layer's save buffer (a uint8 device tensor), as a
-    host fp64 [len(rows)][f] array. Block (padded row / 32, column / 32) is
-    4 KB; lane l of it holds row l % 32, columns 8 Q + 4 (l / 32) .. +3 at
-    Q KB + 16 l."""
+    """Rows `rows` (expert-sorted row ids, host array) of the blocked G or U
+    plane of an MXFP8 layer's save buffer (a uint8 device tensor), as a host
+    fp64 [len(rows)][f] array. Values are 24-bit words, the top three bytes
+    of an fp32 (little-endian). Block (padded row / 32, column / 32) is
+    3 KB; lane l of it holds row l % 32, columns 8 Q + 4 (l / 32) .. +3 as
+    four words at byte 768 Q + 12 l."""
     import torch
     o, n = save_pieces(S, 1, f, E)[which]
-    plane = save[o:o + n].view(torch.float32)
+    plane = save[o:o + n]
     rows = np.asarray(rows)
     offsets = np.asarray(offsets)
     e = np.searchsorted(offsets, rows, side="right") - 1
     pr = padded_offsets(offsets)[e] + rows - offsets[e]
     c = np.arange(f)
     fb = f // 32
-    idx = (((pr[:, None] // 32) * fb + c[None, :] // 32) * 4 + (c[None, :] % 32) // 8) * 256 \
-        + (((c[None, :] // 4) % 2) * 32 + pr[:, None] % 32) * 4 + c[None, :] % 4
-    t = torch.from_numpy(idx.reshape(-1).astype(np.int64)).to(plane.device)
-    return plane[t].cpu().numpy().astype(np.float64).reshape(len(rows), f)
+    byte = ((pr[:, None] // 32) * fb + c[None, :] // 32) * 3072 + ((c[None, :] % 32) // 8) * 768 \
+        + (((c[None, :] // 4) % 2) * 32 + pr[:, None] % 32) * 12 + (c[None, :] % 4) * 3
+    t = torch.from_numpy(byte.reshape(-1).astype(np.int64)).to(plane.device)
+    b = torch.stack([plane[t + i] for i in range(3)], 1).cpu().numpy().astype(np.uint32)
+    bits = (b[:, 0] << 8) | (b[:, 1] << 16) | (b[:, 2] << 24)
+    return bits.view(np.float32).astype(np.float64).reshape(len(rows), f)
 
 
 def bwd_pieces(S, d, f, E):

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
     for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
                        (-3, b"MOE_ERR_MISALIGNED"), (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
         assert lib.moe_status_string(code) == name
@@ -53,9 +53,11 @@ def test_workspace_queries():
     assert L.workspace_size(L.MOE_OP_FFN_BWD, s) == 256 * 4 * 2 * 128 * 4
     assert L.save_size(s) == 3 * 256 * 4 * 128 * 4
     assert L.save_size(shape(dtype="bf16")) == 3 * 256 * 4 * 128 * 2
-    # MXFP8 layers keep G, U, H (and dG|dU) in fp32, beside the weight copies.
+    # MXFP8 layers save G, U as 24-bit planes over the rows padded per expert
+    # (P = S + 63 E rounded up to 64), beside the E4M3 weight copies.
     mx = shape(dtype="mxfp8", d=128)
-    assert L.save_size(mx) > 3 * 256 * 4 * 128 * 4
+    P = (256 * 4 + 63 * 8 + 63) // 64 * 64
+    assert L.save_size(mx) > 2 * P * 128 * 3 + 3 * 8 * 128 * 128
     assert L.workspace_size(L.MOE_OP_FFN_BWD, mx) > 256 * 4 * 2 * 128 * 4
     with pytest.raises(L.MoeError):
         L.workspace_size(L.MOE_OP_DISPATCH, shape(k=9, E=16))
@@ -192,7 +194,7 @@ def test_recompute_flag_sizes_and_checks():
     mxp = L.MoeShape.make(T, d, E, k, f, "mxfp8")
     mxr = L.MoeShape.make(T, d, E, k, f, "mxfp8", L.MOE_FLAG_RECOMPUTE)
     P = (S + 63 * E + 63) // 64 * 64
-    gu = 2 * ((P * f * 4 + 255) // 256 * 256)  # the blocked fp32 G, U planes
+    gu = 2 * ((P * f * 3 + 255) // 256 * 256)  # the blocked 24-bit G, U planes
     ht = (P * f + 16 + 255) // 256 * 256 + (P * f // 32 + 16 + 255) // 256 * 256  # H along the tokens
     assert L.save_size(mxr) == L.save_size(mxp) - gu - ht
     assert L.workspace_size(L.MOE_OP_FFN_FWD, mxr) == L.workspace_size(L.MOE_OP_FFN_FWD, mxp) + ht + gu

@@ -91,7 +91,7 @@ def _expert_device(F, e):
     dv = dict(O=_rows(L.o, rows), dXp=_rows(L.dxp, rows),
               dW_gate=host(L.dw_gate[e]), dW_up=host(L.dw_up[e]), dW_down=host(L.dw_down[e]))
     if F.mx:
-        # MXFP8: fp32 G, U blocked in the save buffer; H, dG | dU and dO
+        # MXFP8: 24-bit G, U blocked in the save buffer; H, dG | dU and dO
         # exist only as E4M3 operands (checked as images); dO's values are
         # the fp32 products of the gates and dy that the device encodes.
         wl = F.wl

@@ -1,9 +1,10 @@
 """GPU parity of the MXFP8 expert layer against the oracle's MXFP8 FFN.
 
 Every grouped-GEMM operand is E4M3 with one E8M0 scale per 32 elements along
-that GEMM's K. The layer keeps its computed operands (G, U, H, dO, dG | dU)
-in fp32 and decides every E4M3 code on the fp32 value; the oracle decides it
-on the exact fp64 value. Checks, max|gpu - ref| / max|ref| per tensor:
+that GEMM's K. The layer keeps G, U in fp32 rounded to 16 mantissa bits and
+decides every E4M3 code of a computed operand (H, dO, dG | dU) on its fp32
+value; the oracle decides it on the exact fp64 value from the same stored
+inputs. Checks, max|gpu - ref| / max|ref| per tensor:
 
 * every E4M3 image the layer writes (K-major xp, dO, H, dG | dU; the
   token-major weight-gradient operands H, dO, Xp, dG | dU) is the oracle's
@@ -133,7 +134,7 @@ def test_mxfp8_layer_matches_mx_oracle(case):
     off = ref["offsets"]
     S, f = wl.T * wl.k, wl.f
     assert layer.d_o is None  # the combine backward writes only dO's E4M3 operands
-    # G, U: fp32, blocked in the save buffer. H and dG | dU exist on the
+    # G, U: 24-bit words, blocked in the save buffer. H and dG | dU exist on the
     # device only as E4M3 operands.
     G, U = (ML.blocked_rows(layer.save, n, np.arange(S), off, S, f, wl.E) for n in ("G", "U"))
     H = G * O.sigmoid(G) * U
@@ -348,4 +349,4 @@ def test_mxfp8_recompute_is_bit_identical(case):
         assert torch.equal(getattr(rec, n), getattr(ref, n)), n
     S, f = wl.T * wl.k, wl.f
     P = (S + 63 * wl.E + 63) // 64 * 64
-    assert rec.save.numel() < ref.save.numel() - 2 * P * f * 4
+    assert rec.save.numel() < ref.save.numel() - 2 * P * f * 3
