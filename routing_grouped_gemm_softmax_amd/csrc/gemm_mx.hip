@@ -390,18 +390,28 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
     }
     return t;
   };
-  // Each lane's byte offset within a tile for A and B load q: row (q * 4 +
-  // wave) * 16 + lane / 4, its 16-byte chunk lane % 4 swizzled by the row.
+  // Rows are interleaved inside each wave's 128-row block: LDS row L (the
+  // rows fragment (L / 32) % 4 reads, lane L % 32) holds tile row
+  // inter_row(L), so fragment f of a wave covers rows f, f + 4, f + 8, ...
+  // of its block and a lane's four fragments are four consecutive rows. Their
+  // eight scale bytes (two 32-blocks each) are then adjacent in the scale
+  // tile, one 8-byte LDS read per side, and each MFMA picks its byte with
+  // the scale operand's byte select. The epilogue writes accumulator row
+  // (column) c of fragment f to row (column) 4 c + f.
+  auto inter_row = [](int L) { return (L & ~127) + 4 * (L & 31) + ((L >> 5) & 3); };
+  // Each lane's byte offset within a tile for A and B load q: LDS row (q * 4
+  // + wave) * 16 + lane / 4, its 16-byte chunk lane % 4 swizzled by that LDS
+  // row, taken from tile row inter_row of it.
   uint32_t voa[LM], vob[LN];
 #pragma unroll
   for (int q = 0; q < LM; ++q) {
     const int row = (q * 4 + wave) * 16 + (lane >> 2);
-    voa[q] = static_cast<uint32_t>(row * p.lda + (((lane & 3) ^ swz_row(row)) << 4));
+    voa[q] = static_cast<uint32_t>(inter_row(row) * p.lda + (((lane & 3) ^ swz_row(row)) << 4));
   }
 #pragma unroll
   for (int q = 0; q < LN; ++q) {
     const int row = (q * 4 + wave) * 16 + (lane >> 2);
-    vob[q] = static_cast<uint32_t>(row * p.ldb + (((lane & 3) ^ swz_row(row)) << 4));
+    vob[q] = static_cast<uint32_t>(inter_row(row) * p.ldb + (((lane & 3) ^ swz_row(row)) << 4));
   }
 
   // Load L of slab kt of the load tile lt.
@@ -439,27 +449,37 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
   floatx16 acc[NB][MB];
   struct Frags {
     v8i m[MB], n[NB];
-    int sm[MB], sn[NB];
+    int sm[2], sn[2];  // fragment f's scale: byte 2 (f % 2) of word f / 2
   };
+  // Fragment FI; with the first fragment of a side also that side's scales:
+  // the 8 bytes of the lane's four interleaved rows, shifted so that the
+  // lane's 32-block (lane / 32) sits in the even bytes.
   auto read_frag = [&](const char* slotp, Frags& F, auto FI) {
     constexpr int fi = decltype(FI)::value;
     const uint8_t* sc = reinterpret_cast<const uint8_t*>(slotp + TILE_M + TILE_N);
-    const int r32 = lane & 31, kb = lane >> 5;
+    const int r32 = lane & 31;
+    const uint32_t kb8 = static_cast<uint32_t>(lane >> 5) * 8;
     if constexpr (fi < MB) {
-      const int row = wm * WM + fi * 32;
-      F.m[fi] = frag_mx(slotp, row, lane);
-      F.sm[fi] = sc[(row + r32) * 2 + kb];
+      F.m[fi] = frag_mx(slotp, wm * WM + fi * 32, lane);
+      if constexpr (fi == 0) {
+        const uint64_t v = *reinterpret_cast<const uint64_t*>(sc + (wm * WM + 4 * r32) * 2) >> kb8;
+        F.sm[0] = static_cast<int>(v);
+        F.sm[1] = static_cast<int>(v >> 32);
+      }
     } else {
       constexpr int j = fi - MB;
-      const int row = wn * WN + j * 32;
-      F.n[j] = frag_mx(slotp + TILE_M, row, lane);
-      F.sn[j] = sc[kScaleArea + (row + r32) * 2 + kb];
+      F.n[j] = frag_mx(slotp + TILE_M, wn * WN + j * 32, lane);
+      if constexpr (j == 0) {
+        const uint64_t v = *reinterpret_cast<const uint64_t*>(sc + kScaleArea + (wn * WN + 4 * r32) * 2) >> kb8;
+        F.sn[0] = static_cast<int>(v);
+        F.sn[1] = static_cast<int>(v >> 32);
+      }
     }
   };
   auto mfma_one = [&](const Frags& F, auto MI) {
     constexpr int mi = decltype(MI)::value, j = mi / MB, i = mi % MB;
-    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.n[j], F.m[i], acc[j][i], 0, 0, 0, F.sn[j], 0,
-                                                               F.sm[i]);
+    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.n[j], F.m[i], acc[j][i], 0, 0, 2 * (j % 2),
+                                                               F.sn[j / 2], 2 * (i % 2), F.sm[i / 2]);
   };
   constexpr int kMfma = MB * NB, kFrags = MB + NB;
 
@@ -472,27 +492,25 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
   };
-  // Staging rows [0, 32) -> global rows g + r * ld for r < rows (4 buffer
-  // stores, non-temporal: the outputs are written once and read by a later
-  // kernel, and the stores complete sooner without allocating in the L2,
-  // which matters because the next slabs' waits count them).
-  auto flush = [&](const char* g, int64_t ld, int rows) {
+  // Staging rows [0, 32) -> rows 4 r + I of the wave's block, whose first
+  // row (at this column half) is g, for rows below `rows` (4 buffer stores,
+  // non-temporal: the outputs are written once and read by a later kernel,
+  // and the stores complete sooner without allocating in the L2, which
+  // matters because the next slabs' waits count them).
+  auto flush = [&](const char* g, int64_t ld, int I, int rows) {
     __builtin_amdgcn_sched_barrier(0);
     wave_sync();
-    const auto rs = make_rsrc(g, static_cast<int64_t>(max(0, min(32, rows))) * ld);
+    const auto rs = make_rsrc(g, static_cast<int64_t>(max(0, min(WM, rows))) * ld);
     const int c = lane & 7;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int r = t * 8 + (lane >> 3);
       typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
       const u32x4 v = *reinterpret_cast<const u32x4*>(wa + r * 128 + ((c ^ (r >> 1)) & 7) * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<uint32_t>(r * ld + c * 16), 0, kStoreNT);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<uint32_t>((4 * r + I) * ld + c * 16), 0, kStoreNT);
     }
     wave_sync();
     __builtin_amdgcn_sched_barrier(0);
-  };
-  auto acc4 = [&](int j, int i, int q) {
-    return pack4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
   };
   auto epilogue = [&](const TileCoord& tc) {
     const int64_t ld = p.ldc * 2;
@@ -512,12 +530,18 @@ __global__ __launch_bounds__(256) void gg_mx_stream_kernel(GemmParams p) {
       out = base + (static_cast<int64_t>(tc.e) * p.cstride + static_cast<int64_t>(tc.m0 + wm * WM) * p.ldc + cn0 +
                     wn * WN) * 2;
     }
-    static_for<2>([&](auto JP) {
+    // Column half H of the wave's block: accumulator columns c (element r
+    // of lane l: c = 8 (r / 4) + 4 (l / 32) + r % 4) in [16 H, 16 H + 16),
+    // i.e. r in [8 H, 8 H + 8); the four fragments' values of one c are
+    // the four adjacent columns 4 c .. 4 c + 3.
+    static_for<2>([&](auto H) {
       static_for<MB>([&](auto I) {
-        static_for<2>([&](auto JJ) {
-          static_for<4>([&](auto Q) { put4(l32, JJ * 32 + 8 * Q + 4 * hl, acc4(JP * 2 + JJ, I, Q)); });
+        static_for<8>([&](auto R) {
+          constexpr int r = 8 * H + R;
+          const int c = 8 * (r / 4) + 4 * hl + r % 4;
+          put4(l32, 4 * c - 64 * H, pack4(acc[0][I][r], acc[1][I][r], acc[2][I][r], acc[3][I][r]));
         });
-        flush(out + static_cast<int64_t>(I) * 32 * ld + JP * 128, ld, rows - 32 * I);
+        flush(out + H * 128, ld, I, rows);
       });
     });
   };
