@@ -182,6 +182,9 @@ __device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rc
 // bits rounded off (to nearest, ties away from zero; relative error at most
 // 2^-17, below the fp32 accumulation error of the GEMM that produced them),
 // four values in three dwords. fp24_round gives the fp32 value that is kept.
+// Its inputs are MFMA results, whose NaNs carry the quiet bit, which the
+// rounding keeps (only a NaN with nothing but the low 8 payload bits would
+// turn into an infinity).
 typedef unsigned int u32x3_t __attribute__((ext_vector_type(3)));
 __device__ __forceinline__ float fp24_round(float x) {
   return __uint_as_float((__float_as_uint(x) + 0x80u) & 0xffffff00u);
