@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -31,16 +32,28 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA / packed vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+_C_COMMENT = re.compile(rb'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"', re.S)
+
+
+def _code_only(text: bytes) -> bytes:
+    """C/C++ source without its comments and blank space at line ends or
+    between lines (string literals kept), so that a change to a comment
+    leaves the hash alone."""
+    text = _C_COMMENT.sub(lambda m: m.group(0) if m.group(0).startswith(b'"') else b" ", text)
+    lines = (ln.rstrip() for ln in text.splitlines())
+    return b"\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash(files=None) -> str:
-    """Hash of the library's kernel sources (all of csrc, or the listed files
-    plus the build script, whose flags shape the code)."""
+    """Hash of the library's kernel sources, comments left out (all of csrc,
+    or the listed files plus the build script, whose flags shape the code)."""
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "routing_grouped_gemm_softmax_amd")
     csrc = os.path.join(pkg, "csrc")
     names = sorted(os.listdir(csrc)) if files is None else sorted(files)
     for n in names:
         with open(os.path.join(csrc, n), "rb") as fh:
-            h.update(n.encode() + fh.read())
+            h.update(n.encode() + _code_only(fh.read()))
     if files is not None:
         with open(os.path.join(pkg, "build.py"), "rb") as fh:
             h.update(b"build.py" + fh.read())

@@ -71,3 +71,15 @@ def test_cpu_baseline_mxfp8_sample_runs():
     r = bench.cpu_baseline(wl, make_inputs(wl, 0), budget_s=1.0)
     assert r["value"] > 0 and r["kind"] == "oracle" and r["cores"] >= 1 and r["cpu_model"]
     assert "whole experts" in r["sample"]
+
+
+def test_source_hash_ignores_comments_only():
+    """The kernel-source fingerprint that dates the traffic counters changes
+    with the code, not with its comments."""
+    import bench
+    a = b'#include "x.h"\n// one\nint f(int v) { return v + 1; }  /* two */\n'
+    b = b'#include "x.h"\n/* other\n text */\nint f(int v) { return v + 1; }\n\n// more\n'
+    c = b'#include "x.h"\nint f(int v) { return v + 2; }\n'
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+    assert b'"x.h"' in bench._code_only(a)
