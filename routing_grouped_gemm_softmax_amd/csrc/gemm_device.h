@@ -498,8 +498,19 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     constexpr int kTgFloats = 32 * 36;
     float* const tgw = reinterpret_cast<float*>(smem + wave * (2 * kTgFloats * 4));
     typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    // 256 x 256 tiles: the blocks go row group by row group, and a group's two
+    // H column blocks (the wave's 64 columns of each K-major row) are staged
+    // in LDS (two buffers of [32 rows][80 bytes] per wave, after the transpose
+    // buffers) and leave 16 rows x 64 bytes per store instead of 32 bytes of
+    // 32 rows. Other tiles store each block's pieces directly.
+    constexpr bool kStageH = (BM == 256 && BN == 256);
+    constexpr int kHst = 2 * 32 * 80;
+    char* const hst = smem + 4 * (2 * kTgFloats * 4) + wave * kHst;
+    static_assert(!kStageH || 4 * (2 * kTgFloats * 4 + kHst) <= 4 * (BM * 64 + BN * 64 + 4 * 1024),
+                  "epilogue LDS fits in the ring");
     static_for<(NB / 2) * MB>([&](auto BI) {
-      constexpr int bi = decltype(BI)::value, JJ = bi / MB, I = bi % MB;
+      constexpr int bi = decltype(BI)::value;
+      constexpr int JJ = kStageH ? bi % (NB / 2) : bi / MB, I = kStageH ? bi / (NB / 2) : bi % MB;
       const int col0 = nt * (BN / 2) + wn * (WN / 2) + JJ * 32;
       const bool live = rel0 + I * 32 < n64;
       float gk[16], uk[16], h[16];
@@ -540,9 +551,26 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
                               ldexpf(h[4 * Q + 2], 127 - code), ldexpf(h[4 * Q + 3], 127 - code));
         const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
         const auto c = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{a[0], a[1], c[0], c[1]}, rQ,
-                                               static_cast<uint32_t>((I * 32 + l32) * p.mxq_ld + col0 + 16 * hl), 0,
-                                               0);
+        if constexpr (kStageH) {
+          char* const hb = hst + (I & 1) * (kHst / 2);
+          *reinterpret_cast<u32x4_t*>(hb + l32 * 80 + JJ * 32 + 16 * hl) = u32x4_t{a[0], a[1], c[0], c[1]};
+          if constexpr (JJ == NB / 2 - 1) {
+            wave_sync();
+            const int c16 = lane & 3;
+            const int cbase = nt * (BN / 2) + wn * (WN / 2);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int r = t * 16 + (lane >> 2);
+              __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(hb + r * 80 + c16 * 16), rQ,
+                                                     static_cast<uint32_t>((I * 32 + r) * p.mxq_ld + cbase + c16 * 16),
+                                                     0, 0);
+            }
+          }
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{a[0], a[1], c[0], c[1]}, rQ,
+                                                 static_cast<uint32_t>((I * 32 + l32) * p.mxq_ld + col0 + 16 * hl), 0,
+                                                 0);
+        }
         const auto rS = make_rsrc(p.mxs + static_cast<int64_t>(col0 / 64) * p.mxs_slab +
                                       static_cast<int64_t>(mrow) * 2,
                                   static_cast<int64_t>(rows) * 2);
@@ -623,15 +651,28 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     // Per-wave LDS: two transpose buffers [2 tensors][32 columns][36].
     constexpr int kTgFloats = 2 * 32 * 36;
     float* const tgw = reinterpret_cast<float*>(smem + wave * (2 * kTgFloats * 4));
+    // 256 x 256 tiles (a wave's 128 columns are one 128-byte line of each
+    // K-major row): the blocks go row group by row group, and a group's four
+    // column blocks are staged in LDS (two buffers of [2 tensors][32 rows][144
+    // bytes] per wave, after the transpose buffers) and leave as whole lines,
+    // 8 rows per store, instead of 32 bytes of 32 rows per store. Other tiles
+    // store each block's 16-byte pieces directly, column block by column block.
+    constexpr bool kStageK = (BM == 256 && BN == 256);
+    constexpr int kKst = 2 * 2 * 32 * 144;
+    char* const kst = smem + 4 * (2 * kTgFloats * 4) + wave * kKst;
+    static_assert(!kStageK || 4 * (2 * kTgFloats * 4 + kKst) <= 4 * (BM * 64 + BN * 64 + 4 * 1024),
+                  "epilogue LDS fits in the ring");
+    constexpr auto blk_j = [](int bi) { return kStageK ? bi % NB : bi / MB; };
+    constexpr auto blk_i = [](int bi) { return kStageK ? bi / NB : bi % MB; };
     static_for<kAhead>([&](auto B0) {
       constexpr int b0 = decltype(B0)::value;
-      if constexpr (b0 < NB * MB) load_block(B0, b0 / MB, b0 % MB);
+      if constexpr (b0 < NB * MB) load_block(B0, blk_j(b0), blk_i(b0));
     });
     static_for<NB * MB>([&](auto BI) {
-      constexpr int bi = decltype(BI)::value, J = bi / MB, I = bi % MB, b = bi % (kAhead + 1);
+      constexpr int bi = decltype(BI)::value, J = blk_j(bi), I = blk_i(bi), b = bi % (kAhead + 1);
       if constexpr (bi + kAhead < NB * MB)
-        load_block(std::integral_constant<int, (bi + kAhead) % (kAhead + 1)>{}, (bi + kAhead) / MB,
-                   (bi + kAhead) % MB);
+        load_block(std::integral_constant<int, (bi + kAhead) % (kAhead + 1)>{}, blk_j(bi + kAhead),
+                   blk_i(bi + kAhead));
       float* const tg = tgw + (bi & 1) * kTgFloats;
       const int col0 = n0 + wn * WN + J * 32;
       float dg[16], du[16], gq[16], uq[16];
@@ -692,9 +733,29 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
           return u32x4_t{a[0], a[1], c[0], c[1]};
         };
         const u32x4_t vg = pack16(wg), vu = pack16(wu);
-        const uint32_t qoff = static_cast<uint32_t>((I * 32 + l32) * p.mxq_ld + col0 + 16 * hl);
-        __builtin_amdgcn_raw_buffer_store_b128(vg, rQ, qoff, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(vu, rQ, qoff + static_cast<uint32_t>(p.f), 0, 0);
+        if constexpr (kStageK) {
+          char* const kb = kst + (I & 1) * (kKst / 2);
+          *reinterpret_cast<u32x4_t*>(kb + l32 * 144 + J * 32 + 16 * hl) = vg;
+          *reinterpret_cast<u32x4_t*>(kb + 32 * 144 + l32 * 144 + J * 32 + 16 * hl) = vu;
+          if constexpr (J == NB - 1) {
+            wave_sync();
+            const int c16 = lane & 7;
+            const int cbase = n0 + wn * WN;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int r = t * 8 + (lane >> 3);
+              const u32x4_t g = *reinterpret_cast<const u32x4_t*>(kb + r * 144 + c16 * 16);
+              const u32x4_t u = *reinterpret_cast<const u32x4_t*>(kb + 32 * 144 + r * 144 + c16 * 16);
+              const uint32_t off = static_cast<uint32_t>((I * 32 + r) * p.mxq_ld + cbase + c16 * 16);
+              __builtin_amdgcn_raw_buffer_store_b128(g, rQ, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(u, rQ, off + static_cast<uint32_t>(p.f), 0, 0);
+            }
+          }
+        } else {
+          const uint32_t qoff = static_cast<uint32_t>((I * 32 + l32) * p.mxq_ld + col0 + 16 * hl);
+          __builtin_amdgcn_raw_buffer_store_b128(vg, rQ, qoff, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(vu, rQ, qoff + static_cast<uint32_t>(p.f), 0, 0);
+        }
         // Scales: row r's byte of 32-block col / 32 (rows past the end dropped).
         const auto rS = make_rsrc(p.mxs + static_cast<int64_t>(col0 / 64) * p.mxs_slab + static_cast<int64_t>(mrow) * 2,
                                   static_cast<int64_t>(rows) * 2);
