@@ -54,7 +54,9 @@
  *  - Validation is host-side only and never reads device memory. Errors:
  *    MOE_ERR_INVALID_ARG (null pointer, bad sizes, k > E), MOE_ERR_UNSUPPORTED
  *    (d or f not a multiple of 64, E > 256, k > 8, dtype not available for
- *    the call), MOE_ERR_MISALIGNED (a tensor pointer not 16-byte aligned),
+ *    the call, T*k above 2^30, d or f above 65536; MXFP8 layers: T*k + 63 E
+ *    + 63 of 2^23 or more), MOE_ERR_MISALIGNED (a tensor pointer not 16-byte
+ *    aligned),
  *    MOE_ERR_WORKSPACE (workspace/save buffer smaller than the query says),
  *    MOE_ERR_HIP (a launch failed; the message names the HIP error).
  *    On error nothing is enqueued. moe_last_error_message() gives a

@@ -55,6 +55,12 @@ int check_shape(const moe_shape* s) {
   // Index arithmetic is 32-bit for row ids and 64-bit for element offsets.
   if (s->T * s->k > (int64_t)1 << 30 || s->d > 65536 || s->f > 65536 || s->T > (int64_t)1 << 28)
     return fail(MOE_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  // MXFP8 weight-gradient tiles address 256 rows of a token-major operand
+  // (P bytes each, the routed rows padded per expert) through one buffer
+  // descriptor and 32-bit offsets: P < 2^23.
+  if (s->dtype == MOE_MXFP8 && moe::mx_padded_rows(s->T * s->k, s->E) >= (int64_t)1 << 23)
+    return fail(MOE_ERR_UNSUPPORTED, "MXFP8 layers support T*k + 63*E + 63 below 2^23 (got T*k = %lld, E = %lld)",
+                (long long)(s->T * s->k), (long long)s->E);
   return MOE_OK;
 }
 

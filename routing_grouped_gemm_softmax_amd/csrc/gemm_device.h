@@ -632,7 +632,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx16 (&acc)[BN
     // G, U in the blocked layout the gate/up epilogue writes (3 KB per 32 x
     // 32 block, lane order): blocks past the expert's padded rows read 0.
     const int fb = p.f / 32;
-    const int64_t gb0 = (pt0 / 32) * fb * 3072, gbytes = static_cast<int64_t>(max(0, n64 - rel0) / 32) * fb * 3072;
+    // The range covers this wave's row blocks only (at most WM rows), so it
+    // stays far below the 2^31 bytes a descriptor holds however long the expert.
+    const int64_t gb0 = (pt0 / 32) * fb * 3072;
+    const int64_t gbytes = static_cast<int64_t>(min(WM, max(0, n64 - rel0)) / 32) * fb * 3072;
     const auto rG = make_rsrc(static_cast<const char*>(p.e0) + gb0, gbytes);
     const auto rU = make_rsrc(static_cast<const char*>(p.e1) + gb0, gbytes);
     const auto rQ = make_rsrc(p.mxq + static_cast<int64_t>(mrow) * p.mxq_ld, rows * p.mxq_ld);

@@ -223,3 +223,17 @@ def test_grouped_quantize_argument_checks():
     assert lib.mxfp8_quantize_grouped(p, 64, 64, p, 0, p, p, None) == L.MOE_ERR_INVALID_ARG
     assert lib.mxfp8_quantize_grouped(p, 64, 64, p, 257, p, p, None) == L.MOE_ERR_INVALID_ARG
     assert lib.mxfp8_quantize_grouped(p, 1 << 31, 1, p, 1, p, p, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_mxfp8_routed_rows_limit():
+    """MXFP8 layers address a weight-gradient tile's 256 token-major rows (P
+    bytes each, P = T*k + 63 E + 63 rounded down to 64) with 32-bit offsets:
+    P must stay below 2^23, i.e. T*k + 63 E + 63 < 2^23. The bf16 layer of
+    the same size is accepted."""
+    lim = (1 << 23) - 64 - 63 * 8  # T*k + 63 E + 63 = 2^23 - 1 at E = 8 and T*k = lim + 56
+    ok = L.MoeShape.make(lim // 4, 128, 8, 4, 128, "mxfp8")
+    assert L.workspace_size(L.MOE_OP_FFN_FWD, ok) > 0
+    big = L.MoeShape.make((lim + 64) // 4, 128, 8, 4, 128, "mxfp8")
+    with pytest.raises(L.MoeError, match="MXFP8 layers support"):
+        L.workspace_size(L.MOE_OP_FFN_FWD, big)
+    assert L.workspace_size(L.MOE_OP_FFN_FWD, L.MoeShape.make((lim + 64) // 4, 128, 8, 4, 128, "bf16")) >= 0
