@@ -54,6 +54,11 @@ CASES = {
     # dgrad and both weight gradients run as streaming persistent kernels;
     # ragged row tiles, two empty experts, odd slab counts per tile.
     "stream_ragged_empty": ("bf16_zipf", dict(T=2048, d=512, E=8, f=256, dtype="mxfp8"), [4, 0, 2, 1, 3, 1, 0, 5]),
+    # d and f odd multiples of 128 at 1024 rows per expert: 256 x 128 tiles
+    # for the down dgrad (N = f), the down forward and gate/up dgrad (N = d),
+    # 128 x 128 tiles for the weight gradients (M = d); the gate/up forward
+    # (N = 2f) keeps 256 x 256.
+    "narrow_256x128": ("mxfp8_balanced", dict(T=2048, d=640, E=8, f=384), None),
     # The largest expert count and top-k: 16 rows per expert, each padded to
     # 64 in the weight-gradient layouts.
     "max_E256_k8": ("mxfp8_balanced", dict(T=512, d=128, E=256, k=8, f=128), None),
