@@ -49,6 +49,10 @@ CASES = {
                             [30, 9, 4, 2, 1, 1, 1, 1, 0, 1, 1, 1, 1, 1, 1, 1]),
     # The largest expert count and top-k the library takes, learned routing:
     # about 9 rows per expert, 16 router column blocks, eight slots per token.
+    # d and f odd multiples of 128 at about 1024 rows per expert: 256 x 128
+    # tiles (and their quarter-tile tails) for the down forward, down dgrad
+    # and gate/up dgrad; 128-row weight-gradient tiles.
+    "bf16_256x128_tiles": ("bf16_e8", dict(T=2048, d=384, f=640), None),
     "bf16_max_E256_k8": ("bf16_e8", dict(T=300, d=128, E=256, k=8, f=128), None),
     # The router at wider d: a ragged last block of 16 tokens at d = 512, and
     # d = 4096 with eight 16-expert blocks (32 k steps per wave).
