@@ -216,9 +216,13 @@ struct TileCoord {
 // tile counts, so any wave maps a tile index to its coordinates with
 // lane-local compares and one ballot (no LDS, no barrier).
 //
-// Tiles are numbered by a logical index L: groups of 8 row tiles sweep the
-// column tiles, so tiles close in L share operands in L2. With R tiles and
-// `cus` workgroups running at once, the rem = R % cus tiles past the last full
+// Tiles are numbered by a logical index L so that tiles close in L share
+// operands in L2: groups of 8 row tiles sweep the column tiles. With tiles of
+// 256 rows the groups run on across expert boundaries; with shorter tiles an
+// expert's few row tiles form a group of their own, so that a group does not
+// read the weight panels of several experts (by measurement: the first order
+// is as fast as the second at 256-row tiles and slower at 128). With R tiles
+// and `cus` workgroups running at once, the rem = R % cus tiles past the last full
 // round would keep the chip mostly idle for a whole tile time; when 4 rem <=
 // cus they are left to a second launch (p.tail = 1) of a kernel with
 // half-height, half-width tiles that takes each as 4 quarters, all in one
@@ -253,8 +257,8 @@ struct RowTileMap {
     const int rem = R >= cus ? R % cus : R;
     return 4 * rem > cus ? R : R - rem;
   }
-  // Coordinates of tile L (wave-uniform; e = -1 if L is past the end).
-  __device__ __forceinline__ TileCoord at(int L, int lane) const {
+  // Groups of 8 row tiles taken across the expert boundaries.
+  __device__ __forceinline__ TileCoord at_across(int L, int lane) const {
     constexpr int GM = 8;
     const int g = L / (GM * NT);
     const int gm = min(GM, RM - g * GM);
@@ -277,6 +281,38 @@ struct RowTileMap {
     t.row0 = __builtin_amdgcn_readfirstlane(__shfl(row0, src, kWave));
     t.row_end = __builtin_amdgcn_readfirstlane(__shfl(row_end, src, kWave));
     t.nt = __builtin_amdgcn_readfirstlane(local / gm);
+    t.m0 = 0;
+    return t;
+  }
+  // Coordinates of tile L (wave-uniform; e = -1 if L is past the end).
+  __device__ __forceinline__ TileCoord at(int L, int lane) const {
+    constexpr int GM = 8;
+    if (tbm >= 256) return at_across(L, lane);
+    // The lane holding L's expert finds it; the rest is wave-uniform.
+    int e_sel = -1, t0_sel = 0, tq_sel = 0, beg_sel = 0, end_sel = 0, run = excl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t0 = run * NT;
+      if (L >= t0 && L < t0 + tq[q] * NT) {
+        e_sel = lane * 4 + q;
+        t0_sel = t0;
+        tq_sel = tq[q];
+        beg_sel = beg[q];
+        end_sel = end[q];
+      }
+      run += tq[q];
+    }
+    const uint64_t who = __ballot(e_sel >= 0);
+    TileCoord t{-1, 0, 0, 0, 0};
+    if (!who) return t;
+    const int src = __ffsll(static_cast<long long>(who)) - 1;
+    t.e = __builtin_amdgcn_readfirstlane(__shfl(e_sel, src, kWave));
+    const int local = L - __builtin_amdgcn_readfirstlane(__shfl(t0_sel, src, kWave));
+    const int tqe = __builtin_amdgcn_readfirstlane(__shfl(tq_sel, src, kWave));
+    const int g = local / (GM * NT), gm = min(GM, tqe - g * GM), in_g = local - g * GM * NT;
+    t.row0 = __builtin_amdgcn_readfirstlane(__shfl(beg_sel, src, kWave)) + (g * GM + in_g % gm) * tbm;
+    t.row_end = __builtin_amdgcn_readfirstlane(__shfl(end_sel, src, kWave));
+    t.nt = in_g / gm;
     t.m0 = 0;
     return t;
   }
