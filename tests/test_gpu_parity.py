@@ -53,6 +53,10 @@ CASES = {
     # tiles (and their quarter-tile tails) for the down forward, down dgrad
     # and gate/up dgrad; 128-row weight-gradient tiles.
     "bf16_256x128_tiles": ("bf16_e8", dict(T=2048, d=384, f=640), None),
+    # 128-row tiles (about 256 rows per expert) around one expert of 1541
+    # rows: its 13 row tiles form tile groups of 8 and 5, the other experts'
+    # groups hold 2 to 5; the last expert gets no rows.
+    "bf16_128row_tiles_hot_expert": ("bf16_zipf", dict(T=2048, d=256, E=32, f=256), [6, 1.5] + [0.5] * 29 + [0]),
     "bf16_max_E256_k8": ("bf16_e8", dict(T=300, d=128, E=256, k=8, f=128), None),
     # The router at wider d: a ragged last block of 16 tokens at d = 512, and
     # d = 4096 with eight 16-expert blocks (32 k steps per wave).
